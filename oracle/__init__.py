@@ -1,0 +1,21 @@
+"""CPU oracle for the group-wise 4-bit weight-only linear layer.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import it.  The HIP library never imports, links or calls anything here, and
+nothing here calls the HIP library.  See ``woq_ref`` for the definitions and
+the readings of the pages they follow.
+"""
+from .woq_ref import (  # noqa: F401
+    QMAX_ASYM,
+    QMAX_SYM,
+    OracleError,
+    bf16_bits_to_f64,
+    bf16_round_bits,
+    dequantize_int4_groups,
+    linear_int4_groups,
+    pack_uint4,
+    quantize_groups,
+    rint_half_even,
+    unpack_uint4,
+)

@@ -1,0 +1,265 @@
+"""CPU oracle for the group-wise 4-bit weight-only linear layer.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  This module is the yardstick the HIP
+library is measured against.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import it.  It shares no code,
+tables or constants with the HIP library, and never calls it.
+
+Everything is plain NumPy, evaluated in float64, written to be checked against
+the pages by eye.  Sources (page title, then section):
+
+* linnet docs, "Quantization": the std.quant table (the Int4GroupLinear layout
+  ``weight [Out, In/Group, Group/2; u8]``, scale and zero ``[Out, In/Group]``,
+  optional ``order [In; i32]`` and bias; ``dequantize_int4_groups`` computes
+  ``(q - zero) * scale`` per group; ``linear_int4_groups`` is a linear layer
+  over those weights), the sentence on packed 4-bit formats (two values per
+  byte, even element in the low nibble), section "Group-wise 4-bit weights"
+  (16 levels per group with a scale and a zero point) and section "Importing
+  GPTQ and AWQ" (an act-order layer gathers its inputs through ``order``).
+* tinyllm L8.5, "Quantization: int8, int4 group (packed), fp8, KV quant":
+  section 2 "Principles" (symmetric scaling, ties-to-even rounding, the
+  half-step bound, packing), section 3 "Worked example by hand".
+* "20. Quantization" (inference book): section "Symmetric quantization, from
+  scratch" (s = a/Q, codes clamp(round(w/s)), worked example), the edge case
+  of an all-zero group getting scale 1, section "Packing".
+* "4.8 Quantization II": section "The Quantization Landscape: A Taxonomy"
+  (asymmetric scheme with a zero point; half-step bound; s^2/12 noise) and
+  section "Per-Group INT4" (unsigned codes [0, 15] with a zero point).
+
+Readings taken where the pages are silent or disagree (each is listed with
+its reason in the design notes of the repository):
+
+R1  The rounding step rounds the *real* quotient ``Q*w/range`` to the nearest
+    integer, ties to even, evaluated as one float64 division of float64
+    operands.  This reproduces the inference book's worked example
+    ``[-2,-1,0,1,2] -> [-7,-4,0,4,7]``; forming the quotient in float32
+    against the stored scale would give ``[-7,-3,0,3,7]`` there.
+R2  Asymmetric scheme: ``range = max - min`` of the raw group (not widened to
+    include 0); ``scale = f32(range/15)``; ``zero = clamp(rint(-15*min/range),
+    0, 15)``; ``q = clamp(rint(15*w/range) + zero, 0, 15)``.  The rounding is
+    applied to ``w/scale`` before the zero point is added.
+R3  A group with range 0 gets scale 1 (the inference book's rule for an
+    all-zero group, extended to any constant group): ``zero = clamp(rint(-min),
+    0, 15)``, ``q = clamp(rint(w) + zero, 0, 15)``.
+R4  Symmetric scheme (worked-example mode): ``a = max|w|``; ``scale =
+    f32(a/7)``; ``c = clamp(rint(7*w/a), -7, 7)``; stored unsigned as
+    ``q = c + 8`` with ``zero = 8``, so ``(q - zero)*scale = c*scale``.  An
+    all-zero group gets scale 1 and c = 0.
+R5  Scale is stored as float32 and zero as uint8.
+R6  ``order`` is a gather: ``x'[m, k] = x[m, order[k]]``.
+R7  Dequantization forms ``(q - zero) * scale`` once, rounded to float32, and
+    then (for a bfloat16 result) rounds that float32 to bfloat16.
+R8  The linear layer's exact value is ``sum_k x'[m,k] * (q-z)*s + bias[n]``
+    with the float64-exact ``(q - z)*s`` (a 4-bit integer times a float32 is
+    exact in float64).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "QMAX_ASYM",
+    "QMAX_SYM",
+    "rint_half_even",
+    "quantize_groups",
+    "pack_uint4",
+    "unpack_uint4",
+    "dequantize_int4_groups",
+    "linear_int4_groups",
+    "bf16_round_bits",
+    "bf16_bits_to_f64",
+]
+
+QMAX_ASYM = 15   # unsigned 4-bit codes 0..15 ("Per-Group INT4", 4.8 Quantization II)
+QMAX_SYM = 7     # symmetric 4-bit limit Q = 2^(b-1) - 1 ("20. Quantization")
+
+
+class OracleError(ValueError):
+    """Input the pages' rules refuse (bad shapes, non-finite weights, codes > 15)."""
+
+
+def rint_half_even(a):
+    """Round to the nearest integer, halves to the even neighbour.
+
+    tinyllm L8.5 section 2 ("Principles") fixes ties-to-even for every rounding;
+    numpy's ``rint`` is IEEE round-to-nearest-even on float64.
+    """
+    return np.rint(np.asarray(a, dtype=np.float64))
+
+
+def _check_groups(w: np.ndarray, group: int):
+    if w.ndim != 2:
+        raise OracleError("weight must be a matrix [Out, In]")
+    if group < 1:
+        raise OracleError("group must be positive")
+    if w.shape[1] % group != 0:
+        raise OracleError("group must divide In (the Int4GroupLinear layout has In/Group groups)")
+    if not np.all(np.isfinite(w)):
+        raise OracleError("weights must be finite")
+
+
+def quantize_groups(w, group: int, symmetric: bool = False):
+    """Round-to-nearest group quantizer.
+
+    Args:
+      w: float32 [N, K].  group: consecutive inputs per group (must divide K).
+      symmetric: False -> asymmetric min/max scheme with a zero point (R2, R3);
+                 True  -> symmetric absmax scheme stored offset by 8 (R4).
+    Returns:
+      q uint8 [N, K] in 0..15, scale float32 [N, K/group], zero uint8 [N, K/group].
+    """
+    w = np.asarray(w, dtype=np.float32)
+    _check_groups(w, group)
+    n, k = w.shape
+    ng = k // group
+    wg = w.reshape(n, ng, group).astype(np.float64)   # exact widening
+
+    if symmetric:
+        a = np.max(np.abs(wg), axis=-1)                     # group absmax (exact)
+        nonzero = a > 0
+        a_safe = np.where(nonzero, a, 1.0)
+        scale = np.where(nonzero, (a_safe / QMAX_SYM), 1.0).astype(np.float32)
+        c = rint_half_even((QMAX_SYM * wg) / a_safe[..., None])
+        c = np.clip(c, -QMAX_SYM, QMAX_SYM)
+        c = np.where(nonzero[..., None], c, 0.0)
+        q = (c + 8).astype(np.uint8)
+        zero = np.full((n, ng), 8, dtype=np.uint8)
+        return q.reshape(n, k), scale, zero
+
+    mn = np.min(wg, axis=-1)
+    mx = np.max(wg, axis=-1)
+    d = mx - mn                                          # float64 subtraction
+    flat = d == 0
+    d_safe = np.where(flat, 1.0, d)
+
+    scale = np.where(flat, 1.0, d_safe / QMAX_ASYM).astype(np.float32)
+    z_ratio = rint_half_even((-QMAX_ASYM * mn) / d_safe)
+    z_flat = rint_half_even(-mn)
+    zero = np.clip(np.where(flat, z_flat, z_ratio), 0, QMAX_ASYM)
+
+    r_ratio = rint_half_even((QMAX_ASYM * wg) / d_safe[..., None])
+    r_flat = rint_half_even(wg)
+    r = np.where(flat[..., None], r_flat, r_ratio)
+    q = np.clip(r + zero[..., None], 0, QMAX_ASYM)
+
+    return (q.astype(np.uint8).reshape(n, k), scale, zero.astype(np.uint8))
+
+
+def pack_uint4(q):
+    """Two 4-bit codes per byte: element 2j in the low nibble, 2j+1 in the high nibble.
+
+    The packing sentence of linnet "Quantization" and tinyllm L8.5 section 2
+    ("Packing").  The last axis must have even length and every code must be
+    at most 15; anything else is refused.
+    """
+    q = np.asarray(q)
+    if q.shape[-1] % 2 != 0:
+        raise OracleError("an odd number of codes cannot be packed two per byte")
+    if q.size and (q.min() < 0 or q.max() > 15):
+        raise OracleError("codes must lie in 0..15")
+    q = q.astype(np.uint8)
+    lo = q[..., 0::2]
+    hi = q[..., 1::2]
+    return (lo | (hi << np.uint8(4))).astype(np.uint8)
+
+
+def unpack_uint4(packed):
+    """Inverse of :func:`pack_uint4`: byte b -> (b & 0xF, b >> 4), unsigned."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & np.uint8(0x0F)
+    out[..., 1::2] = p >> np.uint8(4)
+    return out
+
+
+def _codes_rows(packed, n: int, k: int):
+    p = np.asarray(packed, dtype=np.uint8).reshape(n, k // 2)
+    return unpack_uint4(p)                             # [n, k]
+
+
+def _dequant_exact(q_rows, scale_rows, zero_rows, group: int):
+    """(q - zero) * scale per group as exact float64 values (R8)."""
+    n, k = q_rows.shape
+    ng = k // group
+    qi = q_rows.reshape(n, ng, group).astype(np.float64)
+    z = zero_rows.astype(np.float64)[..., None]
+    s = scale_rows.astype(np.float32).astype(np.float64)[..., None]
+    return ((qi - z) * s).reshape(n, k)
+
+
+def bf16_round_bits(f32):
+    """float32 -> bfloat16 bit patterns, round to nearest, ties to even.
+
+    Definition: keep the upper 16 bits of the float32 encoding after adding
+    half of the dropped unit, with the tie going to an even kept value.
+    Only finite inputs are expected here.
+    """
+    u = np.asarray(f32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    rounded = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f64(bits):
+    """bfloat16 bit patterns -> exact float64 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def dequantize_int4_groups(packed, scale, zero, n: int, k: int, group: int,
+                           out: str = "f32"):
+    """Group dequantization ``(q - zero) * scale`` (R7).
+
+    packed uint8 [N, K/2] (or [N, K/G, G/2]); scale float32 [N, K/G];
+    zero uint8 [N, K/G].  ``out="f32"`` returns float32 [N, K]; ``out="bf16"``
+    returns the bfloat16 bit patterns (uint16 [N, K]) of the float32 result.
+    """
+    if group < 2 or group % 2 or k % group:
+        raise OracleError("group must be even and divide K")
+    q = _codes_rows(packed, n, k)
+    w64 = _dequant_exact(q, np.asarray(scale).reshape(n, k // group),
+                         np.asarray(zero).reshape(n, k // group), group)
+    w32 = w64.astype(np.float32)                      # one rounding of an exact value
+    if out == "f32":
+        return w32
+    if out == "bf16":
+        return bf16_round_bits(w32)
+    raise OracleError("out must be 'f32' or 'bf16'")
+
+
+def linear_int4_groups(x, packed, scale, zero, n: int, k: int, group: int,
+                       bias=None, order=None, rows=None, block_rows: int = 1024):
+    """Exact-as-float64 value of ``y = x' . dequant(W)^T + bias`` (R6, R8).
+
+    x: activations [M, K]; a uint16 array is read as bfloat16 bit patterns,
+       anything else as real values.
+    packed/scale/zero: the Int4GroupLinear tensors for W [N, K].
+    bias: float32 [N] or None.  order: int32 [K] or None (gather, R6).
+    rows: optional index array of output columns n to compute (the rest are
+       not formed); the result then has shape [M, len(rows)].
+    Returns float64 [M, N] (or [M, len(rows)]).
+    """
+    if group < 2 or group % 2 or k % group:
+        raise OracleError("group must be even and divide K")
+    x = np.asarray(x)
+    xv = bf16_bits_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
+    if xv.ndim != 2 or xv.shape[1] != k:
+        raise OracleError("x must be [M, K]")
+    if order is not None:
+        order = np.asarray(order, dtype=np.int64)
+        if order.shape != (k,) or (k and (order.min() < 0 or order.max() >= k)):
+            raise OracleError("order must hold K indices in [0, K)")
+        xv = xv[:, order]                               # gather: x'[m,k] = x[m, order[k]]
+    ng = k // group
+    p = np.asarray(packed, dtype=np.uint8).reshape(n, k // 2)
+    s = np.asarray(scale, dtype=np.float32).reshape(n, ng)
+    z = np.asarray(zero, dtype=np.uint8).reshape(n, ng)
+    idx = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    y = np.empty((xv.shape[0], idx.size), dtype=np.float64)
+    for b0 in range(0, idx.size, block_rows):
+        sel = idx[b0:b0 + block_rows]
+        w_rows = _dequant_exact(unpack_uint4(p[sel]), s[sel], z[sel], group)
+        y[:, b0:b0 + sel.size] = xv @ w_rows.T
+    if bias is not None:
+        y += np.asarray(bias, dtype=np.float32).astype(np.float64)[idx][None, :]
+    return y
