@@ -1,0 +1,175 @@
+/*
+ * woq.h - group-wise 4-bit weight-only linear layers on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libwoq.so.  Every pointer argument is a plain address: "device"
+ * pointers are HIP device memory (for example from hipMalloc or a PyTorch
+ * tensor's data_ptr()), "host" pointers are ordinary process memory.  Sizes
+ * are element counts unless a name ends in _bytes.  All tensors are dense and
+ * row-major.  The caller owns every buffer; the library keeps no pointer after
+ * a call returns.
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the legacy
+ * default stream).  Calls marked ASYNC only enqueue work on that stream and
+ * return; results are ready when the stream reaches them.  Calls marked SYNC
+ * wait for their own work on that stream before returning.
+ *
+ * Errors: every entry point validates its arguments on the host before it
+ * enqueues anything and returns a woq_status.  A call that returns anything
+ * but WOQ_OK because of an argument check has enqueued nothing and written
+ * nothing.  Data-dependent errors (WOQ_ENONFINITE, WOQ_ERANGE) are found on
+ * the device; the outputs of such a call are then unspecified.
+ *
+ * Weight layout (linnet docs "Quantization", std.quant table, row
+ * Int4GroupLinear; section "Group-wise 4-bit weights"): for a weight W[N, K]
+ * (N outputs, K inputs) and a group size G dividing K,
+ *   packed [N, K/G, G/2] uint8  - two 4-bit codes per byte, the code of the
+ *                                 even input in the low nibble, the odd one in
+ *                                 the high nibble (the packing sentence of the
+ *                                 same page);
+ *   scale  [N, K/G] float32;
+ *   zero   [N, K/G] uint8      - each 0..15;
+ * and W_hat[n, k] = (q[n, k] - zero[n, k/G]) * scale[n, k/G].
+ */
+#ifndef WOQ_H
+#define WOQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WOQ_OK = 0,
+  WOQ_EINVAL = 1,        /* a required pointer is NULL, a size is negative, an enum is unknown */
+  WOQ_ESHAPE = 2,        /* sizes inconsistent with each other (odd count, K odd, ...) */
+  WOQ_EGROUP = 3,        /* group < 1, group does not divide K, or odd where the layout needs even */
+  WOQ_ENONFINITE = 4,    /* a weight is NaN or infinite (data-dependent) */
+  WOQ_ERANGE = 5,        /* a code exceeds 15 (data-dependent) */
+  WOQ_EWORKSPACE = 6,    /* workspace missing or smaller than woq_linear_workspace_bytes() */
+  WOQ_EUNSUPPORTED = 7,  /* valid input this build has no kernel for (group size, sizes >= 2^31) */
+  WOQ_EALIGN = 8,        /* a pointer lacks the alignment stated for it below */
+  WOQ_EHIP = 9           /* the HIP runtime reported an error */
+} woq_status;
+
+typedef enum { WOQ_F32 = 0, WOQ_BF16 = 1 } woq_dtype;
+
+/* Short English description of a status code (static storage, never NULL). */
+const char* woq_status_str(int32_t status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t woq_version(void);
+
+/*
+ * Group quantizer, round to nearest with ties to even.  SYNC.
+ *   Asymmetric (symmetric = 0): the GPTQ/AWQ-style scheme with a zero point
+ *     ("4.8 Quantization II", section "Per-Group INT4": unsigned codes 0..15
+ *     with a zero point; linnet "Quantization", section "Group-wise 4-bit
+ *     weights").  Per group: range = max - min (float64);
+ *     scale = float32(range / 15); zero = clamp(rint(-15*min/range), 0, 15);
+ *     q = clamp(rint(15*w/range) + zero, 0, 15).  A group with range 0 gets
+ *     scale 1, zero = clamp(rint(-min), 0, 15), q = clamp(rint(w) + zero, 0, 15)
+ *     (an all-zero group gets scale 1: "20. Quantization", the edge cases
+ *     after quantize_groupwise).
+ *   Symmetric (symmetric = 1): "20. Quantization", section "Symmetric
+ *     quantization, from scratch", with Q = 7: a = max|w|;
+ *     scale = float32(a / 7); c = clamp(rint(7*w/a), -7, 7); stored unsigned as
+ *     q = c + 8 with zero = 8.  An all-zero group gets scale 1 and c = 0.
+ *   Every quotient is one correctly rounded float64 division of the exact
+ *   operands, so the rounding decision is taken on the real quotient.
+ * Arguments: w [n, k] float32 (device, 4-byte aligned); group >= 1 divides k;
+ *   outputs q [n, k] uint8 (codes, unpacked), scale [n, k/group] float32,
+ *   zero [n, k/group] uint8 (device).
+ * Errors: WOQ_EINVAL, WOQ_EGROUP, WOQ_ENONFINITE (any NaN or infinity in w),
+ *   WOQ_EUNSUPPORTED (n*k >= 2^40), WOQ_EHIP.
+ */
+int32_t woq_quantize_groups(const float* w, int64_t n, int64_t k, int32_t group,
+                            int32_t symmetric, uint8_t* q, float* scale, uint8_t* zero,
+                            void* stream);
+
+/*
+ * Pack 4-bit codes two per byte: packed[i] = q[2i] | q[2i+1] << 4 (linnet
+ * "Quantization", packing sentence; tinyllm L8.5 section 2 "Principles",
+ * Packing).  SYNC (it reports codes above 15).
+ * Arguments: q [count] uint8 (device), count even; packed [count/2] uint8 (device).
+ * Errors: WOQ_EINVAL, WOQ_ESHAPE (odd count), WOQ_ERANGE (a code > 15), WOQ_EHIP.
+ */
+int32_t woq_pack_uint4(const uint8_t* q, int64_t count, uint8_t* packed, void* stream);
+
+/*
+ * Unpack unsigned nibbles: q[2i] = packed[i] & 15, q[2i+1] = packed[i] >> 4
+ * (linnet "Quantization", std.quant table, unpack_uint4).  ASYNC.
+ * Arguments: packed [count/2] uint8 (device); count even; q [count] uint8 (device).
+ * Errors: WOQ_EINVAL, WOQ_ESHAPE (odd count), WOQ_EHIP.
+ */
+int32_t woq_unpack_uint4(const uint8_t* packed, int64_t count, uint8_t* q, void* stream);
+
+/*
+ * Group dequantization W_hat = (q - zero) * scale (linnet "Quantization",
+ * std.quant table, dequantize_int4_groups).  The product is formed in float32
+ * (one rounding of the exact value); with out_dtype = WOQ_BF16 that float32 is
+ * then rounded to bfloat16, ties to even.  ASYNC.
+ * Arguments: packed [n, k/2] uint8, scale [n, k/group] float32,
+ *   zero [n, k/group] uint8 (device); group even, divides k;
+ *   w_hat [n, k] of out_dtype (device).
+ * Errors: WOQ_EINVAL, WOQ_EGROUP, WOQ_EUNSUPPORTED (n*k >= 2^40), WOQ_EHIP.
+ */
+int32_t woq_dequantize_int4_groups(const uint8_t* packed, const float* scale,
+                                   const uint8_t* zero, int64_t n, int64_t k, int32_t group,
+                                   int32_t out_dtype, void* w_hat, void* stream);
+
+/*
+ * Workspace the linear layer needs for these sizes, in bytes (0 when none).
+ * Pure host function.  has_order != 0 when an act-order gather will be passed.
+ */
+size_t woq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group,
+                                  int32_t has_order);
+
+/*
+ * Linear layer over group-wise 4-bit weights (linnet "Quantization", std.quant
+ * table, linear_int4_groups; section "Importing GPTQ and AWQ" for the
+ * act-order gather):
+ *   y[m, n] = sum_k x'[m, k] * W_hat[n, k] + bias[n],
+ *   x'[m, k] = order ? x[m, order[k]] : x[m, k].
+ * x is bfloat16; products and sums are float32; the sum over each group is
+ * multiplied by that group's scale in float32; bias is added in float32; a
+ * bfloat16 y is rounded once from that float32 value, ties to even.  ASYNC.
+ * Arguments:
+ *   x_bf16 [m, k] bfloat16 (device, 16-byte aligned);
+ *   packed [n, k/2] uint8 (device, 16-byte aligned); scale [n, k/group] float32
+ *   (device, 4-byte aligned); zero [n, k/group] uint8 (device);
+ *   bias [n] float32 (device) or NULL; order [k] int32 (device) or NULL - every
+ *   entry must lie in [0, k) (entries outside are clamped into range, never read
+ *   out of bounds; the result is then unspecified);
+ *   group in {32, 64, 128, 256}, dividing k;
+ *   y [m, n] of y_dtype (device, 4-byte aligned for float32, 2-byte for bfloat16),
+ *   which must not overlap any input;
+ *   workspace (device, 256-byte aligned) of at least
+ *   woq_linear_workspace_bytes(m, n, k, group, order != NULL) bytes, or NULL
+ *   when that is 0.  The workspace holds only scratch; it need not be cleared.
+ * m == 0 or n == 0 is a no-op; k == 0 gives y = bias (or 0).
+ * Errors: WOQ_EINVAL, WOQ_EGROUP, WOQ_EUNSUPPORTED (group outside the list,
+ *   m, n or k >= 2^31), WOQ_EALIGN, WOQ_EWORKSPACE, WOQ_EHIP.
+ */
+int32_t woq_linear_int4_groups(const void* x_bf16, int64_t m, const uint8_t* packed,
+                               const float* scale, const uint8_t* zero, const float* bias,
+                               const int32_t* order, int64_t n, int64_t k, int32_t group,
+                               int32_t y_dtype, void* y, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * Describe the kernel plan woq_linear_int4_groups uses for these sizes: the
+ * path (skinny MFMA for m <= 64, tiled MFMA GEMM above), tiles, waves and
+ * whether an input pre-pass runs.  Writes a NUL-terminated string of at most
+ * len bytes into buf (host).  Pure host function.
+ * Errors: WOQ_EINVAL (buf NULL, len 0), plus the shape errors of the linear call.
+ */
+int32_t woq_linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, int32_t has_order,
+                        char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WOQ_H */

@@ -1,0 +1,144 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every symbol
+include/woq.h declares, and its pure-host functions and argument checks
+behave as documented.  Only calls that return before any HIP call are made.
+"""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import weight_only_quantization_amd as woq
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "woq.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(woq_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return woq.load()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for must in ("woq_quantize_groups", "woq_pack_uint4", "woq_unpack_uint4",
+                 "woq_dequantize_int4_groups", "woq_linear_int4_groups",
+                 "woq_linear_workspace_bytes", "woq_linear_plan", "woq_status_str"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libwoq.so does not export {name}"
+
+
+def test_status_strings(lib):
+    for code in range(10):
+        s = lib.woq_status_str(code).decode()
+        assert s and s != "unknown status"
+    assert lib.woq_status_str(99).decode() == "unknown status"
+    assert lib.woq_version() >= 100
+
+
+@pytest.mark.parametrize("m,n,k,g,path", [
+    (1, 4096, 4096, 128, "skinny_mfma"), (16, 14336, 4096, 32, "skinny_mfma"),
+    (17, 4096, 4096, 128, "gemm_mfma"), (2048, 14336, 4096, 128, "gemm_mfma"),
+    (0, 64, 256, 32, "none"), (3, 64, 0, 32, "bias_fill"),
+])
+def test_plan_paths(m, n, k, g, path):
+    assert f"path={path}" in woq.linear_plan(m, n, k, g)
+
+
+def test_plan_mentions_gather_for_act_order():
+    assert "gather" in woq.linear_plan(1, 8192, 28672, 128, has_order=True)
+
+
+def test_workspace_sizes():
+    assert woq.linear_workspace_bytes(1, 4096, 4096, 128, False) == 0
+    ws = woq.linear_workspace_bytes(1, 8192, 28672, 128, True)
+    assert ws >= 1 * 28672 * 2 and ws % 256 == 0
+    big = woq.linear_workspace_bytes(2048, 14336, 4096, 128, False)
+    assert big >= 2048 * 4096 * 2 + (4096 // 128) * 2048 * 4
+
+
+@pytest.mark.parametrize("m,n,k,g,status", [
+    (-1, 64, 256, 32, "WOQ_EINVAL"),
+    (1, 64, 256, 48, "WOQ_EGROUP"),      # 48 does not divide 256
+    (1, 64, 240, 48, "WOQ_EUNSUPPORTED"),  # valid layout, no kernel for group 48
+    (1, 64, 256, 33, "WOQ_EGROUP"),      # odd group
+    (1, 64, 256, 0, "WOQ_EGROUP"),
+    (1, 64, 96, 64, "WOQ_EGROUP"),       # 64 does not divide 96
+    (1, 1 << 31, 256, 32, "WOQ_EUNSUPPORTED"),
+])
+def test_linear_rejects_bad_shapes_before_any_launch(lib, m, n, k, g, status):
+    rc = lib.woq_linear_int4_groups(None, m, None, None, None, None, None, n, k, g, 1,
+                                    None, None, 0, None)
+    assert woq.STATUS[rc] == status
+
+
+def test_linear_rejects_null_pointers_and_bad_dtype(lib):
+    fake = ctypes.c_void_p(4096)   # never dereferenced: validation fails first
+    rc = lib.woq_linear_int4_groups(None, 1, fake, fake, fake, None, None, 64, 256, 32, 1,
+                                    fake, None, 0, None)
+    assert woq.STATUS[rc] == "WOQ_EINVAL"
+    rc = lib.woq_linear_int4_groups(fake, 1, fake, fake, fake, None, None, 64, 256, 32, 7,
+                                    fake, None, 0, None)
+    assert woq.STATUS[rc] == "WOQ_EINVAL"
+    rc = lib.woq_linear_int4_groups(fake, 1, fake, fake, fake, None, None, 64, 256, 32, 1,
+                                    None, None, 0, None)
+    assert woq.STATUS[rc] == "WOQ_EINVAL"
+
+
+def test_linear_rejects_misalignment_and_missing_workspace(lib):
+    a16 = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    rc = lib.woq_linear_int4_groups(odd, 1, a16, a16, a16, None, None, 64, 256, 32, 1,
+                                    a16, None, 0, None)
+    assert woq.STATUS[rc] == "WOQ_EALIGN"
+    rc = lib.woq_linear_int4_groups(a16, 1, odd, a16, a16, None, None, 64, 256, 32, 1,
+                                    a16, None, 0, None)
+    assert woq.STATUS[rc] == "WOQ_EALIGN"
+    # act-order needs a gather buffer
+    rc = lib.woq_linear_int4_groups(a16, 1, a16, a16, a16, None, a16, 64, 256, 32, 1,
+                                    a16, None, 0, None)
+    assert woq.STATUS[rc] == "WOQ_EWORKSPACE"
+    # the GEMM path needs its pre-pass buffers
+    rc = lib.woq_linear_int4_groups(a16, 64, a16, a16, a16, None, None, 64, 256, 32, 1,
+                                    a16, a16, 16, None)
+    assert woq.STATUS[rc] == "WOQ_EWORKSPACE"
+
+
+def test_empty_calls_are_noops(lib):
+    assert lib.woq_linear_int4_groups(None, 0, None, None, None, None, None, 64, 256, 32, 1,
+                                      None, None, 0, None) == 0
+    assert lib.woq_linear_int4_groups(None, 4, None, None, None, None, None, 0, 256, 32, 1,
+                                      None, None, 0, None) == 0
+    assert lib.woq_quantize_groups(None, 0, 256, 32, 0, None, None, None, None) == 0
+    assert lib.woq_pack_uint4(None, 0, None, None) == 0
+    assert lib.woq_unpack_uint4(None, 0, None, None) == 0
+    assert lib.woq_dequantize_int4_groups(None, None, None, 0, 256, 32, 0, None, None) == 0
+
+
+def test_codec_argument_checks(lib):
+    fake = ctypes.c_void_p(4096)
+    assert woq.STATUS[lib.woq_pack_uint4(fake, 3, fake, None)] == "WOQ_ESHAPE"
+    assert woq.STATUS[lib.woq_unpack_uint4(fake, -2, fake, None)] == "WOQ_EINVAL"
+    assert woq.STATUS[lib.woq_quantize_groups(fake, 2, 10, 4, 0, fake, fake, fake, None)] == "WOQ_EGROUP"
+    assert woq.STATUS[lib.woq_quantize_groups(fake, 2, 8, 4, 2, fake, fake, fake, None)] == "WOQ_EINVAL"
+    assert woq.STATUS[lib.woq_quantize_groups(None, 2, 8, 4, 0, fake, fake, fake, None)] == "WOQ_EINVAL"
+    assert woq.STATUS[lib.woq_dequantize_int4_groups(fake, fake, fake, 2, 12, 3, 0, fake, None)] == "WOQ_EGROUP"
+    assert woq.STATUS[lib.woq_dequantize_int4_groups(fake, fake, fake, 2, 12, 4, 5, fake, None)] == "WOQ_EINVAL"
+    assert woq.STATUS[lib.woq_dequantize_int4_groups(fake, fake, None, 2, 12, 4, 0, fake, None)] == "WOQ_EINVAL"
+
+
+def test_plan_buffer_checks(lib):
+    assert woq.STATUS[lib.woq_linear_plan(1, 64, 256, 32, 0, None, 16)] == "WOQ_EINVAL"
+    buf = ctypes.create_string_buffer(8)
+    assert lib.woq_linear_plan(1, 64, 256, 32, 0, buf, len(buf)) == 0
+    assert len(buf.value) == 7          # truncated, NUL-terminated

@@ -1,0 +1,239 @@
+"""Group-wise 4-bit weight-only linear layers on MI355X (gfx950).
+
+Thin Python binding of ``libwoq.so`` (C ABI declared in ``include/woq.h``).
+Every function here only marshals arguments: it checks that tensors live on
+the GPU with the expected dtype, allocates outputs and workspace with
+PyTorch, and passes raw device pointers plus the current HIP stream to the
+library.  All arithmetic runs in the library's HIP kernels; there is no
+fallback path, and a missing or unloadable library raises.
+
+Names follow the std.quant functions of the linnet docs "Quantization" page:
+``quantize_groups``, ``pack_uint4``, ``unpack_uint4``,
+``dequantize_int4_groups``, ``linear_int4_groups`` (C names carry a ``woq_``
+prefix).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from pathlib import Path
+from typing import Optional
+
+import torch  # loads the HIP runtime that libwoq.so then binds to
+
+__all__ = [
+    "WoqError",
+    "load",
+    "library_path",
+    "quantize_groups",
+    "pack_uint4",
+    "unpack_uint4",
+    "dequantize_int4_groups",
+    "linear_int4_groups",
+    "linear_workspace_bytes",
+    "linear_plan",
+    "STATUS",
+]
+
+_PKG = Path(__file__).resolve().parent
+_LIB: Optional[ctypes.CDLL] = None
+
+STATUS = {
+    0: "WOQ_OK", 1: "WOQ_EINVAL", 2: "WOQ_ESHAPE", 3: "WOQ_EGROUP", 4: "WOQ_ENONFINITE",
+    5: "WOQ_ERANGE", 6: "WOQ_EWORKSPACE", 7: "WOQ_EUNSUPPORTED", 8: "WOQ_EALIGN", 9: "WOQ_EHIP",
+}
+F32, BF16 = 0, 1
+
+
+class WoqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        msg = _LIB.woq_status_str(status).decode() if _LIB is not None else ""
+        super().__init__(f"{where}: {self.name} ({msg})")
+
+
+def library_path() -> Path:
+    return Path(os.environ.get("WOQ_LIBRARY", _PKG / "libwoq.so"))
+
+
+def load() -> ctypes.CDLL:
+    """Load libwoq.so (once).  Raises if it is missing: there is no fallback."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not path.exists():
+        raise ImportError(f"{path} is missing; build it with __graft_entry__.build() "
+                          "or python weight_only_quantization_amd/_build.py")
+    lib = ctypes.CDLL(str(path))
+    c_i32, c_i64, c_p, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    sig = {
+        "woq_status_str": (ctypes.c_char_p, [c_i32]),
+        "woq_version": (c_i32, []),
+        "woq_quantize_groups": (c_i32, [c_p, c_i64, c_i64, c_i32, c_i32, c_p, c_p, c_p, c_p]),
+        "woq_pack_uint4": (c_i32, [c_p, c_i64, c_p, c_p]),
+        "woq_unpack_uint4": (c_i32, [c_p, c_i64, c_p, c_p]),
+        "woq_dequantize_int4_groups": (c_i32, [c_p, c_p, c_p, c_i64, c_i64, c_i32, c_i32, c_p, c_p]),
+        "woq_linear_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i32, c_i32]),
+        "woq_linear_int4_groups": (c_i32, [c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_i64, c_i64,
+                                           c_i32, c_i32, c_p, c_p, c_sz, c_p]),
+        "woq_linear_plan": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, ctypes.c_char_p, c_sz]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise WoqError(status, where)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def quantize_groups(w: torch.Tensor, group: int = 128, symmetric: bool = False):
+    """Round-to-nearest group quantizer on the GPU.
+
+    w: float32 [N, K].  Returns (q uint8 [N, K] codes 0..15, scale float32
+    [N, K/group], zero uint8 [N, K/group]).  Synchronizes the current stream.
+    """
+    lib = load()
+    _need(w, torch.float32, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    n, k = w.shape
+    ng = k // group if group > 0 else 0
+    q = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    scale = torch.empty((n, ng), dtype=torch.float32, device=w.device)
+    zero = torch.empty((n, ng), dtype=torch.uint8, device=w.device)
+    _check(lib.woq_quantize_groups(_ptr(w), n, k, group, int(bool(symmetric)), _ptr(q),
+                                   _ptr(scale), _ptr(zero), _stream()), "quantize_groups")
+    return q, scale, zero
+
+
+def pack_uint4(q: torch.Tensor) -> torch.Tensor:
+    """uint8 codes [..., 2c] -> packed bytes [..., c] (even element in the low nibble)."""
+    lib = load()
+    _need(q, torch.uint8, "q")
+    if q.shape[-1] % 2:
+        raise ValueError("last dimension must be even")
+    out = torch.empty(q.shape[:-1] + (q.shape[-1] // 2,), dtype=torch.uint8, device=q.device)
+    _check(lib.woq_pack_uint4(_ptr(q), q.numel(), _ptr(out), _stream()), "pack_uint4")
+    return out
+
+
+def unpack_uint4(packed: torch.Tensor) -> torch.Tensor:
+    """packed bytes [..., c] -> uint8 codes [..., 2c]."""
+    lib = load()
+    _need(packed, torch.uint8, "packed")
+    out = torch.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=torch.uint8,
+                      device=packed.device)
+    _check(lib.woq_unpack_uint4(_ptr(packed), out.numel(), _ptr(out), _stream()), "unpack_uint4")
+    return out
+
+
+def _weight_dims(packed: torch.Tensor, scale: torch.Tensor, group: Optional[int]):
+    n = packed.shape[0]
+    k = 2 * (packed.numel() // n) if n else 0
+    if group is None:
+        if scale.dim() != 2 or scale.shape[1] == 0:
+            raise ValueError("cannot infer the group size from scale")
+        group = k // scale.shape[1]
+    return n, k, int(group)
+
+
+def dequantize_int4_groups(packed: torch.Tensor, scale: torch.Tensor, zero: torch.Tensor,
+                           group: Optional[int] = None,
+                           out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """(q - zero) * scale per group -> [N, K] float32 or bfloat16."""
+    lib = load()
+    _need(packed, torch.uint8, "packed")
+    _need(scale, torch.float32, "scale")
+    _need(zero, torch.uint8, "zero")
+    n, k, group = _weight_dims(packed, scale, group)
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    out = torch.empty((n, k), dtype=out_dtype, device=packed.device)
+    _check(lib.woq_dequantize_int4_groups(_ptr(packed), _ptr(scale), _ptr(zero), n, k, group,
+                                          F32 if out_dtype == torch.float32 else BF16, _ptr(out),
+                                          _stream()), "dequantize_int4_groups")
+    return out
+
+
+def linear_workspace_bytes(m: int, n: int, k: int, group: int, has_order: bool) -> int:
+    return int(load().woq_linear_workspace_bytes(m, n, k, group, int(bool(has_order))))
+
+
+def linear_plan(m: int, n: int, k: int, group: int, has_order: bool = False) -> str:
+    """The kernel plan the library uses for these sizes (a one-line description)."""
+    lib = load()
+    buf = ctypes.create_string_buffer(512)
+    _check(lib.woq_linear_plan(m, n, k, group, int(bool(has_order)), buf, len(buf)), "linear_plan")
+    return buf.value.decode()
+
+
+def linear_int4_groups(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tensor,
+                       zero: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                       order: Optional[torch.Tensor] = None, group: Optional[int] = None,
+                       out_dtype: torch.dtype = torch.bfloat16,
+                       out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = x' . dequant(W)^T + bias with x' = x[:, order] when order is given.
+
+    x: bfloat16 [M, K]; packed uint8 [N, K/2] (or [N, K/G, G/2]); scale float32
+    [N, K/G]; zero uint8 [N, K/G]; bias float32 [N] or None; order int32 [K] or
+    None.  Returns y [M, N] of out_dtype (bfloat16 or float32).  Asynchronous
+    on the current stream.
+    """
+    lib = load()
+    _need(x, torch.bfloat16, "x")
+    _need(packed, torch.uint8, "packed")
+    _need(scale, torch.float32, "scale")
+    _need(zero, torch.uint8, "zero")
+    if bias is not None:
+        _need(bias, torch.float32, "bias")
+    if order is not None:
+        _need(order, torch.int32, "order")
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    m = x.shape[0]
+    n, k, group = _weight_dims(packed, scale, group)
+    if x.shape[1] != k:
+        raise ValueError(f"x has {x.shape[1]} inputs, the weight {k}")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    else:
+        _need(out, out_dtype, "out")
+    need = int(lib.woq_linear_workspace_bytes(m, n, k, group, int(order is not None)))
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsb = workspace.numel() if (need and workspace is not None) else 0
+    _check(lib.woq_linear_int4_groups(_ptr(x), m, _ptr(packed), _ptr(scale), _ptr(zero),
+                                      _ptr(bias), _ptr(order), n, k, group,
+                                      F32 if out_dtype == torch.float32 else BF16, _ptr(out),
+                                      _ptr(workspace) if need else None, wsb, _stream()),
+           "linear_int4_groups")
+    return out

@@ -1,0 +1,295 @@
+// C ABI of libwoq.so: argument validation, kernel planning and dispatch.
+// Every check runs on the host before anything is enqueued, so a call that
+// fails validation has no effect.
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "woq_internal.h"
+
+namespace woq {
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+bool linear_group_ok(int32_t g) { return g == 32 || g == 64 || g == 128 || g == 256; }
+
+int32_t check_linear_shape(int64_t m, int64_t n, int64_t k, int32_t group) {
+  if (m < 0 || n < 0 || k < 0) return WOQ_EINVAL;
+  if (group < 1) return WOQ_EGROUP;
+  if (!linear_group_ok(group)) return (group % 2 || k % group) ? WOQ_EGROUP : WOQ_EUNSUPPORTED;
+  if (k % group) return WOQ_EGROUP;
+  if (m >= kMaxDim || n >= kMaxDim || k >= kMaxDim) return WOQ_EUNSUPPORTED;
+  return WOQ_OK;
+}
+
+// Optional tuning override of the skinny launch shape: WOQ_SKINNY="ns,waves".
+bool skinny_override(int* ns, int* waves) {
+  static int cached = -1, c_ns = 0, c_w = 0;
+  if (cached < 0) {
+    cached = 0;
+    if (const char* e = std::getenv("WOQ_SKINNY")) {
+      int a = 0, b = 0;
+      if (std::sscanf(e, "%d,%d", &a, &b) == 2 && (a == 1 || a == 2) && b >= 1 && b <= 16) {
+        c_ns = a;
+        c_w = b;
+        cached = 1;
+      }
+    }
+  }
+  if (cached == 1) {
+    *ns = c_ns;
+    *waves = c_w;
+  }
+  return cached == 1;
+}
+
+int pow2_floor(int64_t v) {
+  int p = 1;
+  while ((int64_t)p * 2 <= v) p *= 2;
+  return p;
+}
+
+}  // namespace
+
+LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_order) {
+  LinearPlan p;
+  if (m == 0 || n == 0) return p;
+  if (k == 0) {
+    p.path = 3;
+    return p;
+  }
+  p.gb = group >= 128 ? 4 : group / 32;
+  if (m <= 16) {
+    p.path = 1;
+    p.mt = 1;
+    p.fold_rows = m == 1 ? 1 : 4;
+    p.prep = has_order ? 1 : 0;
+    const int64_t nsub = (n + 15) / 16;
+    const int64_t nsteps = (k + 127) / 128;
+    int ns = (nsub >= 2048 && p.gb >= 2) ? 2 : 1;
+    int64_t tiles = (nsub + ns - 1) / ns;
+    int64_t want = 4096 / (tiles > 0 ? tiles : 1);
+    int waves = pow2_floor(want < 1 ? 1 : want);
+    if (waves > 16) waves = 16;
+    while (waves > 1 && waves > nsteps) waves /= 2;
+    int o_ns, o_w;
+    if (skinny_override(&o_ns, &o_w) && (o_ns == 1 || p.gb >= 2)) {
+      ns = o_ns;
+      waves = o_w;
+      tiles = (nsub + ns - 1) / ns;
+    }
+    p.ns = ns;
+    p.waves = waves;
+    p.grid = tiles;
+    return p;
+  }
+  p.path = 2;
+  p.prep = 1;
+  p.bm = 128;
+  p.bn = 256;
+  p.waves = 8;
+  p.mpad = ((m + 127) / 128) * 128;
+  p.grid = ((m + 127) / 128) * ((n + 255) / 256);
+  return p;
+}
+
+LinearWorkspace linear_workspace_layout(int64_t m, int64_t n, int64_t k, int32_t group,
+                                        bool has_order) {
+  LinearWorkspace w;
+  const LinearPlan p = linear_plan(m, n, k, group, has_order);
+  if (p.path == 1 && has_order) {
+    w.xg_off = 0;
+    w.xg_bytes = round256((size_t)m * (size_t)k * 2);
+  } else if (p.path == 2) {
+    w.xg_off = 0;
+    w.xg_bytes = round256((size_t)m * (size_t)k * 2);
+    w.xs_off = w.xg_bytes;
+    const int64_t piece = group < 128 ? group : 128;   // sums per group part inside a k step
+    w.xs_bytes = round256((size_t)(k / piece) * (size_t)p.mpad * 4);
+  }
+  w.total = w.xg_bytes + w.xs_bytes;
+  return w;
+}
+
+}  // namespace woq
+
+using namespace woq;
+
+extern "C" {
+
+const char* woq_status_str(int32_t status) {
+  switch (status) {
+    case WOQ_OK: return "ok";
+    case WOQ_EINVAL: return "invalid argument (null pointer, negative size or unknown enum)";
+    case WOQ_ESHAPE: return "inconsistent sizes";
+    case WOQ_EGROUP: return "group size invalid for this layout (must be even where packed, >= 1, and divide K)";
+    case WOQ_ENONFINITE: return "non-finite weight";
+    case WOQ_ERANGE: return "code outside 0..15";
+    case WOQ_EWORKSPACE: return "workspace missing or too small";
+    case WOQ_EUNSUPPORTED: return "unsupported (group not in {32,64,128,256} or sizes too large)";
+    case WOQ_EALIGN: return "pointer not aligned as required";
+    case WOQ_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t woq_version(void) { return 100; }
+
+int32_t woq_quantize_groups(const float* w, int64_t n, int64_t k, int32_t group,
+                            int32_t symmetric, uint8_t* q, float* scale, uint8_t* zero,
+                            void* stream) {
+  if (n < 0 || k < 0) return WOQ_EINVAL;
+  if (symmetric != 0 && symmetric != 1) return WOQ_EINVAL;
+  if (group < 1 || (k > 0 && k % group)) return WOQ_EGROUP;
+  if (n * k >= kMaxElems) return WOQ_EUNSUPPORTED;
+  if (n == 0 || k == 0) return WOQ_OK;
+  if (!w || !q || !scale || !zero) return WOQ_EINVAL;
+  if (!aligned(w, 4) || !aligned(scale, 4)) return WOQ_EALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint32_t* flag = nullptr;
+  WOQ_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&flag), sizeof(uint32_t), s));
+  int32_t st = hip_status(hipMemsetAsync(flag, 0, sizeof(uint32_t), s));
+  if (st == WOQ_OK) st = launch_quantize(w, n, k, group, symmetric, q, scale, zero, flag, s);
+  uint32_t hflag = 0;
+  if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(&hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+  if (st == WOQ_OK) st = hip_status(hipStreamSynchronize(s));
+  (void)hipFreeAsync(flag, s);
+  if (st != WOQ_OK) return st;
+  return hflag ? WOQ_ENONFINITE : WOQ_OK;
+}
+
+int32_t woq_pack_uint4(const uint8_t* q, int64_t count, uint8_t* packed, void* stream) {
+  if (count < 0) return WOQ_EINVAL;
+  if (count % 2) return WOQ_ESHAPE;
+  if (count >= kMaxElems) return WOQ_EUNSUPPORTED;
+  if (count == 0) return WOQ_OK;
+  if (!q || !packed) return WOQ_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint32_t* flag = nullptr;
+  WOQ_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&flag), sizeof(uint32_t), s));
+  int32_t st = hip_status(hipMemsetAsync(flag, 0, sizeof(uint32_t), s));
+  if (st == WOQ_OK) st = launch_pack(q, count, packed, flag, s);
+  uint32_t hflag = 0;
+  if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(&hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+  if (st == WOQ_OK) st = hip_status(hipStreamSynchronize(s));
+  (void)hipFreeAsync(flag, s);
+  if (st != WOQ_OK) return st;
+  return hflag ? WOQ_ERANGE : WOQ_OK;
+}
+
+int32_t woq_unpack_uint4(const uint8_t* packed, int64_t count, uint8_t* q, void* stream) {
+  if (count < 0) return WOQ_EINVAL;
+  if (count % 2) return WOQ_ESHAPE;
+  if (count >= kMaxElems) return WOQ_EUNSUPPORTED;
+  if (count == 0) return WOQ_OK;
+  if (!q || !packed) return WOQ_EINVAL;
+  return launch_unpack(packed, count, q, reinterpret_cast<hipStream_t>(stream));
+}
+
+int32_t woq_dequantize_int4_groups(const uint8_t* packed, const float* scale,
+                                   const uint8_t* zero, int64_t n, int64_t k, int32_t group,
+                                   int32_t out_dtype, void* w_hat, void* stream) {
+  if (n < 0 || k < 0) return WOQ_EINVAL;
+  if (out_dtype != WOQ_F32 && out_dtype != WOQ_BF16) return WOQ_EINVAL;
+  if (group < 2 || group % 2 || (k > 0 && k % group)) return WOQ_EGROUP;
+  if (n * k >= kMaxElems) return WOQ_EUNSUPPORTED;
+  if (n == 0 || k == 0) return WOQ_OK;
+  if (!packed || !scale || !zero || !w_hat) return WOQ_EINVAL;
+  if (!aligned(scale, 4) || !aligned(w_hat, out_dtype == WOQ_F32 ? 4 : 2)) return WOQ_EALIGN;
+  return launch_dequantize(packed, scale, zero, n, k, group, out_dtype, w_hat,
+                           reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t woq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group,
+                                  int32_t has_order) {
+  if (check_linear_shape(m, n, k, group) != WOQ_OK) return 0;
+  return linear_workspace_layout(m, n, k, group, has_order != 0).total;
+}
+
+int32_t woq_linear_int4_groups(const void* x_bf16, int64_t m, const uint8_t* packed,
+                               const float* scale, const uint8_t* zero, const float* bias,
+                               const int32_t* order, int64_t n, int64_t k, int32_t group,
+                               int32_t y_dtype, void* y, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  int32_t st = check_linear_shape(m, n, k, group);
+  if (st != WOQ_OK) return st;
+  if (y_dtype != WOQ_F32 && y_dtype != WOQ_BF16) return WOQ_EINVAL;
+  if (m == 0 || n == 0) return WOQ_OK;
+  if (!y) return WOQ_EINVAL;
+  if (!aligned(y, y_dtype == WOQ_F32 ? 4 : 2)) return WOQ_EALIGN;
+  if (bias && !aligned(bias, 4)) return WOQ_EALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (k == 0) return launch_fill_bias(bias, (int32_t)m, (int32_t)n, y_dtype == WOQ_BF16, y, s);
+  if (!x_bf16 || !packed || !scale || !zero) return WOQ_EINVAL;
+  if (!aligned(x_bf16, 16) || !aligned(packed, 16) || !aligned(scale, 4)) return WOQ_EALIGN;
+  const bool has_order = order != nullptr;
+  if (has_order && !aligned(order, 4)) return WOQ_EALIGN;
+  const LinearPlan plan = linear_plan(m, n, k, group, has_order);
+  const LinearWorkspace ws = linear_workspace_layout(m, n, k, group, has_order);
+  if (ws.total > 0) {
+    if (!workspace || workspace_bytes < ws.total) return WOQ_EWORKSPACE;
+    if (!aligned(workspace, 256)) return WOQ_EALIGN;
+  }
+  char* wsb = static_cast<char*>(workspace);
+  LinearArgs a{};
+  a.x = static_cast<const uint16_t*>(x_bf16);
+  a.packed = packed;
+  a.scale = scale;
+  a.zero = zero;
+  a.bias = bias;
+  a.y = y;
+  a.m = (int32_t)m;
+  a.n = (int32_t)n;
+  a.k = (int32_t)k;
+  a.group = group;
+  a.y_bf16 = y_dtype == WOQ_BF16;
+  a.mpad = plan.mpad;
+  if (plan.path == 1) {
+    if (has_order) {
+      uint16_t* xg = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
+      st = launch_prep(a.x, order, a.m, a.k, group, 0, xg, nullptr, m, s);
+      if (st != WOQ_OK) return st;
+      a.x = xg;
+    }
+    return launch_skinny(a, plan, s);
+  }
+  uint16_t* xg = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
+  float* xs = reinterpret_cast<float*>(wsb + ws.xs_off);
+  st = launch_prep(a.x, order, a.m, a.k, group, 1, xg, xs, plan.mpad, s);
+  if (st != WOQ_OK) return st;
+  a.x = xg;
+  a.xs = xs;
+  return launch_gemm(a, plan, s);
+}
+
+int32_t woq_linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, int32_t has_order,
+                        char* buf, size_t len) {
+  if (!buf || len == 0) return WOQ_EINVAL;
+  const int32_t st = check_linear_shape(m, n, k, group);
+  if (st != WOQ_OK) return st;
+  const LinearPlan p = linear_plan(m, n, k, group, has_order != 0);
+  const size_t ws = linear_workspace_layout(m, n, k, group, has_order != 0).total;
+  switch (p.path) {
+    case 0: std::snprintf(buf, len, "path=none"); break;
+    case 3: std::snprintf(buf, len, "path=bias_fill"); break;
+    case 1:
+      std::snprintf(buf, len,
+                    "path=skinny_mfma mt=%d fold_rows=%d ns=%d waves=%d group_blocks=%d grid=%lld "
+                    "prep=%s workspace=%zu",
+                    p.mt, p.fold_rows, p.ns, p.waves, p.gb, (long long)p.grid,
+                    p.prep ? "gather" : "none", ws);
+      break;
+    default:
+      std::snprintf(buf, len,
+                    "path=gemm_mfma tile=%dx%d waves=%d group_blocks=%d grid=%lld prep=%s workspace=%zu",
+                    p.bm, p.bn, p.waves, p.gb, (long long)p.grid,
+                    has_order ? "gather+reorder+groupsum" : "reorder+groupsum", ws);
+  }
+  return WOQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,363 @@
+// Quantize / pack / unpack / dequantize kernels for the Int4GroupLinear layout
+// (linnet docs "Quantization", std.quant table).  None of these is on the
+// linear layer's hot path; they are load-time and inspection kernels, written
+// for exactness first: every rounding decision is the same one the float64
+// rule in the public header describes.
+#include "woq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace woq {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ bool finite_f32(float v) {
+  return (__float_as_uint(v) & 0x7f800000u) != 0x7f800000u;
+}
+
+// Per-group parameters of the asymmetric rule (min/max range, zero point) or
+// of the symmetric rule (absmax, zero fixed at 8).  `den` is the float64
+// divisor of Q*w, `qmax` the code limit Q.
+struct GroupRule {
+  double den;     // range (asymmetric) or absmax (symmetric); 1 for a flat group
+  double zero;    // zero point as a float64 integer
+  float scale;
+  bool flat;
+};
+
+__device__ __forceinline__ GroupRule asym_rule(double mn, double mx) {
+  GroupRule r;
+  const double d = mx - mn;
+  r.flat = (d == 0.0);
+  if (r.flat) {
+    r.den = 1.0;
+    r.scale = 1.0f;
+    r.zero = fmin(fmax(__builtin_rint(-mn), 0.0), 15.0);
+  } else {
+    r.den = d;
+    r.scale = (float)(d / 15.0);
+    r.zero = fmin(fmax(__builtin_rint((-15.0 * mn) / d), 0.0), 15.0);
+  }
+  return r;
+}
+
+__device__ __forceinline__ GroupRule sym_rule(double a) {
+  GroupRule r;
+  r.flat = (a == 0.0);
+  r.den = r.flat ? 1.0 : a;
+  r.scale = r.flat ? 1.0f : (float)(a / 7.0);
+  r.zero = 8.0;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t asym_code(const GroupRule& r, float w) {
+  const double wd = (double)w;
+  const double t = r.flat ? __builtin_rint(wd) : __builtin_rint((15.0 * wd) / r.den);
+  const double q = fmin(fmax(t + r.zero, 0.0), 15.0);
+  return (uint32_t)q;
+}
+
+__device__ __forceinline__ uint32_t sym_code(const GroupRule& r, float w) {
+  if (r.flat) return 8u;
+  const double c = fmin(fmax(__builtin_rint((7.0 * (double)w) / r.den), -7.0), 7.0);
+  return (uint32_t)(int)(c + 8.0);
+}
+
+// L lanes cooperate on one group of 4*L consecutive weights (float4 per lane).
+template <int L>
+__global__ __launch_bounds__(kThreads) void quantize_coop_kernel(
+    const float* __restrict__ w, int64_t ngroups, int32_t symmetric, int32_t q_aligned,
+    uint8_t* __restrict__ q, float* __restrict__ scale, uint8_t* __restrict__ zero,
+    uint32_t* __restrict__ flag) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < ngroups * L; t += stride) {
+    const int64_t gi = t / L;
+    const int li = (int)(t % L);
+    const int64_t base = gi * (4 * L) + 4 * li;
+    const float4 v = *reinterpret_cast<const float4*>(w + base);
+    int bad = (finite_f32(v.x) && finite_f32(v.y) && finite_f32(v.z) && finite_f32(v.w)) ? 0 : 1;
+    float lo = fminf(fminf(v.x, v.y), fminf(v.z, v.w));
+    float hi = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+    float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+    for (int off = L / 2; off > 0; off >>= 1) {
+      lo = fminf(lo, __shfl_xor(lo, off, L));
+      hi = fmaxf(hi, __shfl_xor(hi, off, L));
+      am = fmaxf(am, __shfl_xor(am, off, L));
+      bad |= __shfl_xor(bad, off, L);   // every lane takes part in every shuffle
+    }
+    if (bad) {
+      if (li == 0) atomicOr(flag, 1u);
+      continue;
+    }
+    const GroupRule r = symmetric ? sym_rule((double)am) : asym_rule((double)lo, (double)hi);
+    uint32_t c0, c1, c2, c3;
+    if (symmetric) {
+      c0 = sym_code(r, v.x); c1 = sym_code(r, v.y); c2 = sym_code(r, v.z); c3 = sym_code(r, v.w);
+    } else {
+      c0 = asym_code(r, v.x); c1 = asym_code(r, v.y); c2 = asym_code(r, v.z); c3 = asym_code(r, v.w);
+    }
+    if (q_aligned) {
+      *reinterpret_cast<uint32_t*>(q + base) = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    } else {
+      q[base] = (uint8_t)c0; q[base + 1] = (uint8_t)c1; q[base + 2] = (uint8_t)c2; q[base + 3] = (uint8_t)c3;
+    }
+    if (li == 0) {
+      scale[gi] = r.scale;
+      zero[gi] = (uint8_t)r.zero;
+    }
+  }
+}
+
+// One thread per group: any group size, any alignment.
+__global__ __launch_bounds__(kThreads) void quantize_thread_kernel(
+    const float* __restrict__ w, int64_t ngroups, int32_t group, int32_t symmetric,
+    uint8_t* __restrict__ q, float* __restrict__ scale, uint8_t* __restrict__ zero,
+    uint32_t* __restrict__ flag) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t gi = (int64_t)blockIdx.x * kThreads + threadIdx.x; gi < ngroups; gi += stride) {
+    const float* g = w + gi * group;
+    bool bad = false;
+    float lo = g[0], hi = g[0], am = 0.0f;
+    for (int e = 0; e < group; ++e) {
+      const float v = g[e];
+      bad = bad || !finite_f32(v);
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
+      am = fmaxf(am, fabsf(v));
+    }
+    if (bad) {
+      atomicOr(flag, 1u);
+      continue;
+    }
+    const GroupRule r = symmetric ? sym_rule((double)am) : asym_rule((double)lo, (double)hi);
+    uint8_t* qo = q + gi * group;
+    for (int e = 0; e < group; ++e)
+      qo[e] = (uint8_t)(symmetric ? sym_code(r, g[e]) : asym_code(r, g[e]));
+    scale[gi] = r.scale;
+    zero[gi] = (uint8_t)r.zero;
+  }
+}
+
+// 16 codes -> 8 bytes per iteration; a code above 15 sets the flag.
+__global__ __launch_bounds__(kThreads) void pack_vec_kernel(const uint4* __restrict__ q, int64_t nvec,
+                                                            uint2* __restrict__ packed,
+                                                            uint32_t* __restrict__ flag) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  bool bad = false;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride) {
+    const uint4 v = q[i];
+    bad = bad || ((v.x | v.y | v.z | v.w) & 0xF0F0F0F0u) != 0u;
+    // byte j of a 4-code word holds code j; fold pairs (2i, 2i+1) into one byte
+    auto fold = [](uint32_t a) -> uint32_t {   // 4 codes -> 2 packed bytes in the low 16 bits
+      const uint32_t even = a & 0x000F000Fu;           // codes 0 and 2
+      const uint32_t odd = (a >> 4) & 0x00F000F0u;     // codes 1 and 3, moved to the high nibble
+      const uint32_t b = even | odd;                   // byte 0 = c0|c1<<4, byte 2 = c2|c3<<4
+      return (b & 0xFFu) | ((b >> 8) & 0xFF00u);
+    };
+    uint2 o;
+    o.x = fold(v.x) | (fold(v.y) << 16);
+    o.y = fold(v.z) | (fold(v.w) << 16);
+    packed[i] = o;
+  }
+  if (bad) atomicOr(flag, 1u);
+}
+
+__global__ __launch_bounds__(kThreads) void pack_byte_kernel(const uint8_t* __restrict__ q, int64_t nbytes,
+                                                             uint8_t* __restrict__ packed,
+                                                             uint32_t* __restrict__ flag) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  bool bad = false;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nbytes; i += stride) {
+    const uint32_t lo = q[2 * i], hi = q[2 * i + 1];
+    bad = bad || lo > 15u || hi > 15u;
+    packed[i] = (uint8_t)((lo & 15u) | ((hi & 15u) << 4));
+  }
+  if (bad) atomicOr(flag, 1u);
+}
+
+// 8 packed bytes -> 16 codes per iteration.
+__global__ __launch_bounds__(kThreads) void unpack_vec_kernel(const uint2* __restrict__ packed, int64_t nvec,
+                                                              uint4* __restrict__ q) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride) {
+    const uint2 p = packed[i];
+    auto spread = [](uint32_t two) -> uint32_t {   // 2 packed bytes (low 16 bits) -> 4 codes
+      const uint32_t b = (two & 0xFFu) | ((two & 0xFF00u) << 8);   // bytes at positions 0 and 2
+      return (b & 0x000F000Fu) | ((b << 4) & 0x0F000F00u);
+    };
+    uint4 o;
+    o.x = spread(p.x & 0xFFFFu);
+    o.y = spread(p.x >> 16);
+    o.z = spread(p.y & 0xFFFFu);
+    o.w = spread(p.y >> 16);
+    q[i] = o;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void unpack_byte_kernel(const uint8_t* __restrict__ packed, int64_t nbytes,
+                                                               uint8_t* __restrict__ q) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nbytes; i += stride) {
+    const uint32_t b = packed[i];
+    q[2 * i] = (uint8_t)(b & 15u);
+    q[2 * i + 1] = (uint8_t)(b >> 4);
+  }
+}
+
+__device__ __forceinline__ uint16_t bf16_bits_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);   // v_cvt_pk_bf16_f32: round to nearest even
+}
+
+__device__ __forceinline__ float dq(uint32_t code, float z, float s) {
+  return ((float)code - z) * s;   // (q - zero) is exact; one float32 rounding of the product
+}
+
+// 4 packed bytes (8 codes of one group) per iteration; group % 8 == 0.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void dequant_vec_kernel(
+    const uint32_t* __restrict__ packed, const float* __restrict__ scale,
+    const uint8_t* __restrict__ zero, int64_t nwords, int64_t words_per_row, int32_t group,
+    void* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t groups_per_row = words_per_row * 8 / group;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nwords; i += stride) {
+    const int64_t row = i / words_per_row;
+    const int64_t col = (i % words_per_row) * 8;            // first k of this word
+    const int64_t gi = row * groups_per_row + col / group;
+    const float s = scale[gi];
+    const float z = (float)zero[gi];
+    const uint32_t d = packed[i];
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = dq((d >> (4 * e)) & 15u, z, s);
+    if (BF16) {
+      uint4 o;
+      o.x = bf16_bits_rne(v[0]) | ((uint32_t)bf16_bits_rne(v[1]) << 16);
+      o.y = bf16_bits_rne(v[2]) | ((uint32_t)bf16_bits_rne(v[3]) << 16);
+      o.z = bf16_bits_rne(v[4]) | ((uint32_t)bf16_bits_rne(v[5]) << 16);
+      o.w = bf16_bits_rne(v[6]) | ((uint32_t)bf16_bits_rne(v[7]) << 16);
+      reinterpret_cast<uint4*>(out)[i] = o;
+    } else {
+      float4* o = reinterpret_cast<float4*>(out) + 2 * i;
+      o[0] = make_float4(v[0], v[1], v[2], v[3]);
+      o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void dequant_byte_kernel(
+    const uint8_t* __restrict__ packed, const float* __restrict__ scale,
+    const uint8_t* __restrict__ zero, int64_t nbytes, int64_t bytes_per_row, int32_t group,
+    void* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t groups_per_row = bytes_per_row * 2 / group;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nbytes; i += stride) {
+    const int64_t row = i / bytes_per_row;
+    const int64_t col = (i % bytes_per_row) * 2;
+    const int64_t gi = row * groups_per_row + col / group;
+    const float s = scale[gi];
+    const float z = (float)zero[gi];
+    const uint32_t b = packed[i];
+    const float v0 = dq(b & 15u, z, s), v1 = dq(b >> 4, z, s);
+    if (BF16) {
+      uint16_t* o = reinterpret_cast<uint16_t*>(out);
+      o[2 * i] = bf16_bits_rne(v0);
+      o[2 * i + 1] = bf16_bits_rne(v1);
+    } else {
+      float* o = reinterpret_cast<float*>(out);
+      o[2 * i] = v0;
+      o[2 * i + 1] = v1;
+    }
+  }
+}
+
+unsigned grid_for(int64_t items) {
+  const int64_t blocks = (items + kThreads - 1) / kThreads;
+  return (unsigned)(blocks < 1 ? 1 : (blocks > 65536 ? 65536 : blocks));
+}
+
+}  // namespace
+
+int32_t launch_quantize(const float* w, int64_t n, int64_t k, int32_t group, int32_t symmetric,
+                        uint8_t* q, float* scale, uint8_t* zero, uint32_t* flag,
+                        hipStream_t stream) {
+  const int64_t ngroups = n * (k / group);
+  if (ngroups == 0) return WOQ_OK;
+  const bool coop = (group % 4 == 0) && group >= 4 && group <= 256 &&
+                    ((group / 4) & (group / 4 - 1)) == 0 && aligned(w, 16);
+  if (coop) {
+    const int L = group / 4;
+    const int32_t qa = aligned(q, 4) ? 1 : 0;
+    const unsigned grid = grid_for(ngroups * L);
+#define WOQ_Q(LL) \
+    case LL: hipLaunchKernelGGL(quantize_coop_kernel<LL>, dim3(grid), dim3(kThreads), 0, stream, \
+                                w, ngroups, symmetric, qa, q, scale, zero, flag); break;
+    switch (L) {
+      WOQ_Q(1) WOQ_Q(2) WOQ_Q(4) WOQ_Q(8) WOQ_Q(16) WOQ_Q(32) WOQ_Q(64)
+      default: return WOQ_EUNSUPPORTED;
+    }
+#undef WOQ_Q
+  } else {
+    hipLaunchKernelGGL(quantize_thread_kernel, dim3(grid_for(ngroups)), dim3(kThreads), 0, stream,
+                       w, ngroups, group, symmetric, q, scale, zero, flag);
+  }
+  return hip_status(hipGetLastError());
+}
+
+int32_t launch_pack(const uint8_t* q, int64_t count, uint8_t* packed, uint32_t* flag,
+                    hipStream_t stream) {
+  if (count == 0) return WOQ_OK;
+  if (count % 16 == 0 && aligned(q, 16) && aligned(packed, 8)) {
+    const int64_t nvec = count / 16;
+    hipLaunchKernelGGL(pack_vec_kernel, dim3(grid_for(nvec)), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const uint4*>(q), nvec, reinterpret_cast<uint2*>(packed), flag);
+  } else {
+    hipLaunchKernelGGL(pack_byte_kernel, dim3(grid_for(count / 2)), dim3(kThreads), 0, stream,
+                       q, count / 2, packed, flag);
+  }
+  return hip_status(hipGetLastError());
+}
+
+int32_t launch_unpack(const uint8_t* packed, int64_t count, uint8_t* q, hipStream_t stream) {
+  if (count == 0) return WOQ_OK;
+  if (count % 16 == 0 && aligned(q, 16) && aligned(packed, 8)) {
+    const int64_t nvec = count / 16;
+    hipLaunchKernelGGL(unpack_vec_kernel, dim3(grid_for(nvec)), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const uint2*>(packed), nvec, reinterpret_cast<uint4*>(q));
+  } else {
+    hipLaunchKernelGGL(unpack_byte_kernel, dim3(grid_for(count / 2)), dim3(kThreads), 0, stream,
+                       packed, count / 2, q);
+  }
+  return hip_status(hipGetLastError());
+}
+
+int32_t launch_dequantize(const uint8_t* packed, const float* scale, const uint8_t* zero,
+                          int64_t n, int64_t k, int32_t group, int32_t out_dtype, void* w_hat,
+                          hipStream_t stream) {
+  const int64_t nbytes = n * (k / 2);
+  if (nbytes == 0) return WOQ_OK;
+  const bool bf16 = out_dtype == WOQ_BF16;
+  const bool vec = group % 8 == 0 && aligned(packed, 4) && aligned(w_hat, 16);
+  if (vec) {
+    const int64_t nwords = nbytes / 4, wpr = k / 8;
+    if (bf16)
+      hipLaunchKernelGGL(dequant_vec_kernel<true>, dim3(grid_for(nwords)), dim3(kThreads), 0, stream,
+                         reinterpret_cast<const uint32_t*>(packed), scale, zero, nwords, wpr, group, w_hat);
+    else
+      hipLaunchKernelGGL(dequant_vec_kernel<false>, dim3(grid_for(nwords)), dim3(kThreads), 0, stream,
+                         reinterpret_cast<const uint32_t*>(packed), scale, zero, nwords, wpr, group, w_hat);
+  } else {
+    if (bf16)
+      hipLaunchKernelGGL(dequant_byte_kernel<true>, dim3(grid_for(nbytes)), dim3(kThreads), 0, stream,
+                         packed, scale, zero, nbytes, k / 2, group, w_hat);
+    else
+      hipLaunchKernelGGL(dequant_byte_kernel<false>, dim3(grid_for(nbytes)), dim3(kThreads), 0, stream,
+                         packed, scale, zero, nbytes, k / 2, group, w_hat);
+  }
+  return hip_status(hipGetLastError());
+}
+
+}  // namespace woq

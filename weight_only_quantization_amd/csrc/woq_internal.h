@@ -1,0 +1,87 @@
+// Internal declarations shared by the translation units of libwoq.so.
+// Not part of the public ABI (that is include/woq.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/woq.h"
+
+namespace woq {
+
+// ---------------------------------------------------------------------------
+// Host-side helpers
+// ---------------------------------------------------------------------------
+
+inline int32_t hip_status(hipError_t e) { return e == hipSuccess ? WOQ_OK : WOQ_EHIP; }
+
+#define WOQ_HIP_TRY(expr)                         \
+  do {                                            \
+    hipError_t woq_e_ = (expr);                   \
+    if (woq_e_ != hipSuccess) return WOQ_EHIP;    \
+  } while (0)
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Workspace carve-up of the linear layer (all offsets 256-byte aligned).
+struct LinearWorkspace {
+  size_t xg_off = 0, xg_bytes = 0;   // gathered and/or pair-permuted activations, bf16 [M, K]
+  size_t xs_off = 0, xs_bytes = 0;   // per-group activation sums, f32 [K/G][Mpad]
+  size_t total = 0;
+};
+
+// Which kernel family runs a linear call, and with what launch shape.
+struct LinearPlan {
+  int path = 0;          // 0 = none (empty), 1 = skinny MFMA (m <= 64), 2 = tiled MFMA GEMM
+  int mt = 1;            // 16-row activation tiles held per wave (skinny path)
+  int fold_rows = 4;     // accumulator rows folded per tile (1 when m == 1)
+  int ns = 1;            // 16-column weight tiles per workgroup (skinny path)
+  int waves = 4;         // waves per workgroup
+  int gb = 4;            // 32-wide k blocks per quantization group inside a 128-wide k step (1, 2, 4)
+  int prep = 0;          // 1 = an input pre-pass kernel runs first
+  int64_t grid = 0;      // workgroups
+  int bm = 0, bn = 0;    // tile of the GEMM path
+  int64_t mpad = 0;      // rows of the per-group sum table (GEMM path)
+};
+
+LinearWorkspace linear_workspace_layout(int64_t m, int64_t n, int64_t k, int32_t group,
+                                        bool has_order);
+LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_order);
+
+// ---------------------------------------------------------------------------
+// Launchers (defined next to their kernels).  All enqueue on `stream` and
+// return a woq_status.  Arguments are already validated.
+// ---------------------------------------------------------------------------
+
+int32_t launch_quantize(const float* w, int64_t n, int64_t k, int32_t group, int32_t symmetric,
+                        uint8_t* q, float* scale, uint8_t* zero, uint32_t* flag,
+                        hipStream_t stream);
+int32_t launch_pack(const uint8_t* q, int64_t count, uint8_t* packed, uint32_t* flag,
+                    hipStream_t stream);
+int32_t launch_unpack(const uint8_t* packed, int64_t count, uint8_t* q, hipStream_t stream);
+int32_t launch_dequantize(const uint8_t* packed, const float* scale, const uint8_t* zero,
+                          int64_t n, int64_t k, int32_t group, int32_t out_dtype, void* w_hat,
+                          hipStream_t stream);
+
+struct LinearArgs {
+  const uint16_t* x;       // bf16 bits [M, K] (possibly the gathered copy)
+  const uint8_t* packed;   // [N, K/2]
+  const float* scale;      // [N, K/G]
+  const uint8_t* zero;     // [N, K/G]
+  const float* bias;       // [N] or null
+  void* y;                 // [M, N]
+  const float* xs;         // per-group sums [K/G][mpad] (GEMM path)
+  int32_t m, n, k, group;
+  int32_t y_bf16;
+  int64_t mpad;
+};
+
+int32_t launch_prep(const uint16_t* x, const int32_t* order, int32_t m, int32_t k, int32_t group,
+                    int32_t permute, uint16_t* xg, float* xs, int64_t mpad, hipStream_t stream);
+int32_t launch_skinny(const LinearArgs& a, const LinearPlan& p, hipStream_t stream);
+int32_t launch_gemm(const LinearArgs& a, const LinearPlan& p, hipStream_t stream);
+int32_t launch_fill_bias(const float* bias, int32_t m, int32_t n, int32_t y_bf16, void* y,
+                         hipStream_t stream);
+
+}  // namespace woq
