@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the group-wise 4-bit linear layer on one MI355X.
+
+One step = the quantized linears of one Llama-3-8B decode token: 32 layers x
+(q, k, v, o, gate, up, down) = 224 linear_int4_groups calls at M=1, group 128,
+bf16 activations, f32 bias on every q projection.  Every layer has its own
+weights (3.76 GB packed + scales + zeros per step), so each step streams the
+weights from HBM rather than from the 256 MB last-level cache.  The step is
+captured once in a HIP graph and replayed.
+
+Printed JSON line (rank 0):
+  value        effective weight GB/s over the whole step (packed + scale + zero
+               bytes / wall time of the replayed graph, launch gaps included)
+  roofline     the skinny decode kernel alone: algorithmic bytes per launch /
+               its average launch duration (HIP events around each launch)
+  prefill      TFLOP/s of the M=2048 GEMM path on both prefill shapes
+  cpu_baseline the CPU oracle's linear on a bounded sample of the same layer
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+METRIC = "int4-g128 linear: effective weight GB/s (% HBM peak) at M=1; TFLOP/s at M=2048"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+GROUP = 128
+TRAFFIC_SUMMARY = ROOT / "profiles" / "traffic_skinny_decode_m1_g128.txt"
+KERNEL_SOURCES = ["linear_skinny.hip", "mfma_common.h"]
+
+
+def weight_bytes(n: int, k: int, group: int = GROUP) -> int:
+    """Packed codes + float32 scale + uint8 zero of an [n, k] weight."""
+    return n * k // 2 + (n * k // group) * 5
+
+
+def algorithmic_bytes(m: int, n: int, k: int, has_bias: bool, group: int = GROUP) -> int:
+    """Bytes a linear call must move at least once: weights, x, y (bf16), bias."""
+    return weight_bytes(n, k, group) + m * k * 2 + m * n * 2 + (n * 4 if has_bias else 0)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update((ROOT / "weight_only_quantization_amd" / "csrc" / name).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary.
+
+    Returns None unless the summary was taken on the current kernel sources.
+    """
+    if not TRAFFIC_SUMMARY.exists():
+        return None
+    fields = {}
+    for line in TRAFFIC_SUMMARY.read_text().splitlines():
+        if ":" in line and not line.startswith("#"):
+            key, _, val = line.partition(":")
+            fields[key.strip()] = val.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def build_decode_step(torch, woq, layers: int, seed: int = 2024):
+    """Seeded weights and activations of `layers` Llama-3-8B layers on the GPU."""
+    from workloads import LLAMA3_8B_LAYER
+
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    calls = []
+    for layer in range(layers):
+        for idx, (role, n, k, has_bias) in enumerate(LLAMA3_8B_LAYER):
+            gen.manual_seed(seed + 100 * layer + idx)
+            w = torch.randn((n, k), generator=gen, device=dev, dtype=torch.float32).mul_(0.02)
+            q, s, z = woq.quantize_groups(w, GROUP)
+            packed = woq.pack_uint4(q)
+            del w, q
+            x = torch.randn((1, k), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            b = (torch.randn((n,), generator=gen, device=dev, dtype=torch.float32).mul_(0.01)
+                 if has_bias else None)
+            y = torch.empty((1, n), dtype=torch.bfloat16, device=dev)
+            calls.append(dict(role=role, n=n, k=k, x=x, packed=packed, scale=s, zero=z, bias=b, y=y))
+    torch.cuda.synchronize()
+    return calls
+
+
+def run_calls(woq, calls):
+    for c in calls:
+        woq.linear_int4_groups(c["x"], c["packed"], c["scale"], c["zero"], bias=c["bias"],
+                               group=GROUP, out=c["y"], out_dtype=c["y"].dtype)
+
+
+def per_launch_durations(torch, woq, calls, reps: int = 2):
+    """Device time of each launch: events around every call, queued behind a spin kernel
+    so the host enqueues the whole step before the GPU reaches it."""
+    durs = []
+    for _ in range(reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in calls]
+        torch.cuda._sleep(int(2.4e9 * 0.05))        # ~50 ms of queued GPU spin
+        for c, (e0, e1) in zip(calls, evs):
+            e0.record()
+            woq.linear_int4_groups(c["x"], c["packed"], c["scale"], c["zero"], bias=c["bias"],
+                                   group=GROUP, out=c["y"], out_dtype=c["y"].dtype)
+            e1.record()
+        torch.cuda.synchronize()
+        durs.append([e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs])   # seconds
+    # per launch, the best of the repetitions
+    return [min(r[i] for r in durs) for i in range(len(calls))]
+
+
+def measure_prefill(torch, woq, reps: int = 5):
+    from workloads import PREFILL
+
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    out = []
+    for case in PREFILL:
+        gen.manual_seed(case.seed_w)
+        w = torch.randn((case.n, case.k), generator=gen, device=dev).mul_(0.02)
+        q, s, z = woq.quantize_groups(w, case.group)
+        packed = woq.pack_uint4(q)
+        del w, q
+        x = torch.randn((case.m, case.k), generator=gen, device=dev).to(torch.bfloat16)
+        y = torch.empty((case.m, case.n), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(woq.linear_workspace_bytes(case.m, case.n, case.k, case.group, False),
+                         dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            woq.linear_int4_groups(x, packed, s, z, group=case.group, out=y, workspace=ws)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(int(2.4e9 * 0.002))
+            e0.record()
+            woq.linear_int4_groups(x, packed, s, z, group=case.group, out=y, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        t = statistics.median(times)
+        flops = 2.0 * case.m * case.n * case.k
+        out.append(dict(shape=f"{case.m}x{case.n}x{case.k}", ms=round(t * 1e3, 4),
+                        tflops=round(flops / t / 1e12, 1)))
+    tot_flops = sum(2.0 * c.m * c.n * c.k for c in PREFILL)
+    tot_t = sum(o["ms"] for o in out) * 1e-3
+    tf = tot_flops / tot_t / 1e12
+    return dict(metric="TFLOP/s at M=2048 (both prefill shapes, pre-pass included)",
+                value=round(tf, 1), peak=BF16_PEAK_TFLOPS, frac=round(tf / BF16_PEAK_TFLOPS, 4),
+                per_shape=out, plan=woq.linear_plan(2048, 14336, 4096, GROUP))
+
+
+def cpu_baseline(min_seconds: float = 10.0, max_passes: int = 8):
+    """The CPU oracle's linear over one Llama-3-8B layer's seven M=1 linears.
+
+    Weights are drawn directly in the Int4GroupLinear layout (the oracle's
+    quantizer is not timed); passes over the layer repeat until min_seconds.
+    """
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                            if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = 1
+    layer = []
+    for idx, (role, n, k, has_bias) in enumerate(workloads.LLAMA3_8B_LAYER):
+        p, s, z = workloads.packed_weights(n, k, GROUP, seed=900 + idx)
+        x = workloads.activations_bf16(1, k, seed=950 + idx)
+        b = workloads.bias(n, seed=990) if has_bias else None
+        layer.append((n, k, p, s, z, x, b))
+    bytes_done, passes = 0, 0
+    t0 = time.perf_counter()
+    while passes < max_passes:
+        for (n, k, p, s, z, x, b) in layer:
+            oracle.linear_int4_groups(x, p, s, z, n, k, GROUP, bias=b)
+            bytes_done += weight_bytes(n, k)
+        passes += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=round(bytes_done / dt / 1e9, 4), unit="GB/s", cores=int(blas_threads),
+                kind="oracle",
+                sample=f"{passes} pass(es) of one Llama-3-8B layer's 7 linears at M=1, group 128 "
+                       f"({bytes_done / 1e9:.2f} GB of weights, {dt:.1f} s; numpy float64; "
+                       f"BLAS threads={blas_threads}, affinity cores={len(os.sched_getaffinity(0))})")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import weight_only_quantization_amd as woq
+
+    woq.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    calls = build_decode_step(torch, woq, args.layers)
+    wbytes = sum(weight_bytes(c["n"], c["k"]) for c in calls)
+    abytes = [algorithmic_bytes(1, c["n"], c["k"], c["bias"] is not None) for c in calls]
+
+    # Warm up eagerly (also on a side stream, as graph capture requires), then capture.
+    run_calls(woq, calls)
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run_calls(woq, calls)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run_calls(woq, calls)
+    step = graph.replay if graph is not None else (lambda: run_calls(woq, calls))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = e0.elapsed_time(e1) * 1e-3
+    ms_per_step = elapsed / args.steps * 1e3
+    value = wbytes * args.steps / elapsed / 1e9
+
+    durs = per_launch_durations(torch, woq, calls)
+    achieved = sum(abytes) / sum(durs) / 1e9
+    traffic = read_traffic()
+    big = [i for i, c in enumerate(calls) if c["n"] * c["k"] == 14336 * 4096]
+    roofline = dict(
+        bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+        kernel="woq::skinny_kernel<MT=1,FR=1,NS=1,GB=4,PF=4> (every launch of the step)",
+        launches=len(calls), avg_launch_us=round(sum(durs) / len(durs) * 1e6, 3),
+        algorithmic_bytes_per_launch=round(sum(abytes) / len(abytes)),
+        traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
+        gate_up_down_14336x4096_GBps=round(sum(abytes[i] for i in big) / sum(durs[i] for i in big) / 1e9, 1),
+        plans={f"{c['n']}x{c['k']}": woq.linear_plan(1, c["n"], c["k"], GROUP)
+               for c in calls[:len(calls) // args.layers]},
+    )
+
+    if args.copy_calibration_mib:
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    prefill = None if args.no_prefill else measure_prefill(torch, woq)
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+
+    line = dict(
+        metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=round(ms_per_step, 4), higher_is_better=True,
+        scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+        config=dict(workload="Llama-3-8B decode linears at M=1: 32 layers x (q,k,v,o,gate,up,down), "
+                             "int4 group 128, bf16 x, f32 bias on q, bf16 y",
+                    m=1, group=GROUP, layers=args.layers, launches_per_step=len(calls),
+                    weight_bytes_per_step=wbytes, hbm_peak_frac=round(value / HBM_PEAK_GBS, 4),
+                    graph=graph is not None, accumulate="f32",
+                    tokens_per_s_linears_only=round(1.0 / (ms_per_step * 1e-3), 1) if args.layers == 32 else None),
+        roofline=roofline, prefill=prefill, cpu_baseline=cpu,
+    )
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

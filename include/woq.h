@@ -138,8 +138,9 @@ size_t woq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group
  * Arguments:
  *   x_bf16 [m, k] bfloat16 (device, 16-byte aligned);
  *   packed [n, k/2] uint8 (device, 16-byte aligned); scale [n, k/group] float32
- *   (device, 4-byte aligned); zero [n, k/group] uint8 (device);
- *   bias [n] float32 (device) or NULL; order [k] int32 (device) or NULL - every
+ *   (device, 16-byte aligned); zero [n, k/group] uint8 (device, 16-byte aligned);
+ *   bias [n] float32 (device) or NULL; order [k] int32 (device, 16-byte
+ *   aligned) or NULL - every
  *   entry must lie in [0, k) (entries outside are clamped into range, never read
  *   out of bounds; the result is then unspecified);
  *   group in {32, 64, 128, 256}, dividing k;

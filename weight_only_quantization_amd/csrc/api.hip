@@ -33,7 +33,7 @@ bool skinny_override(int* ns, int* waves) {
     cached = 0;
     if (const char* e = std::getenv("WOQ_SKINNY")) {
       int a = 0, b = 0;
-      if (std::sscanf(e, "%d,%d", &a, &b) == 2 && (a == 1 || a == 2) && b >= 1 && b <= 16) {
+      if (std::sscanf(e, "%d,%d", &a, &b) == 2 && (a == 1 || a == 2) && b >= 1 && b <= 8) {
         c_ns = a;
         c_w = b;
         cached = 1;
@@ -63,21 +63,24 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
     return p;
   }
   p.gb = group >= 128 ? 4 : group / 32;
-  if (m <= 16) {
+  const int64_t nsub = (n + 15) / 16;
+  const int skinny_ns = (nsub >= 2048 && p.gb >= 2) ? 2 : 1;
+  if (m <= 16 && k < ((int64_t)1 << 26) &&
+      skinny_lds_bytes(m, k, group, 8, skinny_ns) <= kSkinnyLdsLimit) {
     p.path = 1;
     p.mt = 1;
     p.fold_rows = m == 1 ? 1 : 4;
     p.prep = has_order ? 1 : 0;
-    const int64_t nsub = (n + 15) / 16;
     const int64_t nsteps = (k + 127) / 128;
-    int ns = (nsub >= 2048 && p.gb >= 2) ? 2 : 1;
+    int ns = skinny_ns;
     int64_t tiles = (nsub + ns - 1) / ns;
     int64_t want = 4096 / (tiles > 0 ? tiles : 1);
     int waves = pow2_floor(want < 1 ? 1 : want);
-    if (waves > 16) waves = 16;
+    if (waves > 8) waves = 8;
     while (waves > 1 && waves > nsteps) waves /= 2;
     int o_ns, o_w;
-    if (skinny_override(&o_ns, &o_w) && (o_ns == 1 || p.gb >= 2)) {
+    if (skinny_override(&o_ns, &o_w) && (o_ns == 1 || p.gb >= 2) &&
+        skinny_lds_bytes(m, k, group, o_w, o_ns) <= kSkinnyLdsLimit) {
       ns = o_ns;
       waves = o_w;
       tiles = (nsub + ns - 1) / ns;
@@ -225,9 +228,10 @@ int32_t woq_linear_int4_groups(const void* x_bf16, int64_t m, const uint8_t* pac
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (k == 0) return launch_fill_bias(bias, (int32_t)m, (int32_t)n, y_dtype == WOQ_BF16, y, s);
   if (!x_bf16 || !packed || !scale || !zero) return WOQ_EINVAL;
-  if (!aligned(x_bf16, 16) || !aligned(packed, 16) || !aligned(scale, 4)) return WOQ_EALIGN;
+  if (!aligned(x_bf16, 16) || !aligned(packed, 16) || !aligned(scale, 16) || !aligned(zero, 16))
+    return WOQ_EALIGN;
   const bool has_order = order != nullptr;
-  if (has_order && !aligned(order, 4)) return WOQ_EALIGN;
+  if (has_order && !aligned(order, 16)) return WOQ_EALIGN;
   const LinearPlan plan = linear_plan(m, n, k, group, has_order);
   const LinearWorkspace ws = linear_workspace_layout(m, n, k, group, has_order);
   if (ws.total > 0) {

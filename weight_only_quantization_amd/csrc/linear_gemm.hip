@@ -23,51 +23,51 @@ namespace {
 constexpr int kStepK = 128;
 constexpr int kBlockK = 32;
 
-// One thread per (row, piece): deterministic sums.
+// One thread per 8 consecutive inputs of a row (16 bytes).  The lanes of one
+// piece (piece/8 of them, consecutive) add their partial sums in a fixed
+// shuffle tree, so the sums are the same on every run.  Rows from m to mpad
+// only get zero sums.
+template <int LP>   // lanes per piece: piece / 8
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ x,
                                                    const int32_t* __restrict__ order, int32_t m,
-                                                   int32_t k, int32_t piece, int32_t permute,
+                                                   int32_t k, int32_t permute,
                                                    uint16_t* __restrict__ xg, float* __restrict__ xs,
                                                    int64_t mpad) {
-  const int npieces = k / piece;
-  const int64_t total = mpad * npieces;
+  const int cpr = k / 8;                       // chunks per row
+  const int npieces = cpr / LP;
+  const int64_t total = mpad * cpr;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
-    const int64_t row = t / npieces;
-    const int g = (int)(t % npieces);
-    if (row >= m) {
-      if (xs) xs[(int64_t)g * mpad + row] = 0.f;
-      continue;
+    const int64_t row = t / cpr;
+    const int col = (int)(t % cpr);
+    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+    if (row < m) {
+      const uint16_t* xr = x + row * k;
+      if (order) {
+        const u32x4_t i0 = load16(order + col * 8), i1 = load16(order + col * 8 + 4);
+        const int32_t idx[8] = {(int32_t)i0[0], (int32_t)i0[1], (int32_t)i0[2], (int32_t)i0[3],
+                                (int32_t)i1[0], (int32_t)i1[1], (int32_t)i1[2], (int32_t)i1[3]};
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int src = idx[e] < 0 ? 0 : (idx[e] >= k ? k - 1 : idx[e]);   // clamp bad indices
+          h[e] = xr[src];
+        }
+        v = u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      } else {
+        v = load16(xr + col * 8);
+      }
     }
-    const uint16_t* xr = x + row * k;
     float sum = 0.f;
-    for (int b = g * piece; b < (g + 1) * piece; b += 8) {
-      uint16_t v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        int src = b + e;
-        if (order) {
-          src = order[b + e];
-          src = src < 0 ? 0 : (src >= k ? k - 1 : src);   // out-of-range indices are clamped
-        }
-        v[e] = xr[src];
-        sum += __builtin_bit_cast(float, (uint32_t)v[e] << 16);
-      }
-      if (xg) {
-        uint16_t* o = xg + row * k + b;
-        if (permute) {
+    for (int e = 0; e < 4; ++e)
+      sum += __builtin_bit_cast(float, v[e] << 16) + __builtin_bit_cast(float, v[e] & 0xFFFF0000u);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o[2 * e] = v[e];
-            o[2 * e + 1] = v[e + 4];
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = v[e];
-        }
-      }
-    }
-    if (xs) xs[(int64_t)g * mpad + row] = sum;
+    for (int off = 1; off < LP; off <<= 1) sum += __shfl_xor(sum, off, LP);
+    if (row < m && xg)
+      *reinterpret_cast<u32x4_t*>(xg + row * k + col * 8) =
+          permute ? __builtin_bit_cast(u32x4_t, pair_order(v)) : v;
+    if (xs && (col % LP) == 0) xs[(int64_t)(col / LP) * mpad + row] = sum;
   }
 }
 
@@ -178,6 +178,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
 
   // The weights of this step leave gb through the transpose; the next step's
   // loads are issued into gb right after, to land during this step's MFMAs.
+  const uint32_t nib_offset = vgpr_copy(kBf16Offset2);
   auto compute = [&](int stage, int step) {
     const int k0 = step * kStepK;
     const int nb = min(4, (K - k0) / kBlockK);
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
         for (int mt = 0; mt < 4; ++mt) cg[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < GB; ++e) {
-          const bf16x8_t bf = unpack_codes(dw[nt][pc * GB + e]);
+          const bf16x8_t bf = unpack_codes(dw[nt][pc * GB + e], kNibPairMask, nib_offset);
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) cg[mt] = mfma_bf16(af[mt][e], bf, cg[mt]);
         }
@@ -281,12 +282,16 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
 int32_t launch_prep(const uint16_t* x, const int32_t* order, int32_t m, int32_t k, int32_t group,
                     int32_t permute, uint16_t* xg, float* xs, int64_t mpad, hipStream_t stream) {
   const int32_t piece = group < kStepK ? group : kStepK;
-  const int64_t total = mpad * (k / piece);
+  const int64_t total = mpad * (k / 8);
   if (total == 0) return WOQ_OK;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, order, m, k,
-                     piece, permute, xg, xs, mpad);
+  switch (piece / 8) {
+    case 4: hipLaunchKernelGGL(prep_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, x, order, m, k, permute, xg, xs, mpad); break;
+    case 8: hipLaunchKernelGGL(prep_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, stream, x, order, m, k, permute, xg, xs, mpad); break;
+    case 16: hipLaunchKernelGGL(prep_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, x, order, m, k, permute, xg, xs, mpad); break;
+    default: return WOQ_EUNSUPPORTED;
+  }
   return hip_status(hipGetLastError());
 }
 

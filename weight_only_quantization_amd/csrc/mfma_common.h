@@ -26,20 +26,25 @@ constexpr uint32_t kBf16Offset2 = 0x43004300u;
 constexpr float kNibOffset = 128.0f;
 constexpr uint32_t kBf16One2 = 0x3F803F80u;   // bf16 pair (1.0, 1.0)
 
-__device__ __forceinline__ uint32_t nib_pair(uint32_t d) {
-  return (d & kNibPairMask) | kBf16Offset2;
+// A copy of `v` the optimizer cannot fold back into a constant: an identity
+// DPP move.  Holding the bf16 offset this way leaves the nibble mask as the
+// only scalar operand of (d & mask) | offset, which instruction selection
+// then emits as a single v_and_or_b32 (gfx9 reads one scalar per VOP3).
+__device__ __forceinline__ uint32_t vgpr_copy(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xE4, 0xF, 0xF, false);
 }
 
 // One packed dword holds the codes of 8 consecutive inputs k..k+7, input k+e
 // in bits 4e..4e+3.  Expand it to 8 bf16 values 128 + code in slot order
 // (k, k+4, k+1, k+5, k+2, k+6, k+3, k+7): dword v of the result pairs inputs
-// k+v and k+v+4.
-__device__ __forceinline__ bf16x8_t unpack_codes(uint32_t d) {
+// k+v and k+v+4.  `mask` is kNibPairMask and `offset` kBf16Offset2, the
+// latter best held in a vector register (vgpr_copy) by the caller.
+__device__ __forceinline__ bf16x8_t unpack_codes(uint32_t d, uint32_t mask, uint32_t offset) {
   u32x4_t r;
-  r[0] = nib_pair(d);
-  r[1] = nib_pair(d >> 4);
-  r[2] = nib_pair(d >> 8);
-  r[3] = nib_pair(d >> 12);
+  r[0] = (d & mask) | offset;
+  r[1] = ((d >> 4) & mask) | offset;
+  r[2] = ((d >> 8) & mask) | offset;
+  r[3] = ((d >> 12) & mask) | offset;
   return __builtin_bit_cast(bf16x8_t, r);
 }
 

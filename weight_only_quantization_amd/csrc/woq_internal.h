@@ -27,13 +27,13 @@ inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_
 // Workspace carve-up of the linear layer (all offsets 256-byte aligned).
 struct LinearWorkspace {
   size_t xg_off = 0, xg_bytes = 0;   // gathered and/or pair-permuted activations, bf16 [M, K]
-  size_t xs_off = 0, xs_bytes = 0;   // per-group activation sums, f32 [K/G][Mpad]
+  size_t xs_off = 0, xs_bytes = 0;   // per-piece activation sums, f32 [K/min(G,128)][Mpad]
   size_t total = 0;
 };
 
 // Which kernel family runs a linear call, and with what launch shape.
 struct LinearPlan {
-  int path = 0;          // 0 = none (empty), 1 = skinny MFMA (m <= 64), 2 = tiled MFMA GEMM
+  int path = 0;          // 0 none, 1 skinny MFMA (m <= 16), 2 tiled MFMA GEMM, 3 bias only (k == 0)
   int mt = 1;            // 16-row activation tiles held per wave (skinny path)
   int fold_rows = 4;     // accumulator rows folded per tile (1 when m == 1)
   int ns = 1;            // 16-column weight tiles per workgroup (skinny path)
@@ -71,7 +71,7 @@ struct LinearArgs {
   const uint8_t* zero;     // [N, K/G]
   const float* bias;       // [N] or null
   void* y;                 // [M, N]
-  const float* xs;         // per-group sums [K/G][mpad] (GEMM path)
+  const float* xs;         // per-piece sums [K/min(G,128)][mpad] (GEMM path)
   int32_t m, n, k, group;
   int32_t y_bf16;
   int64_t mpad;
@@ -80,6 +80,8 @@ struct LinearArgs {
 int32_t launch_prep(const uint16_t* x, const int32_t* order, int32_t m, int32_t k, int32_t group,
                     int32_t permute, uint16_t* xg, float* xs, int64_t mpad, hipStream_t stream);
 int32_t launch_skinny(const LinearArgs& a, const LinearPlan& p, hipStream_t stream);
+size_t skinny_lds_bytes(int64_t m, int64_t k, int64_t group, int waves, int ns);
+constexpr size_t kSkinnyLdsLimit = 144 * 1024;   // staged activations must fit in LDS (160 KB per CU)
 int32_t launch_gemm(const LinearArgs& a, const LinearPlan& p, hipStream_t stream);
 int32_t launch_fill_bias(const float* bias, int32_t m, int32_t n, int32_t y_bf16, void* y,
                          hipStream_t stream);

@@ -154,3 +154,18 @@ LLAMA3_8B_LAYER = (
     ("down", 4096, 14336, False),
 )
 LLAMA3_8B_LAYERS = 32
+
+
+def packed_weights(n: int, k: int, group: int, seed: int, std: float = 0.02):
+    """Int4GroupLinear tensors drawn directly at random (no quantizer involved).
+
+    packed: uniform bytes [n, k/2]; scale: float32 [n, k/group] with the
+    magnitude a 4-bit grid over N(0, std^2) groups has (|N(0,1)|*std*4/15 +
+    std/15); zero: uniform 0..15.  Used where only the layout and size of a
+    quantized weight matter (timing the CPU oracle on a bounded sample).
+    """
+    rng = np.random.default_rng(seed)
+    packed = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    scale = (np.abs(rng.standard_normal((n, k // group))) * std * 4 / 15 + std / 15).astype(np.float32)
+    zero = rng.integers(0, 16, (n, k // group), dtype=np.uint8)
+    return packed, scale, zero
