@@ -79,7 +79,7 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
     if (waves > 8) waves = 8;
     while (waves > 1 && waves > nsteps) waves /= 2;
     int o_ns, o_w;
-    if (skinny_override(&o_ns, &o_w) && (o_ns == 1 || p.gb >= 2) &&
+    if (skinny_override(&o_ns, &o_w) && (o_ns == 1 || p.gb >= 2) && o_w <= nsteps &&
         skinny_lds_bytes(m, k, group, o_w, o_ns) <= kSkinnyLdsLimit) {
       ns = o_ns;
       waves = o_w;

@@ -14,13 +14,19 @@
 //   row: lane group q reads inputs [k0+32q, k0+32q+32).  Buffer loads return
 //   zero outside the workgroup's rows, so the stream has no branches and the
 //   compiler can keep PF steps of loads in flight with exact vmcnt waits.
-// * A 4x4 transpose across lane groups (two gfx950 lane-swap stages) turns the
-//   loaded bytes into the operand layout of four v_mfma_f32_16x16x32_bf16, one
-//   per 32-wide input block.  Nibbles become bf16 (128 + code) with one
-//   AND-OR per pair.  The MFMA sums x*(128+code) over each quantization group
-//   and the group's contribution is scale * (sum - (128 + zero) * sum_of_x),
-//   with the activation sums taken from the same MFMA unit against ones.
+// * Which input each MFMA operand slot stands for is free as long as the
+//   activation and weight operands agree.  When a group spans the whole step
+//   (G >= 128), MFMA e takes dword e of every lane's load (inputs
+//   k0+32q+8e .. +8), so the loaded bytes are used where they land.  Smaller
+//   groups need each MFMA inside one group: a 4x4 transpose across lane groups
+//   (two gfx950 lane-swap stages) gives MFMA e the 32 inputs of block e.
+// * Nibbles become bf16 (128 + code) with one AND-OR per pair.  The MFMA sums
+//   x*(128+code) over each group piece and the piece adds
+//   scale * (sum - (128 + zero) * sum_of_x); the activation sums come from the
+//   same MFMA unit against ones, the pair (scale, -(128 + zero)) from LDS.
 // * Partial sums of the waves meet in LDS; one pass adds the bias and stores.
+#include <type_traits>
+
 #include "woq_internal.h"
 #include "mfma_common.h"
 
@@ -29,11 +35,16 @@ namespace {
 
 constexpr int kStepK = 128;
 constexpr int kBlockK = 32;
-constexpr int kZeroBytes = 256;          // zero block read by lanes without an activation row
+// LDS starts with a junk block, which absorbs the writes of out-of-range
+// staging chunks, and a zero block, the activations of steps past a wave's last.
+constexpr int kJunkBytes = 256;
+constexpr int kZeroOff = 256;
+constexpr int kXOff = 512;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kOffsetOOB = 0x80000000u;   // a buffer offset no descriptor covers
-// 16-byte staging chunks per thread and batch: activations, scales, zero points
-constexpr int kStageX = 8, kStageS = 4, kStageZ = 2;
+// staging chunks per thread and batch: activations (8 inputs each) and
+// scale / zero-point pairs (4 entries each)
+constexpr int kStageX = 8, kStageS = 4;
 
 struct SkinnyParams {
   const uint16_t* x;
@@ -46,8 +57,9 @@ struct SkinnyParams {
   int32_t group_shift; // log2(group)
   int32_t kpad;        // K rounded up to a whole step
   int32_t xrow;        // LDS row stride of the staged activations, bytes
-  int32_t s_off, z_off;  // LDS offsets of the staged scales and zero points
+  int32_t sz_off;       // LDS offset of the staged (scale, -(128 + zero)) pairs
   int32_t z_bytewise;    // 1 when a row's zero points do not fill whole dwords
+  int32_t t_rows, t_cols;  // workgroup size split into activation rows and 16-byte chunks
   // The nibble mask and the bf16 offset pattern arrive as arguments so they sit
   // in registers: one v_and_or_b32 per pair then expands two codes.
   uint32_t nib_mask, nib_offset;
@@ -71,7 +83,9 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   const int W = blockDim.x >> 6;
   const int T = blockDim.x;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave index made explicitly uniform: everything derived from it (step
+  // offsets, counts, clamps) is then scalar work
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int q = lane >> 4;
   const int c = lane & 15;
@@ -93,122 +107,176 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   // which no descriptor covers.  Computed arithmetically so the stream stays
   // free of branches (and of the conservative waits a branch would force).
   u32x4_t bq[PF][NS];
+  uint32_t boff[NS];              // per-lane byte offset of its row and lane group
+#pragma unroll
+  for (int t = 0; t < NS; ++t) boff[t] = (uint32_t)(16 * t + c) * row_bytes + (uint32_t)(16 * q);
   auto issue = [&](int slot, int i) {
     const uint32_t dead = (uint32_t)(cnt - 1 - i) & kOffsetOOB;
-    const int k0 = (wave + i * W) * kStepK;
+    const uint32_t step_off = (uint32_t)((wave + i * W) * (kStepK / 2)) | dead;   // uniform
 #pragma unroll
-    for (int t = 0; t < NS; ++t)
-      bq[slot][t] = bload16(rb, ((uint32_t)(16 * t + c) * row_bytes + (uint32_t)(k0 / 2 + 16 * q)) | dead);
+    for (int t = 0; t < NS; ++t) bq[slot][t] = bload16(rb, boff[t] + step_off);
   };
 
   // ---- stage activations, scales and zero points in LDS ----------------------
-  // Layout: [zero block][x rows, pair order, zero-padded][scales][zero points].
-  // All staging loads are issued before the weight prefetch, so the one wait
-  // for them leaves the weight loads in flight.
-  const int cpr = p.kpad / 8;                     // 16-byte chunks per activation row
+  // Layout: [junk][zeros][x rows, pair order, zero-padded][(scale, -(128+zero))
+  // float pairs of the workgroup's rows].  Common case: one batch of staging
+  // loads per thread, issued before the weight prefetch, so the waits for them
+  // leave the weight loads in flight.  Every staging load and LDS write is
+  // unconditional (out-of-range loads use an offset no descriptor covers and
+  // read zero; their writes land in the junk block): a load whose register is
+  // consumed on only some paths would make the compiler drain the whole weight
+  // stream inside the main loop.  Larger staging (long rows, many activation
+  // rows, zero-point rows that end inside a dword) runs first, with its own
+  // waits, before the stream starts.
+  const int cpr = p.kpad / 8;                     // 8-input chunks per activation row
   const int xchunks = M * cpr;
-  const uint32_t sbytes = (uint32_t)rows * ngroups * 4, zbytes = (uint32_t)rows * ngroups;
-  const int schunks = (int)((sbytes + 15) / 16), zchunks = (int)((zbytes + 15) / 16);
-  unsigned char* const lds_s = lds + p.s_off;
-  unsigned char* const lds_z = lds + p.z_off;
-  u32x4_t xb[kStageX], sb[kStageS], zb[kStageZ];
-  auto load_x = [&](int base) {
+  const int entries = rows * ngroups;
+  const int szchunks = (entries + 3) / 4;
+  const bool slow = xchunks > kStageX * T || szchunks > kStageS * T || p.z_bytewise;  // uniform
+  u32x4_t xb[kStageX], sb[kStageS];
+  uint32_t xr[kStageX], zb[kStageS];
+  // Thread tid stages the chunks tid, tid+T, ... of the row-major chunk grid
+  // [M][cpr]; (row, col) advance by (t_rows, t_cols) per chunk with one wrap,
+  // so no division runs per chunk.  Each workgroup starts its columns at a
+  // different offset, spreading the shared activation reads over L2 channels.
+  const int rotc = (int)((blockIdx.x * 64u) % (uint32_t)cpr);
+  auto load_x = [&](int batch, int limit) {
+    const int ch0 = tid + batch * kStageX * T;       // one division per batch
+    int row = ch0 / cpr, col = ch0 - row * cpr;
 #pragma unroll
     for (int u = 0; u < kStageX; ++u) {
-      const int ch = base + tid + T * u;
-      const int row = ch / cpr, col = ch % cpr;
-      const bool ok = ch < xchunks && col * 8 < K;
-      xb[u] = bload16(rx, ok ? (uint32_t)(row * K + col * 8) * 2 : kOffsetOOB);
+      int cr = col + rotc;
+      cr = cr >= cpr ? cr - cpr : cr;
+      const bool in = ch0 + T * u < limit;
+      xb[u] = bload16(rx, in && cr * 8 < K ? (uint32_t)(row * K + cr * 8) * 2 : kOffsetOOB);
+      xr[u] = in ? (uint32_t)(kXOff + row * p.xrow + cr * 16) : 0u;
+      col += p.t_cols;
+      row += p.t_rows;
+      if (col >= cpr) { col -= cpr; ++row; }
     }
   };
-  auto put_x = [&](int base) {
+  auto put_x = [&]() {
 #pragma unroll
-    for (int u = 0; u < kStageX; ++u) {
-      const int ch = base + tid + T * u;
-      if (ch < xchunks) {
-        const int row = ch / cpr, col = ch % cpr;
-        *reinterpret_cast<bf16x8_t*>(lds + kZeroBytes + row * p.xrow + col * 16) = pair_order(xb[u]);
-      }
-    }
+    for (int u = 0; u < kStageX; ++u) *reinterpret_cast<bf16x8_t*>(lds + xr[u]) = pair_order(xb[u]);
   };
-  auto load_sz = [&](int sbase, int zbase) {
+  // chunk ch: entries 4ch .. 4ch+3 (entry = row * ngroups + group), 16 bytes
+  // of scales and one dword of zero points
+  auto load_sz = [&](int base, int limit, auto bytewise) {
 #pragma unroll
     for (int u = 0; u < kStageS; ++u) {
-      const int ch = sbase + tid + T * u;
-      sb[u] = bload16(rs, ch < schunks ? (uint32_t)ch * 16 : kOffsetOOB);
-    }
-    // Buffer range checks work on whole dwords; when the zero points end inside
-    // a dword they are fetched byte by byte so none of them reads back as 0.
-    if (p.z_bytewise) {
+      const int ch = base + tid + T * u;
+      const bool in = ch < limit;
+      sb[u] = bload16(rs, in ? (uint32_t)ch * 16 : kOffsetOOB);
+      if constexpr (decltype(bytewise)::value) {
+        // range checks work on whole dwords: the last row may end inside one
+        uint32_t z = 0;
 #pragma unroll
-      for (int u = 0; u < kStageZ; ++u) {
-        const int ch = zbase + tid + T * u;
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const uint32_t off = ch < zchunks ? (uint32_t)(ch * 16 + e) : kOffsetOOB;
-          w[e >> 2] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rz, (int)off, 0, 0) << (8 * (e & 3));
-        }
-        zb[u] = u32x4_t{w[0], w[1], w[2], w[3]};
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < kStageZ; ++u) {
-        const int ch = zbase + tid + T * u;
-        zb[u] = bload16(rz, ch < zchunks ? (uint32_t)ch * 16 : kOffsetOOB);
+        for (int e = 0; e < 4; ++e)
+          z |= (uint32_t)(uint8_t)__builtin_amdgcn_raw_buffer_load_b8(rz, in ? (uint32_t)(4 * ch + e) : kOffsetOOB, 0, 0) << (8 * e);
+        zb[u] = z;
+      } else {
+        zb[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rz, in ? (uint32_t)ch * 4 : kOffsetOOB, 0, 0);
       }
     }
   };
-  auto put_sz = [&](int sbase, int zbase) {
+  auto put_sz = [&](int base, int limit) {
 #pragma unroll
     for (int u = 0; u < kStageS; ++u) {
-      const int ch = sbase + tid + T * u;
-      if (ch < schunks) *reinterpret_cast<u32x4_t*>(lds_s + ch * 16) = sb[u];
-    }
+      const int ch = base + tid + T * u;
+      // (bit_cast of the whole vector: this compiler resolves a bit_cast of
+      // one element of a vector lvalue to element 0)
+      const f32x4_t sv = __builtin_bit_cast(f32x4_t, sb[u]);
+      float f[8];
 #pragma unroll
-    for (int u = 0; u < kStageZ; ++u) {
-      const int ch = zbase + tid + T * u;
-      if (ch < zchunks) *reinterpret_cast<u32x4_t*>(lds_z + ch * 16) = zb[u];
+      for (int e = 0; e < 4; ++e) {
+        f[2 * e] = sv[e];
+        f[2 * e + 1] = -(kNibOffset + (float)((zb[u] >> (8 * e)) & 0xFFu));
+      }
+      f32x4_t* dst = reinterpret_cast<f32x4_t*>(lds + (ch < limit ? p.sz_off + ch * 32 : 0));
+      dst[0] = f32x4_t{f[0], f[1], f[2], f[3]};
+      dst[1] = f32x4_t{f[4], f[5], f[6], f[7]};
     }
   };
-  load_x(0);
-  load_sz(0, 0);
+  if (slow) {
+    for (int batch = 0; batch * kStageX * T < xchunks; ++batch) {
+      load_x(batch, xchunks);
+      put_x();
+    }
+    for (int base = 0; base < szchunks; base += kStageS * T) {
+      load_sz(base, szchunks, std::true_type{});
+      put_sz(base, szchunks);
+    }
+  }
+  // the common case; after slow staging it only touches the junk block
+  const int xlim = slow ? 0 : xchunks, szlim = slow ? 0 : szchunks;
+  load_x(0, xlim);
+  load_sz(0, szlim, std::false_type{});
 #pragma unroll
   for (int u = 0; u < PF; ++u) issue(u, u);       // the weight stream starts now
-  if (tid < kZeroBytes / 16)
-    *reinterpret_cast<u32x4_t*>(lds + tid * 16) = u32x4_t{0u, 0u, 0u, 0u};
-  put_x(0);
-  put_sz(0, 0);
-  for (int base = kStageX * T; base < xchunks; base += kStageX * T) {
-    load_x(base);
-    put_x(base);
-  }
-  for (int sbase = kStageS * T, zbase = kStageZ * T; sbase < schunks || zbase < zchunks;
-       sbase += kStageS * T, zbase += kStageZ * T) {
-    load_sz(sbase, zbase);
-    put_sz(sbase, zbase);
-  }
+  if (tid < 16) *reinterpret_cast<u32x4_t*>(lds + kZeroOff + 16 * tid) = u32x4_t{0u, 0u, 0u, 0u};
+  put_x();
+  put_sz(0, szlim);
   __syncthreads();
 
   // ---- main loop --------------------------------------------------------------
+  constexpr bool kTranspose = GB < 4;
   f32x4_t acc[NS];
 #pragma unroll
   for (int t = 0; t < NS; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const uint32_t row_mask = c < M ? 0xFFFFFFFFu : 0u;   // lanes without a row read the zero block
-  const uint32_t a_lane = (uint32_t)(kZeroBytes + c * p.xrow + 16 * q);
-  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{kBf16One2, kBf16One2, kBf16One2, kBf16One2});
+  // Activation operand of lane (q, i): row i (lanes past the last row repeat
+  // row M-1; their outputs are never stored).  MFMA e reads the chunk of
+  // inputs k0+32q+8e (no transpose) or k0+32e+8q (transpose).
+  const uint32_t a_lane = (uint32_t)(kXOff + min(c, M - 1) * p.xrow + (kTranspose ? 16 : 64) * q);
+  const uint32_t a_zero = (uint32_t)(kZeroOff + (kTranspose ? 16 : 64) * q);
+  constexpr int kAStride = kTranspose ? 64 : 16;
+  const uint32_t sz_lane = (uint32_t)(p.sz_off + c * ngroups * 8);
   const uint32_t nib_offset = vgpr_copy(p.nib_offset);
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{kBf16One2, kBf16One2, kBf16One2, kBf16One2});
 
-  // A dead step (past the wave's last) reads the zero block and zero-filled
-  // weights and scales, so it adds exactly nothing.
-  auto compute = [&](int slot, int i) {
-    const int k0 = (wave + i * W) * kStepK;
-    const uint32_t live_mask = (uint32_t)((i - cnt) >> 31);   // all ones while i < cnt
-    const uint32_t a_addr = (a_lane + (uint32_t)k0 * 2) & row_mask & live_mask;
+  // Step i takes its weights out of ring slot `slot`, refills the slot with
+  // step i + PF as soon as the bytes are out of it, and only then computes;
+  // the scheduling barrier keeps the compiler from sinking the refill below
+  // the arithmetic, which would let the stream run dry once per ring turn.
+  // A step past the wave's last multiplies zero activations (the zero block)
+  // by zero weights and adds exactly nothing.
+  auto step = [&](int slot, int i) {
+    const bool live = i < cnt;
+    const int k0 = min(wave + max(min(i, cnt - 1), 0) * W, nsteps - 1) * kStepK;
+    const uint32_t a_addr = live ? a_lane + (uint32_t)k0 * 2 : a_zero;
     bf16x8_t af[4];
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-      af[jb] = *reinterpret_cast<const bf16x8_t*>(lds + a_addr + 64 * jb);
+    for (int e = 0; e < 4; ++e) af[e] = *reinterpret_cast<const bf16x8_t*>(lds + a_addr + kAStride * e);
+    // (scale, -(128 + zero)) of each tile row and group piece
+    float2 sz[NS][NP];
+#pragma unroll
+    for (int t = 0; t < NS; ++t)
+#pragma unroll
+      for (int pc = 0; pc < NP; ++pc) {
+        const int g = min((k0 + kBlockK * GB * pc) >> p.group_shift, ngroups - 1);
+        sz[t][pc] = *reinterpret_cast<const float2*>(lds + sz_lane + (16 * t * ngroups + g) * 8);
+      }
+    bf16x8_t bw[NS][4];
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      if constexpr (kTranspose) {
+        // The lane swaps work in place; on copies, the slot's registers stay
+        // free for the refill and keep their place from one ring turn to the
+        // next (no copy of a register a load is still writing).
+        uint32_t d0 = vgpr_copy(bq[slot][t][0]), d1 = vgpr_copy(bq[slot][t][1]);
+        uint32_t d2 = vgpr_copy(bq[slot][t][2]), d3 = vgpr_copy(bq[slot][t][3]);
+        transpose4_lanegroups(d0, d1, d2, d3);
+        bw[t][0] = unpack_codes(d0, p.nib_mask, nib_offset);
+        bw[t][1] = unpack_codes(d1, p.nib_mask, nib_offset);
+        bw[t][2] = unpack_codes(d2, p.nib_mask, nib_offset);
+        bw[t][3] = unpack_codes(d3, p.nib_mask, nib_offset);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bw[t][e] = unpack_codes(bq[slot][t][e], p.nib_mask, nib_offset);
+      }
+    }
+    issue(slot, i + PF);
+    __builtin_amdgcn_sched_barrier(0);
+    // activation sums of each group piece, in the accumulator layout
     f32x4_t xs[NP];
 #pragma unroll
     for (int pc = 0; pc < NP; ++pc) {
@@ -219,32 +287,21 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
     }
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
-      uint32_t d0 = bq[slot][t][0], d1 = bq[slot][t][1], d2 = bq[slot][t][2], d3 = bq[slot][t][3];
-      transpose4_lanegroups(d0, d1, d2, d3);
-      const uint32_t dw[4] = {d0, d1, d2, d3};
-      const int srow = (16 * t + c) * ngroups;
 #pragma unroll
       for (int pc = 0; pc < NP; ++pc) {
-        // group of this piece, clamped so padded and dead steps read a finite scale
-        const int g = min((k0 + kBlockK * GB * pc) >> p.group_shift, ngroups - 1);
-        const float s = *reinterpret_cast<const float*>(lds_s + (srow + g) * 4);
-        const float zz = -(kNibOffset + (float)lds_z[srow + g]);
         f32x4_t cg = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < GB; ++e)
-          cg = mfma_bf16(af[pc * GB + e], unpack_codes(dw[pc * GB + e], p.nib_mask, nib_offset), cg);
+        for (int e = 0; e < GB; ++e) cg = mfma_bf16(af[pc * GB + e], bw[t][pc * GB + e], cg);
 #pragma unroll
-        for (int r = 0; r < FR; ++r) acc[t][r] = fmaf(s, fmaf(zz, xs[pc][r], cg[r]), acc[t][r]);
+        for (int r = 0; r < FR; ++r)
+          acc[t][r] = fmaf(sz[t][pc].x, fmaf(sz[t][pc].y, xs[pc][r], cg[r]), acc[t][r]);
       }
     }
   };
 
   for (int i0 = 0; i0 < cnt; i0 += PF) {
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      compute(u, i0 + u);
-      issue(u, i0 + u + PF);
-    }
+    for (int u = 0; u < PF; ++u) step(u, i0 + u);
   }
 
   // ---- combine the waves, add the bias, store ----------------------------------
@@ -316,17 +373,15 @@ int32_t dispatch_gb(const SkinnyParams& sp, const LinearPlan& pl, size_t lds, hi
 }  // namespace
 
 struct SkinnyLds {
-  size_t x_off, s_off, z_off, total;
+  size_t sz_off, total;
 };
 
 SkinnyLds skinny_lds_layout(int64_t m, int64_t k, int64_t group, int waves, int ns) {
   const int64_t kpad = (k + kStepK - 1) / kStepK * kStepK;
-  const int64_t rows = 16 * ns, ngroups = k / group;
+  const int64_t entries = 16 * ns * (k / group);
   SkinnyLds l;
-  l.x_off = kZeroBytes;
-  l.s_off = l.x_off + (size_t)(m * (kpad * 2 + 16));
-  l.z_off = l.s_off + (size_t)((rows * ngroups * 4 + 15) / 16 * 16);
-  const size_t stage = l.z_off + (size_t)((rows * ngroups + 15) / 16 * 16);
+  l.sz_off = (size_t)kXOff + (size_t)(m * (kpad * 2 + 16));
+  const size_t stage = l.sz_off + (size_t)((entries + 3) / 4 * 32);
   const size_t red = waves > 1 ? (size_t)waves * ns * 4 * 64 * 4 : 0;
   l.total = stage > red ? stage : red;
   return l;
@@ -342,8 +397,9 @@ int32_t launch_skinny(const LinearArgs& a, const LinearPlan& pl, hipStream_t str
   while ((1 << gshift) < a.group) ++gshift;
   const SkinnyLds l = skinny_lds_layout(a.m, a.k, a.group, pl.waves, pl.ns);
   SkinnyParams sp{a.x, a.packed, a.scale, a.zero, a.bias, a.y, a.m, a.n, a.k, a.group, a.y_bf16,
-                  gshift, kpad, kpad * 2 + 16, (int32_t)l.s_off, (int32_t)l.z_off,
-                  (a.k / a.group) % 4 != 0 ? 1 : 0, kNibPairMask, kBf16Offset2};
+                  gshift, kpad, kpad * 2 + 16, (int32_t)l.sz_off,
+                  (a.k / a.group) % 4 != 0 ? 1 : 0, 64 * pl.waves / (kpad / 8),
+                  64 * pl.waves % (kpad / 8), kNibPairMask, kBf16Offset2};
   const size_t lds = l.total;
   const bool one = pl.fold_rows == 1;
   switch (pl.ns) {

@@ -81,7 +81,7 @@ int32_t launch_prep(const uint16_t* x, const int32_t* order, int32_t m, int32_t 
                     int32_t permute, uint16_t* xg, float* xs, int64_t mpad, hipStream_t stream);
 int32_t launch_skinny(const LinearArgs& a, const LinearPlan& p, hipStream_t stream);
 size_t skinny_lds_bytes(int64_t m, int64_t k, int64_t group, int waves, int ns);
-constexpr size_t kSkinnyLdsLimit = 144 * 1024;   // staged activations must fit in LDS (160 KB per CU)
+constexpr size_t kSkinnyLdsLimit = 160 * 1024;   // staged activations, scales and zeros share the 160 KB of LDS per CU
 int32_t launch_gemm(const LinearArgs& a, const LinearPlan& p, hipStream_t stream);
 int32_t launch_fill_bias(const float* bias, int32_t m, int32_t n, int32_t y_bf16, void* y,
                          hipStream_t stream);
