@@ -105,25 +105,6 @@ def run_calls(woq, calls):
                                group=GROUP, out=c["y"], out_dtype=c["y"].dtype)
 
 
-def per_launch_durations(torch, woq, calls, reps: int = 2):
-    """Device time of each launch: events around every call, queued behind a spin kernel
-    so the host enqueues the whole step before the GPU reaches it."""
-    durs = []
-    for _ in range(reps):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in calls]
-        torch.cuda._sleep(int(2.4e9 * 0.05))        # ~50 ms of queued GPU spin
-        for c, (e0, e1) in zip(calls, evs):
-            e0.record()
-            woq.linear_int4_groups(c["x"], c["packed"], c["scale"], c["zero"], bias=c["bias"],
-                                   group=GROUP, out=c["y"], out_dtype=c["y"].dtype)
-            e1.record()
-        torch.cuda.synchronize()
-        durs.append([e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs])   # seconds
-    # per launch, the best of the repetitions
-    return [min(r[i] for r in durs) for i in range(len(calls))]
-
-
 def measure_prefill(torch, woq, reps: int = 5):
     from workloads import PREFILL
 
@@ -204,6 +185,100 @@ def cpu_baseline(min_seconds: float = 10.0, max_passes: int = 8):
                        f"BLAS threads={blas_threads}, affinity cores={len(os.sched_getaffinity(0))})")
 
 
+SKINNY_TAG = "skinny_kernel"
+COPY_TAG = "copyBuffer"            # the runtime's device-to-device copy kernel
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirpath: Path, suffix: str) -> Path:
+    hits = sorted(dirpath.rglob(f"*{suffix}"))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {dirpath}")
+    return hits[0]
+
+
+def summarize_profiles(root: Path, copy_mib: int) -> None:
+    """Print the text summaries kept under profiles/ from three rocprofv3 runs.
+
+    root/ktrace: --kernel-trace --stats of the bench; root/fetch and root/write:
+    --pmc FETCH_SIZE and --pmc WRITE_SIZE of a short eager bench that also runs a
+    plain device copy of copy_mib MiB, whose counter reading calibrates the
+    counters to bytes (factor = copied bytes / counted bytes).
+    """
+    trace = _csv_rows(_find(root / "ktrace", "_kernel_trace.csv"))
+    by_kernel = {}
+    for r in trace:
+        name = r["Kernel_Name"]
+        if "woq::" not in name:
+            continue
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        by_kernel.setdefault(name, []).append((int(r["Grid_Size_X"]), dur))
+    out = ["# rocprofv3 kernel trace of bench.py, woq kernels only (durations in microseconds)"]
+    for name, rows in sorted(by_kernel.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        durs = [d for _, d in rows]
+        out.append(f"kernel: {name}")
+        out.append(f"  launches: {len(rows)}  average_us: {statistics.mean(durs) / 1e3:.3f}  "
+                   f"min_us: {min(durs) / 1e3:.3f}  max_us: {max(durs) / 1e3:.3f}")
+        grids = {}
+        for g, d in rows:
+            grids.setdefault(g, []).append(d)
+        for g, ds in sorted(grids.items()):
+            out.append(f"  grid_threads {g}: launches {len(ds)}  average_us {statistics.mean(ds) / 1e3:.3f}")
+    for cand in sorted((root / "ktrace").rglob("*.json")):
+        for line in cand.read_text().splitlines():
+            try:
+                rl = json.loads(line)["roofline"]
+            except (ValueError, KeyError, TypeError):
+                continue
+            out.append(f"bench_avg_launch_us (HIP events around the replayed step graph): {rl['avg_launch_us']}")
+    print("\n".join(out))
+
+    def counter(sub, cname):
+        rows = _csv_rows(_find(root / sub, "_counter_collection.csv"))
+        sk = [float(r["Counter_Value"]) for r in rows
+              if r["Counter_Name"] == cname and SKINNY_TAG in r["Kernel_Name"]]
+        cp = [float(r["Counter_Value"]) for r in rows
+              if r["Counter_Name"] == cname and COPY_TAG in r["Kernel_Name"]]
+        return sk, cp
+
+    f_sk, f_cp = counter("fetch", "FETCH_SIZE")
+    w_sk, w_cp = counter("write", "WRITE_SIZE")
+    copy_bytes = copy_mib << 20
+    if not f_cp or not w_cp:
+        raise SystemExit("the calibration copy is missing from the counter runs")
+    # the largest copy of the run is the calibration copy
+    f_factor = copy_bytes / (max(f_cp) * 1024.0)
+    w_factor = copy_bytes / (max(w_cp) * 1024.0)
+    fetch = statistics.mean(f_sk) * 1024.0 * f_factor
+    write = statistics.mean(w_sk) * 1024.0 * w_factor
+    print()
+    print("# HBM traffic of the skinny decode kernel per launch (rocprofv3 --pmc, copy-calibrated)")
+    # the sources the counted kernel was built from, as the profiled bench printed them
+    src_hash = None
+    for cand in sorted((root / "fetch").rglob("*.json")):
+        for line in cand.read_text().splitlines():
+            try:
+                src_hash = json.loads(line)["roofline"]["kernel_source_sha256_16"]
+            except (ValueError, KeyError, TypeError):
+                continue
+    if src_hash is None:
+        raise SystemExit("the profiled bench's JSON line (fetch/*.json) is missing")
+    print(f"kernel_source_sha256_16: {src_hash}")
+    print(f"launches_counted: {len(f_sk)}")
+    print(f"fetch_KiB_raw_avg: {statistics.mean(f_sk):.1f}")
+    print(f"write_KiB_raw_avg: {statistics.mean(w_sk):.1f}")
+    print(f"copy_calibration_MiB: {copy_mib}")
+    print(f"fetch_factor: {f_factor:.4f}")
+    print(f"write_factor: {w_factor:.4f}")
+    print(f"hbm_bytes_per_launch: {fetch + write:.0f}")
+
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,7 +290,12 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="print the profiles/ summaries from rocprofv3 output under DIR and exit")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(Path(args.summarize_profiles), args.copy_calibration_mib or 512)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -264,18 +344,20 @@ def main():
     ms_per_step = elapsed / args.steps * 1e3
     value = wbytes * args.steps / elapsed / 1e9
 
-    durs = per_launch_durations(torch, woq, calls)
-    achieved = sum(abytes) / sum(durs) / 1e9
+    # The step is one graph of back-to-back launches of the skinny kernel, so the
+    # kernel's average launch duration is the timed region over the launches in it
+    # (inter-launch gaps included, which makes the figure conservative).
+    avg_launch = elapsed / (args.steps * len(calls))
+    achieved = sum(abytes) / len(abytes) / avg_launch / 1e9
     traffic = read_traffic()
-    big = [i for i, c in enumerate(calls) if c["n"] * c["k"] == 14336 * 4096]
     roofline = dict(
         bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
         frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
-        kernel="woq::skinny_kernel<MT=1,FR=1,NS=1,GB=4,PF=4> (every launch of the step)",
-        launches=len(calls), avg_launch_us=round(sum(durs) / len(durs) * 1e6, 3),
+        kernel="woq::skinny_kernel<NS=1,GB=4,PF=4,FR=1> (every launch of the step)",
+        launches=len(calls), avg_launch_us=round(avg_launch * 1e6, 3),
         algorithmic_bytes_per_launch=round(sum(abytes) / len(abytes)),
         traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
-        gate_up_down_14336x4096_GBps=round(sum(abytes[i] for i in big) / sum(durs[i] for i in big) / 1e9, 1),
+        kernel_source_sha256_16=kernel_source_hash(),
         plans={f"{c['n']}x{c['k']}": woq.linear_plan(1, c["n"], c["k"], GROUP)
                for c in calls[:len(calls) // args.layers]},
     )
@@ -284,7 +366,7 @@ def main():
         src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            dst.copy_(src)          # a device-to-device copy: the runtime's copyBuffer kernel
         torch.cuda.synchronize()
         del src, dst
 

@@ -161,7 +161,7 @@ int32_t woq_linear_int4_groups(const void* x_bf16, int64_t m, const uint8_t* pac
 
 /*
  * Describe the kernel plan woq_linear_int4_groups uses for these sizes: the
- * path (skinny MFMA for m <= 64, tiled MFMA GEMM above), tiles, waves and
+ * path (skinny MFMA for m <= 16, tiled MFMA GEMM above), tiles, waves and
  * whether an input pre-pass runs.  Writes a NUL-terminated string of at most
  * len bytes into buf (host).  Pure host function.
  * Errors: WOQ_EINVAL (buf NULL, len 0), plus the shape errors of the linear call.

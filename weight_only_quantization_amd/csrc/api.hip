@@ -74,9 +74,12 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
     const int64_t nsteps = (k + 127) / 128;
     int ns = skinny_ns;
     int64_t tiles = (nsub + ns - 1) / ns;
-    int64_t want = 4096 / (tiles > 0 ? tiles : 1);
+    // About two waves per SIMD over the grid, at most four per workgroup
+    // (measured on the decode shapes: more waves per workgroup only lengthen
+    // the staging and the cross-wave reduction).
+    int64_t want = 2048 / (tiles > 0 ? tiles : 1);
     int waves = pow2_floor(want < 1 ? 1 : want);
-    if (waves > 8) waves = 8;
+    if (waves > 4) waves = 4;
     while (waves > 1 && waves > nsteps) waves /= 2;
     int o_ns, o_w;
     if (skinny_override(&o_ns, &o_w) && (o_ns == 1 || p.gb >= 2) && o_w <= nsteps &&

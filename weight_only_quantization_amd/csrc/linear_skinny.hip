@@ -359,13 +359,14 @@ int32_t launch_one(const SkinnyParams& sp, const LinearPlan& pl, size_t lds, hip
 
 template <int NS, int FR>
 int32_t dispatch_gb(const SkinnyParams& sp, const LinearPlan& pl, size_t lds, hipStream_t stream) {
-  // Prefetch depth: 8 steps with one weight tile per workgroup, 4 with two.
+  // Four steps in flight per wave: deeper rings measured slower on the decode
+  // shapes (more outstanding requests delay every workgroup's staging).
   switch (pl.gb) {
     case 1:   // two tiles of 32-wide groups exceed the register budget
-      if constexpr (NS == 1) return launch_one<1, 1, 8, FR>(sp, pl, lds, stream);
+      if constexpr (NS == 1) return launch_one<1, 1, 4, FR>(sp, pl, lds, stream);
       return WOQ_EUNSUPPORTED;
-    case 2: return launch_one<NS, 2, NS == 1 ? 8 : 4, FR>(sp, pl, lds, stream);
-    case 4: return launch_one<NS, 4, NS == 1 ? 8 : 4, FR>(sp, pl, lds, stream);
+    case 2: return launch_one<NS, 2, 4, FR>(sp, pl, lds, stream);
+    case 4: return launch_one<NS, 4, 4, FR>(sp, pl, lds, stream);
     default: return WOQ_EUNSUPPORTED;
   }
 }
