@@ -151,7 +151,8 @@ size_t woq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group
  *   when that is 0.  The workspace holds only scratch; it need not be cleared.
  * m == 0 or n == 0 is a no-op; k == 0 gives y = bias (or 0).
  * Errors: WOQ_EINVAL, WOQ_EGROUP, WOQ_EUNSUPPORTED (group outside the list,
- *   m, n or k >= 2^31), WOQ_EALIGN, WOQ_EWORKSPACE, WOQ_EHIP.
+ *   m, n or k >= 2^31, or k >= 2^24 on the tiled path, m > 16), WOQ_EALIGN,
+ *   WOQ_EWORKSPACE, WOQ_EHIP.
  */
 int32_t woq_linear_int4_groups(const void* x_bf16, int64_t m, const uint8_t* packed,
                                const float* scale, const uint8_t* zero, const float* bias,

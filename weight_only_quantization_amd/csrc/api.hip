@@ -111,13 +111,16 @@ LinearWorkspace linear_workspace_layout(int64_t m, int64_t n, int64_t k, int32_t
     w.xg_off = 0;
     w.xg_bytes = round256((size_t)m * (size_t)k * 2);
   } else if (p.path == 2) {
+    const int64_t kpad = (k + 127) / 128 * 128;
     w.xg_off = 0;
-    w.xg_bytes = round256((size_t)m * (size_t)k * 2);
+    w.xg_bytes = round256((size_t)m * (size_t)kpad * 2);
     w.xs_off = w.xg_bytes;
     const int64_t piece = group < 128 ? group : 128;   // sums per group part inside a k step
     w.xs_bytes = round256((size_t)(k / piece) * (size_t)p.mpad * 4);
+    w.sz_off = w.xs_off + w.xs_bytes;
+    w.sz_bytes = round256(gemm_sz_bytes(n, k, group));
   }
-  w.total = w.xg_bytes + w.xs_bytes;
+  w.total = w.xg_bytes + w.xs_bytes + w.sz_bytes;
   return w;
 }
 
@@ -255,22 +258,25 @@ int32_t woq_linear_int4_groups(const void* x_bf16, int64_t m, const uint8_t* pac
   a.group = group;
   a.y_bf16 = y_dtype == WOQ_BF16;
   a.mpad = plan.mpad;
+  a.kpad = a.k;
   if (plan.path == 1) {
     if (has_order) {
       uint16_t* xg = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
-      st = launch_prep(a.x, order, a.m, a.k, group, 0, xg, nullptr, m, s);
+      st = launch_prep(a.x, order, a.m, a.k, a.k, group, 0, xg, nullptr, m, s);
       if (st != WOQ_OK) return st;
       a.x = xg;
     }
     return launch_skinny(a, plan, s);
   }
+  if (k >= kGemmMaxK) return WOQ_EUNSUPPORTED;
   uint16_t* xg = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
   float* xs = reinterpret_cast<float*>(wsb + ws.xs_off);
-  st = launch_prep(a.x, order, a.m, a.k, group, 1, xg, xs, plan.mpad, s);
+  a.kpad = (a.k + 127) / 128 * 128;
+  st = launch_prep(a.x, order, a.m, a.k, a.kpad, group, 1, xg, xs, plan.mpad, s);
   if (st != WOQ_OK) return st;
   a.x = xg;
   a.xs = xs;
-  return launch_gemm(a, plan, s);
+  return launch_gemm(a, plan, wsb + ws.sz_off, s);
 }
 
 int32_t woq_linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, int32_t has_order,

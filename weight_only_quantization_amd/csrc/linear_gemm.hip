@@ -1,19 +1,29 @@
-// Tiled linear path (m > 32) and the activation pre-pass.
+// Tiled linear path (m > 16) and the activation pre-pass.
 //
 // Pre-pass: x' = x gathered through the act-order index when one is given
 // (linnet docs "Quantization", section "Importing GPTQ and AWQ": the layer
 // gathers its inputs first), optionally written in the slot order of the
-// nibble unpacker, plus the float32 sum of x' over every "piece": the part of
-// a quantization group inside one 128-wide k step (the whole group for
-// groups of at most 128 inputs).
+// nibble unpacker with each row zero-padded to whole 128-input steps, plus the
+// float32 sum of x' over every "piece": the part of a quantization group inside
+// one 128-wide k step (the whole group for groups of at most 128 inputs).
+// A second small pass lays the scales and zero points out per group as
+// (scale, -(128 + zero)) float pairs, [K/G][N rounded up to 256].
 //
-// GEMM: a workgroup of 8 waves computes a 128 x 256 tile of y.  The activation
-// tile of each 128-wide k step is staged in LDS (double buffered, one barrier
-// per step); every wave streams its own 64 weight rows straight from global
-// memory into registers, transposes them across lane groups and expands the
-// nibbles to bf16 (128 + code) for v_mfma_f32_16x16x32_bf16.  Per
-// quantization group the MFMA sums are folded into float32 accumulators as
-//   acc += scale * (sum - (128 + zero) * group_sum_of_x).
+// GEMM (linnet docs "Quantization", std.quant table, linear_int4_groups): a
+// workgroup of 8 waves computes a 128 x 256 tile of y, each wave 64 x 64 as
+// 2 x 2 tiles of v_mfma_f32_32x32x16_bf16.  Per 128-input step the workgroup
+// streams the activation tile (32 KB), the packed weight tile (16 KB), the
+// piece sums and the scale/zero pairs straight from memory into a ring of
+// three LDS stages with buffer-to-LDS loads, so the memory stream runs two
+// steps ahead without holding registers; one barrier per step hands a stage
+// from the loads to the arithmetic.  Both tiles are stored XOR-swizzled so the
+// reads of 8 neighbouring rows hit distinct banks.  Nibbles become bf16
+// (128 + code) with one AND-OR per pair; each MFMA takes one dword of every
+// lane's 16 loaded bytes (inputs u+32h+8b .. +8 of a 64-input unit u, h the
+// lane half), which keeps every MFMA inside one group for groups of 64 and
+// more; 32-input groups regroup the dwords between the lane halves with two
+// v_permlane32_swap.  Per group piece the MFMA sums fold into float32
+// accumulators as acc += scale * (sum - (128 + zero) * piece_sum_of_x).
 #include "woq_internal.h"
 #include "mfma_common.h"
 
@@ -21,27 +31,29 @@ namespace woq {
 namespace {
 
 constexpr int kStepK = 128;
-constexpr int kBlockK = 32;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+constexpr uint32_t kOffsetOOB = 0x80000000u;   // a buffer offset no descriptor covers
 
 // One thread per 8 consecutive inputs of a row (16 bytes).  The lanes of one
 // piece (piece/8 of them, consecutive) add their partial sums in a fixed
 // shuffle tree, so the sums are the same on every run.  Rows from m to mpad
-// only get zero sums.
+// only get zero sums; columns from k to kpad (the written row stride) get
+// zeros.
 template <int LP>   // lanes per piece: piece / 8
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ x,
                                                    const int32_t* __restrict__ order, int32_t m,
-                                                   int32_t k, int32_t permute,
+                                                   int32_t k, int32_t kpad, int32_t permute,
                                                    uint16_t* __restrict__ xg, float* __restrict__ xs,
                                                    int64_t mpad) {
-  const int cpr = k / 8;                       // chunks per row
-  const int npieces = cpr / LP;
+  const int cpr = kpad / 8;                    // chunks per written row
+  const int kc = k / 8;                        // chunks holding inputs
   const int64_t total = mpad * cpr;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
     const int64_t row = t / cpr;
     const int col = (int)(t % cpr);
     u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-    if (row < m) {
+    if (row < m && col < kc) {
       const uint16_t* xr = x + row * k;
       if (order) {
         const u32x4_t i0 = load16(order + col * 8), i1 = load16(order + col * 8 + 4);
@@ -65,9 +77,28 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
 #pragma unroll
     for (int off = 1; off < LP; off <<= 1) sum += __shfl_xor(sum, off, LP);
     if (row < m && xg)
-      *reinterpret_cast<u32x4_t*>(xg + row * k + col * 8) =
+      *reinterpret_cast<u32x4_t*>(xg + row * kpad + col * 8) =
           permute ? __builtin_bit_cast(u32x4_t, pair_order(v)) : v;
-    if (xs && (col % LP) == 0) xs[(int64_t)(col / LP) * mpad + row] = sum;
+    if (xs && col < kc && (col % LP) == 0) xs[(int64_t)(col / LP) * mpad + row] = sum;
+  }
+}
+
+// sz[g][c] = (scale[c][g], -(128 + zero[c][g])) for c < n, zeros up to npad.
+__global__ __launch_bounds__(256) void sz_prep_kernel(const float* __restrict__ scale,
+                                                      const uint8_t* __restrict__ zero, int32_t n,
+                                                      int32_t ngroups, int32_t npad,
+                                                      f32x2_t* __restrict__ sz) {
+  const int64_t total = (int64_t)ngroups * npad;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+    const int64_t g = t / npad;
+    const int c = (int)(t % npad);
+    f32x2_t v = f32x2_t{0.f, 0.f};
+    if (c < n) {
+      const int64_t e = (int64_t)c * ngroups + g;
+      v = f32x2_t{scale[e], -(kNibOffset + (float)zero[e])};
+    }
+    sz[t] = v;
   }
 }
 
@@ -84,35 +115,66 @@ __global__ __launch_bounds__(256) void fill_bias_kernel(const float* __restrict_
   }
 }
 
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
 constexpr int kBM = 128, kBN = 256;
-constexpr int kWaves = 8;                 // 2 (m) x 4 (n), each wave 64 x 64
-constexpr int kLdsRow = kStepK + 8;       // bf16 elements per LDS row (padding breaks bank aliasing)
-constexpr int kStageElems = kBM * kLdsRow;
+constexpr int kABytes = kBM * kStepK * 2;   // activation tile of one step, bf16
+constexpr int kBBytes = kBN * kStepK / 2;   // packed weight tile of one step
+constexpr int kJunk = 1024;                 // LDS that absorbs the loads of unused slots
+
+// s_waitcnt operand that waits until at most n vector-memory loads of this
+// wave are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int wait_vmcnt(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
+}
+
+// 16 bytes per lane from the buffer straight into LDS: lane l's bytes land at
+// dst + 16 * l (dst is the same for the whole wave).  A device-only function:
+// inside a kernel's lambdas the builtin keeps the host compiler from emitting
+// the kernel's launch stub.
+__device__ __forceinline__ void bload16_lds(__amdgpu_buffer_rsrc_t r, unsigned char* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
 
 struct GemmParams {
-  const uint16_t* xp;     // pair-ordered activations [M, K]
-  const uint8_t* packed;
-  const float* scale;
-  const uint8_t* zero;
+  const uint16_t* xp;     // pair-ordered activations [M, kpad], zero past K
+  const uint8_t* packed;  // [N, K/2]
+  const float* xs;        // piece sums [K/piece][mpad]
+  const f32x2_t* sz;      // (scale, -(128 + zero)) [K/G][npad]
   const float* bias;
-  const float* xs;        // [K/min(G,128)][mpad]
   void* y;
-  int32_t m, n, k, group, y_bf16;
+  int32_t m, n, k, kpad, group, y_bf16;
   int64_t mpad;
+  int32_t npad, ngroups, npieces;
   int32_t tiles_m, tiles_n;
 };
 
-template <int GB>
+// GB: 32-input blocks per group piece inside a step (1, 2 or 4); S: LDS stages.
+template <int GB, int S>
 __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
-  constexpr int NP = 4 / GB;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStageElems];
+  constexpr int NP = 4 / GB;                    // group pieces per step
+  constexpr int kPiece = 32 * GB;               // inputs per piece
+  constexpr int kXsOff = kABytes + kBBytes;     // NP x 1 KB of piece sums (512 B used each)
+  constexpr int kSzOff = kXsOff + NP * 1024;    // NP x 2 KB of (scale, -(128 + zero)) pairs
+  constexpr int kStage = kSzOff + NP * 2048;
+  constexpr int kMeta = (3 * NP + 7) / 8;       // metadata loads per wave and stage
+  constexpr int kLoads = 6 + kMeta;             // loads per wave and stage
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  unsigned char* const junk = lds + S * kStage;
+
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int q = lane >> 4, c = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int h = lane >> 5, j = lane & 31;
   const int wm = wave >> 2, wn = wave & 3;
   const int K = p.k, M = p.m, N = p.n;
-  const int ngroups = K / p.group;
-  const int64_t row_bytes = K / 2;
+  const uint32_t row_bytes = (uint32_t)K / 2;
 
   // Workgroups are dealt to the 8 XCDs round robin; renumber so that the
   // workgroups of one XCD cover neighbouring tiles that share weight columns.
@@ -124,172 +186,236 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int nsteps = (K + kStepK - 1) / kStepK;
 
-  f32x4_t acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const __amdgpu_buffer_rsrc_t ra =
+      rsrc(p.xp + (int64_t)m0 * p.kpad, (uint32_t)min(kBM, M - m0) * (uint32_t)p.kpad * 2);
+  const __amdgpu_buffer_rsrc_t rb =
+      rsrc(p.packed + (int64_t)n0 * row_bytes, (uint32_t)min(kBN, N - n0) * row_bytes);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(p.xs, (uint32_t)((int64_t)p.npieces * p.mpad * 4));
+  const __amdgpu_buffer_rsrc_t rz = rsrc(p.sz, (uint32_t)((int64_t)p.ngroups * p.npad * 8));
 
-  int nrow[4];
-  bool nok[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    nrow[nt] = n0 + 64 * wn + 16 * nt + c;
-    nok[nt] = nrow[nt] < N;
-  }
-
-  // Global -> register staging of the activation tile: 2048 chunks of 16 B,
-  // 4 per thread.
-  u32x4_t ga[4];
-  auto load_a = [&](int step) {
+  // ---- one stage of loads: this wave's share, the same count for every wave --
+  // Activation tile: 32 loads of 4 rows x 256 bytes; lane l of load a fills LDS
+  // row 4a + l/16, position l%16 with chunk (l%16) ^ (row & 7) of that row.
+  // Weight tile: 16 loads of 16 rows x 64 bytes; position l%4 of row 16b + l/4
+  // holds chunk (l%4) ^ ((row >> 1) & 3).  Metadata: per piece one load of the
+  // 128 piece sums (lanes 0..31) and two of 128 (scale, zero) pairs each.
+  auto issue_stage = [&](int slot, int step) {
+    unsigned char* st = lds + slot * kStage;
     const int k0 = step * kStepK;
-    const int kw = min(kStepK, K - k0);
+    const uint32_t dead = step < nsteps ? 0u : kOffsetOOB;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int id = tid + 512 * u;
-      const int row = id >> 4, col = (id & 15) * 8;
-      if (m0 + row < M && col < kw)
-        ga[u] = load16(p.xp + (int64_t)(m0 + row) * K + k0 + col);
-      else
-        ga[u] = u32x4_t{0u, 0u, 0u, 0u};
+      const int a = wave * 4 + u;
+      const int row = 4 * a + (lane >> 4);
+      const int c = (lane & 15) ^ (row & 7);
+      bload16_lds(ra, st + a * 1024, ((uint32_t)row * (uint32_t)p.kpad + (uint32_t)(k0 + 8 * c)) * 2 | dead);
     }
-  };
-  auto store_a = [&](int stage) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int id = tid + 512 * u;
-      const int row = id >> 4, col = (id & 15) * 8;
-      *reinterpret_cast<u32x4_t*>(&lds[stage * kStageElems + row * kLdsRow + col]) = ga[u];
-    }
-  };
-
-  u32x4_t gb[4];
-  auto load_b = [&](int step) {
-    const int k0 = step * kStepK;
-    const int nb = min(4, (K - k0) / kBlockK);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      if (nok[nt] && q < nb)
-        gb[nt] = load16(p.packed + (int64_t)nrow[nt] * row_bytes + k0 / 2 + 16 * q);
-      else
-        gb[nt] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-  };
-
-  // The weights of this step leave gb through the transpose; the next step's
-  // loads are issued into gb right after, to land during this step's MFMAs.
-  const uint32_t nib_offset = vgpr_copy(kBf16Offset2);
-  auto compute = [&](int stage, int step) {
-    const int k0 = step * kStepK;
-    const int nb = min(4, (K - k0) / kBlockK);
-    uint32_t dw[4][4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      uint32_t d0 = gb[nt][0], d1 = gb[nt][1], d2 = gb[nt][2], d3 = gb[nt][3];
-      transpose4_lanegroups(d0, d1, d2, d3);
-      dw[nt][0] = d0; dw[nt][1] = d1; dw[nt][2] = d2; dw[nt][3] = d3;
-    }
-    if (step + 1 < nsteps) load_b(step + 1);
-#pragma unroll
-    for (int pc = 0; pc < NP; ++pc) {
-      if (pc * GB >= nb) break;
-      const int g = (k0 + kBlockK * pc * GB) / p.group;
-      const int pi = (k0 + kBlockK * pc * GB) / (kBlockK * GB);
-      // metadata of this piece: per-row activation sums, per-column scale and zero
-      f32x4_t xsv[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        xsv[mt] = *reinterpret_cast<const f32x4_t*>(p.xs + (int64_t)pi * p.mpad + m0 + 64 * wm + 16 * mt + 4 * q);
-      float sv[4], zv[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int64_t gi = (int64_t)(nok[nt] ? nrow[nt] : 0) * ngroups + g;
-        sv[nt] = nok[nt] ? p.scale[gi] : 0.f;
-        zv[nt] = -(kNibOffset + (float)(nok[nt] ? p.zero[gi] : 0));
-      }
-      bf16x8_t af[4][GB];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int e = 0; e < GB; ++e)
-          af[mt][e] = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const u32x4_t*>(
-                            &lds[stage * kStageElems + (64 * wm + 16 * mt + c) * kLdsRow +
-                                 kBlockK * (pc * GB + e) + 8 * q]));
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        f32x4_t cg[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) cg[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int e = 0; e < GB; ++e) {
-          const bf16x8_t bf = unpack_codes(dw[nt][pc * GB + e], kNibPairMask, nib_offset);
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) cg[mt] = mfma_bf16(af[mt][e], bf, cg[mt]);
-        }
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc[nt][mt][r] = fmaf(sv[nt], fmaf(zv[nt], xsv[mt][r], cg[mt][r]), acc[nt][mt][r]);
-      }
-    }
-  };
-
-  if (nsteps > 0) {
-    load_a(0);
-    load_b(0);
-    store_a(0);
-    __syncthreads();
-  }
-  for (int i0 = 0; i0 < nsteps; i0 += 2) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int i = i0 + u;
-      if (i < nsteps) {
-        const bool more = i + 1 < nsteps;
-        if (more) load_a(i + 1);
-        compute(u, i);
-        if (more) store_a(u ^ 1);
-        __syncthreads();
-      }
+      const int b = wave * 2 + u;
+      const int row = 16 * b + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 1) & 3);
+      const uint32_t off = (uint32_t)(k0 / 2 + 16 * c) < row_bytes
+                               ? (uint32_t)row * row_bytes + (uint32_t)(k0 / 2 + 16 * c) : kOffsetOOB;
+      bload16_lds(rb, st + kABytes + b * 1024, off | dead);
     }
+#pragma unroll
+    for (int u = 0; u < kMeta; ++u) {
+      const int mi = wave * kMeta + u;       // uniform
+      const int pc = mi / 3, part = mi - 3 * pc;
+      unsigned char* dst = junk;
+      uint32_t off = kOffsetOOB;
+      if (pc < NP) {
+        if (part == 0) {
+          const int pi = (k0 + pc * kPiece) / kPiece;
+          dst = st + kXsOff + pc * 1024;
+          if (lane < 32 && pi < p.npieces)
+            off = (uint32_t)(((int64_t)pi * p.mpad + m0 + 4 * lane) * 4);
+        } else {
+          const int g = (k0 + pc * kPiece) / p.group;
+          dst = st + kSzOff + pc * 2048 + (part - 1) * 1024;
+          if (g < p.ngroups)
+            off = (uint32_t)(((int64_t)g * p.npad + n0 + 128 * (part - 1) + 2 * lane) * 8);
+        }
+      }
+      bload16_lds(pc < NP && part == 0 ? rx : rz, dst, off | dead);
+    }
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  const uint32_t nib_offset = vgpr_copy(kBf16Offset2);
+  // LDS byte offsets of this lane's operand rows inside a stage.
+  int arow[2], brow[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    arow[t] = 64 * wm + 32 * t + j;
+    brow[t] = 64 * wn + 32 * t + j;
   }
 
+  auto compute = [&](int slot, int step) {
+    const unsigned char* st = lds + slot * kStage;
+    const int k0 = step * kStepK;
+    f32x16_t cg[2][2];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int n = nrow[nt];
-    if (!nok[nt]) continue;
-    const float b = p.bias ? p.bias[n] : 0.f;
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 64 * wm + 16 * mt + 4 * q + r;
+        for (int r = 0; r < 16; ++r) cg[a][b][r] = 0.f;
+    auto fold = [&](int pc) {
+      if (k0 + pc * kPiece >= K) return;     // a piece past the end of the inputs
+      f32x4_t xsv[2][4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+          xsv[mt][rq] = *reinterpret_cast<const f32x4_t*>(
+              st + kXsOff + pc * 1024 + (64 * wm + 32 * mt + 8 * rq + 4 * h) * 4);
+      f32x2_t szv[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        szv[nt] = *reinterpret_cast<const f32x2_t*>(st + kSzOff + pc * 2048 + brow[nt] * 8);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            acc[mt][nt][r] = fmaf(szv[nt][0], fmaf(szv[nt][1], xsv[mt][r >> 2][r & 3], cg[mt][nt][r]),
+                                  acc[mt][nt][r]);
+            cg[mt][nt][r] = 0.f;
+          }
+    };
+#pragma unroll
+    for (int L = 0; L < 2; ++L) {
+      uint32_t bd[2][4];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int row = brow[nt];
+        const int c = (2 * L + h) ^ ((row >> 1) & 3);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + kABytes + row * 64 + 16 * c);
+        bd[nt][0] = v[0]; bd[nt][1] = v[1]; bd[nt][2] = v[2]; bd[nt][3] = v[3];
+        if constexpr (GB == 1) {
+          // Regroup for 32-input groups: the lower lanes keep their inputs
+          // 0..15 and take the upper lanes' 32..47; the upper lanes end with
+          // 16..31 and 48..63.  Dwords 0, 1 then lie in the unit's first
+          // group on both halves, dwords 2, 3 in its second.
+          auto s0 = __builtin_amdgcn_permlane32_swap(bd[nt][0], bd[nt][2], false, false);
+          bd[nt][0] = s0[0]; bd[nt][2] = s0[1];
+          auto s1 = __builtin_amdgcn_permlane32_swap(bd[nt][1], bd[nt][3], false, false);
+          bd[nt][1] = s1[0]; bd[nt][3] = s1[1];
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        // 8-input chunk of the activations that matches dword b of this half
+        const int cin = GB == 1 ? 4 * (b >> 1) + 2 * h + (b & 1) : 4 * h + b;
+        bf16x8_t af[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const int row = arow[mt];
+          const int c = (8 * L + cin) ^ (row & 7);
+          af[mt] = *reinterpret_cast<const bf16x8_t*>(st + row * 256 + 16 * c);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const bf16x8_t bf = unpack_codes(bd[nt][b], kNibPairMask, nib_offset);
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) cg[mt][nt] = mfma32(af[mt], bf, cg[mt][nt]);
+        }
+        if constexpr (GB == 1) {
+          if (b == 1) fold(2 * L);
+          if (b == 3) fold(2 * L + 1);
+        }
+      }
+      if constexpr (GB == 2) fold(L);
+    }
+    if constexpr (GB == 4) fold(0);
+  };
+
+  // ---- the ring: stage i lives in slot i % S --------------------------------
+#pragma unroll
+  for (int s = 0; s < S; ++s) issue_stage(s, s);
+  int slot = 0;
+  for (int i = 0; i < nsteps; ++i) {
+    // this wave's loads of stage i have landed ...
+    if (i == 0)
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt((S - 1) * kLoads));
+    else
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt((S - 2) * kLoads));
+    // ... and everyone's have; everyone has also finished step i - 1, so its
+    // slot takes step i - 1 + S.  A plain barrier: a __syncthreads fence would
+    // also wait for the loads still streaming into the other stages.
+    __builtin_amdgcn_s_barrier();
+    if (i >= 1) issue_stage(slot == 0 ? S - 1 : slot - 1, i - 1 + S);
+    compute(slot, i);
+    slot = slot == S - 1 ? 0 : slot + 1;
+  }
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int n = n0 + brow[nt];
+      if (n >= N) continue;
+      const float b = p.bias ? p.bias[n] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + 64 * wm + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
         if (m < M) {
-          const float v = acc[nt][mt][r] + b;
+          const float v = acc[mt][nt][r] + b;
           if (p.y_bf16)
             reinterpret_cast<uint16_t*>(p.y)[(int64_t)m * N + n] = f32_to_bf16_bits(v);
           else
             reinterpret_cast<float*>(p.y)[(int64_t)m * N + n] = v;
         }
       }
+    }
+}
+
+template <int GB, int S>
+size_t gemm_lds_bytes() {
+  constexpr int NP = 4 / GB;
+  return (size_t)S * (kABytes + kBBytes + NP * 1024 + NP * 2048) + kJunk;
+}
+
+template <int GB, int S>
+int32_t launch_gemm_t(const GemmParams& gp, hipStream_t stream) {
+  auto kern = gemm_kernel<GB, S>;
+  const size_t lds = gemm_lds_bytes<GB, S>();
+  static bool raised = false;   // raise the dynamic-LDS limit once per instantiation
+  if (!raised) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return WOQ_EHIP;
+    raised = true;
   }
+  hipLaunchKernelGGL(kern, dim3((unsigned)(gp.tiles_m * gp.tiles_n)), dim3(512), lds, stream, gp);
+  return hip_status(hipGetLastError());
 }
 
 }  // namespace
 
-int32_t launch_prep(const uint16_t* x, const int32_t* order, int32_t m, int32_t k, int32_t group,
-                    int32_t permute, uint16_t* xg, float* xs, int64_t mpad, hipStream_t stream) {
+int32_t launch_prep(const uint16_t* x, const int32_t* order, int32_t m, int32_t k, int32_t kpad,
+                    int32_t group, int32_t permute, uint16_t* xg, float* xs, int64_t mpad,
+                    hipStream_t stream) {
   const int32_t piece = group < kStepK ? group : kStepK;
-  const int64_t total = mpad * (k / 8);
+  const int64_t total = mpad * (kpad / 8);
   if (total == 0) return WOQ_OK;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   switch (piece / 8) {
-    case 4: hipLaunchKernelGGL(prep_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, x, order, m, k, permute, xg, xs, mpad); break;
-    case 8: hipLaunchKernelGGL(prep_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, stream, x, order, m, k, permute, xg, xs, mpad); break;
-    case 16: hipLaunchKernelGGL(prep_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, x, order, m, k, permute, xg, xs, mpad); break;
+    case 4: hipLaunchKernelGGL(prep_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, x, order, m, k, kpad, permute, xg, xs, mpad); break;
+    case 8: hipLaunchKernelGGL(prep_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, stream, x, order, m, k, kpad, permute, xg, xs, mpad); break;
+    case 16: hipLaunchKernelGGL(prep_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, x, order, m, k, kpad, permute, xg, xs, mpad); break;
     default: return WOQ_EUNSUPPORTED;
   }
   return hip_status(hipGetLastError());
@@ -306,17 +432,33 @@ int32_t launch_fill_bias(const float* bias, int32_t m, int32_t n, int32_t y_bf16
   return hip_status(hipGetLastError());
 }
 
-int32_t launch_gemm(const LinearArgs& a, const LinearPlan& pl, hipStream_t stream) {
-  GemmParams gp{a.x, a.packed, a.scale, a.zero, a.bias, a.xs, a.y, a.m, a.n, a.k, a.group,
-                a.y_bf16, a.mpad, (a.m + kBM - 1) / kBM, (a.n + kBN - 1) / kBN};
-  const unsigned grid = (unsigned)(gp.tiles_m * gp.tiles_n);
+size_t gemm_sz_bytes(int64_t n, int64_t k, int32_t group) {
+  const int64_t npad = (n + kBN - 1) / kBN * kBN;
+  return (size_t)(k / group) * (size_t)npad * 8;
+}
+
+int32_t launch_gemm(const LinearArgs& a, const LinearPlan& pl, void* sz_ws, hipStream_t stream) {
+  const int32_t ngroups = a.k / a.group;
+  const int32_t npad = (a.n + kBN - 1) / kBN * kBN;
+  {
+    const int64_t total = (int64_t)ngroups * npad;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(sz_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.scale, a.zero,
+                       a.n, ngroups, npad, static_cast<f32x2_t*>(sz_ws));
+    const int32_t st = hip_status(hipGetLastError());
+    if (st != WOQ_OK) return st;
+  }
+  const int32_t piece = a.group < kStepK ? a.group : kStepK;
+  GemmParams gp{a.x, a.packed, a.xs, static_cast<const f32x2_t*>(sz_ws), a.bias, a.y,
+                a.m, a.n, a.k, a.kpad, a.group, a.y_bf16, a.mpad, npad, ngroups, a.k / piece,
+                (a.m + kBM - 1) / kBM, (a.n + kBN - 1) / kBN};
   switch (pl.gb) {
-    case 1: hipLaunchKernelGGL(gemm_kernel<1>, dim3(grid), dim3(512), 0, stream, gp); break;
-    case 2: hipLaunchKernelGGL(gemm_kernel<2>, dim3(grid), dim3(512), 0, stream, gp); break;
-    case 4: hipLaunchKernelGGL(gemm_kernel<4>, dim3(grid), dim3(512), 0, stream, gp); break;
+    case 1: return launch_gemm_t<1, 2>(gp, stream);
+    case 2: return launch_gemm_t<2, 2>(gp, stream);
+    case 4: return launch_gemm_t<4, 3>(gp, stream);
     default: return WOQ_EUNSUPPORTED;
   }
-  return hip_status(hipGetLastError());
 }
 
 }  // namespace woq

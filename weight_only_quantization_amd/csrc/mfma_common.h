@@ -17,6 +17,7 @@ namespace woq {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // bf16 bit pattern 0x4300 is 128.0; OR-ing a nibble n into its low mantissa

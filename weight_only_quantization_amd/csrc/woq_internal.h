@@ -26,8 +26,9 @@ inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_
 
 // Workspace carve-up of the linear layer (all offsets 256-byte aligned).
 struct LinearWorkspace {
-  size_t xg_off = 0, xg_bytes = 0;   // gathered and/or pair-permuted activations, bf16 [M, K]
+  size_t xg_off = 0, xg_bytes = 0;   // gathered and/or pair-permuted activations, bf16 [M, kpad]
   size_t xs_off = 0, xs_bytes = 0;   // per-piece activation sums, f32 [K/min(G,128)][Mpad]
+  size_t sz_off = 0, sz_bytes = 0;   // (scale, -(128 + zero)) pairs, f32x2 [K/G][N rounded to 256]
   size_t total = 0;
 };
 
@@ -74,15 +75,19 @@ struct LinearArgs {
   const float* xs;         // per-piece sums [K/min(G,128)][mpad] (GEMM path)
   int32_t m, n, k, group;
   int32_t y_bf16;
+  int32_t kpad;            // row stride of x (K rounded up to 128 on the GEMM path)
   int64_t mpad;
 };
 
-int32_t launch_prep(const uint16_t* x, const int32_t* order, int32_t m, int32_t k, int32_t group,
-                    int32_t permute, uint16_t* xg, float* xs, int64_t mpad, hipStream_t stream);
+int32_t launch_prep(const uint16_t* x, const int32_t* order, int32_t m, int32_t k, int32_t kpad,
+                    int32_t group, int32_t permute, uint16_t* xg, float* xs, int64_t mpad,
+                    hipStream_t stream);
 int32_t launch_skinny(const LinearArgs& a, const LinearPlan& p, hipStream_t stream);
 size_t skinny_lds_bytes(int64_t m, int64_t k, int64_t group, int waves, int ns);
 constexpr size_t kSkinnyLdsLimit = 160 * 1024;   // staged activations, scales and zeros share the 160 KB of LDS per CU
-int32_t launch_gemm(const LinearArgs& a, const LinearPlan& p, hipStream_t stream);
+size_t gemm_sz_bytes(int64_t n, int64_t k, int32_t group);
+constexpr int64_t kGemmMaxK = (int64_t)1 << 24;   // tile offsets of the GEMM path are 32-bit
+int32_t launch_gemm(const LinearArgs& a, const LinearPlan& p, void* sz_ws, hipStream_t stream);
 int32_t launch_fill_bias(const float* bias, int32_t m, int32_t n, int32_t y_bf16, void* y,
                          hipStream_t stream);
 
