@@ -23,7 +23,9 @@
 // lane half), which keeps every MFMA inside one group for groups of 64 and
 // more; 32-input groups regroup the dwords between the lane halves with two
 // v_permlane32_swap.  Per group piece the MFMA sums fold into float32
-// accumulators as acc += scale * (sum - (128 + zero) * piece_sum_of_x).
+// accumulators as acc += scale * sum; the zero-point term
+// -scale * (128 + zero) * piece_sum_of_x is an outer product and is added by
+// float32 MFMAs (v_mfma_f32_32x32x2_f32), two pieces per instruction.
 #include "woq_internal.h"
 #include "mfma_common.h"
 
@@ -142,6 +144,11 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// float32 32x32x2: lane l supplies row (or column) l % 32 of input l / 32
+__device__ __forceinline__ f32x16_t mfma32f(float a, float b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
 struct GemmParams {
   const uint16_t* xp;     // pair-ordered activations [M, kpad], zero past K
   const uint8_t* packed;  // [N, K/2]
@@ -249,9 +256,10 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  const f32x16_t zero16 = {};
 
   const uint32_t nib_offset = vgpr_copy(kBf16Offset2);
-  // LDS byte offsets of this lane's operand rows inside a stage.
+  // this lane's activation row (A operand) and weight row (B operand) per tile
   int arow[2], brow[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -259,85 +267,133 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
     brow[t] = 64 * wn + 32 * t + j;
   }
 
+  // zero-point operands carried from an even step to the next (one piece per step)
+  float zpa[2] = {0.f, 0.f}, zpb[2] = {0.f, 0.f};
+
   auto compute = [&](int slot, int step) {
     const unsigned char* st = lds + slot * kStage;
     const int k0 = step * kStepK;
-    f32x16_t cg[2][2];
+    // The zero-point part of a piece, -scale * (128 + zero) * piece_sum_of_x,
+    // is an outer product of a column factor and a row factor: it goes
+    // through the matrix unit, two pieces per float32 MFMA.  Operands for
+    // piece pc: row factor -sum_of_x of this lane's activation row, column
+    // factor scale * (128 + zero) of its weight row (zero past the inputs).
+    auto zp_operands = [&](int pc, float (&a)[2], float (&b)[2]) {
+      const bool in = k0 + pc * kPiece < K;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+      for (int mt = 0; mt < 2; ++mt) {
+        const float xv = *reinterpret_cast<const float*>(st + kXsOff + pc * 1024 + arow[mt] * 4);
+        a[mt] = in ? -xv : 0.f;
+      }
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) cg[a][b][r] = 0.f;
-    auto fold = [&](int pc) {
-      if (k0 + pc * kPiece >= K) return;     // a piece past the end of the inputs
-      f32x4_t xsv[2][4];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq)
-          xsv[mt][rq] = *reinterpret_cast<const f32x4_t*>(
-              st + kXsOff + pc * 1024 + (64 * wm + 32 * mt + 8 * rq + 4 * h) * 4);
-      f32x2_t szv[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        szv[nt] = *reinterpret_cast<const f32x2_t*>(st + kSzOff + pc * 2048 + brow[nt] * 8);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            acc[mt][nt][r] = fmaf(szv[nt][0], fmaf(szv[nt][1], xsv[mt][r >> 2][r & 3], cg[mt][nt][r]),
-                                  acc[mt][nt][r]);
-            cg[mt][nt][r] = 0.f;
-          }
+      for (int nt = 0; nt < 2; ++nt) {
+        const f32x2_t v = *reinterpret_cast<const f32x2_t*>(st + kSzOff + pc * 2048 + brow[nt] * 8);
+        b[nt] = -v[0] * v[1];
+      }
     };
+    auto correct = [&]() {
+      if constexpr (NP == 1) {
+        // One piece per step: lane half h carries the pieces of steps with
+        // parity h; the MFMA runs after every odd step.
+        float a[2], b[2];
+        zp_operands(0, a, b);
+        const bool mine = h == (step & 1);
 #pragma unroll
-    for (int L = 0; L < 2; ++L) {
-      uint32_t bd[2][4];
+        for (int t = 0; t < 2; ++t) {
+          zpa[t] = mine ? a[t] : zpa[t];
+          zpb[t] = mine ? b[t] : zpb[t];
+        }
+        if (step & 1) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32f(zpa[mt], zpb[nt], acc[mt][nt]);
+        }
+      } else {
+#pragma unroll
+        for (int pp = 0; pp < NP; pp += 2) {
+          float a[2], b[2];
+          zp_operands(pp + h, a, b);       // lane half h: piece pp + h
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32f(a[mt], b[nt], acc[mt][nt]);
+        }
+      }
+    };
+    // All weight bytes of the step, then the activation fragments one 16-input
+    // block ahead of the MFMAs that use them.
+    uint32_t bd[2][2][4];
+#pragma unroll
+    for (int L = 0; L < 2; ++L)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int row = brow[nt];
         const int c = (2 * L + h) ^ ((row >> 1) & 3);
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + kABytes + row * 64 + 16 * c);
-        bd[nt][0] = v[0]; bd[nt][1] = v[1]; bd[nt][2] = v[2]; bd[nt][3] = v[3];
+        bd[L][nt][0] = v[0]; bd[L][nt][1] = v[1]; bd[L][nt][2] = v[2]; bd[L][nt][3] = v[3];
         if constexpr (GB == 1) {
           // Regroup for 32-input groups: the lower lanes keep their inputs
           // 0..15 and take the upper lanes' 32..47; the upper lanes end with
           // 16..31 and 48..63.  Dwords 0, 1 then lie in the unit's first
           // group on both halves, dwords 2, 3 in its second.
-          auto s0 = __builtin_amdgcn_permlane32_swap(bd[nt][0], bd[nt][2], false, false);
-          bd[nt][0] = s0[0]; bd[nt][2] = s0[1];
-          auto s1 = __builtin_amdgcn_permlane32_swap(bd[nt][1], bd[nt][3], false, false);
-          bd[nt][1] = s1[0]; bd[nt][3] = s1[1];
+          auto s0 = __builtin_amdgcn_permlane32_swap(bd[L][nt][0], bd[L][nt][2], false, false);
+          bd[L][nt][0] = s0[0]; bd[L][nt][2] = s0[1];
+          auto s1 = __builtin_amdgcn_permlane32_swap(bd[L][nt][1], bd[L][nt][3], false, false);
+          bd[L][nt][1] = s1[0]; bd[L][nt][3] = s1[1];
         }
       }
+    auto load_af = [&](int blk, bf16x8_t (&af)[2]) {
+      const int L = blk >> 2, b = blk & 3;
+      // 8-input chunk of the activations that matches dword b of this half
+      const int cin = GB == 1 ? 4 * (b >> 1) + 2 * h + (b & 1) : 4 * h + b;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        // 8-input chunk of the activations that matches dword b of this half
-        const int cin = GB == 1 ? 4 * (b >> 1) + 2 * h + (b & 1) : 4 * h + b;
-        bf16x8_t af[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const int row = arow[mt];
-          const int c = (8 * L + cin) ^ (row & 7);
-          af[mt] = *reinterpret_cast<const bf16x8_t*>(st + row * 256 + 16 * c);
-        }
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const bf16x8_t bf = unpack_codes(bd[nt][b], kNibPairMask, nib_offset);
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) cg[mt][nt] = mfma32(af[mt], bf, cg[mt][nt]);
-        }
-        if constexpr (GB == 1) {
-          if (b == 1) fold(2 * L);
-          if (b == 3) fold(2 * L + 1);
-        }
+      for (int mt = 0; mt < 2; ++mt) {
+        const int row = arow[mt];
+        const int c = (8 * L + cin) ^ (row & 7);
+        af[mt] = *reinterpret_cast<const bf16x8_t*>(st + row * 256 + 16 * c);
       }
-      if constexpr (GB == 2) fold(L);
+    };
+    // Fold of one group piece: acc += scale * sum (the zero-point part is
+    // added by correct()).
+    f32x16_t cg[2][2];
+    auto fold = [&](int pc) {
+      if (k0 + pc * kPiece >= K) return;     // a piece past the end of the inputs
+      float sv[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        sv[nt] = *reinterpret_cast<const float*>(st + kSzOff + pc * 2048 + brow[nt] * 8);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mt][nt][r] = fmaf(sv[nt], cg[mt][nt][r], acc[mt][nt][r]);
+    };
+    bf16x8_t afc[2], afn[2];
+    // The two waves of a SIMD leave the barrier together; raising this wave's
+    // priority for its MFMA phase lets one of them run ahead, so that one
+    // folds (VALU) while the other keeps the matrix unit busy.
+    __builtin_amdgcn_s_setprio(1);
+    load_af(0, afc);
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+      const int L = blk >> 2, b = blk & 3;
+      constexpr int kBlocksPerPiece = 8 / NP;
+      const bool first = blk % kBlocksPerPiece == 0;      // a new piece starts
+      if (blk + 1 < 8) load_af(blk + 1, afn);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const bf16x8_t bf = unpack_codes(bd[L][nt][b], kNibPairMask, nib_offset);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) cg[mt][nt] = mfma32(afc[mt], bf, first ? zero16 : cg[mt][nt]);
+      }
+      if (blk % kBlocksPerPiece == kBlocksPerPiece - 1) fold(blk / kBlocksPerPiece);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) afc[mt] = afn[mt];
     }
-    if constexpr (GB == 4) fold(0);
+    __builtin_amdgcn_s_setprio(0);
+    correct();
   };
 
   // ---- the ring: stage i lives in slot i % S --------------------------------
@@ -359,6 +415,16 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
     slot = slot == S - 1 ? 0 : slot + 1;
   }
   __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+  if constexpr (4 / GB == 1) {
+    if (nsteps & 1) {   // the last (even) step's zero-point term is still pending
+#pragma unroll
+      for (int t = 0; t < 2; ++t) zpa[t] = h ? 0.f : zpa[t];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32f(zpa[mt], zpb[nt], acc[mt][nt]);
+    }
+  }
 
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
