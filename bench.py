@@ -145,6 +145,83 @@ def measure_prefill(torch, woq, reps: int = 5):
                 per_shape=out, plan=woq.linear_plan(2048, 14336, 4096, GROUP))
 
 
+def measure_configs(torch, woq, reps: int = 40, pool_bytes: int = 1 << 30):
+    """Per-launch time of every small-M sweep and act-order configuration.
+
+    Weights are random bytes in the Int4GroupLinear layout (timing does not
+    depend on the values); each configuration rotates over enough copies
+    (>= 1 GB in all) that every launch reads its weights from HBM, not from
+    the 256 MB last-level cache.  Launches are replayed from one HIP graph and
+    timed with events around it.
+    """
+    from workloads import ACTORDER, SWEEP
+
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    out = []
+    pools = {}
+    for case in (*SWEEP, *ACTORDER):
+        key = (case.n, case.k, case.group)
+        wb = weight_bytes(case.n, case.k, case.group)
+        if key not in pools:
+            pools.clear()
+            torch.cuda.empty_cache()
+            copies = max(2, -(-pool_bytes // wb))
+            pools[key] = [
+                (torch.randint(0, 256, (case.n, case.k // 2), generator=gen, device=dev, dtype=torch.uint8),
+                 torch.rand((case.n, case.k // case.group), generator=gen, device=dev).mul_(0.01).add_(1e-3),
+                 torch.randint(0, 16, (case.n, case.k // case.group), generator=gen, device=dev, dtype=torch.uint8))
+                for _ in range(copies)]
+        pool = pools[key]
+        x = torch.randn((case.m, case.k), generator=gen, device=dev).to(torch.bfloat16)
+        y = torch.empty((case.m, case.n), dtype=torch.bfloat16, device=dev)
+        bias = torch.randn((case.n,), generator=gen, device=dev).mul_(0.01) if case.has_bias else None
+        order = (torch.randperm(case.k, generator=gen, device=dev).to(torch.int32)
+                 if case.act_order else None)
+        ws_bytes = woq.linear_workspace_bytes(case.m, case.n, case.k, case.group, order is not None)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+        def call(i):
+            p, sc, z = pool[i % len(pool)]
+            woq.linear_int4_groups(x, p, sc, z, bias=bias, order=order, group=case.group, out=y,
+                                   workspace=ws if ws_bytes else None)
+
+        for i in range(len(pool)):
+            call(i)
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call(0)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                call(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / reps
+        flops = 2.0 * case.m * case.n * case.k
+        ab = algorithmic_bytes(case.m, case.n, case.k, case.has_bias, case.group) + (
+            case.k * 4 if case.act_order else 0)
+        out.append(dict(name=case.name, m=case.m, n=case.n, k=case.k, group=case.group,
+                        us=round(t * 1e6, 2), weight_GBps=round(wb / t / 1e9, 1),
+                        hbm_frac=round(ab / t / 1e9 / HBM_PEAK_GBS, 4),
+                        tflops=round(flops / t / 1e12, 2),
+                        mfma_frac=round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+                        plan=woq.linear_plan(case.m, case.n, case.k, case.group, order is not None)))
+        del g
+    pools.clear()
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(min_seconds: float = 10.0, max_passes: int = 8):
     """The CPU oracle's linear over one Llama-3-8B layer's seven M=1 linears.
 
@@ -287,6 +364,8 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the small-M sweep and act-order per-launch timings")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -371,6 +450,7 @@ def main():
         del src, dst
 
     prefill = None if args.no_prefill else measure_prefill(torch, woq)
+    configs = None if args.no_configs else measure_configs(torch, woq)
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     line = dict(
@@ -383,7 +463,7 @@ def main():
                     weight_bytes_per_step=wbytes, hbm_peak_frac=round(value / HBM_PEAK_GBS, 4),
                     graph=graph is not None, accumulate="f32",
                     tokens_per_s_linears_only=round(1.0 / (ms_per_step * 1e-3), 1) if args.layers == 32 else None),
-        roofline=roofline, prefill=prefill, cpu_baseline=cpu,
+        roofline=roofline, prefill=prefill, configs=configs, cpu_baseline=cpu,
     )
     print(json.dumps(line), flush=True)
 

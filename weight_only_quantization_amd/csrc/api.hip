@@ -65,7 +65,8 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
   p.gb = group >= 128 ? 4 : group / 32;
   const int64_t nsub = (n + 15) / 16;
   const int skinny_ns = (nsub >= 2048 && p.gb >= 2) ? 2 : 1;
-  if (m <= 16 && k < ((int64_t)1 << 26) &&
+  static const bool force_tiled = std::getenv("WOQ_FORCE_TILED") != nullptr;   // tuning aid
+  if (m <= 16 && !force_tiled && k < ((int64_t)1 << 26) &&
       skinny_lds_bytes(m, k, group, 8, skinny_ns) <= kSkinnyLdsLimit) {
     p.path = 1;
     p.mt = 1;
@@ -95,11 +96,19 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
   }
   p.path = 2;
   p.prep = 1;
-  p.bm = 128;
-  p.bn = 256;
-  p.waves = 8;
+  // Tile by the number of activation rows: at small M, narrow tiles keep the
+  // grid wide enough to cover the chip.
+  if (m > 128) {
+    p.bm = 128; p.bn = 256; p.waves = 8;
+  } else if (m > 64) {
+    p.bm = 128; p.bn = 64; p.waves = 4;
+  } else if (m > 32) {
+    p.bm = 64; p.bn = 64; p.waves = 4;
+  } else {
+    p.bm = 32; p.bn = 64; p.waves = 2;
+  }
   p.mpad = ((m + 127) / 128) * 128;
-  p.grid = ((m + 127) / 128) * ((n + 255) / 256);
+  p.grid = ((m + p.bm - 1) / p.bm) * ((n + p.bn - 1) / p.bn);
   return p;
 }
 

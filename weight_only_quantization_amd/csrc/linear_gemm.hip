@@ -119,10 +119,23 @@ __global__ __launch_bounds__(256) void fill_bias_kernel(const float* __restrict_
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128, kBN = 256;
-constexpr int kABytes = kBM * kStepK * 2;   // activation tile of one step, bf16
-constexpr int kBBytes = kBN * kStepK / 2;   // packed weight tile of one step
 constexpr int kJunk = 1024;                 // LDS that absorbs the loads of unused slots
+constexpr int kNPad = 256;                  // column padding of the (scale, zero) table
+
+// Workgroup tile: WM x WN waves, each holding MT x NT tiles of 32 x 32 outputs.
+template <int WM_, int WN_, int MT_, int NT_>
+struct Tile {
+  static constexpr int WM = WM_, WN = WN_, MT = MT_, NT = NT_;
+  static constexpr int kWaves = WM * WN;
+  static constexpr int BM = 32 * MT * WM, BN = 32 * NT * WN;
+  static constexpr int kABytes = BM * kStepK * 2;   // activation tile of one step, bf16
+  static constexpr int kBBytes = BN * kStepK / 2;   // packed weight tile of one step
+  static constexpr int kA = BM / 4;                 // 1 KB activation loads per stage
+  static constexpr int kB = BN / 16;                // 1 KB weight loads per stage
+  static constexpr int kAPer = (kA + kWaves - 1) / kWaves;
+  static constexpr int kBPer = (kB + kWaves - 1) / kWaves;
+  static constexpr int kSzParts = (BN + 127) / 128; // 1 KB (scale, zero) loads per piece
+};
 
 // s_waitcnt operand that waits until at most n vector-memory loads of this
 // wave are outstanding (expcnt and lgkmcnt left at their maxima).
@@ -162,16 +175,22 @@ struct GemmParams {
   int32_t tiles_m, tiles_n;
 };
 
-// GB: 32-input blocks per group piece inside a step (1, 2 or 4); S: LDS stages.
-template <int GB, int S>
-__global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
+// Tl: workgroup tile; GB: 32-input blocks per group piece inside a step (1, 2
+// or 4); S: LDS stages.
+template <class Tl, int GB, int S>
+__global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
+  constexpr int MT = Tl::MT, NT = Tl::NT, kWaves = Tl::kWaves;
+  constexpr int BM = Tl::BM, BN = Tl::BN;
+  constexpr int kABytes = Tl::kABytes, kBBytes = Tl::kBBytes;
   constexpr int NP = 4 / GB;                    // group pieces per step
   constexpr int kPiece = 32 * GB;               // inputs per piece
   constexpr int kXsOff = kABytes + kBBytes;     // NP x 1 KB of piece sums (512 B used each)
-  constexpr int kSzOff = kXsOff + NP * 1024;    // NP x 2 KB of (scale, -(128 + zero)) pairs
-  constexpr int kStage = kSzOff + NP * 2048;
-  constexpr int kMeta = (3 * NP + 7) / 8;       // metadata loads per wave and stage
-  constexpr int kLoads = 6 + kMeta;             // loads per wave and stage
+  constexpr int kSzOff = kXsOff + NP * 1024;    // NP x kSzParts KB of (scale, -(128 + zero)) pairs
+  constexpr int kSzStride = Tl::kSzParts * 1024;
+  constexpr int kStage = kSzOff + NP * kSzStride;
+  constexpr int kMetaTotal = NP * (1 + Tl::kSzParts);
+  constexpr int kMeta = (kMetaTotal + kWaves - 1) / kWaves;   // metadata loads per wave and stage
+  constexpr int kLoads = Tl::kAPer + Tl::kBPer + kMeta;      // loads per wave and stage
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   unsigned char* const junk = lds + S * kStage;
 
@@ -179,7 +198,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int h = lane >> 5, j = lane & 31;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / Tl::WN, wn = wave % Tl::WN;
   const int K = p.k, M = p.m, N = p.n;
   const uint32_t row_bytes = (uint32_t)K / 2;
 
@@ -190,46 +209,50 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
   const int full = (nwg / 8) * 8;
   if (bid < full) bid = (bid % 8) * (full / 8) + bid / 8;
   const int tm = bid % p.tiles_m, tn = bid / p.tiles_m;
-  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int m0 = tm * BM, n0 = tn * BN;
   const int nsteps = (K + kStepK - 1) / kStepK;
 
   const __amdgpu_buffer_rsrc_t ra =
-      rsrc(p.xp + (int64_t)m0 * p.kpad, (uint32_t)min(kBM, M - m0) * (uint32_t)p.kpad * 2);
+      rsrc(p.xp + (int64_t)m0 * p.kpad, (uint32_t)min(BM, M - m0) * (uint32_t)p.kpad * 2);
   const __amdgpu_buffer_rsrc_t rb =
-      rsrc(p.packed + (int64_t)n0 * row_bytes, (uint32_t)min(kBN, N - n0) * row_bytes);
+      rsrc(p.packed + (int64_t)n0 * row_bytes, (uint32_t)min(BN, N - n0) * row_bytes);
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.xs, (uint32_t)((int64_t)p.npieces * p.mpad * 4));
   const __amdgpu_buffer_rsrc_t rz = rsrc(p.sz, (uint32_t)((int64_t)p.ngroups * p.npad * 8));
 
   // ---- one stage of loads: this wave's share, the same count for every wave --
-  // Activation tile: 32 loads of 4 rows x 256 bytes; lane l of load a fills LDS
-  // row 4a + l/16, position l%16 with chunk (l%16) ^ (row & 7) of that row.
-  // Weight tile: 16 loads of 16 rows x 64 bytes; position l%4 of row 16b + l/4
-  // holds chunk (l%4) ^ ((row >> 1) & 3).  Metadata: per piece one load of the
-  // 128 piece sums (lanes 0..31) and two of 128 (scale, zero) pairs each.
+  // Activation tile: BM/4 loads of 4 rows x 256 bytes; lane l of load a fills
+  // LDS row 4a + l/16, position l%16 with chunk (l%16) ^ (row & 7) of that row.
+  // Weight tile: BN/16 loads of 16 rows x 64 bytes; position l%4 of row
+  // 16b + l/4 holds chunk (l%4) ^ ((row >> 1) & 3).  Metadata: per piece one
+  // load of 128 piece sums (lanes 0..31) and 128 (scale, zero) pairs per load.
+  // Load slots past the tile's count read nothing into the junk block.
   auto issue_stage = [&](int slot, int step) {
     unsigned char* st = lds + slot * kStage;
     const int k0 = step * kStepK;
     const uint32_t dead = step < nsteps ? 0u : kOffsetOOB;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int a = wave * 4 + u;
+    for (int u = 0; u < Tl::kAPer; ++u) {
+      const int a = wave * Tl::kAPer + u;     // uniform
       const int row = 4 * a + (lane >> 4);
       const int c = (lane & 15) ^ (row & 7);
-      bload16_lds(ra, st + a * 1024, ((uint32_t)row * (uint32_t)p.kpad + (uint32_t)(k0 + 8 * c)) * 2 | dead);
+      const bool real = a < Tl::kA;
+      bload16_lds(ra, real ? st + a * 1024 : junk,
+                  real ? ((uint32_t)row * (uint32_t)p.kpad + (uint32_t)(k0 + 8 * c)) * 2 | dead : kOffsetOOB);
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int b = wave * 2 + u;
+    for (int u = 0; u < Tl::kBPer; ++u) {
+      const int b = wave * Tl::kBPer + u;     // uniform
       const int row = 16 * b + (lane >> 2);
       const int c = (lane & 3) ^ ((row >> 1) & 3);
-      const uint32_t off = (uint32_t)(k0 / 2 + 16 * c) < row_bytes
+      const bool real = b < Tl::kB;
+      const uint32_t off = real && (uint32_t)(k0 / 2 + 16 * c) < row_bytes
                                ? (uint32_t)row * row_bytes + (uint32_t)(k0 / 2 + 16 * c) : kOffsetOOB;
-      bload16_lds(rb, st + kABytes + b * 1024, off | dead);
+      bload16_lds(rb, real ? st + kABytes + b * 1024 : junk, off | dead);
     }
 #pragma unroll
     for (int u = 0; u < kMeta; ++u) {
       const int mi = wave * kMeta + u;       // uniform
-      const int pc = mi / 3, part = mi - 3 * pc;
+      const int pc = mi / (1 + Tl::kSzParts), part = mi - (1 + Tl::kSzParts) * pc;
       unsigned char* dst = junk;
       uint32_t off = kOffsetOOB;
       if (pc < NP) {
@@ -240,7 +263,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
             off = (uint32_t)(((int64_t)pi * p.mpad + m0 + 4 * lane) * 4);
         } else {
           const int g = (k0 + pc * kPiece) / p.group;
-          dst = st + kSzOff + pc * 2048 + (part - 1) * 1024;
+          dst = st + kSzOff + pc * kSzStride + (part - 1) * 1024;
           if (g < p.ngroups)
             off = (uint32_t)(((int64_t)g * p.npad + n0 + 128 * (part - 1) + 2 * lane) * 8);
         }
@@ -249,26 +272,25 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
     }
   };
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[MT][NT];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < MT; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < NT; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
   const f32x16_t zero16 = {};
 
   const uint32_t nib_offset = vgpr_copy(kBf16Offset2);
   // this lane's activation row (A operand) and weight row (B operand) per tile
-  int arow[2], brow[2];
+  int arow[MT], brow[NT];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    arow[t] = 64 * wm + 32 * t + j;
-    brow[t] = 64 * wn + 32 * t + j;
-  }
+  for (int t = 0; t < MT; ++t) arow[t] = 32 * MT * wm + 32 * t + j;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) brow[t] = 32 * NT * wn + 32 * t + j;
 
   // zero-point operands carried from an even step to the next (one piece per step)
-  float zpa[2] = {0.f, 0.f}, zpb[2] = {0.f, 0.f};
+  float zpa[MT] = {}, zpb[NT] = {};
 
   auto compute = [&](int slot, int step) {
     const unsigned char* st = lds + slot * kStage;
@@ -278,16 +300,16 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
     // through the matrix unit, two pieces per float32 MFMA.  Operands for
     // piece pc: row factor -sum_of_x of this lane's activation row, column
     // factor scale * (128 + zero) of its weight row (zero past the inputs).
-    auto zp_operands = [&](int pc, float (&a)[2], float (&b)[2]) {
+    auto zp_operands = [&](int pc, float (&a)[MT], float (&b)[NT]) {
       const bool in = k0 + pc * kPiece < K;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         const float xv = *reinterpret_cast<const float*>(st + kXsOff + pc * 1024 + arow[mt] * 4);
         a[mt] = in ? -xv : 0.f;
       }
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const f32x2_t v = *reinterpret_cast<const f32x2_t*>(st + kSzOff + pc * 2048 + brow[nt] * 8);
+      for (int nt = 0; nt < NT; ++nt) {
+        const f32x2_t v = *reinterpret_cast<const f32x2_t*>(st + kSzOff + pc * kSzStride + brow[nt] * 8);
         b[nt] = -v[0] * v[1];
       }
     };
@@ -295,39 +317,38 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
       if constexpr (NP == 1) {
         // One piece per step: lane half h carries the pieces of steps with
         // parity h; the MFMA runs after every odd step.
-        float a[2], b[2];
+        float a[MT], b[NT];
         zp_operands(0, a, b);
         const bool mine = h == (step & 1);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          zpa[t] = mine ? a[t] : zpa[t];
-          zpb[t] = mine ? b[t] : zpb[t];
-        }
+        for (int t = 0; t < MT; ++t) zpa[t] = mine ? a[t] : zpa[t];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) zpb[t] = mine ? b[t] : zpb[t];
         if (step & 1) {
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32f(zpa[mt], zpb[nt], acc[mt][nt]);
+            for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma32f(zpa[mt], zpb[nt], acc[mt][nt]);
         }
       } else {
 #pragma unroll
         for (int pp = 0; pp < NP; pp += 2) {
-          float a[2], b[2];
+          float a[MT], b[NT];
           zp_operands(pp + h, a, b);       // lane half h: piece pp + h
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32f(a[mt], b[nt], acc[mt][nt]);
+            for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma32f(a[mt], b[nt], acc[mt][nt]);
         }
       }
     };
     // All weight bytes of the step, then the activation fragments one 16-input
     // block ahead of the MFMAs that use them.
-    uint32_t bd[2][2][4];
+    uint32_t bd[2][NT][4];
 #pragma unroll
     for (int L = 0; L < 2; ++L)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         const int row = brow[nt];
         const int c = (2 * L + h) ^ ((row >> 1) & 3);
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + kABytes + row * 64 + 16 * c);
@@ -343,12 +364,12 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
           bd[L][nt][1] = s1[0]; bd[L][nt][3] = s1[1];
         }
       }
-    auto load_af = [&](int blk, bf16x8_t (&af)[2]) {
+    auto load_af = [&](int blk, bf16x8_t (&af)[MT]) {
       const int L = blk >> 2, b = blk & 3;
       // 8-input chunk of the activations that matches dword b of this half
       const int cin = GB == 1 ? 4 * (b >> 1) + 2 * h + (b & 1) : 4 * h + b;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         const int row = arow[mt];
         const int c = (8 * L + cin) ^ (row & 7);
         af[mt] = *reinterpret_cast<const bf16x8_t*>(st + row * 256 + 16 * c);
@@ -356,21 +377,21 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
     };
     // Fold of one group piece: acc += scale * sum (the zero-point part is
     // added by correct()).
-    f32x16_t cg[2][2];
+    f32x16_t cg[MT][NT];
     auto fold = [&](int pc) {
       if (k0 + pc * kPiece >= K) return;     // a piece past the end of the inputs
-      float sv[2];
+      float sv[NT];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        sv[nt] = *reinterpret_cast<const float*>(st + kSzOff + pc * 2048 + brow[nt] * 8);
+      for (int nt = 0; nt < NT; ++nt)
+        sv[nt] = *reinterpret_cast<const float*>(st + kSzOff + pc * kSzStride + brow[nt] * 8);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[mt][nt][r] = fmaf(sv[nt], cg[mt][nt][r], acc[mt][nt][r]);
     };
-    bf16x8_t afc[2], afn[2];
+    bf16x8_t afc[MT], afn[MT];
     // The two waves of a SIMD leave the barrier together; raising this wave's
     // priority for its MFMA phase lets one of them run ahead, so that one
     // folds (VALU) while the other keeps the matrix unit busy.
@@ -383,14 +404,14 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
       const bool first = blk % kBlocksPerPiece == 0;      // a new piece starts
       if (blk + 1 < 8) load_af(blk + 1, afn);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         const bf16x8_t bf = unpack_codes(bd[L][nt][b], kNibPairMask, nib_offset);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) cg[mt][nt] = mfma32(afc[mt], bf, first ? zero16 : cg[mt][nt]);
+        for (int mt = 0; mt < MT; ++mt) cg[mt][nt] = mfma32(afc[mt], bf, first ? zero16 : cg[mt][nt]);
       }
       if (blk % kBlocksPerPiece == kBlocksPerPiece - 1) fold(blk / kBlocksPerPiece);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) afc[mt] = afn[mt];
+      for (int mt = 0; mt < MT; ++mt) afc[mt] = afn[mt];
     }
     __builtin_amdgcn_s_setprio(0);
     correct();
@@ -418,24 +439,24 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
   if constexpr (4 / GB == 1) {
     if (nsteps & 1) {   // the last (even) step's zero-point term is still pending
 #pragma unroll
-      for (int t = 0; t < 2; ++t) zpa[t] = h ? 0.f : zpa[t];
+      for (int t = 0; t < MT; ++t) zpa[t] = h ? 0.f : zpa[t];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32f(zpa[mt], zpb[nt], acc[mt][nt]);
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma32f(zpa[mt], zpb[nt], acc[mt][nt]);
     }
   }
 
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       const int n = n0 + brow[nt];
       if (n >= N) continue;
       const float b = p.bias ? p.bias[n] : 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + 64 * wm + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int m = m0 + 32 * MT * wm + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
         if (m < M) {
           const float v = acc[mt][nt][r] + b;
           if (p.y_bf16)
@@ -447,16 +468,16 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmParams p) {
     }
 }
 
-template <int GB, int S>
+template <class Tl, int GB, int S>
 size_t gemm_lds_bytes() {
   constexpr int NP = 4 / GB;
-  return (size_t)S * (kABytes + kBBytes + NP * 1024 + NP * 2048) + kJunk;
+  return (size_t)S * (Tl::kABytes + Tl::kBBytes + NP * 1024 + NP * Tl::kSzParts * 1024) + kJunk;
 }
 
-template <int GB, int S>
-int32_t launch_gemm_t(const GemmParams& gp, hipStream_t stream) {
-  auto kern = gemm_kernel<GB, S>;
-  const size_t lds = gemm_lds_bytes<GB, S>();
+template <class Tl, int GB, int S>
+int32_t launch_gemm_t(GemmParams gp, hipStream_t stream) {
+  auto kern = gemm_kernel<Tl, GB, S>;
+  const size_t lds = gemm_lds_bytes<Tl, GB, S>();
   static bool raised = false;   // raise the dynamic-LDS limit once per instantiation
   if (!raised) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -464,8 +485,31 @@ int32_t launch_gemm_t(const GemmParams& gp, hipStream_t stream) {
       return WOQ_EHIP;
     raised = true;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)(gp.tiles_m * gp.tiles_n)), dim3(512), lds, stream, gp);
+  gp.tiles_m = (gp.m + Tl::BM - 1) / Tl::BM;
+  gp.tiles_n = (gp.n + Tl::BN - 1) / Tl::BN;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(gp.tiles_m * gp.tiles_n)), dim3(64 * Tl::kWaves), lds,
+                     stream, gp);
   return hip_status(hipGetLastError());
+}
+
+// Stages in the LDS ring: three (two steps of loads ahead of the arithmetic)
+// where they fit in one CU's LDS, else two.  Deeper rings measured slower on
+// the narrow tiles: they cost workgroups per CU.
+template <class Tl, int GB>
+constexpr int gemm_stages() {
+  constexpr int NP = 4 / GB;
+  constexpr int stage = Tl::kABytes + Tl::kBBytes + NP * 1024 + NP * Tl::kSzParts * 1024;
+  return 3 * stage + kJunk <= 160 * 1024 ? 3 : 2;
+}
+
+template <class Tl>
+int32_t launch_gemm_gb(const GemmParams& gp, int gb, hipStream_t stream) {
+  switch (gb) {
+    case 1: return launch_gemm_t<Tl, 1, gemm_stages<Tl, 1>()>(gp, stream);
+    case 2: return launch_gemm_t<Tl, 2, gemm_stages<Tl, 2>()>(gp, stream);
+    case 4: return launch_gemm_t<Tl, 4, gemm_stages<Tl, 4>()>(gp, stream);
+    default: return WOQ_EUNSUPPORTED;
+  }
 }
 
 }  // namespace
@@ -499,13 +543,13 @@ int32_t launch_fill_bias(const float* bias, int32_t m, int32_t n, int32_t y_bf16
 }
 
 size_t gemm_sz_bytes(int64_t n, int64_t k, int32_t group) {
-  const int64_t npad = (n + kBN - 1) / kBN * kBN;
+  const int64_t npad = (n + kNPad - 1) / kNPad * kNPad;
   return (size_t)(k / group) * (size_t)npad * 8;
 }
 
 int32_t launch_gemm(const LinearArgs& a, const LinearPlan& pl, void* sz_ws, hipStream_t stream) {
   const int32_t ngroups = a.k / a.group;
-  const int32_t npad = (a.n + kBN - 1) / kBN * kBN;
+  const int32_t npad = (a.n + kNPad - 1) / kNPad * kNPad;
   {
     const int64_t total = (int64_t)ngroups * npad;
     int64_t blocks = (total + 255) / 256;
@@ -516,13 +560,17 @@ int32_t launch_gemm(const LinearArgs& a, const LinearPlan& pl, void* sz_ws, hipS
     if (st != WOQ_OK) return st;
   }
   const int32_t piece = a.group < kStepK ? a.group : kStepK;
-  GemmParams gp{a.x, a.packed, a.xs, static_cast<const f32x2_t*>(sz_ws), a.bias, a.y,
-                a.m, a.n, a.k, a.kpad, a.group, a.y_bf16, a.mpad, npad, ngroups, a.k / piece,
-                (a.m + kBM - 1) / kBM, (a.n + kBN - 1) / kBN};
-  switch (pl.gb) {
-    case 1: return launch_gemm_t<1, 2>(gp, stream);
-    case 2: return launch_gemm_t<2, 2>(gp, stream);
-    case 4: return launch_gemm_t<4, 3>(gp, stream);
+  const GemmParams gp{a.x, a.packed, a.xs, static_cast<const f32x2_t*>(sz_ws), a.bias, a.y,
+                      a.m, a.n, a.k, a.kpad, a.group, a.y_bf16, a.mpad, npad, ngroups, a.k / piece,
+                      0, 0};
+  // Tile by the number of activation rows: small M takes narrow tiles so the
+  // grid still covers the chip.
+  switch (pl.bm) {
+    case 32: return launch_gemm_gb<Tile<1, 2, 1, 1>>(gp, pl.gb, stream);    // 32 x 64
+    case 64: return launch_gemm_gb<Tile<2, 2, 1, 1>>(gp, pl.gb, stream);    // 64 x 64
+    case 128:
+      if (pl.bn == 64) return launch_gemm_gb<Tile<2, 2, 2, 1>>(gp, pl.gb, stream);   // 128 x 64
+      return launch_gemm_gb<Tile<2, 4, 2, 2>>(gp, pl.gb, stream);                    // 128 x 256
     default: return WOQ_EUNSUPPORTED;
   }
 }
