@@ -10,13 +10,16 @@
 // (scale, -(128 + zero)) float pairs, [K/G][N rounded up to 256].
 //
 // GEMM (linnet docs "Quantization", std.quant table, linear_int4_groups): a
-// workgroup of 8 waves computes a 128 x 256 tile of y, each wave 64 x 64 as
-// 2 x 2 tiles of v_mfma_f32_32x32x16_bf16.  Per 128-input step the workgroup
-// streams the activation tile (32 KB), the packed weight tile (16 KB), the
-// piece sums and the scale/zero pairs straight from memory into a ring of
-// three LDS stages with buffer-to-LDS loads, so the memory stream runs two
-// steps ahead without holding registers; one barrier per step hands a stage
-// from the loads to the arithmetic.  Both tiles are stored XOR-swizzled so the
+// workgroup computes a BM x BN tile of y from 32 x 32 tiles of
+// v_mfma_f32_32x32x16_bf16.  Large m takes 128 x 256 with 8 waves of 64 x 64
+// (2 x 2 MFMA tiles); smaller m takes 128 x 64, 64 x 64 or 32 x 64 tiles
+// (4, 4 and 2 waves) so that the grid still covers the chip.  Per 128-input
+// step the workgroup streams the activation tile (BM x 256 bytes), the packed
+// weight tile (BN x 64 bytes), the piece sums and the scale/zero pairs
+// straight from memory into a ring of LDS stages (three, or two where three
+// do not fit) with buffer-to-LDS loads, so the memory stream runs ahead
+// without holding registers; one barrier per step hands a stage from the
+// loads to the arithmetic.  Both tiles are stored XOR-swizzled so the
 // reads of 8 neighbouring rows hit distinct banks.  Nibbles become bf16
 // (128 + code) with one AND-OR per pair; each MFMA takes one dword of every
 // lane's 16 loaded bytes (inputs u+32h+8b .. +8 of a 64-input unit u, h the
