@@ -88,6 +88,46 @@ def test_linear_small_all_outputs(woq, m, n, k, group, with_bias, with_order, ou
     check_linear(y, _ref(host, group), f"m={m} n={n} k={k} g={group}")
 
 
+# Decode-path (m <= 4) launch variants: WOQ_GEMV_WAVES sets the planner's
+# target number of waves, which at these small sizes forces each steps-per-wave
+# class (4, 8, 12/16), one or many waves per workgroup, trailing waves with a
+# partial or empty range, group offsets that do not start on a multiple of 4
+# and several activation staging batches.
+GEMV_VARIANTS = [
+    # m, n, k, group, bias, order, target waves, expected "steps_per_wave=.. waves=.."
+    (1, 40, 4096, 128, True, False, 1, (16, 2)),
+    (1, 17, 1920, 128, False, False, 1, (16, 1)),
+    (1, 48, 2048, 64, False, True, 6, (8, 2)),
+    (1, 40, 1536, 32, True, False, 3, (12, 1)),
+    (1, 40, 4096, 256, False, False, 0, (4, 8)),
+    (1, 33, 4160, 64, True, False, 0, (4, 9)),
+    (2, 40, 2048, 128, True, False, 6, (8, 2)),
+    (3, 50, 3072, 256, False, True, 8, (12, 2)),
+    (4, 40, 2048, 32, True, False, 6, (8, 2)),
+    (4, 64, 4096, 128, False, False, 1, (16, 2)),
+    (4, 31, 1152, 32, True, True, 0, (4, 3)),
+]
+
+
+@pytest.mark.parametrize("m,n,k,group,with_bias,with_order,target,shape", GEMV_VARIANTS)
+def test_gemv_launch_variants(woq, monkeypatch, m, n, k, group, with_bias, with_order, target, shape):
+    if target:
+        monkeypatch.setenv("WOQ_GEMV_WAVES", str(target))
+    else:
+        monkeypatch.delenv("WOQ_GEMV_WAVES", raising=False)
+    plan = woq.linear_plan(m, n, k, group, with_order)
+    _say(f"gemv m={m} n={n} k={k} g={group} bias={with_bias} order={with_order} plan: {plan}")
+    assert "path=gemv_mfma" in plan
+    assert f"steps_per_wave={shape[0]} " in plan and f"waves={shape[1]} " in plan
+    dev, host = _make(woq, m, n, k, group, seed=3000 + m + n + k, with_bias=with_bias,
+                      with_order=with_order)
+    ref = _ref(host, group)
+    for out in (torch.float32, torch.bfloat16):
+        y = _run(woq, dev, group, out)
+        torch.cuda.synchronize()
+        check_linear(y, ref, f"gemv m={m} n={n} k={k} g={group}")
+
+
 def test_tiny_workload(woq):
     c = workloads.TINY
     _say(f"tiny workload {c.name}")

@@ -47,6 +47,40 @@ bool skinny_override(int* ns, int* waves) {
   return cached == 1;
 }
 
+// Decode GEMV launch shape.  Each wave takes `cnt` consecutive 128-input
+// steps (4, 8, 12 or 16) and a workgroup of ceil(steps / cnt) waves (at most
+// 16) covers K for 16 outputs.  The smallest cnt whose grid stays within the
+// target number of waves is taken, else the largest: enough waves that every
+// SIMD holds two or more (their instruction streams then overlap), few
+// enough that per-wave set-up stays small against the steps.  WOQ_GEMV_WAVES
+// overrides the target (a tuning aid, read on every call).
+bool gemv_plan(int64_t m, int64_t n, int64_t k, int32_t group, LinearPlan* p) {
+  int64_t target = 3584;
+  if (const char* e = std::getenv("WOQ_GEMV_WAVES")) {
+    const long v = std::strtol(e, nullptr, 10);
+    if (v > 0) target = v;
+  }
+  const int64_t nsteps = (k + 127) / 128;
+  const int64_t tiles = (n + 15) / 16;
+  int64_t cnt = 16;
+  for (int64_t c = 4; c <= 16; c += 4) {
+    const int64_t w = (nsteps + c - 1) / c;
+    if (w <= 16 && tiles * w <= target) {
+      cnt = c;
+      break;
+    }
+  }
+  const int64_t w = (nsteps + cnt - 1) / cnt;
+  if (w > 16) return false;   // more than 1024 threads per workgroup
+  if (gemv_layout(m, k, group, (int)w, (int)cnt).total > kSkinnyLdsLimit) return false;
+  p->path = 4;
+  p->fold_rows = m == 1 ? 1 : 4;
+  p->waves = (int)w;
+  p->cnt = (int)cnt;
+  p->grid = tiles;
+  return true;
+}
+
 int pow2_floor(int64_t v) {
   int p = 1;
   while ((int64_t)p * 2 <= v) p *= 2;
@@ -64,6 +98,11 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
   }
   p.gb = group >= 128 ? 4 : group / 32;
   const int64_t nsub = (n + 15) / 16;
+  const bool force_skinny = std::getenv("WOQ_FORCE_SKINNY") != nullptr;   // tuning aid, read on every call
+  if (m <= 4 && !force_skinny && k < ((int64_t)1 << 26) && gemv_plan(m, n, k, group, &p)) {
+    p.prep = has_order ? 1 : 0;
+    return p;
+  }
   const int skinny_ns = (nsub >= 2048 && p.gb >= 2) ? 2 : 1;
   static const bool force_tiled = std::getenv("WOQ_FORCE_TILED") != nullptr;   // tuning aid
   if (m <= 16 && !force_tiled && k < ((int64_t)1 << 26) &&
@@ -116,7 +155,7 @@ LinearWorkspace linear_workspace_layout(int64_t m, int64_t n, int64_t k, int32_t
                                         bool has_order) {
   LinearWorkspace w;
   const LinearPlan p = linear_plan(m, n, k, group, has_order);
-  if (p.path == 1 && has_order) {
+  if ((p.path == 1 || p.path == 4) && has_order) {
     w.xg_off = 0;
     w.xg_bytes = round256((size_t)m * (size_t)k * 2);
   } else if (p.path == 2) {
@@ -277,6 +316,15 @@ int32_t woq_linear_int4_groups(const void* x_bf16, int64_t m, const uint8_t* pac
     }
     return launch_skinny(a, plan, s);
   }
+  if (plan.path == 4) {
+    if (has_order) {
+      uint16_t* xg = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
+      st = launch_prep(a.x, order, a.m, a.k, a.k, group, 0, xg, nullptr, m, s);
+      if (st != WOQ_OK) return st;
+      a.x = xg;
+    }
+    return launch_gemv(a, plan, s);
+  }
   if (k >= kGemmMaxK) return WOQ_EUNSUPPORTED;
   uint16_t* xg = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
   float* xs = reinterpret_cast<float*>(wsb + ws.xs_off);
@@ -304,6 +352,12 @@ int32_t woq_linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, int32_t 
                     "prep=%s workspace=%zu",
                     p.mt, p.fold_rows, p.ns, p.waves, p.gb, (long long)p.grid,
                     p.prep ? "gather" : "none", ws);
+      break;
+    case 4:
+      std::snprintf(buf, len,
+                    "path=gemv_mfma fold_rows=%d waves=%d steps_per_wave=%d group_blocks=%d grid=%lld "
+                    "prep=%s workspace=%zu",
+                    p.fold_rows, p.waves, p.cnt, p.gb, (long long)p.grid, p.prep ? "gather" : "none", ws);
       break;
     default:
       std::snprintf(buf, len,

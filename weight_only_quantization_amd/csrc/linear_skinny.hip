@@ -42,6 +42,9 @@ constexpr int kZeroOff = 256;
 constexpr int kXOff = 512;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kOffsetOOB = 0x80000000u;   // a buffer offset no descriptor covers
+// s_waitcnt immediate that waits for LDS traffic only: lgkmcnt(0), vmcnt and
+// expcnt at their maxima
+constexpr int kWaitLdsOnly = 0xC07F;
 // staging chunks per thread and batch: activations (8 inputs each) and
 // scale / zero-point pairs (4 entries each)
 constexpr int kStageX = 8, kStageS = 4;
@@ -216,7 +219,11 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   if (tid < 16) *reinterpret_cast<u32x4_t*>(lds + kZeroOff + 16 * tid) = u32x4_t{0u, 0u, 0u, 0u};
   put_x();
   put_sz(0, szlim);
-  __syncthreads();
+  // The staging writes must be visible to the workgroup, but the weight loads
+  // issued above stay in flight across the barrier (__syncthreads would wait
+  // for every outstanding load, draining the ring before the first step).
+  __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
+  __builtin_amdgcn_s_barrier();
 
   // ---- main loop --------------------------------------------------------------
   constexpr bool kTranspose = GB < 4;

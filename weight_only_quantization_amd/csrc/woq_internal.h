@@ -34,7 +34,8 @@ struct LinearWorkspace {
 
 // Which kernel family runs a linear call, and with what launch shape.
 struct LinearPlan {
-  int path = 0;          // 0 none, 1 skinny MFMA (m <= 16), 2 tiled MFMA GEMM, 3 bias only (k == 0)
+  int path = 0;          // 0 none, 1 skinny MFMA (m <= 16), 2 tiled MFMA GEMM, 3 bias only (k == 0),
+                         // 4 decode GEMV (m <= 4)
   int mt = 1;            // 16-row activation tiles held per wave (skinny path)
   int fold_rows = 4;     // accumulator rows folded per tile (1 when m == 1)
   int ns = 1;            // 16-column weight tiles per workgroup (skinny path)
@@ -44,6 +45,7 @@ struct LinearPlan {
   int64_t grid = 0;      // workgroups
   int bm = 0, bn = 0;    // tile of the GEMM path
   int64_t mpad = 0;      // rows of the per-group sum table (GEMM path)
+  int cnt = 0;           // 128-input steps per wave (decode path)
 };
 
 LinearWorkspace linear_workspace_layout(int64_t m, int64_t n, int64_t k, int32_t group,
@@ -83,6 +85,15 @@ int32_t launch_prep(const uint16_t* x, const int32_t* order, int32_t m, int32_t 
                     int32_t group, int32_t permute, uint16_t* xg, float* xs, int64_t mpad,
                     hipStream_t stream);
 int32_t launch_skinny(const LinearArgs& a, const LinearPlan& p, hipStream_t stream);
+// Decode path (m <= 4): LDS layout of one workgroup of `waves` waves with
+// `cnt` steps each.
+struct GemvLayout {
+  int32_t xs_off = 0, sz_off = 0, wave_lds = 0, red_off = 0;
+  size_t total = 0;
+};
+GemvLayout gemv_layout(int64_t m, int64_t k, int64_t group, int waves, int cnt);
+int gemv_cnt_class(int cnt);   // the kernel variant serving `cnt` steps per wave (4, 8, 16; 0: none)
+int32_t launch_gemv(const LinearArgs& a, const LinearPlan& p, hipStream_t stream);
 size_t skinny_lds_bytes(int64_t m, int64_t k, int64_t group, int waves, int ns);
 constexpr size_t kSkinnyLdsLimit = 160 * 1024;   // staged activations, scales and zeros share the 160 KB of LDS per CU
 size_t gemm_sz_bytes(int64_t n, int64_t k, int32_t group);
