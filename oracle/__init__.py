@@ -10,12 +10,17 @@ from .woq_ref import (  # noqa: F401
     QMAX_ASYM,
     QMAX_SYM,
     OracleError,
+    PREP_INPUTS,
+    PREP_ROWS,
     bf16_bits_to_f64,
     bf16_round_bits,
     dequantize_int4_groups,
     linear_int4_groups,
     pack_uint4,
+    prepare_int4,
+    prepared_bytes,
     quantize_groups,
     rint_half_even,
     unpack_uint4,
+    unprepare_int4,
 )

@@ -52,6 +52,16 @@ R7  Dequantization forms ``(q - zero) * scale`` once, rounded to float32, and
 R8  The linear layer's exact value is ``sum_k x'[m,k] * (q-z)*s + bias[n]``
     with the float64-exact ``(q - z)*s`` (a 4-bit integer times a float32 is
     exact in float64).
+R9  Prepared weights.  The linnet page says its fused int4 kernels run on
+    weights re-ordered once at load time ("--prepare") and the inference book
+    names a kernel-specific re-ordering, but neither gives the order.  The
+    order used here is this library's own: blocks of 16 outputs x 128 inputs
+    (1024 bytes), tile-major then step-major; inside a block, lane slot l
+    (16 bytes) holds output row 16t + l % 16, packed bytes
+    [64 s + 16 (l // 16), +16) of that row, i.e. inputs 128 s + 32 (l // 16)
+    .. +32.  Rows past N and bytes past K/2 are zero.  Scale and zero keep the
+    canonical layout.  The linear layer over prepared weights has the value
+    of R8 over the canonical weights they came from.
 """
 from __future__ import annotations
 
@@ -68,6 +78,11 @@ __all__ = [
     "linear_int4_groups",
     "bf16_round_bits",
     "bf16_bits_to_f64",
+    "PREP_ROWS",
+    "PREP_INPUTS",
+    "prepared_bytes",
+    "prepare_int4",
+    "unprepare_int4",
 ]
 
 QMAX_ASYM = 15   # unsigned 4-bit codes 0..15 ("Per-Group INT4", 4.8 Quantization II)
@@ -263,3 +278,44 @@ def linear_int4_groups(x, packed, scale, zero, n: int, k: int, group: int,
     if bias is not None:
         y += np.asarray(bias, dtype=np.float32).astype(np.float64)[idx][None, :]
     return y
+
+
+# ---------------------------------------------------------------------------
+# Prepared (fragment-ordered) weights, R9
+# ---------------------------------------------------------------------------
+
+PREP_ROWS = 16      # outputs per block
+PREP_INPUTS = 128   # inputs per block (64 packed bytes of each row)
+
+
+def prepared_bytes(n: int, k: int) -> int:
+    """Size of the prepared layout of an [n, k] weight: whole 16 x 128 blocks."""
+    return -(-n // PREP_ROWS) * -(-k // PREP_INPUTS) * PREP_ROWS * PREP_INPUTS // 2
+
+
+def _prep_dims(n: int, k: int):
+    if n < 0 or k < 0 or k % 32:
+        raise OracleError("prepared weights need k a multiple of 32")
+    return -(-n // PREP_ROWS), -(-k // PREP_INPUTS)
+
+
+def prepare_int4(packed, n: int, k: int):
+    """Canonical packed rows [n, k/2] -> prepared blocks (R9), a flat uint8 array.
+
+    Blocks are ordered (tile t, step s); block (t, s) is the 4 x 16 x 16-byte
+    array [q][c][byte] = packed row 16t + c, bytes 64 s + 16 q + byte.
+    """
+    nt, ns = _prep_dims(n, k)
+    rows = np.zeros((nt * PREP_ROWS, ns * PREP_INPUTS // 2), dtype=np.uint8)
+    rows[:n, :k // 2] = np.asarray(packed, dtype=np.uint8).reshape(n, k // 2)
+    # [t][c][s][q][byte] -> [t][s][q][c][byte]
+    blocks = rows.reshape(nt, PREP_ROWS, ns, 4, 16).transpose(0, 2, 3, 1, 4)
+    return np.ascontiguousarray(blocks).reshape(-1)
+
+
+def unprepare_int4(prepared, n: int, k: int):
+    """Inverse of :func:`prepare_int4`: prepared blocks -> packed rows [n, k/2]."""
+    nt, ns = _prep_dims(n, k)
+    blocks = np.asarray(prepared, dtype=np.uint8).reshape(nt, ns, 4, PREP_ROWS, 16)
+    rows = blocks.transpose(0, 3, 1, 2, 4).reshape(nt * PREP_ROWS, ns * PREP_INPUTS // 2)
+    return np.ascontiguousarray(rows[:n, :k // 2])

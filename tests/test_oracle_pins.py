@@ -51,6 +51,8 @@ def oracle_impl():
         dequantize_int4_groups=oracle.dequantize_int4_groups,
         linear_int4_groups=oracle.linear_int4_groups,
         bf16_round_bits=oracle.bf16_round_bits,
+        prepare_int4=oracle.prepare_int4,
+        unprepare_int4=oracle.unprepare_int4,
     )
 
 
@@ -346,12 +348,66 @@ def check_shape_rules(impl):
         impl.linear_int4_groups(x, np.zeros((2, 3), np.uint8), s, z, 2, 6, 3)
 
 
+def _position_ids(impl, n, k):
+    """Prepare an [n, k/2] byte matrix whose entries name their own position.
+
+    Bytes hold only 8 bits, so the position p + 1 (0 marks padding) goes
+    through the permutation one base-256 digit at a time and is put back
+    together afterwards.
+    """
+    pos = np.arange(n * (k // 2), dtype=np.int64).reshape(n, k // 2) + 1
+    out = None
+    for d in range(3):
+        digit = ((pos >> (8 * d)) & 0xFF).astype(np.uint8)
+        part = np.asarray(impl.prepare_int4(digit, n, k)).astype(np.int64) << (8 * d)
+        out = part if out is None else out | part
+    return out
+
+
+def check_prepared_fragments(impl):
+    """Prepared weights (R9): every packed byte appears exactly once, padding is
+    zero, each 1 KB block is one (16-row tile, 128-input step), blocks run
+    through the steps of a tile before the next tile, and the 16-byte slot l of
+    a block holds 32 consecutive inputs of tile row l % 16, quarter l // 16 of
+    the step (the MFMA operand order the kernels load).  Sizes include ragged
+    rows and steps."""
+    for n, k in ((1, 32), (16, 128), (17, 96), (33, 288), (40, 1024)):
+        ids = _position_ids(impl, n, k)
+        nt, ns = -(-n // 16), -(-k // 128)
+        assert ids.size == nt * ns * 1024 == oracle.prepared_bytes(n, k)
+        real = ids[ids > 0] - 1
+        assert real.size == n * (k // 2) and np.array_equal(np.sort(real), np.arange(n * (k // 2)))
+        slots = ids.reshape(nt, ns, 64, 16)
+        for t in range(nt):
+            for s_ in range(ns):
+                for l in range(64):
+                    row, quarter = 16 * t + l % 16, l // 16
+                    first_byte = 64 * s_ + 16 * quarter      # inputs 128 s + 32 quarter ..
+                    expect = [row * (k // 2) + first_byte + b + 1
+                              if row < n and first_byte + b < k // 2 else 0 for b in range(16)]
+                    assert list(slots[t, s_, l]) == expect, (n, k, t, s_, l)
+
+
+def check_prepared_roundtrip(impl):
+    """unprepare(prepare(p)) == p on random bytes, ragged sizes included, and a
+    prepared buffer decodes to the same dequantized weights."""
+    rng = np.random.default_rng(11)
+    for n, k in ((3, 64), (16, 4096), (31, 160), (64, 384)):
+        p = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+        pr = impl.prepare_int4(p, n, k)
+        back = impl.unprepare_int4(pr, n, k)
+        assert np.array_equal(np.asarray(back).reshape(n, k // 2), p)
+    with pytest.raises(ValueError):
+        impl.prepare_int4(np.zeros((2, 24), np.uint8), 2, 48)     # k not a multiple of 32
+
+
 ALL_CHECKS = [
     check_rint_ties, check_worked_example_group5, check_worked_example_group4_rows,
     check_pack_exhaustive, check_asym_bruteforce, check_symmetric_bruteforce,
     check_zero_groups, check_half_step_sweep, check_noise_variance,
     check_dequant_closed_form, check_bf16_rounding, check_linear_exact,
     check_linear_onehot_and_zero, check_linear_order_and_rows, check_shape_rules,
+    check_prepared_fragments, check_prepared_roundtrip,
 ]
 
 
@@ -473,7 +529,28 @@ MUTANTS = {
     "bf16_truncation": lambda: _mutant(
         bf16_round_bits=lambda v: (np.asarray(v, np.float32).view(np.uint32) >> 16).astype(np.uint16)),
     "rint_half_away": lambda: _mutant(rint_half_even=lambda a: np.trunc(np.asarray(a) + np.copysign(0.5, a))),
+    "prepare_rows_and_quarters_swapped": lambda: _mutant(
+        prepare_int4=lambda p, n, k: _prepare_variant(p, n, k, swap_lanes=True)),
+    "prepare_step_major_blocks": lambda: _mutant(
+        prepare_int4=lambda p, n, k: _prepare_variant(p, n, k, step_major=True)),
+    "prepare_pads_with_ones": lambda: _mutant(
+        prepare_int4=lambda p, n, k: _prepare_variant(p, n, k, pad=0xFF)),
+    "unprepare_drops_last_tile": lambda: _mutant(
+        unprepare_int4=lambda pr, n, k: oracle.unprepare_int4(pr, n, k)[: max(n - 1, 0) or n]),
 }
+
+
+def _prepare_variant(p, n, k, swap_lanes=False, step_major=False, pad=0):
+    if k % 32:
+        raise ValueError("bad")
+    nt, ns = -(-n // 16), -(-k // 128)
+    rows = np.full((nt * 16, ns * 64), pad, dtype=np.uint8)
+    rows[:n, :k // 2] = np.asarray(p, dtype=np.uint8).reshape(n, k // 2)
+    b = rows.reshape(nt, 16, ns, 4, 16)
+    order = (0, 2, 1, 3, 4) if swap_lanes else (0, 2, 3, 1, 4)
+    if step_major:
+        order = (2, 0, 3, 1, 4)
+    return np.ascontiguousarray(b.transpose(order)).reshape(-1)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
