@@ -11,8 +11,11 @@ captured once in a HIP graph and replayed.
 Printed JSON line (rank 0):
   value        effective weight GB/s over the whole step (packed + scale + zero
                bytes / wall time of the replayed graph, launch gaps included)
-  roofline     the skinny decode kernel alone: algorithmic bytes per launch /
-               its average launch duration (HIP events around each launch)
+  roofline     the decode kernel alone (gemv_kernel, every launch of the step):
+               algorithmic bytes per launch / its average launch duration
+               (HIP events around the replayed step graph)
+  prepared     the same step over prepared (fragment-ordered) weights, made
+               once before timing by woq_prepare_int4
   prefill      TFLOP/s of the M=2048 GEMM path on both prefill shapes
   cpu_baseline the CPU oracle's linear on a bounded sample of the same layer
 """
@@ -35,8 +38,8 @@ METRIC = "int4-g128 linear: effective weight GB/s (% HBM peak) at M=1; TFLOP/s a
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 GROUP = 128
-TRAFFIC_SUMMARY = ROOT / "profiles" / "traffic_skinny_decode_m1_g128.txt"
-KERNEL_SOURCES = ["linear_skinny.hip", "mfma_common.h"]
+TRAFFIC_SUMMARY = ROOT / "profiles" / "traffic_gemv_decode_m1_g128.txt"
+KERNEL_SOURCES = ["linear_gemv.hip", "mfma_common.h"]
 
 
 def weight_bytes(n: int, k: int, group: int = GROUP) -> int:
@@ -103,6 +106,42 @@ def run_calls(woq, calls):
     for c in calls:
         woq.linear_int4_groups(c["x"], c["packed"], c["scale"], c["zero"], bias=c["bias"],
                                group=GROUP, out=c["y"], out_dtype=c["y"].dtype)
+
+
+def run_calls_prepared(woq, calls):
+    for c in calls:
+        woq.linear_int4_groups_prepared(c["x"], c["prepared"], c["scale"], c["zero"], bias=c["bias"],
+                                        out=c["y"], out_dtype=c["y"].dtype)
+
+
+def time_step(torch, run, steps: int, warmup: int, use_graph: bool):
+    """Seconds for `steps` replays of one step (a HIP graph of run(), or run()
+    launched eagerly), after `warmup` untimed ones; events bracket the replays."""
+    run()
+    torch.cuda.synchronize()
+    graph = None
+    if use_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run()           # warm-up on a side stream, as graph capture requires
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run()
+    step = graph.replay if graph is not None else run
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = e0.elapsed_time(e1) * 1e-3
+    del graph
+    return elapsed
 
 
 def measure_prefill(torch, woq, reps: int = 5):
@@ -262,7 +301,7 @@ def cpu_baseline(min_seconds: float = 10.0, max_passes: int = 8):
                        f"BLAS threads={blas_threads}, affinity cores={len(os.sched_getaffinity(0))})")
 
 
-SKINNY_TAG = "skinny_kernel"
+DECODE_TAG = "gemv_kernel"
 COPY_TAG = "copyBuffer"            # the runtime's device-to-device copy kernel
 
 
@@ -318,7 +357,7 @@ def summarize_profiles(root: Path, copy_mib: int) -> None:
     def counter(sub, cname):
         rows = _csv_rows(_find(root / sub, "_counter_collection.csv"))
         sk = [float(r["Counter_Value"]) for r in rows
-              if r["Counter_Name"] == cname and SKINNY_TAG in r["Kernel_Name"]]
+              if r["Counter_Name"] == cname and DECODE_TAG in r["Kernel_Name"]]
         cp = [float(r["Counter_Value"]) for r in rows
               if r["Counter_Name"] == cname and COPY_TAG in r["Kernel_Name"]]
         return sk, cp
@@ -334,7 +373,7 @@ def summarize_profiles(root: Path, copy_mib: int) -> None:
     fetch = statistics.mean(f_sk) * 1024.0 * f_factor
     write = statistics.mean(w_sk) * 1024.0 * w_factor
     print()
-    print("# HBM traffic of the skinny decode kernel per launch (rocprofv3 --pmc, copy-calibrated)")
+    print("# HBM traffic of the decode GEMV kernel per launch (rocprofv3 --pmc, copy-calibrated)")
     # the sources the counted kernel was built from, as the profiled bench printed them
     src_hash = None
     for cand in sorted((root / "fetch").rglob("*.json")):
@@ -367,6 +406,8 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the small-M sweep and act-order per-launch timings")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
+    ap.add_argument("--no-prepared", action="store_true",
+                    help="skip the decode step over prepared weights")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -395,35 +436,12 @@ def main():
     wbytes = sum(weight_bytes(c["n"], c["k"]) for c in calls)
     abytes = [algorithmic_bytes(1, c["n"], c["k"], c["bias"] is not None) for c in calls]
 
-    # Warm up eagerly (also on a side stream, as graph capture requires), then capture.
-    run_calls(woq, calls)
-    torch.cuda.synchronize()
-    graph = None
-    if not args.no_graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            run_calls(woq, calls)
-        torch.cuda.current_stream().wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            run_calls(woq, calls)
-    step = graph.replay if graph is not None else (lambda: run_calls(woq, calls))
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    elapsed = e0.elapsed_time(e1) * 1e-3
+    elapsed = time_step(torch, lambda: run_calls(woq, calls), args.steps, args.warmup,
+                        not args.no_graph)
     ms_per_step = elapsed / args.steps * 1e3
     value = wbytes * args.steps / elapsed / 1e9
 
-    # The step is one graph of back-to-back launches of the skinny kernel, so the
+    # The step is one graph of back-to-back launches of the decode kernel, so the
     # kernel's average launch duration is the timed region over the launches in it
     # (inter-launch gaps included, which makes the figure conservative).
     avg_launch = elapsed / (args.steps * len(calls))
@@ -432,7 +450,7 @@ def main():
     roofline = dict(
         bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
         frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
-        kernel="woq::skinny_kernel<NS=1,GB=4,PF=4,FR=1> (every launch of the step)",
+        kernel="woq::gemv_kernel<GB=4,FR=1,CC,PF=4> (every launch of the step)",
         launches=len(calls), avg_launch_us=round(avg_launch * 1e6, 3),
         algorithmic_bytes_per_launch=round(sum(abytes) / len(abytes)),
         traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
@@ -449,6 +467,25 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    prepared = None
+    if not args.no_prepared:
+        for c in calls:
+            c["prepared"] = woq.prepare_int4(c["packed"])
+        torch.cuda.synchronize()
+        el_p = time_step(torch, lambda: run_calls_prepared(woq, calls), args.steps, args.warmup,
+                         not args.no_graph)
+        val_p = wbytes * args.steps / el_p / 1e9
+        avg_p = el_p / (args.steps * len(calls))
+        prepared = dict(
+            metric="effective weight GB/s at M=1 over prepared weights (same step, same bytes)",
+            value=round(val_p, 1), unit="GB/s", ms_per_step=round(el_p / args.steps * 1e3, 4),
+            hbm_peak_frac=round(val_p / HBM_PEAK_GBS, 4), avg_launch_us=round(avg_p * 1e6, 3),
+            roofline_achieved=round(sum(abytes) / len(abytes) / avg_p / 1e9, 1),
+            roofline_frac=round(sum(abytes) / len(abytes) / avg_p / 1e9 / HBM_PEAK_GBS, 4),
+            note="woq_prepare_int4 re-orders each weight once before timing (load time)")
+        for c in calls:
+            del c["prepared"]
+
     prefill = None if args.no_prefill else measure_prefill(torch, woq)
     configs = None if args.no_configs else measure_configs(torch, woq)
     cpu = None if args.no_cpu_baseline else cpu_baseline()
@@ -461,9 +498,9 @@ def main():
                              "int4 group 128, bf16 x, f32 bias on q, bf16 y",
                     m=1, group=GROUP, layers=args.layers, launches_per_step=len(calls),
                     weight_bytes_per_step=wbytes, hbm_peak_frac=round(value / HBM_PEAK_GBS, 4),
-                    graph=graph is not None, accumulate="f32",
+                    graph=not args.no_graph, accumulate="f32",
                     tokens_per_s_linears_only=round(1.0 / (ms_per_step * 1e-3), 1) if args.layers == 32 else None),
-        roofline=roofline, prefill=prefill, configs=configs, cpu_baseline=cpu,
+        roofline=roofline, prepared=prepared, prefill=prefill, configs=configs, cpu_baseline=cpu,
     )
     print(json.dumps(line), flush=True)
 

@@ -151,7 +151,7 @@ size_t woq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group
  *   when that is 0.  The workspace holds only scratch; it need not be cleared.
  * m == 0 or n == 0 is a no-op; k == 0 gives y = bias (or 0).
  * Errors: WOQ_EINVAL, WOQ_EGROUP, WOQ_EUNSUPPORTED (group outside the list,
- *   m, n or k >= 2^31, or k >= 2^24 on the tiled path, m > 16), WOQ_EALIGN,
+ *   m, n or k >= 2^31, or k >= 2^24 on the tiled GEMM path, m > 16), WOQ_EALIGN,
  *   WOQ_EWORKSPACE, WOQ_EHIP.
  */
 int32_t woq_linear_int4_groups(const void* x_bf16, int64_t m, const uint8_t* packed,
@@ -161,10 +161,61 @@ int32_t woq_linear_int4_groups(const void* x_bf16, int64_t m, const uint8_t* pac
                                size_t workspace_bytes, void* stream);
 
 /*
- * Describe the kernel plan woq_linear_int4_groups uses for these sizes: the
- * path (skinny MFMA for m <= 16, tiled MFMA GEMM above), tiles, waves and
- * whether an input pre-pass runs.  Writes a NUL-terminated string of at most
- * len bytes into buf (host).  Pure host function.
+ * Prepared weights.  The linnet "Quantization" page runs its fused int4
+ * kernels on weights re-ordered once at load time ("--prepare"); the order is
+ * not given there, and the one below is this library's: the layout of a
+ * 16x16x32 MFMA operand, so that one 16-byte load per lane fills a fragment
+ * and a wave reads each 128-input step of 16 outputs as one contiguous
+ * kilobyte.
+ *   For W[n, k] (k a multiple of 32): blocks of 16 outputs x 128 inputs, 1024
+ *   bytes each, ordered tile t = 0 .. ceil(n/16)-1, then step
+ *   s = 0 .. ceil(k/128)-1 inside a tile; 16-byte slot l (0..63) of block
+ *   (t, s) holds output row 16t + l % 16, packed bytes 64 s + 16 (l / 16) ..
+ *   +16 of that row (inputs 128 s + 32 (l / 16) .. +32, nibbles as in the
+ *   canonical layout).  Rows past n and bytes past k/2 are zero.
+ *   Scale and zero keep the canonical [n, k/group] layout.
+ * woq_prepared_bytes: size of that layout, ceil(n/16) * ceil(k/128) * 1024;
+ *   0 for invalid sizes (negative, k not a multiple of 32, n or k >= 2^31).
+ *   Pure host function.
+ */
+size_t woq_prepared_bytes(int64_t n, int64_t k);
+
+/*
+ * Canonical packed [n, k/2] -> prepared layout (above).  ASYNC.
+ * Arguments: packed (device, 16-byte aligned); prepared (device, 16-byte
+ *   aligned) of woq_prepared_bytes(n, k) bytes; the two must not overlap.
+ * Errors: WOQ_EINVAL (negative size, NULL pointer), WOQ_ESHAPE (k not a
+ *   multiple of 32), WOQ_EUNSUPPORTED (n or k >= 2^31, n*k >= 2^40),
+ *   WOQ_EALIGN, WOQ_EHIP.
+ */
+int32_t woq_prepare_int4(const uint8_t* packed, int64_t n, int64_t k, uint8_t* prepared,
+                         void* stream);
+
+/*
+ * Prepared layout -> canonical packed [n, k/2] (the inverse, for validation and
+ * export).  ASYNC.  Same arguments and errors as woq_prepare_int4.
+ */
+int32_t woq_unprepare_int4(const uint8_t* prepared, int64_t n, int64_t k, uint8_t* packed,
+                           void* stream);
+
+/*
+ * woq_linear_int4_groups over prepared weights: identical arguments, results
+ * and errors, except that `prepared` (device, 16-byte aligned, at least
+ * woq_prepared_bytes(n, k) bytes) replaces `packed`.  The result equals that
+ * of woq_linear_int4_groups on the canonical weights the buffer was prepared
+ * from.  woq_linear_workspace_bytes and woq_linear_plan apply unchanged.
+ */
+int32_t woq_linear_int4_groups_prepared(const void* x_bf16, int64_t m, const uint8_t* prepared,
+                                        const float* scale, const uint8_t* zero,
+                                        const float* bias, const int32_t* order, int64_t n,
+                                        int64_t k, int32_t group, int32_t y_dtype, void* y,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Describe the kernel plan the linear calls use for these sizes: the path
+ * (decode GEMV for m <= 4, skinny MFMA for m <= 16, tiled MFMA GEMM above),
+ * tiles, waves and whether an input pre-pass runs.  Writes a NUL-terminated
+ * string of at most len bytes into buf (host).  Pure host function.
  * Errors: WOQ_EINVAL (buf NULL, len 0), plus the shape errors of the linear call.
  */
 int32_t woq_linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, int32_t has_order,

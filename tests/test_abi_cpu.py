@@ -144,3 +144,27 @@ def test_plan_buffer_checks(lib):
     buf = ctypes.create_string_buffer(8)
     assert lib.woq_linear_plan(1, 64, 256, 32, 0, buf, len(buf)) == 0
     assert len(buf.value) == 7          # truncated, NUL-terminated
+
+
+def test_prepared_layout_host_checks(lib):
+    import oracle
+    for n, k in ((0, 0), (1, 32), (17, 96), (4096, 4096), (14336, 4096), (5, 4160)):
+        assert lib.woq_prepared_bytes(n, k) == oracle.prepared_bytes(n, k)
+    assert lib.woq_prepared_bytes(4, 48) == 0          # k not a multiple of 32
+    assert lib.woq_prepared_bytes(-1, 64) == 0
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    for fn in (lib.woq_prepare_int4, lib.woq_unprepare_int4):
+        assert woq.STATUS[fn(fake, 4, 48, fake, None)] == "WOQ_ESHAPE"
+        assert woq.STATUS[fn(fake, -1, 64, fake, None)] == "WOQ_EINVAL"
+        assert woq.STATUS[fn(None, 4, 64, fake, None)] == "WOQ_EINVAL"
+        assert woq.STATUS[fn(odd, 4, 64, fake, None)] == "WOQ_EALIGN"
+        assert woq.STATUS[fn(fake, 1 << 31, 64, fake, None)] == "WOQ_EUNSUPPORTED"
+        assert fn(None, 0, 64, None, None) == 0
+    # the prepared linear shares the canonical one's checks
+    rc = lib.woq_linear_int4_groups_prepared(fake, 1, odd, fake, fake, None, None, 64, 256, 32, 1,
+                                             fake, None, 0, None)
+    assert woq.STATUS[rc] == "WOQ_EALIGN"
+    rc = lib.woq_linear_int4_groups_prepared(fake, 1, fake, fake, fake, None, None, 64, 256, 48, 1,
+                                             fake, None, 0, None)
+    assert woq.STATUS[rc] == "WOQ_EGROUP"

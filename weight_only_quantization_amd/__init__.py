@@ -30,6 +30,10 @@ __all__ = [
     "unpack_uint4",
     "dequantize_int4_groups",
     "linear_int4_groups",
+    "linear_int4_groups_prepared",
+    "prepare_int4",
+    "unprepare_int4",
+    "prepared_bytes",
     "linear_workspace_bytes",
     "linear_plan",
     "STATUS",
@@ -79,6 +83,11 @@ def load() -> ctypes.CDLL:
         "woq_linear_int4_groups": (c_i32, [c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_i64, c_i64,
                                            c_i32, c_i32, c_p, c_p, c_sz, c_p]),
         "woq_linear_plan": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, ctypes.c_char_p, c_sz]),
+        "woq_prepared_bytes": (c_sz, [c_i64, c_i64]),
+        "woq_prepare_int4": (c_i32, [c_p, c_i64, c_i64, c_p, c_p]),
+        "woq_unprepare_int4": (c_i32, [c_p, c_i64, c_i64, c_p, c_p]),
+        "woq_linear_int4_groups_prepared": (c_i32, [c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_i64, c_i64,
+                                                    c_i32, c_i32, c_p, c_p, c_sz, c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -193,6 +202,60 @@ def linear_plan(m: int, n: int, k: int, group: int, has_order: bool = False) -> 
     return buf.value.decode()
 
 
+def prepared_bytes(n: int, k: int) -> int:
+    """Bytes of the prepared (fragment-ordered) layout of an [n, k] weight."""
+    return int(load().woq_prepared_bytes(n, k))
+
+
+def prepare_int4(packed: torch.Tensor, k: Optional[int] = None) -> torch.Tensor:
+    """Canonical packed rows [N, K/2] (or [N, K/G, G/2]) -> prepared uint8 buffer.
+
+    The layout is the one ``woq_prepare_int4`` documents: 1 KB blocks of 16
+    outputs x 128 inputs in MFMA operand order.  Asynchronous.
+    """
+    lib = load()
+    _need(packed, torch.uint8, "packed")
+    n = packed.shape[0]
+    kk = 2 * (packed.numel() // n) if n else 0
+    k = kk if k is None else k
+    if k != kk:
+        raise ValueError(f"packed holds {kk} inputs per row, not {k}")
+    out = torch.empty(max(prepared_bytes(n, k), 1), dtype=torch.uint8, device=packed.device)
+    _check(lib.woq_prepare_int4(_ptr(packed), n, k, _ptr(out), _stream()), "prepare_int4")
+    return out[:prepared_bytes(n, k)]
+
+
+def unprepare_int4(prepared: torch.Tensor, n: int, k: int) -> torch.Tensor:
+    """Inverse of :func:`prepare_int4`: prepared buffer -> packed rows [N, K/2]."""
+    lib = load()
+    _need(prepared, torch.uint8, "prepared")
+    if prepared.numel() < prepared_bytes(n, k):
+        raise ValueError("prepared buffer is smaller than the layout of [n, k]")
+    out = torch.empty((n, k // 2), dtype=torch.uint8, device=prepared.device)
+    _check(lib.woq_unprepare_int4(_ptr(prepared), n, k, _ptr(out), _stream()), "unprepare_int4")
+    return out
+
+
+def linear_int4_groups_prepared(x: torch.Tensor, prepared: torch.Tensor, scale: torch.Tensor,
+                                zero: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                                order: Optional[torch.Tensor] = None,
+                                out_dtype: torch.dtype = torch.bfloat16,
+                                out: Optional[torch.Tensor] = None,
+                                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """:func:`linear_int4_groups` over prepared weights (see :func:`prepare_int4`).
+
+    N comes from scale [N, K/G], K from x [M, K], the group from both.
+    """
+    _need(scale, torch.float32, "scale")
+    if x.dim() != 2 or scale.dim() != 2 or scale.shape[1] == 0:
+        raise ValueError("x must be [M, K] and scale [N, K/G]")
+    n, k = scale.shape[0], x.shape[1]
+    if prepared.numel() < prepared_bytes(n, k):
+        raise ValueError("prepared buffer is smaller than the layout of [n, k]")
+    return _linear(x, prepared, scale, zero, bias, order, n, k, k // scale.shape[1], out_dtype,
+                   out, workspace, True)
+
+
 def linear_int4_groups(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tensor,
                        zero: torch.Tensor, bias: Optional[torch.Tensor] = None,
                        order: Optional[torch.Tensor] = None, group: Optional[int] = None,
@@ -206,9 +269,20 @@ def linear_int4_groups(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tenso
     None.  Returns y [M, N] of out_dtype (bfloat16 or float32).  Asynchronous
     on the current stream.
     """
+    _need(packed, torch.uint8, "packed")
+    _need(scale, torch.float32, "scale")
+    n, k, group = _weight_dims(packed, scale, group)
+    if x.dim() == 2 and x.shape[1] != k:
+        raise ValueError(f"x has {x.shape[1]} inputs, the weight {k}")
+    return _linear(x, packed, scale, zero, bias, order, n, k, group, out_dtype, out, workspace,
+                   False)
+
+
+def _linear(x, weights, scale, zero, bias, order, n, k, group, out_dtype, out, workspace,
+            prepared: bool):
     lib = load()
     _need(x, torch.bfloat16, "x")
-    _need(packed, torch.uint8, "packed")
+    _need(weights, torch.uint8, "prepared" if prepared else "packed")
     _need(scale, torch.float32, "scale")
     _need(zero, torch.uint8, "zero")
     if bias is not None:
@@ -218,9 +292,6 @@ def linear_int4_groups(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tenso
     if x.dim() != 2:
         raise ValueError("x must be [M, K]")
     m = x.shape[0]
-    n, k, group = _weight_dims(packed, scale, group)
-    if x.shape[1] != k:
-        raise ValueError(f"x has {x.shape[1]} inputs, the weight {k}")
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype must be float32 or bfloat16")
     if out is None:
@@ -231,9 +302,9 @@ def linear_int4_groups(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tenso
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wsb = workspace.numel() if (need and workspace is not None) else 0
-    _check(lib.woq_linear_int4_groups(_ptr(x), m, _ptr(packed), _ptr(scale), _ptr(zero),
-                                      _ptr(bias), _ptr(order), n, k, group,
-                                      F32 if out_dtype == torch.float32 else BF16, _ptr(out),
-                                      _ptr(workspace) if need else None, wsb, _stream()),
-           "linear_int4_groups")
+    fn = lib.woq_linear_int4_groups_prepared if prepared else lib.woq_linear_int4_groups
+    _check(fn(_ptr(x), m, _ptr(weights), _ptr(scale), _ptr(zero), _ptr(bias), _ptr(order), n, k,
+              group, F32 if out_dtype == torch.float32 else BF16, _ptr(out),
+              _ptr(workspace) if need else None, wsb, _stream()),
+           "linear_int4_groups_prepared" if prepared else "linear_int4_groups")
     return out

@@ -49,28 +49,36 @@ bool skinny_override(int* ns, int* waves) {
 
 // Decode GEMV launch shape.  Each wave takes `cnt` consecutive 128-input
 // steps (4, 8, 12 or 16) and a workgroup of ceil(steps / cnt) waves (at most
-// 16) covers K for 16 outputs.  The smallest cnt whose grid stays within the
-// target number of waves is taken, else the largest: enough waves that every
-// SIMD holds two or more (their instruction streams then overlap), few
-// enough that per-wave set-up stays small against the steps.  WOQ_GEMV_WAVES
-// overrides the target (a tuning aid, read on every call).
+// 16) covers K for 16 outputs.  A step costs the fewest instructions for
+// m = 1 and groups of 128 or more (no lane transpose, one piece per step), so
+// there long ranges (16 steps) amortize each wave's set-up best; 64-wide
+// groups take 8, and 32-wide groups or m > 1 take 4 (more, shorter waves
+// overlap the heavier steps).  Small grids give up range length until about
+// 1536 waves cover the chip; the 16-wave limit per workgroup can force longer
+// ranges.  (Measured on the 14336x4096, 4096x14336 and 4096x4096 decode
+// shapes for every group size at m = 1 and 4.)  WOQ_GEMV_WAVES replaces the
+// rule by "the smallest cnt whose grid has at most this many waves" (a
+// tuning aid, read on every call).
 bool gemv_plan(int64_t m, int64_t n, int64_t k, int32_t group, LinearPlan* p) {
-  int64_t target = 3584;
-  if (const char* e = std::getenv("WOQ_GEMV_WAVES")) {
-    const long v = std::strtol(e, nullptr, 10);
-    if (v > 0) target = v;
-  }
   const int64_t nsteps = (k + 127) / 128;
   const int64_t tiles = (n + 15) / 16;
-  int64_t cnt = 16;
-  for (int64_t c = 4; c <= 16; c += 4) {
-    const int64_t w = (nsteps + c - 1) / c;
-    if (w <= 16 && tiles * w <= target) {
-      cnt = c;
-      break;
+  auto waves = [&](int64_t c) { return (nsteps + c - 1) / c; };
+  int64_t cnt;
+  if (const char* e = std::getenv("WOQ_GEMV_WAVES"); e && std::strtol(e, nullptr, 10) > 0) {
+    const int64_t target = std::strtol(e, nullptr, 10);
+    cnt = 16;
+    for (int64_t c = 4; c <= 16; c += 4) {
+      if (waves(c) <= 16 && tiles * waves(c) <= target) {
+        cnt = c;
+        break;
+      }
     }
+  } else {
+    cnt = (m == 1 && group >= 128) ? 16 : (m == 1 && group == 64) ? 8 : 4;
+    while (cnt > 4 && tiles * waves(cnt) < 1536) cnt -= 4;
+    while (cnt < 16 && waves(cnt) > 16) cnt += 4;
   }
-  const int64_t w = (nsteps + cnt - 1) / cnt;
+  const int64_t w = waves(cnt);
   if (w > 16) return false;   // more than 1024 threads per workgroup
   if (gemv_layout(m, k, group, (int)w, (int)cnt).total > kSkinnyLdsLimit) return false;
   p->path = 4;
@@ -267,11 +275,16 @@ size_t woq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group
   return linear_workspace_layout(m, n, k, group, has_order != 0).total;
 }
 
-int32_t woq_linear_int4_groups(const void* x_bf16, int64_t m, const uint8_t* packed,
-                               const float* scale, const uint8_t* zero, const float* bias,
-                               const int32_t* order, int64_t n, int64_t k, int32_t group,
-                               int32_t y_dtype, void* y, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the two linear entry points; `prepared` selects the weight
+// layout the kernels address.
+int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const float* scale,
+                    const uint8_t* zero, const float* bias, const int32_t* order, int64_t n,
+                    int64_t k, int32_t group, int32_t y_dtype, void* y, void* workspace,
+                    size_t workspace_bytes, void* stream, int32_t prepared) {
   int32_t st = check_linear_shape(m, n, k, group);
   if (st != WOQ_OK) return st;
   if (y_dtype != WOQ_F32 && y_dtype != WOQ_BF16) return WOQ_EINVAL;
@@ -307,6 +320,7 @@ int32_t woq_linear_int4_groups(const void* x_bf16, int64_t m, const uint8_t* pac
   a.y_bf16 = y_dtype == WOQ_BF16;
   a.mpad = plan.mpad;
   a.kpad = a.k;
+  a.prepared = prepared;
   if (plan.path == 1) {
     if (has_order) {
       uint16_t* xg = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
@@ -334,6 +348,55 @@ int32_t woq_linear_int4_groups(const void* x_bf16, int64_t m, const uint8_t* pac
   a.x = xg;
   a.xs = xs;
   return launch_gemm(a, plan, wsb + ws.sz_off, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t woq_linear_int4_groups(const void* x_bf16, int64_t m, const uint8_t* packed,
+                               const float* scale, const uint8_t* zero, const float* bias,
+                               const int32_t* order, int64_t n, int64_t k, int32_t group,
+                               int32_t y_dtype, void* y, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return linear_impl(x_bf16, m, packed, scale, zero, bias, order, n, k, group, y_dtype, y,
+                     workspace, workspace_bytes, stream, 0);
+}
+
+int32_t woq_linear_int4_groups_prepared(const void* x_bf16, int64_t m, const uint8_t* prepared,
+                                        const float* scale, const uint8_t* zero,
+                                        const float* bias, const int32_t* order, int64_t n,
+                                        int64_t k, int32_t group, int32_t y_dtype, void* y,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  return linear_impl(x_bf16, m, prepared, scale, zero, bias, order, n, k, group, y_dtype, y,
+                     workspace, workspace_bytes, stream, 1);
+}
+
+size_t woq_prepared_bytes(int64_t n, int64_t k) {
+  if (n < 0 || k < 0 || k % 32 || n >= kMaxDim || k >= kMaxDim) return 0;
+  return (size_t)prepared_bytes(n, k);
+}
+
+int32_t woq_prepare_int4(const uint8_t* packed, int64_t n, int64_t k, uint8_t* prepared,
+                         void* stream) {
+  if (n < 0 || k < 0) return WOQ_EINVAL;
+  if (k % 32) return WOQ_ESHAPE;
+  if (n >= kMaxDim || k >= kMaxDim || n * k >= kMaxElems) return WOQ_EUNSUPPORTED;
+  if (n == 0 || k == 0) return WOQ_OK;
+  if (!packed || !prepared) return WOQ_EINVAL;
+  if (!aligned(packed, 16) || !aligned(prepared, 16)) return WOQ_EALIGN;
+  return launch_prepare(packed, n, k, prepared, reinterpret_cast<hipStream_t>(stream));
+}
+
+int32_t woq_unprepare_int4(const uint8_t* prepared, int64_t n, int64_t k, uint8_t* packed,
+                           void* stream) {
+  if (n < 0 || k < 0) return WOQ_EINVAL;
+  if (k % 32) return WOQ_ESHAPE;
+  if (n >= kMaxDim || k >= kMaxDim || n * k >= kMaxElems) return WOQ_EUNSUPPORTED;
+  if (n == 0 || k == 0) return WOQ_OK;
+  if (!packed || !prepared) return WOQ_EINVAL;
+  if (!aligned(packed, 16) || !aligned(prepared, 16)) return WOQ_EALIGN;
+  return launch_unprepare(prepared, n, k, packed, reinterpret_cast<hipStream_t>(stream));
 }
 
 int32_t woq_linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, int32_t has_order,

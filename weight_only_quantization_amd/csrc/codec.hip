@@ -279,6 +279,40 @@ unsigned grid_for(int64_t items) {
   return (unsigned)(blocks < 1 ? 1 : (blocks > 65536 ? 65536 : blocks));
 }
 
+// Prepared (fragment-ordered) weights: blocks of 16 outputs x 128 inputs
+// (1024 bytes), tile-major then step-major; 16-byte slot l of block (t, s)
+// holds row 16t + l % 16, packed bytes 64 s + 16 (l / 16) .. +16.  One thread
+// per 16-byte slot; rows past n and bytes past k/2 are zero.
+__global__ __launch_bounds__(kThreads) void prepare_kernel(const uint8_t* __restrict__ packed, int64_t n,
+                                                           int64_t row_bytes, int64_t nsteps,
+                                                           int64_t nslots, uint4* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nslots; i += stride) {
+    const int64_t b = i >> 6;
+    const int l = (int)(i & 63);
+    const int64_t t = b / nsteps, st = b - t * nsteps;
+    const int64_t row = 16 * t + (l & 15);
+    const int64_t byte = 64 * st + 16 * (l >> 4);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (row < n && byte < row_bytes) v = *reinterpret_cast<const uint4*>(packed + row * row_bytes + byte);
+    out[i] = v;
+  }
+}
+
+// Inverse: one thread per 16-byte chunk of the canonical rows.
+__global__ __launch_bounds__(kThreads) void unprepare_kernel(const uint4* __restrict__ prepared,
+                                                             int64_t row_bytes, int64_t nsteps,
+                                                             int64_t nchunks, uint8_t* __restrict__ packed) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t cpr = row_bytes / 16;
+  for (int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x; j < nchunks; j += stride) {
+    const int64_t row = j / cpr, cc = j - row * cpr;
+    const int64_t st = cc >> 2;
+    const int l = (int)(16 * (cc & 3) + (row & 15));
+    *reinterpret_cast<uint4*>(packed + row * row_bytes + 16 * cc) = prepared[((row >> 4) * nsteps + st) * 64 + l];
+  }
+}
+
 }  // namespace
 
 int32_t launch_quantize(const float* w, int64_t n, int64_t k, int32_t group, int32_t symmetric,
@@ -357,6 +391,26 @@ int32_t launch_dequantize(const uint8_t* packed, const float* scale, const uint8
       hipLaunchKernelGGL(dequant_byte_kernel<false>, dim3(grid_for(nbytes)), dim3(kThreads), 0, stream,
                          packed, scale, zero, nbytes, k / 2, group, w_hat);
   }
+  return hip_status(hipGetLastError());
+}
+
+int32_t launch_prepare(const uint8_t* packed, int64_t n, int64_t k, uint8_t* prepared,
+                       hipStream_t stream) {
+  const int64_t nsteps = (k + 127) / 128;
+  const int64_t nslots = (n + 15) / 16 * nsteps * 64;
+  if (nslots == 0) return WOQ_OK;
+  hipLaunchKernelGGL(prepare_kernel, dim3(grid_for(nslots)), dim3(kThreads), 0, stream,
+                     packed, n, k / 2, nsteps, nslots, reinterpret_cast<uint4*>(prepared));
+  return hip_status(hipGetLastError());
+}
+
+int32_t launch_unprepare(const uint8_t* prepared, int64_t n, int64_t k, uint8_t* packed,
+                         hipStream_t stream) {
+  const int64_t nsteps = (k + 127) / 128;
+  const int64_t nchunks = n * (k / 32);
+  if (nchunks == 0) return WOQ_OK;
+  hipLaunchKernelGGL(unprepare_kernel, dim3(grid_for(nchunks)), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const uint4*>(prepared), k / 2, nsteps, nchunks, packed);
   return hip_status(hipGetLastError());
 }
 

@@ -167,7 +167,7 @@ __device__ __forceinline__ f32x16_t mfma32f(float a, float b, f32x16_t c) {
 
 struct GemmParams {
   const uint16_t* xp;     // pair-ordered activations [M, kpad], zero past K
-  const uint8_t* packed;  // [N, K/2]
+  const uint8_t* packed;  // [N, K/2], or prepared blocks
   const float* xs;        // piece sums [K/piece][mpad]
   const f32x2_t* sz;      // (scale, -(128 + zero)) [K/G][npad]
   const float* bias;
@@ -176,6 +176,7 @@ struct GemmParams {
   int64_t mpad;
   int32_t npad, ngroups, npieces;
   int32_t tiles_m, tiles_n;
+  int32_t prepared;       // 1: packed holds prepared 1 KB blocks
 };
 
 // Tl: workgroup tile; GB: 32-input blocks per group piece inside a step (1, 2
@@ -217,8 +218,13 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
 
   const __amdgpu_buffer_rsrc_t ra =
       rsrc(p.xp + (int64_t)m0 * p.kpad, (uint32_t)min(BM, M - m0) * (uint32_t)p.kpad * 2);
+  // Weights: canonical rows, or prepared 1 KB blocks (16 rows x one step,
+  // tile-major; slot l of a block holds row l % 16, quarter l / 16 of the step).
+  const bool prep = p.prepared != 0;   // uniform
+  const int ptiles = min(BN / 16, (N + 15) / 16 - n0 / 16);
   const __amdgpu_buffer_rsrc_t rb =
-      rsrc(p.packed + (int64_t)n0 * row_bytes, (uint32_t)min(BN, N - n0) * row_bytes);
+      prep ? rsrc(p.packed + (int64_t)(n0 / 16) * nsteps * 1024, (uint32_t)(ptiles * nsteps) * 1024u)
+           : rsrc(p.packed + (int64_t)n0 * row_bytes, (uint32_t)min(BN, N - n0) * row_bytes);
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.xs, (uint32_t)((int64_t)p.npieces * p.mpad * 4));
   const __amdgpu_buffer_rsrc_t rz = rsrc(p.sz, (uint32_t)((int64_t)p.ngroups * p.npad * 8));
 
@@ -248,8 +254,10 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
       const int row = 16 * b + (lane >> 2);
       const int c = (lane & 3) ^ ((row >> 1) & 3);
       const bool real = b < Tl::kB;
-      const uint32_t off = real && (uint32_t)(k0 / 2 + 16 * c) < row_bytes
-                               ? (uint32_t)row * row_bytes + (uint32_t)(k0 / 2 + 16 * c) : kOffsetOOB;
+      const uint32_t off = !real ? kOffsetOOB
+                           : prep ? (uint32_t)(b * nsteps + step) * 1024u + 16u * (uint32_t)(16 * c + (lane >> 2))
+                           : (uint32_t)(k0 / 2 + 16 * c) < row_bytes ? (uint32_t)row * row_bytes + (uint32_t)(k0 / 2 + 16 * c)
+                                                                     : kOffsetOOB;
       bload16_lds(rb, real ? st + kABytes + b * 1024 : junk, off | dead);
     }
 #pragma unroll
@@ -565,7 +573,7 @@ int32_t launch_gemm(const LinearArgs& a, const LinearPlan& pl, void* sz_ws, hipS
   const int32_t piece = a.group < kStepK ? a.group : kStepK;
   const GemmParams gp{a.x, a.packed, a.xs, static_cast<const f32x2_t*>(sz_ws), a.bias, a.y,
                       a.m, a.n, a.k, a.kpad, a.group, a.y_bf16, a.mpad, npad, ngroups, a.k / piece,
-                      0, 0};
+                      0, 0, a.prepared};
   // Tile by the number of activation rows: small M takes narrow tiles so the
   // grid still covers the chip.
   switch (pl.bm) {

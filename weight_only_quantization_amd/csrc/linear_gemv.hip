@@ -54,6 +54,7 @@ struct GemvParams {
   int32_t group_shift;  // log2(group)
   int32_t x_batches;    // activation staging batches of XL loads per lane
   int32_t z_bytewise;   // 1 when a row's groups do not fill whole dwords
+  int32_t prepared;     // 1: weights in the prepared layout
   int32_t wave_lds;     // LDS bytes per wave
   int32_t xs_off;       // offsets inside a wave's region: piece sums
   int32_t sz_off;       //   (scale, -(128 + zero)) pairs
@@ -132,7 +133,13 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   const int live = min(cnt, p.nsteps - s0);        // <= 0 for a wave past K
   const uint32_t wbase = (uint32_t)(wave * p.wave_lds);
 
-  const __amdgpu_buffer_rsrc_t rb = rsrc(p.packed + (int64_t)row0 * row_bytes, (uint32_t)rows * row_bytes);
+  // Weights: canonical rows [N, K/2], or prepared 1 KB blocks (16 rows x one
+  // 128-input step, tile-major) whose 16-byte slot l is exactly lane l's share
+  // of a step, so a step is one contiguous kilobyte.
+  const bool prep = p.prepared != 0;   // uniform
+  const __amdgpu_buffer_rsrc_t rb =
+      prep ? rsrc(p.packed + (int64_t)blockIdx.x * p.nsteps * 1024, (uint32_t)p.nsteps * 1024u)
+           : rsrc(p.packed + (int64_t)row0 * row_bytes, (uint32_t)rows * row_bytes);
   const __amdgpu_buffer_rsrc_t rs = rsrc(p.scale + (int64_t)row0 * p.ngroups, (uint32_t)(rows * p.ngroups) * 4u);
   const __amdgpu_buffer_rsrc_t rz = rsrc(p.zero + (int64_t)row0 * p.ngroups, (uint32_t)(rows * p.ngroups));
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.x, (uint32_t)M * (uint32_t)K * 2u);
@@ -209,10 +216,12 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   // ---- weight ring --------------------------------------------------------------
   // Steps past this wave's range load nothing: their offsets get bit 31.
   u32x4_t bq[PF];
-  const uint32_t boff = (uint32_t)c * row_bytes + 16u * (uint32_t)q + (uint32_t)s0 * (kStepK / 2);
+  const uint32_t bstep = prep ? 1024u : (uint32_t)(kStepK / 2);   // bytes per step and lane group
+  const uint32_t boff = prep ? 16u * (uint32_t)lane + (uint32_t)s0 * 1024u
+                             : (uint32_t)c * row_bytes + 16u * (uint32_t)q + (uint32_t)s0 * (kStepK / 2);
   auto issue = [&](int slot, int i) {
     const uint32_t dead = (uint32_t)(live - 1 - i) & kOffsetOOB;    // uniform
-    bq[slot] = bload16(rb, (boff + (uint32_t)i * (kStepK / 2)) | dead);
+    bq[slot] = bload16(rb, (boff + (uint32_t)i * bstep) | dead);
   };
 
   load_x();
@@ -405,7 +414,7 @@ int32_t launch_gemv(const LinearArgs& a, const LinearPlan& pl, hipStream_t strea
   const int32_t xl = pl.fold_rows == 1 ? cc / 4 : 4;
   const int32_t loads = (a.m * pl.cnt / 4 + xl - 1) / xl;
   GemvParams gp{a.x, a.packed, a.scale, a.zero, a.bias, a.y, a.m, a.n, a.k, a.y_bf16,
-                nsteps, pl.cnt, ngroups, gshift, loads, ngroups % 4 != 0 ? 1 : 0,
+                nsteps, pl.cnt, ngroups, gshift, loads, ngroups % 4 != 0 ? 1 : 0, a.prepared,
                 l.wave_lds, l.xs_off, l.sz_off, l.red_off, kNibPairMask, kBf16Offset2};
   return pl.fold_rows == 1 ? dispatch_gb<1>(gp, pl, l.total, stream)
                            : dispatch_gb<4>(gp, pl, l.total, stream);

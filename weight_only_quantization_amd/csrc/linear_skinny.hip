@@ -63,6 +63,7 @@ struct SkinnyParams {
   int32_t sz_off;       // LDS offset of the staged (scale, -(128 + zero)) pairs
   int32_t z_bytewise;    // 1 when a row's zero points do not fill whole dwords
   int32_t t_rows, t_cols;  // workgroup size split into activation rows and 16-byte chunks
+  int32_t prepared;        // 1: weights in the prepared layout
   // The nibble mask and the bf16 offset pattern arrive as arguments so they sit
   // in registers: one v_and_or_b32 per pair then expands two codes.
   uint32_t nib_mask, nib_offset;
@@ -100,7 +101,14 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   const int rows = min(NS * 16, N - row0);
   const int cnt = wave < nsteps ? (nsteps - wave + W - 1) / W : 0;
 
-  const __amdgpu_buffer_rsrc_t rb = rsrc(p.packed + (int64_t)row0 * row_bytes, (uint32_t)rows * row_bytes);
+  // Weights: canonical rows, or prepared 1 KB blocks (16 rows x one step,
+  // tile-major) whose 16-byte slot l is lane l's share of a step.
+  const bool prep = p.prepared != 0;   // uniform
+  const int tile0 = blockIdx.x * NS;
+  const int ptiles = min(NS, (N + 15) / 16 - tile0);
+  const __amdgpu_buffer_rsrc_t rb =
+      prep ? rsrc(p.packed + (int64_t)tile0 * nsteps * 1024, (uint32_t)(ptiles * nsteps) * 1024u)
+           : rsrc(p.packed + (int64_t)row0 * row_bytes, (uint32_t)rows * row_bytes);
   const __amdgpu_buffer_rsrc_t rs = rsrc(p.scale + (int64_t)row0 * ngroups, (uint32_t)rows * ngroups * 4);
   const __amdgpu_buffer_rsrc_t rz = rsrc(p.zero + (int64_t)row0 * ngroups, (uint32_t)rows * ngroups);
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.x, (uint32_t)M * (uint32_t)K * 2);
@@ -112,10 +120,13 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   u32x4_t bq[PF][NS];
   uint32_t boff[NS];              // per-lane byte offset of its row and lane group
 #pragma unroll
-  for (int t = 0; t < NS; ++t) boff[t] = (uint32_t)(16 * t + c) * row_bytes + (uint32_t)(16 * q);
+  for (int t = 0; t < NS; ++t)
+    boff[t] = prep ? (uint32_t)(t * nsteps) * 1024u + 16u * (uint32_t)lane
+                   : (uint32_t)(16 * t + c) * row_bytes + (uint32_t)(16 * q);
+  const uint32_t bstep = prep ? 1024u : (uint32_t)(kStepK / 2);
   auto issue = [&](int slot, int i) {
     const uint32_t dead = (uint32_t)(cnt - 1 - i) & kOffsetOOB;
-    const uint32_t step_off = (uint32_t)((wave + i * W) * (kStepK / 2)) | dead;   // uniform
+    const uint32_t step_off = (uint32_t)(wave + i * W) * bstep | dead;   // uniform
 #pragma unroll
     for (int t = 0; t < NS; ++t) bq[slot][t] = bload16(rb, boff[t] + step_off);
   };
@@ -407,7 +418,7 @@ int32_t launch_skinny(const LinearArgs& a, const LinearPlan& pl, hipStream_t str
   SkinnyParams sp{a.x, a.packed, a.scale, a.zero, a.bias, a.y, a.m, a.n, a.k, a.group, a.y_bf16,
                   gshift, kpad, kpad * 2 + 16, (int32_t)l.sz_off,
                   (a.k / a.group) % 4 != 0 ? 1 : 0, 64 * pl.waves / (kpad / 8),
-                  64 * pl.waves % (kpad / 8), kNibPairMask, kBf16Offset2};
+                  64 * pl.waves % (kpad / 8), a.prepared, kNibPairMask, kBf16Offset2};
   const size_t lds = l.total;
   const bool one = pl.fold_rows == 1;
   switch (pl.ns) {

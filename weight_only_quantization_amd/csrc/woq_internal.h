@@ -66,10 +66,16 @@ int32_t launch_unpack(const uint8_t* packed, int64_t count, uint8_t* q, hipStrea
 int32_t launch_dequantize(const uint8_t* packed, const float* scale, const uint8_t* zero,
                           int64_t n, int64_t k, int32_t group, int32_t out_dtype, void* w_hat,
                           hipStream_t stream);
+// Prepared weights: 1 KB blocks of 16 outputs x 128 inputs (see woq.h).
+inline int64_t prepared_bytes(int64_t n, int64_t k) { return (n + 15) / 16 * ((k + 127) / 128) * 1024; }
+int32_t launch_prepare(const uint8_t* packed, int64_t n, int64_t k, uint8_t* prepared,
+                       hipStream_t stream);
+int32_t launch_unprepare(const uint8_t* prepared, int64_t n, int64_t k, uint8_t* packed,
+                         hipStream_t stream);
 
 struct LinearArgs {
   const uint16_t* x;       // bf16 bits [M, K] (possibly the gathered copy)
-  const uint8_t* packed;   // [N, K/2]
+  const uint8_t* packed;   // [N, K/2], or prepared blocks when `prepared`
   const float* scale;      // [N, K/G]
   const uint8_t* zero;     // [N, K/G]
   const float* bias;       // [N] or null
@@ -79,6 +85,7 @@ struct LinearArgs {
   int32_t y_bf16;
   int32_t kpad;            // row stride of x (K rounded up to 128 on the GEMM path)
   int64_t mpad;
+  int32_t prepared;        // 1: weights in the prepared (fragment-ordered) layout
 };
 
 int32_t launch_prep(const uint16_t* x, const int32_t* order, int32_t m, int32_t k, int32_t kpad,
