@@ -346,12 +346,9 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   }
 }
 
-#ifndef GEMV_PF_LONG
-#define GEMV_PF_LONG 4
-#endif
 template <int GB, int FR, int CC>
 int32_t launch_one(const GemvParams& gp, const LinearPlan& pl, size_t lds, hipStream_t stream) {
-  auto kern = gemv_kernel<GB, FR, CC, (CC >= 8 ? GEMV_PF_LONG : 4)>;
+  auto kern = gemv_kernel<GB, FR, CC, 4>;
   if (lds > 64 * 1024) {
     static bool raised = false;   // raise the dynamic-LDS limit once per instantiation
     if (!raised) {
