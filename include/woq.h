@@ -151,7 +151,7 @@ size_t woq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group
  *   when that is 0.  The workspace holds only scratch; it need not be cleared.
  * m == 0 or n == 0 is a no-op; k == 0 gives y = bias (or 0).
  * Errors: WOQ_EINVAL, WOQ_EGROUP, WOQ_EUNSUPPORTED (group outside the list,
- *   m, n or k >= 2^31, or k >= 2^24 on the tiled GEMM path, m > 16), WOQ_EALIGN,
+ *   m, n or k >= 2^31, or k >= 2^24 on the tiled GEMM path, m > 32), WOQ_EALIGN,
  *   WOQ_EWORKSPACE, WOQ_EHIP.
  */
 int32_t woq_linear_int4_groups(const void* x_bf16, int64_t m, const uint8_t* packed,
@@ -213,7 +213,7 @@ int32_t woq_linear_int4_groups_prepared(const void* x_bf16, int64_t m, const uin
 
 /*
  * Describe the kernel plan the linear calls use for these sizes: the path
- * (decode GEMV for m <= 4, skinny MFMA for m <= 16, tiled MFMA GEMM above),
+ * (decode GEMV for m <= 4, small-M MFMA for m <= 32, tiled MFMA GEMM above),
  * tiles, waves and whether an input pre-pass runs.  Writes a NUL-terminated
  * string of at most len bytes into buf (host).  Pure host function.
  * Errors: WOQ_EINVAL (buf NULL, len 0), plus the shape errors of the linear call.

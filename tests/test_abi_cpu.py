@@ -50,7 +50,8 @@ def test_status_strings(lib):
     (1, 4096, 4096, 128, "gemv_mfma"), (4, 14336, 4096, 32, "gemv_mfma"),
     (1, 8192, 28672, 128, "gemv_mfma"), (1, 64, 40960, 128, "skinny_mfma"),
     (5, 4096, 4096, 128, "skinny_mfma"), (16, 14336, 4096, 32, "skinny_mfma"),
-    (17, 4096, 4096, 128, "gemm_mfma"), (2048, 14336, 4096, 128, "gemm_mfma"),
+    (17, 4096, 4096, 128, "skinny_mfma"), (32, 14336, 4096, 256, "skinny_mfma"),
+    (33, 4096, 4096, 128, "gemm_mfma"), (2048, 14336, 4096, 128, "gemm_mfma"),
     (0, 64, 256, 32, "none"), (3, 64, 0, 32, "bias_fill"),
 ])
 def test_plan_paths(m, n, k, g, path):

@@ -65,9 +65,10 @@ SMALL = [
     (8, 300, 1024, 64, True, False),
     (15, 17, 640, 128, False, False),
     (16, 512, 2048, 32, True, True),
-    (17, 200, 512, 128, True, False),    # first row count on the GEMM path
-    (32, 64, 160, 32, False, True),
-    (33, 257, 1024, 256, True, False),
+    (17, 200, 512, 128, True, False),    # two activation tiles on the small-M path
+    (32, 64, 160, 32, False, True),      # last row count on the small-M path, 32-input tail step
+    (24, 1000, 1920, 64, True, False),   # 8 waves, several weight tiles per workgroup
+    (33, 257, 1024, 256, True, False),   # first row count on the GEMM path
     (64, 1000, 512, 64, False, False),
     (100, 300, 384, 128, True, True),
     (128, 256, 1024, 32, False, False),
@@ -126,6 +127,39 @@ def test_gemv_launch_variants(woq, monkeypatch, m, n, k, group, with_bias, with_
         y = _run(woq, dev, group, out)
         torch.cuda.synchronize()
         check_linear(y, ref, f"gemv m={m} n={n} k={k} g={group}")
+
+
+# Small-M path launch variants: WOQ_SKINNY="tiles,cnt" forces the number of
+# 16-row weight tiles per workgroup (1, 2, 4: ragged last workgroups included)
+# and the steps per wave (partial last waves, ranges that straddle groups,
+# 32-input tail steps), with one and two activation tiles.
+SKINNY_VARIANTS = [
+    # m, n, k, group, bias, order, "tiles,cnt", expected (tiles, waves)
+    (5, 100, 1024, 128, True, False, "4,2", (4, 4)),
+    (16, 70, 2048, 32, False, True, "2,4", (2, 4)),
+    (9, 130, 1280, 64, True, False, "4,4", (4, 3)),
+    (20, 50, 1536, 256, False, False, "2,6", (2, 2)),
+    (32, 33, 864, 32, True, True, "4,2", (4, 4)),
+    (12, 64, 4096, 128, False, False, "1,16", (1, 2)),
+    (1, 40, 40960, 128, True, False, "4,40", (2, 8)),   # LDS allows 2 tiles, not 4
+]
+
+
+@pytest.mark.parametrize("m,n,k,group,with_bias,with_order,override,shape", SKINNY_VARIANTS)
+def test_skinny_launch_variants(woq, monkeypatch, m, n, k, group, with_bias, with_order, override, shape):
+    monkeypatch.setenv("WOQ_SKINNY", override)
+    monkeypatch.setenv("WOQ_FORCE_SKINNY", "1")
+    plan = woq.linear_plan(m, n, k, group, with_order)
+    _say(f"skinny m={m} n={n} k={k} g={group} bias={with_bias} order={with_order} plan: {plan}")
+    assert "path=skinny_mfma" in plan
+    assert f"weight_tiles={shape[0]} " in plan and f"waves={shape[1]} " in plan
+    dev, host = _make(woq, m, n, k, group, seed=5000 + m + n + k, with_bias=with_bias,
+                      with_order=with_order)
+    ref = _ref(host, group)
+    for out in (torch.float32, torch.bfloat16):
+        y = _run(woq, dev, group, out)
+        torch.cuda.synchronize()
+        check_linear(y, ref, f"skinny m={m} n={n} k={k} g={group}")
 
 
 def test_tiny_workload(woq):

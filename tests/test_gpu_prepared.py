@@ -64,7 +64,7 @@ def _ref(host, group, rows=None):
 
 
 CASES = [
-    # m, n, k, group, bias, order: every path (decode GEMV m <= 4, skinny m <= 16,
+    # m, n, k, group, bias, order: every path (decode GEMV m <= 4, small-M m <= 32,
     # tiled GEMM above), every group size, ragged n and k
     (1, 64, 256, 32, False, False),
     (1, 100, 96, 32, True, False),
@@ -76,6 +76,7 @@ CASES = [
     (8, 300, 1024, 64, True, False),
     (16, 520, 2048, 32, True, True),
     (17, 200, 512, 128, True, False),
+    (28, 300, 1024, 128, False, False),    # two activation tiles
     (64, 1000, 576, 64, False, False),
     (130, 257, 1024, 256, True, True),
     (300, 520, 4096, 128, False, False),

@@ -26,25 +26,49 @@ int32_t check_linear_shape(int64_t m, int64_t n, int64_t k, int32_t group) {
   return WOQ_OK;
 }
 
-// Optional tuning override of the skinny launch shape: WOQ_SKINNY="ns,waves".
-bool skinny_override(int* ns, int* waves) {
-  static int cached = -1, c_ns = 0, c_w = 0;
-  if (cached < 0) {
-    cached = 0;
-    if (const char* e = std::getenv("WOQ_SKINNY")) {
-      int a = 0, b = 0;
-      if (std::sscanf(e, "%d,%d", &a, &b) == 2 && (a == 1 || a == 2) && b >= 1 && b <= 8) {
-        c_ns = a;
-        c_w = b;
-        cached = 1;
-      }
-    }
+// Optional tuning override of the small-M launch shape: WOQ_SKINNY="tiles,cnt"
+// (16-row weight tiles per workgroup, 128-input steps per wave; read on every call).
+bool skinny_override(int* tiles, int* cnt) {
+  const char* e = std::getenv("WOQ_SKINNY");
+  int a = 0, b = 0;
+  if (!e || std::sscanf(e, "%d,%d", &a, &b) != 2) return false;
+  if (!(a == 1 || a == 2 || a == 4) || b < 2 || b % 2 != 0) return false;
+  *tiles = a;
+  *cnt = b;
+  return true;
+}
+
+// Small-M launch shape (m <= 32).  A wave takes `cnt` consecutive 128-input
+// steps (even, at least 2) and a workgroup of at most 8 waves covers K; the
+// workgroup takes 4 weight tiles when that still leaves about 200 workgroups
+// (the tiles share each activation operand), else 2 or 1.  The per-wave
+// (scale, zero) staging must fit next to the reduction area in LDS; wider
+// tiles give way first.  (Measured on 14336x4096, 4096x14336 and 4096x4096 at
+// m = 5..32 and every group size.)
+bool skinny_plan(int64_t m, int64_t n, int64_t k, int32_t group, LinearPlan* p) {
+  const int64_t nsteps = (k + 127) / 128;
+  const int64_t tiles = (n + 15) / 16;
+  int64_t cnt = (nsteps + 7) / 8;
+  if (cnt < 2) cnt = 2;
+  cnt = (cnt + 1) / 2 * 2;
+  int t = tiles >= 800 ? 4 : (tiles >= 400 ? 2 : 1);
+  int o_t, o_c;
+  if (skinny_override(&o_t, &o_c) && (nsteps + o_c - 1) / o_c <= 8) {
+    t = o_t;
+    cnt = o_c;
   }
-  if (cached == 1) {
-    *ns = c_ns;
-    *waves = c_w;
-  }
-  return cached == 1;
+  const int64_t waves = (nsteps + cnt - 1) / cnt;
+  if (waves > 8 || cnt >= ((int64_t)1 << 20)) return false;
+  while (t > 1 && skinny_lds_layout(m, k, group, (int)waves, t, (int)cnt).total > kSkinnyLdsLimit) t /= 2;
+  if (skinny_lds_layout(m, k, group, (int)waves, t, (int)cnt).total > kSkinnyLdsLimit) return false;
+  p->path = 1;
+  p->mt = (int)((m + 15) / 16);
+  p->fold_rows = 4;
+  p->ns = t;
+  p->waves = (int)waves;
+  p->cnt = (int)cnt;
+  p->grid = (tiles + t - 1) / t;
+  return true;
 }
 
 // Decode GEMV launch shape.  Each wave takes `cnt` consecutive 128-input
@@ -89,12 +113,6 @@ bool gemv_plan(int64_t m, int64_t n, int64_t k, int32_t group, LinearPlan* p) {
   return true;
 }
 
-int pow2_floor(int64_t v) {
-  int p = 1;
-  while ((int64_t)p * 2 <= v) p *= 2;
-  return p;
-}
-
 }  // namespace
 
 LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_order) {
@@ -105,40 +123,14 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
     return p;
   }
   p.gb = group >= 128 ? 4 : group / 32;
-  const int64_t nsub = (n + 15) / 16;
   const bool force_skinny = std::getenv("WOQ_FORCE_SKINNY") != nullptr;   // tuning aid, read on every call
   if (m <= 4 && !force_skinny && k < ((int64_t)1 << 26) && gemv_plan(m, n, k, group, &p)) {
     p.prep = has_order ? 1 : 0;
     return p;
   }
-  const int skinny_ns = (nsub >= 2048 && p.gb >= 2) ? 2 : 1;
   static const bool force_tiled = std::getenv("WOQ_FORCE_TILED") != nullptr;   // tuning aid
-  if (m <= 16 && !force_tiled && k < ((int64_t)1 << 26) &&
-      skinny_lds_bytes(m, k, group, 8, skinny_ns) <= kSkinnyLdsLimit) {
-    p.path = 1;
-    p.mt = 1;
-    p.fold_rows = m == 1 ? 1 : 4;
+  if (m <= 32 && !force_tiled && k < ((int64_t)1 << 26) && skinny_plan(m, n, k, group, &p)) {
     p.prep = has_order ? 1 : 0;
-    const int64_t nsteps = (k + 127) / 128;
-    int ns = skinny_ns;
-    int64_t tiles = (nsub + ns - 1) / ns;
-    // About two waves per SIMD over the grid, at most four per workgroup
-    // (measured on the decode shapes: more waves per workgroup only lengthen
-    // the staging and the cross-wave reduction).
-    int64_t want = 2048 / (tiles > 0 ? tiles : 1);
-    int waves = pow2_floor(want < 1 ? 1 : want);
-    if (waves > 4) waves = 4;
-    while (waves > 1 && waves > nsteps) waves /= 2;
-    int o_ns, o_w;
-    if (skinny_override(&o_ns, &o_w) && (o_ns == 1 || p.gb >= 2) && o_w <= nsteps &&
-        skinny_lds_bytes(m, k, group, o_w, o_ns) <= kSkinnyLdsLimit) {
-      ns = o_ns;
-      waves = o_w;
-      tiles = (nsub + ns - 1) / ns;
-    }
-    p.ns = ns;
-    p.waves = waves;
-    p.grid = tiles;
     return p;
   }
   p.path = 2;
@@ -411,10 +403,9 @@ int32_t woq_linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, int32_t 
     case 3: std::snprintf(buf, len, "path=bias_fill"); break;
     case 1:
       std::snprintf(buf, len,
-                    "path=skinny_mfma mt=%d fold_rows=%d ns=%d waves=%d group_blocks=%d grid=%lld "
-                    "prep=%s workspace=%zu",
-                    p.mt, p.fold_rows, p.ns, p.waves, p.gb, (long long)p.grid,
-                    p.prep ? "gather" : "none", ws);
+                    "path=skinny_mfma act_tiles=%d weight_tiles=%d waves=%d steps_per_wave=%d "
+                    "group_blocks=%d grid=%lld prep=%s workspace=%zu",
+                    p.mt, p.ns, p.waves, p.cnt, p.gb, (long long)p.grid, p.prep ? "gather" : "none", ws);
       break;
     case 4:
       std::snprintf(buf, len,

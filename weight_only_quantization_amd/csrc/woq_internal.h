@@ -34,18 +34,18 @@ struct LinearWorkspace {
 
 // Which kernel family runs a linear call, and with what launch shape.
 struct LinearPlan {
-  int path = 0;          // 0 none, 1 skinny MFMA (m <= 16), 2 tiled MFMA GEMM, 3 bias only (k == 0),
+  int path = 0;          // 0 none, 1 small-M MFMA (m <= 32), 2 tiled MFMA GEMM, 3 bias only (k == 0),
                          // 4 decode GEMV (m <= 4)
-  int mt = 1;            // 16-row activation tiles held per wave (skinny path)
+  int mt = 1;            // 16-row activation tiles (small-M path)
   int fold_rows = 4;     // accumulator rows folded per tile (1 when m == 1)
-  int ns = 1;            // 16-column weight tiles per workgroup (skinny path)
+  int ns = 1;            // 16-row weight tiles per workgroup (small-M path)
   int waves = 4;         // waves per workgroup
   int gb = 4;            // 32-wide k blocks per quantization group inside a 128-wide k step (1, 2, 4)
   int prep = 0;          // 1 = an input pre-pass kernel runs first
   int64_t grid = 0;      // workgroups
   int bm = 0, bn = 0;    // tile of the GEMM path
   int64_t mpad = 0;      // rows of the per-group sum table (GEMM path)
-  int cnt = 0;           // 128-input steps per wave (decode path)
+  int cnt = 0;           // 128-input steps per wave (decode and small-M paths)
 };
 
 LinearWorkspace linear_workspace_layout(int64_t m, int64_t n, int64_t k, int32_t group,
@@ -101,8 +101,16 @@ struct GemvLayout {
 GemvLayout gemv_layout(int64_t m, int64_t k, int64_t group, int waves, int cnt);
 int gemv_cnt_class(int cnt);   // the kernel variant serving `cnt` steps per wave (4, 8, 16; 0: none)
 int32_t launch_gemv(const LinearArgs& a, const LinearPlan& p, hipStream_t stream);
-size_t skinny_lds_bytes(int64_t m, int64_t k, int64_t group, int waves, int ns);
-constexpr size_t kSkinnyLdsLimit = 160 * 1024;   // staged activations, scales and zeros share the 160 KB of LDS per CU
+// Small-M path: LDS of one workgroup of `waves` waves, `tiles` 16-row weight
+// tiles and `cnt` steps per wave (per-wave (scale, zero) staging, then the
+// cross-wave reduction area).
+struct SkinnyLds {
+  int32_t ngw = 0, sz_bytes = 0;
+  int64_t red_off = 0;
+  size_t total = 0;
+};
+SkinnyLds skinny_lds_layout(int64_t m, int64_t k, int64_t group, int waves, int tiles, int cnt);
+constexpr size_t kSkinnyLdsLimit = 160 * 1024;   // LDS per CU
 size_t gemm_sz_bytes(int64_t n, int64_t k, int32_t group);
 constexpr int64_t kGemmMaxK = (int64_t)1 << 24;   // tile offsets of the GEMM path are 32-bit
 int32_t launch_gemm(const LinearArgs& a, const LinearPlan& p, void* sz_ws, hipStream_t stream);
