@@ -22,8 +22,11 @@
 // * Per group piece: acc += scale * (sum x(128 + code) - (128 + zero) * sum x);
 //   the sums of x come from the same MFMA unit against a ones operand, already
 //   in the accumulator layout.  Each wave stages the (scale, -(128 + zero))
-//   pairs of its rows and groups in its own LDS area first, with every staging
-//   load issued before the first conversion.
+//   pairs of its rows and groups in its own LDS area; those loads go out just
+//   before the first steps of the stream and are converted behind them.
+// * Per step the activation registers are refilled as soon as they are
+//   converted, and each weight tile's as soon as it is unpacked, so one tile's
+//   operands are live at a time.
 // * The waves' partial tiles meet in LDS (fixed order); bias, then y.
 #include "woq_internal.h"
 #include "mfma_common.h"
@@ -37,7 +40,7 @@ constexpr uint32_t kOffsetOOB = 0x80000000u;   // a buffer offset no descriptor 
 // s_waitcnt immediate that waits for LDS traffic only: lgkmcnt(0), vmcnt and
 // expcnt at their maxima
 constexpr int kWaitLdsOnly = 0xC07F;
-constexpr int kStageBatch = 8;   // staged (scale, zero) entries per lane and batch
+constexpr int kStageBatch = 24;  // staged (scale, zero) entries per lane and batch
 constexpr int kPF = 2;           // steps of loads in flight per wave
 
 struct SkinnyParams {
@@ -92,35 +95,38 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
 
   // 1. (scale, -(128 + zero)) of this wave's groups [gb, gb + ngw) for the
   //    workgroup's rows, [row][group] float pairs; groups past the row read zero.
+  //    The first batch of staging loads goes out before the weight stream and is
+  //    converted after it, so the two latencies overlap.
   const int gb = (s0 * kStepK) / G;
   const int ngw = p.ngw;
   unsigned char* szl = lds + wave * p.sz_bytes;
-  {
-    const __amdgpu_buffer_rsrc_t rs =
-        rsrc(p.scale + (int64_t)tile0 * 16 * p.ngroups, (uint32_t)(wg_rows * p.ngroups) * 4u);
-    const __amdgpu_buffer_rsrc_t rz =
-        rsrc(p.zero + (int64_t)tile0 * 16 * p.ngroups, (uint32_t)(wg_rows * p.ngroups));
-    const int total = 16 * T * ngw;
-    for (int base = 0; base < total; base += 64 * kStageBatch) {
-      float sv[kStageBatch];
-      uint32_t zv[kStageBatch];
+  const __amdgpu_buffer_rsrc_t rs =
+      rsrc(p.scale + (int64_t)tile0 * 16 * p.ngroups, (uint32_t)(wg_rows * p.ngroups) * 4u);
+  const __amdgpu_buffer_rsrc_t rz =
+      rsrc(p.zero + (int64_t)tile0 * 16 * p.ngroups, (uint32_t)(wg_rows * p.ngroups));
+  const int sz_total = 16 * T * ngw;
+  float sv[kStageBatch];
+  uint32_t zv[kStageBatch];
+  auto stage_load = [&](int base) {
 #pragma unroll
-      for (int b = 0; b < kStageBatch; ++b) {
-        const int e = base + lane + 64 * b;
-        const int r = e / ngw, g = e % ngw;
-        const bool in = e < total && r < wg_rows && gb + g < p.ngroups;
-        const uint32_t idx = (uint32_t)(r * p.ngroups + gb + g);
-        sv[b] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, in ? idx * 4u : kOffsetOOB, 0, 0));
-        zv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rz, in ? idx : kOffsetOOB, 0, 0);
-      }
-#pragma unroll
-      for (int b = 0; b < kStageBatch; ++b) {
-        const int e = base + lane + 64 * b;
-        if (e < total)
-          *reinterpret_cast<f32x2_t*>(szl + e * 8) = f32x2_t{sv[b], -(kNibOffset + (float)(zv[b] & 0xFFu))};
-      }
+    for (int b = 0; b < kStageBatch; ++b) {
+      const int e = base + lane + 64 * b;
+      const int r = e / ngw, g = e % ngw;
+      const bool in = e < sz_total && r < wg_rows && gb + g < p.ngroups;
+      const uint32_t idx = (uint32_t)(r * p.ngroups + gb + g);
+      sv[b] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, in ? idx * 4u : kOffsetOOB, 0, 0));
+      zv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rz, in ? idx : kOffsetOOB, 0, 0);
     }
-  }
+  };
+  auto stage_store = [&](int base) {
+#pragma unroll
+    for (int b = 0; b < kStageBatch; ++b) {
+      const int e = base + lane + 64 * b;
+      if (e < sz_total)
+        *reinterpret_cast<f32x2_t*>(szl + e * 8) = f32x2_t{sv[b], -(kNibOffset + (float)(zv[b] & 0xFFu))};
+    }
+  };
+  stage_load(0);
 
   // 2. the streams.  Weights: canonical rows [N, K/2] (lane (q, c): row c,
   //    bytes 64 s + 16 q of step s) or prepared 1 KB blocks (slot = lane).
@@ -149,10 +155,12 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   }
   u32x4_t wb[kPF][T];
   u32x4_t xb[kPF][MT][4];
-  auto issue = [&](int slot, int i) {
+  auto issue_w = [&](int slot, int t, int i) {
     const uint32_t dead = (uint32_t)(live - 1 - i) & kOffsetOOB;
-#pragma unroll
-    for (int t = 0; t < T; ++t) wb[slot][t] = bload16(rb, (woff[t] + (uint32_t)i * wstep) | dead);
+    wb[slot][t] = bload16(rb, (woff[t] + (uint32_t)i * wstep) | dead);
+  };
+  auto issue_x = [&](int slot, int i) {
+    const uint32_t dead = (uint32_t)(live - 1 - i) & kOffsetOOB;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const bool in_k = i * kStepK + kXEIn * e < xlim;
@@ -162,8 +170,18 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
                                                        : kOffsetOOB);
     }
   };
+  auto issue = [&](int slot, int i) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) issue_w(slot, t, i);
+    issue_x(slot, i);
+  };
 #pragma unroll
   for (int u = 0; u < kPF; ++u) issue(u, u);
+  stage_store(0);
+  for (int base = 64 * kStageBatch; base < sz_total; base += 64 * kStageBatch) {
+    stage_load(base);
+    stage_store(base);
+  }
 
   const uint32_t nib_offset = vgpr_copy(p.nib_offset);
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{kBf16One2, kBf16One2, kBf16One2, kBf16One2});
@@ -194,36 +212,34 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
         xsum[mt][pc] = s;
       }
     }
-    bf16x8_t bw[T][4];
+    issue_x(slot, i + kPF);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
+      bf16x8_t bw[4];
       if constexpr (kTranspose) {
         // the lane swaps work on copies, so the slot's registers are free for the refill
         uint32_t d0 = vgpr_copy(wb[slot][t][0]), d1 = vgpr_copy(wb[slot][t][1]);
         uint32_t d2 = vgpr_copy(wb[slot][t][2]), d3 = vgpr_copy(wb[slot][t][3]);
         transpose4_lanegroups(d0, d1, d2, d3);
-        bw[t][0] = unpack_codes(d0, p.nib_mask, nib_offset);
-        bw[t][1] = unpack_codes(d1, p.nib_mask, nib_offset);
-        bw[t][2] = unpack_codes(d2, p.nib_mask, nib_offset);
-        bw[t][3] = unpack_codes(d3, p.nib_mask, nib_offset);
+        bw[0] = unpack_codes(d0, p.nib_mask, nib_offset);
+        bw[1] = unpack_codes(d1, p.nib_mask, nib_offset);
+        bw[2] = unpack_codes(d2, p.nib_mask, nib_offset);
+        bw[3] = unpack_codes(d3, p.nib_mask, nib_offset);
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bw[t][e] = unpack_codes(wb[slot][t][e], p.nib_mask, nib_offset);
+        for (int e = 0; e < 4; ++e) bw[e] = unpack_codes(wb[slot][t][e], p.nib_mask, nib_offset);
       }
-    }
-    issue(slot, i + kPF);
-    __builtin_amdgcn_sched_barrier(0);
+      issue_w(slot, t, i + kPF);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int pc = 0; pc < NP; ++pc) {
-      const int g = (i * kStepK + 32 * GB * pc) / G;   // group inside the wave's range
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
+      for (int pc = 0; pc < NP; ++pc) {
+        const int g = (i * kStepK + 32 * GB * pc) / G;   // group inside the wave's range
         const f32x2_t sz = *reinterpret_cast<const f32x2_t*>(szl + ((16 * t + c) * ngw + g) * 8);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           f32x4_t cg = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int e = 0; e < GB; ++e) cg = mfma_bf16(af[mt][pc * GB + e], bw[t][pc * GB + e], cg);
+          for (int e = 0; e < GB; ++e) cg = mfma_bf16(af[mt][pc * GB + e], bw[pc * GB + e], cg);
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[mt][t][r] = fmaf(sz.x, fmaf(sz.y, xsum[mt][pc][r], cg[r]), acc[mt][t][r]);
         }
