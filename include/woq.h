@@ -212,6 +212,41 @@ int32_t woq_linear_int4_groups_prepared(const void* x_bf16, int64_t m, const uin
                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Several linear layers over the same activations in one call (for example the
+ * q, k and v projections of an attention block, or the gate and up projections
+ * of an MLP): for i < count,
+ *   y[i][m, n[i]] = x[m, k] . W_hat_i^T + bias[i],
+ * each exactly as woq_linear_int4_groups (or, with prepared = 1,
+ * woq_linear_int4_groups_prepared) would compute it with the same launch plan;
+ * results agree with the separate calls within floating-point rounding (the
+ * grouped call plans for the summed row count).  At m <= 4 all the matrices
+ * share one decode launch, which saves a kernel launch per extra matrix;
+ * other m run the matrices one after another.  ASYNC.
+ * Arguments:
+ *   x_bf16 [m, k] bfloat16 (device, 16-byte aligned), shared by every matrix;
+ *   count in 1 .. 4;
+ *   packed, scale, zero, y: host arrays of count device pointers, element i
+ *     laid out and aligned as in woq_linear_int4_groups for n[i] rows
+ *     (packed[i] holds the prepared layout when prepared = 1);
+ *   bias: host array of count device pointers (an element may be NULL), or NULL;
+ *   n: host array of count row counts; k, group, y_dtype as in
+ *     woq_linear_int4_groups;
+ *   workspace of at least the largest woq_linear_workspace_bytes(m, n[i], k,
+ *     group, 0), or NULL when that is 0.
+ *   No output may overlap an input or another output.  The act-order gather is
+ *   not offered here.
+ * Errors: as woq_linear_int4_groups for each matrix, checked for all of them
+ *   before anything is enqueued; WOQ_EINVAL for count outside 1 .. 4, NULL
+ *   arrays or prepared not 0 or 1.
+ */
+int32_t woq_linear_int4_groups_grouped(const void* x_bf16, int64_t m, int32_t count,
+                                       const uint8_t* const* packed, const float* const* scale,
+                                       const uint8_t* const* zero, const float* const* bias,
+                                       const int64_t* n, int64_t k, int32_t group,
+                                       int32_t prepared, int32_t y_dtype, void* const* y,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Describe the kernel plan the linear calls use for these sizes: the path
  * (decode GEMV for m <= 4, small-M MFMA for m <= 32, tiled MFMA GEMM above),
  * tiles, waves and whether an input pre-pass runs.  Writes a NUL-terminated

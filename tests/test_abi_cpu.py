@@ -117,6 +117,29 @@ def test_linear_rejects_misalignment_and_missing_workspace(lib):
     assert woq.STATUS[rc] == "WOQ_EWORKSPACE"
 
 
+def test_grouped_call_checks_every_matrix_first(lib):
+    a16 = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    P = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    N = lambda *v: (ctypes.c_int64 * len(v))(*v)
+    ok3 = P(a16, a16, a16)
+
+    def call(count, packed=ok3, scale=ok3, zero=ok3, bias=None, n=N(64, 32, 16), k=256, g=32,
+             prepared=0, ydt=1, y=ok3, m=1):
+        return woq.STATUS[lib.woq_linear_int4_groups_grouped(a16, m, count, packed, scale, zero, bias, n, k,
+                                                             g, prepared, ydt, y, None, 0, None)]
+
+    assert call(0) == "WOQ_EINVAL" and call(5) == "WOQ_EINVAL"
+    assert call(3, packed=None) == "WOQ_EINVAL" and call(3, n=None) == "WOQ_EINVAL"
+    assert call(3, prepared=2) == "WOQ_EINVAL" and call(3, ydt=7) == "WOQ_EINVAL"
+    assert call(3, y=P(a16, None, a16)) == "WOQ_EINVAL"            # one output missing
+    assert call(3, zero=P(a16, a16, odd)) == "WOQ_EALIGN"         # checked for the last matrix too
+    assert call(3, n=N(64, -1, 16)) == "WOQ_EINVAL"
+    assert call(2, g=48) == "WOQ_EGROUP"
+    assert call(3, m=0) == "WOQ_OK"                                # nothing to do
+    assert call(2, n=N(0, 0)) == "WOQ_OK"
+
+
 def test_empty_calls_are_noops(lib):
     assert lib.woq_linear_int4_groups(None, 0, None, None, None, None, None, 64, 256, 32, 1,
                                       None, None, 0, None) == 0

@@ -31,6 +31,7 @@ __all__ = [
     "dequantize_int4_groups",
     "linear_int4_groups",
     "linear_int4_groups_prepared",
+    "linear_int4_groups_grouped",
     "prepare_int4",
     "unprepare_int4",
     "prepared_bytes",
@@ -88,6 +89,8 @@ def load() -> ctypes.CDLL:
         "woq_unprepare_int4": (c_i32, [c_p, c_i64, c_i64, c_p, c_p]),
         "woq_linear_int4_groups_prepared": (c_i32, [c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_i64, c_i64,
                                                     c_i32, c_i32, c_p, c_p, c_sz, c_p]),
+        "woq_linear_int4_groups_grouped": (c_i32, [c_p, c_i64, c_i32, c_p, c_p, c_p, c_p, c_p, c_i64,
+                                                   c_i32, c_i32, c_i32, c_p, c_p, c_sz, c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -216,7 +219,7 @@ def prepare_int4(packed: torch.Tensor, k: Optional[int] = None) -> torch.Tensor:
     lib = load()
     _need(packed, torch.uint8, "packed")
     n = packed.shape[0]
-    kk = 2 * (packed.numel() // n) if n else 0
+    kk = 2 * (packed.numel() // n) if n else (k or 0)
     k = kk if k is None else k
     if k != kk:
         raise ValueError(f"packed holds {kk} inputs per row, not {k}")
@@ -308,3 +311,60 @@ def _linear(x, weights, scale, zero, bias, order, n, k, group, out_dtype, out, w
               _ptr(workspace) if need else None, wsb, _stream()),
            "linear_int4_groups_prepared" if prepared else "linear_int4_groups")
     return out
+
+
+def linear_int4_groups_grouped(x: torch.Tensor, mats, prepared: bool = False,
+                               out_dtype: torch.dtype = torch.bfloat16, outs=None,
+                               workspace: Optional[torch.Tensor] = None):
+    """Several linears over the same activations in one call.
+
+    mats: 1..4 tuples (weights, scale, zero, bias or None), weights being packed
+    rows [N_i, K/2] (or the prepared buffer when ``prepared``); all share x
+    [M, K] and the group size.  Returns the list of y_i [M, N_i].  At M <= 4 the
+    matrices share one kernel launch.  Asynchronous on the current stream.
+    """
+    lib = load()
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    if not 1 <= len(mats) <= 4:
+        raise ValueError("between 1 and 4 matrices")
+    m, k = x.shape
+    group = None
+    ns = []
+    for i, (w, sc, z, b) in enumerate(mats):
+        _need(w, torch.uint8, f"weights[{i}]")
+        _need(sc, torch.float32, f"scale[{i}]")
+        _need(z, torch.uint8, f"zero[{i}]")
+        if b is not None:
+            _need(b, torch.float32, f"bias[{i}]")
+        if sc.dim() != 2 or sc.shape[1] == 0:
+            raise ValueError("scale must be [N, K/G]")
+        g = k // sc.shape[1]
+        if group is not None and g != group:
+            raise ValueError("all matrices must share the group size")
+        group = g
+        ns.append(sc.shape[0])
+        need = prepared_bytes(sc.shape[0], k) if prepared else sc.shape[0] * k // 2
+        if w.numel() < need:
+            raise ValueError(f"weights[{i}] hold fewer bytes than an [{sc.shape[0]}, {k}] weight")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    if outs is None:
+        outs = [torch.empty((m, n), dtype=out_dtype, device=x.device) for n in ns]
+    else:
+        for i, o in enumerate(outs):
+            _need(o, out_dtype, f"outs[{i}]")
+    need = max(int(lib.woq_linear_workspace_bytes(m, n, k, group, 0)) for n in ns)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    cnt = len(mats)
+    arr = lambda vals: (ctypes.c_void_p * cnt)(*vals)
+    _check(lib.woq_linear_int4_groups_grouped(
+        _ptr(x), m, cnt, arr([_ptr(w) for w, _, _, _ in mats]), arr([_ptr(sc) for _, sc, _, _ in mats]),
+        arr([_ptr(z) for _, _, z, _ in mats]), arr([_ptr(b) for _, _, _, b in mats]),
+        (ctypes.c_int64 * cnt)(*ns), k, group, int(bool(prepared)),
+        F32 if out_dtype == torch.float32 else BF16, arr([_ptr(o) for o in outs]),
+        _ptr(workspace) if need else None, workspace.numel() if need else 0, _stream()),
+        "linear_int4_groups_grouped")
+    return outs

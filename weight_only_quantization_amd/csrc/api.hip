@@ -364,6 +364,67 @@ int32_t woq_linear_int4_groups_prepared(const void* x_bf16, int64_t m, const uin
                      workspace, workspace_bytes, stream, 1);
 }
 
+int32_t woq_linear_int4_groups_grouped(const void* x_bf16, int64_t m, int32_t count,
+                                       const uint8_t* const* packed, const float* const* scale,
+                                       const uint8_t* const* zero, const float* const* bias,
+                                       const int64_t* n, int64_t k, int32_t group,
+                                       int32_t prepared, int32_t y_dtype, void* const* y,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (count < 1 || count > kMaxGrouped || !packed || !scale || !zero || !n || !y) return WOQ_EINVAL;
+  if (prepared != 0 && prepared != 1) return WOQ_EINVAL;
+  if (y_dtype != WOQ_F32 && y_dtype != WOQ_BF16) return WOQ_EINVAL;
+  // Every matrix is validated as the single call would before anything is enqueued.
+  int64_t rows16 = 0;
+  for (int i = 0; i < count; ++i) {
+    const int32_t st = check_linear_shape(m, n[i], k, group);
+    if (st != WOQ_OK) return st;
+    if (m == 0 || n[i] == 0 || k == 0) continue;
+    if (!x_bf16 || !packed[i] || !scale[i] || !zero[i] || !y[i]) return WOQ_EINVAL;
+    if (!aligned(y[i], y_dtype == WOQ_F32 ? 4 : 2)) return WOQ_EALIGN;
+    if (bias && bias[i] && !aligned(bias[i], 4)) return WOQ_EALIGN;
+    if (!aligned(x_bf16, 16) || !aligned(packed[i], 16) || !aligned(scale[i], 16) || !aligned(zero[i], 16))
+      return WOQ_EALIGN;
+    rows16 += (n[i] + 15) / 16 * 16;
+  }
+  if (m == 0) return WOQ_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  LinearPlan plan;
+  if (k > 0 && m <= 4 && rows16 > 0 && rows16 < kMaxDim && k < ((int64_t)1 << 26) &&
+      std::getenv("WOQ_FORCE_SKINNY") == nullptr && gemv_plan(m, rows16, k, group, &plan)) {
+    // one decode launch over all the matrices
+    LinearArgs args[kMaxGrouped];
+    int used = 0;
+    for (int i = 0; i < count; ++i) {
+      if (n[i] == 0) continue;
+      LinearArgs& a = args[used++];
+      a = LinearArgs{};
+      a.x = static_cast<const uint16_t*>(x_bf16);
+      a.packed = packed[i];
+      a.scale = scale[i];
+      a.zero = zero[i];
+      a.bias = bias ? bias[i] : nullptr;
+      a.y = y[i];
+      a.m = (int32_t)m;
+      a.n = (int32_t)n[i];
+      a.k = (int32_t)k;
+      a.group = group;
+      a.y_bf16 = y_dtype == WOQ_BF16;
+      a.kpad = a.k;
+      a.prepared = prepared;
+    }
+    plan.gb = group >= 128 ? 4 : group / 32;
+    return used ? launch_gemv_grouped(args, used, plan, s) : WOQ_OK;
+  }
+  // otherwise one call per matrix, in order, sharing the workspace
+  for (int i = 0; i < count; ++i) {
+    const int32_t st = linear_impl(x_bf16, m, packed[i], scale[i], zero[i], bias ? bias[i] : nullptr,
+                                   nullptr, n[i], k, group, y_dtype, y[i], workspace, workspace_bytes,
+                                   stream, prepared);
+    if (st != WOQ_OK) return st;
+  }
+  return WOQ_OK;
+}
+
 size_t woq_prepared_bytes(int64_t n, int64_t k) {
   if (n < 0 || k < 0 || k % 32 || n >= kMaxDim || k >= kMaxDim) return 0;
   return (size_t)prepared_bytes(n, k);

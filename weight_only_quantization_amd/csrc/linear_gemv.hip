@@ -40,14 +40,22 @@ constexpr int kSzPerBatch = 16;    // (scale, zero) entries per row staged by on
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-struct GemvParams {
-  const uint16_t* x;
+// One weight matrix of a launch.  A launch serves up to kMaxGrouped matrices
+// that share the activations (and so K and the group size): workgroups
+// [tile_begin, next tile_begin) take the 16-row tiles of matrix i.
+struct GemvProblem {
   const uint8_t* packed;
   const float* scale;
   const uint8_t* zero;
   const float* bias;
   void* y;
-  int32_t m, n, k, y_bf16;
+  int32_t n;
+  int32_t tile_begin;
+};
+
+struct GemvParams {
+  const uint16_t* x;
+  int32_t m, k, y_bf16;
   int32_t nsteps;       // 128-input steps covering k
   int32_t cnt;          // steps owned by each wave, a multiple of 4
   int32_t ngroups;      // groups per row
@@ -62,6 +70,8 @@ struct GemvParams {
   // The nibble mask and the bf16 offset pattern arrive as arguments so they sit
   // in registers: one v_and_or_b32 per pair then expands two codes.
   uint32_t nib_mask, nib_offset;
+  int32_t nprob;
+  GemvProblem prob[kMaxGrouped];
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
@@ -124,10 +134,17 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4;
   const int c = lane & 15;
-  const int M = p.m, N = p.n, K = p.k;
+  // this workgroup's matrix (uniform)
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGrouped; ++i)
+    if (i < p.nprob && (int)blockIdx.x >= p.prob[i].tile_begin) pi = i;
+  const GemvProblem& pr = p.prob[pi];
+  const int tile = (int)blockIdx.x - pr.tile_begin;
+  const int M = p.m, N = pr.n, K = p.k;
   const int cnt = p.cnt;
   const uint32_t row_bytes = (uint32_t)K / 2;
-  const int row0 = blockIdx.x * 16;
+  const int row0 = tile * 16;
   const int rows = min(16, N - row0);
   const int s0 = wave * cnt;                       // first step of this wave
   const int live = min(cnt, p.nsteps - s0);        // <= 0 for a wave past K
@@ -138,10 +155,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   // of a step, so a step is one contiguous kilobyte.
   const bool prep = p.prepared != 0;   // uniform
   const __amdgpu_buffer_rsrc_t rb =
-      prep ? rsrc(p.packed + (int64_t)blockIdx.x * p.nsteps * 1024, (uint32_t)p.nsteps * 1024u)
-           : rsrc(p.packed + (int64_t)row0 * row_bytes, (uint32_t)rows * row_bytes);
-  const __amdgpu_buffer_rsrc_t rs = rsrc(p.scale + (int64_t)row0 * p.ngroups, (uint32_t)(rows * p.ngroups) * 4u);
-  const __amdgpu_buffer_rsrc_t rz = rsrc(p.zero + (int64_t)row0 * p.ngroups, (uint32_t)(rows * p.ngroups));
+      prep ? rsrc(pr.packed + (int64_t)tile * p.nsteps * 1024, (uint32_t)p.nsteps * 1024u)
+           : rsrc(pr.packed + (int64_t)row0 * row_bytes, (uint32_t)rows * row_bytes);
+  const __amdgpu_buffer_rsrc_t rs = rsrc(pr.scale + (int64_t)row0 * p.ngroups, (uint32_t)(rows * p.ngroups) * 4u);
+  const __amdgpu_buffer_rsrc_t rz = rsrc(pr.zero + (int64_t)row0 * p.ngroups, (uint32_t)(rows * p.ngroups));
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.x, (uint32_t)M * (uint32_t)K * 2u);
 
   // ---- staging loads: activations, then scales and zero points -----------------
@@ -311,15 +328,15 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   const int n = row0 + c;
   auto store = [&](const f32x4_t& v) {
     if (lane < 16 && n < N) {
-      const float bv = p.bias ? p.bias[n] : 0.f;
+      const float bv = pr.bias ? pr.bias[n] : 0.f;
 #pragma unroll
       for (int r = 0; r < FR; ++r) {
         if (r < M) {
           const float o = v[r] + bv;
           if (p.y_bf16)
-            reinterpret_cast<uint16_t*>(p.y)[(int64_t)r * N + n] = f32_to_bf16_bits(o);
+            reinterpret_cast<uint16_t*>(pr.y)[(int64_t)r * N + n] = f32_to_bf16_bits(o);
           else
-            reinterpret_cast<float*>(p.y)[(int64_t)r * N + n] = o;
+            reinterpret_cast<float*>(pr.y)[(int64_t)r * N + n] = o;
         }
       }
     }
@@ -401,7 +418,9 @@ GemvLayout gemv_layout(int64_t m, int64_t k, int64_t group, int waves, int cnt) 
   return l;
 }
 
-int32_t launch_gemv(const LinearArgs& a, const LinearPlan& pl, hipStream_t stream) {
+int32_t launch_gemv_grouped(const LinearArgs* args, int count, const LinearPlan& pl,
+                            hipStream_t stream) {
+  const LinearArgs& a = args[0];
   int32_t gshift = 0;
   while ((1 << gshift) < a.group) ++gshift;
   const GemvLayout l = gemv_layout(a.m, a.k, a.group, pl.waves, pl.cnt);
@@ -410,11 +429,23 @@ int32_t launch_gemv(const LinearArgs& a, const LinearPlan& pl, hipStream_t strea
   const int cc = gemv_cnt_class(pl.cnt);
   const int32_t xl = pl.fold_rows == 1 ? cc / 4 : 4;
   const int32_t loads = (a.m * pl.cnt / 4 + xl - 1) / xl;
-  GemvParams gp{a.x, a.packed, a.scale, a.zero, a.bias, a.y, a.m, a.n, a.k, a.y_bf16,
-                nsteps, pl.cnt, ngroups, gshift, loads, ngroups % 4 != 0 ? 1 : 0, a.prepared,
-                l.wave_lds, l.xs_off, l.sz_off, l.red_off, kNibPairMask, kBf16Offset2};
-  return pl.fold_rows == 1 ? dispatch_gb<1>(gp, pl, l.total, stream)
-                           : dispatch_gb<4>(gp, pl, l.total, stream);
+  GemvParams gp{a.x, a.m, a.k, a.y_bf16, nsteps, pl.cnt, ngroups, gshift, loads,
+                ngroups % 4 != 0 ? 1 : 0, a.prepared, l.wave_lds, l.xs_off, l.sz_off, l.red_off,
+                kNibPairMask, kBf16Offset2, count, {}};
+  int32_t tb = 0;
+  for (int i = 0; i < count; ++i) {
+    gp.prob[i] = GemvProblem{args[i].packed, args[i].scale, args[i].zero, args[i].bias, args[i].y,
+                             args[i].n, tb};
+    tb += (args[i].n + 15) / 16;
+  }
+  LinearPlan p2 = pl;
+  p2.grid = tb;
+  return pl.fold_rows == 1 ? dispatch_gb<1>(gp, p2, l.total, stream)
+                           : dispatch_gb<4>(gp, p2, l.total, stream);
+}
+
+int32_t launch_gemv(const LinearArgs& a, const LinearPlan& pl, hipStream_t stream) {
+  return launch_gemv_grouped(&a, 1, pl, stream);
 }
 
 }  // namespace woq

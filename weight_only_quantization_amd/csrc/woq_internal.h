@@ -101,6 +101,11 @@ struct GemvLayout {
 GemvLayout gemv_layout(int64_t m, int64_t k, int64_t group, int waves, int cnt);
 int gemv_cnt_class(int cnt);   // the kernel variant serving `cnt` steps per wave (4, 8, 16; 0: none)
 int32_t launch_gemv(const LinearArgs& a, const LinearPlan& p, hipStream_t stream);
+// Up to kMaxGrouped matrices with the same m, k, group, layout and activations in
+// one decode launch; `p` is the plan for their summed row count.
+constexpr int kMaxGrouped = 4;
+int32_t launch_gemv_grouped(const LinearArgs* args, int count, const LinearPlan& p,
+                            hipStream_t stream);
 // Small-M path: LDS of one workgroup of `waves` waves, `tiles` 16-row weight
 // tiles and `cnt` steps per wave (per-wave (scale, zero) staging, then the
 // cross-wave reduction area).
