@@ -14,8 +14,10 @@ Printed JSON line (rank 0):
   roofline     the decode kernel alone (gemv_kernel, every launch of the step):
                algorithmic bytes per launch / its average launch duration
                (HIP events around the replayed step graph)
+  grouped      the same step with q/k/v and gate/up each run as one grouped
+               call (woq_linear_int4_groups_grouped: one launch per group)
   prepared     the same step over prepared (fragment-ordered) weights, made
-               once before timing by woq_prepare_int4
+               once before timing by woq_prepare_int4 (also grouped)
   prefill      TFLOP/s of the M=2048 GEMM path on both prefill shapes
   cpu_baseline the CPU oracle's linear on a bounded sample of the same layer
 """
@@ -106,6 +108,26 @@ def run_calls(woq, calls):
     for c in calls:
         woq.linear_int4_groups(c["x"], c["packed"], c["scale"], c["zero"], bias=c["bias"],
                                group=GROUP, out=c["y"], out_dtype=c["y"].dtype)
+
+
+def grouped_plan(calls, layers: int):
+    """The decode step with the projections that share an input in one call:
+    per layer (q, k, v) on q's activations, o, (gate, up) on gate's, down."""
+    per = len(calls) // layers
+    groups = []
+    for layer in range(layers):
+        c = calls[layer * per:(layer + 1) * per]
+        roles = {cc["role"]: cc for cc in c}
+        for names in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+            groups.append([roles[nm] for nm in names])
+    return groups
+
+
+def run_groups(woq, groups, prepared: bool = False):
+    key = "prepared" if prepared else "packed"
+    for g in groups:
+        woq.linear_int4_groups_grouped(g[0]["x"], [(c[key], c["scale"], c["zero"], c["bias"]) for c in g],
+                                       prepared=prepared, out_dtype=g[0]["y"].dtype, outs=[c["y"] for c in g])
 
 
 def run_calls_prepared(woq, calls):
@@ -467,6 +489,21 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # The same step with the projections that share their input grouped into one
+    # call each (q, k, v; gate, up): one decode launch per group.
+    groups = grouped_plan(calls, args.layers)
+    el_g = time_step(torch, lambda: run_groups(woq, groups), args.steps, args.warmup, not args.no_graph)
+    avg_g = el_g / (args.steps * len(groups))
+    grouped = dict(
+        metric="effective weight GB/s at M=1, projections sharing an input grouped (same linears, same bytes)",
+        value=round(wbytes * args.steps / el_g / 1e9, 1), unit="GB/s",
+        ms_per_step=round(el_g / args.steps * 1e3, 4), launches_per_step=len(groups),
+        hbm_peak_frac=round(wbytes * args.steps / el_g / 1e9 / HBM_PEAK_GBS, 4),
+        avg_launch_us=round(avg_g * 1e6, 3),
+        roofline_achieved=round(sum(abytes) / len(groups) / avg_g / 1e9, 1),
+        roofline_frac=round(sum(abytes) / len(groups) / avg_g / 1e9 / HBM_PEAK_GBS, 4),
+        note="woq_linear_int4_groups_grouped: per layer (q,k,v) and (gate,up) share one launch each")
+
     prepared = None
     if not args.no_prepared:
         for c in calls:
@@ -476,8 +513,12 @@ def main():
                          not args.no_graph)
         val_p = wbytes * args.steps / el_p / 1e9
         avg_p = el_p / (args.steps * len(calls))
+        el_pg = time_step(torch, lambda: run_groups(woq, groups, prepared=True), args.steps, args.warmup,
+                          not args.no_graph)
         prepared = dict(
             metric="effective weight GB/s at M=1 over prepared weights (same step, same bytes)",
+            grouped_value=round(wbytes * args.steps / el_pg / 1e9, 1),
+            grouped_ms_per_step=round(el_pg / args.steps * 1e3, 4),
             value=round(val_p, 1), unit="GB/s", ms_per_step=round(el_p / args.steps * 1e3, 4),
             hbm_peak_frac=round(val_p / HBM_PEAK_GBS, 4), avg_launch_us=round(avg_p * 1e6, 3),
             roofline_achieved=round(sum(abytes) / len(abytes) / avg_p / 1e9, 1),
@@ -500,7 +541,8 @@ def main():
                     weight_bytes_per_step=wbytes, hbm_peak_frac=round(value / HBM_PEAK_GBS, 4),
                     graph=not args.no_graph, accumulate="f32",
                     tokens_per_s_linears_only=round(1.0 / (ms_per_step * 1e-3), 1) if args.layers == 32 else None),
-        roofline=roofline, prepared=prepared, prefill=prefill, configs=configs, cpu_baseline=cpu,
+        roofline=roofline, grouped=grouped, prepared=prepared, prefill=prefill, configs=configs,
+        cpu_baseline=cpu,
     )
     print(json.dumps(line), flush=True)
 
