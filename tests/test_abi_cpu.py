@@ -58,6 +58,23 @@ def test_plan_paths(m, n, k, g, path):
     assert f"path={path}" in woq.linear_plan(m, n, k, g)
 
 
+@pytest.mark.parametrize("m,n,tail", [
+    (2048, 14336, 2048),    # 896 tiles: the 128 of the last round become 256 tiles of 64 rows
+    (2048, 4096, 0),        # 256 tiles: one full round
+    (1024, 14336, 0),       # 448 tiles: the last round is 3/4 full
+    (200, 33064, 296),      # ragged rows and columns: 2 trailing tile columns
+    (129, 256, 0),          # one tile
+])
+def test_plan_tail_split(m, n, tail):
+    plan = woq.linear_plan(m, n, 256, 128)
+    fields = dict(f.split("=", 1) for f in plan.split())
+    assert fields["path"] == "gemm_mfma" and fields["tile"] == "128x256"
+    assert int(fields["tail_cols"]) == tail
+    tm, tn = -(-m // 128), -(-n // 256)
+    cols = -(-tail // 256)
+    assert int(fields["grid"]) == tm * (tn - cols) + (-(-m // 64)) * cols
+
+
 def test_plan_mentions_gather_for_act_order():
     assert "gather" in woq.linear_plan(1, 8192, 28672, 128, has_order=True)
 

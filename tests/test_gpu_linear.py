@@ -74,6 +74,7 @@ SMALL = [
     (128, 256, 1024, 32, False, False),
     (129, 130, 256, 128, True, False),
     (256, 512, 4096, 128, False, True),
+    (200, 33064, 256, 128, True, False),  # the last tile columns in a second launch of 64-row tiles
 ]
 
 

@@ -147,7 +147,23 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
     p.bm = 32; p.bn = 64; p.waves = 2;
   }
   p.mpad = ((m + 127) / 128) * 128;
-  p.grid = ((m + p.bm - 1) / p.bm) * ((n + p.bn - 1) / p.bn);
+  const int64_t tm = (m + p.bm - 1) / p.bm, tn = (n + p.bn - 1) / p.bn;
+  p.grid = tm * tn;
+  if (p.bn == 256) {
+    // 128 x 256 tiles run one workgroup per compute unit.  When the last round
+    // would be at most half full, the trailing tile columns that hold it go to
+    // a second launch as 64-row tiles (half the work each, twice as many), so
+    // that round takes about half as long.
+    const int64_t rem = p.grid % kComputeUnits;
+    if (p.grid > kComputeUnits && rem != 0 && 2 * rem <= kComputeUnits) {
+      const int64_t cols = (rem + tm - 1) / tm;
+      const int64_t tail_tiles = ((m + 63) / 64) * cols;
+      if (cols < tn && tail_tiles <= kComputeUnits) {
+        p.tail_n = n - (tn - cols) * 256;
+        p.grid = tm * (tn - cols) + tail_tiles;
+      }
+    }
+  }
   return p;
 }
 
@@ -476,8 +492,9 @@ int32_t woq_linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, int32_t 
       break;
     default:
       std::snprintf(buf, len,
-                    "path=gemm_mfma tile=%dx%d waves=%d group_blocks=%d grid=%lld prep=%s workspace=%zu",
-                    p.bm, p.bn, p.waves, p.gb, (long long)p.grid,
+                    "path=gemm_mfma tile=%dx%d waves=%d group_blocks=%d tail_cols=%lld grid=%lld prep=%s "
+                    "workspace=%zu",
+                    p.bm, p.bn, p.waves, p.gb, (long long)p.tail_n, (long long)p.grid,
                     has_order ? "gather+reorder+groupsum" : "reorder+groupsum", ws);
   }
   return WOQ_OK;

@@ -176,7 +176,9 @@ struct GemmParams {
   int64_t mpad;
   int32_t npad, ngroups, npieces;
   int32_t tiles_m, tiles_n;
+  int32_t n_base, n_cols; // this launch computes output columns [n_base, n_base + n_cols)
   int32_t prepared;       // 1: packed holds prepared 1 KB blocks
+  int32_t vec_out;        // 1: y is 16-byte aligned and its rows are whole 16-byte chunks
 };
 
 // Tl: workgroup tile; GB: 32-input blocks per group piece inside a step (1, 2
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
   const int full = (nwg / 8) * 8;
   if (bid < full) bid = (bid % 8) * (full / 8) + bid / 8;
   const int tm = bid % p.tiles_m, tn = bid / p.tiles_m;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BM, n0 = p.n_base + tn * BN;
   const int nsteps = (K + kStepK - 1) / kStepK;
 
   const __amdgpu_buffer_rsrc_t ra =
@@ -302,6 +304,11 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
 
   // zero-point operands carried from an even step to the next (one piece per step)
   float zpa[MT] = {}, zpb[NT] = {};
+  // MFMA sums of the current group piece, and the fold of the last finished
+  // piece still to be added (its scales)
+  f32x16_t cg[MT][NT];
+  float fold_sv[NT] = {};
+  bool fold_pending = false;
 
   auto compute = [&](int slot, int step) {
     const unsigned char* st = lds + slot * kStage;
@@ -386,21 +393,15 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
         af[mt] = *reinterpret_cast<const bf16x8_t*>(st + row * 256 + 16 * c);
       }
     };
-    // Fold of one group piece: acc += scale * sum (the zero-point part is
-    // added by correct()).
-    f32x16_t cg[MT][NT];
-    auto fold = [&](int pc) {
-      if (k0 + pc * kPiece >= K) return;     // a piece past the end of the inputs
-      float sv[NT];
+    // Fold of one group piece, acc += scale * sum (the zero-point part is added
+    // by correct()), deferred to the first block of the next piece: there the
+    // fold of each 32x32 tile sits right before that tile's first MFMA of the
+    // new piece, so the matrix unit works on one tile while the vector unit
+    // folds the next.  The scales of a finished piece are read at its end (the
+    // stage may be refilled before the next piece starts).
+    auto fold_tile = [&](int mt, int nt) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        sv[nt] = *reinterpret_cast<const float*>(st + kSzOff + pc * kSzStride + brow[nt] * 8);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[mt][nt][r] = fmaf(sv[nt], cg[mt][nt][r], acc[mt][nt][r]);
+      for (int r = 0; r < 16; ++r) acc[mt][nt][r] = fmaf(fold_sv[nt], cg[mt][nt][r], acc[mt][nt][r]);
     };
     bf16x8_t afc[MT], afn[MT];
     // The two waves of a SIMD leave the barrier together; raising this wave's
@@ -413,14 +414,25 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
       const int L = blk >> 2, b = blk & 3;
       constexpr int kBlocksPerPiece = 8 / NP;
       const bool first = blk % kBlocksPerPiece == 0;      // a new piece starts
+      const bool folding = first && fold_pending;          // uniform
       if (blk + 1 < 8) load_af(blk + 1, afn);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const bf16x8_t bf = unpack_codes(bd[L][nt][b], kNibPairMask, nib_offset);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) cg[mt][nt] = mfma32(afc[mt], bf, first ? zero16 : cg[mt][nt]);
+        for (int mt = 0; mt < MT; ++mt) {
+          if (folding) fold_tile(mt, nt);
+          cg[mt][nt] = mfma32(afc[mt], bf, first ? zero16 : cg[mt][nt]);
+        }
       }
-      if (blk % kBlocksPerPiece == kBlocksPerPiece - 1) fold(blk / kBlocksPerPiece);
+      if (blk % kBlocksPerPiece == kBlocksPerPiece - 1) {
+        // this piece's fold is pending (pieces past the end of the inputs add nothing)
+        const int pc = blk / kBlocksPerPiece;
+        fold_pending = k0 + pc * kPiece < K;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          fold_sv[nt] = *reinterpret_cast<const float*>(st + kSzOff + pc * kSzStride + brow[nt] * 8);
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) afc[mt] = afn[mt];
     }
@@ -447,6 +459,14 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
     slot = slot == S - 1 ? 0 : slot + 1;
   }
   __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+  if (fold_pending) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mt][nt][r] = fmaf(fold_sv[nt], cg[mt][nt][r], acc[mt][nt][r]);
+  }
   if constexpr (4 / GB == 1) {
     if (nsteps & 1) {   // the last (even) step's zero-point term is still pending
 #pragma unroll
@@ -458,6 +478,54 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
     }
   }
 
+  // Epilogue.  A lane of a 32 x 32 MFMA tile holds 16 rows of one column, so
+  // storing straight from the accumulators writes 2 bytes (or 4) per lane.
+  // Where the tile fits in the LDS ring (free once every wave is past its
+  // last step) it is staged there row-major and leaves in 16-byte chunks.
+  constexpr int kEsz = 4;                                  // bytes per staged float32
+  constexpr int kOutStride = BN * kEsz + 32;               // padded row: the lane halves' rows 4 apart hit other banks
+  constexpr bool kStaged = BM * kOutStride <= S * kStage;
+  if (kStaged && p.vec_out) {
+    __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int n = n0 + brow[nt];
+        const float b = p.bias && n < N ? p.bias[n] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * MT * wm + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+          *reinterpret_cast<float*>(lds + row * kOutStride + brow[nt] * kEsz) = acc[mt][nt][r] + b;
+        }
+      }
+    __syncthreads();
+    // 16-byte output chunks: 8 bf16 or 4 float32 columns; N is a whole number
+    // of chunks, so a chunk is wholly inside or wholly past the last column.
+    const int ecols = p.y_bf16 ? 8 : 4;
+    const int cpr = BN / ecols;
+    for (int c = tid; c < BM * cpr; c += 64 * kWaves) {
+      const int row = c / cpr, col = (c - row * cpr) * ecols;
+      const int m = m0 + row, n = n0 + col;
+      if (m >= M || n >= N) continue;
+      const float* src = reinterpret_cast<const float*>(lds + row * kOutStride + col * kEsz);
+      if (p.y_bf16) {
+        const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(src);
+        const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(src + 4);
+        u32x4_t o;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          o[e] = (uint32_t)f32_to_bf16_bits(lo[2 * e]) | ((uint32_t)f32_to_bf16_bits(lo[2 * e + 1]) << 16);
+          o[e + 2] = (uint32_t)f32_to_bf16_bits(hi[2 * e]) | ((uint32_t)f32_to_bf16_bits(hi[2 * e + 1]) << 16);
+        }
+        *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(p.y) + (int64_t)m * N + n) = o;
+      } else {
+        *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.y) + (int64_t)m * N + n) =
+            *reinterpret_cast<const f32x4_t*>(src);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -497,7 +565,7 @@ int32_t launch_gemm_t(GemmParams gp, hipStream_t stream) {
     raised = true;
   }
   gp.tiles_m = (gp.m + Tl::BM - 1) / Tl::BM;
-  gp.tiles_n = (gp.n + Tl::BN - 1) / Tl::BN;
+  gp.tiles_n = (gp.n_cols + Tl::BN - 1) / Tl::BN;
   hipLaunchKernelGGL(kern, dim3((unsigned)(gp.tiles_m * gp.tiles_n)), dim3(64 * Tl::kWaves), lds,
                      stream, gp);
   return hip_status(hipGetLastError());
@@ -573,7 +641,8 @@ int32_t launch_gemm(const LinearArgs& a, const LinearPlan& pl, void* sz_ws, hipS
   const int32_t piece = a.group < kStepK ? a.group : kStepK;
   const GemmParams gp{a.x, a.packed, a.xs, static_cast<const f32x2_t*>(sz_ws), a.bias, a.y,
                       a.m, a.n, a.k, a.kpad, a.group, a.y_bf16, a.mpad, npad, ngroups, a.k / piece,
-                      0, 0, a.prepared};
+                      0, 0, 0, a.n, a.prepared,
+                      (reinterpret_cast<uintptr_t>(a.y) % 16 == 0 && a.n % (a.y_bf16 ? 8 : 4) == 0) ? 1 : 0};
   // Tile by the number of activation rows: small M takes narrow tiles so the
   // grid still covers the chip.
   switch (pl.bm) {
@@ -581,6 +650,16 @@ int32_t launch_gemm(const LinearArgs& a, const LinearPlan& pl, void* sz_ws, hipS
     case 64: return launch_gemm_gb<Tile<2, 2, 1, 1>>(gp, pl.gb, stream);    // 64 x 64
     case 128:
       if (pl.bn == 64) return launch_gemm_gb<Tile<2, 2, 2, 1>>(gp, pl.gb, stream);   // 128 x 64
+      if (pl.tail_n > 0) {
+        // columns before the tail in 128 x 256 tiles, the tail in 64 x 256
+        GemmParams head = gp, tail = gp;
+        head.n_cols = (int32_t)(a.n - pl.tail_n);
+        tail.n_base = head.n_cols;
+        tail.n_cols = (int32_t)pl.tail_n;
+        const int32_t st = launch_gemm_gb<Tile<2, 4, 2, 2>>(head, pl.gb, stream);
+        if (st != WOQ_OK) return st;
+        return launch_gemm_gb<Tile<2, 4, 1, 2>>(tail, pl.gb, stream);                // 64 x 256
+      }
       return launch_gemm_gb<Tile<2, 4, 2, 2>>(gp, pl.gb, stream);                    // 128 x 256
     default: return WOQ_EUNSUPPORTED;
   }

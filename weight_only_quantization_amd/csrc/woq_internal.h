@@ -46,7 +46,13 @@ struct LinearPlan {
   int bm = 0, bn = 0;    // tile of the GEMM path
   int64_t mpad = 0;      // rows of the per-group sum table (GEMM path)
   int cnt = 0;           // 128-input steps per wave (decode and small-M paths)
+  int64_t tail_n = 0;    // GEMM path: trailing output columns left to a second launch of
+                         // 64-row tiles, so that the last round of workgroups is not half empty
 };
+
+// Compute units of one MI355X (gfx950): the GEMM path sizes its grid in rounds of this many
+// workgroups (one workgroup per compute unit at a time).
+constexpr int64_t kComputeUnits = 256;
 
 LinearWorkspace linear_workspace_layout(int64_t m, int64_t n, int64_t k, int32_t group,
                                         bool has_order);
