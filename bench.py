@@ -166,7 +166,9 @@ def time_step(torch, run, steps: int, warmup: int, use_graph: bool):
     return elapsed
 
 
-def measure_prefill(torch, woq, reps: int = 5):
+def measure_prefill(torch, woq, reps: int = 5, calls: int = 20):
+    """Per-call time of each prefill shape: `calls` back-to-back launches (pre-pass
+    included) between two events, median of `reps` repetitions, after warm-up."""
     from workloads import PREFILL
 
     dev = torch.device("cuda")
@@ -182,18 +184,18 @@ def measure_prefill(torch, woq, reps: int = 5):
         y = torch.empty((case.m, case.n), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(woq.linear_workspace_bytes(case.m, case.n, case.k, case.group, False),
                          dtype=torch.uint8, device=dev)
-        for _ in range(2):
+        for _ in range(5):
             woq.linear_int4_groups(x, packed, s, z, group=case.group, out=y, workspace=ws)
         torch.cuda.synchronize()
         times = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda._sleep(int(2.4e9 * 0.002))
             e0.record()
-            woq.linear_int4_groups(x, packed, s, z, group=case.group, out=y, workspace=ws)
+            for _ in range(calls):
+                woq.linear_int4_groups(x, packed, s, z, group=case.group, out=y, workspace=ws)
             e1.record()
             torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1) * 1e-3)
+            times.append(e0.elapsed_time(e1) * 1e-3 / calls)
         t = statistics.median(times)
         flops = 2.0 * case.m * case.n * case.k
         out.append(dict(shape=f"{case.m}x{case.n}x{case.k}", ms=round(t * 1e3, 4),
@@ -201,7 +203,7 @@ def measure_prefill(torch, woq, reps: int = 5):
     tot_flops = sum(2.0 * c.m * c.n * c.k for c in PREFILL)
     tot_t = sum(o["ms"] for o in out) * 1e-3
     tf = tot_flops / tot_t / 1e12
-    return dict(metric="TFLOP/s at M=2048 (both prefill shapes, pre-pass included)",
+    return dict(metric="TFLOP/s at M=2048 (both prefill shapes, pre-pass included, back-to-back calls)",
                 value=round(tf, 1), peak=BF16_PEAK_TFLOPS, frac=round(tf / BF16_PEAK_TFLOPS, 4),
                 per_shape=out, plan=woq.linear_plan(2048, 14336, 4096, GROUP))
 
@@ -428,6 +430,7 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the small-M sweep and act-order per-launch timings")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
+    ap.add_argument("--no-grouped", action="store_true", help="skip the grouped-call step")
     ap.add_argument("--no-prepared", action="store_true",
                     help="skip the decode step over prepared weights")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -492,17 +495,19 @@ def main():
     # The same step with the projections that share their input grouped into one
     # call each (q, k, v; gate, up): one decode launch per group.
     groups = grouped_plan(calls, args.layers)
-    el_g = time_step(torch, lambda: run_groups(woq, groups), args.steps, args.warmup, not args.no_graph)
-    avg_g = el_g / (args.steps * len(groups))
-    grouped = dict(
-        metric="effective weight GB/s at M=1, projections sharing an input grouped (same linears, same bytes)",
-        value=round(wbytes * args.steps / el_g / 1e9, 1), unit="GB/s",
-        ms_per_step=round(el_g / args.steps * 1e3, 4), launches_per_step=len(groups),
-        hbm_peak_frac=round(wbytes * args.steps / el_g / 1e9 / HBM_PEAK_GBS, 4),
-        avg_launch_us=round(avg_g * 1e6, 3),
-        roofline_achieved=round(sum(abytes) / len(groups) / avg_g / 1e9, 1),
-        roofline_frac=round(sum(abytes) / len(groups) / avg_g / 1e9 / HBM_PEAK_GBS, 4),
-        note="woq_linear_int4_groups_grouped: per layer (q,k,v) and (gate,up) share one launch each")
+    grouped = None
+    if not args.no_grouped:
+        el_g = time_step(torch, lambda: run_groups(woq, groups), args.steps, args.warmup, not args.no_graph)
+        avg_g = el_g / (args.steps * len(groups))
+        grouped = dict(
+            metric="effective weight GB/s at M=1, projections sharing an input grouped (same linears, same bytes)",
+            value=round(wbytes * args.steps / el_g / 1e9, 1), unit="GB/s",
+            ms_per_step=round(el_g / args.steps * 1e3, 4), launches_per_step=len(groups),
+            hbm_peak_frac=round(wbytes * args.steps / el_g / 1e9 / HBM_PEAK_GBS, 4),
+            avg_launch_us=round(avg_g * 1e6, 3),
+            roofline_achieved=round(sum(abytes) / len(groups) / avg_g / 1e9, 1),
+            roofline_frac=round(sum(abytes) / len(groups) / avg_g / 1e9 / HBM_PEAK_GBS, 4),
+            note="woq_linear_int4_groups_grouped: per layer (q,k,v) and (gate,up) share one launch each")
 
     prepared = None
     if not args.no_prepared:
@@ -513,12 +518,12 @@ def main():
                          not args.no_graph)
         val_p = wbytes * args.steps / el_p / 1e9
         avg_p = el_p / (args.steps * len(calls))
-        el_pg = time_step(torch, lambda: run_groups(woq, groups, prepared=True), args.steps, args.warmup,
-                          not args.no_graph)
+        el_pg = None if args.no_grouped else time_step(
+            torch, lambda: run_groups(woq, groups, prepared=True), args.steps, args.warmup, not args.no_graph)
         prepared = dict(
             metric="effective weight GB/s at M=1 over prepared weights (same step, same bytes)",
-            grouped_value=round(wbytes * args.steps / el_pg / 1e9, 1),
-            grouped_ms_per_step=round(el_pg / args.steps * 1e3, 4),
+            grouped_value=None if el_pg is None else round(wbytes * args.steps / el_pg / 1e9, 1),
+            grouped_ms_per_step=None if el_pg is None else round(el_pg / args.steps * 1e3, 4),
             value=round(val_p, 1), unit="GB/s", ms_per_step=round(el_p / args.steps * 1e3, 4),
             hbm_peak_frac=round(val_p / HBM_PEAK_GBS, 4), avg_launch_us=round(avg_p * 1e6, 3),
             roofline_achieved=round(sum(abytes) / len(abytes) / avg_p / 1e9, 1),
