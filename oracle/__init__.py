@@ -8,19 +8,26 @@ the readings of the pages they follow.
 """
 from .woq_ref import (  # noqa: F401
     QMAX_ASYM,
+    QMAX_S4,
     QMAX_SYM,
+    QMIN_S4,
     OracleError,
     PREP_INPUTS,
     PREP_ROWS,
     bf16_bits_to_f64,
     bf16_round_bits,
     dequantize_int4_groups,
+    dequantize_int4_sym_f16,
     linear_int4_groups,
+    linear_int4_sym_f16,
+    pack_int4,
     pack_uint4,
     prepare_int4,
+    quantize_int4_sym_f16,
     prepared_bytes,
     quantize_groups,
     rint_half_even,
+    unpack_int4,
     unpack_uint4,
     unprepare_int4,
 )

@@ -62,6 +62,17 @@ R9  Prepared weights.  The linnet page says its fused int4 kernels run on
     .. +32.  Rows past N and bytes past K/2 are zero.  Scale and zero keep the
     canonical layout.  The linear layer over prepared weights has the value
     of R8 over the canonical weights they came from.
+R10 Signed int4 groups with float16 scales (tinyllm L8.5, section 2, "int4
+    per group" and "Packing"): per group of G inputs, ``s16 =
+    float16(amax / 7)`` with the quotient formed in float32 (the page forms
+    every quotient in float32) and then rounded once more, to float16,
+    ties to even; codes ``c = clamp(rint(float32(w / s16)), -8, 7)``, the
+    quotient again in float32, against the stored float16 value.  A group
+    whose s16 is 0 (all zero, or amax / 7 below float16's range) gets codes 0
+    and scale 0; an s16 that overflows float16 is refused.  Bytes hold two
+    4-bit two's complement codes, the even input in the low nibble.
+    ``dequant = c * s16`` (exact in float32), and the linear layer's exact
+    value is ``sum_k x'[m,k] * c * s16 + bias[n]`` as in R8.
 """
 from __future__ import annotations
 
@@ -83,6 +94,13 @@ __all__ = [
     "prepared_bytes",
     "prepare_int4",
     "unprepare_int4",
+    "QMIN_S4",
+    "QMAX_S4",
+    "quantize_int4_sym_f16",
+    "pack_int4",
+    "unpack_int4",
+    "dequantize_int4_sym_f16",
+    "linear_int4_sym_f16",
 ]
 
 QMAX_ASYM = 15   # unsigned 4-bit codes 0..15 ("Per-Group INT4", 4.8 Quantization II)
@@ -319,3 +337,114 @@ def unprepare_int4(prepared, n: int, k: int):
     blocks = np.asarray(prepared, dtype=np.uint8).reshape(nt, ns, 4, PREP_ROWS, 16)
     rows = blocks.transpose(0, 3, 1, 2, 4).reshape(nt * PREP_ROWS, ns * PREP_INPUTS // 2)
     return np.ascontiguousarray(rows[:n, :k // 2])
+
+
+# ---------------------------------------------------------------------------
+# Signed int4 groups with float16 scales, R10
+# ---------------------------------------------------------------------------
+
+QMIN_S4 = -8   # 4-bit two's complement range (tinyllm L8.5, "int4 per group")
+QMAX_S4 = 7
+
+
+def quantize_int4_sym_f16(w, group: int = 32):
+    """Symmetric signed int4 per group with a float16 scale (R10).
+
+    tinyllm L8.5 section 2, "int4 per group": s16 = float16(amax / 7), codes
+    rint(w / s16) against the stored float16 scale; zero or underflowing
+    groups get codes 0; a float16 overflow is an error.
+    Args: w float32 [N, K]; group divides K and is even.
+    Returns: codes int8 [N, K] in -8..7, scale float16 [N, K/group].
+    """
+    w = np.asarray(w, dtype=np.float32)
+    _check_groups(w, group)
+    if group % 2:
+        raise OracleError("an odd group cannot be packed two per byte")
+    n, k = w.shape
+    ng = k // group
+    wg = w.reshape(n, ng, group)
+    amax = np.max(np.abs(wg), axis=-1)                       # float32, exact
+    q32 = amax / np.float32(QMAX_S4)                         # float32 quotient
+    with np.errstate(over="ignore"):
+        s16 = q32.astype(np.float16)                         # round to float16, ties to even
+    if not np.all(np.isfinite(s16)):
+        raise OracleError("a group scale overflows float16")
+    s = s16.astype(np.float32)                               # the stored value, exactly
+    live = s > 0
+    quot = wg / np.where(live, s, np.float32(1))[..., None]  # float32 quotient against s16
+    c = np.clip(rint_half_even(quot), QMIN_S4, QMAX_S4)
+    c = np.where(live[..., None], c, 0.0)
+    return c.astype(np.int8).reshape(n, k), s16
+
+
+def pack_int4(c):
+    """Two signed 4-bit codes per byte, two's complement, even element low.
+
+    tinyllm L8.5 section 2, "Packing": nibble = c & 0xF.  Codes outside
+    -8..7 and odd widths are refused.
+    """
+    c = np.asarray(c)
+    if c.shape[-1] % 2 != 0:
+        raise OracleError("an odd number of codes cannot be packed two per byte")
+    if c.size and (c.min() < QMIN_S4 or c.max() > QMAX_S4):
+        raise OracleError("signed 4-bit codes lie in -8..7")
+    nib = (c.astype(np.int16) & 0xF).astype(np.uint8)
+    return (nib[..., 0::2] | (nib[..., 1::2] << np.uint8(4))).astype(np.uint8)
+
+
+def unpack_int4(packed):
+    """Inverse of :func:`pack_int4`: each nibble sign-extended (v >= 8 is v - 16)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    nib = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.int16)
+    nib[..., 0::2] = p & np.uint8(0x0F)
+    nib[..., 1::2] = p >> np.uint8(4)
+    return np.where(nib >= 8, nib - 16, nib).astype(np.int8)
+
+
+def _sym_exact(c_rows, s16_rows, group: int):
+    """c * s16 per group as exact float64 values (R10)."""
+    n, k = c_rows.shape
+    s = np.asarray(s16_rows, dtype=np.float16).astype(np.float64)[..., None]
+    return (c_rows.reshape(n, k // group, group).astype(np.float64) * s).reshape(n, k)
+
+
+def dequantize_int4_sym_f16(packed, scale16, n: int, k: int, group: int, out: str = "f32"):
+    """``c * s16`` per group (R10); float32 [N, K], or bfloat16 bit patterns of it."""
+    if group < 2 or group % 2 or k % group:
+        raise OracleError("group must be even and divide K")
+    c = unpack_int4(np.asarray(packed, dtype=np.uint8).reshape(n, k // 2))
+    w32 = _sym_exact(c, np.asarray(scale16).reshape(n, k // group), group).astype(np.float32)
+    if out == "f32":
+        return w32
+    if out == "bf16":
+        return bf16_round_bits(w32)
+    raise OracleError("out must be 'f32' or 'bf16'")
+
+
+def linear_int4_sym_f16(x, packed, scale16, n: int, k: int, group: int,
+                        bias=None, order=None, rows=None, block_rows: int = 1024):
+    """Exact-as-float64 value of ``y = x' . dequant(W)^T + bias`` for R10 weights.
+
+    Arguments as :func:`linear_int4_groups`, with float16 scales and no zero.
+    """
+    if group < 2 or group % 2 or k % group:
+        raise OracleError("group must be even and divide K")
+    x = np.asarray(x)
+    xv = bf16_bits_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
+    if xv.ndim != 2 or xv.shape[1] != k:
+        raise OracleError("x must be [M, K]")
+    if order is not None:
+        order = np.asarray(order, dtype=np.int64)
+        if order.shape != (k,) or (k and (order.min() < 0 or order.max() >= k)):
+            raise OracleError("order must hold K indices in [0, K)")
+        xv = xv[:, order]
+    p = np.asarray(packed, dtype=np.uint8).reshape(n, k // 2)
+    s = np.asarray(scale16, dtype=np.float16).reshape(n, k // group)
+    idx = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    y = np.empty((xv.shape[0], idx.size), dtype=np.float64)
+    for b0 in range(0, idx.size, block_rows):
+        sel = idx[b0:b0 + block_rows]
+        y[:, b0:b0 + sel.size] = xv @ _sym_exact(unpack_int4(p[sel]), s[sel], group).T
+    if bias is not None:
+        y += np.asarray(bias, dtype=np.float32).astype(np.float64)[idx][None, :]
+    return y
