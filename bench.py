@@ -44,14 +44,16 @@ TRAFFIC_SUMMARY = ROOT / "profiles" / "traffic_gemv_decode_m1_g128.txt"
 KERNEL_SOURCES = ["linear_gemv.hip", "mfma_common.h"]
 
 
-def weight_bytes(n: int, k: int, group: int = GROUP) -> int:
-    """Packed codes + float32 scale + uint8 zero of an [n, k] weight."""
-    return n * k // 2 + (n * k // group) * 5
+def weight_bytes(n: int, k: int, group: int = GROUP, sym16: bool = False) -> int:
+    """Packed codes + float32 scale + uint8 zero of an [n, k] weight (or, for
+    signed codes, packed codes + float16 scale)."""
+    return n * k // 2 + (n * k // group) * (2 if sym16 else 5)
 
 
-def algorithmic_bytes(m: int, n: int, k: int, has_bias: bool, group: int = GROUP) -> int:
+def algorithmic_bytes(m: int, n: int, k: int, has_bias: bool, group: int = GROUP,
+                      sym16: bool = False) -> int:
     """Bytes a linear call must move at least once: weights, x, y (bf16), bias."""
-    return weight_bytes(n, k, group) + m * k * 2 + m * n * 2 + (n * 4 if has_bias else 0)
+    return weight_bytes(n, k, group, sym16) + m * k * 2 + m * n * 2 + (n * 4 if has_bias else 0)
 
 
 def kernel_source_hash() -> str:
@@ -208,8 +210,10 @@ def measure_prefill(torch, woq, reps: int = 5, calls: int = 20):
                 per_shape=out, plan=woq.linear_plan(2048, 14336, 4096, GROUP))
 
 
-def measure_configs(torch, woq, reps: int = 40, pool_bytes: int = 1 << 30):
-    """Per-launch time of every small-M sweep and act-order configuration.
+def measure_configs(torch, woq, reps: int = 40, pool_bytes: int = 1 << 30, cases=None,
+                    sym16: bool = False):
+    """Per-launch time of every small-M sweep and act-order configuration (or of
+    `cases`; with sym16, over signed codes with float16 scales).
 
     Weights are random bytes in the Int4GroupLinear layout (timing does not
     depend on the values); each configuration rotates over enough copies
@@ -224,18 +228,25 @@ def measure_configs(torch, woq, reps: int = 40, pool_bytes: int = 1 << 30):
     gen.manual_seed(77)
     out = []
     pools = {}
-    for case in (*SWEEP, *ACTORDER):
+    for case in (cases if cases is not None else (*SWEEP, *ACTORDER)):
         key = (case.n, case.k, case.group)
-        wb = weight_bytes(case.n, case.k, case.group)
+        wb = weight_bytes(case.n, case.k, case.group, sym16)
         if key not in pools:
             pools.clear()
             torch.cuda.empty_cache()
             copies = max(2, -(-pool_bytes // wb))
-            pools[key] = [
-                (torch.randint(0, 256, (case.n, case.k // 2), generator=gen, device=dev, dtype=torch.uint8),
-                 torch.rand((case.n, case.k // case.group), generator=gen, device=dev).mul_(0.01).add_(1e-3),
-                 torch.randint(0, 16, (case.n, case.k // case.group), generator=gen, device=dev, dtype=torch.uint8))
-                for _ in range(copies)]
+            ng = case.k // case.group
+            if sym16:
+                pools[key] = [
+                    (torch.randint(0, 256, (case.n, case.k // 2), generator=gen, device=dev, dtype=torch.uint8),
+                     torch.rand((case.n, ng), generator=gen, device=dev).mul_(0.01).add_(1e-3).half(), None)
+                    for _ in range(copies)]
+            else:
+                pools[key] = [
+                    (torch.randint(0, 256, (case.n, case.k // 2), generator=gen, device=dev, dtype=torch.uint8),
+                     torch.rand((case.n, ng), generator=gen, device=dev).mul_(0.01).add_(1e-3),
+                     torch.randint(0, 16, (case.n, ng), generator=gen, device=dev, dtype=torch.uint8))
+                    for _ in range(copies)]
         pool = pools[key]
         x = torch.randn((case.m, case.k), generator=gen, device=dev).to(torch.bfloat16)
         y = torch.empty((case.m, case.n), dtype=torch.bfloat16, device=dev)
@@ -247,8 +258,12 @@ def measure_configs(torch, woq, reps: int = 40, pool_bytes: int = 1 << 30):
 
         def call(i):
             p, sc, z = pool[i % len(pool)]
-            woq.linear_int4_groups(x, p, sc, z, bias=bias, order=order, group=case.group, out=y,
-                                   workspace=ws if ws_bytes else None)
+            if sym16:
+                woq.linear_int4_sym(x, p, sc, bias=bias, order=order, group=case.group, out=y,
+                                    workspace=ws if ws_bytes else None)
+            else:
+                woq.linear_int4_groups(x, p, sc, z, bias=bias, order=order, group=case.group, out=y,
+                                       workspace=ws if ws_bytes else None)
 
         for i in range(len(pool)):
             call(i)
@@ -271,7 +286,7 @@ def measure_configs(torch, woq, reps: int = 40, pool_bytes: int = 1 << 30):
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) * 1e-3 / reps
         flops = 2.0 * case.m * case.n * case.k
-        ab = algorithmic_bytes(case.m, case.n, case.k, case.has_bias, case.group) + (
+        ab = algorithmic_bytes(case.m, case.n, case.k, case.has_bias, case.group, sym16) + (
             case.k * 4 if case.act_order else 0)
         out.append(dict(name=case.name, m=case.m, n=case.n, k=case.k, group=case.group,
                         us=round(t * 1e6, 2), weight_GBps=round(wb / t / 1e9, 1),
@@ -534,6 +549,12 @@ def main():
 
     prefill = None if args.no_prefill else measure_prefill(torch, woq)
     configs = None if args.no_configs else measure_configs(torch, woq)
+    sym16 = None
+    if not args.no_configs:
+        from workloads import SYM16
+        sym16 = dict(
+            note="signed int4 codes with float16 scales, no zero point (woq_linear_int4_sym_f16)",
+            configs=measure_configs(torch, woq, cases=SYM16, sym16=True))
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     line = dict(
@@ -547,6 +568,7 @@ def main():
                     graph=not args.no_graph, accumulate="f32",
                     tokens_per_s_linears_only=round(1.0 / (ms_per_step * 1e-3), 1) if args.layers == 32 else None),
         roofline=roofline, grouped=grouped, prepared=prepared, prefill=prefill, configs=configs,
+        sym16=sym16,
         cpu_baseline=cpu,
     )
     print(json.dumps(line), flush=True)

@@ -247,6 +247,89 @@ int32_t woq_linear_int4_groups_grouped(const void* x_bf16, int64_t m, int32_t co
                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ---- Signed int4 groups with float16 scales ----
+ * The int4 group format of tinyllm L8.5 ("Quantization: int8, int4 group
+ * (packed), fp8, KV quant", section 2 "Principles", "int4 per group" and
+ * "Packing"): symmetric codes c in -8..7 stored as 4-bit two's complement,
+ * two per byte with the even input in the low nibble, [n, k/2] uint8; one
+ * float16 scale per group of `group` consecutive inputs, [n, k/group]; no zero
+ * point.  W_hat = c * scale.
+ */
+
+/*
+ * Quantizer.  SYNC (it reports bad weights).  Per group: amax = max|w|;
+ * s16 = float16(amax / 7), the quotient a float32 division then rounded to
+ * float16, ties to even; c = clamp(rint(w / s16), -8, 7), the quotient a
+ * float32 division against the stored float16 value, ties to even.  A group
+ * whose s16 is 0 (all zero, or amax / 7 below float16's smallest subnormal)
+ * gets codes 0 and scale 0.
+ * Arguments: w [n, k] float32 (device, 4-byte aligned); group even, divides k;
+ *   outputs codes [n, k] int8 (device), scale16 [n, k/group] float16 bits
+ *   (device, 2-byte aligned).
+ * Errors: WOQ_EINVAL, WOQ_EGROUP, WOQ_ENONFINITE (a NaN or infinity in w),
+ *   WOQ_ERANGE (an s16 that overflows float16), WOQ_EUNSUPPORTED (n*k >= 2^40),
+ *   WOQ_EHIP.  On an error the outputs of the offending groups are not written.
+ */
+int32_t woq_quantize_int4_sym_f16(const float* w, int64_t n, int64_t k, int32_t group,
+                                  int8_t* codes, uint16_t* scale16, void* stream);
+
+/*
+ * Pack signed codes two per byte: packed[i] = (c[2i] & 15) | (c[2i+1] & 15) << 4.
+ * SYNC (it reports codes outside -8..7).
+ * Arguments: codes [count] int8 (device), count even; packed [count/2] uint8 (device).
+ * Errors: WOQ_EINVAL, WOQ_ESHAPE (odd count), WOQ_ERANGE (a code outside -8..7), WOQ_EHIP.
+ */
+int32_t woq_pack_int4(const int8_t* codes, int64_t count, uint8_t* packed, void* stream);
+
+/*
+ * Unpack signed nibbles, each sign-extended (a nibble v >= 8 is v - 16).  ASYNC.
+ * Arguments: packed [count/2] uint8 (device); count even; codes [count] int8 (device).
+ * Errors: WOQ_EINVAL, WOQ_ESHAPE (odd count), WOQ_EHIP.
+ */
+int32_t woq_unpack_int4(const uint8_t* packed, int64_t count, int8_t* codes, void* stream);
+
+/*
+ * Dequantize W_hat = c * s16, exact in float32; with out_dtype = WOQ_BF16 that
+ * float32 is rounded to bfloat16, ties to even.  ASYNC.
+ * Arguments: packed [n, k/2] uint8, scale16 [n, k/group] float16 bits (device,
+ *   2-byte aligned); group even, divides k; w_hat [n, k] of out_dtype (device).
+ * Errors: WOQ_EINVAL, WOQ_EGROUP, WOQ_EUNSUPPORTED (n*k >= 2^40), WOQ_EHIP.
+ */
+int32_t woq_dequantize_int4_sym_f16(const uint8_t* packed, const uint16_t* scale16, int64_t n,
+                                    int64_t k, int32_t group, int32_t out_dtype, void* w_hat,
+                                    void* stream);
+
+/*
+ * Linear layer over signed int4 groups with float16 scales:
+ *   y[m, n] = sum_k x'[m, k] * c[n, k] * s16[n, k / group] + bias[n],
+ *   x'[m, k] = order ? x[m, order[k]] : x[m, k].
+ * The same kernels, paths, workspace (woq_linear_workspace_bytes), plan
+ * (woq_linear_plan), float32 arithmetic and error bound as
+ * woq_linear_int4_groups: a signed nibble v is read as the unsigned code v ^ 8
+ * with zero point 8, so each group is folded as scale * (sum - 8 * sum of x).
+ * ASYNC.
+ * Arguments: as woq_linear_int4_groups, with scale16 [n, k/group] float16 bits
+ *   (device, 16-byte aligned) in place of scale and zero.
+ * Errors: as woq_linear_int4_groups.
+ */
+int32_t woq_linear_int4_sym_f16(const void* x_bf16, int64_t m, const uint8_t* packed,
+                                const uint16_t* scale16, const float* bias, const int32_t* order,
+                                int64_t n, int64_t k, int32_t group, int32_t y_dtype, void* y,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * woq_linear_int4_sym_f16 over weights prepared with woq_prepare_int4 (the
+ * byte order of the prepared layout does not depend on what the nibbles mean).
+ * Arguments, results and errors as woq_linear_int4_sym_f16, with `prepared`
+ * (device, 16-byte aligned, woq_prepared_bytes(n, k) bytes) replacing `packed`.
+ */
+int32_t woq_linear_int4_sym_f16_prepared(const void* x_bf16, int64_t m, const uint8_t* prepared,
+                                         const uint16_t* scale16, const float* bias,
+                                         const int32_t* order, int64_t n, int64_t k, int32_t group,
+                                         int32_t y_dtype, void* y, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/*
  * Describe the kernel plan the linear calls use for these sizes: the path
  * (decode GEMV for m <= 4, small-M MFMA for m <= 32, tiled MFMA GEMM above),
  * tiles, waves and whether an input pre-pass runs.  Writes a NUL-terminated

@@ -209,3 +209,29 @@ def test_prepared_layout_host_checks(lib):
     rc = lib.woq_linear_int4_groups_prepared(fake, 1, fake, fake, fake, None, None, 64, 256, 48, 1,
                                              fake, None, 0, None)
     assert woq.STATUS[rc] == "WOQ_EGROUP"
+
+
+def test_signed_format_entry_points_validate_first(lib):
+    fake = ctypes.c_void_p(1 << 20)    # never dereferenced: validation fails first
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    st = lambda rc: woq.STATUS[rc]
+    assert st(lib.woq_quantize_int4_sym_f16(fake, 4, 96, 3, fake, fake, None)) == "WOQ_EGROUP"
+    assert st(lib.woq_quantize_int4_sym_f16(fake, 4, 96, 5, fake, fake, None)) == "WOQ_EGROUP"
+    assert st(lib.woq_quantize_int4_sym_f16(None, 4, 96, 32, fake, fake, None)) == "WOQ_EINVAL"
+    assert st(lib.woq_quantize_int4_sym_f16(fake, 0, 96, 32, None, None, None)) == "WOQ_OK"
+    assert st(lib.woq_pack_int4(fake, 7, fake, None)) == "WOQ_ESHAPE"
+    assert st(lib.woq_pack_int4(None, 8, fake, None)) == "WOQ_EINVAL"
+    assert st(lib.woq_unpack_int4(fake, 7, fake, None)) == "WOQ_ESHAPE"
+    assert st(lib.woq_dequantize_int4_sym_f16(fake, fake, 4, 64, 32, 7, fake, None)) == "WOQ_EINVAL"
+    assert st(lib.woq_dequantize_int4_sym_f16(fake, fake, 4, 64, 24, 0, fake, None)) == "WOQ_EGROUP"
+    # the linear: missing scale, misaligned scale, empty problem, unsupported group
+    assert st(lib.woq_linear_int4_sym_f16(fake, 1, fake, None, None, None, 64, 256, 32, 1,
+                                          fake, None, 0, None)) == "WOQ_EINVAL"
+    assert st(lib.woq_linear_int4_sym_f16(fake, 1, fake, odd, None, None, 64, 256, 32, 1,
+                                          fake, None, 0, None)) == "WOQ_EALIGN"
+    assert st(lib.woq_linear_int4_sym_f16(fake, 0, fake, fake, None, None, 64, 256, 32, 1,
+                                          fake, None, 0, None)) == "WOQ_OK"
+    assert st(lib.woq_linear_int4_sym_f16(fake, 1, fake, fake, None, None, 64, 256, 16, 1,
+                                          fake, None, 0, None)) == "WOQ_EUNSUPPORTED"
+    assert st(lib.woq_linear_int4_sym_f16_prepared(fake, 1, fake, None, None, None, 64, 256, 32,
+                                                   1, fake, None, 0, None)) == "WOQ_EINVAL"

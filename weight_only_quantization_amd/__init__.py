@@ -37,6 +37,11 @@ __all__ = [
     "prepared_bytes",
     "linear_workspace_bytes",
     "linear_plan",
+    "quantize_int4_sym",
+    "pack_int4",
+    "unpack_int4",
+    "dequantize_int4_sym",
+    "linear_int4_sym",
     "STATUS",
 ]
 
@@ -91,6 +96,14 @@ def load() -> ctypes.CDLL:
                                                     c_i32, c_i32, c_p, c_p, c_sz, c_p]),
         "woq_linear_int4_groups_grouped": (c_i32, [c_p, c_i64, c_i32, c_p, c_p, c_p, c_p, c_p, c_i64,
                                                    c_i32, c_i32, c_i32, c_p, c_p, c_sz, c_p]),
+        "woq_quantize_int4_sym_f16": (c_i32, [c_p, c_i64, c_i64, c_i32, c_p, c_p, c_p]),
+        "woq_pack_int4": (c_i32, [c_p, c_i64, c_p, c_p]),
+        "woq_unpack_int4": (c_i32, [c_p, c_i64, c_p, c_p]),
+        "woq_dequantize_int4_sym_f16": (c_i32, [c_p, c_p, c_i64, c_i64, c_i32, c_i32, c_p, c_p]),
+        "woq_linear_int4_sym_f16": (c_i32, [c_p, c_i64, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i32,
+                                            c_i32, c_p, c_p, c_sz, c_p]),
+        "woq_linear_int4_sym_f16_prepared": (c_i32, [c_p, c_i64, c_p, c_p, c_p, c_p, c_i64, c_i64,
+                                                     c_i32, c_i32, c_p, c_p, c_sz, c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -282,12 +295,15 @@ def linear_int4_groups(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tenso
 
 
 def _linear(x, weights, scale, zero, bias, order, n, k, group, out_dtype, out, workspace,
-            prepared: bool):
+            prepared: bool, sym16: bool = False):
     lib = load()
     _need(x, torch.bfloat16, "x")
     _need(weights, torch.uint8, "prepared" if prepared else "packed")
-    _need(scale, torch.float32, "scale")
-    _need(zero, torch.uint8, "zero")
+    if sym16:
+        _need(scale, torch.float16, "scale")
+    else:
+        _need(scale, torch.float32, "scale")
+        _need(zero, torch.uint8, "zero")
     if bias is not None:
         _need(bias, torch.float32, "bias")
     if order is not None:
@@ -305,12 +321,103 @@ def _linear(x, weights, scale, zero, bias, order, n, k, group, out_dtype, out, w
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wsb = workspace.numel() if (need and workspace is not None) else 0
+    y_dtype = F32 if out_dtype == torch.float32 else BF16
+    ws_ptr = _ptr(workspace) if need else None
+    if sym16:
+        fn = lib.woq_linear_int4_sym_f16_prepared if prepared else lib.woq_linear_int4_sym_f16
+        _check(fn(_ptr(x), m, _ptr(weights), _ptr(scale), _ptr(bias), _ptr(order), n, k, group,
+                  y_dtype, _ptr(out), ws_ptr, wsb, _stream()),
+               "linear_int4_sym_f16_prepared" if prepared else "linear_int4_sym_f16")
+        return out
     fn = lib.woq_linear_int4_groups_prepared if prepared else lib.woq_linear_int4_groups
     _check(fn(_ptr(x), m, _ptr(weights), _ptr(scale), _ptr(zero), _ptr(bias), _ptr(order), n, k,
-              group, F32 if out_dtype == torch.float32 else BF16, _ptr(out),
-              _ptr(workspace) if need else None, wsb, _stream()),
+              group, y_dtype, _ptr(out), ws_ptr, wsb, _stream()),
            "linear_int4_groups_prepared" if prepared else "linear_int4_groups")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Signed int4 groups with float16 scales (tinyllm L8.5, "int4 per group")
+# ---------------------------------------------------------------------------
+
+def quantize_int4_sym(w: torch.Tensor, group: int = 32):
+    """Symmetric signed int4 per group with a float16 scale on the GPU.
+
+    w: float32 [N, K].  Returns (codes int8 [N, K] in -8..7, scale float16
+    [N, K/group]): s16 = float16(amax / 7), codes rint(w / s16).  Synchronizes.
+    """
+    lib = load()
+    _need(w, torch.float32, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    n, k = w.shape
+    ng = k // group if group > 0 else 0
+    codes = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    scale = torch.empty((n, ng), dtype=torch.float16, device=w.device)
+    _check(lib.woq_quantize_int4_sym_f16(_ptr(w), n, k, group, _ptr(codes), _ptr(scale), _stream()),
+           "quantize_int4_sym_f16")
+    return codes, scale
+
+
+def pack_int4(codes: torch.Tensor) -> torch.Tensor:
+    """int8 codes -8..7 [..., 2c] -> bytes [..., c], 4-bit two's complement, even element low."""
+    lib = load()
+    _need(codes, torch.int8, "codes")
+    if codes.shape[-1] % 2:
+        raise ValueError("last dimension must be even")
+    out = torch.empty(codes.shape[:-1] + (codes.shape[-1] // 2,), dtype=torch.uint8, device=codes.device)
+    _check(lib.woq_pack_int4(_ptr(codes), codes.numel(), _ptr(out), _stream()), "pack_int4")
+    return out
+
+
+def unpack_int4(packed: torch.Tensor) -> torch.Tensor:
+    """bytes [..., c] -> int8 codes [..., 2c], each nibble sign-extended."""
+    lib = load()
+    _need(packed, torch.uint8, "packed")
+    out = torch.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=torch.int8, device=packed.device)
+    _check(lib.woq_unpack_int4(_ptr(packed), out.numel(), _ptr(out), _stream()), "unpack_int4")
+    return out
+
+
+def dequantize_int4_sym(packed: torch.Tensor, scale: torch.Tensor, group: Optional[int] = None,
+                        out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """codes * float16 scale per group -> [N, K] float32 or bfloat16."""
+    lib = load()
+    _need(packed, torch.uint8, "packed")
+    _need(scale, torch.float16, "scale")
+    n, k, group = _weight_dims(packed, scale, group)
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    out = torch.empty((n, k), dtype=out_dtype, device=packed.device)
+    _check(lib.woq_dequantize_int4_sym_f16(_ptr(packed), _ptr(scale), n, k, group,
+                                           F32 if out_dtype == torch.float32 else BF16, _ptr(out),
+                                           _stream()), "dequantize_int4_sym_f16")
+    return out
+
+
+def linear_int4_sym(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tensor,
+                    bias: Optional[torch.Tensor] = None, order: Optional[torch.Tensor] = None,
+                    group: Optional[int] = None, out_dtype: torch.dtype = torch.bfloat16,
+                    out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    prepared: bool = False) -> torch.Tensor:
+    """y = x' . (codes * s16)^T + bias over signed int4 groups with float16 scales.
+
+    x: bfloat16 [M, K]; packed uint8 [N, K/2] (or, with prepared=True, the
+    buffer of :func:`prepare_int4`); scale float16 [N, K/G]; bias float32 [N] or
+    None; order int32 [K] or None.  Asynchronous on the current stream.
+    """
+    _need(scale, torch.float16, "scale")
+    if x.dim() != 2 or scale.dim() != 2 or scale.shape[1] == 0:
+        raise ValueError("x must be [M, K] and scale [N, K/G]")
+    n, k = scale.shape[0], x.shape[1]
+    if prepared:
+        if packed.numel() < prepared_bytes(n, k):
+            raise ValueError("prepared buffer is smaller than the layout of [n, k]")
+    elif packed.numel() != n * (k // 2):
+        raise ValueError(f"packed holds {packed.numel()} bytes, expected {n * (k // 2)}")
+    g = k // scale.shape[1] if group is None else group
+    return _linear(x, packed, scale, None, bias, order, n, k, g, out_dtype, out, workspace,
+                   prepared, sym16=True)
 
 
 def linear_int4_groups_grouped(x: torch.Tensor, mats, prepared: bool = False,

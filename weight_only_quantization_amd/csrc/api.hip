@@ -277,6 +277,70 @@ int32_t woq_dequantize_int4_groups(const uint8_t* packed, const float* scale,
                            reinterpret_cast<hipStream_t>(stream));
 }
 
+int32_t woq_quantize_int4_sym_f16(const float* w, int64_t n, int64_t k, int32_t group,
+                                  int8_t* codes, uint16_t* scale16, void* stream) {
+  if (n < 0 || k < 0) return WOQ_EINVAL;
+  if (group < 2 || group % 2 || (k > 0 && k % group)) return WOQ_EGROUP;
+  if (n * k >= kMaxElems) return WOQ_EUNSUPPORTED;
+  if (n == 0 || k == 0) return WOQ_OK;
+  if (!w || !codes || !scale16) return WOQ_EINVAL;
+  if (!aligned(w, 4) || !aligned(scale16, 2)) return WOQ_EALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint32_t* flag = nullptr;
+  WOQ_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&flag), sizeof(uint32_t), s));
+  int32_t st = hip_status(hipMemsetAsync(flag, 0, sizeof(uint32_t), s));
+  if (st == WOQ_OK) st = launch_quantize_s16(w, n, k, group, codes, scale16, flag, s);
+  uint32_t hflag = 0;
+  if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(&hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+  if (st == WOQ_OK) st = hip_status(hipStreamSynchronize(s));
+  (void)hipFreeAsync(flag, s);
+  if (st != WOQ_OK) return st;
+  if (hflag & 1u) return WOQ_ENONFINITE;
+  return hflag ? WOQ_ERANGE : WOQ_OK;
+}
+
+int32_t woq_pack_int4(const int8_t* codes, int64_t count, uint8_t* packed, void* stream) {
+  if (count < 0) return WOQ_EINVAL;
+  if (count % 2) return WOQ_ESHAPE;
+  if (count >= kMaxElems) return WOQ_EUNSUPPORTED;
+  if (count == 0) return WOQ_OK;
+  if (!codes || !packed) return WOQ_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint32_t* flag = nullptr;
+  WOQ_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&flag), sizeof(uint32_t), s));
+  int32_t st = hip_status(hipMemsetAsync(flag, 0, sizeof(uint32_t), s));
+  if (st == WOQ_OK) st = launch_pack_s4(codes, count, packed, flag, s);
+  uint32_t hflag = 0;
+  if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(&hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+  if (st == WOQ_OK) st = hip_status(hipStreamSynchronize(s));
+  (void)hipFreeAsync(flag, s);
+  if (st != WOQ_OK) return st;
+  return hflag ? WOQ_ERANGE : WOQ_OK;
+}
+
+int32_t woq_unpack_int4(const uint8_t* packed, int64_t count, int8_t* codes, void* stream) {
+  if (count < 0) return WOQ_EINVAL;
+  if (count % 2) return WOQ_ESHAPE;
+  if (count >= kMaxElems) return WOQ_EUNSUPPORTED;
+  if (count == 0) return WOQ_OK;
+  if (!codes || !packed) return WOQ_EINVAL;
+  return launch_unpack_s4(packed, count, codes, reinterpret_cast<hipStream_t>(stream));
+}
+
+int32_t woq_dequantize_int4_sym_f16(const uint8_t* packed, const uint16_t* scale16, int64_t n,
+                                    int64_t k, int32_t group, int32_t out_dtype, void* w_hat,
+                                    void* stream) {
+  if (n < 0 || k < 0) return WOQ_EINVAL;
+  if (out_dtype != WOQ_F32 && out_dtype != WOQ_BF16) return WOQ_EINVAL;
+  if (group < 2 || group % 2 || (k > 0 && k % group)) return WOQ_EGROUP;
+  if (n * k >= kMaxElems) return WOQ_EUNSUPPORTED;
+  if (n == 0 || k == 0) return WOQ_OK;
+  if (!packed || !scale16 || !w_hat) return WOQ_EINVAL;
+  if (!aligned(scale16, 2) || !aligned(w_hat, out_dtype == WOQ_F32 ? 4 : 2)) return WOQ_EALIGN;
+  return launch_dequantize_s16(packed, scale16, n, k, group, out_dtype, w_hat,
+                               reinterpret_cast<hipStream_t>(stream));
+}
+
 size_t woq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group,
                                   int32_t has_order) {
   if (check_linear_shape(m, n, k, group) != WOQ_OK) return 0;
@@ -287,12 +351,15 @@ size_t woq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group
 
 namespace {
 
-// Shared body of the two linear entry points; `prepared` selects the weight
-// layout the kernels address.
+// Shared body of the linear entry points; `prepared` selects the weight layout
+// the kernels address, `scale16` (non-null) the signed codes with float16
+// scales and no zero point.
 int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const float* scale,
                     const uint8_t* zero, const float* bias, const int32_t* order, int64_t n,
                     int64_t k, int32_t group, int32_t y_dtype, void* y, void* workspace,
-                    size_t workspace_bytes, void* stream, int32_t prepared) {
+                    size_t workspace_bytes, void* stream, int32_t prepared,
+                    const uint16_t* scale16 = nullptr) {
+  const bool sym16 = scale16 != nullptr;
   int32_t st = check_linear_shape(m, n, k, group);
   if (st != WOQ_OK) return st;
   if (y_dtype != WOQ_F32 && y_dtype != WOQ_BF16) return WOQ_EINVAL;
@@ -302,9 +369,9 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
   if (bias && !aligned(bias, 4)) return WOQ_EALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (k == 0) return launch_fill_bias(bias, (int32_t)m, (int32_t)n, y_dtype == WOQ_BF16, y, s);
-  if (!x_bf16 || !packed || !scale || !zero) return WOQ_EINVAL;
-  if (!aligned(x_bf16, 16) || !aligned(packed, 16) || !aligned(scale, 16) || !aligned(zero, 16))
-    return WOQ_EALIGN;
+  if (!x_bf16 || !packed || (!sym16 && (!scale || !zero))) return WOQ_EINVAL;
+  if (!aligned(x_bf16, 16) || !aligned(packed, 16)) return WOQ_EALIGN;
+  if (sym16 ? !aligned(scale16, 16) : (!aligned(scale, 16) || !aligned(zero, 16))) return WOQ_EALIGN;
   const bool has_order = order != nullptr;
   if (has_order && !aligned(order, 16)) return WOQ_EALIGN;
   const LinearPlan plan = linear_plan(m, n, k, group, has_order);
@@ -329,6 +396,8 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
   a.mpad = plan.mpad;
   a.kpad = a.k;
   a.prepared = prepared;
+  a.sym16 = sym16 ? 1 : 0;
+  a.scale16 = scale16;
   if (plan.path == 1) {
     if (has_order) {
       uint16_t* xg = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
@@ -369,6 +438,25 @@ int32_t woq_linear_int4_groups(const void* x_bf16, int64_t m, const uint8_t* pac
                                size_t workspace_bytes, void* stream) {
   return linear_impl(x_bf16, m, packed, scale, zero, bias, order, n, k, group, y_dtype, y,
                      workspace, workspace_bytes, stream, 0);
+}
+
+int32_t woq_linear_int4_sym_f16(const void* x_bf16, int64_t m, const uint8_t* packed,
+                                const uint16_t* scale16, const float* bias, const int32_t* order,
+                                int64_t n, int64_t k, int32_t group, int32_t y_dtype, void* y,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (k > 0 && m > 0 && n > 0 && !scale16) return WOQ_EINVAL;
+  return linear_impl(x_bf16, m, packed, nullptr, nullptr, bias, order, n, k, group, y_dtype, y,
+                     workspace, workspace_bytes, stream, 0, scale16);
+}
+
+int32_t woq_linear_int4_sym_f16_prepared(const void* x_bf16, int64_t m, const uint8_t* prepared,
+                                         const uint16_t* scale16, const float* bias,
+                                         const int32_t* order, int64_t n, int64_t k, int32_t group,
+                                         int32_t y_dtype, void* y, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  if (k > 0 && m > 0 && n > 0 && !scale16) return WOQ_EINVAL;
+  return linear_impl(x_bf16, m, prepared, nullptr, nullptr, bias, order, n, k, group, y_dtype, y,
+                     workspace, workspace_bytes, stream, 1, scale16);
 }
 
 int32_t woq_linear_int4_groups_prepared(const void* x_bf16, int64_t m, const uint8_t* prepared,

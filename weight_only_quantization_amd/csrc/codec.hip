@@ -274,6 +274,95 @@ __global__ __launch_bounds__(kThreads) void dequant_byte_kernel(
   }
 }
 
+// ---- signed int4 groups with float16 scales (tinyllm L8.5, "int4 per group") ----
+// s16 = float16(amax / 7), the quotient a float32 division rounded once more
+// to float16 (ties to even); codes rint(w / s16), the quotient again in
+// float32 against the stored float16 value, clamped to -8..7; a group whose
+// s16 is 0 gets codes 0.  Flag bit 0: a non-finite weight; bit 1: an s16 that
+// overflows float16.  One thread per group.
+__global__ __launch_bounds__(kThreads) void quantize_s16_kernel(
+    const float* __restrict__ w, int64_t ngroups, int32_t group, int8_t* __restrict__ codes,
+    uint16_t* __restrict__ scale16, uint32_t* __restrict__ flag) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t gi = (int64_t)blockIdx.x * kThreads + threadIdx.x; gi < ngroups; gi += stride) {
+    const float* g = w + gi * group;
+    bool bad = false;
+    float am = 0.0f;
+    for (int e = 0; e < group; ++e) {
+      const float v = g[e];
+      bad = bad || !finite_f32(v);
+      am = fmaxf(am, fabsf(v));
+    }
+    if (bad) {
+      atomicOr(flag, 1u);
+      continue;
+    }
+    const _Float16 h = (_Float16)(am / 7.0f);   // float32 quotient, then float16 (round to nearest even)
+    const float s = (float)h;
+    if (!finite_f32(s)) {
+      atomicOr(flag, 2u);
+      continue;
+    }
+    int8_t* co = codes + gi * group;
+    for (int e = 0; e < group; ++e) {
+      const float c = s > 0.0f ? fminf(fmaxf(__builtin_rintf(g[e] / s), -8.0f), 7.0f) : 0.0f;
+      co[e] = (int8_t)c;
+    }
+    scale16[gi] = __builtin_bit_cast(uint16_t, h);
+  }
+}
+
+// Two signed codes per byte, 4-bit two's complement, even element low.  A code
+// outside -8..7 sets the flag.
+__global__ __launch_bounds__(kThreads) void pack_s4_kernel(const int8_t* __restrict__ c, int64_t nbytes,
+                                                           uint8_t* __restrict__ packed,
+                                                           uint32_t* __restrict__ flag) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  bool bad = false;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nbytes; i += stride) {
+    const int lo = c[2 * i], hi = c[2 * i + 1];
+    bad = bad || lo < -8 || lo > 7 || hi < -8 || hi > 7;
+    packed[i] = (uint8_t)((lo & 15) | ((hi & 15) << 4));
+  }
+  if (bad) atomicOr(flag, 1u);
+}
+
+// Each nibble sign-extended to a byte (v >= 8 is v - 16).
+__global__ __launch_bounds__(kThreads) void unpack_s4_kernel(const uint8_t* __restrict__ packed, int64_t nbytes,
+                                                             int8_t* __restrict__ c) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nbytes; i += stride) {
+    const int b = packed[i];
+    c[2 * i] = (int8_t)(((b & 15) ^ 8) - 8);
+    c[2 * i + 1] = (int8_t)(((b >> 4) ^ 8) - 8);
+  }
+}
+
+// W_hat = c * s16: exact in float32 (a 4-bit integer times an 11-bit significand).
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void dequant_s16_kernel(
+    const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scale16, int64_t nbytes,
+    int64_t bytes_per_row, int32_t group, void* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t groups_per_row = bytes_per_row * 2 / group;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nbytes; i += stride) {
+    const int64_t row = i / bytes_per_row;
+    const int64_t col = (i % bytes_per_row) * 2;
+    const float s = (float)__builtin_bit_cast(_Float16, scale16[row * groups_per_row + col / group]);
+    const int b = packed[i];
+    const float v0 = (float)(((b & 15) ^ 8) - 8) * s, v1 = (float)(((b >> 4) ^ 8) - 8) * s;
+    if (BF16) {
+      uint16_t* o = reinterpret_cast<uint16_t*>(out);
+      o[2 * i] = bf16_bits_rne(v0);
+      o[2 * i + 1] = bf16_bits_rne(v1);
+    } else {
+      float* o = reinterpret_cast<float*>(out);
+      o[2 * i] = v0;
+      o[2 * i + 1] = v1;
+    }
+  }
+}
+
 unsigned grid_for(int64_t items) {
   const int64_t blocks = (items + kThreads - 1) / kThreads;
   return (unsigned)(blocks < 1 ? 1 : (blocks > 65536 ? 65536 : blocks));
@@ -411,6 +500,43 @@ int32_t launch_unprepare(const uint8_t* prepared, int64_t n, int64_t k, uint8_t*
   if (nchunks == 0) return WOQ_OK;
   hipLaunchKernelGGL(unprepare_kernel, dim3(grid_for(nchunks)), dim3(kThreads), 0, stream,
                      reinterpret_cast<const uint4*>(prepared), k / 2, nsteps, nchunks, packed);
+  return hip_status(hipGetLastError());
+}
+
+int32_t launch_quantize_s16(const float* w, int64_t n, int64_t k, int32_t group, int8_t* codes,
+                            uint16_t* scale16, uint32_t* flag, hipStream_t stream) {
+  const int64_t ngroups = n * (k / group);
+  if (ngroups == 0) return WOQ_OK;
+  hipLaunchKernelGGL(quantize_s16_kernel, dim3(grid_for(ngroups)), dim3(kThreads), 0, stream,
+                     w, ngroups, group, codes, scale16, flag);
+  return hip_status(hipGetLastError());
+}
+
+int32_t launch_pack_s4(const int8_t* c, int64_t count, uint8_t* packed, uint32_t* flag,
+                       hipStream_t stream) {
+  if (count == 0) return WOQ_OK;
+  hipLaunchKernelGGL(pack_s4_kernel, dim3(grid_for(count / 2)), dim3(kThreads), 0, stream,
+                     c, count / 2, packed, flag);
+  return hip_status(hipGetLastError());
+}
+
+int32_t launch_unpack_s4(const uint8_t* packed, int64_t count, int8_t* c, hipStream_t stream) {
+  if (count == 0) return WOQ_OK;
+  hipLaunchKernelGGL(unpack_s4_kernel, dim3(grid_for(count / 2)), dim3(kThreads), 0, stream,
+                     packed, count / 2, c);
+  return hip_status(hipGetLastError());
+}
+
+int32_t launch_dequantize_s16(const uint8_t* packed, const uint16_t* scale16, int64_t n, int64_t k,
+                              int32_t group, int32_t out_dtype, void* w_hat, hipStream_t stream) {
+  const int64_t nbytes = n * (k / 2);
+  if (nbytes == 0) return WOQ_OK;
+  if (out_dtype == WOQ_BF16)
+    hipLaunchKernelGGL(dequant_s16_kernel<true>, dim3(grid_for(nbytes)), dim3(kThreads), 0, stream,
+                       packed, scale16, nbytes, k / 2, group, w_hat);
+  else
+    hipLaunchKernelGGL(dequant_s16_kernel<false>, dim3(grid_for(nbytes)), dim3(kThreads), 0, stream,
+                       packed, scale16, nbytes, k / 2, group, w_hat);
   return hip_status(hipGetLastError());
 }
 

@@ -38,6 +38,7 @@ namespace {
 constexpr int kStepK = 128;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kOffsetOOB = 0x80000000u;   // a buffer offset no descriptor covers
+constexpr uint32_t kSignFlip = 0x88888888u;    // two's complement nibble v -> unsigned v ^ 8 (zero point 8)
 
 // One thread per 8 consecutive inputs of a row (16 bytes).  The lanes of one
 // piece (piece/8 of them, consecutive) add their partial sums in a fixed
@@ -89,9 +90,11 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
 }
 
 // sz[g][c] = (scale[c][g], -(128 + zero[c][g])) for c < n, zeros up to npad.
-__global__ __launch_bounds__(256) void sz_prep_kernel(const float* __restrict__ scale,
+// With signed codes the scale is float16 and the zero point 8 (the codes are
+// read as v ^ 8).
+__global__ __launch_bounds__(256) void sz_prep_kernel(const void* __restrict__ scale,
                                                       const uint8_t* __restrict__ zero, int32_t n,
-                                                      int32_t ngroups, int32_t npad,
+                                                      int32_t ngroups, int32_t npad, int32_t sym16,
                                                       f32x2_t* __restrict__ sz) {
   const int64_t total = (int64_t)ngroups * npad;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -101,7 +104,10 @@ __global__ __launch_bounds__(256) void sz_prep_kernel(const float* __restrict__ 
     f32x2_t v = f32x2_t{0.f, 0.f};
     if (c < n) {
       const int64_t e = (int64_t)c * ngroups + g;
-      v = f32x2_t{scale[e], -(kNibOffset + (float)zero[e])};
+      if (sym16)
+        v = f32x2_t{(float)static_cast<const _Float16*>(scale)[e], -(kNibOffset + 8.0f)};
+      else
+        v = f32x2_t{static_cast<const float*>(scale)[e], -(kNibOffset + (float)zero[e])};
     }
     sz[t] = v;
   }
@@ -179,11 +185,13 @@ struct GemmParams {
   int32_t n_base, n_cols; // this launch computes output columns [n_base, n_base + n_cols)
   int32_t prepared;       // 1: packed holds prepared 1 KB blocks
   int32_t vec_out;        // 1: y is 16-byte aligned and its rows are whole 16-byte chunks
+  int32_t sym16;          // 1: signed two's complement codes (float16 scales in the table)
 };
 
 // Tl: workgroup tile; GB: 32-input blocks per group piece inside a step (1, 2
-// or 4); S: LDS stages.
-template <class Tl, int GB, int S>
+// or 4); S: LDS stages; S16: signed two's complement codes (read as v ^ 8,
+// one XOR per dword; the scale table already holds zero point 8).
+template <class Tl, int GB, int S, bool S16>
 __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
   constexpr int MT = Tl::MT, NT = Tl::NT, kWaves = Tl::kWaves;
   constexpr int BM = Tl::BM, BN = Tl::BN;
@@ -369,7 +377,8 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
       for (int nt = 0; nt < NT; ++nt) {
         const int row = brow[nt];
         const int c = (2 * L + h) ^ ((row >> 1) & 3);
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + kABytes + row * 64 + 16 * c);
+        u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + kABytes + row * 64 + 16 * c);
+        if constexpr (S16) v ^= u32x4_t{kSignFlip, kSignFlip, kSignFlip, kSignFlip};
         bd[L][nt][0] = v[0]; bd[L][nt][1] = v[1]; bd[L][nt][2] = v[2]; bd[L][nt][3] = v[3];
         if constexpr (GB == 1) {
           // Regroup for 32-input groups: the lower lanes keep their inputs
@@ -553,9 +562,9 @@ size_t gemm_lds_bytes() {
   return (size_t)S * (Tl::kABytes + Tl::kBBytes + NP * 1024 + NP * Tl::kSzParts * 1024) + kJunk;
 }
 
-template <class Tl, int GB, int S>
+template <class Tl, int GB, int S, bool S16>
 int32_t launch_gemm_t(GemmParams gp, hipStream_t stream) {
-  auto kern = gemm_kernel<Tl, GB, S>;
+  auto kern = gemm_kernel<Tl, GB, S, S16>;
   const size_t lds = gemm_lds_bytes<Tl, GB, S>();
   static bool raised = false;   // raise the dynamic-LDS limit once per instantiation
   if (!raised) {
@@ -581,14 +590,19 @@ constexpr int gemm_stages() {
   return 3 * stage + kJunk <= 160 * 1024 ? 3 : 2;
 }
 
-template <class Tl>
-int32_t launch_gemm_gb(const GemmParams& gp, int gb, hipStream_t stream) {
+template <class Tl, bool S16>
+int32_t launch_gemm_s(const GemmParams& gp, int gb, hipStream_t stream) {
   switch (gb) {
-    case 1: return launch_gemm_t<Tl, 1, gemm_stages<Tl, 1>()>(gp, stream);
-    case 2: return launch_gemm_t<Tl, 2, gemm_stages<Tl, 2>()>(gp, stream);
-    case 4: return launch_gemm_t<Tl, 4, gemm_stages<Tl, 4>()>(gp, stream);
+    case 1: return launch_gemm_t<Tl, 1, gemm_stages<Tl, 1>(), S16>(gp, stream);
+    case 2: return launch_gemm_t<Tl, 2, gemm_stages<Tl, 2>(), S16>(gp, stream);
+    case 4: return launch_gemm_t<Tl, 4, gemm_stages<Tl, 4>(), S16>(gp, stream);
     default: return WOQ_EUNSUPPORTED;
   }
+}
+
+template <class Tl>
+int32_t launch_gemm_gb(const GemmParams& gp, int gb, hipStream_t stream) {
+  return gp.sym16 ? launch_gemm_s<Tl, true>(gp, gb, stream) : launch_gemm_s<Tl, false>(gp, gb, stream);
 }
 
 }  // namespace
@@ -633,8 +647,9 @@ int32_t launch_gemm(const LinearArgs& a, const LinearPlan& pl, void* sz_ws, hipS
     const int64_t total = (int64_t)ngroups * npad;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(sz_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.scale, a.zero,
-                       a.n, ngroups, npad, static_cast<f32x2_t*>(sz_ws));
+    hipLaunchKernelGGL(sz_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       a.sym16 ? static_cast<const void*>(a.scale16) : static_cast<const void*>(a.scale),
+                       a.zero, a.n, ngroups, npad, a.sym16, static_cast<f32x2_t*>(sz_ws));
     const int32_t st = hip_status(hipGetLastError());
     if (st != WOQ_OK) return st;
   }
@@ -642,7 +657,8 @@ int32_t launch_gemm(const LinearArgs& a, const LinearPlan& pl, void* sz_ws, hipS
   const GemmParams gp{a.x, a.packed, a.xs, static_cast<const f32x2_t*>(sz_ws), a.bias, a.y,
                       a.m, a.n, a.k, a.kpad, a.group, a.y_bf16, a.mpad, npad, ngroups, a.k / piece,
                       0, 0, 0, a.n, a.prepared,
-                      (reinterpret_cast<uintptr_t>(a.y) % 16 == 0 && a.n % (a.y_bf16 ? 8 : 4) == 0) ? 1 : 0};
+                      (reinterpret_cast<uintptr_t>(a.y) % 16 == 0 && a.n % (a.y_bf16 ? 8 : 4) == 0) ? 1 : 0,
+                      a.sym16};
   // Tile by the number of activation rows: small M takes narrow tiles so the
   // grid still covers the chip.
   switch (pl.bm) {

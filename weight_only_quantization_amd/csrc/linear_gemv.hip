@@ -37,6 +37,7 @@ constexpr uint32_t kOffsetOOB = 0x80000000u;   // a buffer offset no descriptor 
 // expcnt at their maxima
 constexpr int kWaitLdsOnly = 0xC07F;
 constexpr int kSzPerBatch = 16;    // (scale, zero) entries per row staged by one load batch
+constexpr uint32_t kSignFlip = 0x88888888u;   // two's complement nibble v -> unsigned v ^ 8 (zero point 8)
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -45,8 +46,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // [tile_begin, next tile_begin) take the 16-row tiles of matrix i.
 struct GemvProblem {
   const uint8_t* packed;
-  const float* scale;
-  const uint8_t* zero;
+  const void* scale;      // float32, or float16 for signed codes
+  const uint8_t* zero;    // unused for signed codes
   const float* bias;
   void* y;
   int32_t n;
@@ -119,8 +120,12 @@ __device__ __forceinline__ float lane_group_sum(float v) {
 
 // GB: 32-wide blocks per group piece inside a step (1, 2 or 4); FR:
 // accumulator rows folded and stored (1 when m == 1, else 4); CC: the most
-// steps a wave owns (4, 8 or 16); PF: steps of weight loads in flight.
-template <int GB, int FR, int CC, int PF>
+// steps a wave owns (4, 8 or 16); PF: steps of weight loads in flight; S16:
+// signed two's complement codes with float16 scales and no zero point
+// (tinyllm L8.5, "int4 per group").  A signed nibble v is the unsigned code
+// v ^ 8 with zero point 8, so those weights go through the same arithmetic
+// after one XOR per dword.
+template <int GB, int FR, int CC, int PF, bool S16>
 __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   constexpr int NP = 4 / GB;              // group pieces per step
   constexpr int XL = FR == 1 ? CC / 4 : 4;                        // activation loads per batch
@@ -157,8 +162,12 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   const __amdgpu_buffer_rsrc_t rb =
       prep ? rsrc(pr.packed + (int64_t)tile * p.nsteps * 1024, (uint32_t)p.nsteps * 1024u)
            : rsrc(pr.packed + (int64_t)row0 * row_bytes, (uint32_t)rows * row_bytes);
-  const __amdgpu_buffer_rsrc_t rs = rsrc(pr.scale + (int64_t)row0 * p.ngroups, (uint32_t)(rows * p.ngroups) * 4u);
-  const __amdgpu_buffer_rsrc_t rz = rsrc(pr.zero + (int64_t)row0 * p.ngroups, (uint32_t)(rows * p.ngroups));
+  constexpr uint32_t kScaleBytes = S16 ? 2u : 4u;
+  const __amdgpu_buffer_rsrc_t rs =
+      rsrc(static_cast<const char*>(pr.scale) + (int64_t)row0 * p.ngroups * kScaleBytes,
+           (uint32_t)(rows * p.ngroups) * kScaleBytes);
+  const __amdgpu_buffer_rsrc_t rz = rsrc(S16 ? nullptr : pr.zero + (int64_t)row0 * p.ngroups,
+                                         S16 ? 0u : (uint32_t)(rows * p.ngroups));
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.x, (uint32_t)M * (uint32_t)K * 2u);
 
   // ---- staging loads: activations, then scales and zero points -----------------
@@ -206,7 +215,23 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   auto load_sz = [&](int b) {
     const int g = gb + 4 * q + kSzPerBatch * b;
     const uint32_t e0 = (uint32_t)(c * p.ngroups + g);
-    if (!p.z_bytewise) {   // uniform: whole dwords of zero points
+    if constexpr (S16) {   // four float16 scales, kept as raw halves until put_sz
+      zv[b] = 0x08080808u;
+      sv[b] = u32x4_t{0u, 0u, 0u, 0u};
+      if (!p.z_bytewise) {   // uniform: whole 8-byte runs of scales
+        const bool in = c < rows && g < p.ngroups;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, in ? e0 * 2u : kOffsetOOB, 0, 0);
+        sv[b][0] = v[0];
+        sv[b][1] = v[1];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ie = c < rows && g + e < p.ngroups;
+          const uint32_t h = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, ie ? (e0 + e) * 2u : kOffsetOOB, 0, 0);
+          sv[b][e >> 1] |= h << (16 * (e & 1));
+        }
+      }
+    } else if (!p.z_bytewise) {   // uniform: whole dwords of zero points
       const bool in = c < rows && g < p.ngroups;
       sv[b] = bload16(rs, in ? e0 * 4u : kOffsetOOB);
       zv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rz, in ? e0 : kOffsetOOB, 0, 0);
@@ -223,7 +248,17 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   auto put_sz = [&](int b) {
     // (bit_cast of the whole vector: this compiler resolves a bit_cast of one
     // element of a vector lvalue to element 0)
-    const f32x4_t sf = __builtin_bit_cast(f32x4_t, sv[b]);
+    f32x4_t sf;
+    if constexpr (S16) {
+      const u32x4_t raw = sv[b];
+      const uint32_t h01 = raw[0], h23 = raw[1];
+      sf = f32x4_t{(float)__builtin_bit_cast(_Float16, (uint16_t)(h01 & 0xFFFFu)),
+                   (float)__builtin_bit_cast(_Float16, (uint16_t)(h01 >> 16)),
+                   (float)__builtin_bit_cast(_Float16, (uint16_t)(h23 & 0xFFFFu)),
+                   (float)__builtin_bit_cast(_Float16, (uint16_t)(h23 >> 16))};
+    } else {
+      sf = __builtin_bit_cast(f32x4_t, sv[b]);
+    }
     const uint32_t z = zv[b];
     f32x4_t* dst = reinterpret_cast<f32x4_t*>(lds + sz_base + (uint32_t)((c * kSzEntries + 4 * q + kSzPerBatch * b) * 8));
     dst[0] = f32x4_t{sf[0], -(kNibOffset + (float)(z & 0xFFu)), sf[1], -(kNibOffset + (float)((z >> 8) & 0xFFu))};
@@ -297,6 +332,9 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
       // the refill (no copy of a register a load is still writing).
       uint32_t d0 = vgpr_copy(bq[slot][0]), d1 = vgpr_copy(bq[slot][1]);
       uint32_t d2 = vgpr_copy(bq[slot][2]), d3 = vgpr_copy(bq[slot][3]);
+      if constexpr (S16) {
+        d0 ^= kSignFlip; d1 ^= kSignFlip; d2 ^= kSignFlip; d3 ^= kSignFlip;
+      }
       transpose4_lanegroups(d0, d1, d2, d3);
       bw[0] = unpack_codes(d0, p.nib_mask, nib_offset);
       bw[1] = unpack_codes(d1, p.nib_mask, nib_offset);
@@ -304,7 +342,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
       bw[3] = unpack_codes(d3, p.nib_mask, nib_offset);
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bw[e] = unpack_codes(bq[slot][e], p.nib_mask, nib_offset);
+      for (int e = 0; e < 4; ++e) bw[e] = unpack_codes(S16 ? bq[slot][e] ^ kSignFlip : bq[slot][e], p.nib_mask, nib_offset);
     }
     issue(slot, i + PF);
     __builtin_amdgcn_sched_barrier(0);
@@ -363,9 +401,9 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   }
 }
 
-template <int GB, int FR, int CC>
+template <int GB, int FR, int CC, bool S16>
 int32_t launch_one(const GemvParams& gp, const LinearPlan& pl, size_t lds, hipStream_t stream) {
-  auto kern = gemv_kernel<GB, FR, CC, 4>;
+  auto kern = gemv_kernel<GB, FR, CC, 4, S16>;
   if (lds > 64 * 1024) {
     static bool raised = false;   // raise the dynamic-LDS limit once per instantiation
     if (!raised) {
@@ -379,23 +417,23 @@ int32_t launch_one(const GemvParams& gp, const LinearPlan& pl, size_t lds, hipSt
   return hip_status(hipGetLastError());
 }
 
-template <int GB, int FR>
+template <int GB, int FR, bool S16>
 int32_t dispatch_cc(const GemvParams& gp, const LinearPlan& pl, size_t lds, hipStream_t stream) {
   const int cc = gemv_cnt_class(pl.cnt);
   switch (cc) {
-    case 4: return launch_one<GB, FR, 4>(gp, pl, lds, stream);
-    case 8: return launch_one<GB, FR, 8>(gp, pl, lds, stream);
-    case 16: return launch_one<GB, FR, 16>(gp, pl, lds, stream);
+    case 4: return launch_one<GB, FR, 4, S16>(gp, pl, lds, stream);
+    case 8: return launch_one<GB, FR, 8, S16>(gp, pl, lds, stream);
+    case 16: return launch_one<GB, FR, 16, S16>(gp, pl, lds, stream);
     default: return WOQ_EUNSUPPORTED;
   }
 }
 
-template <int FR>
+template <int FR, bool S16>
 int32_t dispatch_gb(const GemvParams& gp, const LinearPlan& pl, size_t lds, hipStream_t stream) {
   switch (pl.gb) {
-    case 1: return dispatch_cc<1, FR>(gp, pl, lds, stream);
-    case 2: return dispatch_cc<2, FR>(gp, pl, lds, stream);
-    case 4: return dispatch_cc<4, FR>(gp, pl, lds, stream);
+    case 1: return dispatch_cc<1, FR, S16>(gp, pl, lds, stream);
+    case 2: return dispatch_cc<2, FR, S16>(gp, pl, lds, stream);
+    case 4: return dispatch_cc<4, FR, S16>(gp, pl, lds, stream);
     default: return WOQ_EUNSUPPORTED;
   }
 }
@@ -434,14 +472,19 @@ int32_t launch_gemv_grouped(const LinearArgs* args, int count, const LinearPlan&
                 kNibPairMask, kBf16Offset2, count, {}};
   int32_t tb = 0;
   for (int i = 0; i < count; ++i) {
-    gp.prob[i] = GemvProblem{args[i].packed, args[i].scale, args[i].zero, args[i].bias, args[i].y,
-                             args[i].n, tb};
+    gp.prob[i] = GemvProblem{args[i].packed,
+                             a.sym16 ? static_cast<const void*>(args[i].scale16)
+                                     : static_cast<const void*>(args[i].scale),
+                             args[i].zero, args[i].bias, args[i].y, args[i].n, tb};
     tb += (args[i].n + 15) / 16;
   }
   LinearPlan p2 = pl;
   p2.grid = tb;
-  return pl.fold_rows == 1 ? dispatch_gb<1>(gp, p2, l.total, stream)
-                           : dispatch_gb<4>(gp, p2, l.total, stream);
+  if (a.sym16)
+    return pl.fold_rows == 1 ? dispatch_gb<1, true>(gp, p2, l.total, stream)
+                             : dispatch_gb<4, true>(gp, p2, l.total, stream);
+  return pl.fold_rows == 1 ? dispatch_gb<1, false>(gp, p2, l.total, stream)
+                           : dispatch_gb<4, false>(gp, p2, l.total, stream);
 }
 
 int32_t launch_gemv(const LinearArgs& a, const LinearPlan& pl, hipStream_t stream) {

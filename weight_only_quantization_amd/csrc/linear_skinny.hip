@@ -42,12 +42,13 @@ constexpr uint32_t kOffsetOOB = 0x80000000u;   // a buffer offset no descriptor 
 constexpr int kWaitLdsOnly = 0xC07F;
 constexpr int kStageBatch = 24;  // staged (scale, zero) entries per lane and batch
 constexpr int kPF = 2;           // steps of loads in flight per wave
+constexpr uint32_t kSignFlip = 0x88888888u;   // two's complement nibble v -> unsigned v ^ 8 (zero point 8)
 
 struct SkinnyParams {
   const uint16_t* x;
   const uint8_t* packed;
-  const float* scale;
-  const uint8_t* zero;
+  const void* scale;      // float32, or float16 for signed codes
+  const uint8_t* zero;    // unused for signed codes
   const float* bias;
   void* y;
   int32_t m, n, k, y_bf16;
@@ -69,8 +70,11 @@ __device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
-// G: group size; MT: 16-row activation tiles; T: 16-row weight tiles per workgroup.
-template <int G, int MT, int T>
+// G: group size; MT: 16-row activation tiles; T: 16-row weight tiles per
+// workgroup; S16: signed two's complement codes with float16 scales and no
+// zero point (tinyllm L8.5, "int4 per group"), run as unsigned codes v ^ 8
+// with zero point 8 after one XOR per dword.
+template <int G, int MT, int T, bool S16>
 __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   constexpr int GB = G >= 128 ? 4 : G / 32;   // 32-input blocks per group piece
   constexpr int NP = 4 / GB;                  // group pieces per step
@@ -100,12 +104,14 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   const int gb = (s0 * kStepK) / G;
   const int ngw = p.ngw;
   unsigned char* szl = lds + wave * p.sz_bytes;
+  constexpr uint32_t kScaleBytes = S16 ? 2u : 4u;
   const __amdgpu_buffer_rsrc_t rs =
-      rsrc(p.scale + (int64_t)tile0 * 16 * p.ngroups, (uint32_t)(wg_rows * p.ngroups) * 4u);
-  const __amdgpu_buffer_rsrc_t rz =
-      rsrc(p.zero + (int64_t)tile0 * 16 * p.ngroups, (uint32_t)(wg_rows * p.ngroups));
+      rsrc(static_cast<const char*>(p.scale) + (int64_t)tile0 * 16 * p.ngroups * kScaleBytes,
+           (uint32_t)(wg_rows * p.ngroups) * kScaleBytes);
+  const __amdgpu_buffer_rsrc_t rz = rsrc(S16 ? nullptr : p.zero + (int64_t)tile0 * 16 * p.ngroups,
+                                         S16 ? 0u : (uint32_t)(wg_rows * p.ngroups));
   const int sz_total = 16 * T * ngw;
-  float sv[kStageBatch];
+  uint32_t sv[kStageBatch];   // float32 bits, or float16 bits for S16 (converted when stored)
   uint32_t zv[kStageBatch];
   auto stage_load = [&](int base) {
 #pragma unroll
@@ -114,16 +120,22 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
       const int r = e / ngw, g = e % ngw;
       const bool in = e < sz_total && r < wg_rows && gb + g < p.ngroups;
       const uint32_t idx = (uint32_t)(r * p.ngroups + gb + g);
-      sv[b] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, in ? idx * 4u : kOffsetOOB, 0, 0));
-      zv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rz, in ? idx : kOffsetOOB, 0, 0);
+      if constexpr (S16) {
+        sv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, in ? idx * 2u : kOffsetOOB, 0, 0);
+        zv[b] = 8u;
+      } else {
+        sv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, in ? idx * 4u : kOffsetOOB, 0, 0);
+        zv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rz, in ? idx : kOffsetOOB, 0, 0);
+      }
     }
   };
   auto stage_store = [&](int base) {
 #pragma unroll
     for (int b = 0; b < kStageBatch; ++b) {
       const int e = base + lane + 64 * b;
+      const float sc = S16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)sv[b]) : __builtin_bit_cast(float, sv[b]);
       if (e < sz_total)
-        *reinterpret_cast<f32x2_t*>(szl + e * 8) = f32x2_t{sv[b], -(kNibOffset + (float)(zv[b] & 0xFFu))};
+        *reinterpret_cast<f32x2_t*>(szl + e * 8) = f32x2_t{sc, -(kNibOffset + (float)(zv[b] & 0xFFu))};
     }
   };
   stage_load(0);
@@ -220,6 +232,9 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
         // the lane swaps work on copies, so the slot's registers are free for the refill
         uint32_t d0 = vgpr_copy(wb[slot][t][0]), d1 = vgpr_copy(wb[slot][t][1]);
         uint32_t d2 = vgpr_copy(wb[slot][t][2]), d3 = vgpr_copy(wb[slot][t][3]);
+        if constexpr (S16) {
+          d0 ^= kSignFlip; d1 ^= kSignFlip; d2 ^= kSignFlip; d3 ^= kSignFlip;
+        }
         transpose4_lanegroups(d0, d1, d2, d3);
         bw[0] = unpack_codes(d0, p.nib_mask, nib_offset);
         bw[1] = unpack_codes(d1, p.nib_mask, nib_offset);
@@ -227,7 +242,8 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
         bw[3] = unpack_codes(d3, p.nib_mask, nib_offset);
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bw[e] = unpack_codes(wb[slot][t][e], p.nib_mask, nib_offset);
+        for (int e = 0; e < 4; ++e)
+          bw[e] = unpack_codes(S16 ? wb[slot][t][e] ^ kSignFlip : wb[slot][t][e], p.nib_mask, nib_offset);
       }
       issue_w(slot, t, i + kPF);
       __builtin_amdgcn_sched_barrier(0);
@@ -288,9 +304,9 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   }
 }
 
-template <int G, int MT, int T>
+template <int G, int MT, int T, bool S16>
 int32_t launch_one(const SkinnyParams& sp, const LinearPlan& pl, size_t lds, hipStream_t stream) {
-  auto kern = skinny_kernel<G, MT, T>;
+  auto kern = skinny_kernel<G, MT, T, S16>;
   if (lds > 64 * 1024) {
     static bool raised = false;   // raise the dynamic-LDS limit once per instantiation
     if (!raised) {
@@ -304,21 +320,21 @@ int32_t launch_one(const SkinnyParams& sp, const LinearPlan& pl, size_t lds, hip
   return hip_status(hipGetLastError());
 }
 
-template <int G, int MT>
+template <int G, int MT, bool S16>
 int32_t dispatch_t(const SkinnyParams& sp, const LinearPlan& pl, size_t lds, hipStream_t s) {
   switch (pl.ns) {
-    case 1: return launch_one<G, MT, 1>(sp, pl, lds, s);
-    case 2: return launch_one<G, MT, 2>(sp, pl, lds, s);
-    case 4: return launch_one<G, MT, 4>(sp, pl, lds, s);
+    case 1: return launch_one<G, MT, 1, S16>(sp, pl, lds, s);
+    case 2: return launch_one<G, MT, 2, S16>(sp, pl, lds, s);
+    case 4: return launch_one<G, MT, 4, S16>(sp, pl, lds, s);
     default: return WOQ_EUNSUPPORTED;
   }
 }
 
-template <int G>
+template <int G, bool S16>
 int32_t dispatch_mt(const SkinnyParams& sp, const LinearPlan& pl, size_t lds, hipStream_t s) {
   switch (pl.mt) {
-    case 1: return dispatch_t<G, 1>(sp, pl, lds, s);
-    case 2: return dispatch_t<G, 2>(sp, pl, lds, s);
+    case 1: return dispatch_t<G, 1, S16>(sp, pl, lds, s);
+    case 2: return dispatch_t<G, 2, S16>(sp, pl, lds, s);
     default: return WOQ_EUNSUPPORTED;
   }
 }
@@ -338,14 +354,24 @@ SkinnyLds skinny_lds_layout(int64_t m, int64_t k, int64_t group, int waves, int 
 
 int32_t launch_skinny(const LinearArgs& a, const LinearPlan& pl, hipStream_t stream) {
   const SkinnyLds l = skinny_lds_layout(a.m, a.k, a.group, pl.waves, pl.ns, pl.cnt);
-  SkinnyParams sp{a.x, a.packed, a.scale, a.zero, a.bias, a.y, a.m, a.n, a.k, a.y_bf16,
+  SkinnyParams sp{a.x, a.packed, a.sym16 ? static_cast<const void*>(a.scale16) : static_cast<const void*>(a.scale),
+                  a.zero, a.bias, a.y, a.m, a.n, a.k, a.y_bf16,
                   (a.k + kStepK - 1) / kStepK, a.k / a.group, a.prepared, pl.cnt, l.ngw,
                   l.sz_bytes, (int32_t)l.red_off, kNibPairMask, kBf16Offset2};
+  if (a.sym16) {
+    switch (a.group) {
+      case 32: return dispatch_mt<32, true>(sp, pl, l.total, stream);
+      case 64: return dispatch_mt<64, true>(sp, pl, l.total, stream);
+      case 128: return dispatch_mt<128, true>(sp, pl, l.total, stream);
+      case 256: return dispatch_mt<256, true>(sp, pl, l.total, stream);
+      default: return WOQ_EUNSUPPORTED;
+    }
+  }
   switch (a.group) {
-    case 32: return dispatch_mt<32>(sp, pl, l.total, stream);
-    case 64: return dispatch_mt<64>(sp, pl, l.total, stream);
-    case 128: return dispatch_mt<128>(sp, pl, l.total, stream);
-    case 256: return dispatch_mt<256>(sp, pl, l.total, stream);
+    case 32: return dispatch_mt<32, false>(sp, pl, l.total, stream);
+    case 64: return dispatch_mt<64, false>(sp, pl, l.total, stream);
+    case 128: return dispatch_mt<128, false>(sp, pl, l.total, stream);
+    case 256: return dispatch_mt<256, false>(sp, pl, l.total, stream);
     default: return WOQ_EUNSUPPORTED;
   }
 }

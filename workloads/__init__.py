@@ -33,6 +33,7 @@ __all__ = [
     "SWEEP",
     "PREFILL",
     "ACTORDER",
+    "SYM16",
     "LLAMA3_8B_LAYER",
 ]
 
@@ -169,3 +170,14 @@ def packed_weights(n: int, k: int, group: int, seed: int, std: float = 0.02):
     scale = (np.abs(rng.standard_normal((n, k // group))) * std * 4 / 15 + std / 15).astype(np.float32)
     zero = rng.integers(0, 16, (n, k // group), dtype=np.uint8)
     return packed, scale, zero
+
+
+# Signed int4 groups with float16 scales (tinyllm L8.5, "int4 per group", whose
+# default group is 32): the decode shapes at M = 1 with groups 32 and 128,
+# one small-M and one prefill shape.
+SYM16 = tuple(
+    [LinearCase(f"sym16_m1_g{g}_{n}x{k}", 1, n, k, g, seed_w=150 + i, seed_x=250 + i)
+     for g in (32, 128) for i, (n, k) in enumerate(((4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)))]
+    + [LinearCase("sym16_m16_g32_14336x4096", 16, 14336, 4096, 32, seed_w=158, seed_x=258),
+       LinearCase("sym16_m2048_g32_4096x14336", 2048, 4096, 14336, 32, seed_w=159, seed_x=259)]
+)
