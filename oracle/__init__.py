@@ -7,6 +7,8 @@ nothing here calls the HIP library.  See ``woq_ref`` for the definitions and
 the readings of the pages they follow.
 """
 from .woq_ref import (  # noqa: F401
+    E2M1_VALUES,
+    MX_BLOCK,
     QMAX_ASYM,
     QMAX_S4,
     QMAX_SYM,
@@ -18,12 +20,15 @@ from .woq_ref import (  # noqa: F401
     bf16_round_bits,
     dequantize_int4_groups,
     dequantize_int4_sym_f16,
+    dequantize_mxfp4,
     linear_int4_groups,
     linear_int4_sym_f16,
+    linear_mxfp4,
     pack_int4,
     pack_uint4,
     prepare_int4,
     quantize_int4_sym_f16,
+    quantize_mxfp4,
     prepared_bytes,
     quantize_groups,
     rint_half_even,

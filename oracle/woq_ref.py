@@ -73,6 +73,21 @@ R10 Signed int4 groups with float16 scales (tinyllm L8.5, section 2, "int4
     4-bit two's complement codes, the even input in the low nibble.
     ``dequant = c * s16`` (exact in float32), and the linear layer's exact
     value is ``sum_k x'[m,k] * c * s16 + bias[n]`` as in R8.
+R11 MXFP4 (linnet "Quantization", std.quant table, dequantize_mxfp4: E2M1
+    values in blocks of 32, one E8M0 scale byte a block; tinyllm L8.5 section
+    2, "MXFP4": a block's power-of-two scale X, elements 0, 0.5, 1, 1.5, 2, 3,
+    4, 6 times X, values above 6X saturate, every element within 2X).  Layout:
+    blocks [N, K/32, 16] uint8, two 4-bit E2M1 codes a byte, the even element
+    in the low nibble (linnet packing sentence); scales [N, K/32] uint8, X =
+    2^(e - 127).  Code c: bit 3 the sign, bits 0..2 index the magnitudes
+    above.  The pages do not say how X is chosen; the reading follows the OCP
+    Microscaling Formats v1.0 rule the page cites for depth: X = 2^(floor(
+    log2 amax) - 2) (2 = the largest E2M1 exponent), e = clamp(floor(log2
+    amax) - 2 + 127, 0, 254), e = 0 for a zero block.  Elements round w / X
+    (exact) to the nearest magnitude, ties to the even code, saturate at 6,
+    and keep their sign (a negative value that rounds to 0 is code 8).
+    ``dequant = code_value * X`` (exact in float32); the linear layer's exact
+    value is ``sum_k x[m,k] * dequant[n,k] + bias[n]``.
 """
 from __future__ import annotations
 
@@ -101,6 +116,11 @@ __all__ = [
     "unpack_int4",
     "dequantize_int4_sym_f16",
     "linear_int4_sym_f16",
+    "MX_BLOCK",
+    "E2M1_VALUES",
+    "quantize_mxfp4",
+    "dequantize_mxfp4",
+    "linear_mxfp4",
 ]
 
 QMAX_ASYM = 15   # unsigned 4-bit codes 0..15 ("Per-Group INT4", 4.8 Quantization II)
@@ -448,3 +468,89 @@ def linear_int4_sym_f16(x, packed, scale16, n: int, k: int, group: int,
     if bias is not None:
         y += np.asarray(bias, dtype=np.float32).astype(np.float64)[idx][None, :]
     return y
+
+
+# ---------------------------------------------------------------------------
+# MXFP4: E2M1 codes in blocks of 32 with an E8M0 scale, R11
+# ---------------------------------------------------------------------------
+
+MX_BLOCK = 32
+E2M1_VALUES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)   # magnitudes of codes 0..7 (tinyllm "MXFP4")
+
+
+def _e2m1_round(v):
+    """Nearest E2M1 code of real values v (float64): ties to the even code, saturating at 6."""
+    mags = np.asarray(E2M1_VALUES)
+    a = np.minimum(np.abs(v), 6.0)
+    d = np.abs(a[..., None] - mags)                            # distance to each magnitude
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best                                           # one or two nearest codes
+    even = cand & ((np.arange(8) % 2) == 0)
+    idx = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+    return (idx + np.where(np.signbit(v), 8, 0)).astype(np.uint8)
+
+
+def _e8m0_value(e):
+    """X = 2^(e - 127) as float64 (255, not a number in E8M0, gives NaN)."""
+    e = np.asarray(e, dtype=np.int64)
+    return np.where(e == 255, np.nan, np.ldexp(1.0, (e - 127).astype(np.int64)))
+
+
+def _e2m1_value(c):
+    c = np.asarray(c, dtype=np.uint8)
+    v = np.asarray(E2M1_VALUES)[c & 7]
+    return np.where(c & 8, -v, v)
+
+
+def quantize_mxfp4(w):
+    """MXFP4 quantizer (R11).  w float32 [N, K], K a multiple of 32.
+
+    Returns codes uint8 [N, K] (0..15, E2M1 bit patterns) and scales uint8
+    [N, K/32] (E8M0).  Non-finite weights are refused.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    _check_groups(w, MX_BLOCK)
+    n, k = w.shape
+    wb = w.reshape(n, k // MX_BLOCK, MX_BLOCK).astype(np.float64)
+    amax = np.max(np.abs(wb), axis=-1)
+    _, ex = np.frexp(amax)                                   # amax = f * 2^ex, f in [0.5, 1)
+    e = np.where(amax > 0, np.clip(ex - 1 - 2 + 127, 0, 254), 0).astype(np.int64)
+    x_scale = _e8m0_value(e)
+    codes = _e2m1_round(wb / x_scale[..., None])              # exact: X is a power of two
+    return codes.reshape(n, k), e.astype(np.uint8)
+
+
+def dequantize_mxfp4(blocks, scales, n: int, k: int, out: str = "f32"):
+    """E2M1 value * 2^(e - 127) per block of 32 (R11); float32 [N, K] or bf16 bits."""
+    if k % MX_BLOCK:
+        raise OracleError("K must be a multiple of 32")
+    c = unpack_uint4(np.asarray(blocks, dtype=np.uint8).reshape(n, k // 2))
+    x_scale = np.repeat(_e8m0_value(np.asarray(scales).reshape(n, k // MX_BLOCK)), MX_BLOCK, axis=1)
+    w32 = (_e2m1_value(c) * x_scale).astype(np.float32)
+    if out == "f32":
+        return w32
+    if out == "bf16":
+        return bf16_round_bits(w32)
+    raise OracleError("out must be 'f32' or 'bf16'")
+
+
+def linear_mxfp4(x, blocks, scales, n: int, k: int, bias=None, rows=None, block_rows: int = 1024):
+    """Exact-as-float64 value of ``y = x . dequant(W)^T + bias`` for MXFP4 weights (R11)."""
+    if k % MX_BLOCK:
+        raise OracleError("K must be a multiple of 32")
+    x = np.asarray(x)
+    xv = bf16_bits_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
+    if xv.ndim != 2 or xv.shape[1] != k:
+        raise OracleError("x must be [M, K]")
+    p = np.asarray(blocks, dtype=np.uint8).reshape(n, k // 2)
+    e = np.asarray(scales, dtype=np.uint8).reshape(n, k // MX_BLOCK)
+    idx = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    y = np.empty((xv.shape[0], idx.size), dtype=np.float64)
+    for b0 in range(0, idx.size, block_rows):
+        sel = idx[b0:b0 + block_rows]
+        w = _e2m1_value(unpack_uint4(p[sel])) * np.repeat(_e8m0_value(e[sel]), MX_BLOCK, axis=1)
+        y[:, b0:b0 + sel.size] = xv @ w.T
+    if bias is not None:
+        y += np.asarray(bias, dtype=np.float32).astype(np.float64)[idx][None, :]
+    return y
+
