@@ -44,16 +44,18 @@ TRAFFIC_SUMMARY = ROOT / "profiles" / "traffic_gemv_decode_m1_g128.txt"
 KERNEL_SOURCES = ["linear_gemv.hip", "mfma_common.h"]
 
 
-def weight_bytes(n: int, k: int, group: int = GROUP, sym16: bool = False) -> int:
-    """Packed codes + float32 scale + uint8 zero of an [n, k] weight (or, for
-    signed codes, packed codes + float16 scale)."""
+def weight_bytes(n: int, k: int, group: int = GROUP, sym16: bool = False, mx: bool = False) -> int:
+    """Packed codes + float32 scale + uint8 zero of an [n, k] weight (for signed
+    codes: packed codes + float16 scale; for MXFP4: codes + one byte per 32)."""
+    if mx:
+        return n * k // 2 + n * k // 32
     return n * k // 2 + (n * k // group) * (2 if sym16 else 5)
 
 
 def algorithmic_bytes(m: int, n: int, k: int, has_bias: bool, group: int = GROUP,
-                      sym16: bool = False) -> int:
+                      sym16: bool = False, mx: bool = False) -> int:
     """Bytes a linear call must move at least once: weights, x, y (bf16), bias."""
-    return weight_bytes(n, k, group, sym16) + m * k * 2 + m * n * 2 + (n * 4 if has_bias else 0)
+    return weight_bytes(n, k, group, sym16, mx) + m * k * 2 + m * n * 2 + (n * 4 if has_bias else 0)
 
 
 def kernel_source_hash() -> str:
@@ -211,9 +213,10 @@ def measure_prefill(torch, woq, reps: int = 5, calls: int = 20):
 
 
 def measure_configs(torch, woq, reps: int = 40, pool_bytes: int = 1 << 30, cases=None,
-                    sym16: bool = False):
+                    sym16: bool = False, mx: bool = False):
     """Per-launch time of every small-M sweep and act-order configuration (or of
-    `cases`; with sym16, over signed codes with float16 scales).
+    `cases`; with sym16, over signed codes with float16 scales; with mx, over
+    MXFP4 weights).
 
     Weights are random bytes in the Int4GroupLinear layout (timing does not
     depend on the values); each configuration rotates over enough copies
@@ -230,13 +233,19 @@ def measure_configs(torch, woq, reps: int = 40, pool_bytes: int = 1 << 30, cases
     pools = {}
     for case in (cases if cases is not None else (*SWEEP, *ACTORDER)):
         key = (case.n, case.k, case.group)
-        wb = weight_bytes(case.n, case.k, case.group, sym16)
+        wb = weight_bytes(case.n, case.k, case.group, sym16, mx)
         if key not in pools:
             pools.clear()
             torch.cuda.empty_cache()
             copies = max(2, -(-pool_bytes // wb))
             ng = case.k // case.group
-            if sym16:
+            if mx:
+                pools[key] = [
+                    (torch.randint(0, 256, (case.n, case.k // 2), generator=gen, device=dev, dtype=torch.uint8),
+                     torch.randint(118, 124, (case.n, case.k // 32), generator=gen, device=dev, dtype=torch.uint8),
+                     None)
+                    for _ in range(copies)]
+            elif sym16:
                 pools[key] = [
                     (torch.randint(0, 256, (case.n, case.k // 2), generator=gen, device=dev, dtype=torch.uint8),
                      torch.rand((case.n, ng), generator=gen, device=dev).mul_(0.01).add_(1e-3).half(), None)
@@ -258,7 +267,9 @@ def measure_configs(torch, woq, reps: int = 40, pool_bytes: int = 1 << 30, cases
 
         def call(i):
             p, sc, z = pool[i % len(pool)]
-            if sym16:
+            if mx:
+                woq.linear_mxfp4(x, p, sc, bias=bias, out=y, workspace=ws if ws_bytes else None)
+            elif sym16:
                 woq.linear_int4_sym(x, p, sc, bias=bias, order=order, group=case.group, out=y,
                                     workspace=ws if ws_bytes else None)
             else:
@@ -286,7 +297,7 @@ def measure_configs(torch, woq, reps: int = 40, pool_bytes: int = 1 << 30, cases
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) * 1e-3 / reps
         flops = 2.0 * case.m * case.n * case.k
-        ab = algorithmic_bytes(case.m, case.n, case.k, case.has_bias, case.group, sym16) + (
+        ab = algorithmic_bytes(case.m, case.n, case.k, case.has_bias, case.group, sym16, mx) + (
             case.k * 4 if case.act_order else 0)
         out.append(dict(name=case.name, m=case.m, n=case.n, k=case.k, group=case.group,
                         us=round(t * 1e6, 2), weight_GBps=round(wb / t / 1e9, 1),
@@ -549,12 +560,16 @@ def main():
 
     prefill = None if args.no_prefill else measure_prefill(torch, woq)
     configs = None if args.no_configs else measure_configs(torch, woq)
-    sym16 = None
+    sym16 = mxfp4 = None
     if not args.no_configs:
         from workloads import SYM16
         sym16 = dict(
             note="signed int4 codes with float16 scales, no zero point (woq_linear_int4_sym_f16)",
             configs=measure_configs(torch, woq, cases=SYM16, sym16=True))
+        from workloads import MXFP4
+        mxfp4 = dict(
+            note="MXFP4: E2M1 codes, one E8M0 scale per block of 32 (woq_linear_mxfp4)",
+            configs=measure_configs(torch, woq, cases=MXFP4, mx=True))
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     line = dict(
@@ -568,7 +583,7 @@ def main():
                     graph=not args.no_graph, accumulate="f32",
                     tokens_per_s_linears_only=round(1.0 / (ms_per_step * 1e-3), 1) if args.layers == 32 else None),
         roofline=roofline, grouped=grouped, prepared=prepared, prefill=prefill, configs=configs,
-        sym16=sym16,
+        sym16=sym16, mxfp4=mxfp4,
         cpu_baseline=cpu,
     )
     print(json.dumps(line), flush=True)

@@ -330,6 +330,61 @@ int32_t woq_linear_int4_sym_f16_prepared(const void* x_bf16, int64_t m, const ui
                                          size_t workspace_bytes, void* stream);
 
 /*
+ * ---- MXFP4 ----
+ * linnet "Quantization" (std.quant table, dequantize_mxfp4: E2M1 values in
+ * blocks of 32, one E8M0 scale byte a block) and tinyllm L8.5 section 2
+ * ("MXFP4": a power-of-two scale X per block, elements 0, 0.5, 1, 1.5, 2, 3, 4, 6
+ * times X, values above 6X saturate).  Layout: blocks [n, k/32, 16] uint8, two
+ * E2M1 codes a byte (bit 3 the sign), the even input in the low nibble; scales
+ * [n, k/32] uint8, X = 2^(e - 127).  W_hat = value(code) * X.
+ */
+
+/*
+ * Quantizer.  SYNC.  Per block of 32: X = 2^(floor(log2 amax) - 2) (the OCP
+ * Microscaling rule; 2 is the largest E2M1 exponent), e = clamp(floor(log2 amax)
+ * - 2 + 127, 0, 254), e = 0 for a zero block; each element w / X (exact) rounds
+ * to the nearest E2M1 magnitude, ties to the even code, saturating at 6, with the
+ * sign of w (a negative value that rounds to 0 gives code 8).
+ * Arguments: w [n, k] float32 (device, 4-byte aligned), k a multiple of 32;
+ *   outputs codes [n, k] uint8 (0..15, pack them with woq_pack_uint4), scales
+ *   [n, k/32] uint8 (device).
+ * Errors: WOQ_EINVAL, WOQ_EGROUP (k not a multiple of 32), WOQ_ENONFINITE,
+ *   WOQ_EUNSUPPORTED (n*k >= 2^40), WOQ_EHIP.
+ */
+int32_t woq_quantize_mxfp4(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
+                           void* stream);
+
+/*
+ * Dequantize W_hat = value(code) * 2^(e - 127), exact in float32 for the scales
+ * the quantizer writes; with out_dtype = WOQ_BF16 that float32 is rounded to
+ * bfloat16, ties to even.  ASYNC.
+ * Arguments: blocks [n, k/2] uint8, scales [n, k/32] uint8 (device); k a
+ *   multiple of 32; w_hat [n, k] of out_dtype (device).
+ * Errors: WOQ_EINVAL, WOQ_EGROUP, WOQ_EUNSUPPORTED (n*k >= 2^40), WOQ_EHIP.
+ */
+int32_t woq_dequantize_mxfp4(const uint8_t* blocks, const uint8_t* scales, int64_t n, int64_t k,
+                             int32_t out_dtype, void* w_hat, void* stream);
+
+/*
+ * Linear layer over MXFP4 weights: y[m, n] = sum_k x[m, k] * W_hat[n, k] + bias[n].
+ * x bfloat16, float32 accumulation.  Each lane's 16 weight bytes are one block,
+ * converted with v_cvt_scalef32_pk_bf16_fp4 into bf16 values already multiplied
+ * by the block's scale (exact: a power of two times a 2-bit significand), so
+ * the products go straight into the MFMA accumulators: m <= 32 on the small-M
+ * kernel, larger m on the tiled GEMM (with its activation pre-pass; workspace as
+ * woq_linear_workspace_bytes(m, n, k, 32, 0)).  A block scale of 255 (not a
+ * number in E8M0) gives NaN outputs.  ASYNC.
+ * Arguments: x_bf16 [m, k] bfloat16 (device, 16-byte aligned); blocks [n, k/2]
+ *   uint8 (device, 16-byte aligned); scales [n, k/32] uint8 (device, 16-byte
+ *   aligned); bias [n] float32 or NULL; k a multiple of 32; y_dtype, y,
+ *   workspace as woq_linear_int4_groups.
+ * Errors: as woq_linear_int4_groups with group 32.
+ */
+int32_t woq_linear_mxfp4(const void* x_bf16, int64_t m, const uint8_t* blocks, const uint8_t* scales,
+                         const float* bias, int64_t n, int64_t k, int32_t y_dtype, void* y,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Describe the kernel plan the linear calls use for these sizes: the path
  * (decode GEMV for m <= 4, small-M MFMA for m <= 32, tiled MFMA GEMM above),
  * tiles, waves and whether an input pre-pass runs.  Writes a NUL-terminated

@@ -235,3 +235,18 @@ def test_signed_format_entry_points_validate_first(lib):
                                           fake, None, 0, None)) == "WOQ_EUNSUPPORTED"
     assert st(lib.woq_linear_int4_sym_f16_prepared(fake, 1, fake, None, None, None, 64, 256, 32,
                                                    1, fake, None, 0, None)) == "WOQ_EINVAL"
+
+
+def test_mxfp4_entry_points_validate_first(lib):
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    st = lambda rc: woq.STATUS[rc]
+    assert st(lib.woq_quantize_mxfp4(fake, 4, 48, fake, fake, None)) == "WOQ_EGROUP"
+    assert st(lib.woq_quantize_mxfp4(None, 4, 64, fake, fake, None)) == "WOQ_EINVAL"
+    assert st(lib.woq_quantize_mxfp4(fake, 0, 64, None, None, None)) == "WOQ_OK"
+    assert st(lib.woq_dequantize_mxfp4(fake, fake, 4, 64, 9, fake, None)) == "WOQ_EINVAL"
+    assert st(lib.woq_dequantize_mxfp4(fake, fake, 4, 40, 0, fake, None)) == "WOQ_EGROUP"
+    assert st(lib.woq_linear_mxfp4(fake, 1, fake, None, None, 64, 256, 1, fake, None, 0, None)) == "WOQ_EINVAL"
+    assert st(lib.woq_linear_mxfp4(fake, 1, fake, odd, None, 64, 256, 1, fake, None, 0, None)) == "WOQ_EALIGN"
+    assert st(lib.woq_linear_mxfp4(fake, 1, fake, fake, None, 64, 48, 1, fake, None, 0, None)) == "WOQ_EGROUP"
+    assert st(lib.woq_linear_mxfp4(fake, 0, fake, fake, None, 64, 256, 1, fake, None, 0, None)) == "WOQ_OK"

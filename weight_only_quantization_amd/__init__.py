@@ -42,6 +42,9 @@ __all__ = [
     "unpack_int4",
     "dequantize_int4_sym",
     "linear_int4_sym",
+    "quantize_mxfp4",
+    "dequantize_mxfp4",
+    "linear_mxfp4",
     "STATUS",
 ]
 
@@ -104,6 +107,10 @@ def load() -> ctypes.CDLL:
                                             c_i32, c_p, c_p, c_sz, c_p]),
         "woq_linear_int4_sym_f16_prepared": (c_i32, [c_p, c_i64, c_p, c_p, c_p, c_p, c_i64, c_i64,
                                                      c_i32, c_i32, c_p, c_p, c_sz, c_p]),
+        "woq_quantize_mxfp4": (c_i32, [c_p, c_i64, c_i64, c_p, c_p, c_p]),
+        "woq_dequantize_mxfp4": (c_i32, [c_p, c_p, c_i64, c_i64, c_i32, c_p, c_p]),
+        "woq_linear_mxfp4": (c_i32, [c_p, c_i64, c_p, c_p, c_p, c_i64, c_i64, c_i32, c_p, c_p, c_sz,
+                                     c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -475,3 +482,80 @@ def linear_int4_groups_grouped(x: torch.Tensor, mats, prepared: bool = False,
         _ptr(workspace) if need else None, workspace.numel() if need else 0, _stream()),
         "linear_int4_groups_grouped")
     return outs
+
+
+# ---------------------------------------------------------------------------
+# MXFP4: E2M1 codes in blocks of 32 with an E8M0 scale byte a block
+# ---------------------------------------------------------------------------
+
+def quantize_mxfp4(w: torch.Tensor):
+    """MXFP4 quantizer on the GPU.  w: float32 [N, K], K a multiple of 32.
+
+    Returns (codes uint8 [N, K] 0..15, scales uint8 [N, K/32] E8M0); pack the
+    codes with :func:`pack_uint4`.  Synchronizes the current stream.
+    """
+    lib = load()
+    _need(w, torch.float32, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    n, k = w.shape
+    codes = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n, k // 32), dtype=torch.uint8, device=w.device)
+    _check(lib.woq_quantize_mxfp4(_ptr(w), n, k, _ptr(codes), _ptr(scales), _stream()), "quantize_mxfp4")
+    return codes, scales
+
+
+def dequantize_mxfp4(blocks: torch.Tensor, scales: torch.Tensor,
+                     out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """E2M1 value * 2^(e - 127) -> [N, K] float32 or bfloat16 (K = 32 * scales.shape[1])."""
+    lib = load()
+    _need(blocks, torch.uint8, "blocks")
+    _need(scales, torch.uint8, "scales")
+    n, k = scales.shape[0], 32 * scales.shape[1]
+    if blocks.numel() != n * k // 2:
+        raise ValueError("blocks must hold N * K / 2 bytes")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    out = torch.empty((n, k), dtype=out_dtype, device=blocks.device)
+    _check(lib.woq_dequantize_mxfp4(_ptr(blocks), _ptr(scales), n, k,
+                                    F32 if out_dtype == torch.float32 else BF16, _ptr(out), _stream()),
+           "dequantize_mxfp4")
+    return out
+
+
+def linear_mxfp4(x: torch.Tensor, blocks: torch.Tensor, scales: torch.Tensor,
+                 bias: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+                 out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = x . dequant(W)^T + bias over MXFP4 weights.
+
+    x: bfloat16 [M, K]; blocks uint8 [N, K/2] (or [N, K/32, 16]); scales uint8
+    [N, K/32]; bias float32 [N] or None.  Asynchronous on the current stream.
+    """
+    lib = load()
+    _need(x, torch.bfloat16, "x")
+    _need(blocks, torch.uint8, "blocks")
+    _need(scales, torch.uint8, "scales")
+    if bias is not None:
+        _need(bias, torch.float32, "bias")
+    if x.dim() != 2 or scales.dim() != 2:
+        raise ValueError("x must be [M, K] and scales [N, K/32]")
+    m, k = x.shape
+    n = scales.shape[0]
+    if scales.shape[1] * 32 != k or blocks.numel() != n * k // 2:
+        raise ValueError("blocks, scales and x disagree on K")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    else:
+        _need(out, out_dtype, "out")
+    need = int(lib.woq_linear_workspace_bytes(m, n, k, 32, 0))
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsb = workspace.numel() if (need and workspace is not None) else 0
+    _check(lib.woq_linear_mxfp4(_ptr(x), m, _ptr(blocks), _ptr(scales), _ptr(bias), n, k,
+                                F32 if out_dtype == torch.float32 else BF16, _ptr(out),
+                                _ptr(workspace) if need else None, wsb, _stream()), "linear_mxfp4")
+    return out
+

@@ -341,6 +341,39 @@ int32_t woq_dequantize_int4_sym_f16(const uint8_t* packed, const uint16_t* scale
                                reinterpret_cast<hipStream_t>(stream));
 }
 
+int32_t woq_quantize_mxfp4(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
+                           void* stream) {
+  if (n < 0 || k < 0) return WOQ_EINVAL;
+  if (k % 32) return WOQ_EGROUP;
+  if (n * k >= kMaxElems) return WOQ_EUNSUPPORTED;
+  if (n == 0 || k == 0) return WOQ_OK;
+  if (!w || !codes || !scales) return WOQ_EINVAL;
+  if (!aligned(w, 4)) return WOQ_EALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint32_t* flag = nullptr;
+  WOQ_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&flag), sizeof(uint32_t), s));
+  int32_t st = hip_status(hipMemsetAsync(flag, 0, sizeof(uint32_t), s));
+  if (st == WOQ_OK) st = launch_quantize_mx(w, n, k, codes, scales, flag, s);
+  uint32_t hflag = 0;
+  if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(&hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+  if (st == WOQ_OK) st = hip_status(hipStreamSynchronize(s));
+  (void)hipFreeAsync(flag, s);
+  if (st != WOQ_OK) return st;
+  return hflag ? WOQ_ENONFINITE : WOQ_OK;
+}
+
+int32_t woq_dequantize_mxfp4(const uint8_t* blocks, const uint8_t* scales, int64_t n, int64_t k,
+                             int32_t out_dtype, void* w_hat, void* stream) {
+  if (n < 0 || k < 0) return WOQ_EINVAL;
+  if (out_dtype != WOQ_F32 && out_dtype != WOQ_BF16) return WOQ_EINVAL;
+  if (k % 32) return WOQ_EGROUP;
+  if (n * k >= kMaxElems) return WOQ_EUNSUPPORTED;
+  if (n == 0 || k == 0) return WOQ_OK;
+  if (!blocks || !scales || !w_hat) return WOQ_EINVAL;
+  if (!aligned(w_hat, out_dtype == WOQ_F32 ? 4 : 2)) return WOQ_EALIGN;
+  return launch_dequantize_mx(blocks, scales, n, k, out_dtype, w_hat, reinterpret_cast<hipStream_t>(stream));
+}
+
 size_t woq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group,
                                   int32_t has_order) {
   if (check_linear_shape(m, n, k, group) != WOQ_OK) return 0;
@@ -358,8 +391,9 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
                     const uint8_t* zero, const float* bias, const int32_t* order, int64_t n,
                     int64_t k, int32_t group, int32_t y_dtype, void* y, void* workspace,
                     size_t workspace_bytes, void* stream, int32_t prepared,
-                    const uint16_t* scale16 = nullptr) {
+                    const uint16_t* scale16 = nullptr, const uint8_t* scale8 = nullptr) {
   const bool sym16 = scale16 != nullptr;
+  const bool mx = scale8 != nullptr;
   int32_t st = check_linear_shape(m, n, k, group);
   if (st != WOQ_OK) return st;
   if (y_dtype != WOQ_F32 && y_dtype != WOQ_BF16) return WOQ_EINVAL;
@@ -369,9 +403,11 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
   if (bias && !aligned(bias, 4)) return WOQ_EALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (k == 0) return launch_fill_bias(bias, (int32_t)m, (int32_t)n, y_dtype == WOQ_BF16, y, s);
-  if (!x_bf16 || !packed || (!sym16 && (!scale || !zero))) return WOQ_EINVAL;
+  if (!x_bf16 || !packed || (!sym16 && !mx && (!scale || !zero))) return WOQ_EINVAL;
   if (!aligned(x_bf16, 16) || !aligned(packed, 16)) return WOQ_EALIGN;
-  if (sym16 ? !aligned(scale16, 16) : (!aligned(scale, 16) || !aligned(zero, 16))) return WOQ_EALIGN;
+  if (mx ? !aligned(scale8, 16)
+         : sym16 ? !aligned(scale16, 16) : (!aligned(scale, 16) || !aligned(zero, 16)))
+    return WOQ_EALIGN;
   const bool has_order = order != nullptr;
   if (has_order && !aligned(order, 16)) return WOQ_EALIGN;
   const LinearPlan plan = linear_plan(m, n, k, group, has_order);
@@ -398,6 +434,8 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
   a.prepared = prepared;
   a.sym16 = sym16 ? 1 : 0;
   a.scale16 = scale16;
+  a.mx = mx ? 1 : 0;
+  a.scale8 = scale8;
   if (plan.path == 1) {
     if (has_order) {
       uint16_t* xg = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
@@ -420,7 +458,8 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
   uint16_t* xg = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
   float* xs = reinterpret_cast<float*>(wsb + ws.xs_off);
   a.kpad = (a.k + 127) / 128 * 128;
-  st = launch_prep(a.x, order, a.m, a.k, a.kpad, group, 1, xg, xs, plan.mpad, s);
+  // MXFP4 weights decode in natural input order and need no piece sums
+  st = launch_prep(a.x, order, a.m, a.k, a.kpad, group, mx ? 0 : 1, xg, mx ? nullptr : xs, plan.mpad, s);
   if (st != WOQ_OK) return st;
   a.x = xg;
   a.xs = xs;
@@ -457,6 +496,14 @@ int32_t woq_linear_int4_sym_f16_prepared(const void* x_bf16, int64_t m, const ui
   if (k > 0 && m > 0 && n > 0 && !scale16) return WOQ_EINVAL;
   return linear_impl(x_bf16, m, prepared, nullptr, nullptr, bias, order, n, k, group, y_dtype, y,
                      workspace, workspace_bytes, stream, 1, scale16);
+}
+
+int32_t woq_linear_mxfp4(const void* x_bf16, int64_t m, const uint8_t* blocks, const uint8_t* scales,
+                         const float* bias, int64_t n, int64_t k, int32_t y_dtype, void* y,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (k > 0 && m > 0 && n > 0 && !scales) return WOQ_EINVAL;
+  return linear_impl(x_bf16, m, blocks, nullptr, nullptr, bias, nullptr, n, k, 32, y_dtype, y,
+                     workspace, workspace_bytes, stream, 0, nullptr, scales);
 }
 
 int32_t woq_linear_int4_groups_prepared(const void* x_bf16, int64_t m, const uint8_t* prepared,

@@ -363,6 +363,74 @@ __global__ __launch_bounds__(kThreads) void dequant_s16_kernel(
   }
 }
 
+// ---- MXFP4: E2M1 codes in blocks of 32 with an E8M0 scale ----
+// X = 2^(floor(log2 amax) - 2), stored as e = clamp(floor(log2 amax) - 2 + 127,
+// 0, 254) (0 for a zero block); codes: w / X (exact) rounded to the nearest of
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the even code, saturating at 6, sign in
+// bit 3.  One thread per block; flag bit 0: a non-finite weight.
+__device__ __forceinline__ float e8m0_value(uint32_t e) {
+  return e == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23);   // 2^(e - 127)
+}
+
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t mag = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                     : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return mag | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+__global__ __launch_bounds__(kThreads) void quantize_mx_kernel(const float* __restrict__ w, int64_t nblocks,
+                                                               uint8_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ scales,
+                                                               uint32_t* __restrict__ flag) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t bi = (int64_t)blockIdx.x * kThreads + threadIdx.x; bi < nblocks; bi += stride) {
+    const float* g = w + bi * 32;
+    bool bad = false;
+    float am = 0.0f;
+    for (int e = 0; e < 32; ++e) {
+      bad = bad || !finite_f32(g[e]);
+      am = fmaxf(am, fabsf(g[e]));
+    }
+    if (bad) {
+      atomicOr(flag, 1u);
+      continue;
+    }
+    const int ex = (int)((__float_as_uint(am) >> 23) & 0xFFu);   // biased exponent; 0 for zero and subnormals
+    const uint32_t e = (uint32_t)min(max(ex - 2, 0), 254);
+    const float inv = __uint_as_float((uint32_t)(254 - e) << 23);  // 1 / X = 2^(127 - e), exact
+    uint8_t* co = codes + bi * 32;
+    for (int k = 0; k < 32; ++k) co[k] = (uint8_t)e2m1_code(g[k] * inv);
+    scales[bi] = (uint8_t)e;
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void dequant_mx_kernel(const uint8_t* __restrict__ blocks,
+                                                              const uint8_t* __restrict__ scales,
+                                                              int64_t nbytes, void* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nbytes; i += stride) {
+    const float x = e8m0_value(scales[i / 16]);
+    const uint32_t b = blocks[i];
+    auto val = [&](uint32_t c) {   // E2M1: exponent bits 2..1, mantissa bit 0 (subnormal at exponent 0)
+      const uint32_t ee = (c >> 1) & 3u, mm = c & 1u;
+      const float m = ee == 0 ? 0.5f * (float)mm : (float)(1u << (ee - 1u)) * (mm ? 1.5f : 1.0f);
+      return ((c & 8u) ? -m : m) * x;
+    };
+    const float v0 = val(b & 15u), v1 = val(b >> 4);
+    if (BF16) {
+      uint16_t* o = reinterpret_cast<uint16_t*>(out);
+      o[2 * i] = bf16_bits_rne(v0);
+      o[2 * i + 1] = bf16_bits_rne(v1);
+    } else {
+      float* o = reinterpret_cast<float*>(out);
+      o[2 * i] = v0;
+      o[2 * i + 1] = v1;
+    }
+  }
+}
+
 unsigned grid_for(int64_t items) {
   const int64_t blocks = (items + kThreads - 1) / kThreads;
   return (unsigned)(blocks < 1 ? 1 : (blocks > 65536 ? 65536 : blocks));
@@ -537,6 +605,28 @@ int32_t launch_dequantize_s16(const uint8_t* packed, const uint16_t* scale16, in
   else
     hipLaunchKernelGGL(dequant_s16_kernel<false>, dim3(grid_for(nbytes)), dim3(kThreads), 0, stream,
                        packed, scale16, nbytes, k / 2, group, w_hat);
+  return hip_status(hipGetLastError());
+}
+
+int32_t launch_quantize_mx(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
+                           uint32_t* flag, hipStream_t stream) {
+  const int64_t nblocks = n * (k / 32);
+  if (nblocks == 0) return WOQ_OK;
+  hipLaunchKernelGGL(quantize_mx_kernel, dim3(grid_for(nblocks)), dim3(kThreads), 0, stream,
+                     w, nblocks, codes, scales, flag);
+  return hip_status(hipGetLastError());
+}
+
+int32_t launch_dequantize_mx(const uint8_t* blocks, const uint8_t* scales, int64_t n, int64_t k,
+                             int32_t out_dtype, void* w_hat, hipStream_t stream) {
+  const int64_t nbytes = n * (k / 2);
+  if (nbytes == 0) return WOQ_OK;
+  if (out_dtype == WOQ_BF16)
+    hipLaunchKernelGGL(dequant_mx_kernel<true>, dim3(grid_for(nbytes)), dim3(kThreads), 0, stream,
+                       blocks, scales, nbytes, w_hat);
+  else
+    hipLaunchKernelGGL(dequant_mx_kernel<false>, dim3(grid_for(nbytes)), dim3(kThreads), 0, stream,
+                       blocks, scales, nbytes, w_hat);
   return hip_status(hipGetLastError());
 }
 

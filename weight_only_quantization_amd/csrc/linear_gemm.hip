@@ -91,10 +91,11 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
 
 // sz[g][c] = (scale[c][g], -(128 + zero[c][g])) for c < n, zeros up to npad.
 // With signed codes the scale is float16 and the zero point 8 (the codes are
-// read as v ^ 8).
+// read as v ^ 8); for MXFP4 (fmt 2) the entry is (2^(e - 127), 0) of the E8M0
+// scale byte e.
 __global__ __launch_bounds__(256) void sz_prep_kernel(const void* __restrict__ scale,
                                                       const uint8_t* __restrict__ zero, int32_t n,
-                                                      int32_t ngroups, int32_t npad, int32_t sym16,
+                                                      int32_t ngroups, int32_t npad, int32_t fmt,
                                                       f32x2_t* __restrict__ sz) {
   const int64_t total = (int64_t)ngroups * npad;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -104,9 +105,12 @@ __global__ __launch_bounds__(256) void sz_prep_kernel(const void* __restrict__ s
     f32x2_t v = f32x2_t{0.f, 0.f};
     if (c < n) {
       const int64_t e = (int64_t)c * ngroups + g;
-      if (sym16)
+      if (fmt == kFmtMX) {
+        const uint32_t eb = static_cast<const uint8_t*>(scale)[e];
+        v = f32x2_t{__uint_as_float(eb == 0 ? 0x00400000u : eb << 23), 0.f};
+      } else if (fmt == kFmtS16) {
         v = f32x2_t{(float)static_cast<const _Float16*>(scale)[e], -(kNibOffset + 8.0f)};
-      else
+      } else
         v = f32x2_t{static_cast<const float*>(scale)[e], -(kNibOffset + (float)zero[e])};
     }
     sz[t] = v;
@@ -186,13 +190,16 @@ struct GemmParams {
   int32_t prepared;       // 1: packed holds prepared 1 KB blocks
   int32_t vec_out;        // 1: y is 16-byte aligned and its rows are whole 16-byte chunks
   int32_t sym16;          // 1: signed two's complement codes (float16 scales in the table)
+  int32_t mx;             // 1: MXFP4 (E2M1 codes; the table holds (2^(e - 127), 0) per block)
 };
 
 // Tl: workgroup tile; GB: 32-input blocks per group piece inside a step (1, 2
 // or 4); S: LDS stages; S16: signed two's complement codes (read as v ^ 8,
 // one XOR per dword; the scale table already holds zero point 8).
-template <class Tl, int GB, int S, bool S16>
+template <class Tl, int GB, int S, int FMT>
 __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
+  constexpr bool S16 = FMT == kFmtS16, MX = FMT == kFmtMX;
+  static_assert(!MX || GB == 1, "MXFP4 blocks hold 32 inputs");
   constexpr int MT = Tl::MT, NT = Tl::NT, kWaves = Tl::kWaves;
   constexpr int BM = Tl::BM, BN = Tl::BN;
   constexpr int kABytes = Tl::kABytes, kBBytes = Tl::kBBytes;
@@ -235,7 +242,8 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t rb =
       prep ? rsrc(p.packed + (int64_t)(n0 / 16) * nsteps * 1024, (uint32_t)(ptiles * nsteps) * 1024u)
            : rsrc(p.packed + (int64_t)n0 * row_bytes, (uint32_t)min(BN, N - n0) * row_bytes);
-  const __amdgpu_buffer_rsrc_t rx = rsrc(p.xs, (uint32_t)((int64_t)p.npieces * p.mpad * 4));
+  // (MXFP4 needs no piece sums: a zero-sized descriptor makes those loads read zero)
+  const __amdgpu_buffer_rsrc_t rx = rsrc(p.xs, MX ? 0u : (uint32_t)((int64_t)p.npieces * p.mpad * 4));
   const __amdgpu_buffer_rsrc_t rz = rsrc(p.sz, (uint32_t)((int64_t)p.ngroups * p.npad * 8));
 
   // ---- one stage of loads: this wave's share, the same count for every wave --
@@ -380,7 +388,7 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
         u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + kABytes + row * 64 + 16 * c);
         if constexpr (S16) v ^= u32x4_t{kSignFlip, kSignFlip, kSignFlip, kSignFlip};
         bd[L][nt][0] = v[0]; bd[L][nt][1] = v[1]; bd[L][nt][2] = v[2]; bd[L][nt][3] = v[3];
-        if constexpr (GB == 1) {
+        if constexpr (GB == 1 && !MX) {
           // Regroup for 32-input groups: the lower lanes keep their inputs
           // 0..15 and take the upper lanes' 32..47; the upper lanes end with
           // 16..31 and 48..63.  Dwords 0, 1 then lie in the unit's first
@@ -394,7 +402,7 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
     auto load_af = [&](int blk, bf16x8_t (&af)[MT]) {
       const int L = blk >> 2, b = blk & 3;
       // 8-input chunk of the activations that matches dword b of this half
-      const int cin = GB == 1 ? 4 * (b >> 1) + 2 * h + (b & 1) : 4 * h + b;
+      const int cin = GB == 1 && !MX ? 4 * (b >> 1) + 2 * h + (b & 1) : 4 * h + b;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int row = arow[mt];
@@ -413,6 +421,34 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
       for (int r = 0; r < 16; ++r) acc[mt][nt][r] = fmaf(fold_sv[nt], cg[mt][nt][r], acc[mt][nt][r]);
     };
     bf16x8_t afc[MT], afn[MT];
+    if constexpr (MX) {
+      // MXFP4: lane half h of 64-input unit L holds block 2L + h of its row,
+      // converted with that block's scale into exact bf16 weights; the MFMAs
+      // accumulate straight into the outputs (no fold, no zero point).
+      float xsc[2][NT];
+#pragma unroll
+      for (int L = 0; L < 2; ++L)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          xsc[L][nt] = *reinterpret_cast<const float*>(st + kSzOff + (2 * L + h) * kSzStride + brow[nt] * 8);
+      __builtin_amdgcn_s_setprio(1);
+      load_af(0, afc);
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) {
+        const int L = blk >> 2, b = blk & 3;
+        if (blk + 1 < 8) load_af(blk + 1, afn);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const bf16x8_t bf = fp4x8_to_bf16(bd[L][nt][b], xsc[L][nt]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt][nt] = mfma32(afc[mt], bf, acc[mt][nt]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) afc[mt] = afn[mt];
+      }
+      __builtin_amdgcn_s_setprio(0);
+      return;
+    }
     // The two waves of a SIMD leave the barrier together; raising this wave's
     // priority for its MFMA phase lets one of them run ahead, so that one
     // folds (VALU) while the other keeps the matrix unit busy.
@@ -562,9 +598,9 @@ size_t gemm_lds_bytes() {
   return (size_t)S * (Tl::kABytes + Tl::kBBytes + NP * 1024 + NP * Tl::kSzParts * 1024) + kJunk;
 }
 
-template <class Tl, int GB, int S, bool S16>
+template <class Tl, int GB, int S, int FMT>
 int32_t launch_gemm_t(GemmParams gp, hipStream_t stream) {
-  auto kern = gemm_kernel<Tl, GB, S, S16>;
+  auto kern = gemm_kernel<Tl, GB, S, FMT>;
   const size_t lds = gemm_lds_bytes<Tl, GB, S>();
   static bool raised = false;   // raise the dynamic-LDS limit once per instantiation
   if (!raised) {
@@ -590,19 +626,20 @@ constexpr int gemm_stages() {
   return 3 * stage + kJunk <= 160 * 1024 ? 3 : 2;
 }
 
-template <class Tl, bool S16>
+template <class Tl, int FMT>
 int32_t launch_gemm_s(const GemmParams& gp, int gb, hipStream_t stream) {
   switch (gb) {
-    case 1: return launch_gemm_t<Tl, 1, gemm_stages<Tl, 1>(), S16>(gp, stream);
-    case 2: return launch_gemm_t<Tl, 2, gemm_stages<Tl, 2>(), S16>(gp, stream);
-    case 4: return launch_gemm_t<Tl, 4, gemm_stages<Tl, 4>(), S16>(gp, stream);
+    case 1: return launch_gemm_t<Tl, 1, gemm_stages<Tl, 1>(), FMT>(gp, stream);
+    case 2: return launch_gemm_t<Tl, 2, gemm_stages<Tl, 2>(), FMT>(gp, stream);
+    case 4: return launch_gemm_t<Tl, 4, gemm_stages<Tl, 4>(), FMT>(gp, stream);
     default: return WOQ_EUNSUPPORTED;
   }
 }
 
 template <class Tl>
 int32_t launch_gemm_gb(const GemmParams& gp, int gb, hipStream_t stream) {
-  return gp.sym16 ? launch_gemm_s<Tl, true>(gp, gb, stream) : launch_gemm_s<Tl, false>(gp, gb, stream);
+  if (gp.mx) return gb == 1 ? launch_gemm_t<Tl, 1, gemm_stages<Tl, 1>(), kFmtMX>(gp, stream) : WOQ_EUNSUPPORTED;
+  return gp.sym16 ? launch_gemm_s<Tl, kFmtS16>(gp, gb, stream) : launch_gemm_s<Tl, kFmtU4>(gp, gb, stream);
 }
 
 }  // namespace
@@ -648,8 +685,10 @@ int32_t launch_gemm(const LinearArgs& a, const LinearPlan& pl, void* sz_ws, hipS
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL(sz_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       a.sym16 ? static_cast<const void*>(a.scale16) : static_cast<const void*>(a.scale),
-                       a.zero, a.n, ngroups, npad, a.sym16, static_cast<f32x2_t*>(sz_ws));
+                       a.mx ? static_cast<const void*>(a.scale8)
+                            : a.sym16 ? static_cast<const void*>(a.scale16) : static_cast<const void*>(a.scale),
+                       a.zero, a.n, ngroups, npad, a.mx ? kFmtMX : a.sym16 ? kFmtS16 : kFmtU4,
+                       static_cast<f32x2_t*>(sz_ws));
     const int32_t st = hip_status(hipGetLastError());
     if (st != WOQ_OK) return st;
   }
@@ -658,7 +697,7 @@ int32_t launch_gemm(const LinearArgs& a, const LinearPlan& pl, void* sz_ws, hipS
                       a.m, a.n, a.k, a.kpad, a.group, a.y_bf16, a.mpad, npad, ngroups, a.k / piece,
                       0, 0, 0, a.n, a.prepared,
                       (reinterpret_cast<uintptr_t>(a.y) % 16 == 0 && a.n % (a.y_bf16 ? 8 : 4) == 0) ? 1 : 0,
-                      a.sym16};
+                      a.sym16, a.mx};
   // Tile by the number of activation rows: small M takes narrow tiles so the
   // grid still covers the chip.
   switch (pl.bm) {

@@ -120,19 +120,25 @@ __device__ __forceinline__ float lane_group_sum(float v) {
 
 // GB: 32-wide blocks per group piece inside a step (1, 2 or 4); FR:
 // accumulator rows folded and stored (1 when m == 1, else 4); CC: the most
-// steps a wave owns (4, 8 or 16); PF: steps of weight loads in flight; S16:
-// signed two's complement codes with float16 scales and no zero point
-// (tinyllm L8.5, "int4 per group").  A signed nibble v is the unsigned code
-// v ^ 8 with zero point 8, so those weights go through the same arithmetic
-// after one XOR per dword.
-template <int GB, int FR, int CC, int PF, bool S16>
+// steps a wave owns (4, 8 or 16); PF: steps of weight loads in flight; FMT:
+// the weight format.  kFmtS16: signed two's complement codes with float16
+// scales and no zero point (tinyllm L8.5, "int4 per group"); a signed nibble v
+// is the unsigned code v ^ 8 with zero point 8, so those weights go through the
+// same arithmetic after one XOR per dword.  kFmtMX: MXFP4 (GB = 1: blocks of
+// 32 inputs, one E8M0 scale each); a lane's 16 loaded bytes are one block,
+// converted by v_cvt_scalef32_pk_bf16_fp4 into bf16 values already multiplied
+// by the block's power-of-two scale (exact), so the MFMAs accumulate straight
+// into the outputs with the activations in natural order and no fold.
+template <int GB, int FR, int CC, int PF, int FMT>
 __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
+  constexpr bool S16 = FMT == kFmtS16, MX = FMT == kFmtMX;
+  static_assert(!MX || GB == 1, "MXFP4 blocks hold 32 inputs");
   constexpr int NP = 4 / GB;              // group pieces per step
   constexpr int XL = FR == 1 ? CC / 4 : 4;                        // activation loads per batch
   constexpr int SZB = CC * NP / kSzPerBatch > 1 ? CC * NP / kSzPerBatch : 1;
   constexpr int kSzEntries = SZB * kSzPerBatch;                   // staged entries per row
   constexpr int kPieceLanes = 4 * GB;     // 8-input chunks per piece
-  constexpr bool kTranspose = GB < 4;
+  constexpr bool kTranspose = GB < 4 && !MX;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int W = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6));
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -162,12 +168,12 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   const __amdgpu_buffer_rsrc_t rb =
       prep ? rsrc(pr.packed + (int64_t)tile * p.nsteps * 1024, (uint32_t)p.nsteps * 1024u)
            : rsrc(pr.packed + (int64_t)row0 * row_bytes, (uint32_t)rows * row_bytes);
-  constexpr uint32_t kScaleBytes = S16 ? 2u : 4u;
+  constexpr uint32_t kScaleBytes = MX ? 1u : (S16 ? 2u : 4u);
   const __amdgpu_buffer_rsrc_t rs =
       rsrc(static_cast<const char*>(pr.scale) + (int64_t)row0 * p.ngroups * kScaleBytes,
            (uint32_t)(rows * p.ngroups) * kScaleBytes);
-  const __amdgpu_buffer_rsrc_t rz = rsrc(S16 ? nullptr : pr.zero + (int64_t)row0 * p.ngroups,
-                                         S16 ? 0u : (uint32_t)(rows * p.ngroups));
+  const __amdgpu_buffer_rsrc_t rz = rsrc(S16 || MX ? nullptr : pr.zero + (int64_t)row0 * p.ngroups,
+                                         S16 || MX ? 0u : (uint32_t)(rows * p.ngroups));
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.x, (uint32_t)M * (uint32_t)K * 2u);
 
   // ---- staging loads: activations, then scales and zero points -----------------
@@ -196,6 +202,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
     for (int j = 0; j < XL; ++j) {
       if (xr[j] < M) {   // uniform
         const int lstep = 4 * xs4[j] + q;
+        if constexpr (MX) {   // natural order, and no piece sums
+          *reinterpret_cast<u32x4_t*>(lds + wbase + (uint32_t)((xr[j] * cnt + lstep) * 256 + 16 * c)) = xb[j];
+          continue;
+        }
         *reinterpret_cast<bf16x8_t*>(lds + wbase + (uint32_t)((xr[j] * cnt + lstep) * 256 + 16 * c)) = pair_order(xb[j]);
         const float sm = lane_group_sum<kPieceLanes>(chunk_sum(xb[j]));
         if ((c & (kPieceLanes - 1)) == 0) {
@@ -215,7 +225,20 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   auto load_sz = [&](int b) {
     const int g = gb + 4 * q + kSzPerBatch * b;
     const uint32_t e0 = (uint32_t)(c * p.ngroups + g);
-    if constexpr (S16) {   // four float16 scales, kept as raw halves until put_sz
+    if constexpr (MX) {   // four E8M0 scale bytes
+      zv[b] = 0u;
+      sv[b] = u32x4_t{0u, 0u, 0u, 0u};
+      if (!p.z_bytewise) {
+        const bool in = c < rows && g < p.ngroups;
+        sv[b][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, in ? e0 : kOffsetOOB, 0, 0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ie = c < rows && g + e < p.ngroups;
+          sv[b][0] |= (uint32_t)(uint8_t)__builtin_amdgcn_raw_buffer_load_b8(rs, ie ? e0 + e : kOffsetOOB, 0, 0) << (8 * e);
+        }
+      }
+    } else if constexpr (S16) {   // four float16 scales, kept as raw halves until put_sz
       zv[b] = 0x08080808u;
       sv[b] = u32x4_t{0u, 0u, 0u, 0u};
       if (!p.z_bytewise) {   // uniform: whole 8-byte runs of scales
@@ -249,7 +272,18 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
     // (bit_cast of the whole vector: this compiler resolves a bit_cast of one
     // element of a vector lvalue to element 0)
     f32x4_t sf;
-    if constexpr (S16) {
+    if constexpr (MX) {   // 2^(e - 127) of each E8M0 byte
+      const u32x4_t raw = sv[b];
+      const uint32_t w4 = raw[0];
+      uint32_t bits[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t eb = (w4 >> (8 * e)) & 0xFFu;
+        bits[e] = eb == 0 ? 0x00400000u : eb << 23;
+      }
+      sf = f32x4_t{__uint_as_float(bits[0]), __uint_as_float(bits[1]), __uint_as_float(bits[2]),
+                   __uint_as_float(bits[3])};
+    } else if constexpr (S16) {
       const u32x4_t raw = sv[b];
       const uint32_t h01 = raw[0], h23 = raw[1];
       sf = f32x4_t{(float)__builtin_bit_cast(_Float16, (uint16_t)(h01 & 0xFFFFu)),
@@ -261,6 +295,11 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
     }
     const uint32_t z = zv[b];
     f32x4_t* dst = reinterpret_cast<f32x4_t*>(lds + sz_base + (uint32_t)((c * kSzEntries + 4 * q + kSzPerBatch * b) * 8));
+    if constexpr (MX) {
+      dst[0] = f32x4_t{sf[0], 0.f, sf[1], 0.f};
+      dst[1] = f32x4_t{sf[2], 0.f, sf[3], 0.f};
+      return;
+    }
     dst[0] = f32x4_t{sf[0], -(kNibOffset + (float)(z & 0xFFu)), sf[1], -(kNibOffset + (float)((z >> 8) & 0xFFu))};
     dst[1] = f32x4_t{sf[2], -(kNibOffset + (float)((z >> 16) & 0xFFu)), sf[3], -(kNibOffset + (float)(z >> 24))};
   };
@@ -309,7 +348,26 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   // the scheduling barrier keeps the compiler from sinking the refill below
   // the arithmetic.  A step past the wave's range multiplies zero activations
   // by zero weights and adds exactly nothing.
+  auto step_mx = [&](int slot, int i) {
+    const uint32_t a_addr = a_lane + (uint32_t)i * 256u;
+    bf16x8_t af[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) af[e] = *reinterpret_cast<const bf16x8_t*>(lds + a_addr + kAStride * e);
+    // this lane's block: 4 i + q of the wave's range
+    const float xsc = *reinterpret_cast<const float*>(lds + sz_lane + (uint32_t)(4 * i + q) * 8u);
+    bf16x8_t bw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bw[e] = fp4x8_to_bf16(bq[slot][e], xsc);
+    issue(slot, i + PF);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mfma_bf16(af[e], bw[e], acc);
+  };
   auto step = [&](int slot, int i) {
+    if constexpr (MX) {
+      step_mx(slot, i);
+      return;
+    }
     const uint32_t a_addr = a_lane + (uint32_t)i * 256u;
     bf16x8_t af[4];
 #pragma unroll
@@ -401,9 +459,9 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   }
 }
 
-template <int GB, int FR, int CC, bool S16>
+template <int GB, int FR, int CC, int FMT>
 int32_t launch_one(const GemvParams& gp, const LinearPlan& pl, size_t lds, hipStream_t stream) {
-  auto kern = gemv_kernel<GB, FR, CC, 4, S16>;
+  auto kern = gemv_kernel<GB, FR, CC, 4, FMT>;
   if (lds > 64 * 1024) {
     static bool raised = false;   // raise the dynamic-LDS limit once per instantiation
     if (!raised) {
@@ -417,23 +475,23 @@ int32_t launch_one(const GemvParams& gp, const LinearPlan& pl, size_t lds, hipSt
   return hip_status(hipGetLastError());
 }
 
-template <int GB, int FR, bool S16>
+template <int GB, int FR, int FMT>
 int32_t dispatch_cc(const GemvParams& gp, const LinearPlan& pl, size_t lds, hipStream_t stream) {
   const int cc = gemv_cnt_class(pl.cnt);
   switch (cc) {
-    case 4: return launch_one<GB, FR, 4, S16>(gp, pl, lds, stream);
-    case 8: return launch_one<GB, FR, 8, S16>(gp, pl, lds, stream);
-    case 16: return launch_one<GB, FR, 16, S16>(gp, pl, lds, stream);
+    case 4: return launch_one<GB, FR, 4, FMT>(gp, pl, lds, stream);
+    case 8: return launch_one<GB, FR, 8, FMT>(gp, pl, lds, stream);
+    case 16: return launch_one<GB, FR, 16, FMT>(gp, pl, lds, stream);
     default: return WOQ_EUNSUPPORTED;
   }
 }
 
-template <int FR, bool S16>
+template <int FR, int FMT>
 int32_t dispatch_gb(const GemvParams& gp, const LinearPlan& pl, size_t lds, hipStream_t stream) {
   switch (pl.gb) {
-    case 1: return dispatch_cc<1, FR, S16>(gp, pl, lds, stream);
-    case 2: return dispatch_cc<2, FR, S16>(gp, pl, lds, stream);
-    case 4: return dispatch_cc<4, FR, S16>(gp, pl, lds, stream);
+    case 1: return dispatch_cc<1, FR, FMT>(gp, pl, lds, stream);
+    case 2: return dispatch_cc<2, FR, FMT>(gp, pl, lds, stream);
+    case 4: return dispatch_cc<4, FR, FMT>(gp, pl, lds, stream);
     default: return WOQ_EUNSUPPORTED;
   }
 }
@@ -473,18 +531,24 @@ int32_t launch_gemv_grouped(const LinearArgs* args, int count, const LinearPlan&
   int32_t tb = 0;
   for (int i = 0; i < count; ++i) {
     gp.prob[i] = GemvProblem{args[i].packed,
-                             a.sym16 ? static_cast<const void*>(args[i].scale16)
-                                     : static_cast<const void*>(args[i].scale),
+                             a.mx ? static_cast<const void*>(args[i].scale8)
+                                  : a.sym16 ? static_cast<const void*>(args[i].scale16)
+                                            : static_cast<const void*>(args[i].scale),
                              args[i].zero, args[i].bias, args[i].y, args[i].n, tb};
     tb += (args[i].n + 15) / 16;
   }
   LinearPlan p2 = pl;
   p2.grid = tb;
+  if (a.mx) {
+    if (pl.gb != 1) return WOQ_EUNSUPPORTED;
+    return pl.fold_rows == 1 ? dispatch_cc<1, 1, kFmtMX>(gp, p2, l.total, stream)
+                             : dispatch_cc<1, 4, kFmtMX>(gp, p2, l.total, stream);
+  }
   if (a.sym16)
-    return pl.fold_rows == 1 ? dispatch_gb<1, true>(gp, p2, l.total, stream)
-                             : dispatch_gb<4, true>(gp, p2, l.total, stream);
-  return pl.fold_rows == 1 ? dispatch_gb<1, false>(gp, p2, l.total, stream)
-                           : dispatch_gb<4, false>(gp, p2, l.total, stream);
+    return pl.fold_rows == 1 ? dispatch_gb<1, kFmtS16>(gp, p2, l.total, stream)
+                             : dispatch_gb<4, kFmtS16>(gp, p2, l.total, stream);
+  return pl.fold_rows == 1 ? dispatch_gb<1, kFmtU4>(gp, p2, l.total, stream)
+                           : dispatch_gb<4, kFmtU4>(gp, p2, l.total, stream);
 }
 
 int32_t launch_gemv(const LinearArgs& a, const LinearPlan& pl, hipStream_t stream) {

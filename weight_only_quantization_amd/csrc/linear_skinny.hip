@@ -71,14 +71,21 @@ __device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t of
 }
 
 // G: group size; MT: 16-row activation tiles; T: 16-row weight tiles per
-// workgroup; S16: signed two's complement codes with float16 scales and no
-// zero point (tinyllm L8.5, "int4 per group"), run as unsigned codes v ^ 8
-// with zero point 8 after one XOR per dword.
-template <int G, int MT, int T, bool S16>
+// workgroup; FMT: the weight format.  kFmtS16: signed two's complement codes
+// with float16 scales and no zero point (tinyllm L8.5, "int4 per group"), run
+// as unsigned codes v ^ 8 with zero point 8 after one XOR per dword.  kFmtMX:
+// MXFP4 (G = 32, E2M1 codes, one E8M0 scale per block): each lane's 16 loaded
+// bytes are one block, which v_cvt_scalef32_pk_bf16_fp4 turns into bf16 values
+// already multiplied by the block's power-of-two scale (exact), so the MFMAs
+// accumulate straight into the outputs, in natural input order, with no
+// per-group fold.
+template <int G, int MT, int T, int FMT>
 __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
+  constexpr bool S16 = FMT == kFmtS16, MX = FMT == kFmtMX;
+  static_assert(!MX || G == 32, "MXFP4 blocks hold 32 inputs");
   constexpr int GB = G >= 128 ? 4 : G / 32;   // 32-input blocks per group piece
   constexpr int NP = 4 / GB;                  // group pieces per step
-  constexpr bool kTranspose = GB < 4;
+  constexpr bool kTranspose = GB < 4 && !MX;
   // inputs, and bytes, between the activation chunks of MFMA e and e + 1
   constexpr int kXEIn = kTranspose ? 32 : 8;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -104,12 +111,12 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   const int gb = (s0 * kStepK) / G;
   const int ngw = p.ngw;
   unsigned char* szl = lds + wave * p.sz_bytes;
-  constexpr uint32_t kScaleBytes = S16 ? 2u : 4u;
+  constexpr uint32_t kScaleBytes = MX ? 1u : (S16 ? 2u : 4u);
   const __amdgpu_buffer_rsrc_t rs =
       rsrc(static_cast<const char*>(p.scale) + (int64_t)tile0 * 16 * p.ngroups * kScaleBytes,
            (uint32_t)(wg_rows * p.ngroups) * kScaleBytes);
-  const __amdgpu_buffer_rsrc_t rz = rsrc(S16 ? nullptr : p.zero + (int64_t)tile0 * 16 * p.ngroups,
-                                         S16 ? 0u : (uint32_t)(wg_rows * p.ngroups));
+  const __amdgpu_buffer_rsrc_t rz = rsrc(S16 || MX ? nullptr : p.zero + (int64_t)tile0 * 16 * p.ngroups,
+                                         S16 || MX ? 0u : (uint32_t)(wg_rows * p.ngroups));
   const int sz_total = 16 * T * ngw;
   uint32_t sv[kStageBatch];   // float32 bits, or float16 bits for S16 (converted when stored)
   uint32_t zv[kStageBatch];
@@ -120,7 +127,10 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
       const int r = e / ngw, g = e % ngw;
       const bool in = e < sz_total && r < wg_rows && gb + g < p.ngroups;
       const uint32_t idx = (uint32_t)(r * p.ngroups + gb + g);
-      if constexpr (S16) {
+      if constexpr (MX) {
+        sv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, in ? idx : kOffsetOOB, 0, 0);
+        zv[b] = 0u;
+      } else if constexpr (S16) {
         sv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, in ? idx * 2u : kOffsetOOB, 0, 0);
         zv[b] = 8u;
       } else {
@@ -133,9 +143,15 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
 #pragma unroll
     for (int b = 0; b < kStageBatch; ++b) {
       const int e = base + lane + 64 * b;
-      const float sc = S16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)sv[b]) : __builtin_bit_cast(float, sv[b]);
-      if (e < sz_total)
-        *reinterpret_cast<f32x2_t*>(szl + e * 8) = f32x2_t{sc, -(kNibOffset + (float)(zv[b] & 0xFFu))};
+      if constexpr (MX) {   // (2^(e - 127), unused)
+        const uint32_t eb = sv[b] & 0xFFu;
+        const float sc = __uint_as_float(eb == 0 ? 0x00400000u : eb << 23);
+        if (e < sz_total) *reinterpret_cast<f32x2_t*>(szl + e * 8) = f32x2_t{sc, 0.f};
+      } else {
+        const float sc = S16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)sv[b]) : __builtin_bit_cast(float, sv[b]);
+        if (e < sz_total)
+          *reinterpret_cast<f32x2_t*>(szl + e * 8) = f32x2_t{sc, -(kNibOffset + (float)(zv[b] & 0xFFu))};
+      }
     }
   };
   stage_load(0);
@@ -207,7 +223,34 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   // i + kPF once its bytes are out (the scheduling barrier keeps the refill
   // ahead of the arithmetic).  A step past the wave's range multiplies zero
   // activations with zero-byte weights and adds nothing.
+  auto step_mx = [&](int slot, int i) {
+    // activations in natural input order; lane (q, c) of weight tile t holds
+    // block 4 i + q of row 16 t + c
+    bf16x8_t af[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) af[mt][e] = __builtin_bit_cast(bf16x8_t, xb[slot][mt][e]);
+    issue_x(slot, i + kPF);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float xs = reinterpret_cast<const f32x2_t*>(szl + ((16 * t + c) * ngw + 4 * i + q) * 8)->x;
+      bf16x8_t bw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bw[e] = fp4x8_to_bf16(wb[slot][t][e], xs);
+      issue_w(slot, t, i + kPF);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[mt][t] = mfma_bf16(af[mt][e], bw[e], acc[mt][t]);
+    }
+  };
   auto step = [&](int slot, int i) {
+    if constexpr (MX) {
+      step_mx(slot, i);
+      return;
+    }
     // activation operands in pair order, and their piece sums: lane (q, c)
     // gets the sums of rows 16 mt + 4q + r, the layout of the accumulators
     bf16x8_t af[MT][4];
@@ -304,9 +347,9 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   }
 }
 
-template <int G, int MT, int T, bool S16>
+template <int G, int MT, int T, int FMT>
 int32_t launch_one(const SkinnyParams& sp, const LinearPlan& pl, size_t lds, hipStream_t stream) {
-  auto kern = skinny_kernel<G, MT, T, S16>;
+  auto kern = skinny_kernel<G, MT, T, FMT>;
   if (lds > 64 * 1024) {
     static bool raised = false;   // raise the dynamic-LDS limit once per instantiation
     if (!raised) {
@@ -320,21 +363,21 @@ int32_t launch_one(const SkinnyParams& sp, const LinearPlan& pl, size_t lds, hip
   return hip_status(hipGetLastError());
 }
 
-template <int G, int MT, bool S16>
+template <int G, int MT, int FMT>
 int32_t dispatch_t(const SkinnyParams& sp, const LinearPlan& pl, size_t lds, hipStream_t s) {
   switch (pl.ns) {
-    case 1: return launch_one<G, MT, 1, S16>(sp, pl, lds, s);
-    case 2: return launch_one<G, MT, 2, S16>(sp, pl, lds, s);
-    case 4: return launch_one<G, MT, 4, S16>(sp, pl, lds, s);
+    case 1: return launch_one<G, MT, 1, FMT>(sp, pl, lds, s);
+    case 2: return launch_one<G, MT, 2, FMT>(sp, pl, lds, s);
+    case 4: return launch_one<G, MT, 4, FMT>(sp, pl, lds, s);
     default: return WOQ_EUNSUPPORTED;
   }
 }
 
-template <int G, bool S16>
+template <int G, int FMT>
 int32_t dispatch_mt(const SkinnyParams& sp, const LinearPlan& pl, size_t lds, hipStream_t s) {
   switch (pl.mt) {
-    case 1: return dispatch_t<G, 1, S16>(sp, pl, lds, s);
-    case 2: return dispatch_t<G, 2, S16>(sp, pl, lds, s);
+    case 1: return dispatch_t<G, 1, FMT>(sp, pl, lds, s);
+    case 2: return dispatch_t<G, 2, FMT>(sp, pl, lds, s);
     default: return WOQ_EUNSUPPORTED;
   }
 }
@@ -354,24 +397,27 @@ SkinnyLds skinny_lds_layout(int64_t m, int64_t k, int64_t group, int waves, int 
 
 int32_t launch_skinny(const LinearArgs& a, const LinearPlan& pl, hipStream_t stream) {
   const SkinnyLds l = skinny_lds_layout(a.m, a.k, a.group, pl.waves, pl.ns, pl.cnt);
-  SkinnyParams sp{a.x, a.packed, a.sym16 ? static_cast<const void*>(a.scale16) : static_cast<const void*>(a.scale),
+  SkinnyParams sp{a.x, a.packed,
+                  a.mx ? static_cast<const void*>(a.scale8)
+                       : a.sym16 ? static_cast<const void*>(a.scale16) : static_cast<const void*>(a.scale),
                   a.zero, a.bias, a.y, a.m, a.n, a.k, a.y_bf16,
                   (a.k + kStepK - 1) / kStepK, a.k / a.group, a.prepared, pl.cnt, l.ngw,
                   l.sz_bytes, (int32_t)l.red_off, kNibPairMask, kBf16Offset2};
+  if (a.mx) return a.group == 32 ? dispatch_mt<32, kFmtMX>(sp, pl, l.total, stream) : WOQ_EUNSUPPORTED;
   if (a.sym16) {
     switch (a.group) {
-      case 32: return dispatch_mt<32, true>(sp, pl, l.total, stream);
-      case 64: return dispatch_mt<64, true>(sp, pl, l.total, stream);
-      case 128: return dispatch_mt<128, true>(sp, pl, l.total, stream);
-      case 256: return dispatch_mt<256, true>(sp, pl, l.total, stream);
+      case 32: return dispatch_mt<32, kFmtS16>(sp, pl, l.total, stream);
+      case 64: return dispatch_mt<64, kFmtS16>(sp, pl, l.total, stream);
+      case 128: return dispatch_mt<128, kFmtS16>(sp, pl, l.total, stream);
+      case 256: return dispatch_mt<256, kFmtS16>(sp, pl, l.total, stream);
       default: return WOQ_EUNSUPPORTED;
     }
   }
   switch (a.group) {
-    case 32: return dispatch_mt<32, false>(sp, pl, l.total, stream);
-    case 64: return dispatch_mt<64, false>(sp, pl, l.total, stream);
-    case 128: return dispatch_mt<128, false>(sp, pl, l.total, stream);
-    case 256: return dispatch_mt<256, false>(sp, pl, l.total, stream);
+    case 32: return dispatch_mt<32, kFmtU4>(sp, pl, l.total, stream);
+    case 64: return dispatch_mt<64, kFmtU4>(sp, pl, l.total, stream);
+    case 128: return dispatch_mt<128, kFmtU4>(sp, pl, l.total, stream);
+    case 256: return dispatch_mt<256, kFmtU4>(sp, pl, l.total, stream);
     default: return WOQ_EUNSUPPORTED;
   }
 }

@@ -49,6 +49,21 @@ __device__ __forceinline__ bf16x8_t unpack_codes(uint32_t d, uint32_t mask, uint
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
+// MXFP4: one dword holds 8 consecutive E2M1 codes (the even input in the low
+// nibble of each byte).  v_cvt_scalef32_pk_bf16_fp4 turns the two codes of one
+// byte into two bf16 values multiplied by `scale`; with a power-of-two scale
+// (an E8M0 block scale) the product is exact.  The result is in natural input
+// order.
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t d, float scale) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  u32x4_t r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3));
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
 // Reorder 8 consecutive bf16 activations (natural order, as 4 dwords) into the
 // slot order of unpack_codes.
 __device__ __forceinline__ bf16x8_t pair_order(u32x4_t raw) {

@@ -94,7 +94,12 @@ struct LinearArgs {
   int32_t prepared;        // 1: weights in the prepared (fragment-ordered) layout
   int32_t sym16;           // 1: signed two's complement codes, float16 scales, no zero point
   const uint16_t* scale16; // [N, K/G] float16 bits when sym16
+  int32_t mx;              // 1: MXFP4 (E2M1 codes, E8M0 scale per block of 32; group = 32)
+  const uint8_t* scale8;   // [N, K/32] E8M0 scale bytes when mx
 };
+
+// Weight formats of the linear kernels' instantiations.
+enum : int { kFmtU4 = 0, kFmtS16 = 1, kFmtMX = 2 };
 
 // Signed int4 groups with float16 scales (quantize syncs through `flag`).
 int32_t launch_quantize_s16(const float* w, int64_t n, int64_t k, int32_t group, int8_t* codes,
@@ -104,6 +109,12 @@ int32_t launch_pack_s4(const int8_t* c, int64_t count, uint8_t* packed, uint32_t
 int32_t launch_unpack_s4(const uint8_t* packed, int64_t count, int8_t* c, hipStream_t stream);
 int32_t launch_dequantize_s16(const uint8_t* packed, const uint16_t* scale16, int64_t n, int64_t k,
                               int32_t group, int32_t out_dtype, void* w_hat, hipStream_t stream);
+
+// MXFP4 (quantize syncs through `flag`).
+int32_t launch_quantize_mx(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
+                           uint32_t* flag, hipStream_t stream);
+int32_t launch_dequantize_mx(const uint8_t* blocks, const uint8_t* scales, int64_t n, int64_t k,
+                             int32_t out_dtype, void* w_hat, hipStream_t stream);
 
 int32_t launch_prep(const uint16_t* x, const int32_t* order, int32_t m, int32_t k, int32_t kpad,
                     int32_t group, int32_t permute, uint16_t* xg, float* xs, int64_t mpad,

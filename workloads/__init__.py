@@ -34,6 +34,7 @@ __all__ = [
     "PREFILL",
     "ACTORDER",
     "SYM16",
+    "MXFP4",
     "LLAMA3_8B_LAYER",
 ]
 
@@ -181,3 +182,15 @@ SYM16 = tuple(
     + [LinearCase("sym16_m16_g32_14336x4096", 16, 14336, 4096, 32, seed_w=158, seed_x=258),
        LinearCase("sym16_m2048_g32_4096x14336", 2048, 4096, 14336, 32, seed_w=159, seed_x=259)]
 )
+
+
+# MXFP4 (linnet "MXFP4 experts"; blocks of 32 with an E8M0 scale): the same
+# decode, small-M and prefill shapes.
+MXFP4 = tuple(
+    [LinearCase(f"mxfp4_m1_{n}x{k}", 1, n, k, 32, seed_w=160 + i, seed_x=260 + i)
+     for i, (n, k) in enumerate(((4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)))]
+    + [LinearCase("mxfp4_m16_14336x4096", 16, 14336, 4096, 32, seed_w=164, seed_x=264),
+       LinearCase("mxfp4_m2048_14336x4096", 2048, 14336, 4096, 32, seed_w=165, seed_x=265),
+       LinearCase("mxfp4_m2048_4096x14336", 2048, 4096, 14336, 32, seed_w=166, seed_x=266)]
+)
+
