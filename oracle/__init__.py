@@ -19,9 +19,11 @@ from .woq_ref import (  # noqa: F401
     bf16_bits_to_f64,
     bf16_round_bits,
     dequantize_int4_groups,
+    dequantize_int4_rows,
     dequantize_int4_sym_f16,
     dequantize_mxfp4,
     linear_int4_groups,
+    linear_int4_rows,
     linear_int4_sym_f16,
     linear_mxfp4,
     pack_int4,
@@ -31,6 +33,7 @@ from .woq_ref import (  # noqa: F401
     quantize_mxfp4,
     prepared_bytes,
     quantize_groups,
+    quantize_int4_rows,
     rint_half_even,
     unpack_int4,
     unpack_uint4,

@@ -88,6 +88,15 @@ R11 MXFP4 (linnet "Quantization", std.quant table, dequantize_mxfp4: E2M1
     and keep their sign (a negative value that rounds to 0 is code 8).
     ``dequant = code_value * X`` (exact in float32); the linear layer's exact
     value is ``sum_k x[m,k] * dequant[n,k] + bias[n]``.
+R12 Int4Linear (linnet "Quantization", std.quant table: weight [Out, In/2]
+    of two signed nibbles a byte, the even element low; one float32 scale a
+    row, as the page's Mlp example declares; dequantize_int4 = unpack, then
+    dequantize).  The page gives the layout, not the quantizer; the rule is
+    tinyllm L8.5's symmetric scaling (section 2) with q_max = 7 and one scale
+    per row: s = float32(amax / 7) (a float32 quotient), codes
+    c = clamp(rint(float32(w / s)), -8, 7), a zero row gets s = 0 and codes 0.
+    ``dequant = c * s`` rounded once to float32; the linear layer's exact value
+    is ``sum_k x'[m,k] * c * s + bias[n]`` with the float64-exact c * s.
 """
 from __future__ import annotations
 
@@ -121,6 +130,9 @@ __all__ = [
     "quantize_mxfp4",
     "dequantize_mxfp4",
     "linear_mxfp4",
+    "quantize_int4_rows",
+    "dequantize_int4_rows",
+    "linear_int4_rows",
 ]
 
 QMAX_ASYM = 15   # unsigned 4-bit codes 0..15 ("Per-Group INT4", 4.8 Quantization II)
@@ -550,6 +562,70 @@ def linear_mxfp4(x, blocks, scales, n: int, k: int, bias=None, rows=None, block_
         sel = idx[b0:b0 + block_rows]
         w = _e2m1_value(unpack_uint4(p[sel])) * np.repeat(_e8m0_value(e[sel]), MX_BLOCK, axis=1)
         y[:, b0:b0 + sel.size] = xv @ w.T
+    if bias is not None:
+        y += np.asarray(bias, dtype=np.float32).astype(np.float64)[idx][None, :]
+    return y
+
+
+# ---------------------------------------------------------------------------
+# Int4Linear: signed int4 codes with one float32 scale a row, R12
+# ---------------------------------------------------------------------------
+
+def quantize_int4_rows(w):
+    """Symmetric signed int4 per row (R12).  w float32 [N, K], K even.
+
+    Returns codes int8 [N, K] in -8..7 and scale float32 [N].
+    """
+    w = np.asarray(w, dtype=np.float32)
+    if w.ndim != 2:
+        raise OracleError("weight must be a matrix [Out, In]")
+    if w.shape[1] % 2:
+        raise OracleError("an odd number of inputs cannot be packed two per byte")
+    if not np.all(np.isfinite(w)):
+        raise OracleError("weights must be finite")
+    amax = np.max(np.abs(w), axis=1) if w.shape[1] else np.zeros(w.shape[0], np.float32)
+    s = (amax / np.float32(QMAX_S4)).astype(np.float32)          # float32 quotient
+    live = s > 0
+    quot = w / np.where(live, s, np.float32(1))[:, None]          # float32 quotient
+    c = np.clip(rint_half_even(quot), QMIN_S4, QMAX_S4)
+    c = np.where(live[:, None], c, 0.0)
+    return c.astype(np.int8), s
+
+
+def _rows_exact(c_rows, s_rows):
+    return c_rows.astype(np.float64) * np.asarray(s_rows, dtype=np.float32).astype(np.float64)[:, None]
+
+
+def dequantize_int4_rows(packed, scale, n: int, k: int, out: str = "f32"):
+    """``c * s`` per row, rounded once to float32 (R12); float32 [N, K] or bf16 bits."""
+    c = unpack_int4(np.asarray(packed, dtype=np.uint8).reshape(n, k // 2))
+    w32 = _rows_exact(c, np.asarray(scale).reshape(n)).astype(np.float32)
+    if out == "f32":
+        return w32
+    if out == "bf16":
+        return bf16_round_bits(w32)
+    raise OracleError("out must be 'f32' or 'bf16'")
+
+
+def linear_int4_rows(x, packed, scale, n: int, k: int, bias=None, order=None, rows=None,
+                     block_rows: int = 1024):
+    """Exact-as-float64 value of ``y = x' . dequant(W)^T + bias`` for Int4Linear weights (R12)."""
+    x = np.asarray(x)
+    xv = bf16_bits_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
+    if xv.ndim != 2 or xv.shape[1] != k:
+        raise OracleError("x must be [M, K]")
+    if order is not None:
+        order = np.asarray(order, dtype=np.int64)
+        if order.shape != (k,) or (k and (order.min() < 0 or order.max() >= k)):
+            raise OracleError("order must hold K indices in [0, K)")
+        xv = xv[:, order]
+    p = np.asarray(packed, dtype=np.uint8).reshape(n, k // 2)
+    s = np.asarray(scale, dtype=np.float32).reshape(n)
+    idx = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    y = np.empty((xv.shape[0], idx.size), dtype=np.float64)
+    for b0 in range(0, idx.size, block_rows):
+        sel = idx[b0:b0 + block_rows]
+        y[:, b0:b0 + sel.size] = xv @ _rows_exact(unpack_int4(p[sel]), s[sel]).T
     if bias is not None:
         y += np.asarray(bias, dtype=np.float32).astype(np.float64)[idx][None, :]
     return y
