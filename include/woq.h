@@ -330,6 +330,59 @@ int32_t woq_linear_int4_sym_f16_prepared(const void* x_bf16, int64_t m, const ui
                                          size_t workspace_bytes, void* stream);
 
 /*
+ * ---- Int4Linear: signed int4 with one float32 scale a row ----
+ * linnet "Quantization", std.quant table: Int4Linear weight [Out, In/2] of
+ * signed 4-bit codes (two's complement nibbles, the even input in the low
+ * nibble) and, as the page's Mlp example declares, scale [Out] float32;
+ * dequantize_int4 = unpack, then dequantize: W_hat = c * scale[row].
+ */
+
+/*
+ * Quantizer (tinyllm L8.5 section 2, symmetric scaling with q_max = 7 and one
+ * scale a row).  SYNC.  s = amax / 7 (a float32 division); c = clamp(rint(w / s),
+ * -8, 7), the quotient a float32 division, ties to even; a zero row gets s = 0
+ * and codes 0.
+ * Arguments: w [n, k] float32 (device, 4-byte aligned), k even; outputs codes
+ *   [n, k] int8 (pack with woq_pack_int4), scale [n] float32 (device, 4-byte
+ *   aligned).
+ * Errors: WOQ_EINVAL, WOQ_ESHAPE (odd k), WOQ_ENONFINITE, WOQ_EUNSUPPORTED
+ *   (n*k >= 2^40), WOQ_EHIP.
+ */
+int32_t woq_quantize_int4_rows(const float* w, int64_t n, int64_t k, int8_t* codes, float* scale,
+                               void* stream);
+
+/*
+ * Dequantize W_hat = c * scale[row], rounded once to float32; with
+ * out_dtype = WOQ_BF16 that float32 is rounded to bfloat16.  ASYNC.
+ * Arguments: packed [n, k/2] uint8, scale [n] float32 (device); w_hat [n, k].
+ * Errors: WOQ_EINVAL, WOQ_ESHAPE (odd k), WOQ_EUNSUPPORTED, WOQ_EHIP.
+ */
+int32_t woq_dequantize_int4_rows(const uint8_t* packed, const float* scale, int64_t n, int64_t k,
+                                 int32_t out_dtype, void* w_hat, void* stream);
+
+/*
+ * Workspace woq_linear_int4_rows needs (0 when none).  Pure host function.
+ */
+size_t woq_linear_int4_rows_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t has_order);
+
+/*
+ * Linear layer over Int4Linear weights:
+ *   y[m, n] = sum_k x'[m, k] * c[n, k] * scale[n] + bias[n],
+ *   x'[m, k] = order ? x[m, order[k]] : x[m, k].
+ * The kernels of woq_linear_int4_sym_f16, run in groups of the largest of 256,
+ * 128, 64 and 32 that divides k, every group with the row's scale.  ASYNC.
+ * Arguments: as woq_linear_int4_groups, with scale [n] float32 (device, 16-byte
+ *   aligned) in place of scale and zero and no group; k a multiple of 32;
+ *   workspace of woq_linear_int4_rows_workspace_bytes bytes.
+ * Errors: as woq_linear_int4_groups; WOQ_ESHAPE for odd k, WOQ_EUNSUPPORTED for
+ *   k not a multiple of 32.
+ */
+int32_t woq_linear_int4_rows(const void* x_bf16, int64_t m, const uint8_t* packed, const float* scale,
+                             const float* bias, const int32_t* order, int64_t n, int64_t k,
+                             int32_t y_dtype, void* y, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
  * ---- MXFP4 ----
  * linnet "Quantization" (std.quant table, dequantize_mxfp4: E2M1 values in
  * blocks of 32, one E8M0 scale byte a block) and tinyllm L8.5 section 2

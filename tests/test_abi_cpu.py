@@ -250,3 +250,21 @@ def test_mxfp4_entry_points_validate_first(lib):
     assert st(lib.woq_linear_mxfp4(fake, 1, fake, odd, None, 64, 256, 1, fake, None, 0, None)) == "WOQ_EALIGN"
     assert st(lib.woq_linear_mxfp4(fake, 1, fake, fake, None, 64, 48, 1, fake, None, 0, None)) == "WOQ_EGROUP"
     assert st(lib.woq_linear_mxfp4(fake, 0, fake, fake, None, 64, 256, 1, fake, None, 0, None)) == "WOQ_OK"
+
+
+def test_int4_rows_entry_points_validate_first(lib):
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    st = lambda rc: woq.STATUS[rc]
+    assert st(lib.woq_quantize_int4_rows(fake, 4, 7, fake, fake, None)) == "WOQ_ESHAPE"
+    assert st(lib.woq_quantize_int4_rows(None, 4, 8, fake, fake, None)) == "WOQ_EINVAL"
+    assert st(lib.woq_quantize_int4_rows(fake, 0, 8, None, None, None)) == "WOQ_OK"
+    assert st(lib.woq_dequantize_int4_rows(fake, fake, 4, 8, 5, fake, None)) == "WOQ_EINVAL"
+    assert st(lib.woq_linear_int4_rows(fake, 1, fake, None, None, None, 64, 256, 1, fake, None, 0, None)) == "WOQ_EINVAL"
+    assert st(lib.woq_linear_int4_rows(fake, 1, fake, odd, None, None, 64, 256, 1, fake, None, 0, None)) == "WOQ_EALIGN"
+    assert st(lib.woq_linear_int4_rows(fake, 1, fake, fake, None, None, 64, 250, 1, fake, None, 0, None)) == "WOQ_EUNSUPPORTED"
+    assert st(lib.woq_linear_int4_rows(fake, 1, fake, fake, None, None, 64, 251, 1, fake, None, 0, None)) == "WOQ_ESHAPE"
+    assert st(lib.woq_linear_int4_rows(fake, 0, fake, fake, None, None, 64, 256, 1, fake, None, 0, None)) == "WOQ_OK"
+    # the row layout runs in the largest supported group dividing k
+    assert lib.woq_linear_int4_rows_workspace_bytes(256, 512, 4096, 0) == lib.woq_linear_workspace_bytes(256, 512, 4096, 256, 0)
+    assert lib.woq_linear_int4_rows_workspace_bytes(256, 512, 96, 0) == lib.woq_linear_workspace_bytes(256, 512, 96, 32, 0)

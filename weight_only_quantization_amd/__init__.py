@@ -42,6 +42,9 @@ __all__ = [
     "unpack_int4",
     "dequantize_int4_sym",
     "linear_int4_sym",
+    "quantize_int4_rows",
+    "dequantize_int4_rows",
+    "linear_int4_rows",
     "quantize_mxfp4",
     "dequantize_mxfp4",
     "linear_mxfp4",
@@ -108,6 +111,11 @@ def load() -> ctypes.CDLL:
         "woq_linear_int4_sym_f16_prepared": (c_i32, [c_p, c_i64, c_p, c_p, c_p, c_p, c_i64, c_i64,
                                                      c_i32, c_i32, c_p, c_p, c_sz, c_p]),
         "woq_quantize_mxfp4": (c_i32, [c_p, c_i64, c_i64, c_p, c_p, c_p]),
+        "woq_quantize_int4_rows": (c_i32, [c_p, c_i64, c_i64, c_p, c_p, c_p]),
+        "woq_dequantize_int4_rows": (c_i32, [c_p, c_p, c_i64, c_i64, c_i32, c_p, c_p]),
+        "woq_linear_int4_rows_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i32]),
+        "woq_linear_int4_rows": (c_i32, [c_p, c_i64, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i32, c_p, c_p,
+                                         c_sz, c_p]),
         "woq_dequantize_mxfp4": (c_i32, [c_p, c_p, c_i64, c_i64, c_i32, c_p, c_p]),
         "woq_linear_mxfp4": (c_i32, [c_p, c_i64, c_p, c_p, c_p, c_i64, c_i64, c_i32, c_p, c_p, c_sz,
                                      c_p]),
@@ -557,5 +565,80 @@ def linear_mxfp4(x: torch.Tensor, blocks: torch.Tensor, scales: torch.Tensor,
     _check(lib.woq_linear_mxfp4(_ptr(x), m, _ptr(blocks), _ptr(scales), _ptr(bias), n, k,
                                 F32 if out_dtype == torch.float32 else BF16, _ptr(out),
                                 _ptr(workspace) if need else None, wsb, _stream()), "linear_mxfp4")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Int4Linear: signed int4 codes with one float32 scale a row
+# ---------------------------------------------------------------------------
+
+def quantize_int4_rows(w: torch.Tensor):
+    """Symmetric signed int4 per row on the GPU: w float32 [N, K] -> (codes int8
+    [N, K] in -8..7, scale float32 [N]); s = amax / 7, codes rint(w / s).  Syncs."""
+    lib = load()
+    _need(w, torch.float32, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    n, k = w.shape
+    codes = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    scale = torch.empty((n,), dtype=torch.float32, device=w.device)
+    _check(lib.woq_quantize_int4_rows(_ptr(w), n, k, _ptr(codes), _ptr(scale), _stream()),
+           "quantize_int4_rows")
+    return codes, scale
+
+
+def dequantize_int4_rows(packed: torch.Tensor, scale: torch.Tensor,
+                         out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """codes * scale[row] -> [N, K] float32 or bfloat16."""
+    lib = load()
+    _need(packed, torch.uint8, "packed")
+    _need(scale, torch.float32, "scale")
+    n = scale.shape[0]
+    k = 2 * (packed.numel() // n) if n else 0
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    out = torch.empty((n, k), dtype=out_dtype, device=packed.device)
+    _check(lib.woq_dequantize_int4_rows(_ptr(packed), _ptr(scale), n, k,
+                                        F32 if out_dtype == torch.float32 else BF16, _ptr(out), _stream()),
+           "dequantize_int4_rows")
+    return out
+
+
+def linear_int4_rows(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tensor,
+                     bias: Optional[torch.Tensor] = None, order: Optional[torch.Tensor] = None,
+                     out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = x' . (codes * scale[row])^T + bias over Int4Linear weights.
+
+    x bfloat16 [M, K]; packed uint8 [N, K/2] of signed nibbles; scale float32
+    [N]; bias float32 [N] or None; order int32 [K] or None.  Asynchronous.
+    """
+    lib = load()
+    _need(x, torch.bfloat16, "x")
+    _need(packed, torch.uint8, "packed")
+    _need(scale, torch.float32, "scale")
+    if bias is not None:
+        _need(bias, torch.float32, "bias")
+    if order is not None:
+        _need(order, torch.int32, "order")
+    if x.dim() != 2 or scale.dim() != 1:
+        raise ValueError("x must be [M, K] and scale [N]")
+    m, k = x.shape
+    n = scale.shape[0]
+    if packed.numel() != n * (k // 2):
+        raise ValueError("packed must hold N * K / 2 bytes")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    else:
+        _need(out, out_dtype, "out")
+    need = int(lib.woq_linear_int4_rows_workspace_bytes(m, n, k, int(order is not None)))
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsb = workspace.numel() if (need and workspace is not None) else 0
+    _check(lib.woq_linear_int4_rows(_ptr(x), m, _ptr(packed), _ptr(scale), _ptr(bias), _ptr(order), n, k,
+                                    F32 if out_dtype == torch.float32 else BF16, _ptr(out),
+                                    _ptr(workspace) if need else None, wsb, _stream()), "linear_int4_rows")
     return out
 

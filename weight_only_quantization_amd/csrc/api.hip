@@ -26,6 +26,14 @@ int32_t check_linear_shape(int64_t m, int64_t n, int64_t k, int32_t group) {
   return WOQ_OK;
 }
 
+// Int4Linear has one scale a row; the kernels run it in groups of the largest
+// supported size dividing k (each group sees the same row scale), 0 if none.
+int32_t rows_group(int64_t k) {
+  for (int32_t g : {256, 128, 64, 32})
+    if (k > 0 && k % g == 0) return g;
+  return 0;
+}
+
 // Optional tuning override of the small-M launch shape: WOQ_SKINNY="tiles,cnt"
 // (16-row weight tiles per workgroup, 128-input steps per wave; read on every call).
 bool skinny_override(int* tiles, int* cnt) {
@@ -374,6 +382,44 @@ int32_t woq_dequantize_mxfp4(const uint8_t* blocks, const uint8_t* scales, int64
   return launch_dequantize_mx(blocks, scales, n, k, out_dtype, w_hat, reinterpret_cast<hipStream_t>(stream));
 }
 
+int32_t woq_quantize_int4_rows(const float* w, int64_t n, int64_t k, int8_t* codes, float* scale,
+                               void* stream) {
+  if (n < 0 || k < 0) return WOQ_EINVAL;
+  if (k % 2) return WOQ_ESHAPE;
+  if (n * k >= kMaxElems) return WOQ_EUNSUPPORTED;
+  if (n == 0) return WOQ_OK;
+  if (!w || !codes || !scale) return WOQ_EINVAL;
+  if (!aligned(w, 4) || !aligned(scale, 4)) return WOQ_EALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint32_t* flag = nullptr;
+  WOQ_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&flag), sizeof(uint32_t), s));
+  int32_t st = hip_status(hipMemsetAsync(flag, 0, sizeof(uint32_t), s));
+  if (st == WOQ_OK) st = launch_quantize_rows(w, n, k, codes, scale, flag, s);
+  uint32_t hflag = 0;
+  if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(&hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+  if (st == WOQ_OK) st = hip_status(hipStreamSynchronize(s));
+  (void)hipFreeAsync(flag, s);
+  if (st != WOQ_OK) return st;
+  return hflag ? WOQ_ENONFINITE : WOQ_OK;
+}
+
+int32_t woq_dequantize_int4_rows(const uint8_t* packed, const float* scale, int64_t n, int64_t k,
+                                 int32_t out_dtype, void* w_hat, void* stream) {
+  if (n < 0 || k < 0) return WOQ_EINVAL;
+  if (out_dtype != WOQ_F32 && out_dtype != WOQ_BF16) return WOQ_EINVAL;
+  if (k % 2) return WOQ_ESHAPE;
+  if (n * k >= kMaxElems) return WOQ_EUNSUPPORTED;
+  if (n == 0 || k == 0) return WOQ_OK;
+  if (!packed || !scale || !w_hat) return WOQ_EINVAL;
+  if (!aligned(scale, 4) || !aligned(w_hat, out_dtype == WOQ_F32 ? 4 : 2)) return WOQ_EALIGN;
+  return launch_dequantize_rows(packed, scale, n, k, out_dtype, w_hat, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t woq_linear_int4_rows_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t has_order) {
+  const int32_t g = rows_group(k);
+  return g ? woq_linear_workspace_bytes(m, n, k, g, has_order) : 0;
+}
+
 size_t woq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group,
                                   int32_t has_order) {
   if (check_linear_shape(m, n, k, group) != WOQ_OK) return 0;
@@ -391,8 +437,10 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
                     const uint8_t* zero, const float* bias, const int32_t* order, int64_t n,
                     int64_t k, int32_t group, int32_t y_dtype, void* y, void* workspace,
                     size_t workspace_bytes, void* stream, int32_t prepared,
-                    const uint16_t* scale16 = nullptr, const uint8_t* scale8 = nullptr) {
-  const bool sym16 = scale16 != nullptr;
+                    const uint16_t* scale16 = nullptr, const uint8_t* scale8 = nullptr,
+                    const float* scale_row = nullptr) {
+  const bool row = scale_row != nullptr;     // Int4Linear: signed codes, one float32 scale a row
+  const bool sym16 = scale16 != nullptr || row;
   const bool mx = scale8 != nullptr;
   int32_t st = check_linear_shape(m, n, k, group);
   if (st != WOQ_OK) return st;
@@ -406,7 +454,8 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
   if (!x_bf16 || !packed || (!sym16 && !mx && (!scale || !zero))) return WOQ_EINVAL;
   if (!aligned(x_bf16, 16) || !aligned(packed, 16)) return WOQ_EALIGN;
   if (mx ? !aligned(scale8, 16)
-         : sym16 ? !aligned(scale16, 16) : (!aligned(scale, 16) || !aligned(zero, 16)))
+         : row ? !aligned(scale_row, 16)
+               : sym16 ? !aligned(scale16, 16) : (!aligned(scale, 16) || !aligned(zero, 16)))
     return WOQ_EALIGN;
   const bool has_order = order != nullptr;
   if (has_order && !aligned(order, 16)) return WOQ_EALIGN;
@@ -436,6 +485,8 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
   a.scale16 = scale16;
   a.mx = mx ? 1 : 0;
   a.scale8 = scale8;
+  a.row_scale = row ? 1 : 0;
+  if (row) a.scale = scale_row;
   if (plan.path == 1) {
     if (has_order) {
       uint16_t* xg = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
@@ -496,6 +547,17 @@ int32_t woq_linear_int4_sym_f16_prepared(const void* x_bf16, int64_t m, const ui
   if (k > 0 && m > 0 && n > 0 && !scale16) return WOQ_EINVAL;
   return linear_impl(x_bf16, m, prepared, nullptr, nullptr, bias, order, n, k, group, y_dtype, y,
                      workspace, workspace_bytes, stream, 1, scale16);
+}
+
+int32_t woq_linear_int4_rows(const void* x_bf16, int64_t m, const uint8_t* packed, const float* scale,
+                             const float* bias, const int32_t* order, int64_t n, int64_t k,
+                             int32_t y_dtype, void* y, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (k > 0 && m > 0 && n > 0 && !scale) return WOQ_EINVAL;
+  const int32_t g = rows_group(k);
+  if (k > 0 && g == 0) return k % 2 ? WOQ_ESHAPE : WOQ_EUNSUPPORTED;
+  return linear_impl(x_bf16, m, packed, nullptr, nullptr, bias, order, n, k, k > 0 ? g : 32, y_dtype,
+                     y, workspace, workspace_bytes, stream, 0, nullptr, nullptr, scale);
 }
 
 int32_t woq_linear_mxfp4(const void* x_bf16, int64_t m, const uint8_t* blocks, const uint8_t* scales,

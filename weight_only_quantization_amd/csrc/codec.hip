@@ -431,6 +431,64 @@ __global__ __launch_bounds__(kThreads) void dequant_mx_kernel(const uint8_t* __r
   }
 }
 
+// ---- Int4Linear: signed int4 codes with one float32 scale a row ----
+// s = amax / 7 (a float32 division), codes clamp(rint(w / s), -8, 7) with the
+// quotient in float32; a zero row gets s = 0 and codes 0.  One wave per row;
+// flag bit 0: a non-finite weight.
+__global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const float* __restrict__ w, int64_t n,
+                                                                 int64_t k, int8_t* __restrict__ codes,
+                                                                 float* __restrict__ scale,
+                                                                 uint32_t* __restrict__ flag) {
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (kThreads / 64);
+  for (int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); row < n; row += waves) {
+    const float* g = w + row * k;
+    bool bad = false;
+    float am = 0.0f;
+    for (int64_t e = lane; e < k; e += 64) {
+      bad = bad || !finite_f32(g[e]);
+      am = fmaxf(am, fabsf(g[e]));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      am = fmaxf(am, __shfl_xor(am, off, 64));
+      bad |= __shfl_xor((int)bad, off, 64) != 0;
+    }
+    if (bad) {
+      if (lane == 0) atomicOr(flag, 1u);
+      continue;
+    }
+    const float s = am / 7.0f;
+    int8_t* co = codes + row * k;
+    for (int64_t e = lane; e < k; e += 64)
+      co[e] = (int8_t)(s > 0.0f ? fminf(fmaxf(__builtin_rintf(g[e] / s), -8.0f), 7.0f) : 0.0f);
+    if (lane == 0) scale[row] = s;
+  }
+}
+
+// W_hat = c * s, one float32 rounding.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void dequant_rows_kernel(const uint8_t* __restrict__ packed,
+                                                                const float* __restrict__ scale,
+                                                                int64_t nbytes, int64_t bytes_per_row,
+                                                                void* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nbytes; i += stride) {
+    const float s = scale[i / bytes_per_row];
+    const int b = packed[i];
+    const float v0 = (float)(((b & 15) ^ 8) - 8) * s, v1 = (float)(((b >> 4) ^ 8) - 8) * s;
+    if (BF16) {
+      uint16_t* o = reinterpret_cast<uint16_t*>(out);
+      o[2 * i] = bf16_bits_rne(v0);
+      o[2 * i + 1] = bf16_bits_rne(v1);
+    } else {
+      float* o = reinterpret_cast<float*>(out);
+      o[2 * i] = v0;
+      o[2 * i + 1] = v1;
+    }
+  }
+}
+
 unsigned grid_for(int64_t items) {
   const int64_t blocks = (items + kThreads - 1) / kThreads;
   return (unsigned)(blocks < 1 ? 1 : (blocks > 65536 ? 65536 : blocks));
@@ -627,6 +685,28 @@ int32_t launch_dequantize_mx(const uint8_t* blocks, const uint8_t* scales, int64
   else
     hipLaunchKernelGGL(dequant_mx_kernel<false>, dim3(grid_for(nbytes)), dim3(kThreads), 0, stream,
                        blocks, scales, nbytes, w_hat);
+  return hip_status(hipGetLastError());
+}
+
+int32_t launch_quantize_rows(const float* w, int64_t n, int64_t k, int8_t* codes, float* scale,
+                             uint32_t* flag, hipStream_t stream) {
+  if (n == 0) return WOQ_OK;
+  const int64_t blocks = (n + kThreads / 64 - 1) / (kThreads / 64);
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)(blocks > 65536 ? 65536 : blocks)), dim3(kThreads), 0,
+                     stream, w, n, k, codes, scale, flag);
+  return hip_status(hipGetLastError());
+}
+
+int32_t launch_dequantize_rows(const uint8_t* packed, const float* scale, int64_t n, int64_t k,
+                               int32_t out_dtype, void* w_hat, hipStream_t stream) {
+  const int64_t nbytes = n * (k / 2);
+  if (nbytes == 0) return WOQ_OK;
+  if (out_dtype == WOQ_BF16)
+    hipLaunchKernelGGL(dequant_rows_kernel<true>, dim3(grid_for(nbytes)), dim3(kThreads), 0, stream,
+                       packed, scale, nbytes, k / 2, w_hat);
+  else
+    hipLaunchKernelGGL(dequant_rows_kernel<false>, dim3(grid_for(nbytes)), dim3(kThreads), 0, stream,
+                       packed, scale, nbytes, k / 2, w_hat);
   return hip_status(hipGetLastError());
 }
 

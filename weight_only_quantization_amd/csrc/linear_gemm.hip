@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
 __global__ __launch_bounds__(256) void sz_prep_kernel(const void* __restrict__ scale,
                                                       const uint8_t* __restrict__ zero, int32_t n,
                                                       int32_t ngroups, int32_t npad, int32_t fmt,
-                                                      f32x2_t* __restrict__ sz) {
+                                                      int32_t row_scale, f32x2_t* __restrict__ sz) {
   const int64_t total = (int64_t)ngroups * npad;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
@@ -108,8 +108,10 @@ __global__ __launch_bounds__(256) void sz_prep_kernel(const void* __restrict__ s
       if (fmt == kFmtMX) {
         const uint32_t eb = static_cast<const uint8_t*>(scale)[e];
         v = f32x2_t{__uint_as_float(eb == 0 ? 0x00400000u : eb << 23), 0.f};
-      } else if (fmt == kFmtS16) {
-        v = f32x2_t{(float)static_cast<const _Float16*>(scale)[e], -(kNibOffset + 8.0f)};
+      } else if (fmt == kFmtS16) {   // float16 per group, or one float32 per row (Int4Linear)
+        const float sc = row_scale ? static_cast<const float*>(scale)[c]
+                                   : (float)static_cast<const _Float16*>(scale)[e];
+        v = f32x2_t{sc, -(kNibOffset + 8.0f)};
       } else
         v = f32x2_t{static_cast<const float*>(scale)[e], -(kNibOffset + (float)zero[e])};
     }
@@ -686,9 +688,10 @@ int32_t launch_gemm(const LinearArgs& a, const LinearPlan& pl, void* sz_ws, hipS
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL(sz_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        a.mx ? static_cast<const void*>(a.scale8)
-                            : a.sym16 ? static_cast<const void*>(a.scale16) : static_cast<const void*>(a.scale),
+                            : a.sym16 && !a.row_scale ? static_cast<const void*>(a.scale16)
+                                                      : static_cast<const void*>(a.scale),
                        a.zero, a.n, ngroups, npad, a.mx ? kFmtMX : a.sym16 ? kFmtS16 : kFmtU4,
-                       static_cast<f32x2_t*>(sz_ws));
+                       a.row_scale, static_cast<f32x2_t*>(sz_ws));
     const int32_t st = hip_status(hipGetLastError());
     if (st != WOQ_OK) return st;
   }

@@ -71,6 +71,7 @@ struct GemvParams {
   // The nibble mask and the bf16 offset pattern arrive as arguments so they sit
   // in registers: one v_and_or_b32 per pair then expands two codes.
   uint32_t nib_mask, nib_offset;
+  int32_t row_scale;    // signed codes with one float32 scale a row (Int4Linear)
   int32_t nprob;
   GemvProblem prob[kMaxGrouped];
 };
@@ -168,10 +169,14 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   const __amdgpu_buffer_rsrc_t rb =
       prep ? rsrc(pr.packed + (int64_t)tile * p.nsteps * 1024, (uint32_t)p.nsteps * 1024u)
            : rsrc(pr.packed + (int64_t)row0 * row_bytes, (uint32_t)rows * row_bytes);
-  constexpr uint32_t kScaleBytes = MX ? 1u : (S16 ? 2u : 4u);
+  // scale element bytes and entries per row: float32 per group, float16 per
+  // group (S16), one float32 per row (S16 with row_scale: Int4Linear), a byte
+  // per block (MX)
+  const bool row_scale = S16 && p.row_scale != 0;   // uniform
+  const uint32_t sbytes = MX ? 1u : (S16 && !row_scale ? 2u : 4u);
+  const int32_t srow = row_scale ? 1 : p.ngroups;
   const __amdgpu_buffer_rsrc_t rs =
-      rsrc(static_cast<const char*>(pr.scale) + (int64_t)row0 * p.ngroups * kScaleBytes,
-           (uint32_t)(rows * p.ngroups) * kScaleBytes);
+      rsrc(static_cast<const char*>(pr.scale) + (int64_t)row0 * srow * sbytes, (uint32_t)(rows * srow) * sbytes);
   const __amdgpu_buffer_rsrc_t rz = rsrc(S16 || MX ? nullptr : pr.zero + (int64_t)row0 * p.ngroups,
                                          S16 || MX ? 0u : (uint32_t)(rows * p.ngroups));
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.x, (uint32_t)M * (uint32_t)K * 2u);
@@ -241,7 +246,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
     } else if constexpr (S16) {   // four float16 scales, kept as raw halves until put_sz
       zv[b] = 0x08080808u;
       sv[b] = u32x4_t{0u, 0u, 0u, 0u};
-      if (!p.z_bytewise) {   // uniform: whole 8-byte runs of scales
+      if (row_scale) {   // the row's one float32 scale, for every group
+        const uint32_t v = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, c < rows ? (uint32_t)c * 4u : kOffsetOOB, 0, 0);
+        sv[b] = u32x4_t{v, v, v, v};
+      } else if (!p.z_bytewise) {   // uniform: whole 8-byte runs of scales
         const bool in = c < rows && g < p.ngroups;
         const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, in ? e0 * 2u : kOffsetOOB, 0, 0);
         sv[b][0] = v[0];
@@ -286,7 +294,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
     } else if constexpr (S16) {
       const u32x4_t raw = sv[b];
       const uint32_t h01 = raw[0], h23 = raw[1];
-      sf = f32x4_t{(float)__builtin_bit_cast(_Float16, (uint16_t)(h01 & 0xFFFFu)),
+      if (row_scale)
+        sf = __builtin_bit_cast(f32x4_t, raw);
+      else
+        sf = f32x4_t{(float)__builtin_bit_cast(_Float16, (uint16_t)(h01 & 0xFFFFu)),
                    (float)__builtin_bit_cast(_Float16, (uint16_t)(h01 >> 16)),
                    (float)__builtin_bit_cast(_Float16, (uint16_t)(h23 & 0xFFFFu)),
                    (float)__builtin_bit_cast(_Float16, (uint16_t)(h23 >> 16))};
@@ -527,13 +538,13 @@ int32_t launch_gemv_grouped(const LinearArgs* args, int count, const LinearPlan&
   const int32_t loads = (a.m * pl.cnt / 4 + xl - 1) / xl;
   GemvParams gp{a.x, a.m, a.k, a.y_bf16, nsteps, pl.cnt, ngroups, gshift, loads,
                 ngroups % 4 != 0 ? 1 : 0, a.prepared, l.wave_lds, l.xs_off, l.sz_off, l.red_off,
-                kNibPairMask, kBf16Offset2, count, {}};
+                kNibPairMask, kBf16Offset2, a.row_scale, count, {}};
   int32_t tb = 0;
   for (int i = 0; i < count; ++i) {
     gp.prob[i] = GemvProblem{args[i].packed,
                              a.mx ? static_cast<const void*>(args[i].scale8)
-                                  : a.sym16 ? static_cast<const void*>(args[i].scale16)
-                                            : static_cast<const void*>(args[i].scale),
+                                  : a.sym16 && !a.row_scale ? static_cast<const void*>(args[i].scale16)
+                                                            : static_cast<const void*>(args[i].scale),
                              args[i].zero, args[i].bias, args[i].y, args[i].n, tb};
     tb += (args[i].n + 15) / 16;
   }

@@ -60,6 +60,7 @@ struct SkinnyParams {
   // The nibble mask and the bf16 offset pattern arrive as arguments so they sit
   // in registers: one v_and_or_b32 per pair then expands two codes.
   uint32_t nib_mask, nib_offset;
+  int32_t row_scale;  // signed codes with one float32 scale a row (Int4Linear)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
@@ -111,10 +112,14 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   const int gb = (s0 * kStepK) / G;
   const int ngw = p.ngw;
   unsigned char* szl = lds + wave * p.sz_bytes;
-  constexpr uint32_t kScaleBytes = MX ? 1u : (S16 ? 2u : 4u);
+  // float32 per group, float16 per group (S16), one float32 per row (S16 with
+  // row_scale: Int4Linear), a byte per block (MX)
+  const bool row_scale = S16 && p.row_scale != 0;   // uniform
+  const uint32_t sbytes = MX ? 1u : (S16 && !row_scale ? 2u : 4u);
+  const int32_t srow = row_scale ? 1 : p.ngroups;
   const __amdgpu_buffer_rsrc_t rs =
-      rsrc(static_cast<const char*>(p.scale) + (int64_t)tile0 * 16 * p.ngroups * kScaleBytes,
-           (uint32_t)(wg_rows * p.ngroups) * kScaleBytes);
+      rsrc(static_cast<const char*>(p.scale) + (int64_t)tile0 * 16 * srow * sbytes,
+           (uint32_t)(wg_rows * srow) * sbytes);
   const __amdgpu_buffer_rsrc_t rz = rsrc(S16 || MX ? nullptr : p.zero + (int64_t)tile0 * 16 * p.ngroups,
                                          S16 || MX ? 0u : (uint32_t)(wg_rows * p.ngroups));
   const int sz_total = 16 * T * ngw;
@@ -131,7 +136,10 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
         sv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, in ? idx : kOffsetOOB, 0, 0);
         zv[b] = 0u;
       } else if constexpr (S16) {
-        sv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, in ? idx * 2u : kOffsetOOB, 0, 0);
+        if (row_scale)
+          sv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, in ? (uint32_t)r * 4u : kOffsetOOB, 0, 0);
+        else
+          sv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, in ? idx * 2u : kOffsetOOB, 0, 0);
         zv[b] = 8u;
       } else {
         sv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, in ? idx * 4u : kOffsetOOB, 0, 0);
@@ -148,7 +156,8 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
         const float sc = __uint_as_float(eb == 0 ? 0x00400000u : eb << 23);
         if (e < sz_total) *reinterpret_cast<f32x2_t*>(szl + e * 8) = f32x2_t{sc, 0.f};
       } else {
-        const float sc = S16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)sv[b]) : __builtin_bit_cast(float, sv[b]);
+        const float sc = S16 && !row_scale ? (float)__builtin_bit_cast(_Float16, (uint16_t)sv[b])
+                                           : __builtin_bit_cast(float, sv[b]);
         if (e < sz_total)
           *reinterpret_cast<f32x2_t*>(szl + e * 8) = f32x2_t{sc, -(kNibOffset + (float)(zv[b] & 0xFFu))};
       }
@@ -399,10 +408,11 @@ int32_t launch_skinny(const LinearArgs& a, const LinearPlan& pl, hipStream_t str
   const SkinnyLds l = skinny_lds_layout(a.m, a.k, a.group, pl.waves, pl.ns, pl.cnt);
   SkinnyParams sp{a.x, a.packed,
                   a.mx ? static_cast<const void*>(a.scale8)
-                       : a.sym16 ? static_cast<const void*>(a.scale16) : static_cast<const void*>(a.scale),
+                       : a.sym16 && !a.row_scale ? static_cast<const void*>(a.scale16)
+                                                 : static_cast<const void*>(a.scale),
                   a.zero, a.bias, a.y, a.m, a.n, a.k, a.y_bf16,
                   (a.k + kStepK - 1) / kStepK, a.k / a.group, a.prepared, pl.cnt, l.ngw,
-                  l.sz_bytes, (int32_t)l.red_off, kNibPairMask, kBf16Offset2};
+                  l.sz_bytes, (int32_t)l.red_off, kNibPairMask, kBf16Offset2, a.row_scale};
   if (a.mx) return a.group == 32 ? dispatch_mt<32, kFmtMX>(sp, pl, l.total, stream) : WOQ_EUNSUPPORTED;
   if (a.sym16) {
     switch (a.group) {

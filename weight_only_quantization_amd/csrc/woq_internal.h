@@ -96,6 +96,7 @@ struct LinearArgs {
   const uint16_t* scale16; // [N, K/G] float16 bits when sym16
   int32_t mx;              // 1: MXFP4 (E2M1 codes, E8M0 scale per block of 32; group = 32)
   const uint8_t* scale8;   // [N, K/32] E8M0 scale bytes when mx
+  int32_t row_scale;       // 1 (with sym16): one float32 scale a row in `scale` [N] (Int4Linear)
 };
 
 // Weight formats of the linear kernels' instantiations.
@@ -115,6 +116,12 @@ int32_t launch_quantize_mx(const float* w, int64_t n, int64_t k, uint8_t* codes,
                            uint32_t* flag, hipStream_t stream);
 int32_t launch_dequantize_mx(const uint8_t* blocks, const uint8_t* scales, int64_t n, int64_t k,
                              int32_t out_dtype, void* w_hat, hipStream_t stream);
+
+// Int4Linear: signed int4 with one float32 scale a row (quantize syncs through `flag`).
+int32_t launch_quantize_rows(const float* w, int64_t n, int64_t k, int8_t* codes, float* scale,
+                             uint32_t* flag, hipStream_t stream);
+int32_t launch_dequantize_rows(const uint8_t* packed, const float* scale, int64_t n, int64_t k,
+                               int32_t out_dtype, void* w_hat, hipStream_t stream);
 
 int32_t launch_prep(const uint16_t* x, const int32_t* order, int32_t m, int32_t k, int32_t kpad,
                     int32_t group, int32_t permute, uint16_t* xg, float* xs, int64_t mpad,
