@@ -22,6 +22,7 @@ from .woq_ref import (  # noqa: F401
     dequantize_int4_rows,
     dequantize_int4_sym_f16,
     dequantize_mxfp4,
+    gptq_quantize,
     linear_int4_groups,
     linear_int4_rows,
     linear_int4_sym_f16,

@@ -97,6 +97,21 @@ R12 Int4Linear (linnet "Quantization", std.quant table: weight [Out, In/2]
     c = clamp(rint(float32(w / s)), -8, 7), a zero row gets s = 0 and codes 0.
     ``dequant = c * s`` rounded once to float32; the linear layer's exact value
     is ``sum_k x'[m,k] * c * s + bias[n]`` with the float64-exact c * s.
+R13 GPTQ ("20. Quantization", stretch exercise 4: accumulate H = 2 X^T X
+    from calibration inputs, quantize column by column, spreading each
+    column's error over the remaining columns with the Cholesky factor of
+    H^-1; linnet "Importing GPTQ and AWQ": in activation order the layer
+    gets an `order` and gathers its inputs).  The steps not printed there
+    follow the published method (Frantar et al., GPTQ): columns with
+    H_jj = 0 are zeroed and get H_jj = 1; with act_order the columns are
+    visited by decreasing H_jj (a stable sort) and `order` is that
+    permutation; H += damp * mean(diag H) * I; U is the upper Cholesky
+    factor of H^-1; for each column i, at the first column of each group
+    the group's scale and zero come from its current (already updated)
+    columns by R2, the column is coded by R2, and with
+    err = (w_i - dequant_i) / U_ii every later column j takes
+    w_j -= err * U_ij.  The factor 2 in H and its normalisation do not
+    change U's use (it scales U and err inversely), so H = X^T X here.
 """
 from __future__ import annotations
 
@@ -133,6 +148,7 @@ __all__ = [
     "quantize_int4_rows",
     "dequantize_int4_rows",
     "linear_int4_rows",
+    "gptq_quantize",
 ]
 
 QMAX_ASYM = 15   # unsigned 4-bit codes 0..15 ("Per-Group INT4", 4.8 Quantization II)
@@ -629,4 +645,66 @@ def linear_int4_rows(x, packed, scale, n: int, k: int, bias=None, order=None, ro
     if bias is not None:
         y += np.asarray(bias, dtype=np.float32).astype(np.float64)[idx][None, :]
     return y
+
+
+# ---------------------------------------------------------------------------
+# GPTQ, R13
+# ---------------------------------------------------------------------------
+
+def _asym_group_params(wg):
+    """R2/R3 scale and zero of each row of a group block wg [N, G] (float64 values)."""
+    mn, mx = wg.min(axis=1), wg.max(axis=1)
+    d = mx - mn
+    flat = d == 0
+    d_safe = np.where(flat, 1.0, d)
+    scale = np.where(flat, 1.0, d_safe / QMAX_ASYM).astype(np.float32)
+    zero = np.clip(np.where(flat, rint_half_even(-mn), rint_half_even((-QMAX_ASYM * mn) / d_safe)), 0, QMAX_ASYM)
+    return scale, zero, flat, d_safe
+
+
+def gptq_quantize(w, x, group: int, act_order: bool = False, damp: float = 0.01):
+    """GPTQ of one layer (R13), in float64.
+
+    w: float32 [N, K]; x: calibration activations [T, K] (a uint16 array is
+    read as bfloat16 bit patterns).  Returns (q uint8 [N, K], scale float32
+    [N, K/G], zero uint8 [N, K/G], order int32 [K] or None), the columns of q
+    (and the groups) in visiting order; the layer gathers its inputs through
+    `order` (R6).
+    """
+    w = np.asarray(w, dtype=np.float32)
+    _check_groups(w, group)
+    n, k = w.shape
+    x = np.asarray(x)
+    xv = bf16_bits_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
+    if xv.ndim != 2 or xv.shape[1] != k:
+        raise OracleError("calibration inputs must be [T, K]")
+    W = w.astype(np.float64)
+    H = xv.T @ xv
+    dead = np.diag(H) == 0
+    H[dead, dead] = 1.0
+    W[:, dead] = 0.0
+    perm = None
+    if act_order:
+        perm = np.argsort(-np.diag(H), kind="stable")
+        W = W[:, perm]
+        H = H[perm][:, perm]
+    H = H + damp * np.mean(np.diag(H)) * np.eye(k)
+    U = np.linalg.cholesky(np.linalg.inv(H)).T                 # upper, H^-1 = U^T U
+    q = np.zeros((n, k), dtype=np.uint8)
+    ng = k // group
+    scale = np.zeros((n, ng), dtype=np.float32)
+    zero = np.zeros((n, ng), dtype=np.uint8)
+    for i in range(k):
+        g = i // group
+        if i % group == 0:
+            sc, zr, flat, d_safe = _asym_group_params(W[:, i:i + group])
+            scale[:, g], zero[:, g] = sc, zr
+        col = W[:, i]
+        r = np.where(flat, rint_half_even(col), rint_half_even((QMAX_ASYM * col) / d_safe))
+        qi = np.clip(r + zero[:, g], 0, QMAX_ASYM)
+        q[:, i] = qi
+        deq = (qi - zero[:, g].astype(np.float64)) * scale[:, g].astype(np.float64)
+        err = (col - deq) / U[i, i]
+        W[:, i + 1:] -= np.outer(err, U[i, i + 1:])
+    return q, scale, zero, (None if perm is None else perm.astype(np.int32))
 
