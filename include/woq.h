@@ -438,6 +438,43 @@ int32_t woq_linear_mxfp4(const void* x_bf16, int64_t m, const uint8_t* blocks, c
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ---- GPTQ: error-compensating quantization of one layer ----
+ * "20. Quantization" (inference book), stretch exercise 4: H = 2 X^T X from
+ * calibration inputs; the columns are quantized one at a time and each
+ * column's error is spread over the columns not yet quantized through the
+ * Cholesky factor of H^-1.  linnet "Importing GPTQ and AWQ": quantized in
+ * activation order, the layer keeps an `order` it gathers its inputs through.
+ * The steps the pages leave open follow the published method (Frantar et al.):
+ *   - columns with H_jj = 0 get H_jj = 1 and their weights set to 0;
+ *   - act_order visits the columns by decreasing H_jj (stable: equal H_jj keep
+ *     column order);
+ *   - H += damp * mean(diag H) * I; U = upper Cholesky factor of H^-1;
+ *   - a group's (scale, zero) come from its current (already updated) weights
+ *     when its first column comes up, by the asymmetric rule of
+ *     woq_quantize_int4_groups (scale = float32(range / 15), zero =
+ *     clamp(rint(-15 min / range), 0, 15));
+ *   - code = clamp(rint(15 w / range) + zero, 0, 15); err = (w - (code - zero) *
+ *     scale) / U_ii; the later weights w_j -= err * U_ij.
+ * All arithmetic is float64 on the device.  SYNC (allocates and frees its
+ * float64 working set: 3 K^2 + (N + 2) K + 256 N doubles).
+ * Arguments: w [n, k] float32 (device, 4-byte aligned); x_bf16 [t, k] bfloat16
+ *   calibration inputs (device, may be NULL when t = 0); group divides k, at
+ *   most 256; act_order 0 or 1; damp >= 0 (0.01 in the method).
+ *   Outputs (device): codes [n, k] uint8 in 0..15, scale [n, k/group] float32
+ *   (4-byte aligned), zero [n, k/group] uint8, all with their columns in
+ *   visiting order (pack the codes with woq_pack_uint4); order [k] int32
+ *   (4-byte aligned), written only when act_order = 1 (the visiting order, to
+ *   pass to the linear calls), may be NULL otherwise.
+ * Errors: WOQ_EINVAL (NULL pointer, negative size, act_order not 0/1, damp
+ *   negative or not finite), WOQ_EGROUP (group < 1 or not dividing k),
+ *   WOQ_EUNSUPPORTED (group > 256, k >= 2^20), WOQ_ENONFINITE (a weight NaN or
+ *   infinite), WOQ_EALIGN, WOQ_EHIP.
+ */
+int32_t woq_gptq_quantize(const float* w, const void* x_bf16, int64_t t, int64_t n, int64_t k, int32_t group,
+                          int32_t act_order, double damp, uint8_t* codes, float* scale, uint8_t* zero,
+                          int32_t* order, void* stream);
+
+/*
  * Describe the kernel plan the linear calls use for these sizes: the path
  * (decode GEMV for m <= 4, small-M MFMA for m <= 32, tiled MFMA GEMM above),
  * tiles, waves and whether an input pre-pass runs.  Writes a NUL-terminated

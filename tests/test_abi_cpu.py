@@ -268,3 +268,24 @@ def test_int4_rows_entry_points_validate_first(lib):
     # the row layout runs in the largest supported group dividing k
     assert lib.woq_linear_int4_rows_workspace_bytes(256, 512, 4096, 0) == lib.woq_linear_workspace_bytes(256, 512, 4096, 256, 0)
     assert lib.woq_linear_int4_rows_workspace_bytes(256, 512, 96, 0) == lib.woq_linear_workspace_bytes(256, 512, 96, 32, 0)
+
+
+def test_gptq_entry_point_validates_first(lib):
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 1)
+    st = lambda rc: woq.STATUS[rc]
+    args = lambda **kw: [kw.get("w", fake), kw.get("x", fake), kw.get("t", 16), kw.get("n", 8), kw.get("k", 256),
+                         kw.get("group", 128), kw.get("act", 0), kw.get("damp", 0.01), fake, fake, fake,
+                         kw.get("order", None), None]
+    assert st(lib.woq_gptq_quantize(*args(group=96))) == "WOQ_EGROUP"
+    assert st(lib.woq_gptq_quantize(*args(group=0))) == "WOQ_EGROUP"
+    assert st(lib.woq_gptq_quantize(*args(k=512, group=512))) == "WOQ_EUNSUPPORTED"
+    assert st(lib.woq_gptq_quantize(*args(act=1))) == "WOQ_EINVAL"              # order missing
+    assert st(lib.woq_gptq_quantize(*args(act=2, order=fake))) == "WOQ_EINVAL"
+    assert st(lib.woq_gptq_quantize(*args(damp=float("nan")))) == "WOQ_EINVAL"
+    assert st(lib.woq_gptq_quantize(*args(damp=-1.0))) == "WOQ_EINVAL"
+    assert st(lib.woq_gptq_quantize(*args(x=None))) == "WOQ_EINVAL"
+    assert st(lib.woq_gptq_quantize(*args(w=odd))) == "WOQ_EALIGN"
+    assert st(lib.woq_gptq_quantize(*args(n=-1))) == "WOQ_EINVAL"
+    assert st(lib.woq_gptq_quantize(*args(n=0))) == "WOQ_OK"
+    assert st(lib.woq_gptq_quantize(*args(k=0))) == "WOQ_OK"

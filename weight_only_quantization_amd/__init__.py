@@ -26,6 +26,7 @@ __all__ = [
     "load",
     "library_path",
     "quantize_groups",
+    "gptq_quantize",
     "pack_uint4",
     "unpack_uint4",
     "dequantize_int4_groups",
@@ -119,6 +120,8 @@ def load() -> ctypes.CDLL:
         "woq_dequantize_mxfp4": (c_i32, [c_p, c_p, c_i64, c_i64, c_i32, c_p, c_p]),
         "woq_linear_mxfp4": (c_i32, [c_p, c_i64, c_p, c_p, c_p, c_i64, c_i64, c_i32, c_p, c_p, c_sz,
                                      c_p]),
+        "woq_gptq_quantize": (c_i32, [c_p, c_p, c_i64, c_i64, c_i64, c_i32, c_i32, ctypes.c_double, c_p, c_p,
+                                      c_p, c_p, c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -170,6 +173,36 @@ def quantize_groups(w: torch.Tensor, group: int = 128, symmetric: bool = False):
     _check(lib.woq_quantize_groups(_ptr(w), n, k, group, int(bool(symmetric)), _ptr(q),
                                    _ptr(scale), _ptr(zero), _stream()), "quantize_groups")
     return q, scale, zero
+
+
+def gptq_quantize(w: torch.Tensor, x: Optional[torch.Tensor], group: int = 128, act_order: bool = False,
+                  damp: float = 0.01):
+    """GPTQ of one layer on the GPU, in float64.
+
+    w: float32 [N, K]; x: bfloat16 calibration inputs [T, K] (None for none).
+    Returns (q uint8 [N, K], scale float32 [N, K/group], zero uint8
+    [N, K/group], order int32 [K] or None), the columns in visiting order; pass
+    `order` to the linear calls.  Synchronizes the current stream.
+    """
+    lib = load()
+    _need(w, torch.float32, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    n, k = w.shape
+    t = 0
+    if x is not None:
+        _need(x, torch.bfloat16, "x")
+        if x.dim() != 2 or x.shape[1] != k:
+            raise ValueError("x must be [T, K]")
+        t = x.shape[0]
+    ng = k // group if group > 0 else 0
+    q = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    scale = torch.empty((n, ng), dtype=torch.float32, device=w.device)
+    zero = torch.empty((n, ng), dtype=torch.uint8, device=w.device)
+    order = torch.empty((k,), dtype=torch.int32, device=w.device) if act_order else None
+    _check(lib.woq_gptq_quantize(_ptr(w), _ptr(x), t, n, k, group, int(bool(act_order)), float(damp), _ptr(q),
+                                 _ptr(scale), _ptr(zero), _ptr(order), _stream()), "gptq_quantize")
+    return q, scale, zero, order
 
 
 def pack_uint4(q: torch.Tensor) -> torch.Tensor:

@@ -1,6 +1,7 @@
 // C ABI of libwoq.so: argument validation, kernel planning and dispatch.
 // Every check runs on the host before anything is enqueued, so a call that
 // fails validation has no effect.
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -401,6 +402,23 @@ int32_t woq_quantize_int4_rows(const float* w, int64_t n, int64_t k, int8_t* cod
   (void)hipFreeAsync(flag, s);
   if (st != WOQ_OK) return st;
   return hflag ? WOQ_ENONFINITE : WOQ_OK;
+}
+
+int32_t woq_gptq_quantize(const float* w, const void* x_bf16, int64_t t, int64_t n, int64_t k, int32_t group,
+                          int32_t act_order, double damp, uint8_t* codes, float* scale, uint8_t* zero,
+                          int32_t* order, void* stream) {
+  if (n < 0 || k < 0 || t < 0 || act_order < 0 || act_order > 1) return WOQ_EINVAL;
+  if (!(damp >= 0.0) || !std::isfinite(damp)) return WOQ_EINVAL;
+  if (group < 1 || (k > 0 && k % group)) return WOQ_EGROUP;
+  if (gptq_block_cols(group) == 0) return WOQ_EUNSUPPORTED;
+  if (k >= (int64_t)1 << 20 || n >= kMaxDim || t >= kMaxDim || n * k >= kMaxElems || t * k >= kMaxElems)
+    return WOQ_EUNSUPPORTED;
+  if (n == 0 || k == 0) return WOQ_OK;
+  if (!w || (t > 0 && !x_bf16) || !codes || !scale || !zero || (act_order && !order)) return WOQ_EINVAL;
+  if (!aligned(w, 4) || !aligned(x_bf16, 2) || !aligned(scale, 4) || (act_order && !aligned(order, 4)))
+    return WOQ_EALIGN;
+  return run_gptq(w, static_cast<const uint16_t*>(x_bf16), t, n, k, group, act_order, damp, codes, scale, zero,
+                  order, reinterpret_cast<hipStream_t>(stream));
 }
 
 int32_t woq_dequantize_int4_rows(const uint8_t* packed, const float* scale, int64_t n, int64_t k,

@@ -1,0 +1,361 @@
+// GPTQ for one layer ("20. Quantization", stretch exercise 4: H = 2 X^T X from
+// calibration inputs, quantize column by column, spreading each column's error
+// over the remaining columns with the Cholesky factor of H^-1; linnet
+// "Importing GPTQ and AWQ": in activation order the layer gathers its inputs
+// through `order`).  Everything runs in float64, so the codes are decided on
+// the same values as a float64 reference up to the rounding of the factorization.
+//
+// * H = X^T X (the factor 2 scales the Cholesky factor and the errors inversely
+//   and cancels).  Columns with H_jj = 0 get H_jj = 1 and zero weights; with
+//   act_order the columns are visited by decreasing H_jj (a stable sort, on the
+//   host); H += damp * mean(diag H) * I.
+// * The upper Cholesky factor U of H^-1 (H^-1 = U^T U) without forming H^-1:
+//   with J the reversal permutation, J H J = L L^T (lower Cholesky) gives
+//   H = (J L J)(J L J)^T, so U = (J L J)^-1 = J L^-1 J.  An unblocked
+//   right-looking Cholesky and a right-looking triangular inverse, two
+//   launches per column each.
+// * The sweep is independent for every output row: a row's codes, scales and
+//   updates use only its own weights and the shared U.  Per block of whole
+//   groups (at least 128 columns), one thread per row keeps the block's weights
+//   in LDS, takes a group's (scale, zero) from its current columns when the
+//   group starts, codes each column, and subtracts err * U from the rest of the
+//   block, err = (w - dequant) / U_ii; a second kernel applies the block's
+//   errors to every later column.  Every weight takes its updates one at a time
+//   in column order, each product rounded before the subtraction.
+#include <algorithm>
+#include <vector>
+
+#include "woq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace woq {
+namespace {
+
+constexpr int kSweepRows = 64;        // sweep: one thread per row
+constexpr int kSweepMinCols = 128;    // columns per sweep block: whole groups, at least this many
+constexpr int kSweepMaxCols = 256;
+
+__device__ __forceinline__ double bf16_to_f64(uint16_t b) {
+  return (double)__uint_as_float((uint32_t)b << 16);
+}
+
+__global__ __launch_bounds__(256) void gptq_finite_kernel(const float* __restrict__ w, int64_t count,
+                                                          uint32_t* __restrict__ flag) {
+  bool bad = false;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < count; e += (int64_t)gridDim.x * 256)
+    bad |= !isfinite(w[e]);
+  if (bad) atomicOr(flag, 1u);
+}
+
+// H[i][j] = sum_t x[t][i] x[t][j] (float64; the bf16 products are exact): 64 x 64
+// tiles, 256 threads of 4 x 4 entries, 16 calibration rows per LDS stage.
+__global__ __launch_bounds__(256) void gptq_h_kernel(const uint16_t* __restrict__ x, int64_t t, int64_t k,
+                                                     double* __restrict__ h) {
+  __shared__ double xa[16][64];
+  __shared__ double xb[16][64];
+  const int64_t i0 = (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * 64;
+  const int ti = threadIdx.x / 16, tj = threadIdx.x % 16;
+  double acc[4][4] = {};
+  for (int64_t r0 = 0; r0 < t; r0 += 16) {
+    for (int e = threadIdx.x; e < 16 * 64; e += 256) {
+      const int rr = e / 64, cc = e % 64;
+      const int64_t r = r0 + rr;
+      xa[rr][cc] = (r < t && i0 + cc < k) ? bf16_to_f64(x[r * k + i0 + cc]) : 0.0;
+      xb[rr][cc] = (r < t && j0 + cc < k) ? bf16_to_f64(x[r * k + j0 + cc]) : 0.0;
+    }
+    __syncthreads();
+    for (int rr = 0; rr < 16; ++rr) {
+      double a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a[u] = xa[rr][4 * ti + u];
+        b[u] = xb[rr][4 * tj + u];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t i = i0 + 4 * ti + u, j = j0 + 4 * tj + v;
+      if (i < k && j < k) h[i * k + j] = acc[u][v];
+    }
+}
+
+__global__ __launch_bounds__(256) void gptq_diag_kernel(const double* __restrict__ h, int64_t k,
+                                                        double* __restrict__ d) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < k) d[i] = h[i * k + i];
+}
+
+// A[a][b] = Hp[K-1-a][K-1-b] with Hp[u][v] = H[perm[u]][perm[v]] off the
+// diagonal and pdiag[u] (dead columns set to 1, then damped) on it.
+__global__ __launch_bounds__(256) void gptq_arrange_kernel(const double* __restrict__ h,
+                                                           const int32_t* __restrict__ perm,
+                                                           const double* __restrict__ pdiag, int64_t k,
+                                                           double* __restrict__ a) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < k * k; e += (int64_t)gridDim.x * 256) {
+    const int64_t u = k - 1 - e / k, v = k - 1 - e % k;
+    a[e] = u == v ? pdiag[u] : h[(int64_t)perm[u] * k + perm[v]];
+  }
+}
+
+// The weights in visiting order, column-major (wc[c][row]), dead columns zero.
+__global__ __launch_bounds__(256) void gptq_weights_kernel(const float* __restrict__ w, const int32_t* __restrict__ perm,
+                                                           const uint8_t* __restrict__ dead, int64_t n, int64_t k,
+                                                           double* __restrict__ wc) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n * k; e += (int64_t)gridDim.x * 256) {
+    const int64_t c = e / n, r = e % n;
+    const int32_t src = perm[c];
+    wc[e] = dead[src] ? 0.0 : (double)w[r * k + src];
+  }
+}
+
+// Cholesky, column j: A[i][j] /= sqrt(A[j][j]) below the diagonal, the root to
+// dg[j] (A[j][j] itself is read by every thread and left alone).
+__global__ __launch_bounds__(256) void gptq_chol_col_kernel(double* __restrict__ a, int64_t k, int64_t j,
+                                                            double* __restrict__ dg) {
+  const int64_t i = j + 1 + (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const double d = sqrt(a[j * k + j]);
+  if (i < k) a[i * k + j] /= d;
+  if (blockIdx.x == 0 && threadIdx.x == 0) dg[j] = d;
+}
+
+// Cholesky, trailing update after column j: A[i][c] -= A[i][j] A[c][j] for j < c <= i.
+__global__ __launch_bounds__(256) void gptq_chol_update_kernel(double* __restrict__ a, int64_t k, int64_t j) {
+  const int64_t m = k - j - 1;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < m * m; e += (int64_t)gridDim.x * 256) {
+    const int64_t i = j + 1 + e / m, c = j + 1 + e % m;
+    if (c <= i) a[i * k + c] -= a[i * k + j] * a[c * k + j];
+  }
+}
+
+__global__ __launch_bounds__(256) void gptq_identity_kernel(double* __restrict__ tm, int64_t k) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < k * k; e += (int64_t)gridDim.x * 256)
+    tm[e] = (e / k == e % k) ? 1.0 : 0.0;
+}
+
+// Triangular inverse T = L^-1 (L: the strictly lower part of A, diagonal dg),
+// row k0 final: T[k0][j] /= L[k0][k0] for j <= k0 ...
+__global__ __launch_bounds__(256) void gptq_tri_row_kernel(double* __restrict__ tm, const double* __restrict__ dg,
+                                                           int64_t k, int64_t k0) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j <= k0) tm[k0 * k + j] /= dg[k0];
+}
+
+// ... and pushed down: T[i][j] -= L[i][k0] T[k0][j] for i > k0, j <= k0.
+__global__ __launch_bounds__(256) void gptq_tri_update_kernel(double* __restrict__ tm, const double* __restrict__ a,
+                                                              int64_t k, int64_t k0) {
+  const int64_t rows = k - k0 - 1, cols = k0 + 1;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < rows * cols; e += (int64_t)gridDim.x * 256) {
+    const int64_t i = k0 + 1 + e / cols, j = e % cols;
+    tm[i * k + j] -= a[i * k + k0] * tm[k0 * k + j];
+  }
+}
+
+// U[i][j] = T[K-1-i][K-1-j] (upper triangular: i <= j).
+__device__ __forceinline__ double u_at(const double* __restrict__ tm, int64_t k, int64_t i, int64_t j) {
+  return tm[(k - 1 - i) * k + (k - 1 - j)];
+}
+
+// Sweep of columns [c0, c0 + nb) (whole groups) for rows [64 b, 64 b + 64).  The
+// group rule is the asymmetric quantizer's: d = max - min over the group's
+// current columns, scale = float32(d / 15), zero = clamp(rint(-15 min / d), 0, 15),
+// codes clamp(rint(15 w / d) + zero, 0, 15); a flat group (d = 0) takes scale 1,
+// zero clamp(rint(-min), 0, 15) and codes clamp(rint(w) + zero, 0, 15).
+__global__ __launch_bounds__(kSweepRows) void gptq_sweep_kernel(double* __restrict__ wc, const double* __restrict__ tm,
+                                                                int64_t n, int64_t k, int32_t group, int64_t c0,
+                                                                int32_t nb, uint8_t* __restrict__ q,
+                                                                float* __restrict__ scale, uint8_t* __restrict__ zero,
+                                                                double* __restrict__ err) {
+  extern __shared__ double vals[];   // [nb][kSweepRows]
+  const int tid = threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * kSweepRows + tid;
+  const bool live = row < n;
+  for (int i = 0; i < nb; ++i) vals[i * kSweepRows + tid] = live ? wc[(c0 + i) * n + row] : 0.0;
+  const int64_t ng = k / group;
+  double d_safe = 1.0, zr = 0.0, sc = 1.0;
+  bool flat = true;
+  for (int i = 0; i < nb; ++i) {
+    const int64_t c = c0 + i;
+    if (c % group == 0) {
+      double mn = vals[i * kSweepRows + tid], mx = mn;
+      for (int e = 1; e < group; ++e) {
+        const double v = vals[(i + e) * kSweepRows + tid];
+        mn = fmin(mn, v);
+        mx = fmax(mx, v);
+      }
+      const double d = mx - mn;
+      flat = d == 0.0;
+      d_safe = flat ? 1.0 : d;
+      sc = flat ? 1.0 : (double)(float)(d / 15.0);
+      zr = fmin(fmax(__builtin_rint(flat ? -mn : (-15.0 * mn) / d_safe), 0.0), 15.0);
+      if (live) {
+        scale[row * ng + c / group] = (float)sc;
+        zero[row * ng + c / group] = (uint8_t)zr;
+      }
+    }
+    const double v = vals[i * kSweepRows + tid];
+    const double r = __builtin_rint(flat ? v : (15.0 * v) / d_safe);
+    const double qi = fmin(fmax(r + zr, 0.0), 15.0);
+    const double e = (v - (qi - zr) * sc) / u_at(tm, k, c, c);
+    if (live) {
+      q[row * k + c] = (uint8_t)qi;
+      err[(int64_t)i * n + row] = e;
+    }
+    for (int j = i + 1; j < nb; ++j) vals[j * kSweepRows + tid] -= e * u_at(tm, k, c, c0 + j);
+  }
+}
+
+// The later columns take the block's errors, one column of the block at a time:
+// wc[cc][row] -= err[i][row] * U[c0 + i][cc] for i = 0 .. nb-1, cc >= c0 + nb.
+constexpr int kTrailCols = 16;
+
+__global__ __launch_bounds__(256) void gptq_trailing_kernel(double* __restrict__ wc, const double* __restrict__ tm,
+                                                            const double* __restrict__ err, int64_t n, int64_t k,
+                                                            int64_t c0, int32_t nb) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t cc0 = c0 + nb + (int64_t)blockIdx.y * kTrailCols;
+  if (row >= n) return;
+  const int cols = (int)std::min<int64_t>(kTrailCols, k - cc0);
+  double acc[kTrailCols];
+#pragma unroll
+  for (int u = 0; u < kTrailCols; ++u) acc[u] = u < cols ? wc[(cc0 + u) * n + row] : 0.0;
+  for (int i = 0; i < nb; ++i) {
+    const double e = err[(int64_t)i * n + row];
+#pragma unroll
+    for (int u = 0; u < kTrailCols; ++u)
+      if (u < cols) acc[u] -= e * u_at(tm, k, c0 + i, cc0 + u);
+  }
+#pragma unroll
+  for (int u = 0; u < kTrailCols; ++u)
+    if (u < cols) wc[(cc0 + u) * n + row] = acc[u];
+}
+
+unsigned flat_grid(int64_t items) {
+  const int64_t blocks = (items + 255) / 256;
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(blocks, 65536));
+}
+
+}  // namespace
+
+int32_t gptq_block_cols(int32_t group) {
+  if (group < 1 || group > kSweepMaxCols) return 0;
+  return group * ((kSweepMinCols + group - 1) / group);
+}
+
+int32_t run_gptq(const float* w, const uint16_t* x, int64_t t, int64_t n, int64_t k, int32_t group,
+                 int32_t act_order, double damp, uint8_t* q, float* scale, uint8_t* zero, int32_t* order,
+                 hipStream_t s) {
+  const int32_t bcols = gptq_block_cols(group);
+  if (bcols == 0) return WOQ_EUNSUPPORTED;
+  static bool raised = false;   // raise the dynamic-LDS limit of the sweep once
+  if (!raised) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gptq_sweep_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)(kSweepMaxCols * kSweepRows * sizeof(double))) != hipSuccess)
+      return WOQ_EHIP;
+    raised = true;
+  }
+  double *h = nullptr, *a = nullptr, *tm = nullptr, *wc = nullptr, *err = nullptr, *dg = nullptr, *dd = nullptr;
+  int32_t* dperm = nullptr;
+  uint8_t* ddead = nullptr;
+  uint32_t* flag = nullptr;
+  int32_t st = WOQ_OK;
+  auto alloc = [&](auto** p, size_t bytes) {
+    if (st == WOQ_OK) st = hip_status(hipMallocAsync(reinterpret_cast<void**>(p), bytes, s));
+  };
+  alloc(&h, (size_t)k * k * 8);
+  alloc(&a, (size_t)k * k * 8);
+  alloc(&tm, (size_t)k * k * 8);
+  alloc(&wc, (size_t)n * k * 8);
+  alloc(&err, (size_t)bcols * n * 8);
+  alloc(&dg, (size_t)k * 8);
+  alloc(&dd, (size_t)k * 8);
+  alloc(&dperm, (size_t)k * 4);
+  alloc(&ddead, (size_t)k);
+  alloc(&flag, sizeof(uint32_t));
+  std::vector<double> diag(k), pdiag(k);
+  std::vector<int32_t> perm(k);
+  std::vector<uint8_t> dead(k);
+  uint32_t hflag = 0;
+  if (st == WOQ_OK) st = hip_status(hipMemsetAsync(flag, 0, sizeof(uint32_t), s));
+  if (st == WOQ_OK) {
+    const unsigned tiles = (unsigned)((k + 63) / 64);
+    hipLaunchKernelGGL(gptq_finite_kernel, dim3(flat_grid(n * k)), dim3(256), 0, s, w, n * k, flag);
+    hipLaunchKernelGGL(gptq_h_kernel, dim3(tiles, tiles), dim3(256), 0, s, x, t, k, h);
+    hipLaunchKernelGGL(gptq_diag_kernel, dim3(flat_grid(k)), dim3(256), 0, s, h, k, dd);
+    st = hip_status(hipGetLastError());
+  }
+  if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(diag.data(), dd, (size_t)k * 8, hipMemcpyDeviceToHost, s));
+  if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(&hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+  if (st == WOQ_OK) st = hip_status(hipStreamSynchronize(s));
+  if (st == WOQ_OK && hflag) st = WOQ_ENONFINITE;
+  if (st == WOQ_OK) {
+    double mean = 0.0;
+    for (int64_t i = 0; i < k; ++i) {
+      dead[i] = diag[i] == 0.0;
+      if (dead[i]) diag[i] = 1.0;
+      mean += diag[i];
+    }
+    mean /= (double)k;
+    for (int64_t i = 0; i < k; ++i) perm[i] = (int32_t)i;
+    if (act_order)
+      std::stable_sort(perm.begin(), perm.end(), [&](int32_t u, int32_t v) { return diag[u] > diag[v]; });
+    for (int64_t i = 0; i < k; ++i) pdiag[i] = diag[perm[i]] + damp * mean;
+    st = hip_status(hipMemcpyAsync(dd, pdiag.data(), (size_t)k * 8, hipMemcpyHostToDevice, s));
+    if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(dperm, perm.data(), (size_t)k * 4, hipMemcpyHostToDevice, s));
+    if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(ddead, dead.data(), (size_t)k, hipMemcpyHostToDevice, s));
+  }
+  if (st == WOQ_OK) {
+    hipLaunchKernelGGL(gptq_arrange_kernel, dim3(flat_grid(k * k)), dim3(256), 0, s, h, dperm, dd, k, a);
+    hipLaunchKernelGGL(gptq_weights_kernel, dim3(flat_grid(n * k)), dim3(256), 0, s, w, dperm, ddead, n, k, wc);
+    hipLaunchKernelGGL(gptq_identity_kernel, dim3(flat_grid(k * k)), dim3(256), 0, s, tm, k);
+    st = hip_status(hipGetLastError());
+    for (int64_t j = 0; j < k && st == WOQ_OK; ++j) {
+      hipLaunchKernelGGL(gptq_chol_col_kernel, dim3(flat_grid(k - j)), dim3(256), 0, s, a, k, j, dg);
+      if (j + 1 < k)
+        hipLaunchKernelGGL(gptq_chol_update_kernel, dim3(flat_grid((k - j - 1) * (k - j - 1))), dim3(256), 0, s, a,
+                           k, j);
+      st = hip_status(hipGetLastError());
+    }
+    for (int64_t k0 = 0; k0 < k && st == WOQ_OK; ++k0) {
+      hipLaunchKernelGGL(gptq_tri_row_kernel, dim3(flat_grid(k0 + 1)), dim3(256), 0, s, tm, dg, k, k0);
+      if (k0 + 1 < k)
+        hipLaunchKernelGGL(gptq_tri_update_kernel, dim3(flat_grid((k - k0 - 1) * (k0 + 1))), dim3(256), 0, s, tm, a,
+                           k, k0);
+      st = hip_status(hipGetLastError());
+    }
+    for (int64_t c0 = 0; c0 < k && st == WOQ_OK; c0 += bcols) {
+      const int32_t nb = (int32_t)std::min<int64_t>(bcols, k - c0);
+      hipLaunchKernelGGL(gptq_sweep_kernel, dim3((unsigned)((n + kSweepRows - 1) / kSweepRows)), dim3(kSweepRows),
+                         (size_t)nb * kSweepRows * sizeof(double), s, wc, tm, n, k, group, c0, nb, q, scale, zero,
+                         err);
+      if (c0 + nb < k) {
+        const unsigned gy = (unsigned)((k - c0 - nb + kTrailCols - 1) / kTrailCols);
+        hipLaunchKernelGGL(gptq_trailing_kernel, dim3((unsigned)((n + 255) / 256), gy), dim3(256), 0, s, wc, tm, err,
+                           n, k, c0, nb);
+      }
+      st = hip_status(hipGetLastError());
+    }
+  }
+  if (st == WOQ_OK && act_order)
+    st = hip_status(hipMemcpyAsync(order, dperm, (size_t)k * 4, hipMemcpyDeviceToDevice, s));
+  // finish before the host vectors the copies read go out of scope
+  const int32_t sync = hip_status(hipStreamSynchronize(s));
+  if (st == WOQ_OK) st = sync;
+  for (void* p : {static_cast<void*>(h), static_cast<void*>(a), static_cast<void*>(tm), static_cast<void*>(wc),
+                  static_cast<void*>(err), static_cast<void*>(dg), static_cast<void*>(dd), static_cast<void*>(dperm),
+                  static_cast<void*>(ddead), static_cast<void*>(flag)})
+    if (p) (void)hipFreeAsync(p, s);
+  (void)hipStreamSynchronize(s);
+  return st;
+}
+
+}  // namespace woq

@@ -123,6 +123,13 @@ int32_t launch_quantize_rows(const float* w, int64_t n, int64_t k, int8_t* codes
 int32_t launch_dequantize_rows(const uint8_t* packed, const float* scale, int64_t n, int64_t k,
                                int32_t out_dtype, void* w_hat, hipStream_t stream);
 
+// GPTQ (gptq.hip): columns per sweep block for a group size (0 if unsupported),
+// and the whole quantization, synchronous.
+int32_t gptq_block_cols(int32_t group);
+int32_t run_gptq(const float* w, const uint16_t* x, int64_t t, int64_t n, int64_t k, int32_t group,
+                 int32_t act_order, double damp, uint8_t* q, float* scale, uint8_t* zero, int32_t* order,
+                 hipStream_t s);
+
 int32_t launch_prep(const uint16_t* x, const int32_t* order, int32_t m, int32_t k, int32_t kpad,
                     int32_t group, int32_t permute, uint16_t* xg, float* xs, int64_t mpad,
                     hipStream_t stream);

@@ -88,6 +88,21 @@ def activations_bf16(m: int, k: int, seed: int) -> np.ndarray:
     return xb.view(torch.int16).numpy().view(np.uint16).copy()
 
 
+def calibration_bf16(t: int, k: int, seed: int, rank: int = 16, noise: float = 0.3,
+                     channel_spread: float = 0.5) -> np.ndarray:
+    """Calibration activations for GPTQ: correlated input channels (a rank-`rank`
+    mix of N(0, 1) factors plus N(0, noise^2) per entry) with a log-normal
+    magnitude per channel (sigma `channel_spread`), rounded to bfloat16; raw
+    uint16 bit patterns [t, k]."""
+    import torch
+
+    rng = np.random.default_rng(seed)
+    mix = rng.standard_normal((t, rank)) @ rng.standard_normal((rank, k)) / np.sqrt(rank)
+    x = (mix + noise * rng.standard_normal((t, k))) * np.exp(channel_spread * rng.standard_normal(k))
+    xb = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+    return xb.view(torch.int16).numpy().view(np.uint16).copy()
+
+
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """Widen raw bfloat16 bit patterns to float32 (exact: a bit shift)."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
