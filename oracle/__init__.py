@@ -22,6 +22,9 @@ from .woq_ref import (  # noqa: F401
     dequantize_int4_rows,
     dequantize_int4_sym_f16,
     dequantize_mxfp4,
+    AWQ_FLOOR,
+    awq_scales,
+    awq_search,
     gptq_quantize,
     linear_int4_groups,
     linear_int4_rows,

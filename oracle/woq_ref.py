@@ -112,6 +112,20 @@ R13 GPTQ ("20. Quantization", stretch exercise 4: accumulate H = 2 X^T X
     err = (w_i - dequant_i) / U_ii every later column j takes
     w_j -= err * U_ij.  The factor 2 in H and its normalisation do not
     change U's use (it scales U and err inversely), so H = X^T X here.
+R14 AWQ ("20. Quantization", stretch exercise 3: for one linear layer, a
+    per-input-channel scale s_j = mean|x_j|^alpha searched over alpha in
+    [0, 1] for the least calibration output error after 4-bit quantization of
+    W diag(s); its scaling identity X W^T = (X S^-1)(W S)^T moves magnitude
+    from the activations to the weights without changing the layer).  The
+    page fixes neither the grid nor the error measure's details; the reading:
+    alpha = i / n_grid for i = 0 .. n_grid (both ends of [0, 1]; n_grid = 20
+    as in the published method, Lin et al.); s = float32(max(mean_t |x_tj|^alpha,
+    1e-4)) (the published method's floor, taken after the power; 0^0 = 1);
+    the scaled weights float32(w * s) (one rounding of the exact product) are
+    quantized by R2; the layer they give is X S^-1 (dequant)^T, so its error
+    is ||X (W - W_hat)^T||_F^2 with W_hat = (q - zero) * scale / s in float64;
+    the first alpha with the least error wins.  The activations' S^-1 is for
+    the caller to fold into the producing operation.
 """
 from __future__ import annotations
 
@@ -149,6 +163,9 @@ __all__ = [
     "dequantize_int4_rows",
     "linear_int4_rows",
     "gptq_quantize",
+    "AWQ_FLOOR",
+    "awq_scales",
+    "awq_search",
 ]
 
 QMAX_ASYM = 15   # unsigned 4-bit codes 0..15 ("Per-Group INT4", 4.8 Quantization II)
@@ -708,3 +725,47 @@ def gptq_quantize(w, x, group: int, act_order: bool = False, damp: float = 0.01)
         W[:, i + 1:] -= np.outer(err, U[i, i + 1:])
     return q, scale, zero, (None if perm is None else perm.astype(np.int32))
 
+
+
+AWQ_FLOOR = 1e-4
+
+
+def awq_scales(mean_abs, alpha: float):
+    """R14 per-channel scales: float32(max(mean_abs^alpha, 1e-4))."""
+    return np.maximum(np.power(np.asarray(mean_abs, np.float64), float(alpha)), AWQ_FLOOR).astype(np.float32)
+
+
+def awq_search(w, x, group: int, n_grid: int = 20):
+    """AWQ scale search for one layer (R14), in float64.
+
+    w: float32 [N, K]; x: calibration activations [T, K], T >= 1 (a uint16
+    array is read as bfloat16 bit patterns).  Returns (q uint8 [N, K], scale
+    float32 [N, K/G], zero uint8 [N, K/G]) of the scaled weights W diag(s),
+    s float32 [K], the chosen grid index, and the error of every grid point
+    (float64 [n_grid + 1]).
+    """
+    w = np.asarray(w, dtype=np.float32)
+    _check_groups(w, group)
+    n, k = w.shape
+    if n_grid < 1:
+        raise OracleError("n_grid must be positive")
+    x = np.asarray(x)
+    xv = bf16_bits_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
+    if xv.ndim != 2 or xv.shape[1] != k or xv.shape[0] < 1:
+        raise OracleError("calibration inputs must be [T, K] with T >= 1")
+    mean_abs = np.abs(xv).mean(axis=0)
+    w64 = w.astype(np.float64)
+    losses = np.zeros(n_grid + 1)
+    best = None
+    for i in range(n_grid + 1):
+        s = awq_scales(mean_abs, i / n_grid)
+        ws = (w64 * s.astype(np.float64)).astype(np.float32)
+        q, sc, zr = quantize_groups(ws, group)
+        deq = (q.reshape(n, k // group, group).astype(np.float64) - zr[:, :, None]) * sc[:, :, None]
+        w_hat = deq.reshape(n, k) / s.astype(np.float64)
+        e = xv @ (w64 - w_hat).T
+        losses[i] = float(np.sum(e * e))
+        if best is None or losses[i] < losses[best[0]]:
+            best = (i, q, sc, zr, s)
+    i, q, sc, zr, s = best
+    return q, sc, zr, s, i, losses
