@@ -475,6 +475,35 @@ int32_t woq_gptq_quantize(const float* w, const void* x_bf16, int64_t t, int64_t
                           int32_t* order, void* stream);
 
 /*
+ * ---- AWQ: activation-aware scale search for one layer ----
+ * "20. Quantization" (inference book), stretch exercise 3: a per-input-channel
+ * scale s_j = mean|x_j|^alpha, alpha searched over [0, 1] for the least
+ * calibration output error after 4-bit quantization of W diag(s); the page's
+ * scaling identity X W^T = (X S^-1)(W S)^T: the scaled layer computes with
+ * X S^-1, which the caller folds into the operation that produces x.
+ *   - alpha = i / n_grid for i = 0 .. n_grid (20 in the published method);
+ *   - s_j = float32(max(mean_t |x_tj|^alpha, 1e-4));
+ *   - the scaled weights float32(w * s) are quantized by the asymmetric group
+ *     rule of woq_quantize_int4_groups;
+ *   - the error of a grid point is ||X (W - W_hat)^T||_F^2 with
+ *     W_hat = (q - zero) * scale / s, in float64; the first least error wins.
+ * SYNC (allocates and frees its working set: about 9 bytes per weight).
+ * Arguments: w [n, k] float32 (device, 4-byte aligned); x_bf16 [t, k] bfloat16
+ *   calibration inputs (device, t >= 1); group divides k; n_grid in 1..1000.
+ *   Outputs (device): codes [n, k] uint8 0..15, scale [n, k/group] float32,
+ *   zero [n, k/group] uint8 of the scaled weights at the chosen alpha (pack the
+ *   codes with woq_pack_uint4); s [k] float32 (4-byte aligned); losses
+ *   [n_grid + 1] float64 (8-byte aligned), the error of every grid point, or
+ *   NULL; best (host) the chosen grid index, or NULL.
+ * Errors: WOQ_EINVAL (NULL pointer, negative size, t < 1, n_grid out of
+ *   range), WOQ_EGROUP, WOQ_EUNSUPPORTED (sizes >= 2^31, t >= 2^25),
+ *   WOQ_ENONFINITE (a scaled weight NaN or infinite), WOQ_EALIGN, WOQ_EHIP.
+ */
+int32_t woq_awq_search(const float* w, const void* x_bf16, int64_t t, int64_t n, int64_t k, int32_t group,
+                       int32_t n_grid, uint8_t* codes, float* scale, uint8_t* zero, float* s, double* losses,
+                       int32_t* best, void* stream);
+
+/*
  * Describe the kernel plan the linear calls use for these sizes: the path
  * (decode GEMV for m <= 4, small-M MFMA for m <= 32, tiled MFMA GEMM above),
  * tiles, waves and whether an input pre-pass runs.  Writes a NUL-terminated

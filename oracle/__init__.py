@@ -24,6 +24,7 @@ from .woq_ref import (  # noqa: F401
     dequantize_mxfp4,
     AWQ_FLOOR,
     awq_scales,
+    awq_error,
     awq_search,
     gptq_quantize,
     linear_int4_groups,

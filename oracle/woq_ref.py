@@ -166,6 +166,7 @@ __all__ = [
     "AWQ_FLOOR",
     "awq_scales",
     "awq_search",
+    "awq_error",
 ]
 
 QMAX_ASYM = 15   # unsigned 4-bit codes 0..15 ("Per-Group INT4", 4.8 Quantization II)
@@ -754,18 +755,28 @@ def awq_search(w, x, group: int, n_grid: int = 20):
     if xv.ndim != 2 or xv.shape[1] != k or xv.shape[0] < 1:
         raise OracleError("calibration inputs must be [T, K] with T >= 1")
     mean_abs = np.abs(xv).mean(axis=0)
-    w64 = w.astype(np.float64)
     losses = np.zeros(n_grid + 1)
     best = None
     for i in range(n_grid + 1):
         s = awq_scales(mean_abs, i / n_grid)
-        ws = (w64 * s.astype(np.float64)).astype(np.float32)
-        q, sc, zr = quantize_groups(ws, group)
-        deq = (q.reshape(n, k // group, group).astype(np.float64) - zr[:, :, None]) * sc[:, :, None]
-        w_hat = deq.reshape(n, k) / s.astype(np.float64)
-        e = xv @ (w64 - w_hat).T
-        losses[i] = float(np.sum(e * e))
+        losses[i], q, sc, zr = awq_error(w, xv, group, s)
         if best is None or losses[i] < losses[best[0]]:
             best = (i, q, sc, zr, s)
     i, q, sc, zr, s = best
     return q, sc, zr, s, i, losses
+
+
+def awq_error(w, xv, group: int, s):
+    """R14 error of one scale vector: quantize float32(w * s) by R2 and return
+    (||X (W - W_hat)^T||_F^2, q, scale, zero), W_hat = (q - zero) * scale / s in
+    float64; xv float64 [T, K]."""
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    w64 = w.astype(np.float64)
+    s64 = np.asarray(s, np.float32).astype(np.float64)
+    ws = (w64 * s64).astype(np.float32)
+    q, sc, zr = quantize_groups(ws, group)
+    deq = (q.reshape(n, k // group, group).astype(np.float64) - zr[:, :, None]) * sc[:, :, None]
+    w_hat = deq.reshape(n, k) / s64
+    e = np.asarray(xv, np.float64) @ (w64 - w_hat).T
+    return float(np.sum(e * e)), q, sc, zr

@@ -289,3 +289,22 @@ def test_gptq_entry_point_validates_first(lib):
     assert st(lib.woq_gptq_quantize(*args(n=-1))) == "WOQ_EINVAL"
     assert st(lib.woq_gptq_quantize(*args(n=0))) == "WOQ_OK"
     assert st(lib.woq_gptq_quantize(*args(k=0))) == "WOQ_OK"
+
+
+def test_awq_entry_point_validates_first(lib):
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    best = ctypes.c_int32(-1)
+    st = lambda rc: woq.STATUS[rc]
+    args = lambda **kw: [kw.get("w", fake), fake, kw.get("t", 16), kw.get("n", 8), kw.get("k", 256),
+                         kw.get("group", 128), kw.get("grid", 20), fake, fake, fake, kw.get("s", fake),
+                         kw.get("losses", None), ctypes.byref(best), None]
+    assert st(lib.woq_awq_search(*args(t=0))) == "WOQ_EINVAL"
+    assert st(lib.woq_awq_search(*args(grid=0))) == "WOQ_EINVAL"
+    assert st(lib.woq_awq_search(*args(grid=1001))) == "WOQ_EINVAL"
+    assert st(lib.woq_awq_search(*args(group=96))) == "WOQ_EGROUP"
+    assert st(lib.woq_awq_search(*args(s=None))) == "WOQ_EINVAL"
+    assert st(lib.woq_awq_search(*args(w=odd))) == "WOQ_EALIGN"
+    assert st(lib.woq_awq_search(*args(losses=odd))) == "WOQ_EALIGN"
+    assert st(lib.woq_awq_search(*args(n=0))) == "WOQ_OK"
+    assert best.value == -1

@@ -27,6 +27,7 @@ __all__ = [
     "library_path",
     "quantize_groups",
     "gptq_quantize",
+    "awq_search",
     "pack_uint4",
     "unpack_uint4",
     "dequantize_int4_groups",
@@ -122,6 +123,8 @@ def load() -> ctypes.CDLL:
                                      c_p]),
         "woq_gptq_quantize": (c_i32, [c_p, c_p, c_i64, c_i64, c_i64, c_i32, c_i32, ctypes.c_double, c_p, c_p,
                                       c_p, c_p, c_p]),
+        "woq_awq_search": (c_i32, [c_p, c_p, c_i64, c_i64, c_i64, c_i32, c_i32, c_p, c_p, c_p, c_p, c_p, c_p,
+                                   c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -203,6 +206,33 @@ def gptq_quantize(w: torch.Tensor, x: Optional[torch.Tensor], group: int = 128, 
     _check(lib.woq_gptq_quantize(_ptr(w), _ptr(x), t, n, k, group, int(bool(act_order)), float(damp), _ptr(q),
                                  _ptr(scale), _ptr(zero), _ptr(order), _stream()), "gptq_quantize")
     return q, scale, zero, order
+
+
+def awq_search(w: torch.Tensor, x: torch.Tensor, group: int = 128, n_grid: int = 20):
+    """AWQ scale search for one layer on the GPU.
+
+    w: float32 [N, K]; x: bfloat16 calibration inputs [T, K], T >= 1.  Returns
+    (q uint8 [N, K], scale float32 [N, K/group], zero uint8 [N, K/group]) of the
+    scaled weights W diag(s), s float32 [K], the chosen grid index (alpha =
+    index / n_grid) and the error of every grid point (float64 [n_grid + 1]).
+    The layer then computes with x / s.  Synchronizes the current stream.
+    """
+    lib = load()
+    _need(w, torch.float32, "w")
+    _need(x, torch.bfloat16, "x")
+    if w.dim() != 2 or x.dim() != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("w must be [N, K] and x [T, K]")
+    n, k = w.shape
+    ng = k // group if group > 0 else 0
+    q = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    scale = torch.empty((n, ng), dtype=torch.float32, device=w.device)
+    zero = torch.empty((n, ng), dtype=torch.uint8, device=w.device)
+    s = torch.empty((k,), dtype=torch.float32, device=w.device)
+    losses = torch.empty((max(n_grid, 0) + 1,), dtype=torch.float64, device=w.device)
+    best = ctypes.c_int32(-1)
+    _check(lib.woq_awq_search(_ptr(w), _ptr(x), x.shape[0], n, k, group, n_grid, _ptr(q), _ptr(scale),
+                              _ptr(zero), _ptr(s), _ptr(losses), ctypes.byref(best), _stream()), "awq_search")
+    return q, scale, zero, s, best.value, losses
 
 
 def pack_uint4(q: torch.Tensor) -> torch.Tensor:

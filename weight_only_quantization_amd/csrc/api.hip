@@ -421,6 +421,22 @@ int32_t woq_gptq_quantize(const float* w, const void* x_bf16, int64_t t, int64_t
                   order, reinterpret_cast<hipStream_t>(stream));
 }
 
+int32_t woq_awq_search(const float* w, const void* x_bf16, int64_t t, int64_t n, int64_t k, int32_t group,
+                       int32_t n_grid, uint8_t* codes, float* scale, uint8_t* zero, float* s, double* losses,
+                       int32_t* best, void* stream) {
+  if (n < 0 || k < 0 || t < 1 || n_grid < 1 || n_grid > 1000) return WOQ_EINVAL;
+  if (group < 1 || (k > 0 && k % group)) return WOQ_EGROUP;
+  if (n >= kMaxDim || k >= kMaxDim || t >= kMaxDim / 64 || n * k >= kMaxElems || t * k >= kMaxElems)
+    return WOQ_EUNSUPPORTED;
+  if (n == 0 || k == 0) return WOQ_OK;
+  if (!w || !x_bf16 || !codes || !scale || !zero || !s) return WOQ_EINVAL;
+  if (!aligned(w, 4) || !aligned(x_bf16, 2) || !aligned(scale, 4) || !aligned(s, 4) ||
+      (losses && !aligned(losses, 8)))
+    return WOQ_EALIGN;
+  return run_awq(w, static_cast<const uint16_t*>(x_bf16), t, n, k, group, n_grid, codes, scale, zero, s, losses,
+                 best, reinterpret_cast<hipStream_t>(stream));
+}
+
 int32_t woq_dequantize_int4_rows(const uint8_t* packed, const float* scale, int64_t n, int64_t k,
                                  int32_t out_dtype, void* w_hat, void* stream) {
   if (n < 0 || k < 0) return WOQ_EINVAL;

@@ -130,6 +130,11 @@ int32_t run_gptq(const float* w, const uint16_t* x, int64_t t, int64_t n, int64_
                  int32_t act_order, double damp, uint8_t* q, float* scale, uint8_t* zero, int32_t* order,
                  hipStream_t s);
 
+// AWQ scale search (awq.hip), synchronous.
+int32_t run_awq(const float* w, const uint16_t* x, int64_t t, int64_t n, int64_t k, int32_t group, int32_t n_grid,
+                uint8_t* q, float* scale, uint8_t* zero, float* s_out, double* losses_out, int32_t* best_out,
+                hipStream_t st);
+
 int32_t launch_prep(const uint16_t* x, const int32_t* order, int32_t m, int32_t k, int32_t kpad,
                     int32_t group, int32_t permute, uint16_t* xg, float* xs, int64_t mpad,
                     hipStream_t stream);
