@@ -28,10 +28,12 @@ from .woq_ref import (  # noqa: F401
     awq_search,
     gptq_quantize,
     linear_int4_groups,
+    linear_int4_groups_zp4,
     linear_int4_rows,
     linear_int4_sym_f16,
     linear_mxfp4,
     pack_int4,
+    pack_zero_points,
     pack_uint4,
     prepare_int4,
     quantize_int4_sym_f16,
@@ -41,6 +43,7 @@ from .woq_ref import (  # noqa: F401
     quantize_int4_rows,
     rint_half_even,
     unpack_int4,
+    unpack_zero_points,
     unpack_uint4,
     unprepare_int4,
 )

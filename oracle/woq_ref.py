@@ -126,6 +126,13 @@ R14 AWQ ("20. Quantization", stretch exercise 3: for one linear layer, a
     is ||X (W - W_hat)^T||_F^2 with W_hat = (q - zero) * scale / s in float64;
     the first alpha with the least error wins.  The activations' S^-1 is for
     the caller to fold into the producing operation.
+R15 packed 4-bit zero points (linnet "Quantization": Int4GroupLinear's
+    layout is ONNX Runtime's MatMulNBits, whose zero points are 4-bit values
+    two a byte).  Per row, the zero points of groups 2j and 2j+1 share byte j,
+    group 2j in the low nibble, as the codes are packed (R4); a row with an
+    odd number of groups ends in a byte whose high nibble is padding, written
+    as 0 and ignored when read.  The layer over packed zero points is the
+    layer over the unpacked ones.
 """
 from __future__ import annotations
 
@@ -167,6 +174,9 @@ __all__ = [
     "awq_scales",
     "awq_search",
     "awq_error",
+    "pack_zero_points",
+    "unpack_zero_points",
+    "linear_int4_groups_zp4",
 ]
 
 QMAX_ASYM = 15   # unsigned 4-bit codes 0..15 ("Per-Group INT4", 4.8 Quantization II)
@@ -780,3 +790,31 @@ def awq_error(w, xv, group: int, s):
     w_hat = deq.reshape(n, k) / s64
     e = np.asarray(xv, np.float64) @ (w64 - w_hat).T
     return float(np.sum(e * e)), q, sc, zr
+
+
+def pack_zero_points(zero):
+    """R15: zero points [N, G_n] (0..15) -> bytes [N, ceil(G_n / 2)], group 2j low."""
+    z = np.asarray(zero)
+    if z.ndim != 2:
+        raise OracleError("zero points must be [N, groups]")
+    if z.size and (z.min() < 0 or z.max() > 15):
+        raise OracleError("zero points must lie in 0..15")
+    z = z.astype(np.uint8)
+    if z.shape[1] % 2:
+        z = np.concatenate([z, np.zeros((z.shape[0], 1), np.uint8)], axis=1)   # the padding nibble
+    return pack_uint4(z)
+
+
+def unpack_zero_points(packed, n: int, ngroups: int):
+    """Inverse of :func:`pack_zero_points`: [N, ceil(G_n / 2)] bytes -> [N, G_n]."""
+    p = np.asarray(packed, dtype=np.uint8).reshape(n, (ngroups + 1) // 2)
+    return unpack_uint4(p)[:, :ngroups]
+
+
+def linear_int4_groups_zp4(x, packed, scale, zero_packed, n: int, k: int, group: int,
+                           bias=None, order=None, rows=None):
+    """The linear layer (R6, R8) over packed zero points (R15)."""
+    if group < 1 or k % group:
+        raise OracleError("group must divide K")
+    zero = unpack_zero_points(zero_packed, n, k // group)
+    return linear_int4_groups(x, packed, scale, zero, n, k, group, bias=bias, order=order, rows=rows)
