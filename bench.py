@@ -44,18 +44,22 @@ TRAFFIC_SUMMARY = ROOT / "profiles" / "traffic_gemv_decode_m1_g128.txt"
 KERNEL_SOURCES = ["linear_gemv.hip", "mfma_common.h"]
 
 
-def weight_bytes(n: int, k: int, group: int = GROUP, sym16: bool = False, mx: bool = False) -> int:
+def weight_bytes(n: int, k: int, group: int = GROUP, sym16: bool = False, mx: bool = False,
+                 zp4: bool = False) -> int:
     """Packed codes + float32 scale + uint8 zero of an [n, k] weight (for signed
-    codes: packed codes + float16 scale; for MXFP4: codes + one byte per 32)."""
+    codes: packed codes + float16 scale; for MXFP4: codes + one byte per 32;
+    with packed zero points: two zero points a byte)."""
     if mx:
         return n * k // 2 + n * k // 32
+    if zp4:
+        return n * k // 2 + (n * k // group) * 4 + n * ((k // group + 1) // 2)
     return n * k // 2 + (n * k // group) * (2 if sym16 else 5)
 
 
 def algorithmic_bytes(m: int, n: int, k: int, has_bias: bool, group: int = GROUP,
-                      sym16: bool = False, mx: bool = False) -> int:
+                      sym16: bool = False, mx: bool = False, zp4: bool = False) -> int:
     """Bytes a linear call must move at least once: weights, x, y (bf16), bias."""
-    return weight_bytes(n, k, group, sym16, mx) + m * k * 2 + m * n * 2 + (n * 4 if has_bias else 0)
+    return weight_bytes(n, k, group, sym16, mx, zp4) + m * k * 2 + m * n * 2 + (n * 4 if has_bias else 0)
 
 
 def kernel_source_hash() -> str:
@@ -213,7 +217,7 @@ def measure_prefill(torch, woq, reps: int = 5, calls: int = 20):
 
 
 def measure_configs(torch, woq, reps: int = 40, pool_bytes: int = 1 << 30, cases=None,
-                    sym16: bool = False, mx: bool = False):
+                    sym16: bool = False, mx: bool = False, zp4: bool = False):
     """Per-launch time of every small-M sweep and act-order configuration (or of
     `cases`; with sym16, over signed codes with float16 scales; with mx, over
     MXFP4 weights).
@@ -233,7 +237,7 @@ def measure_configs(torch, woq, reps: int = 40, pool_bytes: int = 1 << 30, cases
     pools = {}
     for case in (cases if cases is not None else (*SWEEP, *ACTORDER)):
         key = (case.n, case.k, case.group)
-        wb = weight_bytes(case.n, case.k, case.group, sym16, mx)
+        wb = weight_bytes(case.n, case.k, case.group, sym16, mx, zp4)
         if key not in pools:
             pools.clear()
             torch.cuda.empty_cache()
@@ -254,7 +258,8 @@ def measure_configs(torch, woq, reps: int = 40, pool_bytes: int = 1 << 30, cases
                 pools[key] = [
                     (torch.randint(0, 256, (case.n, case.k // 2), generator=gen, device=dev, dtype=torch.uint8),
                      torch.rand((case.n, ng), generator=gen, device=dev).mul_(0.01).add_(1e-3),
-                     torch.randint(0, 16, (case.n, ng), generator=gen, device=dev, dtype=torch.uint8))
+                     torch.randint(0, 256 if zp4 else 16, (case.n, (ng + 1) // 2 if zp4 else ng), generator=gen,
+                                   device=dev, dtype=torch.uint8))
                     for _ in range(copies)]
         pool = pools[key]
         x = torch.randn((case.m, case.k), generator=gen, device=dev).to(torch.bfloat16)
@@ -262,7 +267,8 @@ def measure_configs(torch, woq, reps: int = 40, pool_bytes: int = 1 << 30, cases
         bias = torch.randn((case.n,), generator=gen, device=dev).mul_(0.01) if case.has_bias else None
         order = (torch.randperm(case.k, generator=gen, device=dev).to(torch.int32)
                  if case.act_order else None)
-        ws_bytes = woq.linear_workspace_bytes(case.m, case.n, case.k, case.group, order is not None)
+        ws_bytes = (woq.linear_int4_groups_zp4_workspace_bytes if zp4 else woq.linear_workspace_bytes)(
+            case.m, case.n, case.k, case.group, order is not None)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
         def call(i):
@@ -272,6 +278,9 @@ def measure_configs(torch, woq, reps: int = 40, pool_bytes: int = 1 << 30, cases
             elif sym16:
                 woq.linear_int4_sym(x, p, sc, bias=bias, order=order, group=case.group, out=y,
                                     workspace=ws if ws_bytes else None)
+            elif zp4:
+                woq.linear_int4_groups_zp4(x, p, sc, z, bias=bias, order=order, group=case.group, out=y,
+                                           workspace=ws)
             else:
                 woq.linear_int4_groups(x, p, sc, z, bias=bias, order=order, group=case.group, out=y,
                                        workspace=ws if ws_bytes else None)
@@ -297,7 +306,7 @@ def measure_configs(torch, woq, reps: int = 40, pool_bytes: int = 1 << 30, cases
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) * 1e-3 / reps
         flops = 2.0 * case.m * case.n * case.k
-        ab = algorithmic_bytes(case.m, case.n, case.k, case.has_bias, case.group, sym16, mx) + (
+        ab = algorithmic_bytes(case.m, case.n, case.k, case.has_bias, case.group, sym16, mx, zp4) + (
             case.k * 4 if case.act_order else 0)
         out.append(dict(name=case.name, m=case.m, n=case.n, k=case.k, group=case.group,
                         us=round(t * 1e6, 2), weight_GBps=round(wb / t / 1e9, 1),
@@ -560,8 +569,12 @@ def main():
 
     prefill = None if args.no_prefill else measure_prefill(torch, woq)
     configs = None if args.no_configs else measure_configs(torch, woq)
-    sym16 = mxfp4 = None
+    sym16 = mxfp4 = zp4 = None
     if not args.no_configs:
+        from workloads import ZP4
+        zp4 = dict(
+            note="packed 4-bit zero points, unpacked into the workspace by each call (woq_linear_int4_groups_zp4)",
+            configs=measure_configs(torch, woq, cases=ZP4, zp4=True))
         from workloads import SYM16
         sym16 = dict(
             note="signed int4 codes with float16 scales, no zero point (woq_linear_int4_sym_f16)",
@@ -583,7 +596,7 @@ def main():
                     graph=not args.no_graph, accumulate="f32",
                     tokens_per_s_linears_only=round(1.0 / (ms_per_step * 1e-3), 1) if args.layers == 32 else None),
         roofline=roofline, grouped=grouped, prepared=prepared, prefill=prefill, configs=configs,
-        sym16=sym16, mxfp4=mxfp4,
+        sym16=sym16, mxfp4=mxfp4, zp4=zp4,
         cpu_baseline=cpu,
     )
     print(json.dumps(line), flush=True)

@@ -438,6 +438,54 @@ int32_t woq_linear_mxfp4(const void* x_bf16, int64_t m, const uint8_t* blocks, c
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ---- Packed 4-bit zero points ----
+ * linnet "Quantization": Int4GroupLinear's layout is ONNX Runtime's
+ * MatMulNBits, whose zero points are 4-bit values two a byte.  Per row, the
+ * zero points of groups 2j and 2j+1 share byte j, group 2j in the low nibble;
+ * a row with an odd number of groups ends in a byte whose high nibble is 0
+ * (ignored when read).  Packed size: n * ceil(ngroups / 2) bytes.
+ */
+
+/*
+ * zero [n, ngroups] uint8 (0..15) -> zero_packed [n, ceil(ngroups/2)] (device,
+ * no alignment needed).  SYNC.
+ * Errors: WOQ_EINVAL, WOQ_ERANGE (a value above 15; the output is then
+ *   undefined), WOQ_EUNSUPPORTED (n*ngroups >= 2^40), WOQ_EHIP.
+ */
+int32_t woq_pack_zero_points(const uint8_t* zero, int64_t n, int64_t ngroups, uint8_t* zero_packed,
+                             void* stream);
+
+/*
+ * Inverse of woq_pack_zero_points: zero_packed [n, ceil(ngroups/2)] -> zero
+ * [n, ngroups] uint8 (device).  ASYNC.  Load-time use: unpack once and call
+ * woq_linear_int4_groups, which then costs nothing extra per call.
+ * Errors: WOQ_EINVAL, WOQ_EUNSUPPORTED, WOQ_EHIP.
+ */
+int32_t woq_unpack_zero_points(const uint8_t* zero_packed, int64_t n, int64_t ngroups, uint8_t* zero,
+                               void* stream);
+
+/*
+ * woq_linear_int4_groups with packed zero points: each call first unpacks them
+ * into the head of the workspace (one small launch), then runs the same
+ * kernels.  Arguments, results and errors as woq_linear_int4_groups, with
+ * zero_packed [n, ceil((k/group)/2)] uint8 (device, no alignment needed)
+ * replacing zero, and a workspace (256-byte aligned) of
+ * woq_linear_int4_groups_zp4_workspace_bytes() bytes, never 0 when m, n, k > 0.
+ */
+int32_t woq_linear_int4_groups_zp4(const void* x_bf16, int64_t m, const uint8_t* packed, const float* scale,
+                                   const uint8_t* zero_packed, const float* bias, const int32_t* order, int64_t n,
+                                   int64_t k, int32_t group, int32_t y_dtype, void* y, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace woq_linear_int4_groups_zp4 needs: the unpacked zero points
+ * (rounded up to 256 bytes) plus woq_linear_workspace_bytes(...).  Pure host
+ * function; 0 for invalid shapes or an empty problem.
+ */
+size_t woq_linear_int4_groups_zp4_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group,
+                                                  int32_t has_order);
+
+/*
  * ---- GPTQ: error-compensating quantization of one layer ----
  * "20. Quantization" (inference book), stretch exercise 4: H = 2 X^T X from
  * calibration inputs; the columns are quantized one at a time and each

@@ -27,6 +27,9 @@ __all__ = [
     "library_path",
     "quantize_groups",
     "gptq_quantize",
+    "pack_zero_points",
+    "unpack_zero_points",
+    "linear_int4_groups_zp4",
     "awq_search",
     "pack_uint4",
     "unpack_uint4",
@@ -125,6 +128,11 @@ def load() -> ctypes.CDLL:
                                       c_p, c_p, c_p]),
         "woq_awq_search": (c_i32, [c_p, c_p, c_i64, c_i64, c_i64, c_i32, c_i32, c_p, c_p, c_p, c_p, c_p, c_p,
                                    c_p]),
+        "woq_pack_zero_points": (c_i32, [c_p, c_i64, c_i64, c_p, c_p]),
+        "woq_unpack_zero_points": (c_i32, [c_p, c_i64, c_i64, c_p, c_p]),
+        "woq_linear_int4_groups_zp4": (c_i32, [c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i32, c_i32,
+                                               c_p, c_p, c_sz, c_p]),
+        "woq_linear_int4_groups_zp4_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i32, c_i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -411,6 +419,76 @@ def _linear(x, weights, scale, zero, bias, order, n, k, group, out_dtype, out, w
     _check(fn(_ptr(x), m, _ptr(weights), _ptr(scale), _ptr(zero), _ptr(bias), _ptr(order), n, k,
               group, y_dtype, _ptr(out), ws_ptr, wsb, _stream()),
            "linear_int4_groups_prepared" if prepared else "linear_int4_groups")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Packed 4-bit zero points (the MatMulNBits layout)
+# ---------------------------------------------------------------------------
+
+def pack_zero_points(zero: torch.Tensor) -> torch.Tensor:
+    """zero uint8 [N, G_n] (0..15) -> [N, ceil(G_n / 2)], group 2j in the low nibble.  Syncs."""
+    lib = load()
+    _need(zero, torch.uint8, "zero")
+    if zero.dim() != 2:
+        raise ValueError("zero must be [N, groups]")
+    n, ng = zero.shape
+    out = torch.empty((n, (ng + 1) // 2), dtype=torch.uint8, device=zero.device)
+    _check(lib.woq_pack_zero_points(_ptr(zero), n, ng, _ptr(out), _stream()), "pack_zero_points")
+    return out
+
+
+def unpack_zero_points(zero_packed: torch.Tensor, ngroups: int) -> torch.Tensor:
+    """Inverse of pack_zero_points: [N, ceil(G_n / 2)] -> uint8 [N, G_n].  Asynchronous."""
+    lib = load()
+    _need(zero_packed, torch.uint8, "zero_packed")
+    if zero_packed.dim() != 2 or zero_packed.shape[1] != (ngroups + 1) // 2:
+        raise ValueError("zero_packed must be [N, ceil(ngroups / 2)]")
+    n = zero_packed.shape[0]
+    out = torch.empty((n, ngroups), dtype=torch.uint8, device=zero_packed.device)
+    _check(lib.woq_unpack_zero_points(_ptr(zero_packed), n, ngroups, _ptr(out), _stream()), "unpack_zero_points")
+    return out
+
+
+def linear_int4_groups_zp4_workspace_bytes(m: int, n: int, k: int, group: int, has_order: bool) -> int:
+    return int(load().woq_linear_int4_groups_zp4_workspace_bytes(m, n, k, group, int(bool(has_order))))
+
+
+def linear_int4_groups_zp4(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tensor,
+                           zero_packed: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                           order: Optional[torch.Tensor] = None, group: Optional[int] = None,
+                           out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """linear_int4_groups with packed 4-bit zero points [N, ceil(K/G / 2)].  Asynchronous."""
+    lib = load()
+    _need(x, torch.bfloat16, "x")
+    _need(packed, torch.uint8, "packed")
+    _need(scale, torch.float32, "scale")
+    _need(zero_packed, torch.uint8, "zero_packed")
+    if bias is not None:
+        _need(bias, torch.float32, "bias")
+    if order is not None:
+        _need(order, torch.int32, "order")
+    n, k, group = _weight_dims(packed, scale, group)
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError("x must be [M, K]")
+    if zero_packed.numel() != n * ((k // group + 1) // 2):
+        raise ValueError("zero_packed must hold N * ceil(K/G / 2) bytes")
+    m = x.shape[0]
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    else:
+        _need(out, out_dtype, "out")
+    need = int(lib.woq_linear_int4_groups_zp4_workspace_bytes(m, n, k, group, int(order is not None)))
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsb = workspace.numel() if (need and workspace is not None) else 0
+    _check(lib.woq_linear_int4_groups_zp4(_ptr(x), m, _ptr(packed), _ptr(scale), _ptr(zero_packed), _ptr(bias),
+                                          _ptr(order), n, k, group, F32 if out_dtype == torch.float32 else BF16,
+                                          _ptr(out), _ptr(workspace) if need else None, wsb, _stream()),
+           "linear_int4_groups_zp4")
     return out
 
 

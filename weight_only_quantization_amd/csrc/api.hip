@@ -454,6 +454,39 @@ size_t woq_linear_int4_rows_workspace_bytes(int64_t m, int64_t n, int64_t k, int
   return g ? woq_linear_workspace_bytes(m, n, k, g, has_order) : 0;
 }
 
+size_t woq_linear_int4_groups_zp4_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group,
+                                                  int32_t has_order) {
+  if (check_linear_shape(m, n, k, group) != WOQ_OK) return 0;
+  if (m == 0 || n == 0 || k == 0) return 0;
+  return round256((size_t)n * (size_t)(k / group)) + linear_workspace_layout(m, n, k, group, has_order != 0).total;
+}
+
+int32_t woq_pack_zero_points(const uint8_t* zero, int64_t n, int64_t ngroups, uint8_t* packed, void* stream) {
+  if (n < 0 || ngroups < 0) return WOQ_EINVAL;
+  if (n * ngroups >= kMaxElems) return WOQ_EUNSUPPORTED;
+  if (n == 0 || ngroups == 0) return WOQ_OK;
+  if (!zero || !packed) return WOQ_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint32_t* flag = nullptr;
+  WOQ_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&flag), sizeof(uint32_t), s));
+  int32_t st = hip_status(hipMemsetAsync(flag, 0, sizeof(uint32_t), s));
+  if (st == WOQ_OK) st = launch_pack_zero_points(zero, n, ngroups, packed, flag, s);
+  uint32_t hflag = 0;
+  if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(&hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+  if (st == WOQ_OK) st = hip_status(hipStreamSynchronize(s));
+  (void)hipFreeAsync(flag, s);
+  if (st != WOQ_OK) return st;
+  return hflag ? WOQ_ERANGE : WOQ_OK;
+}
+
+int32_t woq_unpack_zero_points(const uint8_t* packed, int64_t n, int64_t ngroups, uint8_t* zero, void* stream) {
+  if (n < 0 || ngroups < 0) return WOQ_EINVAL;
+  if (n * ngroups >= kMaxElems) return WOQ_EUNSUPPORTED;
+  if (n == 0 || ngroups == 0) return WOQ_OK;
+  if (!zero || !packed) return WOQ_EINVAL;
+  return launch_unpack_zero_points(packed, n, ngroups, zero, reinterpret_cast<hipStream_t>(stream));
+}
+
 size_t woq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group,
                                   int32_t has_order) {
   if (check_linear_shape(m, n, k, group) != WOQ_OK) return 0;
@@ -472,8 +505,9 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
                     int64_t k, int32_t group, int32_t y_dtype, void* y, void* workspace,
                     size_t workspace_bytes, void* stream, int32_t prepared,
                     const uint16_t* scale16 = nullptr, const uint8_t* scale8 = nullptr,
-                    const float* scale_row = nullptr) {
+                    const float* scale_row = nullptr, const uint8_t* zero_packed = nullptr) {
   const bool row = scale_row != nullptr;     // Int4Linear: signed codes, one float32 scale a row
+  const bool zp4 = zero_packed != nullptr;   // packed 4-bit zero points, unpacked into the workspace
   const bool sym16 = scale16 != nullptr || row;
   const bool mx = scale8 != nullptr;
   int32_t st = check_linear_shape(m, n, k, group);
@@ -483,23 +517,31 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
   if (!y) return WOQ_EINVAL;
   if (!aligned(y, y_dtype == WOQ_F32 ? 4 : 2)) return WOQ_EALIGN;
   if (bias && !aligned(bias, 4)) return WOQ_EALIGN;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (k == 0) return launch_fill_bias(bias, (int32_t)m, (int32_t)n, y_dtype == WOQ_BF16, y, s);
-  if (!x_bf16 || !packed || (!sym16 && !mx && (!scale || !zero))) return WOQ_EINVAL;
+  if (k == 0)
+    return launch_fill_bias(bias, (int32_t)m, (int32_t)n, y_dtype == WOQ_BF16, y,
+                            reinterpret_cast<hipStream_t>(stream));
+  if (!x_bf16 || !packed || (!sym16 && !mx && (!scale || (!zero && !zp4)))) return WOQ_EINVAL;
   if (!aligned(x_bf16, 16) || !aligned(packed, 16)) return WOQ_EALIGN;
   if (mx ? !aligned(scale8, 16)
          : row ? !aligned(scale_row, 16)
-               : sym16 ? !aligned(scale16, 16) : (!aligned(scale, 16) || !aligned(zero, 16)))
+               : sym16 ? !aligned(scale16, 16) : (!aligned(scale, 16) || (!zp4 && !aligned(zero, 16))))
     return WOQ_EALIGN;
   const bool has_order = order != nullptr;
   if (has_order && !aligned(order, 16)) return WOQ_EALIGN;
   const LinearPlan plan = linear_plan(m, n, k, group, has_order);
   const LinearWorkspace ws = linear_workspace_layout(m, n, k, group, has_order);
-  if (ws.total > 0) {
-    if (!workspace || workspace_bytes < ws.total) return WOQ_EWORKSPACE;
+  const size_t zbytes = zp4 ? round256((size_t)n * (size_t)(k / group)) : 0;
+  if (ws.total + zbytes > 0) {
+    if (!workspace || workspace_bytes < ws.total + zbytes) return WOQ_EWORKSPACE;
     if (!aligned(workspace, 256)) return WOQ_EALIGN;
   }
-  char* wsb = static_cast<char*>(workspace);
+  char* wsb = static_cast<char*>(workspace) + zbytes;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (zp4) {
+    st = launch_unpack_zero_points(zero_packed, n, k / group, static_cast<uint8_t*>(workspace), s);
+    if (st != WOQ_OK) return st;
+    zero = static_cast<const uint8_t*>(workspace);
+  }
   LinearArgs a{};
   a.x = static_cast<const uint16_t*>(x_bf16);
   a.packed = packed;
@@ -562,6 +604,15 @@ int32_t woq_linear_int4_groups(const void* x_bf16, int64_t m, const uint8_t* pac
                                size_t workspace_bytes, void* stream) {
   return linear_impl(x_bf16, m, packed, scale, zero, bias, order, n, k, group, y_dtype, y,
                      workspace, workspace_bytes, stream, 0);
+}
+
+int32_t woq_linear_int4_groups_zp4(const void* x_bf16, int64_t m, const uint8_t* packed, const float* scale,
+                                   const uint8_t* zero_packed, const float* bias, const int32_t* order, int64_t n,
+                                   int64_t k, int32_t group, int32_t y_dtype, void* y, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (k > 0 && m > 0 && n > 0 && !zero_packed) return WOQ_EINVAL;
+  return linear_impl(x_bf16, m, packed, scale, nullptr, bias, order, n, k, group, y_dtype, y, workspace,
+                     workspace_bytes, stream, 0, nullptr, nullptr, nullptr, zero_packed);
 }
 
 int32_t woq_linear_int4_sym_f16(const void* x_bf16, int64_t m, const uint8_t* packed,

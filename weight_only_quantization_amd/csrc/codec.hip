@@ -489,6 +489,34 @@ __global__ __launch_bounds__(kThreads) void dequant_rows_kernel(const uint8_t* _
   }
 }
 
+// Packed 4-bit zero points (the MatMulNBits layout): per row, groups 2j and
+// 2j+1 share byte j, group 2j in the low nibble; an odd row ends in a byte
+// whose high nibble is 0.  One thread per output byte / per zero point.
+__global__ __launch_bounds__(kThreads) void pack_zp_kernel(const uint8_t* __restrict__ zero, int64_t n,
+                                                           int64_t ng, uint8_t* __restrict__ packed,
+                                                           uint32_t* __restrict__ flag) {
+  const int64_t nb = (ng + 1) / 2;
+  bool bad = false;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n * nb; e += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = e / nb, j = e % nb;
+    const uint32_t lo = zero[r * ng + 2 * j];
+    const uint32_t hi = 2 * j + 1 < ng ? zero[r * ng + 2 * j + 1] : 0u;
+    bad |= (lo | hi) > 15u;
+    packed[e] = (uint8_t)((lo & 15u) | ((hi & 15u) << 4));
+  }
+  if (bad) atomicOr(flag, 1u);
+}
+
+__global__ __launch_bounds__(kThreads) void unpack_zp_kernel(const uint8_t* __restrict__ packed, int64_t n,
+                                                             int64_t ng, uint8_t* __restrict__ zero) {
+  const int64_t nb = (ng + 1) / 2;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n * ng; e += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = e / ng, g = e % ng;
+    const uint32_t b = packed[r * nb + g / 2];
+    zero[e] = (uint8_t)((g & 1) ? (b >> 4) : (b & 15u));
+  }
+}
+
 unsigned grid_for(int64_t items) {
   const int64_t blocks = (items + kThreads - 1) / kThreads;
   return (unsigned)(blocks < 1 ? 1 : (blocks > 65536 ? 65536 : blocks));
@@ -707,6 +735,22 @@ int32_t launch_dequantize_rows(const uint8_t* packed, const float* scale, int64_
   else
     hipLaunchKernelGGL(dequant_rows_kernel<false>, dim3(grid_for(nbytes)), dim3(kThreads), 0, stream,
                        packed, scale, nbytes, k / 2, w_hat);
+  return hip_status(hipGetLastError());
+}
+
+int32_t launch_pack_zero_points(const uint8_t* zero, int64_t n, int64_t ngroups, uint8_t* packed, uint32_t* flag,
+                                hipStream_t stream) {
+  if (n == 0 || ngroups == 0) return WOQ_OK;
+  hipLaunchKernelGGL(pack_zp_kernel, dim3(grid_for(n * ((ngroups + 1) / 2))), dim3(kThreads), 0, stream, zero, n,
+                     ngroups, packed, flag);
+  return hip_status(hipGetLastError());
+}
+
+int32_t launch_unpack_zero_points(const uint8_t* packed, int64_t n, int64_t ngroups, uint8_t* zero,
+                                  hipStream_t stream) {
+  if (n == 0 || ngroups == 0) return WOQ_OK;
+  hipLaunchKernelGGL(unpack_zp_kernel, dim3(grid_for(n * ngroups)), dim3(kThreads), 0, stream, packed, n, ngroups,
+                     zero);
   return hip_status(hipGetLastError());
 }
 

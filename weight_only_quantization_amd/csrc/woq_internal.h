@@ -69,6 +69,10 @@ int32_t launch_quantize(const float* w, int64_t n, int64_t k, int32_t group, int
 int32_t launch_pack(const uint8_t* q, int64_t count, uint8_t* packed, uint32_t* flag,
                     hipStream_t stream);
 int32_t launch_unpack(const uint8_t* packed, int64_t count, uint8_t* q, hipStream_t stream);
+int32_t launch_pack_zero_points(const uint8_t* zero, int64_t n, int64_t ngroups, uint8_t* packed, uint32_t* flag,
+                                hipStream_t stream);
+int32_t launch_unpack_zero_points(const uint8_t* packed, int64_t n, int64_t ngroups, uint8_t* zero,
+                                  hipStream_t stream);
 int32_t launch_dequantize(const uint8_t* packed, const float* scale, const uint8_t* zero,
                           int64_t n, int64_t k, int32_t group, int32_t out_dtype, void* w_hat,
                           hipStream_t stream);

@@ -34,6 +34,7 @@ __all__ = [
     "PREFILL",
     "ACTORDER",
     "SYM16",
+    "ZP4",
     "MXFP4",
     "LLAMA3_8B_LAYER",
 ]
@@ -196,6 +197,16 @@ SYM16 = tuple(
      for g in (32, 128) for i, (n, k) in enumerate(((4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)))]
     + [LinearCase("sym16_m16_g32_14336x4096", 16, 14336, 4096, 32, seed_w=158, seed_x=258),
        LinearCase("sym16_m2048_g32_4096x14336", 2048, 4096, 14336, 32, seed_w=159, seed_x=259)]
+)
+
+
+# Packed 4-bit zero points (the MatMulNBits layout): the g128 decode, small-M
+# and prefill shapes, timed per call (the unpack into the workspace included).
+ZP4 = tuple(
+    [LinearCase(f"zp4_m1_g128_{n}x{k}", 1, n, k, 128, seed_w=170 + i, seed_x=270 + i)
+     for i, (n, k) in enumerate(((4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)))]
+    + [LinearCase("zp4_m16_g128_14336x4096", 16, 14336, 4096, 128, seed_w=174, seed_x=274),
+       LinearCase("zp4_m2048_g128_14336x4096", 2048, 14336, 4096, 128, seed_w=175, seed_x=275)]
 )
 
 
