@@ -581,7 +581,9 @@ def main():
             configs=measure_configs(torch, woq, cases=SYM16, sym16=True))
         from workloads import MXFP4
         mxfp4 = dict(
-            note="MXFP4: E2M1 codes, one E8M0 scale per block of 32 (woq_linear_mxfp4)",
+            note="MXFP4: E2M1 codes, one E8M0 scale per block of 32 (woq_linear_mxfp4); plan strings are "
+                 "woq_linear_plan's for the same sizes at group 32, except that the MXFP4 pre-pass copies the "
+                 "activations in natural order and forms no group sums",
             configs=measure_configs(torch, woq, cases=MXFP4, mx=True))
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
