@@ -255,14 +255,11 @@ int32_t run_gptq(const float* w, const uint16_t* x, int64_t t, int64_t n, int64_
                  hipStream_t s) {
   const int32_t bcols = gptq_block_cols(group);
   if (bcols == 0) return WOQ_EUNSUPPORTED;
-  static bool raised = false;   // raise the dynamic-LDS limit of the sweep once
-  if (!raised) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gptq_sweep_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)(kSweepMaxCols * kSweepRows * sizeof(double))) != hipSuccess)
-      return WOQ_EHIP;
-    raised = true;
-  }
+  static std::atomic<uint64_t> raised{0};   // the sweep's dynamic-LDS limit, one bit per device
+  if (const int32_t st = raise_lds_limit(reinterpret_cast<const void*>(gptq_sweep_kernel),
+                                         (int)(kSweepMaxCols * kSweepRows * sizeof(double)), raised);
+      st != WOQ_OK)
+    return st;
   double *h = nullptr, *a = nullptr, *tm = nullptr, *wc = nullptr, *err = nullptr, *dg = nullptr, *dd = nullptr;
   int32_t* dperm = nullptr;
   uint8_t* ddead = nullptr;

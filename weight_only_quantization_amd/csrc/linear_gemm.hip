@@ -604,13 +604,9 @@ template <class Tl, int GB, int S, int FMT>
 int32_t launch_gemm_t(GemmParams gp, hipStream_t stream) {
   auto kern = gemm_kernel<Tl, GB, S, FMT>;
   const size_t lds = gemm_lds_bytes<Tl, GB, S>();
-  static bool raised = false;   // raise the dynamic-LDS limit once per instantiation
-  if (!raised) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return WOQ_EHIP;
-    raised = true;
-  }
+  static std::atomic<uint64_t> raised{0};   // per instantiation, one bit per device
+  if (const int32_t st = raise_lds_limit(reinterpret_cast<const void*>(kern), (int)lds, raised); st != WOQ_OK)
+    return st;
   gp.tiles_m = (gp.m + Tl::BM - 1) / Tl::BM;
   gp.tiles_n = (gp.n_cols + Tl::BN - 1) / Tl::BN;
   hipLaunchKernelGGL(kern, dim3((unsigned)(gp.tiles_m * gp.tiles_n)), dim3(64 * Tl::kWaves), lds,

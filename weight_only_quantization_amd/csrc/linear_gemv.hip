@@ -474,13 +474,9 @@ template <int GB, int FR, int CC, int FMT>
 int32_t launch_one(const GemvParams& gp, const LinearPlan& pl, size_t lds, hipStream_t stream) {
   auto kern = gemv_kernel<GB, FR, CC, 4, FMT>;
   if (lds > 64 * 1024) {
-    static bool raised = false;   // raise the dynamic-LDS limit once per instantiation
-    if (!raised) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-        return WOQ_EHIP;
-      raised = true;
-    }
+    static std::atomic<uint64_t> raised{0};   // per instantiation, one bit per device
+    const int32_t st = raise_lds_limit(reinterpret_cast<const void*>(kern), 160 * 1024, raised);
+    if (st != WOQ_OK) return st;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)pl.grid), dim3(64 * pl.waves), lds, stream, gp);
   return hip_status(hipGetLastError());

@@ -360,13 +360,9 @@ template <int G, int MT, int T, int FMT>
 int32_t launch_one(const SkinnyParams& sp, const LinearPlan& pl, size_t lds, hipStream_t stream) {
   auto kern = skinny_kernel<G, MT, T, FMT>;
   if (lds > 64 * 1024) {
-    static bool raised = false;   // raise the dynamic-LDS limit once per instantiation
-    if (!raised) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-        return WOQ_EHIP;
-      raised = true;
-    }
+    static std::atomic<uint64_t> raised{0};   // per instantiation, one bit per device
+    const int32_t st = raise_lds_limit(reinterpret_cast<const void*>(kern), 160 * 1024, raised);
+    if (st != WOQ_OK) return st;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)pl.grid), dim3(64 * pl.waves), lds, stream, sp);
   return hip_status(hipGetLastError());

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <atomic>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -15,6 +16,18 @@ namespace woq {
 // ---------------------------------------------------------------------------
 
 inline int32_t hip_status(hipError_t e) { return e == hipSuccess ? WOQ_OK : WOQ_EHIP; }
+
+// Raise a kernel's dynamic-LDS limit to `bytes` on the current device, once per
+// device for each `done` (one bit per device; safe under concurrent callers).
+inline int32_t raise_lds_limit(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return WOQ_EHIP;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return WOQ_OK;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess) return WOQ_EHIP;
+  done.fetch_or(bit, std::memory_order_acq_rel);
+  return WOQ_OK;
+}
 
 #define WOQ_HIP_TRY(expr)                         \
   do {                                            \
