@@ -11,9 +11,9 @@
 //   host); H += damp * mean(diag H) * I.
 // * The upper Cholesky factor U of H^-1 (H^-1 = U^T U) without forming H^-1:
 //   with J the reversal permutation, J H J = L L^T (lower Cholesky) gives
-//   H = (J L J)(J L J)^T, so U = (J L J)^-1 = J L^-1 J.  An unblocked
-//   right-looking Cholesky and a right-looking triangular inverse, two
-//   launches per column each.
+//   H = (J L J)(J L J)^T, so U = (J L J)^-1 = J L^-1 J.  A right-looking
+//   Cholesky and triangular inverse in panels of 32 columns: two small launches
+//   per column inside the panel, one tiled float64 update of the rest per panel.
 // * The sweep is independent for every output row: a row's codes, scales and
 //   updates use only its own weights and the shared U.  Per block of whole
 //   groups (at least 128 columns), one thread per row keeps the block's weights
@@ -127,13 +127,48 @@ __global__ __launch_bounds__(256) void gptq_chol_col_kernel(double* __restrict__
   if (blockIdx.x == 0 && threadIdx.x == 0) dg[j] = d;
 }
 
-// Cholesky, trailing update after column j: A[i][c] -= A[i][j] A[c][j] for j < c <= i.
-__global__ __launch_bounds__(256) void gptq_chol_update_kernel(double* __restrict__ a, int64_t k, int64_t j) {
-  const int64_t m = k - j - 1;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < m * m; e += (int64_t)gridDim.x * 256) {
-    const int64_t i = j + 1 + e / m, c = j + 1 + e % m;
+// Cholesky, the rest of column j's panel: A[i][c] -= A[i][j] A[c][j] for
+// j < c < cend, c <= i (every row below; the later columns wait for the panel's
+// trailing update).
+__global__ __launch_bounds__(256) void gptq_chol_update_kernel(double* __restrict__ a, int64_t k, int64_t j,
+                                                               int64_t cend) {
+  const int64_t rows = k - j - 1, w = cend - j - 1;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < rows * w; e += (int64_t)gridDim.x * 256) {
+    const int64_t i = j + 1 + e / w, c = j + 1 + e % w;
     if (c <= i) a[i * k + c] -= a[i * k + j] * a[c * k + j];
   }
+}
+
+// Panel of columns [j0, j0 + b) done: A[i][c] -= A[i][t] A[c][t] for t = j0 .. j0+b-1
+// in order, for i, c >= j0 + b.  64 x 64 tiles on and below the diagonal (the
+// part of a diagonal tile above it is updated too and never read); the panel's
+// rows of both tiles staged in LDS.
+constexpr int kPanel = 32;
+
+__global__ __launch_bounds__(256) void gptq_chol_trail_kernel(double* __restrict__ a, int64_t k, int64_t j0,
+                                                              int32_t b) {
+  if (blockIdx.x > blockIdx.y) return;   // above the diagonal
+  __shared__ double pi[64][kPanel + 1];
+  __shared__ double pc[64][kPanel + 1];
+  const int64_t base = j0 + b;
+  const int64_t i0 = base + (int64_t)blockIdx.y * 64, c0 = base + (int64_t)blockIdx.x * 64;
+  for (int e = threadIdx.x; e < 64 * kPanel; e += 256) {
+    const int r = e / kPanel, t = e % kPanel;
+    pi[r][t] = (i0 + r < k && t < b) ? a[(i0 + r) * k + j0 + t] : 0.0;
+    pc[r][t] = (c0 + r < k && t < b) ? a[(c0 + r) * k + j0 + t] : 0.0;
+  }
+  __syncthreads();
+  const int ti = threadIdx.x / 16, tc = threadIdx.x % 16;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t i = i0 + 4 * ti + u, c = c0 + 4 * tc + v;
+      if (i >= k || c >= k) continue;
+      double acc = a[i * k + c];
+      for (int t = 0; t < b; ++t) acc -= pi[4 * ti + u][t] * pc[4 * tc + v][t];
+      a[i * k + c] = acc;
+    }
 }
 
 __global__ __launch_bounds__(256) void gptq_identity_kernel(double* __restrict__ tm, int64_t k) {
@@ -149,14 +184,44 @@ __global__ __launch_bounds__(256) void gptq_tri_row_kernel(double* __restrict__ 
   if (j <= k0) tm[k0 * k + j] /= dg[k0];
 }
 
-// ... and pushed down: T[i][j] -= L[i][k0] T[k0][j] for i > k0, j <= k0.
+// ... and pushed down the rest of its panel: T[i][j] -= L[i][k0] T[k0][j] for
+// k0 < i < rend, j <= k0.
 __global__ __launch_bounds__(256) void gptq_tri_update_kernel(double* __restrict__ tm, const double* __restrict__ a,
-                                                              int64_t k, int64_t k0) {
-  const int64_t rows = k - k0 - 1, cols = k0 + 1;
+                                                              int64_t k, int64_t k0, int64_t rend) {
+  const int64_t rows = rend - k0 - 1, cols = k0 + 1;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < rows * cols; e += (int64_t)gridDim.x * 256) {
     const int64_t i = k0 + 1 + e / cols, j = e % cols;
     tm[i * k + j] -= a[i * k + k0] * tm[k0 * k + j];
   }
+}
+
+// Panel of rows [p0, p0 + b) final: T[i][j] -= L[i][r] T[r][j] for r = p0 .. p0+b-1
+// in order, for i >= p0 + b, j < p0 + b (T[r][j] is 0 for j > r, which changes
+// nothing).  64 x 64 tiles; L's panel columns and T's panel rows staged in LDS.
+__global__ __launch_bounds__(256) void gptq_tri_trail_kernel(double* __restrict__ tm, const double* __restrict__ a,
+                                                             int64_t k, int64_t p0, int32_t b) {
+  __shared__ double li[64][kPanel + 1];
+  __shared__ double tr[kPanel][65];
+  const int64_t pend = p0 + b;
+  const int64_t i0 = pend + (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * 64;
+  for (int e = threadIdx.x; e < 64 * kPanel; e += 256) {
+    const int r = e / kPanel, t = e % kPanel;
+    li[r][t] = (i0 + r < k && t < b) ? a[(i0 + r) * k + p0 + t] : 0.0;
+    const int t2 = e / 64, jj = e % 64;
+    tr[t2][jj] = (t2 < b && j0 + jj < pend) ? tm[(p0 + t2) * k + j0 + jj] : 0.0;
+  }
+  __syncthreads();
+  const int ti = threadIdx.x / 16, tj = threadIdx.x % 16;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t i = i0 + 4 * ti + u, j = j0 + 4 * tj + v;
+      if (i >= k || j >= pend) continue;
+      double acc = tm[i * k + j];
+      for (int t = 0; t < b; ++t) acc -= li[4 * ti + u][t] * tr[t][4 * tj + v];
+      tm[i * k + j] = acc;
+    }
 }
 
 // U[i][j] = T[K-1-i][K-1-j] (upper triangular: i <= j).
@@ -315,18 +380,34 @@ int32_t run_gptq(const float* w, const uint16_t* x, int64_t t, int64_t n, int64_
     hipLaunchKernelGGL(gptq_weights_kernel, dim3(flat_grid(n * k)), dim3(256), 0, s, w, dperm, ddead, n, k, wc);
     hipLaunchKernelGGL(gptq_identity_kernel, dim3(flat_grid(k * k)), dim3(256), 0, s, tm, k);
     st = hip_status(hipGetLastError());
-    for (int64_t j = 0; j < k && st == WOQ_OK; ++j) {
-      hipLaunchKernelGGL(gptq_chol_col_kernel, dim3(flat_grid(k - j)), dim3(256), 0, s, a, k, j, dg);
-      if (j + 1 < k)
-        hipLaunchKernelGGL(gptq_chol_update_kernel, dim3(flat_grid((k - j - 1) * (k - j - 1))), dim3(256), 0, s, a,
-                           k, j);
+    // Panels of kPanel columns: inside a panel the column kernels touch only the
+    // panel; one tiled launch then applies the whole panel to the rest.  Every
+    // entry takes the same updates in the same order as column by column.
+    for (int64_t j0 = 0; j0 < k && st == WOQ_OK; j0 += kPanel) {
+      const int64_t jend = std::min<int64_t>(k, j0 + kPanel);
+      for (int64_t j = j0; j < jend; ++j) {
+        hipLaunchKernelGGL(gptq_chol_col_kernel, dim3(flat_grid(k - j)), dim3(256), 0, s, a, k, j, dg);
+        if (j + 1 < jend)
+          hipLaunchKernelGGL(gptq_chol_update_kernel, dim3(flat_grid((k - j - 1) * (jend - j - 1))), dim3(256), 0, s,
+                             a, k, j, jend);
+      }
+      if (jend < k) {
+        const unsigned t = (unsigned)((k - jend + 63) / 64);
+        hipLaunchKernelGGL(gptq_chol_trail_kernel, dim3(t, t), dim3(256), 0, s, a, k, j0, (int32_t)(jend - j0));
+      }
       st = hip_status(hipGetLastError());
     }
-    for (int64_t k0 = 0; k0 < k && st == WOQ_OK; ++k0) {
-      hipLaunchKernelGGL(gptq_tri_row_kernel, dim3(flat_grid(k0 + 1)), dim3(256), 0, s, tm, dg, k, k0);
-      if (k0 + 1 < k)
-        hipLaunchKernelGGL(gptq_tri_update_kernel, dim3(flat_grid((k - k0 - 1) * (k0 + 1))), dim3(256), 0, s, tm, a,
-                           k, k0);
+    for (int64_t p0 = 0; p0 < k && st == WOQ_OK; p0 += kPanel) {
+      const int64_t pend = std::min<int64_t>(k, p0 + kPanel);
+      for (int64_t k0 = p0; k0 < pend; ++k0) {
+        hipLaunchKernelGGL(gptq_tri_row_kernel, dim3(flat_grid(k0 + 1)), dim3(256), 0, s, tm, dg, k, k0);
+        if (k0 + 1 < pend)
+          hipLaunchKernelGGL(gptq_tri_update_kernel, dim3(flat_grid((pend - k0 - 1) * (k0 + 1))), dim3(256), 0, s, tm,
+                             a, k, k0, pend);
+      }
+      if (pend < k)
+        hipLaunchKernelGGL(gptq_tri_trail_kernel, dim3((unsigned)((pend + 63) / 64), (unsigned)((k - pend + 63) / 64)),
+                           dim3(256), 0, s, tm, a, k, p0, (int32_t)(pend - p0));
       st = hip_status(hipGetLastError());
     }
     for (int64_t c0 = 0; c0 < k && st == WOQ_OK; c0 += bcols) {
