@@ -50,7 +50,8 @@ typedef enum {
   WOQ_EWORKSPACE = 6,    /* workspace missing or smaller than woq_linear_workspace_bytes() */
   WOQ_EUNSUPPORTED = 7,  /* valid input this build has no kernel for (group size, sizes >= 2^31) */
   WOQ_EALIGN = 8,        /* a pointer lacks the alignment stated for it below */
-  WOQ_EHIP = 9           /* the HIP runtime reported an error */
+  WOQ_EHIP = 9,          /* the HIP runtime reported an error */
+  WOQ_ENOTPD = 10        /* GPTQ: the damped calibration matrix is not positive definite (data-dependent) */
 } woq_status;
 
 typedef enum { WOQ_F32 = 0, WOQ_BF16 = 1 } woq_dtype;
@@ -516,7 +517,10 @@ size_t woq_linear_int4_groups_zp4_workspace_bytes(int64_t m, int64_t n, int64_t 
  * Errors: WOQ_EINVAL (NULL pointer, negative size, act_order not 0/1, damp
  *   negative or not finite), WOQ_EGROUP (group < 1 or not dividing k),
  *   WOQ_EUNSUPPORTED (group > 256, k >= 2^20), WOQ_ENONFINITE (a weight NaN or
- *   infinite), WOQ_EALIGN, WOQ_EHIP.
+ *   infinite), WOQ_ENOTPD (a Cholesky pivot of the damped, reordered matrix
+ *   is not positive or its root is not finite: damp = 0 with fewer
+ *   calibration rows than inputs can do this; codes, scales and zeros are
+ *   then unspecified), WOQ_EALIGN, WOQ_EHIP.
  */
 int32_t woq_gptq_quantize(const float* w, const void* x_bf16, int64_t t, int64_t n, int64_t k, int32_t group,
                           int32_t act_order, double damp, uint8_t* codes, float* scale, uint8_t* zero,

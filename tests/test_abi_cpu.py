@@ -47,8 +47,9 @@ def test_status_strings(lib):
 
 
 @pytest.mark.parametrize("m,n,k,g,path", [
-    (1, 4096, 4096, 128, "gemv_mfma"), (4, 14336, 4096, 32, "gemv_mfma"),
-    (1, 8192, 28672, 128, "gemv_mfma"), (1, 64, 40960, 128, "skinny_mfma"),
+    (1, 4096, 4096, 128, "rows_dot2"), (4, 14336, 4096, 32, "rows_dot2"),
+    (1, 8192, 28672, 128, "rows_dot2"), (1, 64, 40960, 128, "skinny_mfma"),
+    (2, 4096, 32768, 64, "rows_dot2"), (1, 4096, 32800, 32, "skinny_mfma"),
     (5, 4096, 4096, 128, "skinny_mfma"), (16, 14336, 4096, 32, "skinny_mfma"),
     (17, 4096, 4096, 128, "skinny_mfma"), (32, 14336, 4096, 256, "skinny_mfma"),
     (33, 4096, 4096, 128, "gemm_mfma"), (2048, 14336, 4096, 128, "gemm_mfma"),
@@ -56,6 +57,16 @@ def test_status_strings(lib):
 ])
 def test_plan_paths(m, n, k, g, path):
     assert f"path={path}" in woq.linear_plan(m, n, k, g)
+
+
+def test_plan_decode_kernels(monkeypatch):
+    # canonical rows at m <= 4 stream through the row kernel: rows per workgroup by shape
+    for (m, n, k), u in (((1, 14336, 4096), 4), ((1, 4096, 14336), 16), ((1, 4096, 4096), 4),
+                         ((1, 1024, 4096), 4), ((3, 14336, 4096), 4), ((2, 28672, 4096), 4)):
+        plan = woq.linear_plan(m, n, k, 128)
+        assert f"path=rows_dot2 rows_per_group={u} waves={(k + 2047) // 2048} " in plan, plan
+    monkeypatch.setenv("WOQ_DECODE_MFMA", "1")
+    assert "path=gemv_mfma" in woq.linear_plan(1, 4096, 4096, 128)
 
 
 @pytest.mark.parametrize("m,n,tail", [

@@ -116,3 +116,57 @@ def test_gptq_full_size_sampled(woq, act_order):
     q, s, z, o = got
     sub = (q[torch.from_numpy(rows).cuda()], s[torch.from_numpy(rows).cuda()], z[torch.from_numpy(rows).cuda()], o)
     _compare(sub, oracle.gptq_quantize(w[rows], x, group, act_order=act_order), f"full act_order={act_order}")
+
+
+def _singular_calibration(t, k, seed):
+    """Inputs 0 and 1 equal (2.0 in row 0 only) and orthogonal to every other
+    input: H has the 2x2 block [[4, 4], [4, 4]] apart from the rest, so with no
+    damping the factorization meets an exactly zero pivot in any column order."""
+    x = workloads.calibration_bf16(t, k, seed=seed)
+    x[:, :2] = 0
+    x[0, :] = 0
+    x[0, :2] = 0x4000                                   # bf16 2.0
+    return x
+
+
+def test_gptq_not_positive_definite(woq):
+    _say("gptq singular calibration matrix, no damping")
+    n, k, t, group = 8, 64, 16, 32
+    w = workloads.weight(n, k, seed=41)
+    x = _singular_calibration(t, k, 42)
+    with pytest.raises(np.linalg.LinAlgError):
+        oracle.gptq_quantize(w, x, group, damp=0.0)
+    for act_order in (False, True):
+        with pytest.raises(woq_mod.WoqError) as e:
+            woq.gptq_quantize(torch.from_numpy(w).cuda(), to_dev_bf16(x), group, act_order=act_order, damp=0.0)
+        assert e.value.name == "WOQ_ENOTPD"
+    # the same inputs with damping factor fine on both sides
+    got = woq.gptq_quantize(torch.from_numpy(w).cuda(), to_dev_bf16(x), group, damp=0.01)
+    torch.cuda.synchronize()
+    _compare(got, oracle.gptq_quantize(w, x, group, damp=0.01), "singular x, damp=0.01")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("act_order", [False, True])
+def test_gptq_long_rows_sampled(woq, act_order):
+    """K = 14336 (the down projection's input width): 448 panels of the
+    blocked factorization; codes, scales, zeros and order of sampled rows equal
+    to the oracle's."""
+    n, k, t, group = 4096, 14336, 256, 128
+    _say(f"gptq long rows n={n} k={k} t={t} group={group} act_order={act_order}")
+    w = workloads.weight(n, k, seed=61)
+    x = workloads.calibration_bf16(t, k, seed=62)
+    wd, xd = torch.from_numpy(w).cuda(), to_dev_bf16(x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    got = woq.gptq_quantize(wd, xd, group, act_order=act_order)
+    torch.cuda.synchronize()
+    _say(f"  gpu gptq {time.perf_counter() - t0:.3f} s")
+    rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(7).choice(n, 6, replace=False)]))
+    q, s, z, o = got
+    idx = torch.from_numpy(rows).cuda()
+    t0 = time.perf_counter()
+    want = oracle.gptq_quantize(w[rows], x, group, act_order=act_order)
+    _say(f"  oracle gptq on {len(rows)} rows {time.perf_counter() - t0:.1f} s")
+    _compare((q[idx], s[idx], z[idx], o), want, f"long rows act_order={act_order}")

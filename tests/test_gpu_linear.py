@@ -90,7 +90,7 @@ def test_linear_small_all_outputs(woq, m, n, k, group, with_bias, with_order, ou
     check_linear(y, _ref(host, group), f"m={m} n={n} k={k} g={group}")
 
 
-# Decode-path (m <= 4) launch variants: WOQ_GEMV_WAVES sets the planner's
+# Tile-GEMV (m <= 4) launch variants: WOQ_GEMV_WAVES sets the planner's
 # target number of waves, which at these small sizes forces each steps-per-wave
 # class (4, 8, 12/16), one or many waves per workgroup, trailing waves with a
 # partial or empty range, group offsets that do not start on a multiple of 4
@@ -113,6 +113,7 @@ GEMV_VARIANTS = [
 
 @pytest.mark.parametrize("m,n,k,group,with_bias,with_order,target,shape", GEMV_VARIANTS)
 def test_gemv_launch_variants(woq, monkeypatch, m, n, k, group, with_bias, with_order, target, shape):
+    monkeypatch.setenv("WOQ_DECODE_MFMA", "1")   # canonical rows would take the row-streaming kernel
     if target:
         monkeypatch.setenv("WOQ_GEMV_WAVES", str(target))
     else:
@@ -266,8 +267,7 @@ def _sample_rows(n, seed, count=48):
     return rows
 
 
-FULL = list(workloads.DECODE) + list(workloads.PREFILL) + list(workloads.ACTORDER) + \
-    [c for c in workloads.SWEEP if c.group in (32, 128) or c.m in (1, 128)]
+FULL = list(workloads.DECODE) + list(workloads.PREFILL) + list(workloads.ACTORDER) + list(workloads.SWEEP)
 
 
 @pytest.mark.slow

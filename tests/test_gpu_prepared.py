@@ -83,8 +83,17 @@ CASES = [
 ]
 
 
+@pytest.fixture
+def tile_decode(monkeypatch):
+    """Canonical weights at m <= 4 on the same tile kernel the prepared layout
+    runs on (they would otherwise stream through the row kernel, whose
+    float32 rounding order differs): the bitwise comparisons below are about
+    the two layouts, not about two kernels."""
+    monkeypatch.setenv("WOQ_DECODE_MFMA", "1")
+
+
 @pytest.mark.parametrize("m,n,k,group,with_bias,with_order", CASES)
-def test_linear_prepared(woq, m, n, k, group, with_bias, with_order):
+def test_linear_prepared(woq, tile_decode, m, n, k, group, with_bias, with_order):
     _say(f"prepared linear m={m} n={n} k={k} g={group} bias={with_bias} order={with_order} "
          f"plan: {woq.linear_plan(m, n, k, group, with_order)}")
     dev, host = _make(woq, m, n, k, group, seed=5000 + m + n + k, with_bias=with_bias,
@@ -103,7 +112,7 @@ def test_linear_prepared(woq, m, n, k, group, with_bias, with_order):
 @pytest.mark.parametrize("target,m,n,k,group", [(1, 1, 40, 4096, 128), (6, 1, 48, 2048, 64),
                                                 (3, 1, 40, 1536, 32), (1, 4, 64, 4096, 128),
                                                 (0, 1, 33, 4160, 64)])
-def test_gemv_variants_prepared(woq, monkeypatch, target, m, n, k, group):
+def test_gemv_variants_prepared(woq, tile_decode, monkeypatch, target, m, n, k, group):
     if target:
         monkeypatch.setenv("WOQ_GEMV_WAVES", str(target))
     else:
@@ -125,7 +134,7 @@ FULL = list(workloads.DECODE) + list(workloads.ACTORDER) + list(workloads.PREFIL
 
 @pytest.mark.slow
 @pytest.mark.parametrize("case", FULL, ids=lambda c: c.name)
-def test_full_size_prepared_bitwise(woq, case):
+def test_full_size_prepared_bitwise(woq, tile_decode, case):
     """At full size the prepared call must reproduce the canonical call bit for
     bit (the canonical call is checked against the oracle by the linear tests);
     a few sampled columns are also checked against the oracle directly."""

@@ -158,7 +158,8 @@ def test_linear_small(woq, m, n, k, group, with_bias, with_order, out):
 
 @pytest.mark.parametrize("m,n,k,group", [(1, 100, 1024, 32), (3, 64, 4096, 128), (16, 300, 512, 64),
                                          (130, 256, 640, 128)])
-def test_linear_prepared_is_bit_identical(woq, m, n, k, group):
+def test_linear_prepared_is_bit_identical(woq, monkeypatch, m, n, k, group):
+    monkeypatch.setenv("WOQ_DECODE_MFMA", "1")   # the canonical call on the prepared layout's tile kernel
     _say(f"sym16 prepared m={m} n={n} k={k} g={group}")
     dev, host = _make(woq, m, n, k, group, seed=m + n + k, with_bias=True)
     y = woq.linear_int4_sym(dev["x"], dev["packed"], dev["scale"], bias=dev["bias"], group=group,

@@ -21,6 +21,7 @@ import numpy as np
 import pytest
 
 import oracle
+import workloads
 
 
 def oracle_impl():
@@ -207,3 +208,19 @@ def test_mutant_is_caught(name):
         except (AssertionError, ValueError, IndexError, pytest.fail.Exception) as exc:
             caught.append((check.__name__, type(exc).__name__))
     assert caught, f"planted mistake {name} passed every check"
+
+
+def test_gptq_refuses_a_singular_undamped_matrix():
+    """Without damping, two equal input channels orthogonal to the rest make H
+    exactly singular: the inverse the method factors does not exist, and the
+    oracle raises instead of returning codes from a meaningless factor."""
+    n, k, t, group = 4, 32, 8, 16
+    w = workloads.weight(n, k, seed=43)
+    x = workloads.calibration_bf16(t, k, seed=44)
+    x[:, :2] = 0
+    x[0, :] = 0
+    x[0, :2] = 0x4000
+    with pytest.raises(np.linalg.LinAlgError):
+        oracle.gptq_quantize(w, x, group, damp=0.0)
+    q, s, z, _ = oracle.gptq_quantize(w, x, group, damp=0.01)
+    assert q.shape == (n, k) and np.all(np.isfinite(s))

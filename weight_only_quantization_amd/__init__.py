@@ -62,6 +62,7 @@ _LIB: Optional[ctypes.CDLL] = None
 STATUS = {
     0: "WOQ_OK", 1: "WOQ_EINVAL", 2: "WOQ_ESHAPE", 3: "WOQ_EGROUP", 4: "WOQ_ENONFINITE",
     5: "WOQ_ERANGE", 6: "WOQ_EWORKSPACE", 7: "WOQ_EUNSUPPORTED", 8: "WOQ_EALIGN", 9: "WOQ_EHIP",
+    10: "WOQ_ENOTPD",
 }
 F32, BF16 = 0, 1
 
@@ -155,15 +156,48 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
-def _need(t: torch.Tensor, dtype: torch.dtype, name: str):
+def _need(t: torch.Tensor, dtype: torch.dtype, name: str, gpu: bool = True):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
+    if gpu and not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _check_sizes(m: int, n: int, k: int, *, sized=(), bias=None, order=None, out=None):
+    """Every operand must hold exactly what the kernels address for (m, n, k).
+
+    The kernels size their buffer descriptors from these numbers, not from the
+    allocations, so a short tensor would be read or written out of bounds on the
+    device: refuse it here instead.  ``sized`` lists (name, tensor, elements).
+    """
+    for name, t, numel in sized:
+        if t is not None and t.numel() != numel:
+            raise ValueError(f"{name} holds {t.numel()} elements, expected {numel} for [{n}, {k}]")
+    if bias is not None and bias.numel() != n:
+        raise ValueError(f"bias holds {bias.numel()} elements, expected N = {n}")
+    if order is not None and order.numel() != k:
+        raise ValueError(f"order holds {order.numel()} elements, expected K = {k}")
+    if out is not None and tuple(out.shape) != (m, n):
+        raise ValueError(f"out must be [{m}, {n}], got {list(out.shape)}")
+
+
+def _on_gpu(x: torch.Tensor, **named):
+    """x on the GPU, and every other named tensor (None skipped) on x's device."""
+    if not x.is_cuda:
+        raise ValueError("x must be on the GPU")
+    for name, t in named.items():
+        if t is not None and t.device != x.device:
+            raise ValueError(f"{name} must be on x's device ({x.device}), got {t.device}")
+
+
+def _groups(k: int, group: int) -> int:
+    """Groups per row, or 0 when the group size is invalid (the library then
+    reports it without touching memory)."""
+    return k // group if group > 0 and k % group == 0 else 0
 
 
 def quantize_groups(w: torch.Tensor, group: int = 128, symmetric: bool = False):
@@ -348,7 +382,7 @@ def linear_int4_groups_prepared(x: torch.Tensor, prepared: torch.Tensor, scale: 
 
     N comes from scale [N, K/G], K from x [M, K], the group from both.
     """
-    _need(scale, torch.float32, "scale")
+    _need(scale, torch.float32, "scale", gpu=False)
     if x.dim() != 2 or scale.dim() != 2 or scale.shape[1] == 0:
         raise ValueError("x must be [M, K] and scale [N, K/G]")
     n, k = scale.shape[0], x.shape[1]
@@ -371,8 +405,8 @@ def linear_int4_groups(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tenso
     None.  Returns y [M, N] of out_dtype (bfloat16 or float32).  Asynchronous
     on the current stream.
     """
-    _need(packed, torch.uint8, "packed")
-    _need(scale, torch.float32, "scale")
+    _need(packed, torch.uint8, "packed", gpu=False)
+    _need(scale, torch.float32, "scale", gpu=False)
     n, k, group = _weight_dims(packed, scale, group)
     if x.dim() == 2 and x.shape[1] != k:
         raise ValueError(f"x has {x.shape[1]} inputs, the weight {k}")
@@ -383,26 +417,35 @@ def linear_int4_groups(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tenso
 def _linear(x, weights, scale, zero, bias, order, n, k, group, out_dtype, out, workspace,
             prepared: bool, sym16: bool = False):
     lib = load()
-    _need(x, torch.bfloat16, "x")
-    _need(weights, torch.uint8, "prepared" if prepared else "packed")
+    _need(x, torch.bfloat16, "x", gpu=False)
+    _need(weights, torch.uint8, "prepared" if prepared else "packed", gpu=False)
     if sym16:
-        _need(scale, torch.float16, "scale")
+        _need(scale, torch.float16, "scale", gpu=False)
     else:
-        _need(scale, torch.float32, "scale")
-        _need(zero, torch.uint8, "zero")
+        _need(scale, torch.float32, "scale", gpu=False)
+        _need(zero, torch.uint8, "zero", gpu=False)
     if bias is not None:
-        _need(bias, torch.float32, "bias")
+        _need(bias, torch.float32, "bias", gpu=False)
     if order is not None:
-        _need(order, torch.int32, "order")
-    if x.dim() != 2:
-        raise ValueError("x must be [M, K]")
+        _need(order, torch.int32, "order", gpu=False)
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be [M, {k}]")
     m = x.shape[0]
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype must be float32 or bfloat16")
+    if out is not None:
+        _need(out, out_dtype, "out", gpu=False)
+    ng = _groups(k, group)
+    sized = [("scale", scale, n * ng), ("zero", zero, n * ng)] if ng else []
+    if not prepared:
+        sized.append(("packed", weights, n * (k // 2)))
+    elif weights.numel() < prepared_bytes(n, k):
+        raise ValueError("prepared buffer is smaller than the layout of [n, k]")
+    _check_sizes(m, n, k, sized=sized, bias=bias, order=order, out=out)
+    _on_gpu(x, weights=weights, scale=scale, zero=zero, bias=bias, order=order, out=out,
+            workspace=workspace)
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=x.device)
-    else:
-        _need(out, out_dtype, "out")
     need = int(lib.woq_linear_workspace_bytes(m, n, k, group, int(order is not None)))
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
@@ -461,26 +504,29 @@ def linear_int4_groups_zp4(x: torch.Tensor, packed: torch.Tensor, scale: torch.T
                            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """linear_int4_groups with packed 4-bit zero points [N, ceil(K/G / 2)].  Asynchronous."""
     lib = load()
-    _need(x, torch.bfloat16, "x")
-    _need(packed, torch.uint8, "packed")
-    _need(scale, torch.float32, "scale")
-    _need(zero_packed, torch.uint8, "zero_packed")
+    _need(x, torch.bfloat16, "x", gpu=False)
+    _need(packed, torch.uint8, "packed", gpu=False)
+    _need(scale, torch.float32, "scale", gpu=False)
+    _need(zero_packed, torch.uint8, "zero_packed", gpu=False)
     if bias is not None:
-        _need(bias, torch.float32, "bias")
+        _need(bias, torch.float32, "bias", gpu=False)
     if order is not None:
-        _need(order, torch.int32, "order")
+        _need(order, torch.int32, "order", gpu=False)
     n, k, group = _weight_dims(packed, scale, group)
     if x.dim() != 2 or x.shape[1] != k:
         raise ValueError("x must be [M, K]")
-    if zero_packed.numel() != n * ((k // group + 1) // 2):
-        raise ValueError("zero_packed must hold N * ceil(K/G / 2) bytes")
     m = x.shape[0]
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype must be float32 or bfloat16")
+    if out is not None:
+        _need(out, out_dtype, "out", gpu=False)
+    ng = _groups(k, group)
+    _check_sizes(m, n, k, sized=[("scale", scale, n * ng), ("zero_packed", zero_packed, n * ((ng + 1) // 2))]
+                 if ng else [], bias=bias, order=order, out=out)
+    _on_gpu(x, packed=packed, scale=scale, zero_packed=zero_packed, bias=bias, order=order, out=out,
+            workspace=workspace)
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=x.device)
-    else:
-        _need(out, out_dtype, "out")
     need = int(lib.woq_linear_int4_groups_zp4_workspace_bytes(m, n, k, group, int(order is not None)))
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
@@ -562,7 +608,7 @@ def linear_int4_sym(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tensor,
     buffer of :func:`prepare_int4`); scale float16 [N, K/G]; bias float32 [N] or
     None; order int32 [K] or None.  Asynchronous on the current stream.
     """
-    _need(scale, torch.float16, "scale")
+    _need(scale, torch.float16, "scale", gpu=False)
     if x.dim() != 2 or scale.dim() != 2 or scale.shape[1] == 0:
         raise ValueError("x must be [M, K] and scale [N, K/G]")
     n, k = scale.shape[0], x.shape[1]
@@ -587,7 +633,7 @@ def linear_int4_groups_grouped(x: torch.Tensor, mats, prepared: bool = False,
     matrices share one kernel launch.  Asynchronous on the current stream.
     """
     lib = load()
-    _need(x, torch.bfloat16, "x")
+    _need(x, torch.bfloat16, "x", gpu=False)
     if x.dim() != 2:
         raise ValueError("x must be [M, K]")
     if not 1 <= len(mats) <= 4:
@@ -596,28 +642,44 @@ def linear_int4_groups_grouped(x: torch.Tensor, mats, prepared: bool = False,
     group = None
     ns = []
     for i, (w, sc, z, b) in enumerate(mats):
-        _need(w, torch.uint8, f"weights[{i}]")
-        _need(sc, torch.float32, f"scale[{i}]")
-        _need(z, torch.uint8, f"zero[{i}]")
+        _need(w, torch.uint8, f"weights[{i}]", gpu=False)
+        _need(sc, torch.float32, f"scale[{i}]", gpu=False)
+        _need(z, torch.uint8, f"zero[{i}]", gpu=False)
         if b is not None:
-            _need(b, torch.float32, f"bias[{i}]")
+            _need(b, torch.float32, f"bias[{i}]", gpu=False)
         if sc.dim() != 2 or sc.shape[1] == 0:
             raise ValueError("scale must be [N, K/G]")
         g = k // sc.shape[1]
         if group is not None and g != group:
             raise ValueError("all matrices must share the group size")
         group = g
-        ns.append(sc.shape[0])
-        need = prepared_bytes(sc.shape[0], k) if prepared else sc.shape[0] * k // 2
-        if w.numel() < need:
-            raise ValueError(f"weights[{i}] hold fewer bytes than an [{sc.shape[0]}, {k}] weight")
+        n_i = sc.shape[0]
+        ns.append(n_i)
+        ng = _groups(k, g)
+        sized = [(f"scale[{i}]", sc, n_i * ng), (f"zero[{i}]", z, n_i * ng)] if ng else []
+        if prepared:
+            if w.numel() < prepared_bytes(n_i, k):
+                raise ValueError(f"weights[{i}] hold fewer bytes than an [{n_i}, {k}] weight")
+        else:
+            sized.append((f"weights[{i}]", w, n_i * (k // 2)))
+        _check_sizes(m, n_i, k, sized=sized, bias=b)
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype must be float32 or bfloat16")
+    made_outs = outs is None
     if outs is None:
-        outs = [torch.empty((m, n), dtype=out_dtype, device=x.device) for n in ns]
+        outs = [None] * len(mats)
     else:
+        if len(outs) != len(mats):
+            raise ValueError("one output per matrix")
         for i, o in enumerate(outs):
-            _need(o, out_dtype, f"outs[{i}]")
+            _need(o, out_dtype, f"outs[{i}]", gpu=False)
+            _check_sizes(m, ns[i], k, out=o)
+    for i, (w, sc, z, b) in enumerate(mats):
+        _on_gpu(x, **{f"weights_{i}": w, f"scale_{i}": sc, f"zero_{i}": z, f"bias_{i}": b,
+                      f"outs_{i}": None if outs is None else outs[i]})
+    _on_gpu(x, workspace=workspace)
+    if made_outs:
+        outs = [torch.empty((m, n), dtype=out_dtype, device=x.device) for n in ns]
     need = max(int(lib.woq_linear_workspace_bytes(m, n, k, group, 0)) for n in ns)
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
@@ -682,11 +744,11 @@ def linear_mxfp4(x: torch.Tensor, blocks: torch.Tensor, scales: torch.Tensor,
     [N, K/32]; bias float32 [N] or None.  Asynchronous on the current stream.
     """
     lib = load()
-    _need(x, torch.bfloat16, "x")
-    _need(blocks, torch.uint8, "blocks")
-    _need(scales, torch.uint8, "scales")
+    _need(x, torch.bfloat16, "x", gpu=False)
+    _need(blocks, torch.uint8, "blocks", gpu=False)
+    _need(scales, torch.uint8, "scales", gpu=False)
     if bias is not None:
-        _need(bias, torch.float32, "bias")
+        _need(bias, torch.float32, "bias", gpu=False)
     if x.dim() != 2 or scales.dim() != 2:
         raise ValueError("x must be [M, K] and scales [N, K/32]")
     m, k = x.shape
@@ -695,10 +757,12 @@ def linear_mxfp4(x: torch.Tensor, blocks: torch.Tensor, scales: torch.Tensor,
         raise ValueError("blocks, scales and x disagree on K")
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype must be float32 or bfloat16")
+    if out is not None:
+        _need(out, out_dtype, "out", gpu=False)
+    _check_sizes(m, n, k, bias=bias, out=out)
+    _on_gpu(x, blocks=blocks, scales=scales, bias=bias, out=out, workspace=workspace)
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=x.device)
-    else:
-        _need(out, out_dtype, "out")
     need = int(lib.woq_linear_workspace_bytes(m, n, k, 32, 0))
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
@@ -755,13 +819,13 @@ def linear_int4_rows(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tensor,
     [N]; bias float32 [N] or None; order int32 [K] or None.  Asynchronous.
     """
     lib = load()
-    _need(x, torch.bfloat16, "x")
-    _need(packed, torch.uint8, "packed")
-    _need(scale, torch.float32, "scale")
+    _need(x, torch.bfloat16, "x", gpu=False)
+    _need(packed, torch.uint8, "packed", gpu=False)
+    _need(scale, torch.float32, "scale", gpu=False)
     if bias is not None:
-        _need(bias, torch.float32, "bias")
+        _need(bias, torch.float32, "bias", gpu=False)
     if order is not None:
-        _need(order, torch.int32, "order")
+        _need(order, torch.int32, "order", gpu=False)
     if x.dim() != 2 or scale.dim() != 1:
         raise ValueError("x must be [M, K] and scale [N]")
     m, k = x.shape
@@ -770,10 +834,12 @@ def linear_int4_rows(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tensor,
         raise ValueError("packed must hold N * K / 2 bytes")
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype must be float32 or bfloat16")
+    if out is not None:
+        _need(out, out_dtype, "out", gpu=False)
+    _check_sizes(m, n, k, bias=bias, order=order, out=out)
+    _on_gpu(x, packed=packed, scale=scale, bias=bias, order=order, out=out, workspace=workspace)
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=x.device)
-    else:
-        _need(out, out_dtype, "out")
     need = int(lib.woq_linear_int4_rows_workspace_bytes(m, n, k, int(order is not None)))
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)

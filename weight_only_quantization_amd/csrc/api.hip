@@ -1,6 +1,9 @@
 // C ABI of libwoq.so: argument validation, kernel planning and dispatch.
-// Every check runs on the host before anything is enqueued, so a call that
-// fails validation has no effect.
+// Every argument check runs on the host before anything is enqueued, so a call
+// that fails validation has no effect.  Data-dependent errors (non-finite
+// weights, codes above 15, a factorization that fails) are found by the
+// kernels and reported after they ran; the outputs of such a call are then
+// unspecified.
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -124,7 +127,7 @@ bool gemv_plan(int64_t m, int64_t n, int64_t k, int32_t group, LinearPlan* p) {
 
 }  // namespace
 
-LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_order) {
+LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_order, bool rows_ok) {
   LinearPlan p;
   if (m == 0 || n == 0) return p;
   if (k == 0) {
@@ -132,6 +135,16 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
     return p;
   }
   p.gb = group >= 128 ? 4 : group / 32;
+  // Canonical rows at m <= 4 stream through the row kernel; WOQ_DECODE_MFMA
+  // keeps them on the tile GEMV (a tuning and test aid, read on every call).
+  if (rows_ok && rows_supported(m, k) && std::getenv("WOQ_DECODE_MFMA") == nullptr) {
+    p.path = 5;
+    p.rows_u = rows_per_group(m, n, k);
+    p.waves = rows_waves(k);
+    p.grid = (n + p.rows_u - 1) / p.rows_u;
+    p.prep = has_order ? 1 : 0;
+    return p;
+  }
   const bool force_skinny = std::getenv("WOQ_FORCE_SKINNY") != nullptr;   // tuning aid, read on every call
   if (m <= 4 && !force_skinny && k < ((int64_t)1 << 26) && gemv_plan(m, n, k, group, &p)) {
     p.prep = has_order ? 1 : 0;
@@ -180,7 +193,7 @@ LinearWorkspace linear_workspace_layout(int64_t m, int64_t n, int64_t k, int32_t
                                         bool has_order) {
   LinearWorkspace w;
   const LinearPlan p = linear_plan(m, n, k, group, has_order);
-  if ((p.path == 1 || p.path == 4) && has_order) {
+  if ((p.path == 1 || p.path == 4 || p.path == 5) && has_order) {
     w.xg_off = 0;
     w.xg_bytes = round256((size_t)m * (size_t)k * 2);
   } else if (p.path == 2) {
@@ -215,6 +228,7 @@ const char* woq_status_str(int32_t status) {
     case WOQ_EUNSUPPORTED: return "unsupported (group not in {32,64,128,256} or sizes too large)";
     case WOQ_EALIGN: return "pointer not aligned as required";
     case WOQ_EHIP: return "HIP runtime error";
+    case WOQ_ENOTPD: return "calibration matrix not positive definite (raise the damping)";
     default: return "unknown status";
   }
 }
@@ -528,9 +542,10 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
     return WOQ_EALIGN;
   const bool has_order = order != nullptr;
   if (has_order && !aligned(order, 16)) return WOQ_EALIGN;
-  const LinearPlan plan = linear_plan(m, n, k, group, has_order);
+  const LinearPlan plan = linear_plan(m, n, k, group, has_order, !prepared && !mx);
   const LinearWorkspace ws = linear_workspace_layout(m, n, k, group, has_order);
   const size_t zbytes = zp4 ? round256((size_t)n * (size_t)(k / group)) : 0;
+  if (plan.path == 2 && k >= kGemmMaxK) return WOQ_EUNSUPPORTED;
   if (ws.total + zbytes > 0) {
     if (!workspace || workspace_bytes < ws.total + zbytes) return WOQ_EWORKSPACE;
     if (!aligned(workspace, 256)) return WOQ_EALIGN;
@@ -572,16 +587,15 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
     }
     return launch_skinny(a, plan, s);
   }
-  if (plan.path == 4) {
+  if (plan.path == 4 || plan.path == 5) {
     if (has_order) {
       uint16_t* xg = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
       st = launch_prep(a.x, order, a.m, a.k, a.k, group, 0, xg, nullptr, m, s);
       if (st != WOQ_OK) return st;
       a.x = xg;
     }
-    return launch_gemv(a, plan, s);
+    return plan.path == 5 ? launch_rows(&a, 1, plan.rows_u, s) : launch_gemv(a, plan, s);
   }
-  if (k >= kGemmMaxK) return WOQ_EUNSUPPORTED;
   uint16_t* xg = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
   float* xs = reinterpret_cast<float*>(wsb + ws.xs_off);
   a.kpad = (a.k + 127) / 128 * 128;
@@ -687,8 +701,12 @@ int32_t woq_linear_int4_groups_grouped(const void* x_bf16, int64_t m, int32_t co
   if (m == 0) return WOQ_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   LinearPlan plan;
-  if (k > 0 && m <= 4 && rows16 > 0 && rows16 < kMaxDim && k < ((int64_t)1 << 26) &&
-      std::getenv("WOQ_FORCE_SKINNY") == nullptr && gemv_plan(m, rows16, k, group, &plan)) {
+  int64_t rows_total = 0;
+  for (int i = 0; i < count; ++i) rows_total += n[i];
+  const bool rows = k > 0 && !prepared && rows_supported(m, k) && rows_total > 0 &&
+                    std::getenv("WOQ_DECODE_MFMA") == nullptr;
+  if (rows || (k > 0 && m <= 4 && rows16 > 0 && rows16 < kMaxDim && k < ((int64_t)1 << 26) &&
+               std::getenv("WOQ_FORCE_SKINNY") == nullptr && gemv_plan(m, rows16, k, group, &plan))) {
     // one decode launch over all the matrices
     LinearArgs args[kMaxGrouped];
     int used = 0;
@@ -710,8 +728,10 @@ int32_t woq_linear_int4_groups_grouped(const void* x_bf16, int64_t m, int32_t co
       a.kpad = a.k;
       a.prepared = prepared;
     }
+    if (!used) return WOQ_OK;
+    if (rows) return launch_rows(args, used, rows_per_group(m, rows_total, k), s);
     plan.gb = group >= 128 ? 4 : group / 32;
-    return used ? launch_gemv_grouped(args, used, plan, s) : WOQ_OK;
+    return launch_gemv_grouped(args, used, plan, s);
   }
   // otherwise one call per matrix, in order, sharing the workspace
   for (int i = 0; i < count; ++i) {
@@ -771,6 +791,10 @@ int32_t woq_linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, int32_t 
                     "path=gemv_mfma fold_rows=%d waves=%d steps_per_wave=%d group_blocks=%d grid=%lld "
                     "prep=%s workspace=%zu",
                     p.fold_rows, p.waves, p.cnt, p.gb, (long long)p.grid, p.prep ? "gather" : "none", ws);
+      break;
+    case 5:
+      std::snprintf(buf, len, "path=rows_dot2 rows_per_group=%d waves=%d grid=%lld prep=%s workspace=%zu",
+                    p.rows_u, p.waves, (long long)p.grid, p.prep ? "gather" : "none", ws);
       break;
     default:
       std::snprintf(buf, len,

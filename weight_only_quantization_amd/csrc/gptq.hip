@@ -25,6 +25,8 @@
 #include <algorithm>
 #include <vector>
 
+#include <cfloat>
+
 #include "woq_internal.h"
 
 #pragma clang fp contract(off)
@@ -118,13 +120,19 @@ __global__ __launch_bounds__(256) void gptq_weights_kernel(const float* __restri
 }
 
 // Cholesky, column j: A[i][j] /= sqrt(A[j][j]) below the diagonal, the root to
-// dg[j] (A[j][j] itself is read by every thread and left alone).
+// dg[j] (A[j][j] itself is read by every thread and left alone).  A pivot that
+// is not positive, or a root that is not finite, means the damped matrix is
+// not positive definite: bit 1 of *flag.
 __global__ __launch_bounds__(256) void gptq_chol_col_kernel(double* __restrict__ a, int64_t k, int64_t j,
-                                                            double* __restrict__ dg) {
+                                                            double* __restrict__ dg, uint32_t* __restrict__ flag) {
   const int64_t i = j + 1 + (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const double d = sqrt(a[j * k + j]);
+  const double pv = a[j * k + j];
+  const double d = sqrt(pv);
   if (i < k) a[i * k + j] /= d;
-  if (blockIdx.x == 0 && threadIdx.x == 0) dg[j] = d;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    dg[j] = d;
+    if (!(pv > 0.0) || !(d <= DBL_MAX)) atomicOr(flag, 2u);
+  }
 }
 
 // Cholesky, the rest of column j's panel: A[i][c] -= A[i][j] A[c][j] for
@@ -386,7 +394,7 @@ int32_t run_gptq(const float* w, const uint16_t* x, int64_t t, int64_t n, int64_
     for (int64_t j0 = 0; j0 < k && st == WOQ_OK; j0 += kPanel) {
       const int64_t jend = std::min<int64_t>(k, j0 + kPanel);
       for (int64_t j = j0; j < jend; ++j) {
-        hipLaunchKernelGGL(gptq_chol_col_kernel, dim3(flat_grid(k - j)), dim3(256), 0, s, a, k, j, dg);
+        hipLaunchKernelGGL(gptq_chol_col_kernel, dim3(flat_grid(k - j)), dim3(256), 0, s, a, k, j, dg, flag);
         if (j + 1 < jend)
           hipLaunchKernelGGL(gptq_chol_update_kernel, dim3(flat_grid((k - j - 1) * (jend - j - 1))), dim3(256), 0, s,
                              a, k, j, jend);
@@ -397,6 +405,10 @@ int32_t run_gptq(const float* w, const uint16_t* x, int64_t t, int64_t n, int64_
       }
       st = hip_status(hipGetLastError());
     }
+    // A factor with a non-positive pivot is not used: report it before the inverse.
+    if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(&hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+    if (st == WOQ_OK) st = hip_status(hipStreamSynchronize(s));
+    if (st == WOQ_OK && (hflag & 2u)) st = WOQ_ENOTPD;
     for (int64_t p0 = 0; p0 < k && st == WOQ_OK; p0 += kPanel) {
       const int64_t pend = std::min<int64_t>(k, p0 + kPanel);
       for (int64_t k0 = p0; k0 < pend; ++k0) {

@@ -499,8 +499,11 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
       __builtin_amdgcn_s_waitcnt(wait_vmcnt((S - 2) * kLoads));
     // ... and everyone's have; everyone has also finished step i - 1, so its
     // slot takes step i - 1 + S.  A plain barrier: a __syncthreads fence would
-    // also wait for the loads still streaming into the other stages.
+    // also wait for the loads still streaming into the other stages.  The empty
+    // asm statements keep the compiler from moving LDS accesses across it.
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     if (i >= 1) issue_stage(slot == 0 ? S - 1 : slot - 1, i - 1 + S);
     compute(slot, i);
     slot = slot == S - 1 ? 0 : slot + 1;

@@ -33,9 +33,6 @@ namespace {
 constexpr int kStepK = 128;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kOffsetOOB = 0x80000000u;   // a buffer offset no descriptor covers
-// s_waitcnt immediate that waits for LDS traffic only: lgkmcnt(0), vmcnt and
-// expcnt at their maxima
-constexpr int kWaitLdsOnly = 0xC07F;
 constexpr int kSzPerBatch = 16;    // (scale, zero) entries per row staged by one load batch
 constexpr uint32_t kSignFlip = 0x88888888u;   // two's complement nibble v -> unsigned v ^ 8 (zero point 8)
 
@@ -130,7 +127,7 @@ __device__ __forceinline__ float lane_group_sum(float v) {
 // converted by v_cvt_scalef32_pk_bf16_fp4 into bf16 values already multiplied
 // by the block's power-of-two scale (exact), so the MFMAs accumulate straight
 // into the outputs with the activations in natural order and no fold.
-template <int GB, int FR, int CC, int PF, int FMT>
+template <int GB, int FR, int CC, int PF, int FMT, bool GRP>
 __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   constexpr bool S16 = FMT == kFmtS16, MX = FMT == kFmtMX;
   static_assert(!MX || GB == 1, "MXFP4 blocks hold 32 inputs");
@@ -147,10 +144,14 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   const int q = lane >> 4;
   const int c = lane & 15;
   // this workgroup's matrix (uniform)
+  // (a single matrix is read straight from the arguments; only a grouped
+  // launch pays a second round of argument loads to find its entry)
   int pi = 0;
+  if constexpr (GRP) {
 #pragma unroll
-  for (int i = 1; i < kMaxGrouped; ++i)
-    if (i < p.nprob && (int)blockIdx.x >= p.prob[i].tile_begin) pi = i;
+    for (int i = 1; i < kMaxGrouped; ++i)
+      if (i < p.nprob && (int)blockIdx.x >= p.prob[i].tile_begin) pi = i;
+  }
   const GemvProblem& pr = p.prob[pi];
   const int tile = (int)blockIdx.x - pr.tile_begin;
   const int M = p.m, N = pr.n, K = p.k;
@@ -457,8 +458,11 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
 #pragma unroll
     for (int r = 0; r < FR; ++r) red[(wave * 16 + lane) * FR + r] = acc[r];
   }
-  __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
+  // LDS-only fences: the waves' partials are visible after the barrier, and
+  // no wait for the (empty) weight loads still in flight is added.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   if (wave == 0) {
     f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (lane < 16) {
@@ -472,10 +476,11 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
 
 template <int GB, int FR, int CC, int FMT>
 int32_t launch_one(const GemvParams& gp, const LinearPlan& pl, size_t lds, hipStream_t stream) {
-  auto kern = gemv_kernel<GB, FR, CC, 4, FMT>;
+  const bool grp = gp.nprob > 1;
+  auto kern = grp ? gemv_kernel<GB, FR, CC, 4, FMT, true> : gemv_kernel<GB, FR, CC, 4, FMT, false>;
   if (lds > 64 * 1024) {
-    static std::atomic<uint64_t> raised{0};   // per instantiation, one bit per device
-    const int32_t st = raise_lds_limit(reinterpret_cast<const void*>(kern), 160 * 1024, raised);
+    static std::atomic<uint64_t> raised[2] = {{0}, {0}};   // per kernel, one bit per device
+    const int32_t st = raise_lds_limit(reinterpret_cast<const void*>(kern), 160 * 1024, raised[grp ? 1 : 0]);
     if (st != WOQ_OK) return st;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)pl.grid), dim3(64 * pl.waves), lds, stream, gp);

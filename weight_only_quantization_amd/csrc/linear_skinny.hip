@@ -37,9 +37,6 @@ namespace {
 constexpr int kStepK = 128;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kOffsetOOB = 0x80000000u;   // a buffer offset no descriptor covers
-// s_waitcnt immediate that waits for LDS traffic only: lgkmcnt(0), vmcnt and
-// expcnt at their maxima
-constexpr int kWaitLdsOnly = 0xC07F;
 constexpr int kStageBatch = 24;  // staged (scale, zero) entries per lane and batch
 constexpr int kPF = 2;           // steps of loads in flight per wave
 constexpr uint32_t kSignFlip = 0x88888888u;   // two's complement nibble v -> unsigned v ^ 8 (zero point 8)
@@ -328,8 +325,11 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
 #pragma unroll
     for (int t = 0; t < T; ++t)
       *reinterpret_cast<f32x4_t*>(red + (((wave * MT + mt) * T + t) * 64 + lane) * 4) = acc[mt][t];
-  __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
+  // LDS-only fences: the waves' partials are visible after the barrier, and
+  // no wait for the (empty) weight loads still in flight is added.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   for (int pr = wave; pr < MT * T; pr += W) {
     const int mt = pr / T, t = pr % T;
     f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};

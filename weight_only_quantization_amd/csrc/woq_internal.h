@@ -61,6 +61,7 @@ struct LinearPlan {
   int cnt = 0;           // 128-input steps per wave (decode and small-M paths)
   int64_t tail_n = 0;    // GEMM path: trailing output columns left to a second launch of
                          // 64-row tiles, so that the last round of workgroups is not half empty
+  int rows_u = 0;        // row-streaming decode path (path 5): rows per workgroup
 };
 
 // Compute units of one MI355X (gfx950): the GEMM path sizes its grid in rounds of this many
@@ -69,7 +70,9 @@ constexpr int64_t kComputeUnits = 256;
 
 LinearWorkspace linear_workspace_layout(int64_t m, int64_t n, int64_t k, int32_t group,
                                         bool has_order);
-LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_order);
+// rows_ok: the weights are canonical packed rows of unsigned or signed codes
+// (not prepared, not MXFP4), which the row-streaming decode path can read.
+LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_order, bool rows_ok = true);
 
 // ---------------------------------------------------------------------------
 // Launchers (defined next to their kernels).  All enqueue on `stream` and
@@ -185,5 +188,12 @@ constexpr int64_t kGemmMaxK = (int64_t)1 << 24;   // tile offsets of the GEMM pa
 int32_t launch_gemm(const LinearArgs& a, const LinearPlan& p, void* sz_ws, hipStream_t stream);
 int32_t launch_fill_bias(const float* bias, int32_t m, int32_t n, int32_t y_bf16, void* y,
                          hipStream_t stream);
+// Row-streaming decode path (m <= 4, canonical weights): whether it takes
+// (m, k), its rows per workgroup for n output rows in all, its waves per
+// workgroup, and the launch over up to kMaxGrouped matrices sharing x.
+bool rows_supported(int64_t m, int64_t k);
+int rows_per_group(int64_t m, int64_t n, int64_t k);
+int rows_waves(int64_t k);
+int32_t launch_rows(const LinearArgs* args, int count, int u, hipStream_t stream);
 
 }  // namespace woq

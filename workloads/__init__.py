@@ -27,6 +27,7 @@ __all__ = [
     "activations_bf16",
     "bias",
     "order",
+    "order_with_repeats",
     "bf16_bits_to_f32",
     "TINY",
     "DECODE",
@@ -79,12 +80,25 @@ def weight(n: int, k: int, seed: int, std: float = 0.02,
     return w
 
 
-def activations_bf16(m: int, k: int, seed: int) -> np.ndarray:
-    """x ~ N(0, 1) rounded to bfloat16; returned as raw uint16 bit patterns [m, k]."""
+def activations_bf16(m: int, k: int, seed: int, outlier_frac: float = 0.0, outlier_mult: float = 50.0,
+                     offset: float = 0.0, seed_cols: int = 0) -> np.ndarray:
+    """x ~ N(0, 1) (+ offset) rounded to bfloat16; returned as raw uint16 bit patterns [m, k].
+
+    With ``outlier_frac > 0``, ``round(outlier_frac * k)`` distinct input
+    channels (drawn with ``seed_cols``) are multiplied by ``outlier_mult``: a
+    few salient activation channels, the premise of activation-aware scaling.
+    ``offset`` is added to every entry (a large common mean).
+    """
     import torch
 
     rng = np.random.default_rng(seed)
     x32 = rng.standard_normal((m, k), dtype=np.float32)
+    if outlier_frac > 0:
+        cnt = int(round(outlier_frac * k))
+        cols = np.random.default_rng(seed_cols).choice(k, size=cnt, replace=False)
+        x32[:, cols] *= np.float32(outlier_mult)
+    if offset:
+        x32 += np.float32(offset)
     xb = torch.from_numpy(x32).to(torch.bfloat16)
     return xb.view(torch.int16).numpy().view(np.uint16).copy()
 
@@ -121,6 +135,12 @@ def bias(n: int, seed: int, std: float = 0.01) -> np.ndarray:
 def order(k: int, seed: int) -> np.ndarray:
     """A seeded random permutation of range(k) as int32: the act-order gather index."""
     return np.random.default_rng(seed).permutation(k).astype(np.int32)
+
+
+def order_with_repeats(k: int, seed: int) -> np.ndarray:
+    """k gather indices drawn uniformly from range(k) with replacement (int32):
+    in range but not a permutation, so some inputs repeat and others are skipped."""
+    return np.random.default_rng(seed).integers(0, k, size=k).astype(np.int32)
 
 
 # ---------------------------------------------------------------------------
