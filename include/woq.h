@@ -200,6 +200,27 @@ int32_t woq_unprepare_int4(const uint8_t* prepared, int64_t n, int64_t k, uint8_
                            void* stream);
 
 /*
+ * woq_linear_int4_groups without a caller workspace and without allocating:
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid it).  The workspace is a
+ * fixed device array of woq_linear_noalloc_max_workspace_bytes() bytes
+ * (32 MiB) inside the library; every device the library runs on holds its own
+ * copy until the process ends.  ASYNC.
+ * Arguments, results and errors: as woq_linear_int4_groups without workspace
+ * and workspace_bytes; sizes whose woq_linear_workspace_bytes exceeds the
+ * array return WOQ_EWORKSPACE before anything is enqueued (for example m = 2048
+ * with k = 14336).
+ * Calls that overlap on one device (concurrent streams, or host threads) share
+ * that device's array and race: serialize them.  The array keeps the last
+ * call's contents; nothing in it needs to start cleared.
+ */
+size_t woq_linear_noalloc_max_workspace_bytes(void);
+int32_t woq_linear_int4_groups_noalloc(const void* x_bf16, int64_t m, const uint8_t* packed,
+                                       const float* scale, const uint8_t* zero, const float* bias,
+                                       const int32_t* order, int64_t n, int64_t k, int32_t group,
+                                       int32_t y_dtype, void* y, void* stream);
+
+/*
  * woq_linear_int4_groups over prepared weights: identical arguments, results
  * and errors, except that `prepared` (device, 16-byte aligned, at least
  * woq_prepared_bytes(n, k) bytes) replaces `packed`.  The result equals that

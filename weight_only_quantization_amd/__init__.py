@@ -134,6 +134,9 @@ def load() -> ctypes.CDLL:
         "woq_linear_int4_groups_zp4": (c_i32, [c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i32, c_i32,
                                                c_p, c_p, c_sz, c_p]),
         "woq_linear_int4_groups_zp4_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i32, c_i32]),
+        "woq_linear_noalloc_max_workspace_bytes": (c_sz, []),
+        "woq_linear_int4_groups_noalloc": (c_i32, [c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i32, c_i32,
+                                                   c_p, c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

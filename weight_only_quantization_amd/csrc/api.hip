@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "woq_internal.h"
 
@@ -618,6 +619,65 @@ int32_t woq_linear_int4_groups(const void* x_bf16, int64_t m, const uint8_t* pac
                                size_t workspace_bytes, void* stream) {
   return linear_impl(x_bf16, m, packed, scale, zero, bias, order, n, k, group, y_dtype, y,
                      workspace, workspace_bytes, stream, 0);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of woq_linear_int4_groups_noalloc: a file-scope device array, so
+// that call allocates nothing.  Each device holds its own copy from the load of
+// the library until the process ends; its address on a device is taken once,
+// with that device current, and kept in `scratch_addr`.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void* scratch_addr[kMaxDevices] = {};
+std::mutex scratch_mutex;
+
+// The current device's copy of `scratch` (null with the status on failure).
+void* device_scratch(int32_t* status) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *status = WOQ_EHIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_addr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      *status = WOQ_EHIP;
+      return nullptr;
+    }
+    scratch_addr[dev] = ptr;
+  }
+  *status = WOQ_OK;
+  return scratch_addr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t woq_linear_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
+
+int32_t woq_linear_int4_groups_noalloc(const void* x_bf16, int64_t m, const uint8_t* packed,
+                                       const float* scale, const uint8_t* zero, const float* bias,
+                                       const int32_t* order, int64_t n, int64_t k, int32_t group,
+                                       int32_t y_dtype, void* y, void* stream) {
+  const int32_t st = check_linear_shape(m, n, k, group);
+  if (st != WOQ_OK) return st;
+  const size_t need = linear_workspace_layout(m, n, k, group, order != nullptr).total;
+  if (m == 0 || n == 0 || need == 0)
+    return linear_impl(x_bf16, m, packed, scale, zero, bias, order, n, k, group, y_dtype, y, nullptr, 0,
+                       stream, 0);
+  if (need > kScratchBytes) return WOQ_EWORKSPACE;
+  int32_t dst = WOQ_OK;
+  void* ws = device_scratch(&dst);
+  if (dst != WOQ_OK) return dst;
+  return linear_impl(x_bf16, m, packed, scale, zero, bias, order, n, k, group, y_dtype, y, ws, kScratchBytes,
+                     stream, 0);
 }
 
 int32_t woq_linear_int4_groups_zp4(const void* x_bf16, int64_t m, const uint8_t* packed, const float* scale,
