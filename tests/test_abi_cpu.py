@@ -52,7 +52,8 @@ def test_status_strings(lib):
     (2, 4096, 32768, 64, "rows_dot2"), (1, 4096, 32800, 32, "skinny_mfma"),
     (5, 4096, 4096, 128, "skinny_mfma"), (16, 14336, 4096, 32, "skinny_mfma"),
     (17, 4096, 4096, 128, "skinny_mfma"), (32, 14336, 4096, 256, "skinny_mfma"),
-    (33, 4096, 4096, 128, "gemm_mfma"), (2048, 14336, 4096, 128, "gemm_mfma"),
+    (33, 4096, 4096, 128, "skinny_mfma"), (64, 14336, 4096, 32, "skinny_mfma"),
+    (65, 4096, 4096, 128, "gemm_mfma"), (128, 14336, 4096, 32, "gemm_mfma"), (2048, 14336, 4096, 128, "gemm_mfma"),
     (0, 64, 256, 32, "none"), (3, 64, 0, 32, "bias_fill"),
 ])
 def test_plan_paths(m, n, k, g, path):
@@ -140,7 +141,7 @@ def test_linear_rejects_misalignment_and_missing_workspace(lib):
                                     a16, None, 0, None)
     assert woq.STATUS[rc] == "WOQ_EWORKSPACE"
     # the GEMM path needs its pre-pass buffers
-    rc = lib.woq_linear_int4_groups(a16, 64, a16, a16, a16, None, None, 64, 256, 32, 1,
+    rc = lib.woq_linear_int4_groups(a16, 200, a16, a16, a16, None, None, 64, 256, 32, 1,
                                     a16, a16, 16, None)
     assert woq.STATUS[rc] == "WOQ_EWORKSPACE"
 

@@ -134,7 +134,8 @@ def test_gemv_launch_variants(woq, monkeypatch, m, n, k, group, with_bias, with_
 # Small-M path launch variants: WOQ_SKINNY="tiles,cnt" forces the number of
 # 16-row weight tiles per workgroup (1, 2, 4: ragged last workgroups included)
 # and the steps per wave (partial last waves, ranges that straddle groups,
-# 32-input tail steps), with one and two activation tiles.
+# 32-input tail steps), with one and two activation tiles per wave and one to
+# four wave groups along the rows.
 SKINNY_VARIANTS = [
     # m, n, k, group, bias, order, "tiles,cnt", expected (tiles, waves)
     (5, 100, 1024, 128, True, False, "4,2", (4, 4)),
@@ -144,6 +145,12 @@ SKINNY_VARIANTS = [
     (32, 33, 864, 32, True, True, "4,2", (4, 4)),
     (12, 64, 4096, 128, False, False, "1,16", (1, 2)),
     (1, 40, 40960, 128, True, False, "4,40", (2, 8)),   # LDS allows 2 tiles, not 4
+    # m > 32: wave groups along the activation rows (2 tiles of 16 rows each)
+    (33, 70, 1024, 64, True, True, "2,2", (2, 8)),       # 2 groups x 4 K ranges; one row in the last tile
+    (64, 100, 2048, 128, False, False, "4,4", (4, 8)),
+    (100, 50, 1536, 32, True, False, "1,6", (1, 8)),     # 4 groups x 2 K ranges, ragged rows
+    (128, 130, 4096, 256, False, True, "2,16", (2, 8)),
+    (80, 40, 768, 128, True, True, "2,4", (2, 6)),       # 3 groups x 2 K ranges
 ]
 
 

@@ -1,8 +1,9 @@
 """GPU linear layer on the edge cases of its inputs, on every kernel path.
 
 Each case runs on the row-streaming decode path (m <= 4), the tile GEMV
-(m <= 4 with WOQ_DECODE_MFMA), the small-M MFMA path (5 <= m <= 32) and the
-tiled GEMM (m > 32), and is compared with the float64 oracle to the same
+(m <= 4 with WOQ_DECODE_MFMA), the small-M MFMA path (5 <= m <= 64, and
+m = 100 with its launch shape forced) and the tiled GEMM (m > 64), and is
+compared with the float64 oracle to the same
 gate as every other parity test:
 
 * a gather index that repeats some inputs and skips others (the `order`
@@ -35,8 +36,9 @@ pytestmark = pytest.mark.gpu
 PATHS = {
     "rows": [(1, 300, 2048, 128, {}), (3, 100, 1536, 64, {})],
     "gemv": [(1, 300, 2048, 128, {"WOQ_DECODE_MFMA": "1"}), (4, 100, 1024, 32, {"WOQ_DECODE_MFMA": "1"})],
-    "skinny": [(16, 200, 2048, 128, {}), (7, 64, 1024, 32, {})],
-    "gemm": [(100, 300, 1024, 128, {}), (64, 256, 512, 256, {})],
+    "skinny": [(16, 200, 2048, 128, {}), (7, 64, 1024, 32, {}), (64, 300, 1024, 128, {}),
+               (100, 300, 1024, 128, {"WOQ_SKINNY": "2,2"})],
+    "gemm": [(100, 300, 1024, 128, {}), (160, 256, 512, 256, {})],
 }
 CASES = [(path, *c) for path, cs in PATHS.items() for c in cs]
 PATH_TAG = {"rows": "rows_dot2", "gemv": "gemv_mfma", "skinny": "skinny_mfma", "gemm": "gemm_mfma"}
@@ -50,6 +52,7 @@ def _say(msg):
 def _env(monkeypatch, env):
     monkeypatch.delenv("WOQ_DECODE_MFMA", raising=False)
     monkeypatch.delenv("WOQ_ROWS_U", raising=False)
+    monkeypatch.delenv("WOQ_SKINNY", raising=False)
     for key, val in env.items():
         monkeypatch.setenv(key, val)
 

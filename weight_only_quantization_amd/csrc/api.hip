@@ -51,31 +51,38 @@ bool skinny_override(int* tiles, int* cnt) {
   return true;
 }
 
-// Small-M launch shape (m <= 32).  A wave takes `cnt` consecutive 128-input
-// steps (even, at least 2) and a workgroup of at most 8 waves covers K; the
-// workgroup takes 4 weight tiles when that still leaves about 200 workgroups
-// (the tiles share each activation operand), else 2 or 1.  The per-wave
-// (scale, zero) staging must fit next to the reduction area in LDS; wider
-// tiles give way first.  (Measured on 14336x4096, 4096x14336 and 4096x4096 at
-// m = 5..32 and every group size.)
+// Small-M launch shape (m <= 128; by default m <= 64).  The waves of a workgroup form a WM x WK
+// grid: each of the WM wave groups takes two 16-row activation tiles (one when
+// m <= 16), each of the WK K ranges `cnt` consecutive 128-input steps (even,
+// at least 2), with at most 8 waves; the workgroup takes 4 weight tiles when
+// that still leaves about 200 workgroups (the tiles share each activation
+// operand), else 2 or 1.  The per-range (scale, zero) staging must fit next to
+// the reduction area in LDS; wider tiles give way first.  (Measured on
+// 14336x4096, 4096x14336 and 4096x4096 at m = 5..128 and every group size.)
 bool skinny_plan(int64_t m, int64_t n, int64_t k, int32_t group, LinearPlan* p) {
   const int64_t nsteps = (k + 127) / 128;
   const int64_t tiles = (n + 15) / 16;
-  int64_t cnt = (nsteps + 7) / 8;
+  const int64_t mtt = (m + 15) / 16;
+  const int64_t mt = mtt >= 2 ? 2 : 1;
+  const int64_t wm = (mtt + mt - 1) / mt;
+  if (wm > 8) return false;
+  const int64_t wk_max = 8 / wm;
+  int64_t cnt = (nsteps + wk_max - 1) / wk_max;
   if (cnt < 2) cnt = 2;
   cnt = (cnt + 1) / 2 * 2;
   int t = tiles >= 800 ? 4 : (tiles >= 400 ? 2 : 1);
   int o_t, o_c;
-  if (skinny_override(&o_t, &o_c) && (nsteps + o_c - 1) / o_c <= 8) {
+  if (skinny_override(&o_t, &o_c) && (nsteps + o_c - 1) / o_c <= wk_max) {
     t = o_t;
     cnt = o_c;
   }
-  const int64_t waves = (nsteps + cnt - 1) / cnt;
+  const int64_t waves = wm * ((nsteps + cnt - 1) / cnt);
   if (waves > 8 || cnt >= ((int64_t)1 << 20)) return false;
   while (t > 1 && skinny_lds_layout(m, k, group, (int)waves, t, (int)cnt).total > kSkinnyLdsLimit) t /= 2;
   if (skinny_lds_layout(m, k, group, (int)waves, t, (int)cnt).total > kSkinnyLdsLimit) return false;
   p->path = 1;
-  p->mt = (int)((m + 15) / 16);
+  p->mt = (int)mt;
+  p->wm = (int)wm;
   p->fold_rows = 4;
   p->ns = t;
   p->waves = (int)waves;
@@ -152,7 +159,12 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
     return p;
   }
   static const bool force_tiled = std::getenv("WOQ_FORCE_TILED") != nullptr;   // tuning aid
-  if (m <= 32 && !force_tiled && k < ((int64_t)1 << 26) && skinny_plan(m, n, k, group, &p)) {
+  // The small-M kernel takes up to 64 rows; from 65 to 128 rows it is slower
+  // than the tiled GEMM (measured at 14336x4096 and 4096x14336) and runs only
+  // when its launch shape is forced.
+  int o_t, o_c;
+  const int64_t skinny_max = skinny_override(&o_t, &o_c) ? 128 : 64;
+  if (m <= skinny_max && !force_tiled && k < ((int64_t)1 << 26) && skinny_plan(m, n, k, group, &p)) {
     p.prep = has_order ? 1 : 0;
     return p;
   }
@@ -842,9 +854,9 @@ int32_t woq_linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, int32_t 
     case 3: std::snprintf(buf, len, "path=bias_fill"); break;
     case 1:
       std::snprintf(buf, len,
-                    "path=skinny_mfma act_tiles=%d weight_tiles=%d waves=%d steps_per_wave=%d "
+                    "path=skinny_mfma act_tiles=%d wave_groups=%d weight_tiles=%d waves=%d steps_per_wave=%d "
                     "group_blocks=%d grid=%lld prep=%s workspace=%zu",
-                    p.mt, p.ns, p.waves, p.cnt, p.gb, (long long)p.grid, p.prep ? "gather" : "none", ws);
+                    p.mt, p.wm, p.ns, p.waves, p.cnt, p.gb, (long long)p.grid, p.prep ? "gather" : "none", ws);
       break;
     case 4:
       std::snprintf(buf, len,

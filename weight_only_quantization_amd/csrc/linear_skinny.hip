@@ -1,12 +1,15 @@
-// Small-M linear path (up to 32 activation rows, and the decode shapes the
-// GEMV cannot take): y = x . dequant(W)^T + bias for group-wise 4-bit weights
-// (linnet docs "Quantization", std.quant table, linear_int4_groups).  At these
-// row counts the layer is bound by the weight stream; what matters is that
-// each packed byte is read once, that the activations it meets cost little
-// next to it, and that enough bytes are in flight.
+// Small-M linear path (up to 64 activation rows by default, 128 when forced,
+// and the decode shapes the row kernel cannot take): y = x . dequant(W)^T +
+// bias for group-wise 4-bit weights (linnet docs "Quantization", std.quant
+// table, linear_int4_groups).  At these row counts the layer is bound by the
+// weight stream; what matters is that each packed byte is read once, that the
+// activations it meets cost little next to it, and that enough bytes are in
+// flight.
 //
 // * A workgroup owns T tiles of 16 weight rows (outputs) and all of K; its W
-//   waves split K into contiguous ranges of `cnt` 128-input steps.
+//   waves form WM groups along the activation rows (each takes MT tiles of 16
+//   rows; WM > 1 only above 32 rows) times WK contiguous K ranges of `cnt`
+//   128-input steps.
 // * Per step a lane issues one 16-byte load per weight tile (lane group q
 //   reads inputs [k0 + 32q, k0 + 32q + 32) of row c) and four 16-byte loads
 //   per 16-row activation tile: the activations go straight from memory (they
@@ -37,7 +40,7 @@ namespace {
 constexpr int kStepK = 128;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kOffsetOOB = 0x80000000u;   // a buffer offset no descriptor covers
-constexpr int kStageBatch = 24;  // staged (scale, zero) entries per lane and batch
+constexpr int kStageBatch = 8;   // staged (scale, zero) entries per lane and batch
 constexpr int kPF = 2;           // steps of loads in flight per wave
 constexpr uint32_t kSignFlip = 0x88888888u;   // two's complement nibble v -> unsigned v ^ 8 (zero point 8)
 
@@ -58,6 +61,7 @@ struct SkinnyParams {
   // in registers: one v_and_or_b32 per pair then expands two codes.
   uint32_t nib_mask, nib_offset;
   int32_t row_scale;  // signed codes with one float32 scale a row (Int4Linear)
+  int32_t wm;         // wave groups along the activation rows (each takes MT tiles of 16 rows)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
@@ -92,13 +96,18 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4;
   const int c = lane & 15;
+  // Waves are a WM x WK grid: wave group wm takes activation tiles
+  // [wm MT, wm MT + MT), K range wk takes `cnt` steps.
+  const int WM = p.wm;
+  const int wm = __builtin_amdgcn_readfirstlane(wave % WM);
+  const int wk = __builtin_amdgcn_readfirstlane(wave / WM);
   const int M = p.m, N = p.n, K = p.k;
   const int nsteps = p.nsteps;
   const uint32_t row_bytes = (uint32_t)K / 2;
   const int tile0 = blockIdx.x * T;
   const int wg_rows = __builtin_amdgcn_readfirstlane(min(16 * T, N - 16 * tile0));
   const int cnt = p.cnt;
-  const int s0 = __builtin_amdgcn_readfirstlane(wave * cnt);
+  const int s0 = __builtin_amdgcn_readfirstlane(wk * cnt);
   const int live = __builtin_amdgcn_readfirstlane(max(0, min(cnt, nsteps - s0)));
   const bool prep = p.prepared != 0;
 
@@ -108,7 +117,9 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   //    converted after it, so the two latencies overlap.
   const int gb = (s0 * kStepK) / G;
   const int ngw = p.ngw;
-  unsigned char* szl = lds + wave * p.sz_bytes;
+  // one staging area per K range: the WM waves of a range write the same
+  // values there, and each reads only entries it wrote itself
+  unsigned char* szl = lds + wk * p.sz_bytes;
   // float32 per group, float16 per group (S16), one float32 per row (S16 with
   // row_scale: Int4Linear), a byte per block (MX)
   const bool row_scale = S16 && p.row_scale != 0;   // uniform
@@ -183,9 +194,9 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   bool xrow[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int row = 16 * mt + c;
+    const int row = 16 * (wm * MT + mt) + c;
     xrow[mt] = row < M;
-    xoff[mt] = (uint32_t)(row * K + in0) * 2u;
+    xoff[mt] = (uint32_t)(min(row, M - 1) * K + in0) * 2u;
   }
   u32x4_t wb[kPF][T];
   u32x4_t xb[kPF][MT][4];
@@ -317,8 +328,9 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
     for (int u = 0; u < kPF; ++u) step(u, i0 + u);
   }
 
-  // 3. combine the waves: red[wave][mt][t][lane] (4 floats each); wave w then
-  //    finishes the (mt, t) tiles w, w + W, ... in wave order
+  // 3. combine the K ranges: red[wave][mt][t][lane] (4 floats each); wave w
+  //    then finishes the (wave group, mt, t) tiles w, w + W, ..., adding the K
+  //    ranges in order
   float* red = reinterpret_cast<float*>(lds + p.red_off);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -330,10 +342,12 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  for (int pr = wave; pr < MT * T; pr += W) {
-    const int mt = pr / T, t = pr % T;
+  const int WK = W / WM;
+  for (int pr = wave; pr < WM * MT * T; pr += W) {
+    const int pm = pr / (MT * T), mt = (pr / T) % MT, t = pr % T;
     f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int w = 0; w < W; ++w) {
+    for (int kk = 0; kk < WK; ++kk) {
+      const int w = kk * WM + pm;
       const f32x4_t a = *reinterpret_cast<const f32x4_t*>(red + (((w * MT + mt) * T + t) * 64 + lane) * 4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] += a[r];
@@ -343,7 +357,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
       const float bv = p.bias ? p.bias[n] : 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = 16 * mt + 4 * q + r;
+        const int row = 16 * (pm * MT + mt) + 4 * q + r;
         if (row < M) {
           const float o = v[r] + bv;
           if (p.y_bf16)
@@ -389,12 +403,16 @@ int32_t dispatch_mt(const SkinnyParams& sp, const LinearPlan& pl, size_t lds, hi
 
 }  // namespace
 
+int64_t mt_total(int64_t m) { return (m + 15) / 16; }
+
 SkinnyLds skinny_lds_layout(int64_t m, int64_t k, int64_t group, int waves, int tiles, int cnt) {
   SkinnyLds l;
-  const int64_t mt = (m + 15) / 16;
+  const int64_t mt = (m + 15) / 16 > 1 ? 2 : 1;   // activation tiles per wave
   l.ngw = (int32_t)((cnt * kStepK + group - 1) / group + 1);   // a range may straddle one more group
   l.sz_bytes = 16 * tiles * l.ngw * 8;
-  l.red_off = ((int64_t)waves * l.sz_bytes + 255) / 256 * 256;
+  const int64_t wm = (mt_total(m) + mt - 1) / mt;        // wave groups along the rows
+  const int64_t wk = (waves + wm - 1) / wm;               // K ranges
+  l.red_off = (wk * l.sz_bytes + 255) / 256 * 256;
   l.total = (size_t)l.red_off + (size_t)waves * mt * tiles * 64 * 16;
   (void)k;
   return l;
@@ -408,7 +426,7 @@ int32_t launch_skinny(const LinearArgs& a, const LinearPlan& pl, hipStream_t str
                                                  : static_cast<const void*>(a.scale),
                   a.zero, a.bias, a.y, a.m, a.n, a.k, a.y_bf16,
                   (a.k + kStepK - 1) / kStepK, a.k / a.group, a.prepared, pl.cnt, l.ngw,
-                  l.sz_bytes, (int32_t)l.red_off, kNibPairMask, kBf16Offset2, a.row_scale};
+                  l.sz_bytes, (int32_t)l.red_off, kNibPairMask, kBf16Offset2, a.row_scale, pl.wm};
   if (a.mx) return a.group == 32 ? dispatch_mt<32, kFmtMX>(sp, pl, l.total, stream) : WOQ_EUNSUPPORTED;
   if (a.sym16) {
     switch (a.group) {

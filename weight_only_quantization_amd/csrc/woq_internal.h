@@ -52,6 +52,7 @@ struct LinearPlan {
   int mt = 1;            // 16-row activation tiles (small-M path)
   int fold_rows = 4;     // accumulator rows folded per tile (1 when m == 1)
   int ns = 1;            // 16-row weight tiles per workgroup (small-M path)
+  int wm = 1;            // small-M path: wave groups along the activation rows
   int waves = 4;         // waves per workgroup
   int gb = 4;            // 32-wide k blocks per quantization group inside a 128-wide k step (1, 2, 4)
   int prep = 0;          // 1 = an input pre-pass kernel runs first
