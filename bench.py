@@ -11,15 +11,19 @@ captured once in a HIP graph and replayed.
 Printed JSON line (rank 0):
   value        effective weight GB/s over the whole step (packed + scale + zero
                bytes / wall time of the replayed graph, launch gaps included)
-  roofline     the decode kernel alone (gemv_kernel, every launch of the step):
-               algorithmic bytes per launch / its average launch duration
-               (HIP events around the replayed step graph)
+  roofline     the step's dominant kernel on its own: the row-streaming decode
+               kernel on the gate/up projections (14336x4096, 2 of the 7 linears
+               of a layer and 54 % of the step's bytes with the down projection),
+               algorithmic bytes per launch / average launch duration of a graph
+               of back-to-back launches over >= 1 GB of rotating weight copies
+               (HIP events); the down projection and the whole-step average beside it
   grouped      the same step with q/k/v and gate/up each run as one grouped
                call (woq_linear_int4_groups_grouped: one launch per group)
   prepared     the same step over prepared (fragment-ordered) weights, made
                once before timing by woq_prepare_int4 (also grouped)
   prefill      TFLOP/s of the M=2048 GEMM path on both prefill shapes
-  cpu_baseline the CPU oracle's linear on a bounded sample of the same layer
+  cpu_baseline the CPU oracle (dequantize + float64 matmul) on bounded samples of
+               every configuration, with its core count and a single-thread run
 """
 from __future__ import annotations
 
@@ -40,8 +44,8 @@ METRIC = "int4-g128 linear: effective weight GB/s (% HBM peak) at M=1; TFLOP/s a
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 GROUP = 128
-TRAFFIC_SUMMARY = ROOT / "profiles" / "traffic_gemv_decode_m1_g128.txt"
-KERNEL_SOURCES = ["linear_gemv.hip", "mfma_common.h"]
+TRAFFIC_SUMMARY = ROOT / "profiles" / "traffic_rows_decode_m1_g128.txt"
+KERNEL_SOURCES = ["linear_rows.hip"]
 
 
 def weight_bytes(n: int, k: int, group: int = GROUP, sym16: bool = False, mx: bool = False,
@@ -176,43 +180,55 @@ def time_step(torch, run, steps: int, warmup: int, use_graph: bool):
 
 def measure_prefill(torch, woq, reps: int = 5, calls: int = 20):
     """Per-call time of each prefill shape: `calls` back-to-back launches (pre-pass
-    included) between two events, median of `reps` repetitions, after warm-up."""
+    included) between two events, median of `reps` repetitions, after warm-up;
+    once over the canonical weights and once over prepared ones."""
     from workloads import PREFILL
 
     dev = torch.device("cuda")
     gen = torch.Generator(device=dev)
     out = []
-    for case in PREFILL:
-        gen.manual_seed(case.seed_w)
-        w = torch.randn((case.n, case.k), generator=gen, device=dev).mul_(0.02)
-        q, s, z = woq.quantize_groups(w, case.group)
-        packed = woq.pack_uint4(q)
-        del w, q
-        x = torch.randn((case.m, case.k), generator=gen, device=dev).to(torch.bfloat16)
-        y = torch.empty((case.m, case.n), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(woq.linear_workspace_bytes(case.m, case.n, case.k, case.group, False),
-                         dtype=torch.uint8, device=dev)
+
+    def timed(fn):
         for _ in range(5):
-            woq.linear_int4_groups(x, packed, s, z, group=case.group, out=y, workspace=ws)
+            fn()
         torch.cuda.synchronize()
         times = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for _ in range(calls):
-                woq.linear_int4_groups(x, packed, s, z, group=case.group, out=y, workspace=ws)
+                fn()
             e1.record()
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1) * 1e-3 / calls)
-        t = statistics.median(times)
+        return statistics.median(times)
+
+    for case in PREFILL:
+        gen.manual_seed(case.seed_w)
+        w = torch.randn((case.n, case.k), generator=gen, device=dev).mul_(0.02)
+        q, s, z = woq.quantize_groups(w, case.group)
+        packed = woq.pack_uint4(q)
+        del w, q
+        prep = woq.prepare_int4(packed)
+        x = torch.randn((case.m, case.k), generator=gen, device=dev).to(torch.bfloat16)
+        y = torch.empty((case.m, case.n), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(woq.linear_workspace_bytes(case.m, case.n, case.k, case.group, False),
+                         dtype=torch.uint8, device=dev)
+        t = timed(lambda: woq.linear_int4_groups(x, packed, s, z, group=case.group, out=y, workspace=ws))
+        tp = timed(lambda: woq.linear_int4_groups_prepared(x, prep, s, z, out=y, workspace=ws))
         flops = 2.0 * case.m * case.n * case.k
         out.append(dict(shape=f"{case.m}x{case.n}x{case.k}", ms=round(t * 1e3, 4),
-                        tflops=round(flops / t / 1e12, 1)))
+                        tflops=round(flops / t / 1e12, 1), prepared_ms=round(tp * 1e3, 4),
+                        prepared_tflops=round(flops / tp / 1e12, 1)))
+        del packed, prep, s, z, x, y, ws
     tot_flops = sum(2.0 * c.m * c.n * c.k for c in PREFILL)
     tot_t = sum(o["ms"] for o in out) * 1e-3
+    tot_tp = sum(o["prepared_ms"] for o in out) * 1e-3
     tf = tot_flops / tot_t / 1e12
     return dict(metric="TFLOP/s at M=2048 (both prefill shapes, pre-pass included, back-to-back calls)",
                 value=round(tf, 1), peak=BF16_PEAK_TFLOPS, frac=round(tf / BF16_PEAK_TFLOPS, 4),
+                prepared_value=round(tot_flops / tot_tp / 1e12, 1),
+                prepared_frac=round(tot_flops / tot_tp / 1e12 / BF16_PEAK_TFLOPS, 4),
                 per_shape=out, plan=woq.linear_plan(2048, 14336, 4096, GROUP))
 
 
@@ -299,12 +315,15 @@ def measure_configs(torch, woq, reps: int = 40, pool_bytes: int = 1 << 30, cases
                 call(i)
         g.replay()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / reps
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3 / reps)
+        t = statistics.median(ts)
         flops = 2.0 * case.m * case.n * case.k
         ab = algorithmic_bytes(case.m, case.n, case.k, case.has_bias, case.group, sym16, mx, zp4) + (
             case.k * 4 if case.act_order else 0)
@@ -320,48 +339,88 @@ def measure_configs(torch, woq, reps: int = 40, pool_bytes: int = 1 << 30, cases
     return out
 
 
-def cpu_baseline(min_seconds: float = 10.0, max_passes: int = 8):
-    """The CPU oracle's linear over one Llama-3-8B layer's seven M=1 linears.
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        return 1
 
-    Weights are drawn directly in the Int4GroupLinear layout (the oracle's
-    quantizer is not timed); passes over the layer repeat until min_seconds.
+
+def cpu_baseline():
+    """The CPU oracle (dequantize to exact float64, then a float64 matmul) timed
+    on the host cores, on bounded samples of every configuration.
+
+    Weights are drawn directly in the Int4GroupLinear layout (the quantizer is
+    not timed).  Each configuration computes a sample of its output columns
+    (all of them for the decode shapes), best of three; GB/s counts the sampled
+    rows' weight bytes, GFLOP/s their 2*M*rows*K.  The decode shapes are also
+    run with one BLAS thread.  Dequantization is NumPy element-wise work on one
+    thread; the matmul runs on the BLAS threads.
     """
     import numpy as np
 
     import oracle
     import workloads
 
+    threads = _blas_threads()
+
+    def run(case, rows):
+        p, s_, z = workloads.packed_weights(case.n, case.k, case.group, seed=900 + case.seed_w)
+        x = workloads.activations_bf16(case.m, case.k, seed=950 + case.seed_x)
+        b = workloads.bias(case.n, seed=990) if case.has_bias else None
+        o = workloads.order(case.k, seed=case.seed_order) if case.act_order else None
+        sel = np.arange(case.n) if rows >= case.n else np.linspace(0, case.n - 1, rows).astype(np.int64)
+        best = None
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.linear_int4_groups(x, p, s_, z, case.n, case.k, case.group, bias=b, order=o, rows=sel)
+            dt = time.perf_counter() - t0
+            best = dt if best is None else min(best, dt)
+        wbytes = sel.size * (case.k // 2 + case.k // case.group * 5)
+        return dict(name=case.name, rows=int(sel.size), of_rows=case.n, s=round(best, 4),
+                    weight_GBps=round(wbytes / best / 1e9, 4),
+                    gflops=round(2.0 * case.m * sel.size * case.k / best / 1e9, 3))
+
+    per = []
+    t_all = time.perf_counter()
+    single = []
     try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                            if i.get("user_api") == "blas"] or [1])
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"):
+            single = [run(c, c.n) for c in workloads.DECODE]
     except Exception:  # noqa: BLE001
-        blas_threads = 1
-    layer = []
-    for idx, (role, n, k, has_bias) in enumerate(workloads.LLAMA3_8B_LAYER):
-        p, s, z = workloads.packed_weights(n, k, GROUP, seed=900 + idx)
-        x = workloads.activations_bf16(1, k, seed=950 + idx)
-        b = workloads.bias(n, seed=990) if has_bias else None
-        layer.append((n, k, p, s, z, x, b))
-    bytes_done, passes = 0, 0
-    t0 = time.perf_counter()
-    while passes < max_passes:
-        for (n, k, p, s, z, x, b) in layer:
-            oracle.linear_int4_groups(x, p, s, z, n, k, GROUP, bias=b)
-            bytes_done += weight_bytes(n, k)
-        passes += 1
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    dt = time.perf_counter() - t0
-    return dict(value=round(bytes_done / dt / 1e9, 4), unit="GB/s", cores=int(blas_threads),
+        single = []
+    decode = [run(c, c.n) for c in workloads.DECODE]
+    per += decode
+    per += [run(c, 4096) for c in workloads.SWEEP if c.group == 128 or c.m == 1]
+    per += [run(c, 1024) for c in workloads.PREFILL]
+    per += [run(c, 4096) for c in workloads.ACTORDER]
+    total = time.perf_counter() - t_all
+    # value: the seven M=1 linears of one layer, weight bytes over summed oracle
+    # time, on one thread (the BLAS threads are limited to one; the dequantization
+    # is single-threaded NumPy work either way)
+    base = single if single else decode
+    step_bytes = step_s = 0.0
+    for _, n, k, _ in workloads.LLAMA3_8B_LAYER:
+        hit = [d for d, c in zip(base, workloads.DECODE) if c.n == n and c.k == k][0]
+        step_bytes += weight_bytes(n, k)
+        step_s += hit["s"]
+    return dict(value=round(step_bytes / step_s / 1e9, 4), unit="GB/s", cores=1 if single else int(threads),
                 kind="oracle",
-                sample=f"{passes} pass(es) of one Llama-3-8B layer's 7 linears at M=1, group 128 "
-                       f"({bytes_done / 1e9:.2f} GB of weights, {dt:.1f} s; numpy float64; "
-                       f"BLAS threads={blas_threads}, affinity cores={len(os.sched_getaffinity(0))})")
+                sample=(f"value: one Llama-3-8B layer's seven M=1 group-128 linears computed in full on one "
+                        f"thread (weight bytes / summed oracle time, best of 3); per_config: every decode shape in "
+                        f"full and 4096 (act-order, sweep) or 1024 (prefill) evenly spaced output columns of the "
+                        f"other configurations with {threads} BLAS threads; {total:.1f} s in all; NumPy float64"),
+                blas_threads=int(threads), host_cpus=len(os.sched_getaffinity(0)),
+                per_config=per, single_thread_decode=single)
 
 
-DECODE_TAG = "gemv_kernel"
-COPY_TAG = "copyBuffer"            # the runtime's device-to-device copy kernel
+DOMINANT_TAG = "rows_kernel<4, 1, false, false>"   # 14336x4096 at M=1 (gate, up projections)
+DOMINANT_GRID = 3584 * 128                           # 3584 workgroups of 2 waves
+DOWN_TAG = "rows_kernel<16, 1, false, false>"        # 4096x14336 at M=1 (down projection)
+DOWN_GRID = 256 * 7 * 64                             # 256 workgroups of 7 waves
+COPY_TAG = "copyBuffer"                              # the runtime's device-to-device copy kernel
 
 
 def _csv_rows(path):
@@ -377,81 +436,156 @@ def _find(dirpath: Path, suffix: str) -> Path:
     return hits[0]
 
 
-def summarize_profiles(root: Path, copy_mib: int) -> None:
-    """Print the text summaries kept under profiles/ from three rocprofv3 runs.
+def _bench_line(dirpath: Path):
+    for cand in sorted(dirpath.rglob("*.json")):
+        for line in cand.read_text().splitlines():
+            try:
+                return json.loads(line)
+            except ValueError:
+                continue
+    raise SystemExit(f"no bench JSON line under {dirpath}")
 
-    root/ktrace: --kernel-trace --stats of the bench; root/fetch and root/write:
-    --pmc FETCH_SIZE and --pmc WRITE_SIZE of a short eager bench that also runs a
-    plain device copy of copy_mib MiB, whose counter reading calibrates the
-    counters to bytes (factor = copied bytes / counted bytes).
-    """
-    trace = _csv_rows(_find(root / "ktrace", "_kernel_trace.csv"))
+
+def summarize_trace(root: Path) -> None:
+    """Kernel trace summary: every woq kernel, per launch grid, from the
+    --kernel-trace --stats run under root, and the bench's own figures."""
+    trace = _csv_rows(_find(root, "_kernel_trace.csv"))
     by_kernel = {}
     for r in trace:
         name = r["Kernel_Name"]
         if "woq::" not in name:
             continue
         dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-        by_kernel.setdefault(name, []).append((int(r["Grid_Size_X"]), dur))
-    out = ["# rocprofv3 kernel trace of bench.py, woq kernels only (durations in microseconds)"]
+        grid = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0)
+        by_kernel.setdefault(name, []).append((grid, dur))
+    out = ["# rocprofv3 kernel trace, woq kernels only (durations in microseconds)"]
     for name, rows in sorted(by_kernel.items(), key=lambda kv: -sum(d for _, d in kv[1])):
         durs = [d for _, d in rows]
         out.append(f"kernel: {name}")
         out.append(f"  launches: {len(rows)}  average_us: {statistics.mean(durs) / 1e3:.3f}  "
-                   f"min_us: {min(durs) / 1e3:.3f}  max_us: {max(durs) / 1e3:.3f}")
+                   f"median_us: {statistics.median(durs) / 1e3:.3f}  min_us: {min(durs) / 1e3:.3f}  "
+                   f"max_us: {max(durs) / 1e3:.3f}")
         grids = {}
         for g, d in rows:
             grids.setdefault(g, []).append(d)
         for g, ds in sorted(grids.items()):
-            out.append(f"  grid_threads {g}: launches {len(ds)}  average_us {statistics.mean(ds) / 1e3:.3f}")
-    for cand in sorted((root / "ktrace").rglob("*.json")):
-        for line in cand.read_text().splitlines():
-            try:
-                rl = json.loads(line)["roofline"]
-            except (ValueError, KeyError, TypeError):
-                continue
-            out.append(f"bench_avg_launch_us (HIP events around the replayed step graph): {rl['avg_launch_us']}")
+            out.append(f"  grid_threads {g}: launches {len(ds)}  average_us {statistics.mean(ds) / 1e3:.3f}  "
+                       f"median_us {statistics.median(ds) / 1e3:.3f}")
+    line = _bench_line(root)
+    rl = line.get("roofline")
+    if rl:
+        out.append(f"bench roofline kernel: {rl['kernel']}")
+        out.append(f"bench avg_launch_us (HIP events around a graph of back-to-back launches): "
+                   f"{rl['avg_launch_us']}  achieved_GBps: {rl['achieved']}  frac: {rl['frac']}")
+        d = rl.get("down")
+        if d:
+            out.append(f"bench down projection ({d['kernel']}): avg_launch_us {d['avg_launch_us']}  "
+                       f"frac {d['frac']}")
+    pf = line.get("prefill")
+    if pf:
+        for shp in pf["per_shape"]:
+            out.append(f"bench prefill {shp['shape']}: {shp['ms']} ms per call  {shp['tflops']} TFLOP/s")
     print("\n".join(out))
 
-    def counter(sub, cname):
-        rows = _csv_rows(_find(root / sub, "_counter_collection.csv"))
-        sk = [float(r["Counter_Value"]) for r in rows
-              if r["Counter_Name"] == cname and DECODE_TAG in r["Kernel_Name"]]
-        cp = [float(r["Counter_Value"]) for r in rows
-              if r["Counter_Name"] == cname and COPY_TAG in r["Kernel_Name"]]
-        return sk, cp
 
-    f_sk, f_cp = counter("fetch", "FETCH_SIZE")
-    w_sk, w_cp = counter("write", "WRITE_SIZE")
-    copy_bytes = copy_mib << 20
+def summarize_traffic(root: Path, copy_mib: int) -> None:
+    """HBM bytes per launch of the dominant decode kernel (and of the down
+    projection's) from --pmc FETCH_SIZE (root/fetch) and --pmc WRITE_SIZE
+    (root/write) runs of the eager 32-layer step, each calibrated by a plain
+    device copy of copy_mib MiB in the same run (factor = copied bytes /
+    counted bytes)."""
+
+    def counter(sub, cname, tag, grid):
+        rows = _csv_rows(_find(root / sub, "_counter_collection.csv"))
+        return [float(r["Counter_Value"]) for r in rows
+                if r["Counter_Name"] == cname and tag in r["Kernel_Name"] and int(r["Grid_Size"]) == grid]
+
+    def copies(sub, cname):
+        rows = _csv_rows(_find(root / sub, "_counter_collection.csv"))
+        return [float(r["Counter_Value"]) for r in rows
+                if r["Counter_Name"] == cname and COPY_TAG in r["Kernel_Name"]]
+
+    f_cp, w_cp = copies("fetch", "FETCH_SIZE"), copies("write", "WRITE_SIZE")
     if not f_cp or not w_cp:
         raise SystemExit("the calibration copy is missing from the counter runs")
-    # the largest copy of the run is the calibration copy
-    f_factor = copy_bytes / (max(f_cp) * 1024.0)
+    copy_bytes = copy_mib << 20
+    f_factor = copy_bytes / (max(f_cp) * 1024.0)     # the largest copy of the run is the calibration copy
     w_factor = copy_bytes / (max(w_cp) * 1024.0)
-    fetch = statistics.mean(f_sk) * 1024.0 * f_factor
-    write = statistics.mean(w_sk) * 1024.0 * w_factor
-    print()
-    print("# HBM traffic of the decode GEMV kernel per launch (rocprofv3 --pmc, copy-calibrated)")
-    # the sources the counted kernel was built from, as the profiled bench printed them
-    src_hash = None
-    for cand in sorted((root / "fetch").rglob("*.json")):
-        for line in cand.read_text().splitlines():
-            try:
-                src_hash = json.loads(line)["roofline"]["kernel_source_sha256_16"]
-            except (ValueError, KeyError, TypeError):
-                continue
-    if src_hash is None:
-        raise SystemExit("the profiled bench's JSON line (fetch/*.json) is missing")
+    src_hash = _bench_line(root / "fetch")["kernel_source_sha256_16"]
     print(f"kernel_source_sha256_16: {src_hash}")
-    print(f"launches_counted: {len(f_sk)}")
-    print(f"fetch_KiB_raw_avg: {statistics.mean(f_sk):.1f}")
-    print(f"write_KiB_raw_avg: {statistics.mean(w_sk):.1f}")
     print(f"copy_calibration_MiB: {copy_mib}")
     print(f"fetch_factor: {f_factor:.4f}")
     print(f"write_factor: {w_factor:.4f}")
-    print(f"hbm_bytes_per_launch: {fetch + write:.0f}")
+    for label, tag, grid, (n, k) in (("dominant", DOMINANT_TAG, DOMINANT_GRID, (14336, 4096)),
+                                     ("down", DOWN_TAG, DOWN_GRID, (4096, 14336))):
+        f_sk = counter("fetch", "FETCH_SIZE", tag, grid)
+        w_sk = counter("write", "WRITE_SIZE", tag, grid)
+        if not f_sk or not w_sk:
+            raise SystemExit(f"no {tag} launches with grid {grid} in the counter runs")
+        fetch = statistics.mean(f_sk) * 1024.0 * f_factor
+        write = statistics.mean(w_sk) * 1024.0 * w_factor
+        alg = algorithmic_bytes(1, n, k, False)
+        pre = "" if label == "dominant" else f"{label}_"
+        print(f"{pre}kernel: woq::{tag} grid_threads {grid} ({n}x{k}, M=1, group {GROUP})")
+        print(f"{pre}launches_counted: {len(f_sk)}")
+        print(f"{pre}fetch_KiB_raw_avg: {statistics.mean(f_sk):.1f}")
+        print(f"{pre}write_KiB_raw_avg: {statistics.mean(w_sk):.1f}")
+        print(f"{pre}algorithmic_bytes_per_launch: {alg}")
+        print(f"{pre}hbm_bytes_per_launch: {fetch + write:.0f}")
+        print(f"{pre}traffic_over_algorithmic: {(fetch + write) / alg:.4f}")
 
+
+def summarize_mfma(root: Path) -> None:
+    """MFMA counters of the prefill GEMM launches (root/pmc: --pmc MfmaUtil
+    MfmaFlopsBF16 MfmaFlopsF32) with their durations from the kernel trace of
+    the same command (root/ktrace)."""
+    rows = _csv_rows(_find(root / "pmc", "_counter_collection.csv"))
+    per = {}
+    for r in rows:
+        if "woq::" not in r["Kernel_Name"]:
+            continue
+        key = (r["Kernel_Name"], int(r["Grid_Size"]))
+        per.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    trace = _csv_rows(_find(root / "ktrace", "_kernel_trace.csv"))
+    durs = {}
+    for r in trace:
+        if "woq::" in r["Kernel_Name"]:
+            key = (r["Kernel_Name"], int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0))
+            durs.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    print("# MFMA counters per woq kernel and launch grid (averages over the launches counted)")
+    for (name, grid), cs in sorted(per.items(), key=lambda kv: -statistics.mean(durs.get(kv[0], [0]))):
+        util = statistics.mean(cs.get("MfmaUtil", [float("nan")]))
+        fb = statistics.mean(cs.get("MfmaFlopsBF16", [0.0]))
+        ff = statistics.mean(cs.get("MfmaFlopsF32", [0.0]))
+        d = durs.get((name, grid))
+        print(f"kernel: {name}")
+        print(f"  grid_threads {grid}: launches_counted {len(cs.get('MfmaUtil', []))}  MfmaUtil_pct {util:.2f}  "
+              f"MfmaFlopsBF16 {fb:.4e}  MfmaFlopsF32 {ff:.4e}")
+        if d:
+            us = statistics.mean(d) / 1e3
+            print(f"  kernel_trace: launches {len(d)}  average_us {us:.3f}  "
+                  f"bf16_TFLOPs {fb / (us * 1e-6) / 1e12:.1f}  frac_of_bf16_peak "
+                  f"{fb / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS:.4f}")
+
+
+def measure_dominant(torch, woq, reps: int = 100):
+    """Per-launch time of the decode kernel on the step's two largest shapes
+    (14336x4096: gate and up; 4096x14336: down) at M=1, group 128: `reps`
+    back-to-back launches in one HIP graph over >= 1 GB of rotating weight
+    copies, HIP events around the replay, median of three replays."""
+    from workloads import DECODE
+
+    cases = [c for c in DECODE if (c.n, c.k) in ((14336, 4096), (4096, 14336))]
+    res = {(r["n"], r["k"]): r for r in measure_configs(torch, woq, reps=reps, cases=cases)}
+    out = {}
+    for (n, k), tag in (((14336, 4096), DOMINANT_TAG), ((4096, 14336), DOWN_TAG)):
+        r = res[(n, k)]
+        ab = algorithmic_bytes(1, n, k, False)
+        achieved = ab / (r["us"] * 1e-6) / 1e9
+        out[(n, k)] = dict(kernel=f"woq::{tag} on {n}x{k}, M=1, group {GROUP}", avg_launch_us=r["us"],
+                           algorithmic_bytes_per_launch=ab, achieved=round(achieved, 1),
+                           frac=round(achieved / HBM_PEAK_GBS, 4), plan=r["plan"])
+    return out
 
 
 def main():
@@ -460,21 +594,33 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--only", choices=["all", "step", "dominant", "prefill"], default="all",
+                    help="step: the decode step alone; dominant: the dominant-kernel timing alone; "
+                         "prefill: the M=2048 timing alone (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the small-M sweep and act-order per-launch timings")
-    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
+    ap.add_argument("--no-graph", action="store_true", help="launch the step eagerly instead of replaying a graph")
     ap.add_argument("--no-grouped", action="store_true", help="skip the grouped-call step")
     ap.add_argument("--no-prepared", action="store_true",
                     help="skip the decode step over prepared weights")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
-    ap.add_argument("--summarize-profiles", metavar="DIR",
-                    help="print the profiles/ summaries from rocprofv3 output under DIR and exit")
+    ap.add_argument("--summarize", nargs=2, metavar=("KIND", "DIR"),
+                    help="print a profiles/ summary (KIND: trace, traffic or mfma) from rocprofv3 output "
+                         "under DIR and exit")
     args = ap.parse_args()
-    if args.summarize_profiles:
-        summarize_profiles(Path(args.summarize_profiles), args.copy_calibration_mib or 512)
+    if args.summarize:
+        kind, where = args.summarize
+        if kind == "trace":
+            summarize_trace(Path(where))
+        elif kind == "traffic":
+            summarize_traffic(Path(where), args.copy_calibration_mib or 512)
+        elif kind == "mfma":
+            summarize_mfma(Path(where))
+        else:
+            raise SystemExit("--summarize KIND is one of trace, traffic, mfma")
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -492,6 +638,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.only == "prefill":
+        print(json.dumps(dict(prefill=measure_prefill(torch, woq),
+                              kernel_source_sha256_16=kernel_source_hash())), flush=True)
+        return
+    if args.only == "dominant":
+        dom = measure_dominant(torch, woq)
+        print(json.dumps(dict(roofline=dict(dom[(14336, 4096)], down=dom[(4096, 14336)]),
+                              kernel_source_sha256_16=kernel_source_hash())), flush=True)
+        return
+
     calls = build_decode_step(torch, woq, args.layers)
     wbytes = sum(weight_bytes(c["n"], c["k"]) for c in calls)
     abytes = [algorithmic_bytes(1, c["n"], c["k"], c["bias"] is not None) for c in calls]
@@ -500,24 +656,14 @@ def main():
                         not args.no_graph)
     ms_per_step = elapsed / args.steps * 1e3
     value = wbytes * args.steps / elapsed / 1e9
-
-    # The step is one graph of back-to-back launches of the decode kernel, so the
-    # kernel's average launch duration is the timed region over the launches in it
-    # (inter-launch gaps included, which makes the figure conservative).
+    # the step's launches on average (one graph of back-to-back launches, gaps included)
     avg_launch = elapsed / (args.steps * len(calls))
-    achieved = sum(abytes) / len(abytes) / avg_launch / 1e9
-    traffic = read_traffic()
-    roofline = dict(
-        bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
-        kernel="woq::gemv_kernel<GB=4,FR=1,CC,PF=4> (every launch of the step)",
-        launches=len(calls), avg_launch_us=round(avg_launch * 1e6, 3),
-        algorithmic_bytes_per_launch=round(sum(abytes) / len(abytes)),
-        traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
-        kernel_source_sha256_16=kernel_source_hash(),
-        plans={f"{c['n']}x{c['k']}": woq.linear_plan(1, c["n"], c["k"], GROUP)
-               for c in calls[:len(calls) // args.layers]},
-    )
+    step_avg = dict(avg_launch_us=round(avg_launch * 1e6, 3), launches=len(calls),
+                    algorithmic_bytes_per_launch=round(sum(abytes) / len(abytes)),
+                    achieved=round(sum(abytes) / len(abytes) / avg_launch / 1e9, 1),
+                    frac=round(sum(abytes) / len(abytes) / avg_launch / 1e9 / HBM_PEAK_GBS, 4),
+                    plans={f"{c['n']}x{c['k']}": woq.linear_plan(1, c["n"], c["k"], GROUP)
+                           for c in calls[:len(calls) // args.layers]})
 
     if args.copy_calibration_mib:
         src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
@@ -526,6 +672,11 @@ def main():
             dst.copy_(src)          # a device-to-device copy: the runtime's copyBuffer kernel
         torch.cuda.synchronize()
         del src, dst
+
+    if args.only == "step":
+        print(json.dumps(dict(metric=METRIC, value=round(value, 1), unit="GB/s", ms_per_step=round(ms_per_step, 4),
+                              step_average=step_avg, kernel_source_sha256_16=kernel_source_hash())), flush=True)
+        return
 
     # The same step with the projections that share their input grouped into one
     # call each (q, k, v; gate, up): one decode launch per group.
@@ -540,8 +691,6 @@ def main():
             ms_per_step=round(el_g / args.steps * 1e3, 4), launches_per_step=len(groups),
             hbm_peak_frac=round(wbytes * args.steps / el_g / 1e9 / HBM_PEAK_GBS, 4),
             avg_launch_us=round(avg_g * 1e6, 3),
-            roofline_achieved=round(sum(abytes) / len(groups) / avg_g / 1e9, 1),
-            roofline_frac=round(sum(abytes) / len(groups) / avg_g / 1e9 / HBM_PEAK_GBS, 4),
             note="woq_linear_int4_groups_grouped: per layer (q,k,v) and (gate,up) share one launch each")
 
     prepared = None
@@ -552,7 +701,6 @@ def main():
         el_p = time_step(torch, lambda: run_calls_prepared(woq, calls), args.steps, args.warmup,
                          not args.no_graph)
         val_p = wbytes * args.steps / el_p / 1e9
-        avg_p = el_p / (args.steps * len(calls))
         el_pg = None if args.no_grouped else time_step(
             torch, lambda: run_groups(woq, groups, prepared=True), args.steps, args.warmup, not args.no_graph)
         prepared = dict(
@@ -560,12 +708,25 @@ def main():
             grouped_value=None if el_pg is None else round(wbytes * args.steps / el_pg / 1e9, 1),
             grouped_ms_per_step=None if el_pg is None else round(el_pg / args.steps * 1e3, 4),
             value=round(val_p, 1), unit="GB/s", ms_per_step=round(el_p / args.steps * 1e3, 4),
-            hbm_peak_frac=round(val_p / HBM_PEAK_GBS, 4), avg_launch_us=round(avg_p * 1e6, 3),
-            roofline_achieved=round(sum(abytes) / len(abytes) / avg_p / 1e9, 1),
-            roofline_frac=round(sum(abytes) / len(abytes) / avg_p / 1e9 / HBM_PEAK_GBS, 4),
-            note="woq_prepare_int4 re-orders each weight once before timing (load time)")
+            hbm_peak_frac=round(val_p / HBM_PEAK_GBS, 4),
+            note="woq_prepare_int4 re-orders each weight once before timing (load time); the prepared "
+                 "weights run on the tile GEMV")
         for c in calls:
             del c["prepared"]
+    del calls, groups
+    torch.cuda.empty_cache()
+
+    dom = measure_dominant(torch, woq)
+    gate = dom[(14336, 4096)]
+    roofline = dict(bound="hbm", achieved=gate["achieved"], peak=HBM_PEAK_GBS, unit="GB/s", frac=gate["frac"],
+                    traffic=read_traffic(), kernel=gate["kernel"], avg_launch_us=gate["avg_launch_us"],
+                    algorithmic_bytes_per_launch=gate["algorithmic_bytes_per_launch"],
+                    timing="100 back-to-back launches in one HIP graph over >= 1 GB of rotating weight copies, "
+                           "HIP events around the replay, median of 3",
+                    traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE on the eager 32-layer "
+                                 "step, copy-calibrated)",
+                    kernel_source_sha256_16=kernel_source_hash(), plan=gate["plan"],
+                    down=dom[(4096, 14336)], step_average=step_avg)
 
     prefill = None if args.no_prefill else measure_prefill(torch, woq)
     configs = None if args.no_configs else measure_configs(torch, woq)
@@ -573,7 +734,7 @@ def main():
     if not args.no_configs:
         from workloads import ZP4
         zp4 = dict(
-            note="packed 4-bit zero points, unpacked into the workspace by each call (woq_linear_int4_groups_zp4)",
+            note="packed 4-bit zero points (woq_linear_int4_groups_zp4)",
             configs=measure_configs(torch, woq, cases=ZP4, zp4=True))
         from workloads import SYM16
         sym16 = dict(
@@ -593,7 +754,7 @@ def main():
         scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
         config=dict(workload="Llama-3-8B decode linears at M=1: 32 layers x (q,k,v,o,gate,up,down), "
                              "int4 group 128, bf16 x, f32 bias on q, bf16 y",
-                    m=1, group=GROUP, layers=args.layers, launches_per_step=len(calls),
+                    m=1, group=GROUP, layers=args.layers, launches_per_step=len(abytes),
                     weight_bytes_per_step=wbytes, hbm_peak_frac=round(value / HBM_PEAK_GBS, 4),
                     graph=not args.no_graph, accumulate="f32",
                     tokens_per_s_linears_only=round(1.0 / (ms_per_step * 1e-3), 1) if args.layers == 32 else None),
