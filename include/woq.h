@@ -487,12 +487,15 @@ int32_t woq_unpack_zero_points(const uint8_t* zero_packed, int64_t n, int64_t ng
                                void* stream);
 
 /*
- * woq_linear_int4_groups with packed zero points: each call first unpacks them
- * into the head of the workspace (one small launch), then runs the same
- * kernels.  Arguments, results and errors as woq_linear_int4_groups, with
- * zero_packed [n, ceil((k/group)/2)] uint8 (device, no alignment needed)
- * replacing zero, and a workspace (256-byte aligned) of
- * woq_linear_int4_groups_zp4_workspace_bytes() bytes, never 0 when m, n, k > 0.
+ * woq_linear_int4_groups with packed zero points: the row-streaming, small-M
+ * and GEMM kernels read the nibbles where they read zero bytes otherwise (no
+ * extra launch); only the tile GEMV (m <= 4 when the WOQ_DECODE_MFMA tuning
+ * variable is set) first unpacks them into the head of the workspace.  Arguments, results and errors as
+ * woq_linear_int4_groups, with zero_packed [n, ceil((k/group)/2)] uint8
+ * (device, no alignment needed) replacing zero, and a workspace (256-byte
+ * aligned) of woq_linear_int4_groups_zp4_workspace_bytes() bytes (may be 0).
+ * Results are bit-identical to woq_linear_int4_groups over the unpacked zero
+ * points.
  */
 int32_t woq_linear_int4_groups_zp4(const void* x_bf16, int64_t m, const uint8_t* packed, const float* scale,
                                    const uint8_t* zero_packed, const float* bias, const int32_t* order, int64_t n,
@@ -500,9 +503,10 @@ int32_t woq_linear_int4_groups_zp4(const void* x_bf16, int64_t m, const uint8_t*
                                    size_t workspace_bytes, void* stream);
 
 /*
- * Workspace woq_linear_int4_groups_zp4 needs: the unpacked zero points
- * (rounded up to 256 bytes) plus woq_linear_workspace_bytes(...).  Pure host
- * function; 0 for invalid shapes or an empty problem.
+ * Workspace woq_linear_int4_groups_zp4 needs: woq_linear_workspace_bytes(...),
+ * plus the unpacked zero points (n * k/group bytes rounded up to 256) when the
+ * call runs on the tile GEMV.  Pure host function; 0 for invalid shapes or an
+ * empty problem.
  */
 size_t woq_linear_int4_groups_zp4_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group,
                                                   int32_t has_order);

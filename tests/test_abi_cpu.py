@@ -322,7 +322,7 @@ def test_awq_entry_point_validates_first(lib):
     assert best.value == -1
 
 
-def test_zero_point_entry_points_validate_first(lib):
+def test_zero_point_entry_points_validate_first(lib, monkeypatch):
     fake = ctypes.c_void_p(1 << 20)
     odd = ctypes.c_void_p((1 << 20) + 8)
     st = lambda rc: woq.STATUS[rc]
@@ -332,12 +332,19 @@ def test_zero_point_entry_points_validate_first(lib):
     assert st(lib.woq_unpack_zero_points(fake, 4, 8, None, None)) == "WOQ_EINVAL"
     assert st(lib.woq_unpack_zero_points(None, 4, 0, None, None)) == "WOQ_OK"
     ws = lib.woq_linear_int4_groups_zp4_workspace_bytes
-    # the unpacked zero points (n * k/group, rounded to 256) ahead of the linear's own workspace
-    assert ws(1, 4096, 4096, 128, 0) == 4096 * 32 + lib.woq_linear_workspace_bytes(1, 4096, 4096, 128, 0)
-    assert ws(256, 300, 4096, 64, 1) == 19200 + lib.woq_linear_workspace_bytes(256, 300, 4096, 64, 1)
+    # the kernels read packed zero points as they are: the linear's own workspace ...
+    assert ws(1, 4096, 4096, 128, 0) == lib.woq_linear_workspace_bytes(1, 4096, 4096, 128, 0) == 0
+    assert ws(256, 300, 4096, 64, 1) == lib.woq_linear_workspace_bytes(256, 300, 4096, 64, 1)
+    assert ws(16, 300, 4096, 64, 1) == lib.woq_linear_workspace_bytes(16, 300, 4096, 64, 1)
+    # ... except on the tile GEMV (m <= 4 with WOQ_DECODE_MFMA set), which takes them unpacked
+    # (n * k/group bytes, rounded up to 256)
+    monkeypatch.setenv("WOQ_DECODE_MFMA", "1")
+    assert ws(1, 300, 4096, 128, 0) == (300 * 32 + 255) // 256 * 256 + lib.woq_linear_workspace_bytes(
+        1, 300, 4096, 128, 0)
+    monkeypatch.delenv("WOQ_DECODE_MFMA")
     assert ws(0, 4096, 4096, 128, 0) == 0 and ws(1, 4096, 4000, 128, 0) == 0
-    zp4 = lambda **kw: lib.woq_linear_int4_groups_zp4(fake, 1, fake, fake, kw.get("zp", fake), None, None, 64, 256,
-                                                      128, 1, fake, kw.get("ws", fake), kw.get("wsb", 1 << 20),
+    zp4 = lambda **kw: lib.woq_linear_int4_groups_zp4(fake, 200, fake, fake, kw.get("zp", fake), None, None, 64,
+                                                      256, 128, 1, fake, kw.get("ws", fake), kw.get("wsb", 1 << 20),
                                                       None)
     assert st(zp4(zp=None)) == "WOQ_EINVAL"
     assert st(zp4(ws=None, wsb=0)) == "WOQ_EWORKSPACE"

@@ -4,8 +4,8 @@ linnet "Quantization": Int4GroupLinear's layout is ONNX Runtime's MatMulNBits,
 whose zero points are 4-bit values two a byte (R15 in the oracle).  Packing
 and unpacking bit-exact (every pair of values, odd group counts); the linear
 over packed zero points against the oracle to the linear layer's bar on the
-decode, small-M and GEMM paths, and bit-identical to the same call with the
-zero points unpacked.  Each case prints its name first.
+row-streaming, tile GEMV, small-M and GEMM paths, and bit-identical to the
+same call with the zero points unpacked.  Each case prints its name first.
 """
 import sys
 
@@ -61,10 +61,22 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("m,n,k,group,with_bias,with_order", CASES)
+# the tile GEMV (chosen with WOQ_DECODE_MFMA) unpacks the zero points into the
+# workspace first; every other path reads them packed
+CASES_GEMV = [(1, 300, 384, 128, True, True, "1"), (4, 100, 1280, 256, False, False, "1")]
+
+
+@pytest.mark.parametrize("m,n,k,group,with_bias,with_order,decode_mfma",
+                         [c + ("",) for c in CASES] + CASES_GEMV)
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_linear_zp4(woq, m, n, k, group, with_bias, with_order, out):
-    _say(f"zp4 linear m={m} n={n} k={k} group={group} bias={with_bias} order={with_order} {out}")
+def test_linear_zp4(woq, monkeypatch, m, n, k, group, with_bias, with_order, decode_mfma, out):
+    if decode_mfma:
+        monkeypatch.setenv("WOQ_DECODE_MFMA", decode_mfma)
+    else:
+        monkeypatch.delenv("WOQ_DECODE_MFMA", raising=False)
+    plan = woq.linear_plan(m, n, k, group, with_order)
+    _say(f"zp4 linear m={m} n={n} k={k} group={group} bias={with_bias} order={with_order} {out} plan: {plan}")
+    assert ("path=gemv_mfma" in plan) == bool(decode_mfma)
     seed = m + n + k
     packed, scale, zero = workloads.packed_weights(n, k, group, seed=seed)
     x = workloads.activations_bf16(m, k, seed=seed + 1)

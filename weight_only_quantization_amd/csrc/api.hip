@@ -485,7 +485,9 @@ size_t woq_linear_int4_groups_zp4_workspace_bytes(int64_t m, int64_t n, int64_t 
                                                   int32_t has_order) {
   if (check_linear_shape(m, n, k, group) != WOQ_OK) return 0;
   if (m == 0 || n == 0 || k == 0) return 0;
-  return round256((size_t)n * (size_t)(k / group)) + linear_workspace_layout(m, n, k, group, has_order != 0).total;
+  const LinearPlan plan = linear_plan(m, n, k, group, has_order != 0);
+  return (plan.path == 4 ? round256((size_t)n * (size_t)(k / group)) : 0) +
+         linear_workspace_layout(m, n, k, group, has_order != 0).total;
 }
 
 int32_t woq_pack_zero_points(const uint8_t* zero, int64_t n, int64_t ngroups, uint8_t* packed, void* stream) {
@@ -534,7 +536,7 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
                     const uint16_t* scale16 = nullptr, const uint8_t* scale8 = nullptr,
                     const float* scale_row = nullptr, const uint8_t* zero_packed = nullptr) {
   const bool row = scale_row != nullptr;     // Int4Linear: signed codes, one float32 scale a row
-  const bool zp4 = zero_packed != nullptr;   // packed 4-bit zero points, unpacked into the workspace
+  const bool zp4 = zero_packed != nullptr;   // packed 4-bit zero points
   const bool sym16 = scale16 != nullptr || row;
   const bool mx = scale8 != nullptr;
   int32_t st = check_linear_shape(m, n, k, group);
@@ -557,7 +559,10 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
   if (has_order && !aligned(order, 16)) return WOQ_EALIGN;
   const LinearPlan plan = linear_plan(m, n, k, group, has_order, !prepared && !mx);
   const LinearWorkspace ws = linear_workspace_layout(m, n, k, group, has_order);
-  const size_t zbytes = zp4 ? round256((size_t)n * (size_t)(k / group)) : 0;
+  // The tile GEMV reads one zero point a byte: packed ones are unpacked into the
+  // head of the workspace first; every other path reads them as they are.
+  const bool zp4_unpack = zp4 && plan.path == 4;
+  const size_t zbytes = zp4_unpack ? round256((size_t)n * (size_t)(k / group)) : 0;
   if (plan.path == 2 && k >= kGemmMaxK) return WOQ_EUNSUPPORTED;
   if (ws.total + zbytes > 0) {
     if (!workspace || workspace_bytes < ws.total + zbytes) return WOQ_EWORKSPACE;
@@ -565,10 +570,12 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
   }
   char* wsb = static_cast<char*>(workspace) + zbytes;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (zp4) {
+  if (zp4_unpack) {
     st = launch_unpack_zero_points(zero_packed, n, k / group, static_cast<uint8_t*>(workspace), s);
     if (st != WOQ_OK) return st;
     zero = static_cast<const uint8_t*>(workspace);
+  } else if (zp4) {
+    zero = zero_packed;
   }
   LinearArgs a{};
   a.x = static_cast<const uint16_t*>(x_bf16);
@@ -590,6 +597,7 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
   a.mx = mx ? 1 : 0;
   a.scale8 = scale8;
   a.row_scale = row ? 1 : 0;
+  a.zp4 = zp4 && !zp4_unpack ? 1 : 0;
   if (row) a.scale = scale_row;
   if (plan.path == 1) {
     if (has_order) {

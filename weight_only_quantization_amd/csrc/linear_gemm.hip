@@ -96,7 +96,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
 __global__ __launch_bounds__(256) void sz_prep_kernel(const void* __restrict__ scale,
                                                       const uint8_t* __restrict__ zero, int32_t n,
                                                       int32_t ngroups, int32_t npad, int32_t fmt,
-                                                      int32_t row_scale, f32x2_t* __restrict__ sz) {
+                                                      int32_t row_scale, int32_t zp4,
+                                                      f32x2_t* __restrict__ sz) {
   const int64_t total = (int64_t)ngroups * npad;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
@@ -112,8 +113,12 @@ __global__ __launch_bounds__(256) void sz_prep_kernel(const void* __restrict__ s
         const float sc = row_scale ? static_cast<const float*>(scale)[c]
                                    : (float)static_cast<const _Float16*>(scale)[e];
         v = f32x2_t{sc, -(kNibOffset + 8.0f)};
-      } else
-        v = f32x2_t{static_cast<const float*>(scale)[e], -(kNibOffset + (float)zero[e])};
+      } else {
+        // packed zero points: group g in nibble g & 1 of byte g / 2 of the row
+        const uint32_t zq = zp4 ? (zero[(int64_t)c * ((ngroups + 1) / 2) + g / 2] >> (4 * (g & 1))) & 15u
+                                : zero[e];
+        v = f32x2_t{static_cast<const float*>(scale)[e], -(kNibOffset + (float)zq)};
+      }
     }
     sz[t] = v;
   }
@@ -690,7 +695,7 @@ int32_t launch_gemm(const LinearArgs& a, const LinearPlan& pl, void* sz_ws, hipS
                             : a.sym16 && !a.row_scale ? static_cast<const void*>(a.scale16)
                                                       : static_cast<const void*>(a.scale),
                        a.zero, a.n, ngroups, npad, a.mx ? kFmtMX : a.sym16 ? kFmtS16 : kFmtU4,
-                       a.row_scale, static_cast<f32x2_t*>(sz_ws));
+                       a.row_scale, a.zp4, static_cast<f32x2_t*>(sz_ws));
     const int32_t st = hip_status(hipGetLastError());
     if (st != WOQ_OK) return st;
   }

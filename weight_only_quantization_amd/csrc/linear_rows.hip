@@ -62,6 +62,8 @@ struct RowsParams {
   int32_t m, k, y_bf16;
   int32_t ngroups, group_shift;
   int32_t row_scale;      // signed codes with one float32 scale a row
+  int32_t zp4;            // zero points packed two a byte (group 2j in the low nibble of byte j)
+  int32_t zrow;           // zero-point bytes per row: ngroups, or ceil(ngroups / 2) with zp4
   uint32_t nib_mask, nib_offset;
   int32_t nprob;
   RowsProblem prob[kMaxGrouped];
@@ -195,7 +197,12 @@ __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
   const int srow = row_scale ? 1 : ng;
   const __amdgpu_buffer_rsrc_t rs =
       rsrc(static_cast<const char*>(pr.scale) + (int64_t)row0 * srow * sbytes, (uint32_t)(rows * srow) * sbytes);
-  const __amdgpu_buffer_rsrc_t rz = rsrc(S16 ? nullptr : pr.zero + (int64_t)row0 * ng, S16 ? 0u : (uint32_t)(rows * ng));
+  const int zrow = p.zrow;
+  const __amdgpu_buffer_rsrc_t rz =
+      rsrc(S16 ? nullptr : pr.zero + (int64_t)row0 * zrow, S16 ? 0u : (uint32_t)(rows * zrow));
+  const bool zp4 = p.zp4 != 0;   // uniform
+  const uint32_t zsh = zp4 ? 4u * (uint32_t)(g & 1) : 0u;   // the lane's zero point: bits [zsh, zsh + zbits)
+  const uint32_t zbits = zp4 ? 4u : 8u;
 
   // 1. Activations, scales and zero points first, then every weight load of
   //    the wave: rows past N and lanes past K read zero.
@@ -207,7 +214,7 @@ __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
     for (int i = 0; i < 4; ++i) xr[mm][i] = bload16(rx, ((uint32_t)(xm * K + kin) * 2u + 16u * i) | dead);
   }
   float s[U];
-  float nz[U];
+  uint32_t zr[U];   // zero-point bytes as loaded (converted after the weight loads are out)
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t e = (uint32_t)(u * ng + g);
@@ -216,10 +223,11 @@ __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
         s[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(((uint32_t)u * 4u) | dead), 0, 0));
       else
         s[u] = (float)__builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)((e * 2u) | dead), 0, 0));
-      nz[u] = -136.f;
+      zr[u] = 0u;
     } else {
       s[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)((e * 4u) | dead), 0, 0));
-      nz[u] = (float)(uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rz, (int)(e | dead), 0, 0);
+      const uint32_t ze = zp4 ? (uint32_t)(u * zrow + (g >> 1)) : e;
+      zr[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rz, (int)(ze | dead), 0, 0);
     }
   }
   u32x4_t w[U];
@@ -250,7 +258,8 @@ __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
   float v[MR][U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if constexpr (!S16) nz[u] = -128.f - nz[u];
+    // -(128 + zero): the codes enter the dot product as 128 + q
+    const float nz = S16 ? -136.f : -128.f - (float)__builtin_amdgcn_ubfe(zr[u], zsh, zbits);
 #pragma unroll
     for (int mm = 0; mm < MR; ++mm) {
       float r0 = 0.f, r1 = 0.f;
@@ -262,7 +271,7 @@ __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
         r0 = dot2(((wd >> 8) & mask) | off, xp[mm][4 * d + 2], r0);
         r1 = dot2(((wd >> 12) & mask) | off, xp[mm][4 * d + 3], r1);
       }
-      v[mm][u] = s[u] * fmaf(nz[u], X[mm], r0 + r1);
+      v[mm][u] = s[u] * fmaf(nz, X[mm], r0 + r1);
     }
   }
 
@@ -370,6 +379,8 @@ int32_t launch_rows(const LinearArgs* args, int count, int u, hipStream_t stream
   rp.ngroups = a.k / a.group;
   rp.group_shift = gshift;
   rp.row_scale = a.row_scale;
+  rp.zp4 = a.zp4;
+  rp.zrow = a.zp4 ? (rp.ngroups + 1) / 2 : rp.ngroups;
   rp.nib_mask = 0x000F000Fu;    // one nibble in each bf16 half
   rp.nib_offset = 0x43004300u;  // bf16 pair (128, 128): OR-ing a nibble n gives 128 + n
   rp.nprob = count;

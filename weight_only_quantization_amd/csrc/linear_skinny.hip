@@ -62,6 +62,8 @@ struct SkinnyParams {
   uint32_t nib_mask, nib_offset;
   int32_t row_scale;  // signed codes with one float32 scale a row (Int4Linear)
   int32_t wm;         // wave groups along the activation rows (each takes MT tiles of 16 rows)
+  int32_t zp4;        // zero points packed two a byte (group 2j in the low nibble of byte j)
+  int32_t zrow;       // zero-point bytes per row: ngroups, or ceil(ngroups / 2) with zp4
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
@@ -128,11 +130,14 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   const __amdgpu_buffer_rsrc_t rs =
       rsrc(static_cast<const char*>(p.scale) + (int64_t)tile0 * 16 * srow * sbytes,
            (uint32_t)(wg_rows * srow) * sbytes);
-  const __amdgpu_buffer_rsrc_t rz = rsrc(S16 || MX ? nullptr : p.zero + (int64_t)tile0 * 16 * p.ngroups,
-                                         S16 || MX ? 0u : (uint32_t)(wg_rows * p.ngroups));
+  const int zrow = p.zrow;
+  const bool zp4 = p.zp4 != 0;   // uniform
+  const __amdgpu_buffer_rsrc_t rz = rsrc(S16 || MX ? nullptr : p.zero + (int64_t)tile0 * 16 * zrow,
+                                         S16 || MX ? 0u : (uint32_t)(wg_rows * zrow));
   const int sz_total = 16 * T * ngw;
   uint32_t sv[kStageBatch];   // float32 bits, or float16 bits for S16 (converted when stored)
   uint32_t zv[kStageBatch];
+  uint32_t zs[kStageBatch];   // bit offset of the zero point in its loaded byte
   auto stage_load = [&](int base) {
 #pragma unroll
     for (int b = 0; b < kStageBatch; ++b) {
@@ -143,15 +148,19 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
       if constexpr (MX) {
         sv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, in ? idx : kOffsetOOB, 0, 0);
         zv[b] = 0u;
+        zs[b] = 0u;
       } else if constexpr (S16) {
         if (row_scale)
           sv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, in ? (uint32_t)r * 4u : kOffsetOOB, 0, 0);
         else
           sv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, in ? idx * 2u : kOffsetOOB, 0, 0);
         zv[b] = 8u;
+        zs[b] = 0u;
       } else {
         sv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, in ? idx * 4u : kOffsetOOB, 0, 0);
-        zv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rz, in ? idx : kOffsetOOB, 0, 0);
+        const uint32_t zidx = zp4 ? (uint32_t)(r * zrow + ((gb + g) >> 1)) : idx;
+        zs[b] = zp4 ? 4u * (uint32_t)((gb + g) & 1) : 0u;
+        zv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rz, in ? zidx : kOffsetOOB, 0, 0);
       }
     }
   };
@@ -166,8 +175,9 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
       } else {
         const float sc = S16 && !row_scale ? (float)__builtin_bit_cast(_Float16, (uint16_t)sv[b])
                                            : __builtin_bit_cast(float, sv[b]);
+        const uint32_t zq = __builtin_amdgcn_ubfe(zv[b], zs[b], zp4 ? 4u : 8u);
         if (e < sz_total)
-          *reinterpret_cast<f32x2_t*>(szl + e * 8) = f32x2_t{sc, -(kNibOffset + (float)(zv[b] & 0xFFu))};
+          *reinterpret_cast<f32x2_t*>(szl + e * 8) = f32x2_t{sc, -(kNibOffset + (float)zq)};
       }
     }
   };
@@ -426,7 +436,8 @@ int32_t launch_skinny(const LinearArgs& a, const LinearPlan& pl, hipStream_t str
                                                  : static_cast<const void*>(a.scale),
                   a.zero, a.bias, a.y, a.m, a.n, a.k, a.y_bf16,
                   (a.k + kStepK - 1) / kStepK, a.k / a.group, a.prepared, pl.cnt, l.ngw,
-                  l.sz_bytes, (int32_t)l.red_off, kNibPairMask, kBf16Offset2, a.row_scale, pl.wm};
+                  l.sz_bytes, (int32_t)l.red_off, kNibPairMask, kBf16Offset2, a.row_scale, pl.wm, a.zp4,
+                  a.zp4 ? (a.k / a.group + 1) / 2 : a.k / a.group};
   if (a.mx) return a.group == 32 ? dispatch_mt<32, kFmtMX>(sp, pl, l.total, stream) : WOQ_EUNSUPPORTED;
   if (a.sym16) {
     switch (a.group) {

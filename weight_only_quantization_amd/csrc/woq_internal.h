@@ -118,6 +118,8 @@ struct LinearArgs {
   int32_t mx;              // 1: MXFP4 (E2M1 codes, E8M0 scale per block of 32; group = 32)
   const uint8_t* scale8;   // [N, K/32] E8M0 scale bytes when mx
   int32_t row_scale;       // 1 (with sym16): one float32 scale a row in `scale` [N] (Int4Linear)
+  int32_t zp4;             // 1: `zero` holds packed 4-bit zero points [N, ceil(K/G / 2)], group 2j
+                           //    in the low nibble of byte j (row-streaming, small-M and GEMM paths)
 };
 
 // Weight formats of the linear kernels' instantiations.
