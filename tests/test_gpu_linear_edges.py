@@ -198,3 +198,65 @@ def test_rows_matches_tile_gemv(woq, monkeypatch):
         torch.cuda.synchronize()
         scale = float(a.abs().max())
         assert float((a - b).abs().max()) <= 1e-5 * scale
+
+
+# Small-M activations through the fragment-order pre-pass (WOQ_SKINNY_XFRAG=1)
+# and straight from x (=0): the same bf16 values meet the same weight
+# fragments in the same order, so the outputs are bit-identical; both are
+# checked against the oracle too.  Unsigned codes, signed float16-scale codes
+# and MXFP4, with and without the act-order gather.
+XFRAG_CASES = [
+    # m, n, k, group, bias, order, format
+    (17, 100, 1024, 128, True, False, "u4"),
+    (24, 64, 2048, 32, False, True, "u4"),
+    (33, 70, 1536, 64, True, True, "u4"),
+    (48, 130, 4096, 256, False, False, "u4"),
+    (64, 50, 768, 128, True, True, "u4"),
+    (40, 96, 1024, 32, True, False, "sym16"),
+    (56, 80, 2048, 32, False, False, "mx"),
+]
+
+
+@pytest.mark.parametrize("m,n,k,group,with_bias,with_order,fmt", XFRAG_CASES)
+def test_skinny_fragment_prepass(woq, monkeypatch, m, n, k, group, with_bias, with_order, fmt):
+    _env(monkeypatch, {})
+    seed = 9100 + m + n + k
+    x = workloads.activations_bf16(m, k, seed + 1)
+    b = workloads.bias(n, seed + 2) if with_bias else None
+    o = workloads.order(k, seed + 3) if with_order and fmt != "mx" else None
+    w = workloads.weight(n, k, seed=seed)
+    wd = torch.from_numpy(w).cuda()
+    if fmt == "u4":
+        q, s, z = woq.quantize_groups(wd, group)
+        packed = woq.pack_uint4(q)
+        qr, sr, zr = oracle.quantize_groups(w, group)
+        ref = oracle.linear_int4_groups(x, oracle.pack_uint4(qr), sr, zr, n, k, group, bias=b, order=o)
+        call = lambda out: woq.linear_int4_groups(
+            to_dev_bf16(x), packed, s, z, bias=None if b is None else torch.from_numpy(b).cuda(),
+            order=None if o is None else torch.from_numpy(o).cuda(), group=group, out_dtype=out)
+    elif fmt == "sym16":
+        c, s16 = woq.quantize_int4_sym(wd, group)
+        packed = woq.pack_int4(c)
+        cr, sr = oracle.quantize_int4_sym_f16(w, group)
+        ref = oracle.linear_int4_sym_f16(x, oracle.pack_int4(cr), sr, n, k, group, bias=b)
+        call = lambda out: woq.linear_int4_sym(to_dev_bf16(x), packed, s16,
+                                               bias=None if b is None else torch.from_numpy(b).cuda(),
+                                               group=group, out_dtype=out)
+    else:
+        codes, scales = woq.quantize_mxfp4(wd)
+        blocks = woq.pack_uint4(codes)
+        cr, sr = oracle.quantize_mxfp4(w)
+        ref = oracle.linear_mxfp4(x, oracle.pack_uint4(cr), sr, n, k, bias=b)
+        call = lambda out: woq.linear_mxfp4(to_dev_bf16(x), blocks, scales,
+                                            bias=None if b is None else torch.from_numpy(b).cuda(), out_dtype=out)
+    outs = {}
+    for flag in ("1", "0"):
+        monkeypatch.setenv("WOQ_SKINNY_XFRAG", flag)
+        plan = woq.linear_plan(m, n, k, 32 if fmt == "mx" else group, o is not None)
+        _say(f"xfrag={flag} {fmt} m={m} n={n} k={k} g={group} plan: {plan}")
+        assert "path=skinny_mfma" in plan and (("fragments" in plan) == (flag == "1")), plan
+        outs[flag] = {dt: call(dt) for dt in (torch.float32, torch.bfloat16)}
+        torch.cuda.synchronize()
+    for dt in (torch.float32, torch.bfloat16):
+        assert torch.equal(outs["1"][dt], outs["0"][dt])
+        check_linear(outs["1"][dt], ref, f"xfrag {fmt} m={m} n={n} k={k} g={group}")

@@ -83,6 +83,16 @@ bool skinny_plan(int64_t m, int64_t n, int64_t k, int32_t group, LinearPlan* p) 
   p->path = 1;
   p->mt = (int)mt;
   p->wm = (int)wm;
+  // From 24 rows (groups of 128 and more) or 33 rows (any group) the
+  // activations go through a pre-pass into fragment order: contiguous
+  // kilobyte loads and no in-kernel reordering, which outweigh the extra
+  // launch there (measured on 14336x4096 at groups 32 and 128: 12 % faster at
+  // 32 rows, 19 % at 64; 4 % slower at 17).  WOQ_SKINNY_XFRAG=0/1 overrides
+  // (a tuning aid, read on every call).
+  p->xfrag = mtt >= 2 && nsteps <= 8192 && (m > 32 || (m >= 24 && group >= 128)) ? 1 : 0;
+  if (const char* e = std::getenv("WOQ_SKINNY_XFRAG"); e && (e[0] == '0' || e[0] == '1') && mtt >= 2 &&
+                                                          nsteps <= 8192)
+    p->xfrag = e[0] - '0';
   p->fold_rows = 4;
   p->ns = t;
   p->waves = (int)waves;
@@ -206,7 +216,10 @@ LinearWorkspace linear_workspace_layout(int64_t m, int64_t n, int64_t k, int32_t
                                         bool has_order) {
   LinearWorkspace w;
   const LinearPlan p = linear_plan(m, n, k, group, has_order);
-  if ((p.path == 1 || p.path == 4 || p.path == 5) && has_order) {
+  if (p.path == 1 && p.xfrag) {
+    w.xg_off = 0;
+    w.xg_bytes = round256(xfrag_bytes(m, k));
+  } else if ((p.path == 1 || p.path == 4 || p.path == 5) && has_order) {
     w.xg_off = 0;
     w.xg_bytes = round256((size_t)m * (size_t)k * 2);
   } else if (p.path == 2) {
@@ -600,7 +613,12 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
   a.zp4 = zp4 && !zp4_unpack ? 1 : 0;
   if (row) a.scale = scale_row;
   if (plan.path == 1) {
-    if (has_order) {
+    if (plan.xfrag) {
+      uint16_t* xf = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
+      st = launch_xfrag(a.x, order, a.m, a.k, group, mx ? 1 : 0, xf, s);
+      if (st != WOQ_OK) return st;
+      a.x = xf;
+    } else if (has_order) {
       uint16_t* xg = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
       st = launch_prep(a.x, order, a.m, a.k, a.k, group, 0, xg, nullptr, m, s);
       if (st != WOQ_OK) return st;
@@ -864,7 +882,8 @@ int32_t woq_linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, int32_t 
       std::snprintf(buf, len,
                     "path=skinny_mfma act_tiles=%d wave_groups=%d weight_tiles=%d waves=%d steps_per_wave=%d "
                     "group_blocks=%d grid=%lld prep=%s workspace=%zu",
-                    p.mt, p.wm, p.ns, p.waves, p.cnt, p.gb, (long long)p.grid, p.prep ? "gather" : "none", ws);
+                    p.mt, p.wm, p.ns, p.waves, p.cnt, p.gb, (long long)p.grid,
+                    p.xfrag ? (p.prep ? "gather+fragments" : "fragments") : (p.prep ? "gather" : "none"), ws);
       break;
     case 4:
       std::snprintf(buf, len,

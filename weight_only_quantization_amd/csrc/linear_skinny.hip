@@ -64,6 +64,7 @@ struct SkinnyParams {
   int32_t wm;         // wave groups along the activation rows (each takes MT tiles of 16 rows)
   int32_t zp4;        // zero points packed two a byte (group 2j in the low nibble of byte j)
   int32_t zrow;       // zero-point bytes per row: ngroups, or ceil(ngroups / 2) with zp4
+  int32_t mtiles;     // 16-row activation tiles in the fragment-ordered copy (XF)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
@@ -83,7 +84,9 @@ __device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t of
 // already multiplied by the block's power-of-two scale (exact), so the MFMAs
 // accumulate straight into the outputs, in natural input order, with no
 // per-group fold.
-template <int G, int MT, int T, int FMT>
+// XF: x is the fragment-ordered copy the pre-pass wrote (x_frag_kernel): the
+// four chunks of a step are four contiguous kilobytes, already pair-ordered.
+template <int G, int MT, int T, int FMT, bool XF>
 __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   constexpr bool S16 = FMT == kFmtS16, MX = FMT == kFmtMX;
   static_assert(!MX || G == 32, "MXFP4 blocks hold 32 inputs");
@@ -191,7 +194,8 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   const __amdgpu_buffer_rsrc_t rb =
       prep ? rsrc(p.packed + (int64_t)tile0 * nsteps * 1024, (uint32_t)(wg_tiles * nsteps) * 1024u)
            : rsrc(p.packed + (int64_t)tile0 * 16 * row_bytes, (uint32_t)wg_rows * row_bytes);
-  const __amdgpu_buffer_rsrc_t rx = rsrc(p.x, (uint32_t)M * (uint32_t)K * 2u);
+  const __amdgpu_buffer_rsrc_t rx =
+      rsrc(p.x, XF ? (uint32_t)p.mtiles * (uint32_t)nsteps * 4096u : (uint32_t)M * (uint32_t)K * 2u);
   const uint32_t wstep = prep ? 1024u : 64u;
   uint32_t woff[T];
 #pragma unroll
@@ -216,6 +220,17 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   };
   auto issue_x = [&](int slot, int i) {
     const uint32_t dead = (uint32_t)(live - 1 - i) & kOffsetOOB;
+    if constexpr (XF) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int tile = wm * MT + mt;
+        const uint32_t base = (uint32_t)((tile * nsteps + s0 + i) * 4) * 1024u + 16u * (uint32_t)lane;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          xb[slot][mt][e] = bload16(rx, tile < p.mtiles ? (base + 1024u * (uint32_t)e) | dead : kOffsetOOB);
+      }
+      return;
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const bool in_k = i * kStepK + kXEIn * e < xlim;
@@ -285,7 +300,8 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) af[mt][e] = pair_order(xb[slot][mt][e]);
+      for (int e = 0; e < 4; ++e)
+        af[mt][e] = XF ? __builtin_bit_cast(bf16x8_t, xb[slot][mt][e]) : pair_order(xb[slot][mt][e]);
 #pragma unroll
       for (int pc = 0; pc < NP; ++pc) {
         f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -380,9 +396,48 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p) {
   }
 }
 
-template <int G, int MT, int T, int FMT>
+// Pre-pass for m > 16: one thread per 16-byte chunk of the fragment-ordered
+// copy, enumerated in its storage order (tile, step, chunk e, lane), so the
+// writes are contiguous.  Lane (q, c) of tile t holds, for chunk e of step s,
+// the 8 inputs from s*128 + 32q + 8e (groups of 128 and more, and MXFP4) or
+// s*128 + 8q + 32e (smaller groups) of activation row 16t + c: the inputs the
+// kernel's weight fragments of that lane meet.  The act-order gather happens
+// here too (indices clamped into range, as in the other pre-pass).
+template <bool TR, bool NATURAL>
+__global__ __launch_bounds__(256) void x_frag_kernel(const uint16_t* __restrict__ x,
+                                                     const int32_t* __restrict__ order, int32_t m,
+                                                     int32_t k, int32_t nsteps, int64_t total,
+                                                     uint16_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+    const int lane = (int)(t & 63), e = (int)((t >> 6) & 3);
+    const int64_t ts = t >> 8;
+    const int step = (int)(ts % nsteps), tile = (int)(ts / nsteps);
+    const int q = lane >> 4, c = lane & 15;
+    const int row = 16 * tile + c;
+    const int in = step * kStepK + (TR ? 8 * q + 32 * e : 32 * q + 8 * e);
+    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+    if (row < m && in < k) {   // k is a multiple of 32, so the 8 inputs are all in range
+      const uint16_t* xr = x + (int64_t)row * k;
+      if (order) {
+        uint32_t h[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int32_t src = order[in + i];
+          h[i] = xr[src < 0 ? 0 : (src >= k ? k - 1 : src)];
+        }
+        v = u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      } else {
+        v = load16(xr + in);
+      }
+    }
+    *reinterpret_cast<u32x4_t*>(out + t * 8) = NATURAL ? v : __builtin_bit_cast(u32x4_t, pair_order(v));
+  }
+}
+
+template <int G, int MT, int T, int FMT, bool XF>
 int32_t launch_one(const SkinnyParams& sp, const LinearPlan& pl, size_t lds, hipStream_t stream) {
-  auto kern = skinny_kernel<G, MT, T, FMT>;
+  auto kern = skinny_kernel<G, MT, T, FMT, XF>;
   if (lds > 64 * 1024) {
     static std::atomic<uint64_t> raised{0};   // per instantiation, one bit per device
     const int32_t st = raise_lds_limit(reinterpret_cast<const void*>(kern), 160 * 1024, raised);
@@ -392,21 +447,22 @@ int32_t launch_one(const SkinnyParams& sp, const LinearPlan& pl, size_t lds, hip
   return hip_status(hipGetLastError());
 }
 
-template <int G, int MT, int FMT>
+template <int G, int MT, int FMT, bool XF>
 int32_t dispatch_t(const SkinnyParams& sp, const LinearPlan& pl, size_t lds, hipStream_t s) {
   switch (pl.ns) {
-    case 1: return launch_one<G, MT, 1, FMT>(sp, pl, lds, s);
-    case 2: return launch_one<G, MT, 2, FMT>(sp, pl, lds, s);
-    case 4: return launch_one<G, MT, 4, FMT>(sp, pl, lds, s);
+    case 1: return launch_one<G, MT, 1, FMT, XF>(sp, pl, lds, s);
+    case 2: return launch_one<G, MT, 2, FMT, XF>(sp, pl, lds, s);
+    case 4: return launch_one<G, MT, 4, FMT, XF>(sp, pl, lds, s);
     default: return WOQ_EUNSUPPORTED;
   }
 }
 
+// The fragment-ordered activations serve two activation tiles per wave (m > 16).
 template <int G, int FMT>
 int32_t dispatch_mt(const SkinnyParams& sp, const LinearPlan& pl, size_t lds, hipStream_t s) {
   switch (pl.mt) {
-    case 1: return dispatch_t<G, 1, FMT>(sp, pl, lds, s);
-    case 2: return dispatch_t<G, 2, FMT>(sp, pl, lds, s);
+    case 1: return pl.xfrag ? WOQ_EUNSUPPORTED : dispatch_t<G, 1, FMT, false>(sp, pl, lds, s);
+    case 2: return pl.xfrag ? dispatch_t<G, 2, FMT, true>(sp, pl, lds, s) : dispatch_t<G, 2, FMT, false>(sp, pl, lds, s);
     default: return WOQ_EUNSUPPORTED;
   }
 }
@@ -414,6 +470,28 @@ int32_t dispatch_mt(const SkinnyParams& sp, const LinearPlan& pl, size_t lds, hi
 }  // namespace
 
 int64_t mt_total(int64_t m) { return (m + 15) / 16; }
+
+size_t xfrag_bytes(int64_t m, int64_t k) {
+  return (size_t)mt_total(m) * (size_t)((k + kStepK - 1) / kStepK) * 4096u;
+}
+
+int32_t launch_xfrag(const uint16_t* x, const int32_t* order, int32_t m, int32_t k, int32_t group,
+                     int32_t natural, uint16_t* out, hipStream_t stream) {
+  const int32_t nsteps = (k + kStepK - 1) / kStepK;
+  const int64_t total = mt_total(m) * (int64_t)nsteps * 256;
+  if (total == 0) return WOQ_OK;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  const bool tr = group < kStepK && !natural;   // the kernel's lane-group transpose for groups under 128
+  const dim3 g((unsigned)blocks), b(256);
+  if (natural)
+    hipLaunchKernelGGL((x_frag_kernel<false, true>), g, b, 0, stream, x, order, m, k, nsteps, total, out);
+  else if (tr)
+    hipLaunchKernelGGL((x_frag_kernel<true, false>), g, b, 0, stream, x, order, m, k, nsteps, total, out);
+  else
+    hipLaunchKernelGGL((x_frag_kernel<false, false>), g, b, 0, stream, x, order, m, k, nsteps, total, out);
+  return hip_status(hipGetLastError());
+}
 
 SkinnyLds skinny_lds_layout(int64_t m, int64_t k, int64_t group, int waves, int tiles, int cnt) {
   SkinnyLds l;
@@ -437,7 +515,7 @@ int32_t launch_skinny(const LinearArgs& a, const LinearPlan& pl, hipStream_t str
                   a.zero, a.bias, a.y, a.m, a.n, a.k, a.y_bf16,
                   (a.k + kStepK - 1) / kStepK, a.k / a.group, a.prepared, pl.cnt, l.ngw,
                   l.sz_bytes, (int32_t)l.red_off, kNibPairMask, kBf16Offset2, a.row_scale, pl.wm, a.zp4,
-                  a.zp4 ? (a.k / a.group + 1) / 2 : a.k / a.group};
+                  a.zp4 ? (a.k / a.group + 1) / 2 : a.k / a.group, (int32_t)mt_total(a.m)};
   if (a.mx) return a.group == 32 ? dispatch_mt<32, kFmtMX>(sp, pl, l.total, stream) : WOQ_EUNSUPPORTED;
   if (a.sym16) {
     switch (a.group) {

@@ -63,6 +63,7 @@ struct LinearPlan {
   int64_t tail_n = 0;    // GEMM path: trailing output columns left to a second launch of
                          // 64-row tiles, so that the last round of workgroups is not half empty
   int rows_u = 0;        // row-streaming decode path (path 5): rows per workgroup
+  int xfrag = 0;         // small-M path: a pre-pass writes the activations in MFMA fragment order
 };
 
 // Compute units of one MI355X (gfx950): the GEMM path sizes its grid in rounds of this many
@@ -162,6 +163,13 @@ int32_t launch_prep(const uint16_t* x, const int32_t* order, int32_t m, int32_t 
                     int32_t group, int32_t permute, uint16_t* xg, float* xs, int64_t mpad,
                     hipStream_t stream);
 int32_t launch_skinny(const LinearArgs& a, const LinearPlan& p, hipStream_t stream);
+// Small-M pre-pass: x (gathered through `order` when given) in the small-M
+// kernel's fragment order, [ceil(m/16)][ceil(k/128)][4][64 lanes] 16-byte
+// chunks, pair-ordered unless `natural` (MXFP4); rows past m and inputs past k
+// are zero.
+size_t xfrag_bytes(int64_t m, int64_t k);
+int32_t launch_xfrag(const uint16_t* x, const int32_t* order, int32_t m, int32_t k, int32_t group,
+                     int32_t natural, uint16_t* out, hipStream_t stream);
 // Decode path (m <= 4): LDS layout of one workgroup of `waves` waves with
 // `cnt` steps each.
 struct GemvLayout {
