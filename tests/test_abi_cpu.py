@@ -53,7 +53,8 @@ def test_status_strings(lib):
     (5, 4096, 4096, 128, "skinny_mfma"), (16, 14336, 4096, 32, "skinny_mfma"),
     (17, 4096, 4096, 128, "skinny_mfma"), (32, 14336, 4096, 256, "skinny_mfma"),
     (33, 4096, 4096, 128, "skinny_mfma"), (64, 14336, 4096, 32, "skinny_mfma"),
-    (65, 4096, 4096, 128, "gemm_mfma"), (128, 14336, 4096, 32, "gemm_mfma"), (2048, 14336, 4096, 128, "gemm_mfma"),
+    (65, 4096, 4096, 128, "gemm_mfma"), (128, 14336, 4096, 32, "skinny_mfma"),
+    (128, 4096, 14336, 128, "gemm_mfma"), (129, 14336, 4096, 128, "gemm_mfma"), (2048, 14336, 4096, 128, "gemm_mfma"),
     (0, 64, 256, 32, "none"), (3, 64, 0, 32, "bias_fill"),
 ])
 def test_plan_paths(m, n, k, g, path):

@@ -37,7 +37,7 @@ PATHS = {
     "rows": [(1, 300, 2048, 128, {}), (3, 100, 1536, 64, {})],
     "gemv": [(1, 300, 2048, 128, {"WOQ_DECODE_MFMA": "1"}), (4, 100, 1024, 32, {"WOQ_DECODE_MFMA": "1"})],
     "skinny": [(16, 200, 2048, 128, {}), (7, 64, 1024, 32, {}), (64, 300, 1024, 128, {}),
-               (100, 300, 1024, 128, {"WOQ_SKINNY": "2,2"})],
+               (100, 300, 1024, 128, {"WOQ_SKINNY": "2,4"})],
     "gemm": [(100, 300, 1024, 128, {}), (160, 256, 512, 256, {})],
 }
 CASES = [(path, *c) for path, cs in PATHS.items() for c in cs]
