@@ -152,7 +152,8 @@ size_t woq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group
  *   when that is 0.  The workspace holds only scratch; it need not be cleared.
  * m == 0 or n == 0 is a no-op; k == 0 gives y = bias (or 0).
  * Errors: WOQ_EINVAL, WOQ_EGROUP, WOQ_EUNSUPPORTED (group outside the list,
- *   m, n or k >= 2^31, or k >= 2^24 on the tiled GEMM path, m > 32), WOQ_EALIGN,
+ *   m, n or k >= 2^31, or k >= 2^24 on the tiled GEMM path: m > 128, or
+ *   m > 64 on layers of fewer than 800 16-row tiles), WOQ_EALIGN,
  *   WOQ_EWORKSPACE, WOQ_EHIP.
  */
 int32_t woq_linear_int4_groups(const void* x_bf16, int64_t m, const uint8_t* packed,
@@ -582,8 +583,11 @@ int32_t woq_awq_search(const float* w, const void* x_bf16, int64_t t, int64_t n,
 
 /*
  * Describe the kernel plan the linear calls use for these sizes: the path
- * (decode GEMV for m <= 4, small-M MFMA for m <= 32, tiled MFMA GEMM above),
- * tiles, waves and whether an input pre-pass runs.  Writes a NUL-terminated
+ * (row-streaming decode "rows_dot2" for m <= 4 over canonical weights, tile
+ * GEMV "gemv_mfma" for prepared weights at m <= 4; small-M MFMA
+ * "skinny_mfma" up to 64 rows, and up to 128 on layers of at least 800
+ * 16-row tiles; tiled MFMA GEMM "gemm_mfma" above), tiles, waves and which
+ * input pre-pass runs.  Writes a NUL-terminated
  * string of at most len bytes into buf (host).  Pure host function.
  * Errors: WOQ_EINVAL (buf NULL, len 0), plus the shape errors of the linear call.
  */
