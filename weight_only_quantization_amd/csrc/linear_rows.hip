@@ -213,19 +213,20 @@ __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) xr[mm][i] = bload16(rx, ((uint32_t)(xm * K + kin) * 2u + 16u * i) | dead);
   }
-  float s[U];
-  uint32_t zr[U];   // zero-point bytes as loaded (converted after the weight loads are out)
+  uint32_t sr[U];   // float32 scale bits as loaded (unsigned codes; Int4Linear's row scale)
+  uint32_t zr[U];   // zero-point byte as loaded; float16 scale bits for signed codes
+  // Both are converted after the weight loads are out: a conversion, or a
+  // select between two loads, here would make the wave wait for these loads
+  // before it issues the weight loads.  Signed codes issue both scale loads,
+  // the one their layout does not use at an offset no descriptor covers.
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t e = (uint32_t)(u * ng + g);
     if constexpr (S16) {
-      if (row_scale)
-        s[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(((uint32_t)u * 4u) | dead), 0, 0));
-      else
-        s[u] = (float)__builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)((e * 2u) | dead), 0, 0));
-      zr[u] = 0u;
+      sr[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(row_scale ? ((uint32_t)u * 4u) | dead : kOffsetOOB), 0, 0);
+      zr[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)(row_scale ? kOffsetOOB : (e * 2u) | dead), 0, 0);
     } else {
-      s[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)((e * 4u) | dead), 0, 0));
+      sr[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (int)((e * 4u) | dead), 0, 0);
       const uint32_t ze = zp4 ? (uint32_t)(u * zrow + (g >> 1)) : e;
       zr[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rz, (int)(ze | dead), 0, 0);
     }
@@ -260,6 +261,8 @@ __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
   for (int u = 0; u < U; ++u) {
     // -(128 + zero): the codes enter the dot product as 128 + q
     const float nz = S16 ? -136.f : -128.f - (float)__builtin_amdgcn_ubfe(zr[u], zsh, zbits);
+    const float su = S16 && !row_scale ? (float)__builtin_bit_cast(_Float16, (uint16_t)zr[u])
+                                       : __builtin_bit_cast(float, sr[u]);
 #pragma unroll
     for (int mm = 0; mm < MR; ++mm) {
       float r0 = 0.f, r1 = 0.f;
@@ -271,7 +274,7 @@ __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
         r0 = dot2(((wd >> 8) & mask) | off, xp[mm][4 * d + 2], r0);
         r1 = dot2(((wd >> 12) & mask) | off, xp[mm][4 * d + 3], r1);
       }
-      v[mm][u] = s[u] * fmaf(nz, X[mm], r0 + r1);
+      v[mm][u] = su * fmaf(nz, X[mm], r0 + r1);
     }
   }
 
