@@ -63,12 +63,17 @@ def test_plan_paths(m, n, k, g, path):
 
 def test_plan_decode_kernels(monkeypatch):
     # canonical rows at m <= 4 stream through the row kernel: rows per workgroup by shape
-    for (m, n, k), u in (((1, 14336, 4096), 4), ((1, 4096, 14336), 16), ((1, 4096, 4096), 4),
-                         ((1, 1024, 4096), 4), ((3, 14336, 4096), 4), ((2, 28672, 4096), 4)):
-        plan = woq.linear_plan(m, n, k, 128)
+    for (m, n, k, g), u in (((1, 14336, 4096, 128), 4), ((1, 4096, 14336, 128), 16), ((1, 4096, 4096, 128), 4),
+                            ((1, 1024, 4096, 128), 4), ((3, 4096, 4096, 128), 4), ((2, 28672, 4096, 128), 4),
+                            ((4, 14336, 4096, 64), 4)):
+        plan = woq.linear_plan(m, n, k, g)
         assert f"path=rows_dot2 rows_per_group={u} waves={(k + 2047) // 2048} " in plan, plan
+    # 3 and 4 rows of layers with >= 2^25 weights and groups >= 128 take the small-M MFMA kernel
+    for m, n, k, g in ((3, 14336, 4096, 128), (4, 4096, 14336, 256), (4, 8192, 4096, 128)):
+        assert "path=skinny_mfma" in woq.linear_plan(m, n, k, g)
     monkeypatch.setenv("WOQ_DECODE_MFMA", "1")
     assert "path=gemv_mfma" in woq.linear_plan(1, 4096, 4096, 128)
+    assert "path=gemv_mfma" in woq.linear_plan(4, 14336, 4096, 128)
 
 
 @pytest.mark.parametrize("m,n,tail", [

@@ -159,7 +159,13 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
   p.gb = group >= 128 ? 4 : group / 32;
   // Canonical rows at m <= 4 stream through the row kernel; WOQ_DECODE_MFMA
   // keeps them on the tile GEMV (a tuning and test aid, read on every call).
-  if (rows_ok && rows_supported(m, k) && std::getenv("WOQ_DECODE_MFMA") == nullptr) {
+  // At 3 and 4 rows the row kernel is bound by its dot arithmetic (one v_dot2
+  // per weight pair and row); on layers of at least 2^25 weights with groups
+  // of 128 and more the small-M MFMA kernel is faster there (14336x4096 at
+  // m = 4: 12.8 against 15.1 us; 4096x14336: 13.7 against 16.2 us).
+  const bool decode_mfma = std::getenv("WOQ_DECODE_MFMA") != nullptr;
+  const bool mfma_rows = rows_ok && !decode_mfma && m >= 3 && group >= 128 && n * k >= ((int64_t)1 << 25);
+  if (rows_ok && rows_supported(m, k) && !mfma_rows && !decode_mfma) {
     p.path = 5;
     p.rows_u = rows_per_group(m, n, k);
     p.waves = rows_waves(k);
@@ -168,7 +174,7 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
     return p;
   }
   const bool force_skinny = std::getenv("WOQ_FORCE_SKINNY") != nullptr;   // tuning aid, read on every call
-  if (m <= 4 && !force_skinny && k < ((int64_t)1 << 26) && gemv_plan(m, n, k, group, &p)) {
+  if (m <= 4 && !force_skinny && !mfma_rows && k < ((int64_t)1 << 26) && gemv_plan(m, n, k, group, &p)) {
     p.prep = has_order ? 1 : 0;
     return p;
   }
