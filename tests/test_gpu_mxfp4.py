@@ -132,3 +132,31 @@ def test_full_size_sampled(woq, m, n, k):
     rng = np.random.default_rng(n + 1)
     rows = np.unique(np.concatenate([[0, n - 1, n // 2], rng.choice(n, 48, replace=False)]))
     check_linear(y[:, torch.from_numpy(rows).cuda()], _ref(host, rows), f"mxfp4 full m={m}")
+
+
+# m <= 4: the row-streaming kernel (one E8M0 block per lane, converted with
+# its scale) and the tile GEMV (WOQ_DECODE_MFMA; at k = 32768 with 32-input
+# blocks it hands over to the small-M kernel) on the same calls.
+DECODE = [(1, 300, 2048, True), (1, 37, 64, False), (2, 64, 4096, True), (3, 100, 6144, False),
+          (4, 70, 1024, True), (1, 129, 32768, False)]
+
+
+@pytest.mark.parametrize("kernel", ["rows", "gemv"])
+@pytest.mark.parametrize("m,n,k,with_bias", DECODE)
+def test_decode_paths(woq, monkeypatch, kernel, m, n, k, with_bias):
+    if kernel == "gemv":
+        monkeypatch.setenv("WOQ_DECODE_MFMA", "1")
+    else:
+        monkeypatch.delenv("WOQ_DECODE_MFMA", raising=False)
+    plan = woq.linear_plan(m, n, k, 32)
+    _say(f"mxfp4 decode {kernel} m={m} n={n} k={k} plan: {plan}")
+    if kernel == "rows":
+        assert "path=rows_dot2" in plan, plan
+    else:   # the tile GEMV, or the small-M kernel for rows its LDS budget cannot take
+        assert "path=gemv_mfma" in plan or (k >= 32768 and "path=skinny_mfma" in plan), plan
+    dev, host = _make(woq, m, n, k, seed=7 * m + n + k, with_bias=with_bias)
+    ref = _ref(host)
+    for dt in (torch.float32, torch.bfloat16):
+        y = woq.linear_mxfp4(dev["x"], dev["blocks"], dev["scales"], bias=dev["bias"], out_dtype=dt)
+        torch.cuda.synchronize()
+        check_linear(y, ref, f"mxfp4 decode {kernel} m={m} n={n} k={k}")

@@ -578,7 +578,7 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
     return WOQ_EALIGN;
   const bool has_order = order != nullptr;
   if (has_order && !aligned(order, 16)) return WOQ_EALIGN;
-  const LinearPlan plan = linear_plan(m, n, k, group, has_order, !prepared && !mx);
+  const LinearPlan plan = linear_plan(m, n, k, group, has_order, !prepared);
   const LinearWorkspace ws = linear_workspace_layout(m, n, k, group, has_order);
   // The tile GEMV reads one zero point a byte: packed ones are unpacked into the
   // head of the workspace first; every other path reads them as they are.

@@ -163,10 +163,14 @@ __device__ __forceinline__ float reduce_rows(float* v, int lane) {
 }
 
 // U: rows per workgroup (4, 8, 16); MR: activation rows computed (1, 2 or 4;
-// rows past m repeat the last one and are not stored); S16: signed codes;
-// GRP: several matrices in one launch.
-template <int U, int MR, bool S16, bool GRP>
+// rows past m repeat the last one and are not stored); FMT: unsigned codes,
+// signed codes (kFmtS16) or MXFP4 (kFmtMX: a lane's 32 inputs are one block,
+// whose E2M1 codes v_cvt_scalef32_pk_bf16_fp4 turns into bf16 already
+// multiplied by the block's power-of-two scale, exactly, in natural input
+// order: no fold and no activation sum); GRP: several matrices in one launch.
+template <int U, int MR, int FMT, bool GRP>
 __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
+  constexpr bool S16 = FMT == kFmtS16, MX = FMT == kFmtMX;
   constexpr int kShift = U == 16 ? 2 : (U == 8 ? 3 : 4);   // lane l holds row l >> kShift after the reduction
   __shared__ float red[kMaxWaves * 4 * 16];
   const int lane = threadIdx.x & 63;
@@ -193,13 +197,13 @@ __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
 
   const __amdgpu_buffer_rsrc_t rw = rsrc(pr.packed + (int64_t)row0 * row_bytes, (uint32_t)rows * row_bytes);
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.x, (uint32_t)(M * K) * 2u);
-  const uint32_t sbytes = S16 && !row_scale ? 2u : 4u;
+  const uint32_t sbytes = MX ? 1u : (S16 && !row_scale ? 2u : 4u);
   const int srow = row_scale ? 1 : ng;
   const __amdgpu_buffer_rsrc_t rs =
       rsrc(static_cast<const char*>(pr.scale) + (int64_t)row0 * srow * sbytes, (uint32_t)(rows * srow) * sbytes);
   const int zrow = p.zrow;
   const __amdgpu_buffer_rsrc_t rz =
-      rsrc(S16 ? nullptr : pr.zero + (int64_t)row0 * zrow, S16 ? 0u : (uint32_t)(rows * zrow));
+      rsrc(S16 || MX ? nullptr : pr.zero + (int64_t)row0 * zrow, S16 || MX ? 0u : (uint32_t)(rows * zrow));
   const bool zp4 = p.zp4 != 0;   // uniform
   const uint32_t zsh = zp4 ? 4u * (uint32_t)(g & 1) : 0u;   // the lane's zero point: bits [zsh, zsh + zbits)
   const uint32_t zbits = zp4 ? 4u : 8u;
@@ -222,7 +226,10 @@ __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t e = (uint32_t)(u * ng + g);
-    if constexpr (S16) {
+    if constexpr (MX) {
+      sr[u] = 0u;
+      zr[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)(e | dead), 0, 0);   // E8M0 scale byte
+    } else if constexpr (S16) {
       sr[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(row_scale ? ((uint32_t)u * 4u) | dead : kOffsetOOB), 0, 0);
       zr[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)(row_scale ? kOffsetOOB : (e * 2u) | dead), 0, 0);
     } else {
@@ -240,17 +247,27 @@ __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
   // registers, and the stream starts late.
   __builtin_amdgcn_sched_barrier(0);
 
-  // 2. The lane's activations in the unpacker's pair order, and their sum.
+  // 2. The lane's activations in the unpacker's pair order, and their sum
+  //    (MXFP4: in natural order, no sum).
   uint32_t xp[MR][16];
   float X[MR];
 #pragma unroll
   for (int mm = 0; mm < MR; ++mm) {
+    if constexpr (MX) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pair_order(xr[mm][i], xp[mm] + 4 * i);
-    float t = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const u32x4_t r = xr[mm][i];
+        xp[mm][4 * i + 0] = r[0]; xp[mm][4 * i + 1] = r[1]; xp[mm][4 * i + 2] = r[2]; xp[mm][4 * i + 3] = r[3];
+      }
+      X[mm] = 0.f;
+    } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) t = dot2(xp[mm][i], kOnes2, t);
-    X[mm] = t;
+      for (int i = 0; i < 4; ++i) pair_order(xr[mm][i], xp[mm] + 4 * i);
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) t = dot2(xp[mm][i], kOnes2, t);
+      X[mm] = t;
+    }
   }
 
   // 3. Per row: codes as bf16 (128 + q), dot with the activations, fold.
@@ -259,6 +276,25 @@ __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
   float v[MR][U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
+    if constexpr (MX) {
+      // 2^(e - 127) of the block's E8M0 byte e (e = 0: 2^-127, a float32 subnormal)
+      const uint32_t eb = zr[u] & 0xFFu;
+      const float bs = __builtin_bit_cast(float, eb == 0 ? 0x00400000u : eb << 23);
+#pragma unroll
+      for (int mm = 0; mm < MR; ++mm) {
+        float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t wd = w[u][d];
+          r0 = dot2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, bs, 0)), xp[mm][4 * d + 0], r0);
+          r1 = dot2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, bs, 1)), xp[mm][4 * d + 1], r1);
+          r0 = dot2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, bs, 2)), xp[mm][4 * d + 2], r0);
+          r1 = dot2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, bs, 3)), xp[mm][4 * d + 3], r1);
+        }
+        v[mm][u] = r0 + r1;
+      }
+      continue;
+    }
     // -(128 + zero): the codes enter the dot product as 128 + q
     const float nz = S16 ? -136.f : -128.f - (float)__builtin_amdgcn_ubfe(zr[u], zsh, zbits);
     const float su = S16 && !row_scale ? (float)__builtin_bit_cast(_Float16, (uint16_t)zr[u])
@@ -316,14 +352,16 @@ __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
 }
 
 template <int U, int MR>
-int32_t launch_u(const RowsParams& rp, int64_t grid, int waves, bool s16, hipStream_t stream) {
+int32_t launch_u(const RowsParams& rp, int64_t grid, int waves, int fmt, hipStream_t stream) {
   const dim3 g((unsigned)grid), b(64 * waves);
   if (rp.nprob > 1)   // grouped launches carry unsigned codes only
-    hipLaunchKernelGGL((rows_kernel<U, MR, false, true>), g, b, 0, stream, rp);
-  else if (s16)
-    hipLaunchKernelGGL((rows_kernel<U, MR, true, false>), g, b, 0, stream, rp);
+    hipLaunchKernelGGL((rows_kernel<U, MR, kFmtU4, true>), g, b, 0, stream, rp);
+  else if (fmt == kFmtS16)
+    hipLaunchKernelGGL((rows_kernel<U, MR, kFmtS16, false>), g, b, 0, stream, rp);
+  else if (fmt == kFmtMX)
+    hipLaunchKernelGGL((rows_kernel<U, MR, kFmtMX, false>), g, b, 0, stream, rp);
   else
-    hipLaunchKernelGGL((rows_kernel<U, MR, false, false>), g, b, 0, stream, rp);
+    hipLaunchKernelGGL((rows_kernel<U, MR, kFmtU4, false>), g, b, 0, stream, rp);
   return hip_status(hipGetLastError());
 }
 
@@ -331,16 +369,16 @@ int32_t launch_u(const RowsParams& rp, int64_t grid, int waves, bool s16, hipStr
 // ones would not fit in the 128 registers a 1024-thread workgroup leaves each
 // lane.
 template <int MR>
-int32_t launch_mr(const RowsParams& rp, int u, int64_t grid, int waves, bool s16, hipStream_t stream) {
+int32_t launch_mr(const RowsParams& rp, int u, int64_t grid, int waves, int fmt, hipStream_t stream) {
   if constexpr (MR > 2) {
-    return launch_u<4, MR>(rp, grid, waves, s16, stream);
+    return launch_u<4, MR>(rp, grid, waves, fmt, stream);
   } else if constexpr (MR == 2) {
-    return u == 4 ? launch_u<4, MR>(rp, grid, waves, s16, stream) : launch_u<8, MR>(rp, grid, waves, s16, stream);
+    return u == 4 ? launch_u<4, MR>(rp, grid, waves, fmt, stream) : launch_u<8, MR>(rp, grid, waves, fmt, stream);
   } else {
     switch (u) {
-      case 4: return launch_u<4, MR>(rp, grid, waves, s16, stream);
-      case 8: return launch_u<8, MR>(rp, grid, waves, s16, stream);
-      case 16: return launch_u<16, MR>(rp, grid, waves, s16, stream);
+      case 4: return launch_u<4, MR>(rp, grid, waves, fmt, stream);
+      case 8: return launch_u<8, MR>(rp, grid, waves, fmt, stream);
+      case 16: return launch_u<16, MR>(rp, grid, waves, fmt, stream);
       default: return WOQ_EUNSUPPORTED;
     }
   }
@@ -371,7 +409,7 @@ int rows_waves(int64_t k) { return (int)((k + kChunk - 1) / kChunk); }
 
 int32_t launch_rows(const LinearArgs* args, int count, int u, hipStream_t stream) {
   const LinearArgs& a = args[0];
-  if (!rows_supported(a.m, a.k) || a.prepared || a.mx) return WOQ_EUNSUPPORTED;
+  if (!rows_supported(a.m, a.k) || a.prepared || (a.mx && (count != 1 || a.group != 32))) return WOQ_EUNSUPPORTED;
   int32_t gshift = 0;
   while ((1 << gshift) < a.group) ++gshift;
   RowsParams rp{};
@@ -391,18 +429,19 @@ int32_t launch_rows(const LinearArgs* args, int count, int u, hipStream_t stream
   for (int i = 0; i < count; ++i) {
     const LinearArgs& ai = args[i];
     rp.prob[i] = RowsProblem{ai.packed,
-                             ai.sym16 && !ai.row_scale ? static_cast<const void*>(ai.scale16)
-                                                       : static_cast<const void*>(ai.scale),
+                             ai.mx ? static_cast<const void*>(ai.scale8)
+                                   : ai.sym16 && !ai.row_scale ? static_cast<const void*>(ai.scale16)
+                                                               : static_cast<const void*>(ai.scale),
                              ai.zero, ai.bias, ai.y, ai.n, (int32_t)tb};
     tb += (ai.n + u - 1) / u;
   }
   if (tb == 0) return WOQ_OK;
   const int waves = rows_waves(a.k);
-  const bool s16 = a.sym16 != 0;
+  const int fmt = a.mx ? kFmtMX : a.sym16 ? kFmtS16 : kFmtU4;
   switch (a.m) {
-    case 1: return launch_mr<1>(rp, u, tb, waves, s16, stream);
-    case 2: return launch_mr<2>(rp, u, tb, waves, s16, stream);
-    default: return launch_mr<4>(rp, u, tb, waves, s16, stream);
+    case 1: return launch_mr<1>(rp, u, tb, waves, fmt, stream);
+    case 2: return launch_mr<2>(rp, u, tb, waves, fmt, stream);
+    default: return launch_mr<4>(rp, u, tb, waves, fmt, stream);
   }
 }
 

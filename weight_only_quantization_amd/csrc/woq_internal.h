@@ -72,8 +72,8 @@ constexpr int64_t kComputeUnits = 256;
 
 LinearWorkspace linear_workspace_layout(int64_t m, int64_t n, int64_t k, int32_t group,
                                         bool has_order);
-// rows_ok: the weights are canonical packed rows of unsigned or signed codes
-// (not prepared, not MXFP4), which the row-streaming decode path can read.
+// rows_ok: the weights are canonical packed rows (unsigned or signed codes, or
+// MXFP4 blocks; not prepared), which the row-streaming decode path can read.
 LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_order, bool rows_ok = true);
 
 // ---------------------------------------------------------------------------
