@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 
 #include "woq_internal.h"
@@ -19,6 +20,41 @@ constexpr int64_t kMaxDim = (int64_t)1 << 31;
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Error flags of the synchronous codec calls (non-finite weights, codes above
+// 15): a file-scope device array, one slot per call taken round robin, so
+// those calls allocate nothing.  Its address on a device is taken once, with
+// that device current.  More than kFlagSlots codec calls in flight at once
+// (from as many host threads) would share a slot.
+constexpr int kFlagSlots = 256;
+constexpr int kFlagDevices = 64;
+__device__ __align__(256) uint32_t flag_pool[kFlagSlots];
+void* flag_addr[kFlagDevices] = {};
+std::mutex flag_mutex;
+std::atomic<uint32_t> flag_next{0};
+
+// Clear a slot, run launch(slot) on stream s, read the slot back (synchronizes).
+template <class F>
+int32_t with_flag(hipStream_t s, uint32_t* hflag, F launch) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kFlagDevices) return WOQ_EHIP;
+  void* base = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(flag_mutex);
+    if (!flag_addr[dev]) {
+      void* ptr = nullptr;
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(flag_pool)) != hipSuccess || !ptr) return WOQ_EHIP;
+      flag_addr[dev] = ptr;
+    }
+    base = flag_addr[dev];
+  }
+  uint32_t* flag = static_cast<uint32_t*>(base) + flag_next.fetch_add(1, std::memory_order_relaxed) % kFlagSlots;
+  int32_t st = hip_status(hipMemsetAsync(flag, 0, sizeof(uint32_t), s));
+  if (st == WOQ_OK) st = launch(flag);
+  if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+  if (st == WOQ_OK) st = hip_status(hipStreamSynchronize(s));
+  return st;
+}
 
 bool linear_group_ok(int32_t g) { return g == 32 || g == 64 || g == 128 || g == 256; }
 
@@ -280,14 +316,10 @@ int32_t woq_quantize_groups(const float* w, int64_t n, int64_t k, int32_t group,
   if (!w || !q || !scale || !zero) return WOQ_EINVAL;
   if (!aligned(w, 4) || !aligned(scale, 4)) return WOQ_EALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  uint32_t* flag = nullptr;
-  WOQ_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&flag), sizeof(uint32_t), s));
-  int32_t st = hip_status(hipMemsetAsync(flag, 0, sizeof(uint32_t), s));
-  if (st == WOQ_OK) st = launch_quantize(w, n, k, group, symmetric, q, scale, zero, flag, s);
   uint32_t hflag = 0;
-  if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(&hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
-  if (st == WOQ_OK) st = hip_status(hipStreamSynchronize(s));
-  (void)hipFreeAsync(flag, s);
+  const int32_t st = with_flag(s, &hflag, [&](uint32_t* flag) {
+    return launch_quantize(w, n, k, group, symmetric, q, scale, zero, flag, s);
+  });
   if (st != WOQ_OK) return st;
   return hflag ? WOQ_ENONFINITE : WOQ_OK;
 }
@@ -299,14 +331,10 @@ int32_t woq_pack_uint4(const uint8_t* q, int64_t count, uint8_t* packed, void* s
   if (count == 0) return WOQ_OK;
   if (!q || !packed) return WOQ_EINVAL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  uint32_t* flag = nullptr;
-  WOQ_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&flag), sizeof(uint32_t), s));
-  int32_t st = hip_status(hipMemsetAsync(flag, 0, sizeof(uint32_t), s));
-  if (st == WOQ_OK) st = launch_pack(q, count, packed, flag, s);
   uint32_t hflag = 0;
-  if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(&hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
-  if (st == WOQ_OK) st = hip_status(hipStreamSynchronize(s));
-  (void)hipFreeAsync(flag, s);
+  const int32_t st = with_flag(s, &hflag, [&](uint32_t* flag) {
+    return launch_pack(q, count, packed, flag, s);
+  });
   if (st != WOQ_OK) return st;
   return hflag ? WOQ_ERANGE : WOQ_OK;
 }
@@ -343,14 +371,10 @@ int32_t woq_quantize_int4_sym_f16(const float* w, int64_t n, int64_t k, int32_t 
   if (!w || !codes || !scale16) return WOQ_EINVAL;
   if (!aligned(w, 4) || !aligned(scale16, 2)) return WOQ_EALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  uint32_t* flag = nullptr;
-  WOQ_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&flag), sizeof(uint32_t), s));
-  int32_t st = hip_status(hipMemsetAsync(flag, 0, sizeof(uint32_t), s));
-  if (st == WOQ_OK) st = launch_quantize_s16(w, n, k, group, codes, scale16, flag, s);
   uint32_t hflag = 0;
-  if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(&hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
-  if (st == WOQ_OK) st = hip_status(hipStreamSynchronize(s));
-  (void)hipFreeAsync(flag, s);
+  const int32_t st = with_flag(s, &hflag, [&](uint32_t* flag) {
+    return launch_quantize_s16(w, n, k, group, codes, scale16, flag, s);
+  });
   if (st != WOQ_OK) return st;
   if (hflag & 1u) return WOQ_ENONFINITE;
   return hflag ? WOQ_ERANGE : WOQ_OK;
@@ -363,14 +387,10 @@ int32_t woq_pack_int4(const int8_t* codes, int64_t count, uint8_t* packed, void*
   if (count == 0) return WOQ_OK;
   if (!codes || !packed) return WOQ_EINVAL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  uint32_t* flag = nullptr;
-  WOQ_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&flag), sizeof(uint32_t), s));
-  int32_t st = hip_status(hipMemsetAsync(flag, 0, sizeof(uint32_t), s));
-  if (st == WOQ_OK) st = launch_pack_s4(codes, count, packed, flag, s);
   uint32_t hflag = 0;
-  if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(&hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
-  if (st == WOQ_OK) st = hip_status(hipStreamSynchronize(s));
-  (void)hipFreeAsync(flag, s);
+  const int32_t st = with_flag(s, &hflag, [&](uint32_t* flag) {
+    return launch_pack_s4(codes, count, packed, flag, s);
+  });
   if (st != WOQ_OK) return st;
   return hflag ? WOQ_ERANGE : WOQ_OK;
 }
@@ -407,14 +427,10 @@ int32_t woq_quantize_mxfp4(const float* w, int64_t n, int64_t k, uint8_t* codes,
   if (!w || !codes || !scales) return WOQ_EINVAL;
   if (!aligned(w, 4)) return WOQ_EALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  uint32_t* flag = nullptr;
-  WOQ_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&flag), sizeof(uint32_t), s));
-  int32_t st = hip_status(hipMemsetAsync(flag, 0, sizeof(uint32_t), s));
-  if (st == WOQ_OK) st = launch_quantize_mx(w, n, k, codes, scales, flag, s);
   uint32_t hflag = 0;
-  if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(&hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
-  if (st == WOQ_OK) st = hip_status(hipStreamSynchronize(s));
-  (void)hipFreeAsync(flag, s);
+  const int32_t st = with_flag(s, &hflag, [&](uint32_t* flag) {
+    return launch_quantize_mx(w, n, k, codes, scales, flag, s);
+  });
   if (st != WOQ_OK) return st;
   return hflag ? WOQ_ENONFINITE : WOQ_OK;
 }
@@ -440,14 +456,10 @@ int32_t woq_quantize_int4_rows(const float* w, int64_t n, int64_t k, int8_t* cod
   if (!w || !codes || !scale) return WOQ_EINVAL;
   if (!aligned(w, 4) || !aligned(scale, 4)) return WOQ_EALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  uint32_t* flag = nullptr;
-  WOQ_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&flag), sizeof(uint32_t), s));
-  int32_t st = hip_status(hipMemsetAsync(flag, 0, sizeof(uint32_t), s));
-  if (st == WOQ_OK) st = launch_quantize_rows(w, n, k, codes, scale, flag, s);
   uint32_t hflag = 0;
-  if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(&hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
-  if (st == WOQ_OK) st = hip_status(hipStreamSynchronize(s));
-  (void)hipFreeAsync(flag, s);
+  const int32_t st = with_flag(s, &hflag, [&](uint32_t* flag) {
+    return launch_quantize_rows(w, n, k, codes, scale, flag, s);
+  });
   if (st != WOQ_OK) return st;
   return hflag ? WOQ_ENONFINITE : WOQ_OK;
 }
@@ -517,14 +529,10 @@ int32_t woq_pack_zero_points(const uint8_t* zero, int64_t n, int64_t ngroups, ui
   if (n == 0 || ngroups == 0) return WOQ_OK;
   if (!zero || !packed) return WOQ_EINVAL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  uint32_t* flag = nullptr;
-  WOQ_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&flag), sizeof(uint32_t), s));
-  int32_t st = hip_status(hipMemsetAsync(flag, 0, sizeof(uint32_t), s));
-  if (st == WOQ_OK) st = launch_pack_zero_points(zero, n, ngroups, packed, flag, s);
   uint32_t hflag = 0;
-  if (st == WOQ_OK) st = hip_status(hipMemcpyAsync(&hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
-  if (st == WOQ_OK) st = hip_status(hipStreamSynchronize(s));
-  (void)hipFreeAsync(flag, s);
+  const int32_t st = with_flag(s, &hflag, [&](uint32_t* flag) {
+    return launch_pack_zero_points(zero, n, ngroups, packed, flag, s);
+  });
   if (st != WOQ_OK) return st;
   return hflag ? WOQ_ERANGE : WOQ_OK;
 }
