@@ -416,9 +416,9 @@ def cpu_baseline():
                 per_config=per, single_thread_decode=single)
 
 
-DOMINANT_TAG = "rows_kernel<4, 1, 0, false>"   # 14336x4096 at M=1 (gate, up projections)
+DOMINANT_TAG = "rows_kernel<4, 1, 0, false, 128>"    # 14336x4096 at M=1 (gate, up projections)
 DOMINANT_GRID = 3584 * 128                           # 3584 workgroups of 2 waves
-DOWN_TAG = "rows_kernel<16, 1, 0, false>"        # 4096x14336 at M=1 (down projection)
+DOWN_TAG = "rows_kernel<16, 1, 0, false, 128>"      # 4096x14336 at M=1 (down projection)
 DOWN_GRID = 256 * 7 * 64                             # 256 workgroups of 7 waves
 COPY_TAG = "copyBuffer"                              # the runtime's device-to-device copy kernel
 

@@ -160,6 +160,14 @@ ROWS_VARIANTS = [
     (4, 19, 32768, 128, True, False, 4, 16),   # the longest rows this path takes
     (1, 1000, 30720, 256, False, False, 16, 15),
     (2, 5, 256, 128, True, False, 8, 1),       # fewer rows than one workgroup
+    # groups of 64-256: a wave loads each (scale, zero) pair once for its lanes
+    (1, 45, 4160, 64, True, False, 16, 3),     # 65 groups a row, the last chunk holds one
+    (1, 37, 2304, 256, False, True, 4, 2),     # 9 groups a row: more rows per load than rows
+    (2, 19, 4352, 256, True, False, 8, 3),
+    (1, 37, 2432, 128, True, True, 8, 2),      # second chunk holds 3 groups
+    (2, 41, 2432, 128, False, False, 8, 2),
+    (1, 45, 8576, 128, False, True, 16, 5),    # 67 groups a row, 45 rows: a partial workgroup
+    (1, 7, 128, 128, True, False, 4, 1),       # one group
 ]
 
 

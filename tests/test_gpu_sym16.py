@@ -172,12 +172,13 @@ def test_linear_prepared_is_bit_identical(woq, monkeypatch, m, n, k, group):
     check_linear(yp, _ref(host, group), f"sym16 prepared m={m}")
 
 
-def test_signed_equals_unsigned_with_zero_point_eight(woq):
+@pytest.mark.parametrize("g", [32, 128, 256])
+def test_signed_equals_unsigned_with_zero_point_eight(woq, g):
     """A signed code c is the unsigned code c + 8 with zero point 8: the two
     entry points must agree bit for bit on the same weights, on every path."""
-    _say("sym16 vs unsigned zero 8")
-    rng = np.random.default_rng(9)
-    n, k, g = 96, 1024, 32
+    _say(f"sym16 vs unsigned zero 8 g={g}")
+    rng = np.random.default_rng(9 + g)
+    n, k = 96, 1024
     c = torch.from_numpy(rng.integers(-8, 8, size=(n, k)).astype(np.int8)).cuda()
     s16 = torch.from_numpy(rng.uniform(0.001, 0.01, size=(n, k // g)).astype(np.float16)).cuda()
     packed_s = woq.pack_int4(c)
@@ -189,6 +190,26 @@ def test_signed_equals_unsigned_with_zero_point_eight(woq):
         yu = woq.linear_int4_groups(x, packed_u, s16.float(), zero, group=g, out_dtype=torch.float32)
         torch.cuda.synchronize()
         assert torch.equal(ys, yu), m
+
+
+# Row-streaming widths (WOQ_ROWS_U) at groups of 64-256, where a wave loads
+# each row's float16 scales once and passes them between lanes.
+ROWS_SHARED = [(1, 37, 2432, 128, 16), (1, 45, 4160, 64, 16), (2, 23, 2304, 256, 8), (1, 40, 8576, 128, 8),
+               (3, 9, 640, 128, 4)]
+
+
+@pytest.mark.parametrize("m,n,k,group,u", ROWS_SHARED)
+def test_rows_widths(woq, monkeypatch, m, n, k, group, u):
+    monkeypatch.delenv("WOQ_DECODE_MFMA", raising=False)
+    monkeypatch.setenv("WOQ_ROWS_U", str(u))
+    plan = woq.linear_plan(m, n, k, group, False)
+    _say(f"sym16 rows m={m} n={n} k={k} g={group} u={u} plan: {plan}")
+    assert "path=rows_dot2" in plan and f"rows_per_group={u} " in plan
+    dev, host = _make(woq, m, n, k, group, seed=500 + m + n, with_bias=True)
+    y = woq.linear_int4_sym(dev["x"], dev["packed"], dev["scale"], bias=dev["bias"], group=group,
+                            out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_linear(y, _ref(host, group), f"sym16 rows m={m} u={u}")
 
 
 FULL = [(1, 14336, 4096, 32), (1, 4096, 14336, 32), (16, 14336, 4096, 32), (2048, 4096, 4096, 32)]

@@ -93,3 +93,32 @@ def test_linear_zp4(woq, monkeypatch, m, n, k, group, with_bias, with_order, dec
     assert torch.equal(y, y_ref_call)
     check_linear(y, oracle.linear_int4_groups_zp4(x, packed, scale, zp, n, k, group, bias=b, order=o),
                  f"zp4 m={m} n={n} k={k}")
+
+
+# Row-streaming widths at groups of 64-256, where a wave loads each row's zero
+# bytes once and passes them between lanes: rows per workgroup forced with
+# WOQ_ROWS_U, odd group counts and partial workgroups.
+ROWS_SHARED = [(1, 37, 2432, 128, 16), (1, 45, 8576, 128, 8), (2, 41, 2432, 128, 8), (1, 7, 384, 128, 4),
+               (4, 9, 4224, 128, 4), (1, 45, 4160, 64, 16), (2, 23, 2112, 64, 8), (1, 37, 2304, 256, 4),
+               (1, 40, 4352, 256, 16)]
+
+
+@pytest.mark.parametrize("m,n,k,group,u", ROWS_SHARED)
+def test_rows_widths_zp4(woq, monkeypatch, m, n, k, group, u):
+    monkeypatch.delenv("WOQ_DECODE_MFMA", raising=False)
+    monkeypatch.setenv("WOQ_ROWS_U", str(u))
+    plan = woq.linear_plan(m, n, k, group, False)
+    _say(f"zp4 rows m={m} n={n} k={k} g={group} u={u} plan: {plan}")
+    assert "path=rows_dot2" in plan and f"rows_per_group={u} " in plan
+    seed = 9100 + m + n + k
+    packed, scale, zero = workloads.packed_weights(n, k, group, seed=seed)
+    x = workloads.activations_bf16(m, k, seed=seed + 1)
+    zp = oracle.pack_zero_points(zero)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    y = woq.linear_int4_groups_zp4(to_dev_bf16(x), dev(packed), dev(scale), dev(zp), group=group,
+                                   out_dtype=torch.float32)
+    y_bytes = woq.linear_int4_groups(to_dev_bf16(x), dev(packed), dev(scale), dev(zero), group=group,
+                                     out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_bytes)
+    check_linear(y, oracle.linear_int4_groups_zp4(x, packed, scale, zp, n, k, group), f"zp4 rows m={m} u={u}")

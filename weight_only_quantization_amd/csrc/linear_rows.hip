@@ -22,6 +22,8 @@
 //   with bf16 codes (128 + q) (one AND-OR per code pair, exact) and
 //   v_dot2_f32_bf16 against the activations,
 //     part = s * (sum x (128 + q) - (128 + z) * sum x).
+//   With G >= 64 a pair serves G / 32 lanes; the wave loads each pair once
+//   and passes it to those lanes with ds_bpermute.
 // * The U row partials of the 64 lanes are reduced in registers: lane-pair
 //   swaps (v_permlane32_swap, v_permlane16_swap) and DPP moves halve the set
 //   of rows held per lane at each distance, so the whole reduction costs
@@ -168,9 +170,15 @@ __device__ __forceinline__ float reduce_rows(float* v, int lane) {
 // whose E2M1 codes v_cvt_scalef32_pk_bf16_fp4 turns into bf16 already
 // multiplied by the block's power-of-two scale, exactly, in natural input
 // order: no fold and no activation sum); GRP: several matrices in one launch.
-template <int U, int MR, int FMT, bool GRP>
+// SG (64, 128 or 256; 0: off): groups of SG inputs (scales per group), where
+// the SG / 32 lanes of a group would load the same (scale, zero) pairs.  A
+// wave instead loads 64 distinct entries per instruction, SG / 32 rows of its
+// chunk's 2048 / SG groups, and hands them to the lanes that need them with
+// ds_bpermute: U / (SG / 32) loads of each instead of U.
+template <int U, int MR, int FMT, bool GRP, int SG = 0>
 __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
   constexpr bool S16 = FMT == kFmtS16, MX = FMT == kFmtMX;
+  static_assert(SG == 0 || (!MX && (SG == 64 || SG == 128 || SG == 256)), "shared (scale, zero) loads");
   constexpr int kShift = U == 16 ? 2 : (U == 8 ? 3 : 4);   // lane l holds row l >> kShift after the reduction
   __shared__ float red[kMaxWaves * 4 * 16];
   const int lane = threadIdx.x & 63;
@@ -193,7 +201,7 @@ __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
   const int kin = wave * kChunk + 32 * lane;          // first input of this lane
   const uint32_t dead = kin >= K ? kOffsetOOB : 0u;   // lanes past K load zeros
   const int g = kin >> p.group_shift;
-  const bool row_scale = S16 && p.row_scale != 0;    // uniform
+  const bool row_scale = S16 && SG == 0 && p.row_scale != 0;    // uniform
 
   const __amdgpu_buffer_rsrc_t rw = rsrc(pr.packed + (int64_t)row0 * row_bytes, (uint32_t)rows * row_bytes);
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.x, (uint32_t)(M * K) * 2u);
@@ -223,8 +231,31 @@ __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
   // select between two loads, here would make the wave wait for these loads
   // before it issues the weight loads.  Signed codes issue both scale loads,
   // the one their layout does not use at an offset no descriptor covers.
+  // SG: lane l of load j holds the entry of row kRpl j + l / kNgw and group
+  // kNgw wave + l % kNgw; rows past N and groups past K read zero.
+  constexpr int kRpl = SG ? SG / 32 : 1;   // rows per load = lanes per group
+  constexpr int kNgw = 64 / kRpl;          // groups in a wave's chunk
+  constexpr int kPk = SG ? (U + kRpl - 1) / kRpl : 1;
+  uint32_t spk[kPk], zpk[kPk];
+  if constexpr (SG != 0) {
+#pragma unroll
+    for (int j = 0; j < kPk; ++j) {
+      const int r = kRpl * j + lane / kNgw, gg = kNgw * wave + lane % kNgw;
+      const bool in = r < rows && gg < ng;
+      const uint32_t e = (uint32_t)(r * ng + gg);
+      if constexpr (S16) {   // float16 scale bits
+        spk[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)(in ? e * 2u : kOffsetOOB), 0, 0);
+        zpk[j] = 0u;
+      } else {
+        const uint32_t ze = zp4 ? (uint32_t)(r * zrow + (gg >> 1)) : e;
+        spk[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(in ? e * 4u : kOffsetOOB), 0, 0);
+        zpk[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rz, (int)(in ? ze : kOffsetOOB), 0, 0);
+      }
+    }
+  }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
+    if constexpr (SG != 0) break;
     const uint32_t e = (uint32_t)(u * ng + g);
     if constexpr (MX) {
       sr[u] = 0u;
@@ -246,6 +277,53 @@ __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
   // this the scheduler delays weight loads behind the activation math to save
   // registers, and the stream starts late.
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (SG != 0 && S16) {
+    // As below; the float16 scales of two loads travel together.
+    constexpr int kHw = (kPk + 1) / 2;
+    uint32_t hall[kHw];
+#pragma unroll
+    for (int w2 = 0; w2 < kHw; ++w2) hall[w2] = 0;
+#pragma unroll
+    for (int j = 0; j < kPk; ++j) hall[j / 2] |= (spk[j] & 0xFFFFu) << (16 * (j % 2));
+#pragma unroll
+    for (int c = 0; c < kRpl; ++c) {
+      if (c >= U) break;
+      const int src = 4 * (kNgw * c + lane / kRpl);
+#pragma unroll
+      for (int w2 = 0; w2 < kHw; ++w2) {
+        const uint32_t h = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)hall[w2]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int u = kRpl * (2 * w2 + t) + c;
+          if (u < U) { sr[u] = 0u; zr[u] = h >> (16 * t); }
+        }
+      }
+    }
+  } else if constexpr (SG != 0) {
+    // Row u = kRpl j + c's entry for this lane's group (lane / kRpl of the
+    // chunk) sits in lane kNgw c + lane / kRpl of load j.  The zero bytes of
+    // four loads travel together, byte j % 4 from load j.
+    constexpr int kZw = (kPk + 3) / 4;
+    uint32_t zall[kZw];
+#pragma unroll
+    for (int w4 = 0; w4 < kZw; ++w4) zall[w4] = 0;
+#pragma unroll
+    for (int j = 0; j < kPk; ++j) zall[j / 4] |= (zpk[j] & 0xFFu) << (8 * (j % 4));
+#pragma unroll
+    for (int c = 0; c < kRpl; ++c) {
+      if (c >= U) break;
+      const int src = 4 * (kNgw * c + lane / kRpl);
+      uint32_t zc[kZw];
+#pragma unroll
+      for (int w4 = 0; w4 < kZw; ++w4) zc[w4] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)zall[w4]);
+#pragma unroll
+      for (int j = 0; j < kPk; ++j) {
+        if (kRpl * j + c >= U) break;
+        sr[kRpl * j + c] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)spk[j]);
+        zr[kRpl * j + c] = zc[j / 4] >> (8 * (j % 4));
+      }
+    }
+  }
 
   // 2. The lane's activations in the unpacker's pair order, and their sum
   //    (MXFP4: in natural order, no sum).
@@ -351,17 +429,41 @@ __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
   }
 }
 
+// Groups of 128 or 256 (64 with 16-row workgroups; measured: 4-row ones are
+// 2% slower there) load each (scale, zero) pair once a wave.
+template <int U, int MR, int FMT, bool GRP>
+void launch_fmt(const RowsParams& rp, dim3 g, dim3 b, hipStream_t stream) {
+  if constexpr (FMT != kFmtMX) {
+    const bool shared = !(FMT == kFmtS16 && rp.row_scale);
+    if (shared && rp.group_shift == 7) {
+      hipLaunchKernelGGL((rows_kernel<U, MR, FMT, GRP, 128>), g, b, 0, stream, rp);
+      return;
+    }
+    if (shared && rp.group_shift == 8) {
+      hipLaunchKernelGGL((rows_kernel<U, MR, FMT, GRP, 256>), g, b, 0, stream, rp);
+      return;
+    }
+    if constexpr (U == 16) {
+      if (shared && rp.group_shift == 6) {
+        hipLaunchKernelGGL((rows_kernel<U, MR, FMT, GRP, 64>), g, b, 0, stream, rp);
+        return;
+      }
+    }
+  }
+  hipLaunchKernelGGL((rows_kernel<U, MR, FMT, GRP>), g, b, 0, stream, rp);
+}
+
 template <int U, int MR>
 int32_t launch_u(const RowsParams& rp, int64_t grid, int waves, int fmt, hipStream_t stream) {
   const dim3 g((unsigned)grid), b(64 * waves);
   if (rp.nprob > 1)   // grouped launches carry unsigned codes only
-    hipLaunchKernelGGL((rows_kernel<U, MR, kFmtU4, true>), g, b, 0, stream, rp);
+    launch_fmt<U, MR, kFmtU4, true>(rp, g, b, stream);
   else if (fmt == kFmtS16)
-    hipLaunchKernelGGL((rows_kernel<U, MR, kFmtS16, false>), g, b, 0, stream, rp);
+    launch_fmt<U, MR, kFmtS16, false>(rp, g, b, stream);
   else if (fmt == kFmtMX)
-    hipLaunchKernelGGL((rows_kernel<U, MR, kFmtMX, false>), g, b, 0, stream, rp);
+    launch_fmt<U, MR, kFmtMX, false>(rp, g, b, stream);
   else
-    hipLaunchKernelGGL((rows_kernel<U, MR, kFmtU4, false>), g, b, 0, stream, rp);
+    launch_fmt<U, MR, kFmtU4, false>(rp, g, b, stream);
   return hip_status(hipGetLastError());
 }
 
