@@ -208,9 +208,12 @@ int32_t woq_unprepare_int4(const uint8_t* prepared, int64_t n, int64_t k, uint8_
  * (32 MiB) inside the library; every device the library runs on holds its own
  * copy until the process ends.  ASYNC.
  * Arguments, results and errors: as woq_linear_int4_groups without workspace
- * and workspace_bytes; sizes whose woq_linear_workspace_bytes exceeds the
- * array return WOQ_EWORKSPACE before anything is enqueued (for example m = 2048
- * with k = 14336).
+ * and workspace_bytes.  Where woq_linear_workspace_bytes exceeds the array
+ * because the plan splits K (its float32 partial outputs), the call runs the
+ * same tiles with K whole instead (slower on narrow layers, equal up to float32
+ * summation order); sizes whose workspace exceeds the array even then return
+ * WOQ_EWORKSPACE before anything is enqueued (for example m = 2048 with
+ * k = 14336).
  * Calls that overlap on one device (concurrent streams, or host threads) share
  * that device's array and race: serialize them.  The array keeps the last
  * call's contents; nothing in it needs to start cleared.

@@ -81,7 +81,7 @@ def test_plan_decode_kernels(monkeypatch):
     (2048, 4096, 0),        # 256 tiles: one full round
     (1024, 14336, 0),       # 448 tiles: the last round is 3/4 full
     (200, 33064, 296),      # ragged rows and columns: 2 trailing tile columns
-    (129, 256, 0),          # one tile
+    (384, 16384, 0),        # 192 tiles: three quarters of the chip, one round
 ])
 def test_plan_tail_split(m, n, tail):
     plan = woq.linear_plan(m, n, 256, 128)
@@ -91,6 +91,44 @@ def test_plan_tail_split(m, n, tail):
     tm, tn = -(-m // 128), -(-n // 256)
     cols = -(-tail // 256)
     assert int(fields["grid"]) == tm * (tn - cols) + (-(-m // 64)) * cols
+
+
+@pytest.mark.parametrize("m,n,k,group,tile,splits", [
+    (256, 1024, 4096, 128, "128x64", 8),     # 8 tiles of 128 x 256 x 8 ranges: a quarter of the chip
+    (256, 4096, 4096, 128, "128x256", 8),    # 32 tiles, 32 steps: 8 ranges of 4
+    (256, 4096, 14336, 128, "128x256", 8),
+    (256, 14336, 4096, 128, "128x256", 2),   # 112 tiles
+    (512, 1024, 4096, 128, "128x64", 4),     # 128 x 256 would fill exactly half the chip
+    (512, 14336, 4096, 128, "128x256", 1),   # 224 tiles
+    (128, 4096, 14336, 128, "128x256", 14),  # above 64 rows the small-M kernel wants >= 4 tiles of 16 rows a workgroup
+    (96, 1024, 4096, 128, "128x64", 8),      # at most 16 ranges of >= 4 steps
+    (300, 1000, 4160, 64, "128x64", 5),      # 33 steps: ranges of 8, the last holds one
+    (129, 256, 256, 128, "128x64", 1),       # 2 steps: too short to split
+    (384, 16384, 4096, 128, "128x256", 1),   # 192 tiles of 128 x 256
+    (2048, 4096, 14336, 128, "128x256", 1),
+])
+def test_plan_split_k(m, n, k, group, tile, splits):
+    """Above 64 rows: tiles of 128 x 256 unless, even split over K, they would
+    fill at most half the chip (then 128 x 64); a grid under three quarters of
+    the chip takes K ranges (each an even number of at least 4 steps, at most
+    16 ranges) until it fills one round."""
+    fields = dict(f.split("=", 1) for f in woq.linear_plan(m, n, k, group).split())
+    assert fields["path"] == "gemm_mfma" and fields["tile"] == tile
+    assert int(fields["k_splits"]) == splits
+    bm, bn = map(int, tile.split("x"))
+    tiles = -(-m // bm) * -(-n // bn)
+    assert int(fields["grid"]) == tiles * splits
+    nsteps = -(-k // 128)
+    if splits > 1:
+        assert tiles * splits <= 256 and splits <= 16
+        sps = -(-nsteps // splits)
+        sps += sps & 1
+        assert -(-nsteps // sps) == splits and sps >= 4
+        # the partial outputs, float32 [splits][m][n], are part of the workspace
+        one = woq.linear_workspace_bytes(m, n, k, group, False)
+        assert one >= splits * m * n * 4
+    else:
+        assert tiles >= 192 or nsteps < 8 or (tiles > 128 and 256 // tiles < 2)
 
 
 def test_plan_mentions_gather_for_act_order():

@@ -65,7 +65,7 @@ def _with_workspace(lib, dev, m, n, k, group, out):
 # reordered activations, group sums and scale table); the second is smaller.
 SEQUENCES = [
     [(100, 1000, 2048, 128, True), (40, 300, 1024, 64, False)],
-    [(512, 4096, 4096, 128, False), (3, 4096, 4096, 128, True)],
+    [(300, 4096, 4096, 128, False), (3, 4096, 4096, 128, True)],   # a split over K, then the row kernel
     [(20, 2000, 4096, 32, True), (1, 1024, 4096, 128, True)],
 ]
 
@@ -88,6 +88,37 @@ def test_noalloc_equals_workspace_call(woq, seq):
             torch.cuda.synchronize()
             assert torch.equal(y_na, y_ws), f"call {i}: the two entry points differ"
             check_linear(y_na, ref, f"noalloc call {i} m={m} n={n} k={k}")
+
+
+def test_noalloc_keeps_k_whole_when_the_partials_do_not_fit(woq, monkeypatch):
+    """512 x 4096 x 4096 splits K in 4 with the caller's workspace (34 MB of
+    partial outputs, more than the array); without allocating it runs the
+    same tiles with K whole: bit-identical to the workspace call told to keep K
+    whole, and within the gate of the oracle.  Then a smaller call."""
+    lib = woq.load()
+    cap = lib.woq_linear_noalloc_max_workspace_bytes()
+    for i, (m, n, k, group, with_order) in enumerate([(512, 4096, 4096, 128, False), (40, 300, 1024, 64, True)]):
+        monkeypatch.delenv("WOQ_GEMM_SPLITS", raising=False)
+        plan = woq.linear_plan(m, n, k, group, with_order)
+        _say(f"noalloc unsplit call {i}: m={m} n={n} k={k} g={group} plan: {plan}")
+        if i == 0:
+            assert "k_splits=4" in plan and lib.woq_linear_workspace_bytes(m, n, k, group, 0) > cap
+        dev, ref = _case(woq, m, n, k, group, 9300 + 10 * i + m, with_order)
+        for dt in (torch.float32, torch.bfloat16):
+            y_na = torch.full((m, n), float("nan"), dtype=dt, device="cuda")
+            y_ws = torch.full((m, n), float("nan"), dtype=dt, device="cuda")
+            monkeypatch.delenv("WOQ_GEMM_SPLITS", raising=False)
+            assert _noalloc(lib, dev, m, n, k, group, y_na) == 0
+            # the reference call: the workspace entry point with K kept whole
+            monkeypatch.setenv("WOQ_GEMM_SPLITS", "1")
+            if i == 0:
+                assert "k_splits=1" in woq.linear_plan(m, n, k, group, with_order)
+            st, need = _with_workspace(lib, dev, m, n, k, group, y_ws)
+            monkeypatch.delenv("WOQ_GEMM_SPLITS", raising=False)
+            assert st == 0 and need <= cap
+            torch.cuda.synchronize()
+            assert torch.equal(y_na, y_ws), f"call {i}: the two entry points differ"
+            check_linear(y_na, ref, f"noalloc unsplit call {i} m={m} n={n} k={k}")
 
 
 def test_noalloc_refuses_sizes_beyond_its_array(woq):

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -185,7 +186,8 @@ bool gemv_plan(int64_t m, int64_t n, int64_t k, int32_t group, LinearPlan* p) {
 
 }  // namespace
 
-LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_order, bool rows_ok) {
+LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_order, bool rows_ok,
+                       bool split_ok) {
   LinearPlan p;
   if (m == 0 || n == 0) return p;
   if (k == 0) {
@@ -225,11 +227,26 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
   p.path = 2;
   p.prep = 1;
   // Tile by the number of activation rows: at small M, narrow tiles keep the
-  // grid wide enough to cover the chip.
-  if (m > 128) {
-    p.bm = 128; p.bn = 256; p.waves = 8;
-  } else if (m > 64) {
-    p.bm = 128; p.bn = 64; p.waves = 4;
+  // grid wide enough to cover the chip.  Above 64 rows: 128 x 256 tiles unless
+  // even split over K (below) they would fill at most half the chip, then
+  // 128 x 64 ones.  Measured on 1024x4096, 4096x4096, 4096x14336 and
+  // 14336x4096 at 256 and 512 rows against every tile width (64, 128, 256) and
+  // 1, 2, 4 or 8 K ranges: the rule picks the fastest of the 12 in all 8.
+  // WOQ_GEMM_BN (64, 128 or 256) forces the tile width above 64 rows and
+  // WOQ_GEMM_SPLITS the number of K ranges (tuning aids, read on every call).
+  const int64_t nsteps = (k + 127) / 128;
+  auto ranges_for = [&](int64_t tiles) {
+    return std::max<int64_t>(1, std::min<int64_t>({16, kComputeUnits / tiles, nsteps / 4}));
+  };
+  if (m > 64) {
+    p.bm = 128;
+    const int64_t t256 = ((m + 127) / 128) * ((n + 255) / 256);
+    p.bn = t256 * ranges_for(t256) > kComputeUnits / 2 ? 256 : 64;
+    if (const char* e = std::getenv("WOQ_GEMM_BN")) {
+      const int bn = std::atoi(e);
+      if (bn == 64 || bn == 128 || bn == 256) p.bn = bn;
+    }
+    p.waves = p.bn == 256 ? 8 : 4;
   } else if (m > 32) {
     p.bm = 64; p.bn = 64; p.waves = 4;
   } else {
@@ -238,6 +255,27 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
   p.mpad = ((m + 127) / 128) * 128;
   const int64_t tm = (m + p.bm - 1) / p.bm, tn = (n + p.bn - 1) / p.bn;
   p.grid = tm * tn;
+  // Split-K: a grid under three quarters of the chip takes up to 16 K ranges
+  // of at least 4 steps (an even count) each, as many as keep it within one
+  // round of workgroups; the ranges' float32 partials are summed in order
+  // afterwards.
+  {
+    const char* env_splits = std::getenv("WOQ_GEMM_SPLITS");
+    const int64_t forced = env_splits ? std::atoi(env_splits) : 0;
+    if (split_ok && (forced > 0 || p.grid < kComputeUnits * 3 / 4)) {
+      int64_t s = forced > 0 ? std::min<int64_t>(forced, std::max<int64_t>(nsteps / 2, 1)) : ranges_for(p.grid);
+      if (s >= 2) {
+        int64_t sps = (nsteps + s - 1) / s;
+        sps += sps & 1;
+        s = (nsteps + sps - 1) / sps;
+        if (s >= 2) {
+          p.splits = (int)s;
+          p.sps = (int)sps;
+          p.grid *= s;
+        }
+      }
+    }
+  }
   if (p.bn == 256) {
     // 128 x 256 tiles run one workgroup per compute unit.  When the last round
     // would be at most half full, the trailing tile columns that hold it go to
@@ -257,9 +295,9 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
 }
 
 LinearWorkspace linear_workspace_layout(int64_t m, int64_t n, int64_t k, int32_t group,
-                                        bool has_order) {
+                                        bool has_order, bool split_ok) {
   LinearWorkspace w;
-  const LinearPlan p = linear_plan(m, n, k, group, has_order);
+  const LinearPlan p = linear_plan(m, n, k, group, has_order, true, split_ok);
   if (p.path == 1 && p.xfrag) {
     w.xg_off = 0;
     w.xg_bytes = round256(xfrag_bytes(m, k));
@@ -275,8 +313,10 @@ LinearWorkspace linear_workspace_layout(int64_t m, int64_t n, int64_t k, int32_t
     w.xs_bytes = round256((size_t)(k / piece) * (size_t)p.mpad * 4);
     w.sz_off = w.xs_off + w.xs_bytes;
     w.sz_bytes = round256(gemm_sz_bytes(n, k, group));
+    w.part_off = w.sz_off + w.sz_bytes;
+    w.part_bytes = p.splits > 1 ? round256((size_t)p.splits * (size_t)m * (size_t)n * 4) : 0;
   }
-  w.total = w.xg_bytes + w.xs_bytes + w.sz_bytes;
+  w.total = w.xg_bytes + w.xs_bytes + w.sz_bytes + w.part_bytes;
   return w;
 }
 
@@ -563,7 +603,8 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
                     int64_t k, int32_t group, int32_t y_dtype, void* y, void* workspace,
                     size_t workspace_bytes, void* stream, int32_t prepared,
                     const uint16_t* scale16 = nullptr, const uint8_t* scale8 = nullptr,
-                    const float* scale_row = nullptr, const uint8_t* zero_packed = nullptr) {
+                    const float* scale_row = nullptr, const uint8_t* zero_packed = nullptr,
+                    bool split_ok = true) {
   const bool row = scale_row != nullptr;     // Int4Linear: signed codes, one float32 scale a row
   const bool zp4 = zero_packed != nullptr;   // packed 4-bit zero points
   const bool sym16 = scale16 != nullptr || row;
@@ -586,8 +627,8 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
     return WOQ_EALIGN;
   const bool has_order = order != nullptr;
   if (has_order && !aligned(order, 16)) return WOQ_EALIGN;
-  const LinearPlan plan = linear_plan(m, n, k, group, has_order, !prepared);
-  const LinearWorkspace ws = linear_workspace_layout(m, n, k, group, has_order);
+  const LinearPlan plan = linear_plan(m, n, k, group, has_order, !prepared, split_ok);
+  const LinearWorkspace ws = linear_workspace_layout(m, n, k, group, has_order, split_ok);
   // The tile GEMV reads one zero point a byte: packed ones are unpacked into the
   // head of the workspace first; every other path reads them as they are.
   const bool zp4_unpack = zp4 && plan.path == 4;
@@ -659,6 +700,7 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
   if (st != WOQ_OK) return st;
   a.x = xg;
   a.xs = xs;
+  a.part = reinterpret_cast<float*>(wsb + ws.part_off);
   return launch_gemm(a, plan, wsb + ws.sz_off, s);
 }
 
@@ -726,12 +768,15 @@ int32_t woq_linear_int4_groups_noalloc(const void* x_bf16, int64_t m, const uint
   if (m == 0 || n == 0 || need == 0)
     return linear_impl(x_bf16, m, packed, scale, zero, bias, order, n, k, group, y_dtype, y, nullptr, 0,
                        stream, 0);
-  if (need > kScratchBytes) return WOQ_EWORKSPACE;
+  // A split-K plan whose partial outputs do not fit runs with K whole.
+  const bool split_ok = need <= kScratchBytes;
+  if (!split_ok && linear_workspace_layout(m, n, k, group, order != nullptr, false).total > kScratchBytes)
+    return WOQ_EWORKSPACE;
   int32_t dst = WOQ_OK;
   void* ws = device_scratch(&dst);
   if (dst != WOQ_OK) return dst;
   return linear_impl(x_bf16, m, packed, scale, zero, bias, order, n, k, group, y_dtype, y, ws, kScratchBytes,
-                     stream, 0);
+                     stream, 0, nullptr, nullptr, nullptr, nullptr, split_ok);
 }
 
 int32_t woq_linear_int4_groups_zp4(const void* x_bf16, int64_t m, const uint8_t* packed, const float* scale,
@@ -913,9 +958,9 @@ int32_t woq_linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, int32_t 
       break;
     default:
       std::snprintf(buf, len,
-                    "path=gemm_mfma tile=%dx%d waves=%d group_blocks=%d tail_cols=%lld grid=%lld prep=%s "
-                    "workspace=%zu",
-                    p.bm, p.bn, p.waves, p.gb, (long long)p.tail_n, (long long)p.grid,
+                    "path=gemm_mfma tile=%dx%d waves=%d group_blocks=%d tail_cols=%lld k_splits=%d grid=%lld "
+                    "prep=%s workspace=%zu",
+                    p.bm, p.bn, p.waves, p.gb, (long long)p.tail_n, p.splits, (long long)p.grid,
                     has_order ? "gather+reorder+groupsum" : "reorder+groupsum", ws);
   }
   return WOQ_OK;

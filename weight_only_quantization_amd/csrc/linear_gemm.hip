@@ -137,6 +137,24 @@ __global__ __launch_bounds__(256) void fill_bias_kernel(const float* __restrict_
   }
 }
 
+// Split-K: y = sum over the K ranges of their float32 partials, in range
+// order (the same result on every run), + bias, then y's type.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int32_t splits,
+                                                            int32_t m, int32_t n, const float* __restrict__ bias,
+                                                            int32_t y_bf16, void* __restrict__ y) {
+  const int64_t total = (int64_t)m * n;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+    float v = part[t];
+    for (int r = 1; r < splits; ++r) v += part[(int64_t)r * total + t];
+    if (bias) v += bias[t % n];
+    if (y_bf16)
+      reinterpret_cast<uint16_t*>(y)[t] = f32_to_bf16_bits(v);
+    else
+      reinterpret_cast<float*>(y)[t] = v;
+  }
+}
+
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kJunk = 1024;                 // LDS that absorbs the loads of unused slots
@@ -198,6 +216,9 @@ struct GemmParams {
   int32_t vec_out;        // 1: y is 16-byte aligned and its rows are whole 16-byte chunks
   int32_t sym16;          // 1: signed two's complement codes (float16 scales in the table)
   int32_t mx;             // 1: MXFP4 (E2M1 codes; the table holds (2^(e - 127), 0) per block)
+  int32_t sps;            // 128-input steps per K range (split-K), or nsteps
+  float* part;            // split-K: workgroup (tile, r) writes its float32 partial tile, no
+                          // bias, to part + r * M * N; null: the whole sum goes to y
 };
 
 // Tl: workgroup tile; GB: 32-input blocks per group piece inside a step (1, 2
@@ -230,15 +251,19 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
   const int K = p.k, M = p.m, N = p.n;
   const uint32_t row_bytes = (uint32_t)K / 2;
 
+  // Workgroup r * tiles + t computes tile t over K range r (steps [s0, s1)).
   // Workgroups are dealt to the 8 XCDs round robin; renumber so that the
   // workgroups of one XCD cover neighbouring tiles that share weight columns.
   const int nwg = p.tiles_m * p.tiles_n;
-  int bid = blockIdx.x;
+  const int split = (int)blockIdx.x / nwg;
+  int bid = (int)blockIdx.x - split * nwg;
   const int full = (nwg / 8) * 8;
   if (bid < full) bid = (bid % 8) * (full / 8) + bid / 8;
   const int tm = bid % p.tiles_m, tn = bid / p.tiles_m;
   const int m0 = tm * BM, n0 = p.n_base + tn * BN;
   const int nsteps = (K + kStepK - 1) / kStepK;
+  const int s0 = split * p.sps;
+  const int s1 = min(nsteps, s0 + p.sps);
 
   const __amdgpu_buffer_rsrc_t ra =
       rsrc(p.xp + (int64_t)m0 * p.kpad, (uint32_t)min(BM, M - m0) * (uint32_t)p.kpad * 2);
@@ -263,7 +288,7 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
   auto issue_stage = [&](int slot, int step) {
     unsigned char* st = lds + slot * kStage;
     const int k0 = step * kStepK;
-    const uint32_t dead = step < nsteps ? 0u : kOffsetOOB;
+    const uint32_t dead = step < s1 ? 0u : kOffsetOOB;
 #pragma unroll
     for (int u = 0; u < Tl::kAPer; ++u) {
       const int a = wave * Tl::kAPer + u;     // uniform
@@ -494,11 +519,11 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
 
   // ---- the ring: stage i lives in slot i % S --------------------------------
 #pragma unroll
-  for (int s = 0; s < S; ++s) issue_stage(s, s);
+  for (int s = 0; s < S; ++s) issue_stage(s, s0 + s);
   int slot = 0;
-  for (int i = 0; i < nsteps; ++i) {
+  for (int i = s0; i < s1; ++i) {
     // this wave's loads of stage i have landed ...
-    if (i == 0)
+    if (i == s0)
       __builtin_amdgcn_s_waitcnt(wait_vmcnt((S - 1) * kLoads));
     else
       __builtin_amdgcn_s_waitcnt(wait_vmcnt((S - 2) * kLoads));
@@ -509,7 +534,7 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (i >= 1) issue_stage(slot == 0 ? S - 1 : slot - 1, i - 1 + S);
+    if (i > s0) issue_stage(slot == 0 ? S - 1 : slot - 1, i - 1 + S);
     compute(slot, i);
     slot = slot == S - 1 ? 0 : slot + 1;
   }
@@ -523,7 +548,7 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
         for (int r = 0; r < 16; ++r) acc[mt][nt][r] = fmaf(fold_sv[nt], cg[mt][nt][r], acc[mt][nt][r]);
   }
   if constexpr (4 / GB == 1) {
-    if (nsteps & 1) {   // the last (even) step's zero-point term is still pending
+    if (s1 & 1) {   // the last (even) step's zero-point term is still pending
 #pragma unroll
       for (int t = 0; t < MT; ++t) zpa[t] = h ? 0.f : zpa[t];
 #pragma unroll
@@ -540,14 +565,21 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
   constexpr int kEsz = 4;                                  // bytes per staged float32
   constexpr int kOutStride = BN * kEsz + 32;               // padded row: the lane halves' rows 4 apart hit other banks
   constexpr bool kStaged = BM * kOutStride <= S * kStage;
-  if (kStaged && p.vec_out) {
+  // A K range of a split call leaves its float32 partial tile, without the
+  // bias, in its own slice of the partial buffer.
+  float* const part = p.part ? p.part + (int64_t)split * M * N : nullptr;
+  void* const yout = part ? static_cast<void*>(part) : p.y;
+  const int ybf = part ? 0 : p.y_bf16;
+  const float* const bias = part ? nullptr : p.bias;
+  const bool vec = part ? N % 4 == 0 : p.vec_out != 0;
+  if (kStaged && vec) {
     __syncthreads();
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int n = n0 + brow[nt];
-        const float b = p.bias && n < N ? p.bias[n] : 0.f;
+        const float b = bias && n < N ? bias[n] : 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = 32 * MT * wm + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -557,14 +589,14 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
     __syncthreads();
     // 16-byte output chunks: 8 bf16 or 4 float32 columns; N is a whole number
     // of chunks, so a chunk is wholly inside or wholly past the last column.
-    const int ecols = p.y_bf16 ? 8 : 4;
+    const int ecols = ybf ? 8 : 4;
     const int cpr = BN / ecols;
     for (int c = tid; c < BM * cpr; c += 64 * kWaves) {
       const int row = c / cpr, col = (c - row * cpr) * ecols;
       const int m = m0 + row, n = n0 + col;
       if (m >= M || n >= N) continue;
       const float* src = reinterpret_cast<const float*>(lds + row * kOutStride + col * kEsz);
-      if (p.y_bf16) {
+      if (ybf) {
         const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(src);
         const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(src + 4);
         u32x4_t o;
@@ -573,9 +605,9 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
           o[e] = (uint32_t)f32_to_bf16_bits(lo[2 * e]) | ((uint32_t)f32_to_bf16_bits(lo[2 * e + 1]) << 16);
           o[e + 2] = (uint32_t)f32_to_bf16_bits(hi[2 * e]) | ((uint32_t)f32_to_bf16_bits(hi[2 * e + 1]) << 16);
         }
-        *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(p.y) + (int64_t)m * N + n) = o;
+        *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(yout) + (int64_t)m * N + n) = o;
       } else {
-        *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.y) + (int64_t)m * N + n) =
+        *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(yout) + (int64_t)m * N + n) =
             *reinterpret_cast<const f32x4_t*>(src);
       }
     }
@@ -587,16 +619,16 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
     for (int nt = 0; nt < NT; ++nt) {
       const int n = n0 + brow[nt];
       if (n >= N) continue;
-      const float b = p.bias ? p.bias[n] : 0.f;
+      const float b = bias ? bias[n] : 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + 32 * MT * wm + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
         if (m < M) {
           const float v = acc[mt][nt][r] + b;
-          if (p.y_bf16)
-            reinterpret_cast<uint16_t*>(p.y)[(int64_t)m * N + n] = f32_to_bf16_bits(v);
+          if (ybf)
+            reinterpret_cast<uint16_t*>(yout)[(int64_t)m * N + n] = f32_to_bf16_bits(v);
           else
-            reinterpret_cast<float*>(p.y)[(int64_t)m * N + n] = v;
+            reinterpret_cast<float*>(yout)[(int64_t)m * N + n] = v;
         }
       }
     }
@@ -617,7 +649,9 @@ int32_t launch_gemm_t(GemmParams gp, hipStream_t stream) {
     return st;
   gp.tiles_m = (gp.m + Tl::BM - 1) / Tl::BM;
   gp.tiles_n = (gp.n_cols + Tl::BN - 1) / Tl::BN;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(gp.tiles_m * gp.tiles_n)), dim3(64 * Tl::kWaves), lds,
+  const int nsteps = (gp.k + kStepK - 1) / kStepK;
+  const int splits = (nsteps + gp.sps - 1) / gp.sps;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(gp.tiles_m * gp.tiles_n * splits)), dim3(64 * Tl::kWaves), lds,
                      stream, gp);
   return hip_status(hipGetLastError());
 }
@@ -683,6 +717,34 @@ size_t gemm_sz_bytes(int64_t n, int64_t k, int32_t group) {
   return (size_t)(k / group) * (size_t)npad * 8;
 }
 
+namespace {
+
+int32_t launch_gemm_tiles(const LinearArgs& a, const LinearPlan& pl, const GemmParams& gp, hipStream_t stream) {
+  // Tile by the number of activation rows: small M takes narrow tiles so the
+  // grid still covers the chip.
+  switch (pl.bm) {
+    case 32: return launch_gemm_gb<Tile<1, 2, 1, 1>>(gp, pl.gb, stream);    // 32 x 64
+    case 64: return launch_gemm_gb<Tile<2, 2, 1, 1>>(gp, pl.gb, stream);    // 64 x 64
+    case 128:
+      if (pl.bn == 64) return launch_gemm_gb<Tile<2, 2, 2, 1>>(gp, pl.gb, stream);   // 128 x 64
+      if (pl.bn == 128) return launch_gemm_gb<Tile<2, 2, 2, 2>>(gp, pl.gb, stream);  // 128 x 128
+      if (pl.tail_n > 0) {
+        // columns before the tail in 128 x 256 tiles, the tail in 64 x 256
+        GemmParams head = gp, tail = gp;
+        head.n_cols = (int32_t)(a.n - pl.tail_n);
+        tail.n_base = head.n_cols;
+        tail.n_cols = (int32_t)pl.tail_n;
+        const int32_t st = launch_gemm_gb<Tile<2, 4, 2, 2>>(head, pl.gb, stream);
+        if (st != WOQ_OK) return st;
+        return launch_gemm_gb<Tile<2, 4, 1, 2>>(tail, pl.gb, stream);                // 64 x 256
+      }
+      return launch_gemm_gb<Tile<2, 4, 2, 2>>(gp, pl.gb, stream);                    // 128 x 256
+    default: return WOQ_EUNSUPPORTED;
+  }
+}
+
+}  // namespace
+
 int32_t launch_gemm(const LinearArgs& a, const LinearPlan& pl, void* sz_ws, hipStream_t stream) {
   const int32_t ngroups = a.k / a.group;
   const int32_t npad = (a.n + kNPad - 1) / kNPad * kNPad;
@@ -704,27 +766,16 @@ int32_t launch_gemm(const LinearArgs& a, const LinearPlan& pl, void* sz_ws, hipS
                       a.m, a.n, a.k, a.kpad, a.group, a.y_bf16, a.mpad, npad, ngroups, a.k / piece,
                       0, 0, 0, a.n, a.prepared,
                       (reinterpret_cast<uintptr_t>(a.y) % 16 == 0 && a.n % (a.y_bf16 ? 8 : 4) == 0) ? 1 : 0,
-                      a.sym16, a.mx};
-  // Tile by the number of activation rows: small M takes narrow tiles so the
-  // grid still covers the chip.
-  switch (pl.bm) {
-    case 32: return launch_gemm_gb<Tile<1, 2, 1, 1>>(gp, pl.gb, stream);    // 32 x 64
-    case 64: return launch_gemm_gb<Tile<2, 2, 1, 1>>(gp, pl.gb, stream);    // 64 x 64
-    case 128:
-      if (pl.bn == 64) return launch_gemm_gb<Tile<2, 2, 2, 1>>(gp, pl.gb, stream);   // 128 x 64
-      if (pl.tail_n > 0) {
-        // columns before the tail in 128 x 256 tiles, the tail in 64 x 256
-        GemmParams head = gp, tail = gp;
-        head.n_cols = (int32_t)(a.n - pl.tail_n);
-        tail.n_base = head.n_cols;
-        tail.n_cols = (int32_t)pl.tail_n;
-        const int32_t st = launch_gemm_gb<Tile<2, 4, 2, 2>>(head, pl.gb, stream);
-        if (st != WOQ_OK) return st;
-        return launch_gemm_gb<Tile<2, 4, 1, 2>>(tail, pl.gb, stream);                // 64 x 256
-      }
-      return launch_gemm_gb<Tile<2, 4, 2, 2>>(gp, pl.gb, stream);                    // 128 x 256
-    default: return WOQ_EUNSUPPORTED;
-  }
+                      a.sym16, a.mx, pl.splits > 1 ? pl.sps : (a.k + kStepK - 1) / kStepK,
+                      pl.splits > 1 ? a.part : nullptr};
+  const int32_t st = launch_gemm_tiles(a, pl, gp, stream);
+  if (st != WOQ_OK || pl.splits <= 1) return st;
+  const int64_t total = (int64_t)a.m * a.n;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.part, pl.splits,
+                     a.m, a.n, a.bias, a.y_bf16, a.y);
+  return hip_status(hipGetLastError());
 }
 
 }  // namespace woq

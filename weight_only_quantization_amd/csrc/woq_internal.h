@@ -42,6 +42,7 @@ struct LinearWorkspace {
   size_t xg_off = 0, xg_bytes = 0;   // gathered and/or pair-permuted activations, bf16 [M, kpad]
   size_t xs_off = 0, xs_bytes = 0;   // per-piece activation sums, f32 [K/min(G,128)][Mpad]
   size_t sz_off = 0, sz_bytes = 0;   // (scale, -(128 + zero)) pairs, f32x2 [K/G][N rounded to 256]
+  size_t part_off = 0, part_bytes = 0;   // split-K partial outputs, f32 [splits][M][N]
   size_t total = 0;
 };
 
@@ -64,17 +65,21 @@ struct LinearPlan {
                          // 64-row tiles, so that the last round of workgroups is not half empty
   int rows_u = 0;        // row-streaming decode path (path 5): rows per workgroup
   int xfrag = 0;         // small-M path: a pre-pass writes the activations in MFMA fragment order
+  int splits = 1;        // GEMM path: K ranges over separate workgroups (partials summed after)
+  int sps = 0;           // GEMM path: 128-input steps per K range when splits > 1
 };
 
 // Compute units of one MI355X (gfx950): the GEMM path sizes its grid in rounds of this many
 // workgroups (one workgroup per compute unit at a time).
 constexpr int64_t kComputeUnits = 256;
 
+// split_ok = false: the tiled GEMM keeps K whole (no partial-output buffer).
 LinearWorkspace linear_workspace_layout(int64_t m, int64_t n, int64_t k, int32_t group,
-                                        bool has_order);
+                                        bool has_order, bool split_ok = true);
 // rows_ok: the weights are canonical packed rows (unsigned or signed codes, or
 // MXFP4 blocks; not prepared), which the row-streaming decode path can read.
-LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_order, bool rows_ok = true);
+LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_order, bool rows_ok = true,
+                       bool split_ok = true);
 
 // ---------------------------------------------------------------------------
 // Launchers (defined next to their kernels).  All enqueue on `stream` and
@@ -121,6 +126,7 @@ struct LinearArgs {
   int32_t row_scale;       // 1 (with sym16): one float32 scale a row in `scale` [N] (Int4Linear)
   int32_t zp4;             // 1: `zero` holds packed 4-bit zero points [N, ceil(K/G / 2)], group 2j
                            //    in the low nibble of byte j (row-streaming, small-M and GEMM paths)
+  float* part;             // GEMM path with splits > 1: f32 partial outputs [splits][M][N]
 };
 
 // Weight formats of the linear kernels' instantiations.
