@@ -135,7 +135,11 @@ size_t woq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group
  *   x'[m, k] = order ? x[m, order[k]] : x[m, k].
  * x is bfloat16; products and sums are float32; the sum over each group is
  * multiplied by that group's scale in float32; bias is added in float32; a
- * bfloat16 y is rounded once from that float32 value, ties to even.  ASYNC.
+ * bfloat16 y is rounded once from that float32 value, ties to even.  Where
+ * woq_linear_plan reports k_splits > 1 (the tiled GEMM on narrow layers), K is
+ * cut into that many ranges whose float32 partial sums go through the
+ * workspace and are added in range order (the same result on every run).
+ * ASYNC.
  * Arguments:
  *   x_bf16 [m, k] bfloat16 (device, 16-byte aligned);
  *   packed [n, k/2] uint8 (device, 16-byte aligned); scale [n, k/group] float32
@@ -589,8 +593,9 @@ int32_t woq_awq_search(const float* w, const void* x_bf16, int64_t t, int64_t n,
  * (row-streaming decode "rows_dot2" for m <= 4 over canonical weights, tile
  * GEMV "gemv_mfma" for prepared weights at m <= 4; small-M MFMA
  * "skinny_mfma" up to 64 rows, and up to 128 on layers of at least 800
- * 16-row tiles; tiled MFMA GEMM "gemm_mfma" above), tiles, waves and which
- * input pre-pass runs.  Writes a NUL-terminated
+ * 16-row tiles; tiled MFMA GEMM "gemm_mfma" above), tiles, waves, the
+ * number of K ranges of a split tiled GEMM (k_splits) and which input
+ * pre-pass runs.  Writes a NUL-terminated
  * string of at most len bytes into buf (host).  Pure host function.
  * Errors: WOQ_EINVAL (buf NULL, len 0), plus the shape errors of the linear call.
  */
