@@ -216,7 +216,7 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
     p.prep = has_order ? 1 : 0;
     return p;
   }
-  static const bool force_tiled = std::getenv("WOQ_FORCE_TILED") != nullptr;   // tuning aid
+  const bool force_tiled = std::getenv("WOQ_FORCE_TILED") != nullptr;   // tuning aid, read on every call
   // The small-M kernel takes up to 128 rows (from 65 rows only layers of at
   // least 800 weight tiles of 16 rows: 14336x4096 at 128 rows runs in 41 us
   // against the tiled GEMM's 46 us at group 128, 57 against 89 us at group 32).
@@ -276,7 +276,7 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
       }
     }
   }
-  if (p.bn == 256) {
+  if (p.bm == 128 && p.bn == 256) {
     // 128 x 256 tiles run one workgroup per compute unit.  When the last round
     // would be at most half full, the trailing tile columns that hold it go to
     // a second launch as 64-row tiles (half the work each, twice as many), so
