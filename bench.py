@@ -734,8 +734,13 @@ def main():
 
     prefill = None if args.no_prefill else measure_prefill(torch, woq)
     configs = None if args.no_configs else measure_configs(torch, woq)
-    sym16 = mxfp4 = zp4 = None
+    sym16 = mxfp4 = zp4 = midsize = None
     if not args.no_configs:
+        from workloads import MIDSIZE
+        midsize = dict(
+            note="M = 128 and 256 on the decode shapes: the tiled GEMM, its K split over workgroups where the "
+                 "tiles alone would not fill the chip (k_splits in the plan), or the small-M kernel",
+            configs=measure_configs(torch, woq, cases=MIDSIZE))
         from workloads import ZP4
         zp4 = dict(
             note="packed 4-bit zero points (woq_linear_int4_groups_zp4)",
@@ -763,7 +768,7 @@ def main():
                     graph=not args.no_graph, accumulate="f32",
                     tokens_per_s_linears_only=round(1.0 / (ms_per_step * 1e-3), 1) if args.layers == 32 else None),
         roofline=roofline, grouped=grouped, prepared=prepared, prefill=prefill, configs=configs,
-        sym16=sym16, mxfp4=mxfp4, zp4=zp4,
+        sym16=sym16, mxfp4=mxfp4, zp4=zp4, midsize=midsize,
         cpu_baseline=cpu,
     )
     print(json.dumps(line), flush=True)

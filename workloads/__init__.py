@@ -212,6 +212,15 @@ def packed_weights(n: int, k: int, group: int, seed: int, std: float = 0.02):
 # Signed int4 groups with float16 scales (tinyllm L8.5, "int4 per group", whose
 # default group is 32): the decode shapes at M = 1 with groups 32 and 128,
 # one small-M and one prefill shape.
+# Batches between the small-M kernel and prefill on the same Llama-3-8B
+# shapes (the tiled GEMM, split over K on the narrow layers): sizes only, no
+# figure from the pages.
+MIDSIZE = tuple(
+    LinearCase(f"midsize_m{m}_{n}x{k}", m, n, k, 128, seed_w=180 + i, seed_x=280 + i + 10 * j)
+    for j, m in enumerate((128, 256))
+    for i, (n, k) in enumerate(((1024, 4096), (4096, 4096), (4096, 14336), (14336, 4096)))
+)
+
 SYM16 = tuple(
     [LinearCase(f"sym16_m1_g{g}_{n}x{k}", 1, n, k, g, seed_w=150 + i, seed_x=250 + i)
      for g in (32, 128) for i, (n, k) in enumerate(((4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)))]
