@@ -695,8 +695,8 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
   uint16_t* xg = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
   float* xs = reinterpret_cast<float*>(wsb + ws.xs_off);
   a.kpad = (a.k + 127) / 128 * 128;
-  // MXFP4 weights decode in natural input order and need no piece sums
-  st = launch_prep(a.x, order, a.m, a.k, a.kpad, group, mx ? 0 : 1, xg, mx ? nullptr : xs, plan.mpad, s);
+  // the activation pre-pass and the scale/zero table, one launch
+  st = launch_gemm_prep(a, order, xg, xs, wsb + ws.sz_off, s);
   if (st != WOQ_OK) return st;
   a.x = xg;
   a.xs = xs;

@@ -45,17 +45,29 @@ constexpr uint32_t kSignFlip = 0x88888888u;    // two's complement nibble v -> u
 // shuffle tree, so the sums are the same on every run.  Rows from m to mpad
 // only get zero sums; columns from k to kpad (the written row stride) get
 // zeros.
+struct PrepArgs {
+  const uint16_t* x;
+  const int32_t* order;
+  int32_t m, k, kpad, permute;
+  uint16_t* xg;
+  float* xs;
+  int64_t mpad;
+};
+
+// The grid-stride body, as workgroup `block` of `nblocks` (256 threads each).
 template <int LP>   // lanes per piece: piece / 8
-__global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ x,
-                                                   const int32_t* __restrict__ order, int32_t m,
-                                                   int32_t k, int32_t kpad, int32_t permute,
-                                                   uint16_t* __restrict__ xg, float* __restrict__ xs,
-                                                   int64_t mpad) {
+__device__ __forceinline__ void prep_body(const PrepArgs& a, int64_t block, int64_t nblocks) {
+  const uint16_t* __restrict__ x = a.x;
+  const int32_t* __restrict__ order = a.order;
+  const int32_t m = a.m, k = a.k, kpad = a.kpad, permute = a.permute;
+  uint16_t* __restrict__ xg = a.xg;
+  float* __restrict__ xs = a.xs;
+  const int64_t mpad = a.mpad;
   const int cpr = kpad / 8;                    // chunks per written row
   const int kc = k / 8;                        // chunks holding inputs
   const int64_t total = mpad * cpr;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+  const int64_t stride = nblocks * 256;
+  for (int64_t t = block * 256 + threadIdx.x; t < total; t += stride) {
     const int64_t row = t / cpr;
     const int col = (int)(t % cpr);
     u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
@@ -89,18 +101,30 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
   }
 }
 
+template <int LP>
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
+  prep_body<LP>(a, blockIdx.x, gridDim.x);
+}
+
 // sz[g][c] = (scale[c][g], -(128 + zero[c][g])) for c < n, zeros up to npad.
 // With signed codes the scale is float16 and the zero point 8 (the codes are
 // read as v ^ 8); for MXFP4 (fmt 2) the entry is (2^(e - 127), 0) of the E8M0
 // scale byte e.
-__global__ __launch_bounds__(256) void sz_prep_kernel(const void* __restrict__ scale,
-                                                      const uint8_t* __restrict__ zero, int32_t n,
-                                                      int32_t ngroups, int32_t npad, int32_t fmt,
-                                                      int32_t row_scale, int32_t zp4,
-                                                      f32x2_t* __restrict__ sz) {
+struct SzArgs {
+  const void* scale;
+  const uint8_t* zero;
+  int32_t n, ngroups, npad, fmt, row_scale, zp4;
+  f32x2_t* sz;
+};
+
+__device__ __forceinline__ void sz_body(const SzArgs& a, int64_t block, int64_t nblocks) {
+  const void* __restrict__ scale = a.scale;
+  const uint8_t* __restrict__ zero = a.zero;
+  const int32_t n = a.n, ngroups = a.ngroups, npad = a.npad, fmt = a.fmt, row_scale = a.row_scale, zp4 = a.zp4;
+  f32x2_t* __restrict__ sz = a.sz;
   const int64_t total = (int64_t)ngroups * npad;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+  const int64_t stride = nblocks * 256;
+  for (int64_t t = block * 256 + threadIdx.x; t < total; t += stride) {
     const int64_t g = t / npad;
     const int c = (int)(t % npad);
     f32x2_t v = f32x2_t{0.f, 0.f};
@@ -122,6 +146,16 @@ __global__ __launch_bounds__(256) void sz_prep_kernel(const void* __restrict__ s
     }
     sz[t] = v;
   }
+}
+
+// The activation pre-pass and the scale/zero table in one launch: workgroups
+// below prep_blocks take the first, the rest the second.
+template <int LP>
+__global__ __launch_bounds__(256) void prep_sz_kernel(PrepArgs pa, SzArgs sa, int32_t prep_blocks) {
+  if ((int)blockIdx.x < prep_blocks)
+    prep_body<LP>(pa, blockIdx.x, prep_blocks);
+  else
+    sz_body(sa, (int64_t)blockIdx.x - prep_blocks, (int64_t)gridDim.x - prep_blocks);
 }
 
 __global__ __launch_bounds__(256) void fill_bias_kernel(const float* __restrict__ bias, int32_t m,
@@ -692,10 +726,11 @@ int32_t launch_prep(const uint16_t* x, const int32_t* order, int32_t m, int32_t 
   if (total == 0) return WOQ_OK;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
+  const PrepArgs pa{x, order, m, k, kpad, permute, xg, xs, mpad};
   switch (piece / 8) {
-    case 4: hipLaunchKernelGGL(prep_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, x, order, m, k, kpad, permute, xg, xs, mpad); break;
-    case 8: hipLaunchKernelGGL(prep_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, stream, x, order, m, k, kpad, permute, xg, xs, mpad); break;
-    case 16: hipLaunchKernelGGL(prep_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, x, order, m, k, kpad, permute, xg, xs, mpad); break;
+    case 4: hipLaunchKernelGGL(prep_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, pa); break;
+    case 8: hipLaunchKernelGGL(prep_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, stream, pa); break;
+    case 16: hipLaunchKernelGGL(prep_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, pa); break;
     default: return WOQ_EUNSUPPORTED;
   }
   return hip_status(hipGetLastError());
@@ -745,22 +780,44 @@ int32_t launch_gemm_tiles(const LinearArgs& a, const LinearPlan& pl, const GemmP
 
 }  // namespace
 
+namespace {
+
+SzArgs sz_args(const LinearArgs& a, int32_t ngroups, int32_t npad, void* sz_ws) {
+  return SzArgs{a.mx ? static_cast<const void*>(a.scale8)
+                     : a.sym16 && !a.row_scale ? static_cast<const void*>(a.scale16)
+                                               : static_cast<const void*>(a.scale),
+                a.zero, a.n, ngroups, npad, a.mx ? kFmtMX : a.sym16 ? kFmtS16 : kFmtU4, a.row_scale, a.zp4,
+                static_cast<f32x2_t*>(sz_ws)};
+}
+
+}  // namespace
+
+int32_t launch_gemm_prep(const LinearArgs& a, const int32_t* order, uint16_t* xg, float* xs, void* sz_ws,
+                         hipStream_t stream) {
+  const int32_t ngroups = a.k / a.group;
+  const int32_t npad = (a.n + kNPad - 1) / kNPad * kNPad;
+  const int32_t piece = a.group < kStepK ? a.group : kStepK;
+  const int64_t ptotal = a.mpad * (a.kpad / 8);
+  const int64_t stotal = (int64_t)ngroups * npad;
+  const int64_t pblocks = std::min<int64_t>((ptotal + 255) / 256, 65536);
+  const int64_t sblocks = std::min<int64_t>((stotal + 255) / 256, 65536);
+  if (pblocks + sblocks == 0) return WOQ_OK;
+  // MXFP4 weights decode in natural input order and need no piece sums
+  const PrepArgs pa{a.x, order, a.m, a.k, a.kpad, a.mx ? 0 : 1, xg, a.mx ? nullptr : xs, a.mpad};
+  const SzArgs sa = sz_args(a, ngroups, npad, sz_ws);
+  const dim3 grid((unsigned)(pblocks + sblocks)), block(256);
+  switch (piece / 8) {
+    case 4: hipLaunchKernelGGL(prep_sz_kernel<4>, grid, block, 0, stream, pa, sa, (int32_t)pblocks); break;
+    case 8: hipLaunchKernelGGL(prep_sz_kernel<8>, grid, block, 0, stream, pa, sa, (int32_t)pblocks); break;
+    case 16: hipLaunchKernelGGL(prep_sz_kernel<16>, grid, block, 0, stream, pa, sa, (int32_t)pblocks); break;
+    default: return WOQ_EUNSUPPORTED;
+  }
+  return hip_status(hipGetLastError());
+}
+
 int32_t launch_gemm(const LinearArgs& a, const LinearPlan& pl, void* sz_ws, hipStream_t stream) {
   const int32_t ngroups = a.k / a.group;
   const int32_t npad = (a.n + kNPad - 1) / kNPad * kNPad;
-  {
-    const int64_t total = (int64_t)ngroups * npad;
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(sz_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       a.mx ? static_cast<const void*>(a.scale8)
-                            : a.sym16 && !a.row_scale ? static_cast<const void*>(a.scale16)
-                                                      : static_cast<const void*>(a.scale),
-                       a.zero, a.n, ngroups, npad, a.mx ? kFmtMX : a.sym16 ? kFmtS16 : kFmtU4,
-                       a.row_scale, a.zp4, static_cast<f32x2_t*>(sz_ws));
-    const int32_t st = hip_status(hipGetLastError());
-    if (st != WOQ_OK) return st;
-  }
   const int32_t piece = a.group < kStepK ? a.group : kStepK;
   const GemmParams gp{a.x, a.packed, a.xs, static_cast<const f32x2_t*>(sz_ws), a.bias, a.y,
                       a.m, a.n, a.k, a.kpad, a.group, a.y_bf16, a.mpad, npad, ngroups, a.k / piece,

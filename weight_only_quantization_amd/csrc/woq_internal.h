@@ -202,6 +202,11 @@ SkinnyLds skinny_lds_layout(int64_t m, int64_t k, int64_t group, int waves, int 
 constexpr size_t kSkinnyLdsLimit = 160 * 1024;   // LDS per CU
 size_t gemm_sz_bytes(int64_t n, int64_t k, int32_t group);
 constexpr int64_t kGemmMaxK = (int64_t)1 << 24;   // tile offsets of the GEMM path are 32-bit
+// The GEMM path's inputs in one launch: x gathered/reordered into xg with its
+// piece sums in xs (a.mpad rows, a.kpad stride) and the (scale, -(128 + zero))
+// table into sz_ws; then launch_gemm, which reads them.
+int32_t launch_gemm_prep(const LinearArgs& a, const int32_t* order, uint16_t* xg, float* xs, void* sz_ws,
+                         hipStream_t stream);
 int32_t launch_gemm(const LinearArgs& a, const LinearPlan& p, void* sz_ws, hipStream_t stream);
 int32_t launch_fill_bias(const float* bias, int32_t m, int32_t n, int32_t y_bf16, void* y,
                          hipStream_t stream);
