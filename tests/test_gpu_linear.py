@@ -274,7 +274,8 @@ def _sample_rows(n, seed, count=48):
     return rows
 
 
-FULL = list(workloads.DECODE) + list(workloads.PREFILL) + list(workloads.ACTORDER) + list(workloads.SWEEP)
+FULL = (list(workloads.DECODE) + list(workloads.PREFILL) + list(workloads.ACTORDER) + list(workloads.SWEEP)
+        + list(workloads.MIDSIZE))
 
 
 @pytest.mark.slow
