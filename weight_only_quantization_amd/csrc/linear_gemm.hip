@@ -299,18 +299,11 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
   const int s0 = split * p.sps;
   const int s1 = min(nsteps, s0 + p.sps);
 
-  const __amdgpu_buffer_rsrc_t ra =
-      rsrc(p.xp + (int64_t)m0 * p.kpad, (uint32_t)min(BM, M - m0) * (uint32_t)p.kpad * 2);
   // Weights: canonical rows, or prepared 1 KB blocks (16 rows x one step,
   // tile-major; slot l of a block holds row l % 16, quarter l / 16 of the step).
   const bool prep = p.prepared != 0;   // uniform
   const int ptiles = min(BN / 16, (N + 15) / 16 - n0 / 16);
-  const __amdgpu_buffer_rsrc_t rb =
-      prep ? rsrc(p.packed + (int64_t)(n0 / 16) * nsteps * 1024, (uint32_t)(ptiles * nsteps) * 1024u)
-           : rsrc(p.packed + (int64_t)n0 * row_bytes, (uint32_t)min(BN, N - n0) * row_bytes);
-  // (MXFP4 needs no piece sums: a zero-sized descriptor makes those loads read zero)
-  const __amdgpu_buffer_rsrc_t rx = rsrc(p.xs, MX ? 0u : (uint32_t)((int64_t)p.npieces * p.mpad * 4));
-  const __amdgpu_buffer_rsrc_t rz = rsrc(p.sz, (uint32_t)((int64_t)p.ngroups * p.npad * 8));
+  const int gshift = __builtin_ctz((unsigned)p.group);   // groups are powers of two
 
   // ---- one stage of loads: this wave's share, the same count for every wave --
   // Activation tile: BM/4 loads of 4 rows x 256 bytes; lane l of load a fills
@@ -319,51 +312,84 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
   // 16b + l/4 holds chunk (l%4) ^ ((row >> 1) & 3).  Metadata: per piece one
   // load of 128 piece sums (lanes 0..31) and 128 (scale, zero) pairs per load.
   // Load slots past the tile's count read nothing into the junk block.
+  //
+  // A lane's byte offsets do not change from step to step: each step moves
+  // the base of its buffer descriptors instead and shrinks their size to
+  // what is left past the base, so rows past M or N, pieces and groups past K
+  // and steps past the range (size 0) still read zero.  The offsets below
+  // are relative to the step's bases; kOffsetOOB marks a slot with nothing
+  // to load.
+  uint32_t voa[Tl::kAPer], vob[Tl::kBPer], vom[kMeta];
+#pragma unroll
+  for (int u = 0; u < Tl::kAPer; ++u) {
+    const int a = wave * Tl::kAPer + u;       // uniform
+    const int row = 4 * a + (lane >> 4);
+    const int c = (lane & 15) ^ (row & 7);
+    voa[u] = a < Tl::kA ? ((uint32_t)row * (uint32_t)p.kpad + (uint32_t)(8 * c)) * 2u : kOffsetOOB;
+  }
+#pragma unroll
+  for (int u = 0; u < Tl::kBPer; ++u) {
+    const int b = wave * Tl::kBPer + u;       // uniform
+    const int row = 16 * b + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    vob[u] = b >= Tl::kB ? kOffsetOOB
+             : prep      ? (uint32_t)(b * nsteps) * 1024u + 16u * (uint32_t)(16 * c + (lane >> 2))
+                         : (uint32_t)row * row_bytes + (uint32_t)(16 * c);
+  }
+#pragma unroll
+  for (int u = 0; u < kMeta; ++u) {
+    const int mi = wave * kMeta + u;          // uniform
+    const int pc = mi / (1 + Tl::kSzParts), part = mi - (1 + Tl::kSzParts) * pc;
+    uint32_t off = kOffsetOOB;
+    if (pc < NP && part == 0) {               // piece pc of the step: its sums for rows m0 + 4 lane ..
+      if (lane < 32) off = (uint32_t)(((int64_t)pc * p.mpad + m0 + 4 * lane) * 4);
+    } else if (pc < NP) {                     // its group: pc pieces on when groups are one piece
+      const int pg = (pc * kPiece) >> gshift;
+      off = (uint32_t)(((int64_t)pg * p.npad + n0 + 128 * (part - 1) + 2 * lane) * 8);
+    }
+    vom[u] = off;
+  }
+  const uint16_t* const xbase = p.xp + (int64_t)m0 * p.kpad;
+  const uint32_t xbytes = (uint32_t)min(BM, M - m0) * (uint32_t)p.kpad * 2u;
+  const uint8_t* const wbase = prep ? p.packed + (int64_t)(n0 / 16) * nsteps * 1024 : p.packed + (int64_t)n0 * row_bytes;
+  const uint32_t wbytes = prep ? (uint32_t)(ptiles * nsteps) * 1024u : (uint32_t)min(BN, N - n0) * row_bytes;
+  const bool ktail = !prep && K % kStepK != 0;   // canonical rows whose last step is partial
   auto issue_stage = [&](int slot, int step) {
     unsigned char* st = lds + slot * kStage;
     const int k0 = step * kStepK;
-    const uint32_t dead = step < s1 ? 0u : kOffsetOOB;
+    const bool live = step < s1;              // uniform
+    const __amdgpu_buffer_rsrc_t ra = rsrc(xbase + k0, live ? xbytes - (uint32_t)k0 * 2u : 0u);
+    const uint32_t wstep = prep ? (uint32_t)step * 1024u : (uint32_t)k0 / 2u;
+    // The last step of canonical rows with a partial step keeps the rows'
+    // own ends: its lanes past the end of a row read zero, not the next row.
+    const bool wlast = ktail && k0 + kStepK > K;   // uniform
+    const __amdgpu_buffer_rsrc_t rb = rsrc(wbase + (wlast ? 0u : wstep), !live ? 0u : wlast ? wbytes : wbytes - wstep);
+    const int pi0 = k0 / kPiece, g0 = k0 >> gshift;
+    const __amdgpu_buffer_rsrc_t rx =
+        rsrc(p.xs + (int64_t)pi0 * p.mpad, live && !MX && pi0 < p.npieces ? (uint32_t)((int64_t)(p.npieces - pi0) * p.mpad * 4) : 0u);
+    const __amdgpu_buffer_rsrc_t rz =
+        rsrc(p.sz + (int64_t)g0 * p.npad, live && g0 < p.ngroups ? (uint32_t)((int64_t)(p.ngroups - g0) * p.npad * 8) : 0u);
 #pragma unroll
     for (int u = 0; u < Tl::kAPer; ++u) {
       const int a = wave * Tl::kAPer + u;     // uniform
-      const int row = 4 * a + (lane >> 4);
-      const int c = (lane & 15) ^ (row & 7);
-      const bool real = a < Tl::kA;
-      bload16_lds(ra, real ? st + a * 1024 : junk,
-                  real ? ((uint32_t)row * (uint32_t)p.kpad + (uint32_t)(k0 + 8 * c)) * 2 | dead : kOffsetOOB);
+      bload16_lds(ra, a < Tl::kA ? st + a * 1024 : junk, voa[u]);
     }
 #pragma unroll
     for (int u = 0; u < Tl::kBPer; ++u) {
       const int b = wave * Tl::kBPer + u;     // uniform
-      const int row = 16 * b + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 1) & 3);
-      const bool real = b < Tl::kB;
-      const uint32_t off = !real ? kOffsetOOB
-                           : prep ? (uint32_t)(b * nsteps + step) * 1024u + 16u * (uint32_t)(16 * c + (lane >> 2))
-                           : (uint32_t)(k0 / 2 + 16 * c) < row_bytes ? (uint32_t)row * row_bytes + (uint32_t)(k0 / 2 + 16 * c)
-                                                                     : kOffsetOOB;
-      bload16_lds(rb, real ? st + kABytes + b * 1024 : junk, off | dead);
+      uint32_t off = vob[u];
+      if (wlast) {
+        const int c = (lane & 3) ^ (((16 * b + (lane >> 2)) >> 1) & 3);
+        off = (uint32_t)(k0 / 2 + 16 * c) < row_bytes ? off + (uint32_t)k0 / 2u : kOffsetOOB;
+      }
+      bload16_lds(rb, b < Tl::kB ? st + kABytes + b * 1024 : junk, off);
     }
 #pragma unroll
     for (int u = 0; u < kMeta; ++u) {
       const int mi = wave * kMeta + u;       // uniform
       const int pc = mi / (1 + Tl::kSzParts), part = mi - (1 + Tl::kSzParts) * pc;
-      unsigned char* dst = junk;
-      uint32_t off = kOffsetOOB;
-      if (pc < NP) {
-        if (part == 0) {
-          const int pi = (k0 + pc * kPiece) / kPiece;
-          dst = st + kXsOff + pc * 1024;
-          if (lane < 32 && pi < p.npieces)
-            off = (uint32_t)(((int64_t)pi * p.mpad + m0 + 4 * lane) * 4);
-        } else {
-          const int g = (k0 + pc * kPiece) / p.group;
-          dst = st + kSzOff + pc * kSzStride + (part - 1) * 1024;
-          if (g < p.ngroups)
-            off = (uint32_t)(((int64_t)g * p.npad + n0 + 128 * (part - 1) + 2 * lane) * 8);
-        }
-      }
-      bload16_lds(pc < NP && part == 0 ? rx : rz, dst, off | dead);
+      unsigned char* dst = pc >= NP ? junk : part == 0 ? st + kXsOff + pc * 1024 : st + kSzOff + pc * kSzStride + (part - 1) * 1024;
+      bload16_lds(pc < NP && part == 0 ? rx : rz, dst, vom[u]);
     }
   };
 
@@ -383,6 +409,20 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
   for (int t = 0; t < MT; ++t) arow[t] = 32 * MT * wm + 32 * t + j;
 #pragma unroll
   for (int t = 0; t < NT; ++t) brow[t] = 32 * NT * wn + 32 * t + j;
+  // This lane's LDS offsets inside a stage, so that every read of a step adds
+  // only a constant to one of them.  Activation fragment (unit L, dword b,
+  // tile mt): row arow[mt] = arow[0] + 32 mt, chunk (8 L + cin) ^ (row & 7) =
+  // 8 L + (cin ^ (j & 7)), cin the 8-input chunk that matches dword b of this
+  // lane half.  Weight dwords (unit L, tile nt): row brow[0] + 32 nt, chunk
+  // (2 L + h) ^ ((j >> 1) & 3).
+  int aofs[4], wofs[2];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int cin = GB == 1 && !MX ? 4 * (b >> 1) + 2 * h + (b & 1) : 4 * h + b;
+    aofs[b] = arow[0] * 256 + 16 * (cin ^ (j & 7));
+  }
+#pragma unroll
+  for (int L = 0; L < 2; ++L) wofs[L] = brow[0] * 64 + 16 * ((2 * L + h) ^ ((j >> 1) & 3));
 
   // zero-point operands carried from an even step to the next (one piece per step)
   float zpa[MT] = {}, zpb[NT] = {};
@@ -449,9 +489,7 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
     for (int L = 0; L < 2; ++L)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const int row = brow[nt];
-        const int c = (2 * L + h) ^ ((row >> 1) & 3);
-        u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + kABytes + row * 64 + 16 * c);
+        u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + kABytes + wofs[L] + 2048 * nt);
         if constexpr (S16) v ^= u32x4_t{kSignFlip, kSignFlip, kSignFlip, kSignFlip};
         bd[L][nt][0] = v[0]; bd[L][nt][1] = v[1]; bd[L][nt][2] = v[2]; bd[L][nt][3] = v[3];
         if constexpr (GB == 1 && !MX) {
@@ -467,14 +505,9 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
       }
     auto load_af = [&](int blk, bf16x8_t (&af)[MT]) {
       const int L = blk >> 2, b = blk & 3;
-      // 8-input chunk of the activations that matches dword b of this half
-      const int cin = GB == 1 && !MX ? 4 * (b >> 1) + 2 * h + (b & 1) : 4 * h + b;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int row = arow[mt];
-        const int c = (8 * L + cin) ^ (row & 7);
-        af[mt] = *reinterpret_cast<const bf16x8_t*>(st + row * 256 + 16 * c);
-      }
+      for (int mt = 0; mt < MT; ++mt)
+        af[mt] = *reinterpret_cast<const bf16x8_t*>(st + aofs[b] + 128 * L + 8192 * mt);
     };
     // Fold of one group piece, acc += scale * sum (the zero-point part is added
     // by correct()), deferred to the first block of the next piece: there the
