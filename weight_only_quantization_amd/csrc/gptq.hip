@@ -12,8 +12,9 @@
 // * The upper Cholesky factor U of H^-1 (H^-1 = U^T U) without forming H^-1:
 //   with J the reversal permutation, J H J = L L^T (lower Cholesky) gives
 //   H = (J L J)(J L J)^T, so U = (J L J)^-1 = J L^-1 J.  A right-looking
-//   Cholesky and triangular inverse in panels of 32 columns: two small launches
-//   per column inside the panel, one tiled float64 update of the rest per panel.
+//   Cholesky and triangular inverse in panels of 32 columns: one launch works
+//   through a panel column by column, one tiled float64 update applies it to
+//   the rest.
 // * The sweep is independent for every output row: a row's codes, scales and
 //   updates use only its own weights and the shared U.  Per block of whole
 //   groups (at least 128 columns), one thread per row keeps the block's weights
@@ -119,64 +120,154 @@ __global__ __launch_bounds__(256) void gptq_weights_kernel(const float* __restri
   }
 }
 
-// Cholesky, column j: A[i][j] /= sqrt(A[j][j]) below the diagonal, the root to
-// dg[j] (A[j][j] itself is read by every thread and left alone).  A pivot that
-// is not positive, or a root that is not finite, means the damped matrix is
-// not positive definite: bit 1 of *flag.
-__global__ __launch_bounds__(256) void gptq_chol_col_kernel(double* __restrict__ a, int64_t k, int64_t j,
-                                                            double* __restrict__ dg, uint32_t* __restrict__ flag) {
-  const int64_t i = j + 1 + (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const double pv = a[j * k + j];
-  const double d = sqrt(pv);
-  if (i < k) a[i * k + j] /= d;
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    dg[j] = d;
-    if (!(pv > 0.0) || !(d <= DBL_MAX)) atomicOr(flag, 2u);
-  }
-}
-
-// Cholesky, the rest of column j's panel: A[i][c] -= A[i][j] A[c][j] for
-// j < c < cend, c <= i (every row below; the later columns wait for the panel's
-// trailing update).
-__global__ __launch_bounds__(256) void gptq_chol_update_kernel(double* __restrict__ a, int64_t k, int64_t j,
-                                                               int64_t cend) {
-  const int64_t rows = k - j - 1, w = cend - j - 1;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < rows * w; e += (int64_t)gridDim.x * 256) {
-    const int64_t i = j + 1 + e / w, c = j + 1 + e % w;
-    if (c <= i) a[i * k + c] -= a[i * k + j] * a[c * k + j];
-  }
-}
-
 // Panel of columns [j0, j0 + b) done: A[i][c] -= A[i][t] A[c][t] for t = j0 .. j0+b-1
 // in order, for i, c >= j0 + b.  64 x 64 tiles on and below the diagonal (the
 // part of a diagonal tile above it is updated too and never read); the panel's
-// rows of both tiles staged in LDS.
+// rows of both tiles pass through LDS kChunk columns at a time while every
+// entry stays in a register.
 constexpr int kPanel = 32;
+constexpr int kChunk = 32;
 
 __global__ __launch_bounds__(256) void gptq_chol_trail_kernel(double* __restrict__ a, int64_t k, int64_t j0,
                                                               int32_t b) {
   if (blockIdx.x > blockIdx.y) return;   // above the diagonal
-  __shared__ double pi[64][kPanel + 1];
-  __shared__ double pc[64][kPanel + 1];
+  __shared__ double pi[64][kChunk + 1];
+  __shared__ double pc[64][kChunk + 1];
   const int64_t base = j0 + b;
   const int64_t i0 = base + (int64_t)blockIdx.y * 64, c0 = base + (int64_t)blockIdx.x * 64;
-  for (int e = threadIdx.x; e < 64 * kPanel; e += 256) {
-    const int r = e / kPanel, t = e % kPanel;
-    pi[r][t] = (i0 + r < k && t < b) ? a[(i0 + r) * k + j0 + t] : 0.0;
-    pc[r][t] = (c0 + r < k && t < b) ? a[(c0 + r) * k + j0 + t] : 0.0;
-  }
-  __syncthreads();
   const int ti = threadIdx.x / 16, tc = threadIdx.x % 16;
+  double acc[4][4];
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t i = i0 + 4 * ti + u, c = c0 + 4 * tc + v;
-      if (i >= k || c >= k) continue;
-      double acc = a[i * k + c];
-      for (int t = 0; t < b; ++t) acc -= pi[4 * ti + u][t] * pc[4 * tc + v][t];
-      a[i * k + c] = acc;
+      acc[u][v] = (i < k && c < k) ? a[i * k + c] : 0.0;
     }
+  for (int t0 = 0; t0 < b; t0 += kChunk) {
+    const int nt = min(kChunk, b - t0);
+    for (int e = threadIdx.x; e < 64 * kChunk; e += 256) {
+      const int r = e / kChunk, t = e % kChunk;
+      pi[r][t] = (i0 + r < k && t < nt) ? a[(i0 + r) * k + j0 + t0 + t] : 0.0;
+      pc[r][t] = (c0 + r < k && t < nt) ? a[(c0 + r) * k + j0 + t0 + t] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        for (int t = 0; t < nt; ++t) acc[u][v] -= pi[4 * ti + u][t] * pc[4 * tc + v][t];
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t i = i0 + 4 * ti + u, c = c0 + 4 * tc + v;
+      if (i < k && c < k) a[i * k + c] = acc[u][v];
+    }
+}
+
+// Cholesky, a whole panel of columns [j0, j0 + b) in one launch (b <= kPanel):
+// for j = j0 .. j0+b-1 in order, A[i][j] /= sqrt(A[j][j]) for i > j, then
+// A[i][c] -= A[i][j] A[c][j] for j < c < j0 + b, c <= i; one thread per row
+// i >= j0.  The values A[c][j] of the panel's own b rows are what every row
+// needs, so each workgroup factors that b x b block in LDS itself (the same
+// operations in the same order in every workgroup, hence the same values), and
+// workgroup 0 writes it back with the roots.  Every entry takes the same
+// operations in the same order as column by column.
+__global__ __launch_bounds__(256) void gptq_chol_panel_kernel(double* __restrict__ a, int64_t k, int64_t j0,
+                                                              int32_t b, double* __restrict__ dg,
+                                                              uint32_t* __restrict__ flag) {
+  __shared__ double blk[kPanel][kPanel + 1];   // blk[r][c] = A[j0 + r][j0 + c], c <= r
+  __shared__ double root[kPanel];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < kPanel * kPanel; e += 256) {
+    const int r = e / kPanel, c = e % kPanel;
+    blk[r][c] = (r < b && c <= r) ? a[(j0 + r) * k + j0 + c] : 0.0;
+  }
+  // this thread's row below the block: its b panel entries
+  const int64_t i = j0 + b + (int64_t)blockIdx.x * 256 + tid;
+  const bool mine = i < k;
+  double v[kPanel];
+#pragma unroll
+  for (int c = 0; c < kPanel; ++c) v[c] = (mine && c < b) ? a[i * k + j0 + c] : 0.0;
+  __syncthreads();
+  for (int j = 0; j < b; ++j) {
+    // the block's column j (threads 0 .. b-1 own its rows)
+    if (tid == 0) {
+      const double pv = blk[j][j];
+      const double d = sqrt(pv);
+      root[j] = d;
+      if (blockIdx.x == 0) {
+        dg[j0 + j] = d;
+        if (!(pv > 0.0) || !(d <= DBL_MAX)) atomicOr(flag, 2u);
+      }
+    }
+    __syncthreads();
+    const double d = root[j];
+    if (tid > j && tid < b) blk[tid][j] /= d;
+    __syncthreads();
+    if (tid > j && tid < b)
+      for (int c = j + 1; c <= tid; ++c) blk[tid][c] -= blk[tid][j] * blk[c][j];
+    // this thread's row: the same two operations against the block's column j
+#pragma unroll
+    for (int jj = 0; jj < kPanel; ++jj) {
+      if (jj != j) continue;
+      v[jj] /= d;
+#pragma unroll
+      for (int c = jj + 1; c < kPanel; ++c)
+        if (c < b) v[c] -= v[jj] * blk[c][jj];
+    }
+    __syncthreads();
+  }
+  if (mine) {
+#pragma unroll
+    for (int c = 0; c < kPanel; ++c)
+      if (c < b) a[i * k + j0 + c] = v[c];
+  }
+  if (blockIdx.x == 0)
+    for (int e = tid; e < kPanel * kPanel; e += 256) {
+      const int r = e / kPanel, c = e % kPanel;
+      if (r < b && c < r) a[(j0 + r) * k + j0 + c] = blk[r][c];
+    }
+}
+
+// Triangular inverse T = L^-1, a whole panel of rows [p0, p0 + b) in one launch:
+// for r = p0 .. p0+b-1 in order, T[r][j] /= L[r][r] for j <= r, then
+// T[i][j] -= L[i][r] T[r][j] for r < i < p0 + b, j <= r; one thread per column
+// j < p0 + b, the column's b panel entries in registers.  Every entry takes the
+// same operations in the same order as row by row.
+__global__ __launch_bounds__(256) void gptq_tri_panel_kernel(double* __restrict__ tm, const double* __restrict__ a,
+                                                             const double* __restrict__ dg, int64_t k, int64_t p0,
+                                                             int32_t b) {
+  __shared__ double lb[kPanel][kPanel + 1];    // lb[i][r] = L[p0 + i][p0 + r], r < i
+  __shared__ double dgs[kPanel];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < kPanel * kPanel; e += 256) {
+    const int i = e / kPanel, r = e % kPanel;
+    lb[i][r] = (i < b && r < i) ? a[(p0 + i) * k + p0 + r] : 0.0;
+  }
+  if (tid < kPanel) dgs[tid] = tid < b ? dg[p0 + tid] : 1.0;
+  const int64_t j = (int64_t)blockIdx.x * 256 + tid;
+  const bool mine = j < p0 + b;
+  double t[kPanel];
+#pragma unroll
+  for (int r = 0; r < kPanel; ++r) t[r] = (mine && r < b) ? tm[(p0 + r) * k + j] : 0.0;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kPanel; ++r) {
+    if (r >= b || j > p0 + r) continue;   // T[p0 + r][j] is final zero above the diagonal
+    t[r] /= dgs[r];
+#pragma unroll
+    for (int i = r + 1; i < kPanel; ++i)
+      if (i < b) t[i] -= lb[i][r] * t[r];
+  }
+  if (mine) {
+#pragma unroll
+    for (int r = 0; r < kPanel; ++r)
+      if (r < b) tm[(p0 + r) * k + j] = t[r];
+  }
 }
 
 __global__ __launch_bounds__(256) void gptq_identity_kernel(double* __restrict__ tm, int64_t k) {
@@ -184,51 +275,47 @@ __global__ __launch_bounds__(256) void gptq_identity_kernel(double* __restrict__
     tm[e] = (e / k == e % k) ? 1.0 : 0.0;
 }
 
-// Triangular inverse T = L^-1 (L: the strictly lower part of A, diagonal dg),
-// row k0 final: T[k0][j] /= L[k0][k0] for j <= k0 ...
-__global__ __launch_bounds__(256) void gptq_tri_row_kernel(double* __restrict__ tm, const double* __restrict__ dg,
-                                                           int64_t k, int64_t k0) {
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (j <= k0) tm[k0 * k + j] /= dg[k0];
-}
-
-// ... and pushed down the rest of its panel: T[i][j] -= L[i][k0] T[k0][j] for
-// k0 < i < rend, j <= k0.
-__global__ __launch_bounds__(256) void gptq_tri_update_kernel(double* __restrict__ tm, const double* __restrict__ a,
-                                                              int64_t k, int64_t k0, int64_t rend) {
-  const int64_t rows = rend - k0 - 1, cols = k0 + 1;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < rows * cols; e += (int64_t)gridDim.x * 256) {
-    const int64_t i = k0 + 1 + e / cols, j = e % cols;
-    tm[i * k + j] -= a[i * k + k0] * tm[k0 * k + j];
-  }
-}
-
 // Panel of rows [p0, p0 + b) final: T[i][j] -= L[i][r] T[r][j] for r = p0 .. p0+b-1
 // in order, for i >= p0 + b, j < p0 + b (T[r][j] is 0 for j > r, which changes
-// nothing).  64 x 64 tiles; L's panel columns and T's panel rows staged in LDS.
+// nothing).  64 x 64 tiles; L's panel columns and T's panel rows pass through
+// LDS kChunk at a time while every entry stays in a register.
 __global__ __launch_bounds__(256) void gptq_tri_trail_kernel(double* __restrict__ tm, const double* __restrict__ a,
                                                              int64_t k, int64_t p0, int32_t b) {
-  __shared__ double li[64][kPanel + 1];
-  __shared__ double tr[kPanel][65];
+  __shared__ double li[64][kChunk + 1];
+  __shared__ double tr[kChunk][65];
   const int64_t pend = p0 + b;
   const int64_t i0 = pend + (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * 64;
-  for (int e = threadIdx.x; e < 64 * kPanel; e += 256) {
-    const int r = e / kPanel, t = e % kPanel;
-    li[r][t] = (i0 + r < k && t < b) ? a[(i0 + r) * k + p0 + t] : 0.0;
-    const int t2 = e / 64, jj = e % 64;
-    tr[t2][jj] = (t2 < b && j0 + jj < pend) ? tm[(p0 + t2) * k + j0 + jj] : 0.0;
-  }
-  __syncthreads();
   const int ti = threadIdx.x / 16, tj = threadIdx.x % 16;
+  double acc[4][4];
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t i = i0 + 4 * ti + u, j = j0 + 4 * tj + v;
-      if (i >= k || j >= pend) continue;
-      double acc = tm[i * k + j];
-      for (int t = 0; t < b; ++t) acc -= li[4 * ti + u][t] * tr[t][4 * tj + v];
-      tm[i * k + j] = acc;
+      acc[u][v] = (i < k && j < pend) ? tm[i * k + j] : 0.0;
+    }
+  for (int t0 = 0; t0 < b; t0 += kChunk) {
+    const int nt = min(kChunk, b - t0);
+    for (int e = threadIdx.x; e < 64 * kChunk; e += 256) {
+      const int r = e / kChunk, t = e % kChunk;
+      li[r][t] = (i0 + r < k && t < nt) ? a[(i0 + r) * k + p0 + t0 + t] : 0.0;
+      const int t2 = e / 64, jj = e % 64;
+      tr[t2][jj] = (t2 < nt && j0 + jj < pend) ? tm[(p0 + t0 + t2) * k + j0 + jj] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        for (int t = 0; t < nt; ++t) acc[u][v] -= li[4 * ti + u][t] * tr[t][4 * tj + v];
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t i = i0 + 4 * ti + u, j = j0 + 4 * tj + v;
+      if (i < k && j < pend) tm[i * k + j] = acc[u][v];
     }
 }
 
@@ -393,12 +480,8 @@ int32_t run_gptq(const float* w, const uint16_t* x, int64_t t, int64_t n, int64_
     // entry takes the same updates in the same order as column by column.
     for (int64_t j0 = 0; j0 < k && st == WOQ_OK; j0 += kPanel) {
       const int64_t jend = std::min<int64_t>(k, j0 + kPanel);
-      for (int64_t j = j0; j < jend; ++j) {
-        hipLaunchKernelGGL(gptq_chol_col_kernel, dim3(flat_grid(k - j)), dim3(256), 0, s, a, k, j, dg, flag);
-        if (j + 1 < jend)
-          hipLaunchKernelGGL(gptq_chol_update_kernel, dim3(flat_grid((k - j - 1) * (jend - j - 1))), dim3(256), 0, s,
-                             a, k, j, jend);
-      }
+      hipLaunchKernelGGL(gptq_chol_panel_kernel, dim3((unsigned)std::max<int64_t>(1, (k - jend + 255) / 256)), dim3(256),
+                         0, s, a, k, j0, (int32_t)(jend - j0), dg, flag);
       if (jend < k) {
         const unsigned t = (unsigned)((k - jend + 63) / 64);
         hipLaunchKernelGGL(gptq_chol_trail_kernel, dim3(t, t), dim3(256), 0, s, a, k, j0, (int32_t)(jend - j0));
@@ -411,12 +494,8 @@ int32_t run_gptq(const float* w, const uint16_t* x, int64_t t, int64_t n, int64_
     if (st == WOQ_OK && (hflag & 2u)) st = WOQ_ENOTPD;
     for (int64_t p0 = 0; p0 < k && st == WOQ_OK; p0 += kPanel) {
       const int64_t pend = std::min<int64_t>(k, p0 + kPanel);
-      for (int64_t k0 = p0; k0 < pend; ++k0) {
-        hipLaunchKernelGGL(gptq_tri_row_kernel, dim3(flat_grid(k0 + 1)), dim3(256), 0, s, tm, dg, k, k0);
-        if (k0 + 1 < pend)
-          hipLaunchKernelGGL(gptq_tri_update_kernel, dim3(flat_grid((pend - k0 - 1) * (k0 + 1))), dim3(256), 0, s, tm,
-                             a, k, k0, pend);
-      }
+      hipLaunchKernelGGL(gptq_tri_panel_kernel, dim3((unsigned)((pend + 255) / 256)), dim3(256), 0, s, tm, a, dg, k, p0,
+                         (int32_t)(pend - p0));
       if (pend < k)
         hipLaunchKernelGGL(gptq_tri_trail_kernel, dim3((unsigned)((pend + 63) / 64), (unsigned)((k - pend + 63) / 64)),
                            dim3(256), 0, s, tm, a, k, p0, (int32_t)(pend - p0));
