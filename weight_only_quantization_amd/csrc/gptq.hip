@@ -121,49 +121,58 @@ __global__ __launch_bounds__(256) void gptq_weights_kernel(const float* __restri
 }
 
 // Panel of columns [j0, j0 + b) done: A[i][c] -= A[i][t] A[c][t] for t = j0 .. j0+b-1
-// in order, for i, c >= j0 + b.  64 x 64 tiles on and below the diagonal (the
-// part of a diagonal tile above it is updated too and never read); the panel's
-// rows of both tiles pass through LDS kChunk columns at a time while every
-// entry stays in a register.
+// in order, for i, c >= j0 + b.  kTT x kTT tiles on and below the diagonal (the
+// part of a diagonal tile above it is updated too and never read), 8 x 8
+// entries a thread, held in registers; the panel's rows of both tiles pass
+// through LDS kChunk columns at a time (the column tile's rows stored as
+// 16 v + tc for row 8 tc + v, so the 16 threads of a row group read distinct
+// banks).
 constexpr int kPanel = 32;
-constexpr int kChunk = 32;
+constexpr int kChunk = 16;
+constexpr int kTT = 128;
 
 __global__ __launch_bounds__(256) void gptq_chol_trail_kernel(double* __restrict__ a, int64_t k, int64_t j0,
                                                               int32_t b) {
   if (blockIdx.x > blockIdx.y) return;   // above the diagonal
-  __shared__ double pi[64][kChunk + 1];
-  __shared__ double pc[64][kChunk + 1];
+  __shared__ double pi[kTT][kChunk + 1];
+  __shared__ double pc[kTT][kChunk + 1];
   const int64_t base = j0 + b;
-  const int64_t i0 = base + (int64_t)blockIdx.y * 64, c0 = base + (int64_t)blockIdx.x * 64;
+  const int64_t i0 = base + (int64_t)blockIdx.y * kTT, c0 = base + (int64_t)blockIdx.x * kTT;
   const int ti = threadIdx.x / 16, tc = threadIdx.x % 16;
-  double acc[4][4];
+  double acc[8][8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < 8; ++u)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t i = i0 + 4 * ti + u, c = c0 + 4 * tc + v;
+    for (int v = 0; v < 8; ++v) {
+      const int64_t i = i0 + 8 * ti + u, c = c0 + 8 * tc + v;
       acc[u][v] = (i < k && c < k) ? a[i * k + c] : 0.0;
     }
   for (int t0 = 0; t0 < b; t0 += kChunk) {
     const int nt = min(kChunk, b - t0);
-    for (int e = threadIdx.x; e < 64 * kChunk; e += 256) {
+    for (int e = threadIdx.x; e < kTT * kChunk; e += 256) {
       const int r = e / kChunk, t = e % kChunk;
       pi[r][t] = (i0 + r < k && t < nt) ? a[(i0 + r) * k + j0 + t0 + t] : 0.0;
-      pc[r][t] = (c0 + r < k && t < nt) ? a[(c0 + r) * k + j0 + t0 + t] : 0.0;
+      pc[(r % 8) * 16 + r / 8][t] = (c0 + r < k && t < nt) ? a[(c0 + r) * k + j0 + t0 + t] : 0.0;
     }
     __syncthreads();
+    for (int t = 0; t < nt; ++t) {
+      double x[8], y[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 8; ++u) x[u] = pi[8 * ti + u][t];
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        for (int t = 0; t < nt; ++t) acc[u][v] -= pi[4 * ti + u][t] * pc[4 * tc + v][t];
+      for (int v = 0; v < 8; ++v) y[v] = pc[16 * v + tc][t];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) acc[u][v] -= x[u] * y[v];
+    }
     __syncthreads();
   }
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < 8; ++u)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t i = i0 + 4 * ti + u, c = c0 + 4 * tc + v;
+    for (int v = 0; v < 8; ++v) {
+      const int64_t i = i0 + 8 * ti + u, c = c0 + 8 * tc + v;
       if (i < k && c < k) a[i * k + c] = acc[u][v];
     }
 }
@@ -277,44 +286,51 @@ __global__ __launch_bounds__(256) void gptq_identity_kernel(double* __restrict__
 
 // Panel of rows [p0, p0 + b) final: T[i][j] -= L[i][r] T[r][j] for r = p0 .. p0+b-1
 // in order, for i >= p0 + b, j < p0 + b (T[r][j] is 0 for j > r, which changes
-// nothing).  64 x 64 tiles; L's panel columns and T's panel rows pass through
-// LDS kChunk at a time while every entry stays in a register.
+// nothing).  kTT x kTT tiles, 8 x 8 entries a thread in registers; L's panel
+// columns and T's panel rows pass through LDS kChunk at a time (T's columns
+// stored as 16 v + tj for column 8 tj + v, as in the factor's update).
 __global__ __launch_bounds__(256) void gptq_tri_trail_kernel(double* __restrict__ tm, const double* __restrict__ a,
                                                              int64_t k, int64_t p0, int32_t b) {
-  __shared__ double li[64][kChunk + 1];
-  __shared__ double tr[kChunk][65];
+  __shared__ double li[kTT][kChunk + 1];
+  __shared__ double tr[kChunk][kTT + 1];
   const int64_t pend = p0 + b;
-  const int64_t i0 = pend + (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * 64;
+  const int64_t i0 = pend + (int64_t)blockIdx.y * kTT, j0 = (int64_t)blockIdx.x * kTT;
   const int ti = threadIdx.x / 16, tj = threadIdx.x % 16;
-  double acc[4][4];
+  double acc[8][8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < 8; ++u)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t i = i0 + 4 * ti + u, j = j0 + 4 * tj + v;
+    for (int v = 0; v < 8; ++v) {
+      const int64_t i = i0 + 8 * ti + u, j = j0 + 8 * tj + v;
       acc[u][v] = (i < k && j < pend) ? tm[i * k + j] : 0.0;
     }
   for (int t0 = 0; t0 < b; t0 += kChunk) {
     const int nt = min(kChunk, b - t0);
-    for (int e = threadIdx.x; e < 64 * kChunk; e += 256) {
+    for (int e = threadIdx.x; e < kTT * kChunk; e += 256) {
       const int r = e / kChunk, t = e % kChunk;
       li[r][t] = (i0 + r < k && t < nt) ? a[(i0 + r) * k + p0 + t0 + t] : 0.0;
-      const int t2 = e / 64, jj = e % 64;
-      tr[t2][jj] = (t2 < nt && j0 + jj < pend) ? tm[(p0 + t0 + t2) * k + j0 + jj] : 0.0;
+      const int t2 = e / kTT, jj = e % kTT;
+      tr[t2][(jj % 8) * 16 + jj / 8] = (t2 < nt && j0 + jj < pend) ? tm[(p0 + t0 + t2) * k + j0 + jj] : 0.0;
     }
     __syncthreads();
+    for (int t = 0; t < nt; ++t) {
+      double x[8], y[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 8; ++u) x[u] = li[8 * ti + u][t];
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        for (int t = 0; t < nt; ++t) acc[u][v] -= li[4 * ti + u][t] * tr[t][4 * tj + v];
+      for (int v = 0; v < 8; ++v) y[v] = tr[t][16 * v + tj];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) acc[u][v] -= x[u] * y[v];
+    }
     __syncthreads();
   }
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < 8; ++u)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t i = i0 + 4 * ti + u, j = j0 + 4 * tj + v;
+    for (int v = 0; v < 8; ++v) {
+      const int64_t i = i0 + 8 * ti + u, j = j0 + 8 * tj + v;
       if (i < k && j < pend) tm[i * k + j] = acc[u][v];
     }
 }
@@ -483,7 +499,7 @@ int32_t run_gptq(const float* w, const uint16_t* x, int64_t t, int64_t n, int64_
       hipLaunchKernelGGL(gptq_chol_panel_kernel, dim3((unsigned)std::max<int64_t>(1, (k - jend + 255) / 256)), dim3(256),
                          0, s, a, k, j0, (int32_t)(jend - j0), dg, flag);
       if (jend < k) {
-        const unsigned t = (unsigned)((k - jend + 63) / 64);
+        const unsigned t = (unsigned)((k - jend + kTT - 1) / kTT);
         hipLaunchKernelGGL(gptq_chol_trail_kernel, dim3(t, t), dim3(256), 0, s, a, k, j0, (int32_t)(jend - j0));
       }
       st = hip_status(hipGetLastError());
@@ -497,7 +513,7 @@ int32_t run_gptq(const float* w, const uint16_t* x, int64_t t, int64_t n, int64_
       hipLaunchKernelGGL(gptq_tri_panel_kernel, dim3((unsigned)((pend + 255) / 256)), dim3(256), 0, s, tm, a, dg, k, p0,
                          (int32_t)(pend - p0));
       if (pend < k)
-        hipLaunchKernelGGL(gptq_tri_trail_kernel, dim3((unsigned)((pend + 63) / 64), (unsigned)((k - pend + 63) / 64)),
+        hipLaunchKernelGGL(gptq_tri_trail_kernel, dim3((unsigned)((pend + kTT - 1) / kTT), (unsigned)((k - pend + kTT - 1) / kTT)),
                            dim3(256), 0, s, tm, a, k, p0, (int32_t)(pend - p0));
       st = hip_status(hipGetLastError());
     }
