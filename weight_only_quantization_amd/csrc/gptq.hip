@@ -12,7 +12,7 @@
 // * The upper Cholesky factor U of H^-1 (H^-1 = U^T U) without forming H^-1:
 //   with J the reversal permutation, J H J = L L^T (lower Cholesky) gives
 //   H = (J L J)(J L J)^T, so U = (J L J)^-1 = J L^-1 J.  A right-looking
-//   Cholesky and triangular inverse in panels of 32 columns: one launch works
+//   Cholesky and triangular inverse in panels of 64 columns: one launch works
 //   through a panel column by column, one tiled float64 update applies it to
 //   the rest.
 // * The sweep is independent for every output row: a row's codes, scales and
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void gptq_weights_kernel(const float* __restri
 // through LDS kChunk columns at a time (the column tile's rows stored as
 // 16 v + tc for row 8 tc + v, so the 16 threads of a row group read distinct
 // banks).
-constexpr int kPanel = 32;
+constexpr int kPanel = 64;
 constexpr int kChunk = 16;
 constexpr int kTT = 128;
 
@@ -202,7 +202,9 @@ __global__ __launch_bounds__(256) void gptq_chol_panel_kernel(double* __restrict
 #pragma unroll
   for (int c = 0; c < kPanel; ++c) v[c] = (mine && c < b) ? a[i * k + j0 + c] : 0.0;
   __syncthreads();
-  for (int j = 0; j < b; ++j) {
+#pragma unroll
+  for (int j = 0; j < kPanel; ++j) {
+    if (j >= b) continue;   // uniform
     // the block's column j (threads 0 .. b-1 own its rows)
     if (tid == 0) {
       const double pv = blk[j][j];
@@ -220,14 +222,10 @@ __global__ __launch_bounds__(256) void gptq_chol_panel_kernel(double* __restrict
     if (tid > j && tid < b)
       for (int c = j + 1; c <= tid; ++c) blk[tid][c] -= blk[tid][j] * blk[c][j];
     // this thread's row: the same two operations against the block's column j
+    v[j] /= d;
 #pragma unroll
-    for (int jj = 0; jj < kPanel; ++jj) {
-      if (jj != j) continue;
-      v[jj] /= d;
-#pragma unroll
-      for (int c = jj + 1; c < kPanel; ++c)
-        if (c < b) v[c] -= v[jj] * blk[c][jj];
-    }
+    for (int c = j + 1; c < kPanel; ++c)
+      if (c < b) v[c] -= v[j] * blk[c][j];
     __syncthreads();
   }
   if (mine) {
