@@ -17,9 +17,9 @@
 //   the rest.
 // * The sweep is independent for every output row: a row's codes, scales and
 //   updates use only its own weights and the shared U.  Per block of whole
-//   groups (at least 128 columns), one thread per row keeps the block's weights
-//   in LDS, takes a group's (scale, zero) from its current columns when the
-//   group starts, codes each column, and subtracts err * U from the rest of the
+//   groups (at least 128 columns), four lanes per row keep the block's weights
+//   in LDS, take a group's (scale, zero) from its current columns when the
+//   group starts, code each column, and subtract err * U from the rest of the
 //   block, err = (w - dequant) / U_ii; a second kernel applies the block's
 //   errors to every later column.  Every weight takes its updates one at a time
 //   in column order, each product rounded before the subtraction.
@@ -35,7 +35,7 @@
 namespace woq {
 namespace {
 
-constexpr int kSweepRows = 64;        // sweep: one thread per row
+constexpr int kSweepRows = 16;        // sweep: rows per workgroup, four lanes a row
 constexpr int kSweepMinCols = 128;    // columns per sweep block: whole groups, at least this many
 constexpr int kSweepMaxCols = 256;
 
@@ -338,52 +338,68 @@ __device__ __forceinline__ double u_at(const double* __restrict__ tm, int64_t k,
   return tm[(k - 1 - i) * k + (k - 1 - j)];
 }
 
-// Sweep of columns [c0, c0 + nb) (whole groups) for rows [64 b, 64 b + 64).  The
+// Sweep of columns [c0, c0 + nb) (whole groups) for rows [16 b, 16 b + 16), four
+// lanes a row: lane share p holds the row's block columns j with j % 4 == p (in
+// LDS) and applies every update to them.  Column i's owner (share i % 4) codes
+// it and passes its error to the row's other lanes; a group's min and max are
+// each lane's over its columns, then over the four (exact, in any order).  The
 // group rule is the asymmetric quantizer's: d = max - min over the group's
 // current columns, scale = float32(d / 15), zero = clamp(rint(-15 min / d), 0, 15),
 // codes clamp(rint(15 w / d) + zero, 0, 15); a flat group (d = 0) takes scale 1,
-// zero clamp(rint(-min), 0, 15) and codes clamp(rint(w) + zero, 0, 15).
-__global__ __launch_bounds__(kSweepRows) void gptq_sweep_kernel(double* __restrict__ wc, const double* __restrict__ tm,
-                                                                int64_t n, int64_t k, int32_t group, int64_t c0,
-                                                                int32_t nb, uint8_t* __restrict__ q,
-                                                                float* __restrict__ scale, uint8_t* __restrict__ zero,
-                                                                double* __restrict__ err) {
+// zero clamp(rint(-min), 0, 15) and codes clamp(rint(w) + zero, 0, 15).  Every
+// entry takes its updates one at a time in column order, as with one thread a row.
+__global__ __launch_bounds__(4 * kSweepRows) void gptq_sweep_kernel(double* __restrict__ wc, const double* __restrict__ tm,
+                                                                    int64_t n, int64_t k, int32_t group, int64_t c0,
+                                                                    int32_t nb, uint8_t* __restrict__ q,
+                                                                    float* __restrict__ scale, uint8_t* __restrict__ zero,
+                                                                    double* __restrict__ err) {
   extern __shared__ double vals[];   // [nb][kSweepRows]
-  const int tid = threadIdx.x;
-  const int64_t row = (int64_t)blockIdx.x * kSweepRows + tid;
+  const int lane = threadIdx.x;
+  const int rl = lane >> 2, share = lane & 3;
+  const int64_t row = (int64_t)blockIdx.x * kSweepRows + rl;
   const bool live = row < n;
-  for (int i = 0; i < nb; ++i) vals[i * kSweepRows + tid] = live ? wc[(c0 + i) * n + row] : 0.0;
+  for (int j = share; j < nb; j += 4) vals[j * kSweepRows + rl] = live ? wc[(c0 + j) * n + row] : 0.0;
   const int64_t ng = k / group;
   double d_safe = 1.0, zr = 0.0, sc = 1.0;
   bool flat = true;
   for (int i = 0; i < nb; ++i) {
     const int64_t c = c0 + i;
     if (c % group == 0) {
-      double mn = vals[i * kSweepRows + tid], mx = mn;
-      for (int e = 1; e < group; ++e) {
-        const double v = vals[(i + e) * kSweepRows + tid];
+      // this lane's columns of the group (none for a lane past a group of 2)
+      double mn = INFINITY, mx = -INFINITY;
+      for (int j = i + ((share - i) & 3); j < i + group; j += 4) {
+        const double v = vals[j * kSweepRows + rl];
         mn = fmin(mn, v);
         mx = fmax(mx, v);
       }
+      mn = fmin(mn, __shfl_xor(mn, 1));
+      mx = fmax(mx, __shfl_xor(mx, 1));
+      mn = fmin(mn, __shfl_xor(mn, 2));
+      mx = fmax(mx, __shfl_xor(mx, 2));
       const double d = mx - mn;
       flat = d == 0.0;
       d_safe = flat ? 1.0 : d;
       sc = flat ? 1.0 : (double)(float)(d / 15.0);
       zr = fmin(fmax(__builtin_rint(flat ? -mn : (-15.0 * mn) / d_safe), 0.0), 15.0);
-      if (live) {
+      if (live && share == 0) {
         scale[row * ng + c / group] = (float)sc;
         zero[row * ng + c / group] = (uint8_t)zr;
       }
     }
-    const double v = vals[i * kSweepRows + tid];
-    const double r = __builtin_rint(flat ? v : (15.0 * v) / d_safe);
-    const double qi = fmin(fmax(r + zr, 0.0), 15.0);
-    const double e = (v - (qi - zr) * sc) / u_at(tm, k, c, c);
-    if (live) {
-      q[row * k + c] = (uint8_t)qi;
-      err[(int64_t)i * n + row] = e;
+    const int owner = i & 3;
+    double e = 0.0;
+    if (share == owner) {
+      const double v = vals[i * kSweepRows + rl];
+      const double r = __builtin_rint(flat ? v : (15.0 * v) / d_safe);
+      const double qi = fmin(fmax(r + zr, 0.0), 15.0);
+      e = (v - (qi - zr) * sc) / u_at(tm, k, c, c);
+      if (live) {
+        q[row * k + c] = (uint8_t)qi;
+        err[(int64_t)i * n + row] = e;
+      }
     }
-    for (int j = i + 1; j < nb; ++j) vals[j * kSweepRows + tid] -= e * u_at(tm, k, c, c0 + j);
+    e = __shfl(e, (lane & ~3) | owner);
+    for (int j = i + 1 + ((share - i - 1) & 3); j < nb; j += 4) vals[j * kSweepRows + rl] -= e * u_at(tm, k, c, c0 + j);
   }
 }
 
@@ -517,7 +533,7 @@ int32_t run_gptq(const float* w, const uint16_t* x, int64_t t, int64_t n, int64_
     }
     for (int64_t c0 = 0; c0 < k && st == WOQ_OK; c0 += bcols) {
       const int32_t nb = (int32_t)std::min<int64_t>(bcols, k - c0);
-      hipLaunchKernelGGL(gptq_sweep_kernel, dim3((unsigned)((n + kSweepRows - 1) / kSweepRows)), dim3(kSweepRows),
+      hipLaunchKernelGGL(gptq_sweep_kernel, dim3((unsigned)((n + kSweepRows - 1) / kSweepRows)), dim3(4 * kSweepRows),
                          (size_t)nb * kSweepRows * sizeof(double), s, wc, tm, n, k, group, c0, nb, q, scale, zero,
                          err);
       if (c0 + nb < k) {
