@@ -734,8 +734,14 @@ def main():
 
     prefill = None if args.no_prefill else measure_prefill(torch, woq)
     configs = None if args.no_configs else measure_configs(torch, woq)
-    sym16 = mxfp4 = zp4 = midsize = None
+    sym16 = mxfp4 = zp4 = midsize = smallbatch = None
     if not args.no_configs:
+        from workloads import SMALLBATCH
+        smallbatch = dict(
+            note="M = 16 and 64 on the decode shapes: layers under 800 tiles of 16 rows run on the small-M path "
+                 "with the activation slice in LDS (K split over workgroups, partials summed in order), "
+                 "14336x4096 on the small-M kernel",
+            configs=measure_configs(torch, woq, cases=SMALLBATCH))
         from workloads import MIDSIZE
         midsize = dict(
             note="M = 128 and 256 on the decode shapes: the tiled GEMM, its K split over workgroups where the "
@@ -768,7 +774,7 @@ def main():
                     graph=not args.no_graph, accumulate="f32",
                     tokens_per_s_linears_only=round(1.0 / (ms_per_step * 1e-3), 1) if args.layers == 32 else None),
         roofline=roofline, grouped=grouped, prepared=prepared, prefill=prefill, configs=configs,
-        sym16=sym16, mxfp4=mxfp4, zp4=zp4, midsize=midsize,
+        sym16=sym16, mxfp4=mxfp4, zp4=zp4, smallbatch=smallbatch, midsize=midsize,
         cpu_baseline=cpu,
     )
     print(json.dumps(line), flush=True)

@@ -81,7 +81,9 @@ int main(void) {
          WOQ_EWORKSPACE);
   EXPECT(woq_linear_int4_groups(a16, 200, a16, a16, a16, NULL, NULL, 64, 256, 32, 1, a16, a16, 16, NULL),
          WOQ_EWORKSPACE);
-  EXPECT(woq_linear_int4_groups(a16, 48, a16, a16, a16, NULL, NULL, 64, 256, 32, 1, a16, a16, 16, NULL),
+  EXPECT(woq_linear_int4_groups(a16, 48, a16, a16, a16, NULL, NULL, 64, 4096, 32, 1, a16, a16, 16, NULL),
+         WOQ_EWORKSPACE);   /* the small-M path's K-range partials need their buffer */
+  EXPECT(woq_linear_int4_groups(a16, 48, a16, a16, a16, NULL, NULL, 14336, 256, 32, 1, a16, a16, 16, NULL),
          WOQ_EWORKSPACE);   /* the small-M fragment pre-pass needs its buffer */
   EXPECT(woq_linear_int4_groups(NULL, 0, NULL, NULL, NULL, NULL, NULL, 64, 256, 32, 1, NULL, NULL, 0, NULL),
          WOQ_OK);

@@ -51,14 +51,40 @@ def test_status_strings(lib):
     (1, 8192, 28672, 128, "rows_dot2"), (1, 64, 40960, 128, "skinny_mfma"),
     (2, 4096, 32768, 64, "rows_dot2"), (1, 4096, 32800, 32, "skinny_mfma"),
     (5, 4096, 4096, 128, "skinny_mfma"), (16, 14336, 4096, 32, "skinny_mfma"),
-    (17, 4096, 4096, 128, "skinny_mfma"), (32, 14336, 4096, 256, "skinny_mfma"),
-    (33, 4096, 4096, 128, "skinny_mfma"), (64, 14336, 4096, 32, "skinny_mfma"),
+    (17, 4096, 4096, 128, "smallm_lds"), (32, 14336, 4096, 256, "skinny_mfma"),
+    (33, 4096, 4096, 128, "smallm_lds"), (64, 14336, 4096, 32, "skinny_mfma"),
+    (15, 4096, 14336, 128, "skinny_mfma"), (16, 4096, 14336, 128, "smallm_lds"),
+    (64, 4096, 14336, 256, "smallm_lds"), (64, 4096, 14336, 32, "skinny_mfma"),
+    (48, 1024, 4096, 128, "smallm_lds"), (16, 12800, 4096, 128, "skinny_mfma"),
     (65, 4096, 4096, 128, "gemm_mfma"), (128, 14336, 4096, 32, "skinny_mfma"),
     (128, 4096, 14336, 128, "gemm_mfma"), (129, 14336, 4096, 128, "gemm_mfma"), (2048, 14336, 4096, 128, "gemm_mfma"),
     (0, 64, 256, 32, "none"), (3, 64, 0, 32, "bias_fill"),
 ])
 def test_plan_paths(m, n, k, g, path):
     assert f"path={path}" in woq.linear_plan(m, n, k, g)
+
+
+def test_plan_smallm_lds(monkeypatch):
+    # 16..64 rows on layers under 800 tiles of 16 rows: 8-step K ranges from K = 8192
+    # (two tiles a wave above 32 rows), else 4; the partial buffer is workspace
+    for (m, n, k, g), (t, s, r) in (((16, 4096, 14336, 128), (1, 8, 14)), ((64, 4096, 14336, 128), (2, 8, 14)),
+                                    ((32, 4096, 14336, 32), (1, 8, 14)), ((24, 4096, 4096, 128), (1, 4, 8)),
+                                    ((64, 1024, 4160, 64), (1, 4, 9))):
+        plan = woq.linear_plan(m, n, k, g)
+        assert f"path=smallm_lds act_tiles={1 if m <= 16 else (2 if m <= 32 else 4)} " in plan, plan
+        assert f"weight_tiles_per_wave={t} waves=8 steps_per_range={s} k_ranges={r} " in plan, plan
+        part = r * m * n * 4
+        assert woq.linear_workspace_bytes(m, n, k, g, False) == (part + 255) // 256 * 256
+        xg = (m * k * 2 + 255) // 256 * 256
+        assert woq.linear_workspace_bytes(m, n, k, g, True) == xg + (part + 255) // 256 * 256
+    # tuning aids: "0" keeps calls off the path, "T,S" forces a shape from 5 rows up
+    monkeypatch.setenv("WOQ_SM", "0")
+    assert "path=skinny_mfma" in woq.linear_plan(16, 4096, 14336, 128)
+    monkeypatch.setenv("WOQ_SM", "2,4")
+    plan = woq.linear_plan(5, 14336, 4096, 128)
+    assert "path=smallm_lds" in plan and "weight_tiles_per_wave=2 waves=8 steps_per_range=4 k_ranges=8" in plan
+    monkeypatch.setenv("WOQ_SM", "2,8")   # two tiles of 8-step ranges at 64 rows and group 32: LDS too small
+    assert "path=smallm_lds" not in woq.linear_plan(64, 4096, 14336, 32)
 
 
 def test_plan_decode_kernels(monkeypatch):

@@ -2,7 +2,9 @@
 
 Each case runs on the row-streaming decode path (m <= 4), the tile GEMV
 (m <= 4 with WOQ_DECODE_MFMA), the small-M MFMA path (5 <= m <= 64, and
-m = 100 with its launch shape forced) and the tiled GEMM (m > 64), and is
+m = 100 with its launch shape forced), the small-M path with the activation
+slice in LDS (16 <= m <= 64 on narrow layers, and m = 5 with its launch shape
+forced) and the tiled GEMM (m > 64), and is
 compared with the float64 oracle to the same
 gate as every other parity test:
 
@@ -36,12 +38,15 @@ pytestmark = pytest.mark.gpu
 PATHS = {
     "rows": [(1, 300, 2048, 128, {}), (3, 100, 1536, 64, {})],
     "gemv": [(1, 300, 2048, 128, {"WOQ_DECODE_MFMA": "1"}), (4, 100, 1024, 32, {"WOQ_DECODE_MFMA": "1"})],
-    "skinny": [(16, 200, 2048, 128, {}), (7, 64, 1024, 32, {}), (64, 300, 1024, 128, {}),
+    "skinny": [(16, 200, 2048, 128, {"WOQ_SM": "0"}), (7, 64, 1024, 32, {}), (64, 300, 1024, 128, {"WOQ_SM": "0"}),
                (100, 300, 1024, 128, {"WOQ_SKINNY": "2,4"})],
+    "smallm": [(16, 200, 2048, 128, {}), (64, 300, 1024, 128, {}), (24, 1000, 8192, 32, {}),
+               (5, 100, 1024, 64, {"WOQ_SM": "2,4"})],
     "gemm": [(100, 300, 1024, 128, {}), (160, 256, 512, 256, {})],
 }
 CASES = [(path, *c) for path, cs in PATHS.items() for c in cs]
-PATH_TAG = {"rows": "rows_dot2", "gemv": "gemv_mfma", "skinny": "skinny_mfma", "gemm": "gemm_mfma"}
+PATH_TAG = {"rows": "rows_dot2", "gemv": "gemv_mfma", "skinny": "skinny_mfma", "smallm": "smallm_lds",
+            "gemm": "gemm_mfma"}
 
 
 def _say(msg):
@@ -53,6 +58,7 @@ def _env(monkeypatch, env):
     monkeypatch.delenv("WOQ_DECODE_MFMA", raising=False)
     monkeypatch.delenv("WOQ_ROWS_U", raising=False)
     monkeypatch.delenv("WOQ_SKINNY", raising=False)
+    monkeypatch.delenv("WOQ_SM", raising=False)
     for key, val in env.items():
         monkeypatch.setenv(key, val)
 
@@ -227,7 +233,7 @@ XFRAG_CASES = [
 
 @pytest.mark.parametrize("m,n,k,group,with_bias,with_order,fmt", XFRAG_CASES)
 def test_skinny_fragment_prepass(woq, monkeypatch, m, n, k, group, with_bias, with_order, fmt):
-    _env(monkeypatch, {})
+    _env(monkeypatch, {"WOQ_SM": "0"})   # these narrow layers would otherwise take the LDS small-M path
     seed = 9100 + m + n + k
     x = workloads.activations_bf16(m, k, seed + 1)
     b = workloads.bias(n, seed + 2) if with_bias else None

@@ -18,7 +18,7 @@ CSRC = PKG / "csrc"
 BUILD = ROOT / "_build"
 LIB = PKG / "libwoq.so"
 
-SOURCES = ["api.hip", "codec.hip", "linear_rows.hip", "linear_gemv.hip", "linear_skinny.hip", "linear_gemm.hip", "gptq.hip", "awq.hip"]
+SOURCES = ["api.hip", "codec.hip", "linear_rows.hip", "linear_gemv.hip", "linear_skinny.hip", "linear_smallm.hip", "linear_gemm.hip", "gptq.hip", "awq.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -142,6 +142,56 @@ bool skinny_plan(int64_t m, int64_t n, int64_t k, int32_t group, LinearPlan* p) 
   return true;
 }
 
+// Small-M launch shape with the activation slice in LDS (path 6, 5 <= m <= 64):
+// workgroups of 8 waves with T weight tiles each (T in {1, 2}), K ranges of S
+// steps (S in {4, 8}).  Ranges of 8 steps from K = 8192 (fewer, larger partials
+// where K is long), else 4; two tiles a wave above 32 rows with 8-step ranges;
+// a shape whose LDS does not fit gives way to one tile, and if that does not
+// fit either the path declines (shorter ranges would double the partials).
+// (Measured on 1024x4096, 4096x4096, 4096x14336 and 14336x4096 at 5..64 rows,
+// groups 32, 128 and 256, against every shape.)  More than one range needs
+// the partial buffer (split_ok).  WOQ_SM="T,S" forces a shape (a tuning aid,
+// read on every call).
+bool sm_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool split_ok, LinearPlan* p) {
+  if (m < 5 || m > 64 || k >= ((int64_t)1 << 24) || m * k * 2 >= ((int64_t)1 << 31)) return false;
+  const int64_t nsteps = (k + 127) / 128;
+  const int64_t tiles = (n + 15) / 16;
+  const int mt = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
+  auto fits = [&](int t, int st) {
+    const int64_t ranges = (nsteps + st - 1) / st;
+    return (ranges == 1 || split_ok) && sm_lds_bytes(mt, st, t, group, false) <= kSkinnyLdsLimit;
+  };
+  int t = 0, st = 0;
+  int ft = 0, fs = 0;
+  const char* e = std::getenv("WOQ_SM");
+  if (e && std::sscanf(e, "%d,%d", &ft, &fs) == 2 && (ft == 1 || ft == 2) && (fs == 4 || fs == 8)) {
+    if (!fits(ft, fs)) return false;
+    t = ft;
+    st = fs;
+  } else {
+    const int s_pref = nsteps >= 64 ? 8 : 4;
+    const int t_pref = s_pref == 8 && m > 32 ? 2 : 1;
+    const int cand[2][2] = {{t_pref, s_pref}, {1, s_pref}};
+    for (const auto& c : cand) {
+      if (fits(c[0], c[1])) {
+        t = c[0];
+        st = c[1];
+        break;
+      }
+    }
+    if (t == 0) return false;
+  }
+  p->path = 6;
+  p->mt = mt;
+  p->ns = t;
+  p->cnt = st;
+  p->waves = 8;
+  p->splits = (int)((nsteps + st - 1) / st);
+  p->grid = (tiles + 8 * t - 1) / (8 * t) * p->splits;
+  p->fold_rows = 4;
+  return true;
+}
+
 // Decode GEMV launch shape.  Each wave takes `cnt` consecutive 128-input
 // steps (4, 8, 12 or 16) and a workgroup of ceil(steps / cnt) waves (at most
 // 16) covers K for 16 outputs.  A step costs the fewest instructions for
@@ -217,6 +267,25 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
     return p;
   }
   const bool force_tiled = std::getenv("WOQ_FORCE_TILED") != nullptr;   // tuning aid, read on every call
+  // From 16 to 64 rows, layers narrower than 800 tiles of 16 rows (where the
+  // small-M kernel below gives each workgroup fewer than 4 tiles, so every
+  // workgroup re-reads x for few weight rows) run on the path with the
+  // activation slice in LDS: 4096x14336 at 16 rows 23.1 -> 17.4 us, at 64 rows
+  // 37.9 -> 30.7 us; 1024x4096 at 48 rows 13.1 -> 11.8 us.  On wider layers and
+  // below 16 rows the small-M kernel is as fast or faster.  WOQ_SM="0" keeps
+  // every call off it, "T,S" puts every call of 5..64 rows on it with that
+  // shape, and a forced small-M shape (WOQ_SKINNY) keeps the rule from
+  // applying (tuning aids, read on every call).
+  {
+    const char* e = std::getenv("WOQ_SM");
+    const bool off = e && e[0] == '0';
+    const bool forced = e && !off;
+    const bool rule = m >= 16 && (n + 15) / 16 < 800 && std::getenv("WOQ_SKINNY") == nullptr;
+    if (!force_tiled && !off && (forced || rule) && sm_plan(m, n, k, group, split_ok, &p)) {
+      p.prep = has_order ? 1 : 0;
+      return p;
+    }
+  }
   // The small-M kernel takes up to 128 rows (from 65 rows only layers of at
   // least 800 weight tiles of 16 rows: 14336x4096 at 128 rows runs in 41 us
   // against the tiled GEMM's 46 us at group 128, 57 against 89 us at group 32).
@@ -304,6 +373,11 @@ LinearWorkspace linear_workspace_layout(int64_t m, int64_t n, int64_t k, int32_t
   } else if ((p.path == 1 || p.path == 4 || p.path == 5) && has_order) {
     w.xg_off = 0;
     w.xg_bytes = round256((size_t)m * (size_t)k * 2);
+  } else if (p.path == 6) {
+    w.xg_off = 0;
+    w.xg_bytes = has_order ? round256((size_t)m * (size_t)k * 2) : 0;
+    w.part_off = w.xg_bytes;
+    w.part_bytes = p.splits > 1 ? round256((size_t)p.splits * (size_t)m * (size_t)n * 4) : 0;
   } else if (p.path == 2) {
     const int64_t kpad = (k + 127) / 128 * 128;
     w.xg_off = 0;
@@ -683,6 +757,16 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
     }
     return launch_skinny(a, plan, s);
   }
+  if (plan.path == 6) {
+    if (has_order) {
+      uint16_t* xg = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
+      st = launch_prep(a.x, order, a.m, a.k, a.k, group, 0, xg, nullptr, m, s);
+      if (st != WOQ_OK) return st;
+      a.x = xg;
+    }
+    a.part = reinterpret_cast<float*>(wsb + ws.part_off);
+    return launch_sm(a, plan, s);
+  }
   if (plan.path == 4 || plan.path == 5) {
     if (has_order) {
       uint16_t* xg = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
@@ -945,6 +1029,12 @@ int32_t woq_linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, int32_t 
                     "group_blocks=%d grid=%lld prep=%s workspace=%zu",
                     p.mt, p.wm, p.ns, p.waves, p.cnt, p.gb, (long long)p.grid,
                     p.xfrag ? (p.prep ? "gather+fragments" : "fragments") : (p.prep ? "gather" : "none"), ws);
+      break;
+    case 6:
+      std::snprintf(buf, len,
+                    "path=smallm_lds act_tiles=%d weight_tiles_per_wave=%d waves=%d steps_per_range=%d "
+                    "k_ranges=%d group_blocks=%d grid=%lld prep=%s workspace=%zu",
+                    p.mt, p.ns, p.waves, p.cnt, p.splits, p.gb, (long long)p.grid, p.prep ? "gather" : "none", ws);
       break;
     case 4:
       std::snprintf(buf, len,

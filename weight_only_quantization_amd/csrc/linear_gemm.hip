@@ -190,6 +190,36 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
+// The same, four consecutive outputs a thread (n a multiple of 4, so the four
+// share a row; y aligned to four of its elements).
+__global__ __launch_bounds__(256) void splitk_reduce4_kernel(const float* __restrict__ part, int32_t splits,
+                                                             int32_t m, int32_t n, const float* __restrict__ bias,
+                                                             int32_t y_bf16, void* __restrict__ y) {
+  const int64_t total4 = (int64_t)m * n / 4;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const f32x4_t* p4 = reinterpret_cast<const f32x4_t*>(part);
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total4; t += stride) {
+    f32x4_t v = p4[t];
+    for (int r = 1; r < splits; ++r) {
+      const f32x4_t a = p4[(int64_t)r * total4 + t];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += a[e];
+    }
+    if (bias) {
+      const f32x4_t b = *reinterpret_cast<const f32x4_t*>(bias + (4 * t) % n);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += b[e];
+    }
+    if (y_bf16) {
+      uint32_t lo = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+      uint32_t hi = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+      reinterpret_cast<uint2*>(y)[t] = make_uint2(lo, hi);
+    } else {
+      reinterpret_cast<f32x4_t*>(y)[t] = v;
+    }
+  }
+}
+
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kJunk = 1024;                 // LDS that absorbs the loads of unused slots
@@ -865,11 +895,21 @@ int32_t launch_gemm(const LinearArgs& a, const LinearPlan& pl, void* sz_ws, hipS
                       pl.splits > 1 ? a.part : nullptr};
   const int32_t st = launch_gemm_tiles(a, pl, gp, stream);
   if (st != WOQ_OK || pl.splits <= 1) return st;
-  const int64_t total = (int64_t)a.m * a.n;
-  int64_t blocks = (total + 255) / 256;
+  return launch_splitk_reduce(a.part, pl.splits, a.m, a.n, a.bias, a.y_bf16, a.y, stream);
+}
+
+int32_t launch_splitk_reduce(const float* part, int32_t splits, int32_t m, int32_t n, const float* bias,
+                             int32_t y_bf16, void* y, hipStream_t stream) {
+  const int64_t total = (int64_t)m * n;
+  const bool vec = n % 4 == 0 && aligned(part, 16) && aligned(y, y_bf16 ? 8 : 16) && (!bias || aligned(bias, 16));
+  int64_t blocks = ((vec ? total / 4 : total) + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.part, pl.splits,
-                     a.m, a.n, a.bias, a.y_bf16, a.y);
+  if (vec)
+    hipLaunchKernelGGL(splitk_reduce4_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, splits, m, n,
+                       bias, y_bf16, y);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, splits, m, n,
+                       bias, y_bf16, y);
   return hip_status(hipGetLastError());
 }
 

@@ -48,11 +48,12 @@ struct LinearWorkspace {
 
 // Which kernel family runs a linear call, and with what launch shape.
 struct LinearPlan {
-  int path = 0;          // 0 none, 1 small-M MFMA (m <= 32), 2 tiled MFMA GEMM, 3 bias only (k == 0),
-                         // 4 decode GEMV (m <= 4)
+  int path = 0;          // 0 none, 1 small-M MFMA (m <= 128), 2 tiled MFMA GEMM, 3 bias only (k == 0),
+                         // 4 decode GEMV (m <= 4), 5 row-streaming decode (m <= 4),
+                         // 6 small-M MFMA with the activation slice in LDS (5 <= m <= 64)
   int mt = 1;            // 16-row activation tiles (small-M path)
   int fold_rows = 4;     // accumulator rows folded per tile (1 when m == 1)
-  int ns = 1;            // 16-row weight tiles per workgroup (small-M path)
+  int ns = 1;            // 16-row weight tiles per workgroup (small-M path; per wave on path 6)
   int wm = 1;            // small-M path: wave groups along the activation rows
   int waves = 4;         // waves per workgroup
   int gb = 4;            // 32-wide k blocks per quantization group inside a 128-wide k step (1, 2, 4)
@@ -60,12 +61,12 @@ struct LinearPlan {
   int64_t grid = 0;      // workgroups
   int bm = 0, bn = 0;    // tile of the GEMM path
   int64_t mpad = 0;      // rows of the per-group sum table (GEMM path)
-  int cnt = 0;           // 128-input steps per wave (decode and small-M paths)
+  int cnt = 0;           // 128-input steps per wave (decode and small-M paths; per K range on path 6)
   int64_t tail_n = 0;    // GEMM path: trailing output columns left to a second launch of
                          // 64-row tiles, so that the last round of workgroups is not half empty
   int rows_u = 0;        // row-streaming decode path (path 5): rows per workgroup
   int xfrag = 0;         // small-M path: a pre-pass writes the activations in MFMA fragment order
-  int splits = 1;        // GEMM path: K ranges over separate workgroups (partials summed after)
+  int splits = 1;        // GEMM path and path 6: K ranges over separate workgroups (partials summed after)
   int sps = 0;           // GEMM path: 128-input steps per K range when splits > 1
 };
 
@@ -208,6 +209,16 @@ constexpr int64_t kGemmMaxK = (int64_t)1 << 24;   // tile offsets of the GEMM pa
 int32_t launch_gemm_prep(const LinearArgs& a, const int32_t* order, uint16_t* xg, float* xs, void* sz_ws,
                          hipStream_t stream);
 int32_t launch_gemm(const LinearArgs& a, const LinearPlan& p, void* sz_ws, hipStream_t stream);
+// Split-K second pass: y = the [splits][m][n] float32 partials summed in
+// slice order, + bias, in y's type.
+int32_t launch_splitk_reduce(const float* part, int32_t splits, int32_t m, int32_t n, const float* bias,
+                             int32_t y_bf16, void* y, hipStream_t stream);
+// Small-M path with the activation slice in LDS (path 6): LDS bytes of one
+// workgroup (mt activation tiles, `steps` per K range, `tiles` weight tiles
+// per wave), and the launch (kernel, then the split-K pass when the plan has
+// more than one K range; a.part is the partial buffer).
+size_t sm_lds_bytes(int mt, int steps, int tiles, int32_t group, bool mx);
+int32_t launch_sm(const LinearArgs& a, const LinearPlan& p, hipStream_t stream);
 int32_t launch_fill_bias(const float* bias, int32_t m, int32_t n, int32_t y_bf16, void* y,
                          hipStream_t stream);
 // Row-streaming decode path (m <= 4, canonical weights): whether it takes

@@ -38,6 +38,8 @@ __all__ = [
     "ZP4",
     "MXFP4",
     "LLAMA3_8B_LAYER",
+    "MIDSIZE",
+    "SMALLBATCH",
 ]
 
 
@@ -218,6 +220,16 @@ def packed_weights(n: int, k: int, group: int, seed: int, std: float = 0.02):
 MIDSIZE = tuple(
     LinearCase(f"midsize_m{m}_{n}x{k}", m, n, k, 128, seed_w=180 + i, seed_x=280 + i + 10 * j)
     for j, m in enumerate((128, 256))
+    for i, (n, k) in enumerate(((1024, 4096), (4096, 4096), (4096, 14336), (14336, 4096)))
+)
+
+# Small batches (16 and 64 rows) on the same Llama-3-8B shapes: the layers
+# narrower than 800 tiles of 16 rows run on the small-M path with the
+# activation slice in LDS, 14336x4096 on the small-M kernel.  Sizes only, no
+# figure from the pages.
+SMALLBATCH = tuple(
+    LinearCase(f"smallbatch_m{m}_{n}x{k}", m, n, k, 128, seed_w=185 + i, seed_x=285 + i + 10 * j)
+    for j, m in enumerate((16, 64))
     for i, (n, k) in enumerate(((1024, 4096), (4096, 4096), (4096, 14336), (14336, 4096)))
 )
 
