@@ -481,6 +481,9 @@ def summarize_trace(root: Path) -> None:
         if d:
             out.append(f"bench down projection ({d['kernel']}): avg_launch_us {d['avg_launch_us']}  "
                        f"frac {d['frac']}")
+    for c in line.get("smallbatch") or []:
+        out.append(f"bench {c['name']}: {c['us']} us per call (HIP events, graph of back-to-back calls)  "
+                   f"plan: {c['plan']}")
     pf = line.get("prefill")
     if pf:
         for shp in pf["per_shape"]:
@@ -594,9 +597,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=32)
-    ap.add_argument("--only", choices=["all", "step", "dominant", "prefill"], default="all",
+    ap.add_argument("--only", choices=["all", "step", "dominant", "prefill", "smallbatch"], default="all",
                     help="step: the decode step alone; dominant: the dominant-kernel timing alone; "
-                         "prefill: the M=2048 timing alone (profiling runs)")
+                         "prefill: the M=2048 timing alone; smallbatch: M = 16 and 64 on the decode "
+                         "shapes alone (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
@@ -640,6 +644,11 @@ def main():
 
     if args.only == "prefill":
         print(json.dumps(dict(prefill=measure_prefill(torch, woq),
+                              kernel_source_sha256_16=kernel_source_hash())), flush=True)
+        return
+    if args.only == "smallbatch":
+        from workloads import SMALLBATCH
+        print(json.dumps(dict(smallbatch=measure_configs(torch, woq, cases=SMALLBATCH),
                               kernel_source_sha256_16=kernel_source_hash())), flush=True)
         return
     if args.only == "dominant":

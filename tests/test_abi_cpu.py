@@ -53,7 +53,8 @@ def test_status_strings(lib):
     (5, 4096, 4096, 128, "skinny_mfma"), (16, 14336, 4096, 32, "skinny_mfma"),
     (17, 4096, 4096, 128, "smallm_lds"), (32, 14336, 4096, 256, "skinny_mfma"),
     (33, 4096, 4096, 128, "smallm_lds"), (64, 14336, 4096, 32, "skinny_mfma"),
-    (15, 4096, 14336, 128, "skinny_mfma"), (16, 4096, 14336, 128, "smallm_lds"),
+    (7, 4096, 14336, 128, "skinny_mfma"), (8, 4096, 14336, 128, "smallm_lds"),
+    (15, 4096, 4096, 128, "skinny_mfma"), (16, 4096, 14336, 128, "smallm_lds"),
     (64, 4096, 14336, 256, "smallm_lds"), (64, 4096, 14336, 32, "skinny_mfma"),
     (48, 1024, 4096, 128, "smallm_lds"), (16, 12800, 4096, 128, "skinny_mfma"),
     (65, 4096, 4096, 128, "gemm_mfma"), (128, 14336, 4096, 32, "skinny_mfma"),

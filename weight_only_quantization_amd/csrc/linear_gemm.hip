@@ -173,15 +173,26 @@ __global__ __launch_bounds__(256) void fill_bias_kernel(const float* __restrict_
 }
 
 // Split-K: y = sum over the K ranges of their float32 partials, in range
-// order (the same result on every run), + bias, then y's type.
+// order (the same result on every run), + bias, then y's type.  The slices
+// are loaded kReduceBatch at a time before any is added, so a call waits for
+// ceil(splits / kReduceBatch) memory round trips rather than one per range.
+constexpr int kReduceBatch = 8;
+
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int32_t splits,
                                                             int32_t m, int32_t n, const float* __restrict__ bias,
                                                             int32_t y_bf16, void* __restrict__ y) {
   const int64_t total = (int64_t)m * n;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
-    float v = part[t];
-    for (int r = 1; r < splits; ++r) v += part[(int64_t)r * total + t];
+    float v = 0.f;
+    for (int r0 = 0; r0 < splits; r0 += kReduceBatch) {
+      float a[kReduceBatch];
+#pragma unroll
+      for (int j = 0; j < kReduceBatch; ++j) a[j] = r0 + j < splits ? part[(int64_t)(r0 + j) * total + t] : 0.f;
+#pragma unroll
+      for (int j = 0; j < kReduceBatch; ++j)
+        if (r0 + j < splits) v = r0 + j == 0 ? a[j] : v + a[j];
+    }
     if (bias) v += bias[t % n];
     if (y_bf16)
       reinterpret_cast<uint16_t*>(y)[t] = f32_to_bf16_bits(v);
@@ -199,11 +210,22 @@ __global__ __launch_bounds__(256) void splitk_reduce4_kernel(const float* __rest
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const f32x4_t* p4 = reinterpret_cast<const f32x4_t*>(part);
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total4; t += stride) {
-    f32x4_t v = p4[t];
-    for (int r = 1; r < splits; ++r) {
-      const f32x4_t a = p4[(int64_t)r * total4 + t];
+    f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int r0 = 0; r0 < splits; r0 += kReduceBatch) {
+      f32x4_t a[kReduceBatch];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] += a[e];
+      for (int j = 0; j < kReduceBatch; ++j)
+        a[j] = r0 + j < splits ? p4[(int64_t)(r0 + j) * total4 + t] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kReduceBatch; ++j) {
+        if (r0 + j >= splits) continue;
+        if (r0 + j == 0) {
+          v = a[j];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += a[j][e];
+        }
+      }
     }
     if (bias) {
       const f32x4_t b = *reinterpret_cast<const f32x4_t*>(bias + (4 * t) % n);
