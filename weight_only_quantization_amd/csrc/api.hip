@@ -781,13 +781,10 @@ int32_t linear_impl(const void* x_bf16, int64_t m, const uint8_t* packed, const 
   uint16_t* xg = reinterpret_cast<uint16_t*>(wsb + ws.xg_off);
   float* xs = reinterpret_cast<float*>(wsb + ws.xs_off);
   a.kpad = (a.k + 127) / 128 * 128;
-  // The activation pre-pass and the scale/zero table, one launch.  Without a
-  // gather and with K a multiple of 128 the GEMM reads x as given (natural
-  // order, rows of whole steps) and the pass only forms the piece sums.
-  const bool direct = !has_order && a.kpad == a.k;
-  st = launch_gemm_prep(a, order, direct ? nullptr : xg, xs, wsb + ws.sz_off, s);
+  // the activation pre-pass and the scale/zero table, one launch
+  st = launch_gemm_prep(a, order, xg, xs, wsb + ws.sz_off, s);
   if (st != WOQ_OK) return st;
-  if (!direct) a.x = xg;
+  a.x = xg;
   a.xs = xs;
   a.part = reinterpret_cast<float*>(wsb + ws.part_off);
   return launch_gemm(a, plan, wsb + ws.sz_off, s);
@@ -1056,7 +1053,7 @@ int32_t woq_linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, int32_t 
                     "path=gemm_mfma tile=%dx%d waves=%d group_blocks=%d tail_cols=%lld k_splits=%d grid=%lld "
                     "prep=%s workspace=%zu",
                     p.bm, p.bn, p.waves, p.gb, (long long)p.tail_n, p.splits, (long long)p.grid,
-                    has_order ? "gather+copy+groupsum" : (k % 128 == 0 ? "groupsum" : "copy+groupsum"), ws);
+                    has_order ? "gather+reorder+groupsum" : "reorder+groupsum", ws);
   }
   return WOQ_OK;
 }

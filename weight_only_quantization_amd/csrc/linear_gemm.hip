@@ -1,12 +1,11 @@
 // Tiled linear path (m > 16) and the activation pre-pass.
 //
-// Pre-pass: the float32 sum of x' over every "piece" (the part of a
-// quantization group inside one 128-wide k step: the whole group for groups
-// of at most 128 inputs), x' = x gathered through the act-order index when one
-// is given (linnet docs "Quantization", section "Importing GPTQ and AWQ": the
-// layer gathers its inputs first).  x' itself is written out, in natural
-// order with each row zero-padded to whole 128-input steps, only when the
-// GEMM cannot read x as given (a gather, or K not a multiple of 128).
+// Pre-pass: x' = x gathered through the act-order index when one is given
+// (linnet docs "Quantization", section "Importing GPTQ and AWQ": the layer
+// gathers its inputs first), optionally written in the slot order of the
+// nibble unpacker with each row zero-padded to whole 128-input steps, plus the
+// float32 sum of x' over every "piece": the part of a quantization group inside
+// one 128-wide k step (the whole group for groups of at most 128 inputs).
 // A second small pass lays the scales and zero points out per group as
 // (scale, -(128 + zero)) float pairs, [K/G][N rounded up to 256].
 //
@@ -22,8 +21,7 @@
 // without holding registers; one barrier per step hands a stage from the
 // loads to the arithmetic.  Both tiles are stored XOR-swizzled so the
 // reads of 8 neighbouring rows hit distinct banks.  Nibbles become bf16
-// (128 + code) in natural input order (one shift, then a byte permute and an
-// AND-OR per pair: the activations need no reordering); each MFMA takes one dword of every
+// (128 + code) with one AND-OR per pair; each MFMA takes one dword of every
 // lane's 16 loaded bytes (inputs u+32h+8b .. +8 of a 64-input unit u, h the
 // lane half), which keeps every MFMA inside one group for groups of 64 and
 // more; 32-input groups regroup the dwords between the lane halves with two
@@ -290,8 +288,7 @@ __device__ __forceinline__ f32x16_t mfma32f(float a, float b, f32x16_t c) {
 }
 
 struct GemmParams {
-  const uint16_t* xp;     // activations in natural order [M, kpad], zero past K (the caller's x when
-                          // no gather is needed and K is a multiple of 128, else the pre-pass copy)
+  const uint16_t* xp;     // pair-ordered activations [M, kpad], zero past K
   const uint8_t* packed;  // [N, K/2], or prepared blocks
   const float* xs;        // piece sums [K/piece][mpad]
   const f32x2_t* sz;      // (scale, -(128 + zero)) [K/G][npad]
@@ -622,7 +619,7 @@ __global__ __launch_bounds__(64 * Tl::kWaves) void gemm_kernel(GemmParams p) {
       if (blk + 1 < 8) load_af(blk + 1, afn);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const bf16x8_t bf = unpack_codes_natural(bd[L][nt][b], kNibPairMask, nib_offset);
+        const bf16x8_t bf = unpack_codes(bd[L][nt][b], kNibPairMask, nib_offset);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           if (folding) fold_tile(mt, nt);
@@ -892,13 +889,11 @@ int32_t launch_gemm_prep(const LinearArgs& a, const int32_t* order, uint16_t* xg
   const int32_t piece = a.group < kStepK ? a.group : kStepK;
   const int64_t ptotal = a.mpad * (a.kpad / 8);
   const int64_t stotal = (int64_t)ngroups * npad;
+  const int64_t pblocks = std::min<int64_t>((ptotal + 255) / 256, 65536);
   const int64_t sblocks = std::min<int64_t>((stotal + 255) / 256, 65536);
-  // Every format meets the activations in natural input order; MXFP4 needs no
-  // piece sums.  xg null: the GEMM reads x as given, and the pass only forms
-  // the piece sums (nothing at all for MXFP4) beside the (scale, zero) table.
-  const PrepArgs pa{a.x, order, a.m, a.k, a.kpad, 0, xg, a.mx ? nullptr : xs, a.mpad};
-  const int64_t pblocks = !xg && a.mx ? 0 : std::min<int64_t>((ptotal + 255) / 256, 65536);
   if (pblocks + sblocks == 0) return WOQ_OK;
+  // MXFP4 weights decode in natural input order and need no piece sums
+  const PrepArgs pa{a.x, order, a.m, a.k, a.kpad, a.mx ? 0 : 1, xg, a.mx ? nullptr : xs, a.mpad};
   const SzArgs sa = sz_args(a, ngroups, npad, sz_ws);
   const dim3 grid((unsigned)(pblocks + sblocks)), block(256);
   switch (piece / 8) {

@@ -49,20 +49,6 @@ __device__ __forceinline__ bf16x8_t unpack_codes(uint32_t d, uint32_t mask, uint
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
-// The same 8 codes in natural input order: dword v of the result pairs inputs
-// k+2v and k+2v+1.  A byte permute places byte v of d (codes 2v, 2v+1) and
-// byte v of d >> 4 (codes 2v+1, 2v+2) in the two halves, and the AND-OR keeps
-// the low nibble of each: one shift, four permutes and four AND-ORs a dword.
-__device__ __forceinline__ bf16x8_t unpack_codes_natural(uint32_t d, uint32_t mask, uint32_t offset) {
-  const uint32_t t = d >> 4;
-  u32x4_t r;
-  r[0] = (__builtin_amdgcn_perm(t, d, 0x0C040C00u) & mask) | offset;
-  r[1] = (__builtin_amdgcn_perm(t, d, 0x0C050C01u) & mask) | offset;
-  r[2] = (__builtin_amdgcn_perm(t, d, 0x0C060C02u) & mask) | offset;
-  r[3] = (__builtin_amdgcn_perm(t, d, 0x0C070C03u) & mask) | offset;
-  return __builtin_bit_cast(bf16x8_t, r);
-}
-
 // MXFP4: one dword holds 8 consecutive E2M1 codes (the even input in the low
 // nibble of each byte).  v_cvt_scalef32_pk_bf16_fp4 turns the two codes of one
 // byte into two bf16 values multiplied by `scale`; with a power-of-two scale
