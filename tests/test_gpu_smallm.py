@@ -153,3 +153,36 @@ def test_mxfp4(woq, monkeypatch, shape, m, n, k):
                          out_dtype=torch.float32)
     torch.cuda.synchronize()
     check_linear(y, ref, f"smallm MXFP4 m={m} {shape}")
+
+
+# Default plans at the edges: 256 K ranges (the split-K pass adds them in
+# batches), a single output row (7 of the 8 waves only help load the slice),
+# ragged rows and columns with groups of 256.
+EDGE = [
+    # m, n, k, group
+    (16, 100, 262144, 128),
+    (64, 1, 4096, 64),
+    (20, 17, 8192, 256),
+    (8, 300, 16384, 128),
+]
+
+
+@pytest.mark.parametrize("m,n,k,group", EDGE)
+def test_default_plan_edges(woq, monkeypatch, m, n, k, group):
+    monkeypatch.delenv("WOQ_SM", raising=False)
+    plan = woq.linear_plan(m, n, k, group, False)
+    assert "path=smallm_lds" in plan, plan
+    _say(f"smallm edge m={m} n={n} k={k} g={group} plan: {plan}")
+    seed = 9940 + m + n + k
+    w = workloads.weight(n, k, seed=seed)
+    x = workloads.activations_bf16(m, k, seed=seed + 1)
+    b = workloads.bias(n, seed=seed + 2)
+    q, s, z = woq.quantize_groups(torch.from_numpy(w).cuda(), group)
+    qr, sr, zr = oracle.quantize_groups(w, group)
+    ref = oracle.linear_int4_groups(x, oracle.pack_uint4(qr), sr, zr, n, k, group, bias=b)
+    packed = woq.pack_uint4(q)
+    for out in (torch.float32, torch.bfloat16):
+        y = woq.linear_int4_groups(to_dev_bf16(x), packed, s, z, bias=torch.from_numpy(b).cuda(), group=group,
+                                   out_dtype=out)
+        torch.cuda.synchronize()
+        check_linear(y, ref, f"smallm edge m={m} n={n} k={k} {out}")
