@@ -1,7 +1,8 @@
 // Small-M linear path with the activations shared through LDS: y = x .
 // dequant(W)^T + bias for group-wise 4-bit weights (linnet docs
 // "Quantization", std.quant table, linear_int4_groups), for 5 to 64
-// activation rows.  At these row counts the layer is bound by the weight
+// activation rows (by default from 16, or 8 when K >= 8192, on layers under
+// 800 tiles of 16 rows).  At these row counts the layer is bound by the weight
 // stream, and what decides the time is how little else moves: the
 // activations are read by every workgroup that covers a K range, so each
 // workgroup owns many weight rows and only a slice of K.
@@ -16,12 +17,14 @@
 //   operand order of the 16x16x32 instruction (chunk e of lane (q, c) of
 //   activation tile mt at step i holds the 8 inputs its weight dword e meets,
 //   in the unpacker's pair order), so that an operand is one contiguous
-//   ds_read_b128.  The sums of x over every group piece come from the same
+//   ds_read_b128; each 16-byte slot is XOR-swizzled by (step, chunk) so the
+//   slice stores spread over all banks.  The sums of x over every group piece come from the same
 //   loads: 8 values per thread in a fixed order, then a butterfly of lane
 //   exchanges (each lane of a piece ends with the same bits).
-// * Every wave issues all of its weight loads (T tiles x S steps, 16 bytes a
-//   lane: lane (q, c) reads inputs [32q, 32q + 32) of row c of a step) before
-//   it touches the activations, so the whole layer is in flight early.
+// * Every wave issues its slice loads, then its (scale, zero) loads, then all
+//   of its weight loads (T tiles x S steps, 16 bytes a lane: lane (q, c) reads
+//   inputs [32q, 32q + 32) of row c of a step), and only then waits, for its
+//   slice loads alone, to store the slice: the whole layer is in flight early.
 // * Per step and tile: nibbles become bf16 (128 + code) with one AND-OR per
 //   pair; per group piece the MFMAs give sum x (128 + code), and the fold
 //   acc += scale * (that - (128 + zero) * sum x) applies the zero point and
@@ -30,7 +33,8 @@
 //   across lane groups so each MFMA stays inside one group; MXFP4 converts
 //   each lane's block with its E8M0 scale (exact) and needs no fold.
 // * (scale, -(128 + zero)) pairs of the wave's rows and the range's groups
-//   are staged per wave in LDS, loaded before the weight stream.
+//   are staged per wave in LDS after the slice barrier (a wave reads only its
+//   own area, so its stores need no barrier).
 // * One K range: bias added, y stored.  More: the float32 partial tile goes
 //   to slice r of a [ranges][M][N] workspace buffer and a second pass adds
 //   the slices in range order (the same bits on every run), adds the bias
