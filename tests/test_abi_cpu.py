@@ -57,6 +57,8 @@ def test_status_strings(lib):
     (15, 4096, 4096, 128, "skinny_mfma"), (16, 4096, 14336, 128, "smallm_lds"),
     (64, 4096, 14336, 256, "smallm_lds"), (64, 4096, 14336, 32, "skinny_mfma"),
     (48, 1024, 4096, 128, "smallm_lds"), (16, 12800, 4096, 128, "skinny_mfma"),
+    (8, 1024, 4096, 128, "smallm_lds"), (8, 4096, 4096, 128, "skinny_mfma"), (7, 1024, 4096, 128, "skinny_mfma"),
+    (8, 1024, 4096, 32, "skinny_mfma"), (12, 4096, 14336, 256, "smallm_lds"), (12, 4096, 14336, 64, "skinny_mfma"),
     (65, 4096, 4096, 128, "gemm_mfma"), (128, 14336, 4096, 32, "skinny_mfma"),
     (128, 4096, 14336, 128, "gemm_mfma"), (129, 14336, 4096, 128, "gemm_mfma"), (2048, 14336, 4096, 128, "gemm_mfma"),
     (0, 64, 256, 32, "none"), (3, 64, 0, 32, "bias_fill"),

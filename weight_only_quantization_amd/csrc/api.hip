@@ -267,13 +267,15 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
     return p;
   }
   const bool force_tiled = std::getenv("WOQ_FORCE_TILED") != nullptr;   // tuning aid, read on every call
-  // From 16 to 64 rows (from 8 when K >= 8192), layers narrower than 800 tiles
+  // From 16 to 64 rows (from 8 with groups of 128 or more when K >= 8192 or
+  // N <= 1024), layers narrower than 800 tiles
   // of 16 rows (where the small-M kernel below gives each workgroup fewer than
   // 4 tiles, so every workgroup re-reads x for few weight rows) run on the
   // path with the activation slice in LDS: 4096x14336 at 16 rows 23.1 -> 15.3
   // us, at 64 rows 37.9 -> 31.0 us, at 8 rows 16.3 -> 14.9 us; 1024x4096 at 16
-  // rows 8.8 -> 6.9 us.  On wider layers and below 16 rows of shorter K the
-  // small-M kernel is as fast or faster.  WOQ_SM="0" keeps
+  // rows 8.8 -> 6.9 us, at 8 and 12 rows 7.3 / 8.2 -> 6.8 us.  On wider layers,
+  // and below 16 rows with groups of 32 or shorter K, the small-M kernel is as
+  // fast or faster.  WOQ_SM="0" keeps
   // every call off it, "T,S" puts every call of 5..64 rows on it with that
   // shape, and a forced small-M shape (WOQ_SKINNY) keeps the rule from
   // applying (tuning aids, read on every call).
@@ -281,7 +283,8 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
     const char* e = std::getenv("WOQ_SM");
     const bool off = e && e[0] == '0';
     const bool forced = e && !off;
-    const bool rule = (m >= 16 || (m >= 8 && k >= 8192)) && (n + 15) / 16 < 800 &&
+    const int64_t tiles = (n + 15) / 16;
+    const bool rule = (m >= 16 || (m >= 8 && group >= 128 && (k >= 8192 || tiles <= 64))) && tiles < 800 &&
                       std::getenv("WOQ_SKINNY") == nullptr;
     if (!force_tiled && !off && (forced || rule) && sm_plan(m, n, k, group, split_ok, &p)) {
       p.prep = has_order ? 1 : 0;

@@ -1,8 +1,8 @@
 // Small-M linear path with the activations shared through LDS: y = x .
 // dequant(W)^T + bias for group-wise 4-bit weights (linnet docs
 // "Quantization", std.quant table, linear_int4_groups), for 5 to 64
-// activation rows (by default from 16, or 8 when K >= 8192, on layers under
-// 800 tiles of 16 rows).  At these row counts the layer is bound by the weight
+// activation rows (by default from 16, or from 8 with groups of 128 or more
+// when K >= 8192 or N <= 1024, on layers under 800 tiles of 16 rows).  At these row counts the layer is bound by the weight
 // stream, and what decides the time is how little else moves: the
 // activations are read by every workgroup that covers a K range, so each
 // workgroup owns many weight rows and only a slice of K.
