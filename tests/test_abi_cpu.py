@@ -97,9 +97,14 @@ def test_plan_decode_kernels(monkeypatch):
                             ((4, 14336, 4096, 64), 4)):
         plan = woq.linear_plan(m, n, k, g)
         assert f"path=rows_dot2 rows_per_group={u} waves={(k + 2047) // 2048} " in plan, plan
-    # 3 and 4 rows of layers with >= 2^25 weights and groups >= 128 take the small-M MFMA kernel
-    for m, n, k, g in ((3, 14336, 4096, 128), (4, 4096, 14336, 256), (4, 8192, 4096, 128)):
+    # 3 and 4 rows of layers with >= 2^25 weights and groups >= 128 take the small-M MFMA kernel,
+    # or the tile GEMV when K >= 8192
+    for m, n, k, g in ((3, 14336, 4096, 128), (4, 8192, 4096, 128)):
         assert "path=skinny_mfma" in woq.linear_plan(m, n, k, g)
+    for m, n, k, g in ((4, 4096, 14336, 256), (3, 4096, 14336, 128)):
+        assert "path=gemv_mfma" in woq.linear_plan(m, n, k, g)
+    # (where the tile GEMV's staging does not fit in LDS, the small-M kernel keeps them)
+    assert "path=skinny_mfma" in woq.linear_plan(4, 8192, 28672, 128)
     monkeypatch.setenv("WOQ_DECODE_MFMA", "1")
     assert "path=gemv_mfma" in woq.linear_plan(1, 4096, 4096, 128)
     assert "path=gemv_mfma" in woq.linear_plan(4, 14336, 4096, 128)
