@@ -101,8 +101,10 @@ def test_plan_decode_kernels(monkeypatch):
     # or the tile GEMV when K >= 8192
     for m, n, k, g in ((3, 14336, 4096, 128), (4, 8192, 4096, 128)):
         assert "path=skinny_mfma" in woq.linear_plan(m, n, k, g)
-    for m, n, k, g in ((4, 4096, 14336, 256), (3, 4096, 14336, 128)):
+    for m, n, k, g in ((4, 4096, 14336, 256), (3, 4096, 14336, 128), (2, 4096, 14336, 128), (2, 8192, 28672, 128)):
         assert "path=gemv_mfma" in woq.linear_plan(m, n, k, g)
+    for m, n, k, g in ((2, 14336, 4096, 128), (2, 4096, 14336, 64), (1, 4096, 14336, 128)):
+        assert "path=rows_dot2" in woq.linear_plan(m, n, k, g)
     # (where the tile GEMV's staging does not fit in LDS, the small-M kernel keeps them)
     assert "path=skinny_mfma" in woq.linear_plan(4, 8192, 28672, 128)
     monkeypatch.setenv("WOQ_DECODE_MFMA", "1")

@@ -252,7 +252,8 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
   // of 128 and more the small-M MFMA kernel is faster there (14336x4096 at
   // m = 4: 12.8 against 15.1 us; 4096x14336: 13.7 against 16.2 us).
   const bool decode_mfma = std::getenv("WOQ_DECODE_MFMA") != nullptr;
-  const bool mfma_rows = rows_ok && !decode_mfma && m >= 3 && group >= 128 && n * k >= ((int64_t)1 << 25);
+  const bool mfma_rows = rows_ok && !decode_mfma && (m >= 3 || (m == 2 && k >= 8192)) && group >= 128 &&
+                         n * k >= ((int64_t)1 << 25);
   if (rows_ok && rows_supported(m, k) && !mfma_rows && !decode_mfma) {
     p.path = 5;
     p.rows_u = rows_per_group(m, n, k);
@@ -262,9 +263,11 @@ LinearPlan linear_plan(int64_t m, int64_t n, int64_t k, int32_t group, bool has_
     return p;
   }
   const bool force_skinny = std::getenv("WOQ_FORCE_SKINNY") != nullptr;   // tuning aid, read on every call
-  // The tile GEMV takes those 3-4 rows when K >= 8192: 4096x14336 at m = 4
-  // 13.0 against 14.5 us on the small-M kernel (on 14336x4096 the small-M
-  // kernel stays ahead, 12.8 against 13.7 us).
+  // The tile GEMV takes those 3-4 rows, and 2 rows, when K >= 8192: 4096x14336
+  // at m = 4 13.0 against 14.5 us on the small-M kernel, at m = 2 10.7 against
+  // 11.5 us on the row kernel; 8192x28672 at m = 2 32.3 against 43 us (on
+  // 14336x4096 the small-M kernel stays ahead at m = 3-4, 12.8 against 13.7 us,
+  // and the row kernel at m = 2, 10.6 against 12.5 us).
   const bool mfma_gemv = mfma_rows && k >= 8192;
   if (m <= 4 && !force_skinny && (!mfma_rows || mfma_gemv) && k < ((int64_t)1 << 26) &&
       gemv_plan(m, n, k, group, &p)) {
