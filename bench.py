@@ -481,7 +481,7 @@ def summarize_trace(root: Path) -> None:
         if d:
             out.append(f"bench down projection ({d['kernel']}): avg_launch_us {d['avg_launch_us']}  "
                        f"frac {d['frac']}")
-    for c in line.get("smallbatch") or []:
+    for c in (line.get("smallbatch") or []) + (line.get("fewrows") or []):
         out.append(f"bench {c['name']}: {c['us']} us per call (HIP events, graph of back-to-back calls)  "
                    f"plan: {c['plan']}")
     pf = line.get("prefill")
@@ -597,10 +597,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=32)
-    ap.add_argument("--only", choices=["all", "step", "dominant", "prefill", "smallbatch"], default="all",
+    ap.add_argument("--only", choices=["all", "step", "dominant", "prefill", "smallbatch", "fewrows"],
+                    default="all",
                     help="step: the decode step alone; dominant: the dominant-kernel timing alone; "
                          "prefill: the M=2048 timing alone; smallbatch: M = 16 and 64 on the decode "
-                         "shapes alone (profiling runs)")
+                         "shapes alone; fewrows: M = 2 to 4 on the decode shapes alone (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
@@ -649,6 +650,11 @@ def main():
     if args.only == "smallbatch":
         from workloads import SMALLBATCH
         print(json.dumps(dict(smallbatch=measure_configs(torch, woq, cases=SMALLBATCH),
+                              kernel_source_sha256_16=kernel_source_hash())), flush=True)
+        return
+    if args.only == "fewrows":
+        from workloads import FEWROWS
+        print(json.dumps(dict(fewrows=measure_configs(torch, woq, cases=FEWROWS),
                               kernel_source_sha256_16=kernel_source_hash())), flush=True)
         return
     if args.only == "dominant":
@@ -743,8 +749,13 @@ def main():
 
     prefill = None if args.no_prefill else measure_prefill(torch, woq)
     configs = None if args.no_configs else measure_configs(torch, woq)
-    sym16 = mxfp4 = zp4 = midsize = smallbatch = None
+    sym16 = mxfp4 = zp4 = midsize = smallbatch = fewrows = None
     if not args.no_configs:
+        from workloads import FEWROWS
+        fewrows = dict(
+            note="M = 2 to 4 on the decode shapes and 8192x28672: the row-streaming kernel, or the tile GEMV "
+                 "on layers of at least 2^25 weights with K >= 8192",
+            configs=measure_configs(torch, woq, cases=FEWROWS))
         from workloads import SMALLBATCH
         smallbatch = dict(
             note="M = 16 and 64 on the decode shapes: layers under 800 tiles of 16 rows run on the small-M path "
@@ -783,7 +794,7 @@ def main():
                     graph=not args.no_graph, accumulate="f32",
                     tokens_per_s_linears_only=round(1.0 / (ms_per_step * 1e-3), 1) if args.layers == 32 else None),
         roofline=roofline, grouped=grouped, prepared=prepared, prefill=prefill, configs=configs,
-        sym16=sym16, mxfp4=mxfp4, zp4=zp4, smallbatch=smallbatch, midsize=midsize,
+        sym16=sym16, mxfp4=mxfp4, zp4=zp4, fewrows=fewrows, smallbatch=smallbatch, midsize=midsize,
         cpu_baseline=cpu,
     )
     print(json.dumps(line), flush=True)

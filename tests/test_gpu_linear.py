@@ -275,7 +275,7 @@ def _sample_rows(n, seed, count=48):
 
 
 FULL = (list(workloads.DECODE) + list(workloads.PREFILL) + list(workloads.ACTORDER) + list(workloads.SWEEP)
-        + list(workloads.MIDSIZE) + list(workloads.SMALLBATCH))
+        + list(workloads.MIDSIZE) + list(workloads.SMALLBATCH) + list(workloads.FEWROWS))
 
 
 @pytest.mark.slow

@@ -40,6 +40,7 @@ __all__ = [
     "LLAMA3_8B_LAYER",
     "MIDSIZE",
     "SMALLBATCH",
+    "FEWROWS",
 ]
 
 
@@ -231,6 +232,17 @@ SMALLBATCH = tuple(
     LinearCase(f"smallbatch_m{m}_{n}x{k}", m, n, k, 128, seed_w=185 + i, seed_x=285 + i + 10 * j)
     for j, m in enumerate((16, 64))
     for i, (n, k) in enumerate(((1024, 4096), (4096, 4096), (4096, 14336), (14336, 4096)))
+)
+
+# Two to four activation rows (a few decode streams at once) on the same
+# Llama-3-8B shapes and on 8192x28672: the row-streaming kernel, or the tile
+# GEMV on the layers of at least 2^25 weights with K >= 8192.  Sizes only, no
+# figure from the pages.
+FEWROWS = tuple(
+    [LinearCase(f"fewrows_m{m}_{n}x{k}", m, n, k, 128, seed_w=190 + i, seed_x=290 + i + 10 * j)
+     for j, m in enumerate((2, 3, 4))
+     for i, (n, k) in enumerate(((1024, 4096), (4096, 4096), (4096, 14336), (14336, 4096)))]
+    + [LinearCase(f"fewrows_m{m}_8192x28672", m, 8192, 28672, 128, seed_w=195, seed_x=295 + m) for m in (2, 4)]
 )
 
 SYM16 = tuple(
