@@ -80,6 +80,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 __device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
+// Prepared weights are read once per call as whole 1 KB blocks: cache policy
+// nt (non-temporal) with sc1 (agent scope) streams them through L2 without
+// displacing the activations, and skips the compute unit's vector L1.
+// Canonical rows are read 64 bytes a step, so each cache line serves two
+// steps and keeps the default policy.
+constexpr int kStreamPolicy = 0x12;   // sc1 | nt
+__device__ __forceinline__ u32x4_t bload16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kStreamPolicy));
+}
 
 // Sum of the 8 bf16 values of a 16-byte chunk, in float32.  (The whole
 // vector is bit-cast: this compiler resolves a bit_cast of one element of a
@@ -127,7 +136,7 @@ __device__ __forceinline__ float lane_group_sum(float v) {
 // converted by v_cvt_scalef32_pk_bf16_fp4 into bf16 values already multiplied
 // by the block's power-of-two scale (exact), so the MFMAs accumulate straight
 // into the outputs with the activations in natural order and no fold.
-template <int GB, int FR, int CC, int PF, int FMT, bool GRP>
+template <int GB, int FR, int CC, int PF, int FMT, bool GRP, bool PREP>
 __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   constexpr bool S16 = FMT == kFmtS16, MX = FMT == kFmtMX;
   static_assert(!MX || GB == 1, "MXFP4 blocks hold 32 inputs");
@@ -166,7 +175,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
   // Weights: canonical rows [N, K/2], or prepared 1 KB blocks (16 rows x one
   // 128-input step, tile-major) whose 16-byte slot l is exactly lane l's share
   // of a step, so a step is one contiguous kilobyte.
-  const bool prep = p.prepared != 0;   // uniform
+  constexpr bool prep = PREP;   // p.prepared != 0
   const __amdgpu_buffer_rsrc_t rb =
       prep ? rsrc(pr.packed + (int64_t)tile * p.nsteps * 1024, (uint32_t)p.nsteps * 1024u)
            : rsrc(pr.packed + (int64_t)row0 * row_bytes, (uint32_t)rows * row_bytes);
@@ -324,7 +333,11 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
                              : (uint32_t)c * row_bytes + 16u * (uint32_t)q + (uint32_t)s0 * (kStepK / 2);
   auto issue = [&](int slot, int i) {
     const uint32_t dead = (uint32_t)(live - 1 - i) & kOffsetOOB;    // uniform
-    bq[slot] = bload16(rb, (boff + (uint32_t)i * bstep) | dead);
+    const uint32_t off = (boff + (uint32_t)i * bstep) | dead;
+    if constexpr (PREP)
+      bq[slot] = bload16_stream(rb, off);
+    else
+      bq[slot] = bload16(rb, off);
   };
 
   load_x();
@@ -477,10 +490,13 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
 template <int GB, int FR, int CC, int FMT>
 int32_t launch_one(const GemvParams& gp, const LinearPlan& pl, size_t lds, hipStream_t stream) {
   const bool grp = gp.nprob > 1;
-  auto kern = grp ? gemv_kernel<GB, FR, CC, 4, FMT, true> : gemv_kernel<GB, FR, CC, 4, FMT, false>;
+  const bool prep = gp.prepared != 0;
+  auto kern = grp ? (prep ? gemv_kernel<GB, FR, CC, 4, FMT, true, true> : gemv_kernel<GB, FR, CC, 4, FMT, true, false>)
+                  : (prep ? gemv_kernel<GB, FR, CC, 4, FMT, false, true> : gemv_kernel<GB, FR, CC, 4, FMT, false, false>);
   if (lds > 64 * 1024) {
-    static std::atomic<uint64_t> raised[2] = {{0}, {0}};   // per kernel, one bit per device
-    const int32_t st = raise_lds_limit(reinterpret_cast<const void*>(kern), 160 * 1024, raised[grp ? 1 : 0]);
+    static std::atomic<uint64_t> raised[4] = {{0}, {0}, {0}, {0}};   // per kernel, one bit per device
+    const int32_t st = raise_lds_limit(reinterpret_cast<const void*>(kern), 160 * 1024,
+                                       raised[(grp ? 1 : 0) + (prep ? 2 : 0)]);
     if (st != WOQ_OK) return st;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)pl.grid), dim3(64 * pl.waves), lds, stream, gp);

@@ -78,6 +78,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 __device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
+// Weight loads: every packed byte is read once per call, in whole cache lines.
+// Cache policy nt (non-temporal) with sc1 (agent scope): the lines stream
+// through L2 without displacing the activations and scales that other
+// workgroups re-read, and are not kept in the compute unit's vector L1.
+constexpr int kStreamPolicy = 0x12;   // sc1 | nt
+__device__ __forceinline__ u32x4_t bload16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kStreamPolicy));
+}
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
@@ -272,7 +280,7 @@ __global__ __launch_bounds__(1024) void rows_kernel(RowsParams p) {
   u32x4_t w[U];
   const uint32_t woff = ((uint32_t)kin / 2u) | dead;
 #pragma unroll
-  for (int u = 0; u < U; ++u) w[u] = bload16(rw, woff + (uint32_t)u * row_bytes);
+  for (int u = 0; u < U; ++u) w[u] = bload16_stream(rw, woff + (uint32_t)u * row_bytes);
   // Every load above is issued before any of them is waited for: without
   // this the scheduler delays weight loads behind the activation math to save
   // registers, and the stream starts late.
