@@ -211,11 +211,13 @@ __global__ __launch_bounds__(256) void splitk_reduce4_kernel(const float* __rest
   const f32x4_t* p4 = reinterpret_cast<const f32x4_t*>(part);
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total4; t += stride) {
     f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // Each partial is read exactly once: non-temporal loads.
     for (int r0 = 0; r0 < splits; r0 += kReduceBatch) {
       f32x4_t a[kReduceBatch];
 #pragma unroll
       for (int j = 0; j < kReduceBatch; ++j)
-        a[j] = r0 + j < splits ? p4[(int64_t)(r0 + j) * total4 + t] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        a[j] = r0 + j < splits ? __builtin_nontemporal_load(p4 + (int64_t)(r0 + j) * total4 + t)
+                               : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < kReduceBatch; ++j) {
         if (r0 + j >= splits) continue;
